@@ -1,0 +1,267 @@
+"""CPU oracle for block-sparse video self-attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It wraps ``liboracle.so`` (plain C, double precision,
+OpenMP) built from ``bsa_oracle.c`` in this folder; it shares no code with the
+GPU library and the GPU library never imports it.
+
+Each wrapper marshals numpy arrays into the C routine of the same name; the
+arithmetic, and the citation of the page passage each step follows, live in
+``bsa_oracle.c``.  bf16 tensors travel as ``uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "bsa_oracle.c")
+
+TILE = 64
+# extents (t, h, w) of the nine 64-token shapes, by shape id
+SHAPE_NAMES = ["4x4x4", "2x4x8", "2x8x4", "8x4x2", "4x2x8", "4x8x2", "8x2x4", "2x2x16", "16x2x2"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-std=c11", "-Wall", "-shared", "-fPIC",
+               "-o", tmp, SRC_PATH, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.orc_perm_static.argtypes = [i32, i32, i32, i32, i32, i32, P]
+        L.orc_perm_static.restype = i32
+        L.orc_shape_extent.argtypes = [i32, i32]
+        L.orc_shape_extent.restype = i32
+        L.orc_shape_stats.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, P]
+        L.orc_shape_stats.restype = None
+        L.orc_shape_choose.argtypes = [P, i32, i32, i32, i32, f64, f64, P, P]
+        L.orc_shape_choose.restype = None
+        L.orc_perm_dynamic.argtypes = [P, i32, i32, i32, i32, P]
+        L.orc_perm_dynamic.restype = i32
+        L.orc_gather.argtypes = [P, P, i32, i32, i64, i32, i32, P]
+        L.orc_gather.restype = None
+        L.orc_scatter.argtypes = [P, P, i32, i32, i64, i32, i32, P]
+        L.orc_scatter.restype = None
+        L.orc_pool.argtypes = [P, i32, i32, i32, i32, i32, P]
+        L.orc_pool.restype = None
+        L.orc_topk.argtypes = [P, P, i32, i32, i32, i32, i32, P, i32, P, P, P, P]
+        L.orc_topk.restype = None
+        L.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, f64, P, i32, P, P]
+        L.orc_attention.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def perm_static(grid, tile=(4, 4, 4)) -> np.ndarray:
+    """Tiled video slot -> raster video index for static tiles, ``int32 [T*H*W]``."""
+    T, Hg, W = grid
+    out = np.empty(T * Hg * W, np.int32)
+    if lib().orc_perm_static(T, Hg, W, *tile, _ptr(out)) != 0:
+        raise ValueError("grid not divisible by the tile, or tile is not 64 tokens")
+    return out
+
+
+def shape_extent(shape_id: int):
+    return tuple(lib().orc_shape_extent(shape_id, a) for a in range(3))
+
+
+def shape_stats(q_raster: np.ndarray, n_prefix: int, grid) -> np.ndarray:
+    """Mean |delta Q| along (t, h, w) per 8x8x8 region, ``float64 [B, R, 3]``."""
+    q = _c(q_raster, np.uint16)
+    B, Ntot, H, D = q.shape
+    T, Hg, W = grid
+    assert Ntot == n_prefix + T * Hg * W
+    R = (T // 8) * (Hg // 8) * (W // 8)
+    out = np.empty((B, R, 3), np.float64)
+    lib().orc_shape_stats(_ptr(q), B, n_prefix, T, Hg, W, H, D, _ptr(out))
+    return out
+
+
+def shape_choose(stats: np.ndarray, grid, tau: float, rel_eps: float = 1e-4):
+    """Shape id per region (``uint8 [B, R]``) and near-threshold flags."""
+    st = _c(stats, np.float64)
+    B, R, _ = st.shape
+    T, Hg, W = grid
+    shape = np.empty((B, R), np.uint8)
+    near = np.empty((B, R), np.uint8)
+    lib().orc_shape_choose(_ptr(st), B, T, Hg, W, float(tau), float(rel_eps), _ptr(shape), _ptr(near))
+    return shape, near
+
+
+def perm_dynamic(shape: np.ndarray, grid) -> np.ndarray:
+    """Tiled video slot -> raster video index per batch, ``int32 [B, T*H*W]``."""
+    sh = _c(shape, np.uint8)
+    B = sh.shape[0]
+    T, Hg, W = grid
+    out = np.empty((B, T * Hg * W), np.int32)
+    if lib().orc_perm_dynamic(_ptr(sh), B, T, Hg, W, _ptr(out)) != 0:
+        raise ValueError("invalid shape map")
+    return out
+
+
+def _perm_b(perm, B, Nv):
+    p = _c(perm, np.int32)
+    if p.ndim == 1:
+        p = np.ascontiguousarray(np.broadcast_to(p, (B, Nv)))
+    assert p.shape == (B, Nv)
+    return p
+
+
+def gather(x_raster: np.ndarray, perm: np.ndarray, n_prefix: int) -> np.ndarray:
+    """Raster ``[B, Ntot, H, D]`` -> tiled ``[B, H, Ntot, D]`` (exact copies)."""
+    x = _c(x_raster, np.uint16)
+    B, Ntot, H, D = x.shape
+    Nv = Ntot - n_prefix
+    p = _perm_b(perm, B, Nv)
+    out = np.empty((B, H, Ntot, D), np.uint16)
+    lib().orc_gather(_ptr(x), _ptr(p), B, n_prefix, Nv, H, D, _ptr(out))
+    return out
+
+
+def scatter(x_tiled: np.ndarray, perm: np.ndarray, n_prefix: int) -> np.ndarray:
+    """Tiled ``[B, H, Ntot, D]`` -> raster ``[B, Ntot, H, D]`` (exact copies)."""
+    x = _c(x_tiled, np.uint16)
+    B, H, Ntot, D = x.shape
+    Nv = Ntot - n_prefix
+    p = _perm_b(perm, B, Nv)
+    out = np.empty((B, Ntot, H, D), np.uint16)
+    lib().orc_scatter(_ptr(x), _ptr(p), B, n_prefix, Nv, H, D, _ptr(out))
+    return out
+
+
+def pool(x_tiled: np.ndarray, n_prefix: int) -> np.ndarray:
+    """Per video tile mean of the 64 tokens, ``float32 [B, H, nvt, D]``."""
+    x = _c(x_tiled, np.uint16)
+    B, H, Ntot, D = x.shape
+    nvt = (Ntot - n_prefix) // TILE
+    out = np.empty((B, H, nvt, D), np.float32)
+    lib().orc_pool(_ptr(x), B, H, n_prefix, nvt, D, _ptr(out))
+    return out
+
+
+def topk(qp: np.ndarray, kp: np.ndarray, k: int, rows=None):
+    """Kept video key tiles per query tile.
+
+    Returns ``(idx int32 [B,H,nrows,k] ascending, s_k, s_k1, mag)``; the last
+    three are ``float64 [B,H,nrows]`` (k-th score, (k+1)-th score or NaN,
+    largest sum of |products| in the row)."""
+    q = _c(qp, np.float32)
+    kk = _c(kp, np.float32)
+    B, H, n, D = q.shape
+    if not 1 <= k <= n:
+        raise ValueError("k out of range")
+    r = None if rows is None else _c(rows, np.int32)
+    nrows = n if r is None else r.shape[0]
+    idx = np.empty((B, H, nrows, k), np.int32)
+    s_k = np.empty((B, H, nrows), np.float64)
+    s_k1 = np.empty((B, H, nrows), np.float64)
+    mag = np.empty((B, H, nrows), np.float64)
+    lib().orc_topk(_ptr(q), _ptr(kk), B, H, n, D, k, _ptr(r), nrows, _ptr(idx), _ptr(s_k),
+                   _ptr(s_k1), _ptr(mag))
+    return idx, s_k, s_k1, mag
+
+
+def attention(q_bh, k_bh, v_bh, n_prefix: int, idx_bh, scale: float, qtiles):
+    """Exact double-precision attention for one (b,h) slice of tiled tensors.
+
+    ``q_bh, k_bh, v_bh``: ``uint16 [Ntot, D]``; ``idx_bh``: ``int32 [nvt, k]``
+    (may be empty when there are no video tiles); ``qtiles``: tiled query tile
+    numbers.  Returns ``(out float64 [nq, 64, D], lse float64 [nq, 64])``."""
+    q = _c(q_bh, np.uint16)
+    kx = _c(k_bh, np.uint16)
+    v = _c(v_bh, np.uint16)
+    Ntot, D = q.shape
+    nvt = (Ntot - n_prefix) // TILE
+    ix = _c(idx_bh, np.int32)
+    k = ix.shape[1] if ix.ndim == 2 else 0
+    qt = _c(qtiles, np.int32)
+    nq = qt.shape[0]
+    out = np.empty((nq, TILE, D), np.float64)
+    lse = np.empty((nq, TILE), np.float64)
+    lib().orc_attention(_ptr(q), _ptr(kx), _ptr(v), n_prefix, nvt, D, k, _ptr(ix), float(scale),
+                        _ptr(qt), nq, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def plan(q_tiled, k_tiled, n_prefix: int, k: int):
+    """Pool Q and K, score and select: ``(qp, kp, idx, s_k, s_k1, mag)``."""
+    qp = pool(q_tiled, n_prefix)
+    kp = pool(k_tiled, n_prefix)
+    idx, s_k, s_k1, mag = topk(qp, kp, k)
+    return qp, kp, idx, s_k, s_k1, mag
+
+
+def forward_full(q_tiled, k_tiled, v_tiled, n_prefix: int, idx, scale: float):
+    """Attention output for every query tile of every (b,h): ``float64 [B,H,Ntot,D]``."""
+    B, H, Ntot, D = q_tiled.shape
+    nqt = Ntot // TILE
+    out = np.empty((B, H, Ntot, D), np.float64)
+    lse = np.empty((B, H, Ntot), np.float64)
+    tiles = np.arange(nqt, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            ix = idx[b, h] if idx is not None else np.zeros((0, 0), np.int32)
+            o, l = attention(q_tiled[b, h], k_tiled[b, h], v_tiled[b, h], n_prefix, ix, scale, tiles)
+            out[b, h] = o.reshape(Ntot, D)
+            lse[b, h] = l.reshape(Ntot)
+    return out, lse
+
+
+def reference(q_raster, k_raster, v_raster, *, grid, n_prefix: int, k: int, scale: float,
+              tile=(4, 4, 4), dynamic: bool = False, tau: float = 0.10):
+    """The whole path on raster inputs; returns a dict with every intermediate.
+
+    Output ``o`` is raster ``float64 [B, Ntot, H, D]``."""
+    B = q_raster.shape[0]
+    res = {}
+    if dynamic:
+        st = shape_stats(q_raster, n_prefix, grid)
+        shape, near = shape_choose(st, grid, tau)
+        perm = perm_dynamic(shape, grid)
+        res.update(stats=st, shape=shape, shape_near=near)
+    else:
+        perm = np.ascontiguousarray(np.broadcast_to(perm_static(grid, tile), (B, grid[0] * grid[1] * grid[2])))
+    qt = gather(q_raster, perm, n_prefix)
+    kt = gather(k_raster, perm, n_prefix)
+    vt = gather(v_raster, perm, n_prefix)
+    qp, kp, idx, s_k, s_k1, mag = plan(qt, kt, n_prefix, k)
+    o_t, lse = forward_full(qt, kt, vt, n_prefix, idx, scale)
+    # scatter the float64 output back to raster order
+    Bq, H, Ntot, D = o_t.shape
+    o = np.empty((Bq, Ntot, H, D), np.float64)
+    for b in range(Bq):
+        src = np.empty(Ntot, np.int64)
+        src[:n_prefix] = np.arange(n_prefix)
+        src[n_prefix:] = n_prefix + perm[b]
+        o[b, src] = o_t[b].transpose(1, 0, 2)
+    res.update(perm=perm, q_tiled=qt, k_tiled=kt, v_tiled=vt, qp=qp, kp=kp, idx=idx, s_k=s_k,
+               s_k1=s_k1, mag=mag, o_tiled=o_t, lse=lse, o=o)
+    return res

@@ -172,7 +172,7 @@ def topk(qp: np.ndarray, kp: np.ndarray, k: int, rows=None):
 
     Returns ``(idx int32 [B,H,nrows,k] ascending, s_k, s_k1, mag)``; the last
     three are ``float64 [B,H,nrows]`` (k-th score, (k+1)-th score or NaN,
-    largest sum of |products| in the row)."""
+    larger sum of |products| of those two entries)."""
     q = _c(qp, np.float32)
     kk = _c(kp, np.float32)
     B, H, n, D = q.shape

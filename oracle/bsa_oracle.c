@@ -407,8 +407,9 @@ static int cmp_int(const void *a, const void *b)
  * pooled vectors; the kept set is the first k of j ordered by (-s_ij, j),
  * written in ascending j order to idx[b][h][row][0..k).
  * Per row also: s_k (k-th largest), s_k1 ((k+1)-th, or NaN when k == n) and
- * mag = max_j sum_d |qp_i[d] kp_j[d]| (scale of the rounding error of any
- * single-precision evaluation of the scores).  Any of these may be NULL.
+ * mag = the larger of sum_d |qp_i[d] kp_j[d]| over the k-th and (k+1)-th
+ * entries (what bounds the rounding error of a single-precision evaluation of
+ * the two scores that decide the boundary).  Any of these may be NULL.
  * qp, kp: [B][H][n][D]; idx: [B][H][nrows][k]; s_k, s_k1, mag: [B][H][nrows].
  */
 void orc_topk(const float *qp, const float *kp, int B, int H, int n, int D, int k,
@@ -424,20 +425,24 @@ void orc_topk(const float *qp, const float *kp, int B, int H, int n, int D, int 
             const float *q = qp + ((int64_t)bh * n + i) * D;
             scored *sc = (scored *)malloc(sizeof(scored) * (size_t)n);
             int *keep = (int *)malloc(sizeof(int) * (size_t)k);
-            double mx = 0.0;
             for (int j = 0; j < n; ++j) {
                 const float *kk = kp + ((int64_t)bh * n + j) * D;
-                double s = 0.0, a = 0.0;
-                for (int d = 0; d < D; ++d) {
+                double s = 0.0;
+                for (int d = 0; d < D; ++d)
                     s += (double)q[d] * (double)kk[d];
-                    a += fabs((double)q[d] * (double)kk[d]);
-                }
                 sc[j].s = s;
                 sc[j].j = j;
+            }
+            qsort(sc, (size_t)n, sizeof(scored), cmp_scored);
+            double mx = 0.0;
+            for (int t = k - 1; t <= k && t < n; ++t) {
+                const float *kk = kp + ((int64_t)bh * n + sc[t].j) * D;
+                double a = 0.0;
+                for (int d = 0; d < D; ++d)
+                    a += fabs((double)q[d] * (double)kk[d]);
                 if (a > mx)
                     mx = a;
             }
-            qsort(sc, (size_t)n, sizeof(scored), cmp_scored);
             for (int t = 0; t < k; ++t)
                 keep[t] = sc[t].j;
             qsort(keep, (size_t)k, sizeof(int), cmp_int);

@@ -1,0 +1,196 @@
+"""Benchmark: one step = the whole block-sparse attention path on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--keep K]
+
+A step runs, on one stream, every stage of the path over one batch of
+synthetic inputs already resident in HBM: tile order (BUILD), gather of Q, K
+and V into tile order, the plan (pooling, pooled scores, top-k), the sparse
+attention forward, and the scatter of O back to raster order.  The default
+workload is the 720p Prism-scale grid: 32 x 48 x 80 tokens (1,920 tiles of
+4x4x4), batch 2, 24 heads, head_dim 128, 480 kept tiles per query tile.
+
+Prints one JSON line: effective TFLOP/s over the kept tiles (4*B*H*D * sum of
+attended key tokens per query) for the whole step, the forward kernel's
+roofline against the bf16 dense MFMA peak, per-stage times from HIP events on
+the launch stream, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (256 CUs x 2.4 GHz)
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective TFLOP/s (kept tiles) + ms/call, 122,880-token grid @25% keep, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prism720p")
+    ap.add_argument("--keep", type=int, default=None, help="override kept tiles per query tile")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tiles", type=int, default=96, help="query tiles in the CPU oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, q, k, v, n_tiles: int):
+    """The oracle on one (batch, head) slice: gather, pooling and top-k over all
+    of the head's rows, attention on `n_tiles` sampled query tiles; the head's
+    time is extrapolated linearly over its query tiles."""
+    import oracle
+    b, h = 0, 0
+    sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+    qs, ks, vs = sl(q), sl(k), sl(v)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    if wl.dynamic:
+        st = oracle.shape_stats(qs, wl.n_prefix, wl.grid)
+        shape, _ = oracle.shape_choose(st, wl.grid, float(np.float32(wl.tau)))
+        perm = oracle.perm_dynamic(shape, wl.grid)
+    else:
+        perm = oracle.perm_static(wl.grid, wl.tile)[None]
+    qt, kt, vt = (oracle.gather(x, perm, wl.n_prefix) for x in (qs, ks, vs))
+    qp, kp = oracle.pool(qt, wl.n_prefix), oracle.pool(kt, wl.n_prefix)
+    idx, *_ = oracle.topk(qp, kp, wl.keep_tiles)
+    t_plan = time.perf_counter() - t0
+    nqt = wl.n_tokens // 64
+    rng = np.random.default_rng(1234)
+    tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0], float(np.float32(wl.scale)), tiles)
+    t_attn = time.perf_counter() - t0
+    head_seconds = t_plan + t_attn * nqt / len(tiles)
+    head_flops = wl.effective_flops() / (wl.batch * wl.heads)
+    return {
+        "value": head_flops / head_seconds / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "ms_per_call_extrapolated": head_seconds * wl.batch * wl.heads * 1e3,
+        "sample": (f"one (batch, head) slice of the same workload: gather + pool + top-k over all {wl.n_video_tiles} "
+                   f"query tiles ({t_plan:.2f} s) and fp64 attention on {len(tiles)} of {nqt} query tiles "
+                   f"({t_attn:.2f} s), extrapolated linearly to the head and scaled by the head's share of "
+                   f"the effective FLOPs"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_attention_39_amd as bsa
+    import synthetic as S
+
+    wl = S.WORKLOADS[args.workload]
+    if args.keep:
+        wl = wl.with_keep(args.keep)
+    t0 = time.perf_counter()
+    q, k, v = S.qkv(wl)
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] {wl.name}: inputs generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        c = torch.empty_like(a)
+        torch.cuda.synchronize()
+        c.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done", file=sys.stderr, flush=True)
+        del a, c
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+    att = bsa.BlockSparseAttention(desc)
+    out = torch.empty_like(qd)
+    torch.cuda.synchronize()
+
+    stages = ["build", "gather", "plan", "forward", "scatter"]
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        mark(0)
+        att.build(qd)
+        mark(1)
+        att.gather_qkv(qd, kd, vd)
+        mark(2)
+        att.plan()
+        mark(3)
+        att.forward()
+        mark(4)
+        att.scatter_out(out)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_stage = {s: [] for s in stages}
+    totals = []
+    for ev in events:
+        for j, s in enumerate(stages):
+            per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
+        totals.append(ev[0].elapsed_time(ev[5]))
+    ms_step = float(np.mean(totals))
+    F = wl.effective_flops()
+    fwd_ms = float(np.mean(per_stage["forward"]))
+    achieved = F / (fwd_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": F / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid_thw": list(wl.grid), "tokens": wl.n_tokens,
+                   "video_tiles": wl.n_video_tiles, "prefix_tokens": wl.n_prefix, "batch": wl.batch,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "keep_tiles": wl.keep_tiles,
+                   "tile": "dynamic" if wl.dynamic else "x".join(map(str, wl.tile)),
+                   "effective_tflop_per_call": F / 1e12},
+        "roofline": {"bound": "mfma", "kernel": "sparse_fwd_kernel<128>" if wl.head_dim == 128 else
+                     "sparse_fwd_kernel<64>", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "skipped_tile_ratio": 1.0 - wl.keep_tiles / wl.n_video_tiles,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_tiles)
+        print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,18 @@
+"""Block-sparse self-attention for video DiTs on AMD Instinct MI355X (gfx950).
+
+Tokens of a T x H x W latent grid are grouped into 64-token tiles (static
+4x4x4 or dynamic per-region shapes); every query tile keeps the top-k key tiles
+by pooled score and attends exactly to them (plus an optional dense prefix).
+All of it runs in the hand-written HIP kernels of ``libbsa.so`` behind the C
+ABI in ``include/bsa.h``; this package is the thin Python binding.
+"""
+from ._lib import (EXPORTS, LIB_PATH, MAX_VIDEO_TILES, PERM_BUILD, PERM_GATHER, PERM_GATHER_VT, PERM_SCATTER,
+                   TILE_DYNAMIC, TILE_STATIC, BsaError, Desc, lib)
+from .api import (BlockSparseAttention, forward, gather, gather_vt, make_desc, permute_build, plan, pooled_views,
+                  scatter, workspace_size)
+
+lib()  # fail at import if the HIP library was not built
+
+__all__ = ["BlockSparseAttention", "BsaError", "Desc", "EXPORTS", "LIB_PATH", "MAX_VIDEO_TILES", "forward",
+           "gather", "gather_vt", "make_desc", "permute_build", "plan", "pooled_views", "scatter", "workspace_size",
+           "PERM_BUILD", "PERM_GATHER", "PERM_GATHER_VT", "PERM_SCATTER", "TILE_STATIC", "TILE_DYNAMIC"]

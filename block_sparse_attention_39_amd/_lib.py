@@ -1,0 +1,62 @@
+"""ctypes loader for libbsa.so and the mirror of ``bsa_desc`` (include/bsa.h).
+
+The library is built in-tree by ``python -m block_sparse_attention_39_amd.build``;
+importing this module without it raises at once: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
+
+BSA_OK = 0
+STATUS_NAMES = {0: "BSA_OK", -1: "BSA_ERR_NULL", -2: "BSA_ERR_SHAPE", -3: "BSA_ERR_UNSUPPORTED",
+                -4: "BSA_ERR_ALIGN", -5: "BSA_ERR_WORKSPACE", -6: "BSA_ERR_LAUNCH", -7: "BSA_ERR_ARG"}
+TILE_STATIC, TILE_DYNAMIC = 0, 1
+PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_VT = 0, 1, 2, 3
+MAX_VIDEO_TILES = 8192
+# the exported entry points, in the order include/bsa.h declares them
+EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_status_string", "bsa_version")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("grid_t", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("n_prefix", ctypes.c_int32), ("tile_mode", ctypes.c_int32), ("tile_t", ctypes.c_int32),
+                ("tile_h", ctypes.c_int32), ("tile_w", ctypes.c_int32), ("keep_tiles", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dyn_tau", ctypes.c_float)]
+
+    def __repr__(self):
+        return "Desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().bsa_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_sparse_attention_39_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, D = ctypes.c_void_p, ctypes.POINTER(Desc)
+        L.bsa_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        L.bsa_permute.argtypes = [D, ctypes.c_int, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.bsa_plan.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
+        L.bsa_forward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.bsa_status_string.argtypes = [ctypes.c_int]
+        L.bsa_status_string.restype = ctypes.c_char_p
+        L.bsa_version.argtypes = []
+        for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib

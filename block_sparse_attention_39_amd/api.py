@@ -1,0 +1,160 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Tensors are torch tensors on the GPU (torch provides device memory and the
+stream); every function passes raw device pointers to libbsa.so and raises
+``BsaError`` on a non-zero status.  All compute runs in the library's HIP
+kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_VT, PERM_SCATTER, TILE_DYNAMIC, TILE_STATIC, BsaError,
+                   Desc, lib)
+
+
+def make_desc(batch: int, heads: int, head_dim: int, grid, keep_tiles: int, *, scale: float | None = None,
+              n_prefix: int = 0, dynamic: bool = False, tile=(4, 4, 4), tau: float = 0.10) -> Desc:
+    T, H, W = grid
+    return Desc(batch, heads, head_dim, T, H, W, n_prefix, TILE_DYNAMIC if dynamic else TILE_STATIC,
+                tile[0], tile[1], tile[2], keep_tiles,
+                1.0 / math.sqrt(head_dim) if scale is None else scale, tau)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory (libbsa has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise BsaError(status, where)
+
+
+def workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "bsa_workspace_size")
+    return n.value
+
+
+def permute_build(desc: Desc, perm, shape_map=None, q_raster=None, workspace=None, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_BUILD, _ptr(q_raster), _ptr(perm), _ptr(shape_map), None, None,
+                             _ptr(workspace), ws, _stream(stream)), "bsa_permute(BUILD)")
+
+
+def gather(desc: Desc, src, dst, perm, stream=None):
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER, None, _ptr(perm), None, _ptr(src), _ptr(dst), None, 0,
+                             _stream(stream)), "bsa_permute(GATHER)")
+
+
+def gather_vt(desc: Desc, src, dst, perm, stream=None):
+    """Raster V -> tiled order transposed inside every 64-token tile ([B, H, Ntot/64, D, 64])."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER_VT, None, _ptr(perm), None, _ptr(src), _ptr(dst), None,
+                             0, _stream(stream)), "bsa_permute(GATHER_VT)")
+
+
+def scatter(desc: Desc, src, dst, perm, stream=None):
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_SCATTER, None, _ptr(perm), None, _ptr(src), _ptr(dst), None, 0,
+                             _stream(stream)), "bsa_permute(SCATTER)")
+
+
+def plan(desc: Desc, q_tiled, k_tiled, block_idx, workspace, stream=None):
+    ws = workspace.numel() * workspace.element_size()
+    _check(lib().bsa_plan(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_tiled), _ptr(block_idx), _ptr(workspace), ws,
+                          _stream(stream)), "bsa_plan")
+
+
+def forward(desc: Desc, q_tiled, k_tiled, vt_tiled, block_idx, o_tiled, lse=None, workspace=None, stream=None):
+    """``vt_tiled`` is V in the per-tile transposed layout written by gather_vt.
+    With ``workspace`` the video query tiles run as the grouped persistent grid."""
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bsa_forward(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_tiled), _ptr(vt_tiled), _ptr(block_idx),
+                             _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws, _stream(stream)), "bsa_forward")
+
+
+def pooled_views(desc: Desc, workspace):
+    """(qbar, kbar) float views of the workspace after bsa_plan ([B, H, nVT, D])."""
+    B, H, D = desc.batch, desc.heads, desc.head_dim
+    nvt = desc.grid_t * desc.grid_h * desc.grid_w // 64
+    n = B * H * nvt * D
+    pooled_bytes = (n * 4 + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    q = f[:n * 4].view(torch.float32).view(B, H, nvt, D)
+    k = f[pooled_bytes:pooled_bytes + n * 4].view(torch.float32).view(B, H, nvt, D)
+    return q, k
+
+
+class BlockSparseAttention:
+    """Owns the device buffers of one problem size and runs the whole path:
+    permutation (build, gather Q/K/V), plan, forward and the output scatter.
+
+    ``__call__(q, k, v)`` takes raster bf16 tensors ``[B, Ntot, H, D]`` on the
+    GPU and returns the raster output.  Buffers are allocated once, through
+    torch, in the constructor."""
+
+    def __init__(self, desc: Desc, device="cuda", with_lse: bool = False, grouped: bool = True):
+        self.desc = desc
+        B, H, D = desc.batch, desc.heads, desc.head_dim
+        self.n_video = desc.grid_t * desc.grid_h * desc.grid_w
+        self.n_tot = desc.n_prefix + self.n_video
+        self.nvt = self.n_video // 64
+        self.dynamic = desc.tile_mode == TILE_DYNAMIC
+        bf = torch.bfloat16
+        self.perm = torch.empty((B, max(self.n_video, 1)), dtype=torch.int32, device=device)
+        regions = (desc.grid_t // 8) * (desc.grid_h // 8) * (desc.grid_w // 8)
+        self.shape_map = torch.empty((B, max(regions, 1)), dtype=torch.uint8, device=device) if self.dynamic else None
+        self.q_t, self.k_t, self.o_t = (torch.empty((B, H, self.n_tot, D), dtype=bf, device=device)
+                                        for _ in range(3))
+        self.vt_t = torch.empty((B, H, self.n_tot // 64, D, 64), dtype=bf, device=device)
+        self.block_idx = torch.empty((B, H, max(self.nvt, 1), max(desc.keep_tiles, 1)), dtype=torch.int32,
+                                     device=device)
+        self.workspace = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device)
+        self.lse = torch.empty((B, H, self.n_tot), dtype=torch.float32, device=device) if with_lse else None
+        self.grouped = grouped
+
+    def build(self, q, stream=None):
+        permute_build(self.desc, self.perm, self.shape_map, q if self.dynamic else None, self.workspace, stream)
+
+    def gather_qkv(self, q, k, v, stream=None):
+        gather(self.desc, q, self.q_t, self.perm, stream)
+        gather(self.desc, k, self.k_t, self.perm, stream)
+        gather_vt(self.desc, v, self.vt_t, self.perm, stream)
+
+    def plan(self, stream=None):
+        plan(self.desc, self.q_t, self.k_t, self.block_idx, self.workspace, stream)
+
+    def forward(self, stream=None):
+        forward(self.desc, self.q_t, self.k_t, self.vt_t, self.block_idx, self.o_t, self.lse,
+                self.workspace if self.grouped else None, stream)
+
+    def scatter_out(self, out, stream=None):
+        scatter(self.desc, self.o_t, out, self.perm, stream)
+
+    def __call__(self, q, k, v, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        self.build(q, stream)
+        self.gather_qkv(q, k, v, stream)
+        self.plan(stream)
+        self.forward(stream)
+        self.scatter_out(out, stream)
+        return out

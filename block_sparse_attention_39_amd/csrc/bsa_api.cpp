@@ -1,0 +1,230 @@
+// The C ABI of libbsa.so (declared in include/bsa.h): host-side validation of
+// every argument, workspace layout, and the kernel launches in order.
+// Validation runs entirely on the host and returns before any HIP call, so a
+// rejected call enqueues nothing.
+#include "bsa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "bsa_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kScoreChunkBytes = size_t(1) << 30;  // cap on the score buffer
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Geo {
+    int64_t B, H, D, T, Hg, W, npf, n_video, n_tot, nvt, npt, BH, k, regions;
+    bool dynamic;
+    bool empty;
+};
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bsa_status check_desc(const bsa_desc* d, Geo* g) {
+    if (!d) return BSA_ERR_NULL;
+    if (d->batch < 0 || d->heads < 0 || d->grid_t < 0 || d->grid_h < 0 || d->grid_w < 0 || d->n_prefix < 0)
+        return BSA_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return BSA_ERR_UNSUPPORTED;
+    if (d->n_prefix % bsa::kTile) return BSA_ERR_SHAPE;
+    if (!std::isfinite(d->scale) || !(d->scale > 0.f)) return BSA_ERR_ARG;
+    g->B = d->batch;
+    g->H = d->heads;
+    g->D = d->head_dim;
+    g->T = d->grid_t;
+    g->Hg = d->grid_h;
+    g->W = d->grid_w;
+    g->npf = d->n_prefix;
+    g->n_video = g->T * g->Hg * g->W;
+    if (d->tile_mode == BSA_TILE_STATIC) {
+        g->dynamic = false;
+        if (d->tile_t < 1 || d->tile_h < 1 || d->tile_w < 1) return BSA_ERR_SHAPE;
+        if ((int64_t)d->tile_t * d->tile_h * d->tile_w != bsa::kTile) return BSA_ERR_SHAPE;
+        if (g->T % d->tile_t || g->Hg % d->tile_h || g->W % d->tile_w) return BSA_ERR_SHAPE;
+    } else if (d->tile_mode == BSA_TILE_DYNAMIC) {
+        g->dynamic = true;
+        if (g->T % 8 || g->Hg % 8 || g->W % 8) return BSA_ERR_SHAPE;
+        if (!std::isfinite(d->dyn_tau) || d->dyn_tau < 0.f) return BSA_ERR_ARG;
+    } else {
+        return BSA_ERR_ARG;
+    }
+    g->n_tot = g->npf + g->n_video;
+    g->nvt = g->n_video / bsa::kTile;
+    g->npt = g->npf / bsa::kTile;
+    g->BH = g->B * g->H;
+    g->regions = (g->T / 8) * (g->Hg / 8) * (g->W / 8);
+    g->k = d->keep_tiles;
+    if (g->nvt > 0 && (g->k < 1 || g->k > g->nvt)) return BSA_ERR_SHAPE;
+    // index arithmetic limits: block counts and per-tensor element counts
+    if (g->BH * (g->npt + g->nvt) > INT32_MAX) return BSA_ERR_UNSUPPORTED;
+    if (g->n_tot > INT32_MAX / 2) return BSA_ERR_UNSUPPORTED;
+    g->empty = (g->BH == 0 || g->n_tot == 0);
+    return BSA_OK;
+}
+
+struct Layout {
+    size_t qbar, kbar, scores, partial, fwd, total;
+    int64_t chunk_bh;  // (batch, head) pairs scored per pass
+};
+
+Layout layout(const Geo& g) {
+    Layout L{};
+    const size_t pooled = align_up((size_t)g.BH * g.nvt * g.D * sizeof(float));
+    L.qbar = 0;
+    L.kbar = pooled;
+    L.scores = 2 * pooled;
+    const size_t per_bh = (size_t)g.nvt * g.nvt * sizeof(float);
+    int64_t chunk = per_bh ? (int64_t)(kScoreChunkBytes / per_bh) : 1;
+    if (chunk < 1) chunk = 1;
+    if (chunk > g.BH) chunk = g.BH;
+    L.chunk_bh = chunk;
+    const size_t plan_bytes = (g.nvt > 0 && g.BH > 0) ? L.scores + align_up((size_t)chunk * per_bh) : 0;
+    const size_t build_bytes = g.dynamic ? align_up((size_t)g.B * g.regions * g.H * 3 * sizeof(double)) : 0;
+    L.partial = 0;
+    // the forward's block-group progress counters sit after the plan's region,
+    // so the pooled means stay readable after a forward call
+    L.fwd = align_up(plan_bytes);
+    const size_t fwd_end = L.fwd + align_up(bsa::forward_workspace_bytes());
+    L.total = fwd_end > build_bytes ? fwd_end : build_bytes;
+    return L;
+}
+
+bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int bsa_version(void) { return BSA_VERSION; }
+
+const char* bsa_status_string(bsa_status s) {
+    switch (s) {
+        case BSA_OK: return "ok";
+        case BSA_ERR_NULL: return "a required pointer is NULL";
+        case BSA_ERR_SHAPE: return "inconsistent sizes (grid, tile, prefix or keep_tiles)";
+        case BSA_ERR_UNSUPPORTED: return "unsupported size (head_dim must be 64 or 128; too many tiles)";
+        case BSA_ERR_ALIGN: return "a tensor pointer is not suitably aligned";
+        case BSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case BSA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case BSA_ERR_ARG: return "invalid argument (enum value, scale or tau)";
+    }
+    return "unknown status";
+}
+
+bsa_status bsa_workspace_size(const bsa_desc* desc, size_t* bytes) {
+    if (!bytes) return BSA_ERR_NULL;
+    Geo g;
+    const bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    *bytes = layout(g).total;
+    return BSA_OK;
+}
+
+bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32_t* perm, uint8_t* shape_map,
+                       const void* src, void* dst, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (op != BSA_PERM_BUILD && op != BSA_PERM_GATHER && op != BSA_PERM_SCATTER && op != BSA_PERM_GATHER_VT)
+        return BSA_ERR_ARG;
+    if (g.B == 0 || g.n_tot == 0) return BSA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (op == BSA_PERM_BUILD) {
+        if (g.n_video == 0) return BSA_OK;
+        if (!perm) return BSA_ERR_NULL;
+        if (misaligned(perm, 4)) return BSA_ERR_ALIGN;
+        if (!g.dynamic)
+            return launched(bsa::launch_perm_static((int)g.B, (int)g.T, (int)g.Hg, (int)g.W, desc->tile_t,
+                                                    desc->tile_h, desc->tile_w, perm, s));
+        if (g.H == 0) return BSA_ERR_SHAPE;  // the statistic needs at least one head
+        if (!q_raster || !shape_map) return BSA_ERR_NULL;
+        if (misaligned(q_raster, 16)) return BSA_ERR_ALIGN;
+        const Layout L = layout(g);
+        if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+        if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + L.partial);
+        hipError_t e = bsa::launch_shape_stats(static_cast<const uint16_t*>(q_raster), partial, (int)g.B, (int)g.H,
+                                               (int)g.D, (int)g.npf, (int)g.T, (int)g.Hg, (int)g.W, s);
+        if (e == hipSuccess)
+            e = bsa::launch_shape_choose(partial, shape_map, (int)g.B, (int)g.H, (int)g.D, (int)g.T, (int)g.Hg,
+                                         (int)g.W, desc->dyn_tau, s);
+        if (e == hipSuccess) e = bsa::launch_perm_dynamic(shape_map, perm, (int)g.B, (int)g.T, (int)g.Hg, (int)g.W, s);
+        return launched(e);
+    }
+    if (g.H == 0) return BSA_OK;
+    if (!src || !dst || (g.n_video > 0 && !perm)) return BSA_ERR_NULL;
+    if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
+    if (op == BSA_PERM_GATHER_VT)
+        return launched(bsa::launch_gather_vt(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
+                                              (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s));
+    return launched(bsa::launch_permute_copy(op == BSA_PERM_SCATTER, static_cast<const uint16_t*>(src),
+                                             static_cast<uint16_t*>(dst), perm, (int)g.B, (int)g.H, (int)g.D,
+                                             (int)g.npf, g.n_video, s));
+}
+
+bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_tiled, int32_t* block_idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.empty || g.nvt == 0) return BSA_OK;
+    if (!q_tiled || !k_tiled || !block_idx) return BSA_ERR_NULL;
+    if (misaligned(q_tiled, 16) || misaligned(k_tiled, 16) || misaligned(block_idx, 4)) return BSA_ERR_ALIGN;
+    const Layout L = layout(g);
+    if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+    if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    float* qbar = reinterpret_cast<float*>(w + L.qbar);
+    float* kbar = reinterpret_cast<float*>(w + L.kbar);
+    float* scores = reinterpret_cast<float*>(w + L.scores);
+    hipError_t e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+                                    qbar, kbar, (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s);
+    for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
+        const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
+        e = bsa::launch_scores(qbar + b0 * g.nvt * g.D, kbar + b0 * g.nvt * g.D, scores, (int)cnt, (int)g.nvt,
+                               (int)g.D, s);
+        if (e == hipSuccess)
+            e = bsa::launch_topk(scores, block_idx + b0 * g.nvt * g.k, (int)(cnt * g.nvt), (int)g.nvt, (int)g.k, s);
+    }
+    return launched(e);
+}
+
+bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_tiled, const void* vt_tiled,
+                       const int32_t* block_idx, void* o_tiled, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.empty) return BSA_OK;
+    if (!q_tiled || !k_tiled || !vt_tiled || !o_tiled || (g.nvt > 0 && !block_idx)) return BSA_ERR_NULL;
+    if (misaligned(q_tiled, 16) || misaligned(k_tiled, 16) || misaligned(vt_tiled, 16) || misaligned(o_tiled, 16) ||
+        misaligned(block_idx, 4) || misaligned(lse, 4))
+        return BSA_ERR_ALIGN;
+    int* progress = nullptr;
+    if (ws) {
+        const Layout L = layout(g);
+        if (ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+        if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
+    }
+    bsa::ForwardArgs a;
+    a.q = static_cast<const uint16_t*>(q_tiled);
+    a.k = static_cast<const uint16_t*>(k_tiled);
+    a.vt = static_cast<const uint16_t*>(vt_tiled);
+    a.idx = block_idx;
+    a.o = static_cast<uint16_t*>(o_tiled);
+    a.lse = lse;
+    a.BH = (int)g.BH;
+    a.npt = (int)g.npt;
+    a.nvt = (int)g.nvt;
+    a.keep = (int)g.k;
+    a.scale_log2 = desc->scale * 1.4426950408889634f;
+    return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

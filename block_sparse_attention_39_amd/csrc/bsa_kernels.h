@@ -1,0 +1,61 @@
+// Internal launchers of libbsa.so (not part of the C ABI).  Each returns the
+// HIP error of its launch; all sizes were validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace bsa {
+
+constexpr int kTile = 64;  // tokens per tile
+
+// Static tile order: perm[b][p] for all b (the same closed form per batch).
+hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int tw, int32_t* perm,
+                              hipStream_t s);
+
+// Raster [B][Ntot][H][D] <-> tiled [B][H][Ntot][D] through perm (prefix kept in place).
+hipError_t launch_permute_copy(bool to_raster, const uint16_t* src, uint16_t* dst, const int32_t* perm,
+                               int B, int H, int D, int n_prefix, int64_t n_video, hipStream_t s);
+
+// Raster [B][Ntot][H][D] -> per-tile transposed [B][H][Ntot/64][D][64] (the V operand layout).
+hipError_t launch_gather_vt(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
+                            int n_prefix, int64_t n_video, hipStream_t s);
+
+// Dynamic shapes: per-(b, region, head) partial |delta| sums, then shape choice
+// and the permutation.
+hipError_t launch_shape_stats(const uint16_t* q_raster, double* partial, int B, int H, int D, int n_prefix,
+                              int T, int Hg, int W, hipStream_t s);
+hipError_t launch_shape_choose(const double* partial, uint8_t* shape_map, int B, int H, int D, int T, int Hg,
+                               int W, float tau, hipStream_t s);
+hipError_t launch_perm_dynamic(const uint8_t* shape_map, int32_t* perm, int B, int T, int Hg, int W,
+                               hipStream_t s);
+
+// Mean of the 64 tokens of every video tile of Q and K -> float [BH][nvt][D].
+hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_tiled, float* qbar, float* kbar, int BH,
+                       int n_prefix, int nvt, int D, hipStream_t s);
+
+// scores[bh][i][j] = qbar_i . kbar_j (float) for bh in [0, BH).
+hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, int BH, int n, int D,
+                         hipStream_t s);
+
+// Per row: the k largest scores (lower index first on ties), ascending indices.
+hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s);
+
+struct ForwardArgs {
+    const uint16_t* q;       // tiled [BH][Ntot][D]
+    const uint16_t* k;
+    const uint16_t* vt;      // per-tile transposed [BH][Ntot/64][D][64]
+    const int32_t* idx;      // [BH][nvt][keep]
+    uint16_t* o;             // tiled [BH][Ntot][D]
+    float* lse;              // [BH][Ntot] or null
+    int BH;
+    int npt;                 // prefix tiles
+    int nvt;                 // video tiles
+    int keep;                // kept video tiles per video query tile
+    float scale_log2;        // scale * log2(e)
+};
+// progress: forward_workspace_bytes() of device memory for the grouped launch
+// of the video query tiles, or null for one block per query tile.
+size_t forward_workspace_bytes();
+hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s);
+
+}  // namespace bsa

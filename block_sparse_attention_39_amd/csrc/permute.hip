@@ -1,0 +1,162 @@
+// Token permutation between raster order and tile order.
+//
+// Tokens are regrouped so that every 64-token tile is contiguous per head
+// ("Sparse VideoGen TPU 최적화 ..." page, section "실무에서 배울 최적화 기준": token
+// permutation makes a sparsity pattern's tiles contiguous, and its cost is
+// measured on its own).  The copy is a pure HBM-bound gather: each block moves
+// one tile of 64 tokens for every head, reading 256-byte head rows of the
+// raster layout and writing 16 KB contiguous runs per head in the tiled layout.
+#include "bsa_kernels.h"
+
+namespace bsa {
+namespace {
+
+// Static tile order: tile id = raster index in the tile grid (t slowest),
+// tokens raster inside the tile ("Prism / Kandinsky 6 speed ablation" page,
+// section on Prism: the default 64-token tile is 4x4x4).
+__global__ void perm_static_kernel(int T, int Hg, int W, int tt, int th, int tw, int64_t n_video, int B,
+                                   int32_t* __restrict__ perm) {
+    const int64_t total = n_video * B;
+    const int nbh = Hg / th, nbw = W / tw;
+    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+         g += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = g % n_video;
+        const int64_t tile = p / kTile;
+        const int r = (int)(p % kTile);
+        const int64_t a = tile / ((int64_t)nbh * nbw);
+        const int bb = (int)((tile / nbw) % nbh);
+        const int cc = (int)(tile % nbw);
+        const int x = r / (th * tw), y = (r / tw) % th, z = r % tw;
+        const int64_t t = a * tt + x;
+        const int h = bb * th + y, w = cc * tw + z;
+        perm[g] = (int32_t)((t * Hg + h) * W + w);
+    }
+}
+
+// One block per (batch, 64-token tile of the tiled order); 256 threads.
+// Work item = (head, token in tile, 16-byte chunk), chunk fastest, so a wave
+// writes (gather) or reads (scatter) contiguous 256-byte head rows of the
+// tiled tensor and touches 256-byte head rows of the raster tensor.
+template <bool kToRaster>
+__global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           const int32_t* __restrict__ perm, int H, int C,
+                                                           int n_prefix, int64_t n_video, int64_t n_tot) {
+    __shared__ int64_t tok[kTile];
+    const int b = blockIdx.y;
+    const int64_t p0 = (int64_t)blockIdx.x * kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t p = p0 + threadIdx.x;
+        tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
+    }
+    __syncthreads();
+    const int items = kTile * H * C;
+#pragma unroll 4
+    for (int it = threadIdx.x; it < items; it += 256) {
+        const int c = it % C;
+        const int pl = (it / C) % kTile;
+        const int h = it / (C * kTile);
+        const int64_t tiled = (((int64_t)b * H + h) * n_tot + p0 + pl) * C + c;
+        const int64_t raster = (((int64_t)b * n_tot + tok[pl]) * H + h) * C + c;
+        if (kToRaster)
+            dst[raster] = src[tiled];
+        else
+            dst[tiled] = src[raster];
+    }
+}
+
+// Raster V -> per-tile transposed layout [B][H][tile][D][64]: the 64 tokens of
+// a tile become the contiguous dimension, which is the operand layout of the
+// P V product in the attention kernel.  One block per (batch, tile); work item
+// = (head, group of 8 tokens, 8-channel chunk), chunk fastest: a thread reads
+// 8 token rows of 16 bytes (256-byte head rows across a wave), transposes the
+// 8 x 8 block of bf16 values in registers and writes 8 channel rows of 16
+// bytes (8 consecutive tokens each).
+__device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ inline uint32_t word_of(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
+
+__global__ __launch_bounds__(256) void gather_vt_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        const int32_t* __restrict__ perm, int H, int C,
+                                                        int n_prefix, int64_t n_video, int64_t n_tot) {
+    __shared__ int64_t tok[kTile];
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    const int64_t p0 = tile * kTile;
+    const int64_t n_tiles = n_tot / kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t p = p0 + threadIdx.x;
+        tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
+    }
+    __syncthreads();
+    const int D = C * 8;
+    const int items = H * 8 * C;
+    for (int it = threadIdx.x; it < items; it += 256) {
+        const int dc = it % C;
+        const int g = (it / C) % 8;
+        const int h = it / (8 * C);
+        uint4 r0, r1, r2, r3, r4, r5, r6, r7;
+        auto row = [&](int i) { return src[(((int64_t)b * n_tot + tok[8 * g + i]) * H + h) * C + dc]; };
+        r0 = row(0); r1 = row(1); r2 = row(2); r3 = row(3);
+        r4 = row(4); r5 = row(5); r6 = row(6); r7 = row(7);
+        // out[e] holds channel 8*dc + e of tokens 8*g .. 8*g + 7
+        uint4* out = dst + ((((int64_t)b * H + h) * n_tiles + tile) * D + 8 * dc) * (kTile / 8) + g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1;
+            uint4 o;
+            if (e & 1) {
+                o.x = hi_pair(word_of(r0, w), word_of(r1, w));
+                o.y = hi_pair(word_of(r2, w), word_of(r3, w));
+                o.z = hi_pair(word_of(r4, w), word_of(r5, w));
+                o.w = hi_pair(word_of(r6, w), word_of(r7, w));
+            } else {
+                o.x = lo_pair(word_of(r0, w), word_of(r1, w));
+                o.y = lo_pair(word_of(r2, w), word_of(r3, w));
+                o.z = lo_pair(word_of(r4, w), word_of(r5, w));
+                o.w = lo_pair(word_of(r6, w), word_of(r7, w));
+            }
+            out[e * (kTile / 8)] = o;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather_vt(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
+                            int n_prefix, int64_t n_video, hipStream_t s) {
+    const int64_t n_tot = n_prefix + n_video;
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_vt_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
+                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int tw, int32_t* perm,
+                              hipStream_t s) {
+    const int64_t n_video = (int64_t)T * Hg * W;
+    const int64_t total = n_video * B;
+    if (total == 0) return hipSuccess;
+    const int threads = 256;
+    const int64_t want = (total + threads - 1) / threads;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(perm_static_kernel, dim3(blocks), dim3(threads), 0, s, T, Hg, W, tt, th, tw, n_video, B,
+                       perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_copy(bool to_raster, const uint16_t* src, uint16_t* dst, const int32_t* perm, int B,
+                               int H, int D, int n_prefix, int64_t n_video, hipStream_t s) {
+    const int64_t n_tot = n_prefix + n_video;
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    const int C = D / 8;
+    if (to_raster)
+        hipLaunchKernelGGL(permute_copy_kernel<true>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm,
+                           H, C, n_prefix, n_video, n_tot);
+    else
+        hipLaunchKernelGGL(permute_copy_kernel<false>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm,
+                           H, C, n_prefix, n_video, n_tot);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,242 @@
+// Tile selection: pooling, pooled scores and per-row top-k.
+//
+// "Prism / Kandinsky 6 speed ablation" page, section "같은 계산량 안에서 볼 곳을
+// 고르는 Prism": a tile's relevance is judged from the mean of its 64 tokens, and
+// each query tile keeps the (1 - sparsity) best key tiles.  The score is the dot
+// product of the pooled query and key vectors; equal scores go to the lower key
+// tile number; kept lists are written in ascending order.
+//
+// pool   : HBM-bound read of Q and K once; one wave per tile, 16-byte loads,
+//          double accumulation (exact for bf16 inputs), one rounding to float,
+//          cross-lane reduction with wave shuffles.
+// scores : float GEMM per (batch, head) of the pooled vectors, 64x64 output
+//          blocks through LDS.
+// topk   : one block per row; 8-bit radix select on the order-preserving
+//          integer image of the float scores (4 passes, LDS histogram), then an
+//          index-ordered compaction that takes every score above the threshold
+//          and the lowest-numbered ties.
+#include "bsa_kernels.h"
+
+namespace bsa {
+namespace {
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// ---------------------------------------------------------------- pooling --
+// Block = 4 waves, one tile per wave.  Lane l reads chunk c = l % C of rows
+// r = l / C + i * (64 / C); the wave then folds the 64 / C lanes that share c.
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
+                                                   float* __restrict__ qbar, float* __restrict__ kbar, int BH,
+                                                   int n_prefix, int nvt) {
+    constexpr int C = D / 8;         // 16-byte chunks per row
+    constexpr int RPI = 64 / C;      // rows covered by one wave-wide load
+    constexpr int ITER = kTile / RPI;
+    const int lane = threadIdx.x & 63;
+    const int64_t tiles_per_tensor = (int64_t)BH * nvt;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= 2 * tiles_per_tensor) return;
+    const bool is_k = g >= tiles_per_tensor;
+    const int64_t t = is_k ? g - tiles_per_tensor : g;
+    const int64_t bh = t / nvt, i = t % nvt;
+    const int64_t n_tot = n_prefix + (int64_t)nvt * kTile;
+    const uint4* src = (is_k ? k : q) + ((bh * n_tot + n_prefix + i * kTile) * C);
+    const int c = lane % C, r0 = lane / C;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const uint4 x = src[(r0 + it * RPI) * C + c];
+        acc[0] += (double)bf_lo(x.x);
+        acc[1] += (double)bf_hi(x.x);
+        acc[2] += (double)bf_lo(x.y);
+        acc[3] += (double)bf_hi(x.y);
+        acc[4] += (double)bf_lo(x.z);
+        acc[5] += (double)bf_hi(x.z);
+        acc[6] += (double)bf_lo(x.w);
+        acc[7] += (double)bf_hi(x.w);
+    }
+#pragma unroll
+    for (int o = C; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
+    if (lane < C) {
+        float4 lo, hi;
+        lo.x = (float)(acc[0] * (1.0 / kTile));
+        lo.y = (float)(acc[1] * (1.0 / kTile));
+        lo.z = (float)(acc[2] * (1.0 / kTile));
+        lo.w = (float)(acc[3] * (1.0 / kTile));
+        hi.x = (float)(acc[4] * (1.0 / kTile));
+        hi.y = (float)(acc[5] * (1.0 / kTile));
+        hi.z = (float)(acc[6] * (1.0 / kTile));
+        hi.w = (float)(acc[7] * (1.0 / kTile));
+        float4* dst = (float4*)((is_k ? kbar : qbar) + t * D) + 2 * c;
+        dst[0] = lo;
+        dst[1] = hi;
+    }
+}
+
+// ----------------------------------------------------------------- scores --
+// S[bh][i][j] = sum_d A[bh][i][d] B[bh][j][d], float.  Block = 256 threads,
+// 64x64 output block; thread (ty, tx) computes rows 4ty..4ty+3, cols 4tx..4tx+3.
+// Operands are staged transposed in LDS ([d][row]) in slabs of 32 channels.
+__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ A, const float* __restrict__ Bm,
+                                                     float* __restrict__ S, int n, int D) {
+    constexpr int KS = 32;
+    __shared__ float4 As[KS][16 + 1];
+    __shared__ float4 Bs[KS][16 + 1];
+    const int bh = blockIdx.z;
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const float* Ab = A + (int64_t)bh * n * D;
+    const float* Bb = Bm + (int64_t)bh * n * D;
+    float acc[4][4] = {};
+    for (int d0 = 0; d0 < D; d0 += KS) {
+        // load 64 rows x 32 channels of A and B: 2048 floats each, 8 per thread
+        for (int e = threadIdx.x; e < 64 * KS; e += 256) {
+            const int row = e / KS, dd = e % KS;
+            const float a = (i0 + row < n) ? Ab[(int64_t)(i0 + row) * D + d0 + dd] : 0.f;
+            const float b = (j0 + row < n) ? Bb[(int64_t)(j0 + row) * D + d0 + dd] : 0.f;
+            reinterpret_cast<float*>(&As[dd][row >> 2])[row & 3] = a;
+            reinterpret_cast<float*>(&Bs[dd][row >> 2])[row & 3] = b;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int dd = 0; dd < KS; ++dd) {
+            const float4 a = As[dd][ty];
+            const float4 b = Bs[dd][tx];
+            const float av[4] = {a.x, a.y, a.z, a.w};
+            const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+        }
+        __syncthreads();
+    }
+    float* Sb = S + (int64_t)bh * n * n;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 4 * ty + u;
+        if (i >= n) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int j = j0 + 4 * tx + v;
+            if (j < n) Sb[(int64_t)i * n + j] = acc[u][v];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ top-k --
+// Order-preserving unsigned image of a float (larger float -> larger key);
+// -0 is folded onto +0 so that equal scores give equal keys.
+__device__ inline uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive scan over a block of 256 threads (4 waves); returns the inclusive
+// prefix and writes the block total to *total.
+__device__ inline int block_scan_256(int x, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    return v + before;
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, int32_t* __restrict__ idx, int n,
+                                                   int k) {
+    extern __shared__ uint32_t keys[];  // [n]
+    __shared__ int hist[256];
+    __shared__ int wsum[4];
+    __shared__ int sel_digit, sel_above;
+    const int64_t row = blockIdx.x;
+    const float* s = S + row * n;
+    for (int j = threadIdx.x; j < n; j += 256) keys[j] = order_key(s[j]);
+    uint32_t prefix = 0, mask = 0;
+    int need = k;  // how many of the keys matching `prefix` are still to take
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[threadIdx.x] = 0;
+        __syncthreads();
+        for (int j = threadIdx.x; j < n; j += 256) {
+            const uint32_t key = keys[j];
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
+        __syncthreads();
+        // counts from the top digit down: thread t holds digit 255 - t
+        const int cnt = hist[255 - threadIdx.x];
+        int tot;
+        const int incl = block_scan_256(cnt, wsum, &tot);
+        const int excl = incl - cnt;
+        if (excl < need && incl >= need) {
+            sel_digit = 255 - threadIdx.x;
+            sel_above = excl;
+        }
+        __syncthreads();
+        need -= sel_above;
+        prefix |= (uint32_t)sel_digit << shift;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    // prefix is now the key of the k-th largest score; `need` of the keys equal
+    // to it are taken, lowest index first.
+    const uint32_t thr = prefix;
+    int32_t* out = idx + row * k;
+    int taken = 0, ties = 0;
+    for (int j0 = 0; j0 < n; j0 += 256) {
+        const int j = j0 + threadIdx.x;
+        const uint32_t key = (j < n) ? keys[j] : 0u;
+        const int is_tie = (j < n && key == thr) ? 1 : 0;
+        int tie_tot;
+        const int tie_rank = block_scan_256(is_tie, wsum, &tie_tot) - is_tie + ties;
+        const int sel = (j < n) && (key > thr || (is_tie && tie_rank < need));
+        int sel_tot;
+        const int pos = block_scan_256(sel, wsum, &sel_tot) - sel + taken;
+        if (sel) out[pos] = j;
+        taken += sel_tot;
+        ties += tie_tot;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_tiled, float* qbar, float* kbar, int BH,
+                       int n_prefix, int nvt, int D, hipStream_t s) {
+    const int64_t tiles = 2LL * BH * nvt;
+    if (tiles == 0) return hipSuccess;
+    const dim3 grid((unsigned)((tiles + 3) / 4));
+    if (D == 128)
+        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_tiled,
+                           qbar, kbar, BH, n_prefix, nvt);
+    else
+        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_tiled,
+                           qbar, kbar, BH, n_prefix, nvt);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, int BH, int n, int D,
+                         hipStream_t s) {
+    if (BH == 0 || n == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64), (unsigned)BH);
+    hipLaunchKernelGGL(scores_kernel, grid, dim3(256), 0, s, qbar, kbar, scores, n, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), (size_t)n * sizeof(uint32_t), s, scores, idx,
+                       n, k);
+    return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,174 @@
+/*
+ * bsa.h -- C ABI of libbsa.so: block-sparse self-attention over a video token
+ * grid, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources by page title and section):
+ *   "Prism / Kandinsky 6 speed ablation" (oh-my-gpu.com), section
+ *   "같은 계산량 안에서 볼 곳을 고르는 Prism" (Prism picks where to look within the
+ *   same compute): tokens of the T x H x W latent grid are grouped into 64-token
+ *   tiles (4x4x4 by default, or a per-8x8x8-region shape chosen from how fast
+ *   each axis varies); every query tile keeps only its most relevant key tiles,
+ *   relevance being judged from the mean of each tile's 64 tokens; sparsity s
+ *   keeps (1-s) of the key tiles (s = 0.75 keeps 480 of 1,920).
+ *   "Sparse VideoGen TPU 최적화: 비디오 생성 추론 지연을 줄이는 실무 기준"
+ *   (aibase.it), section "이론적 sparsity와 물리적 sparsity의 차이": skipped tiles
+ *   cost nothing and kept tiles are computed whole, with no per-element mask;
+ *   section "실무에서 배울 최적화 기준": tokens are first permuted so that each
+ *   tile is contiguous.
+ *   "RTX 4090에서 5초 영상 72초: Ref2VA VSA" (pulmap.app), section
+ *   "조건 토큰은 왜 다르게 다루나": a conditioning prefix of segment-pure tiles is
+ *   attended densely and never pruned; top-k applies to video key tiles only.
+ *
+ * A call sequence:  bsa_permute(BUILD) -> bsa_permute(GATHER) for Q and K,
+ * bsa_permute(GATHER_VT) for V -> bsa_plan -> bsa_forward ->
+ * bsa_permute(SCATTER) for O.
+ *
+ * Layouts (row-major, bf16 = IEEE bfloat16):
+ *   raster  bf16 [B][Ntot][H][D]   the dense prefix first (n_prefix tokens, already
+ *                                   in 64-token segment-pure tiles), then the video
+ *                                   grid in (t, h, w) raster order, t slowest.
+ *   tiled   bf16 [B][H][Ntot][D]   prefix unchanged, then the video tokens in tile
+ *                                   order: tile 0's 64 tokens, tile 1's, ...; inside
+ *                                   a tile, tokens in (t, h, w) raster order.
+ *   tiled_t bf16 [B][H][Ntot/64][D][64]  the tiled order, transposed inside each
+ *                                   64-token tile: channel-major, the tile's 64
+ *                                   tokens contiguous (the V operand of bsa_forward).
+ *   perm    int32 [B][Nvideo]      tiled video slot -> raster video token index
+ *                                   (0-based, not counting the prefix).
+ *   block_idx int32 [B][H][nVT][k] per video query tile, the k kept video key tiles
+ *                                   (video tile numbers 0..nVT-1), ascending.
+ * Ntot = n_prefix + Nvideo, Nvideo = grid_t*grid_h*grid_w, nVT = Nvideo/64.
+ *
+ * Ownership and threading: the caller allocates every buffer (device memory),
+ * including the workspace.  The library allocates nothing, frees nothing,
+ * never synchronises and keeps no state: calls are reentrant.  All work is
+ * enqueued on `stream` (a hipStream_t; NULL means the default stream).  Inputs
+ * are only read; outputs are entirely overwritten.
+ *
+ * Errors: every precondition is checked on the host before anything is
+ * enqueued; a failed check returns a negative bsa_status and enqueues nothing.
+ * A launch failure reported by the HIP runtime returns BSA_ERR_LAUNCH.  Faults
+ * inside kernels surface at the caller's next synchronisation.  Nothing throws.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSA_OK = 0,
+    BSA_ERR_NULL = -1,        /* a required pointer is NULL */
+    BSA_ERR_SHAPE = -2,       /* sizes inconsistent: grid not divisible, bad prefix, k out of range */
+    BSA_ERR_UNSUPPORTED = -3, /* valid but not implemented: head_dim not 64/128, too many tiles */
+    BSA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+    BSA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than bsa_workspace_size() */
+    BSA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch */
+    BSA_ERR_ARG = -7          /* bad enum value or non-finite / non-positive scale */
+} bsa_status;
+
+enum { BSA_TILE_STATIC = 0, BSA_TILE_DYNAMIC = 1 };
+enum { BSA_PERM_BUILD = 0, BSA_PERM_GATHER = 1, BSA_PERM_SCATTER = 2, BSA_PERM_GATHER_VT = 3 };
+
+/* Largest number of video tiles per (batch, head) that bsa_plan accepts. */
+#define BSA_MAX_VIDEO_TILES 8192
+
+typedef struct bsa_desc {
+    int32_t batch;      /* B >= 0 (0: every call is a no-op returning BSA_OK)         */
+    int32_t heads;      /* H >= 0 (0: no-op)                                           */
+    int32_t head_dim;   /* D, 64 or 128                                                */
+    int32_t grid_t;     /* video grid T x H x W, each >= 0; T*H*W a multiple of 64     */
+    int32_t grid_h;
+    int32_t grid_w;
+    int32_t n_prefix;   /* dense prefix tokens, a multiple of 64, >= 0                 */
+    int32_t tile_mode;  /* BSA_TILE_STATIC or BSA_TILE_DYNAMIC                         */
+    int32_t tile_t;     /* static tile extents; product 64; must divide the grid       */
+    int32_t tile_h;     /*   (ignored in dynamic mode, where the grid must be a        */
+    int32_t tile_w;     /*    multiple of 8 on every axis)                             */
+    int32_t keep_tiles; /* k: kept video key tiles per video query tile, 1..nVT        */
+                        /*   (0 when there is no video)                                */
+    float scale;        /* softmax scale applied to q.k, finite and > 0 (1/sqrt(D))    */
+    float dyn_tau;      /* dynamic shapes: isotropy margin tau >= 0 (0.10 typical)     */
+} bsa_desc;
+
+/*
+ * Bytes of device workspace that bsa_plan, bsa_forward and
+ * bsa_permute(BUILD, dynamic) need for `desc`; one buffer of this size serves
+ * all three on one stream.  Host-only; enqueues nothing.  After bsa_plan's
+ * work has run, the workspace starts with the pooled tile means
+ *   float qbar[B][H][nVT][D], then float kbar[B][H][nVT][D]
+ * (each the mean of the tile's 64 tokens), each region 256-byte aligned;
+ * bsa_forward does not overwrite them.
+ */
+bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
+
+/*
+ * Token permutation between raster and tiled order.
+ *  op = BSA_PERM_BUILD: write `perm` [B][Nvideo].  Static mode: the closed-form
+ *       tile order (tiles in raster order of the tile grid).  Dynamic mode: read
+ *       `q_raster` (bf16 raster, the queries), for every batch element and 8x8x8
+ *       region compute the mean |difference| of adjacent tokens along t, h and w
+ *       over all heads and channels, choose one of the nine 64-token shapes
+ *       (id: 0 4x4x4, 1 2x4x8, 2 2x8x4, 3 8x4x2, 4 4x2x8, 5 4x8x2, 6 8x2x4,
+ *       7 2x2x16, 8 16x2x2; extents t x h x w) and write it to `shape_map`
+ *       [B][R] (R = regions, raster order), then the permutation: regions in
+ *       raster order, 8 tiles per region in raster order inside the region; a
+ *       pair of regions sharing a 16-long shape lays its 16 tiles over the two
+ *       regions' tile slots.  Uses the workspace; `src`/`dst` unused.
+ *  op = BSA_PERM_GATHER: `src` raster -> `dst` tiled (Q, K or V).
+ *  op = BSA_PERM_SCATTER: `src` tiled -> `dst` raster (the output).
+ *  op = BSA_PERM_GATHER_VT: `src` raster -> `dst` tiled_t (V).
+ * Gather and scatter read `perm` and copy bf16 values exactly; the prefix
+ * tokens keep their positions.  Source and destination must not overlap.
+ */
+bsa_status bsa_permute(const bsa_desc *desc, int op, const void *q_raster, int32_t *perm,
+                       uint8_t *shape_map, const void *src, void *dst, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/*
+ * Tile selection.  From the tiled Q and K (bf16): the mean of each video
+ * tile's 64 tokens (summed exactly, rounded once to float), the score
+ * s_ij = sum_d qbar_i[d] kbar_j[d] (float), and per (b, h, video query tile i)
+ * the keep_tiles video key tiles with the largest s_ij, equal scores going to
+ * the lower tile number, written ascending to `block_idx`.  Prefix tiles are
+ * never scored (they are always attended).  Uses the workspace.
+ */
+bsa_status bsa_plan(const bsa_desc *desc, const void *q_tiled, const void *k_tiled,
+                    int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Attention over the kept tiles.  `q_tiled`, `k_tiled` and `o_tiled` are in the
+ * tiled layout, `vt_tiled` in the tiled_t layout.  For each query token of video tile i the
+ * keys are the prefix tokens and the tokens of the tiles block_idx[b][h][i][:];
+ * prefix query tokens attend to every token.  o = softmax(scale * q K^T) V with
+ * bf16 products accumulated in float, a float online softmax, and o rounded to
+ * bf16 (`o_tiled`, tiled layout).  `lse` (optional, NULL to skip) receives
+ * float [B][H][Ntot]: the natural log of sum_j exp(scale * q.k_j) per query.
+ * `block_idx` may be NULL only when there is no video.
+ * `ws` (optional): a workspace of bsa_workspace_size() bytes, 256-byte aligned.
+ * With it, the video query tiles run as a persistent grid whose blocks, per
+ * XCD, sweep the key tiles in step so that a key tile is fetched once into the
+ * XCD's L2 for all of them; without it (NULL), one block per query tile.  The
+ * results are the same either way.  Calls given the same workspace must not
+ * run concurrently.
+ */
+bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_tiled,
+                       const void *vt_tiled, const int32_t *block_idx, void *o_tiled, float *lse,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *bsa_status_string(bsa_status status);
+
+/* ABI version of this header (major * 100 + minor). */
+int bsa_version(void);
+
+#define BSA_VERSION 300
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

@@ -1,0 +1,174 @@
+"""The C ABI on the host: the library loads, exports what include/bsa.h
+declares, sizes its workspace, and rejects every bad argument before touching
+the GPU (these calls return before any HIP call, so they run without one)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_39_amd as bsa
+from block_sparse_attention_39_amd._lib import Desc, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = open(os.path.join(ROOT, "include", "bsa.h")).read()
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, ARG = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 1 << 20  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    return sorted(set(re.findall(r"^\s*(?:bsa_status|const char \*|int)\s*\**\s*(bsa_\w+)\s*\(", HEADER, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == sorted(bsa.EXPORTS)
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    m = re.search(r"#define BSA_VERSION (\d+)", HEADER)
+    assert lib().bsa_version() == int(m.group(1))
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, ARG):
+        assert lib().bsa_status_string(code)
+    assert lib().bsa_status_string(123) == b"unknown status"
+
+
+def test_header_limits_match_binding():
+    m = re.search(r"#define BSA_MAX_VIDEO_TILES (\d+)", HEADER)
+    assert int(m.group(1)) == bsa.MAX_VIDEO_TILES
+
+
+def cfg(**kw):
+    base = dict(batch=2, heads=3, head_dim=128, grid=(8, 8, 12), keep_tiles=5)
+    base.update(kw)
+    grid = base.pop("grid")
+    return bsa.make_desc(base.pop("batch"), base.pop("heads"), base.pop("head_dim"), grid, base.pop("keep_tiles"),
+                         **base)
+
+
+def ws_size(d):
+    n = ctypes.c_size_t(0)
+    st = lib().bsa_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_formula():
+    d = bsa.make_desc(2, 24, 128, (32, 48, 80), 480)
+    st, n = ws_size(d)
+    assert st == OK
+    pooled = 2 * 24 * 1920 * 128 * 4
+    fwd = 8 * 64 * 4   # block-group progress counters of the forward
+    assert n == 2 * pooled + 48 * 1920 * 1920 * 4 + fwd
+    # dynamic mode also covers the per-(batch, region, head) statistic
+    dd = bsa.make_desc(2, 24, 128, (32, 48, 80), 480, dynamic=True)
+    assert ws_size(dd)[1] >= 2 * 240 * 24 * 3 * 8
+    # no video: nothing to plan, only the forward's counters
+    assert ws_size(bsa.make_desc(1, 2, 64, (0, 0, 0), 0, n_prefix=128)) == (OK, fwd)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(head_dim=96), UNSUP),
+    (dict(head_dim=32), UNSUP),
+    (dict(grid=(8, 8, 10)), SHAPE),              # not divisible by the 4x4x4 tile
+    (dict(keep_tiles=0), SHAPE),
+    (dict(keep_tiles=13), SHAPE),                # 12 video tiles
+    (dict(n_prefix=100), SHAPE),
+    (dict(tile=(4, 4, 2)), SHAPE),               # 32 tokens
+    (dict(tile=(0, 8, 8)), SHAPE),
+    (dict(scale=float("nan")), ARG),
+    (dict(scale=0.0), ARG),
+    (dict(scale=-1.0), ARG),
+    (dict(batch=-1), SHAPE),
+    (dict(dynamic=True), SHAPE),                 # dynamic grid must be a multiple of 8
+    (dict(dynamic=True, grid=(8, 8, 16), tau=-0.5), ARG),
+])
+def test_descriptor_errors(kw, expect):
+    d = cfg(**kw)
+    assert ws_size(d)[0] == expect
+    L = lib()
+    assert L.bsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == expect
+    assert L.bsa_plan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == expect
+    assert L.bsa_permute(ctypes.byref(d), 1, None, FAKE, None, FAKE, FAKE, None, 0, None) == expect
+
+
+def test_bad_tile_mode_and_op():
+    d = cfg()
+    d.tile_mode = 7
+    assert ws_size(d)[0] == ARG
+    d = cfg()
+    assert lib().bsa_permute(ctypes.byref(d), 9, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
+
+
+def test_null_pointers():
+    L = lib()
+    assert L.bsa_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == NULL
+    d = cfg()
+    assert L.bsa_workspace_size(ctypes.byref(d), None) == NULL
+    assert L.bsa_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == NULL
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        assert L.bsa_forward(ctypes.byref(d), *args, None, None, 0, None) == NULL
+    assert L.bsa_plan(ctypes.byref(d), None, FAKE, FAKE, FAKE, 1 << 40, None) == NULL
+    assert L.bsa_plan(ctypes.byref(d), FAKE, FAKE, None, FAKE, 1 << 40, None) == NULL
+    assert L.bsa_permute(ctypes.byref(d), 0, None, None, None, None, None, None, 0, None) == NULL
+    assert L.bsa_permute(ctypes.byref(d), 1, None, None, None, FAKE, FAKE, None, 0, None) == NULL
+    assert L.bsa_permute(ctypes.byref(d), 2, None, FAKE, None, None, FAKE, None, 0, None) == NULL
+    dd = cfg(dynamic=True, grid=(8, 8, 16))
+    assert L.bsa_permute(ctypes.byref(dd), 0, None, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == NULL
+    assert L.bsa_permute(ctypes.byref(dd), 0, FAKE, FAKE, None, None, None, FAKE, 1 << 40, None) == NULL
+
+
+def test_alignment_and_workspace_errors():
+    L = lib()
+    d = cfg()
+    bad = FAKE + 8
+    assert L.bsa_forward(ctypes.byref(d), bad, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ALIGN
+    assert L.bsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 2, FAKE, None, None, 0, None) == ALIGN
+    assert L.bsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 1, None, 0, None) == ALIGN
+    st, need = ws_size(d)
+    assert L.bsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == WS
+    assert L.bsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, need, None) == ALIGN
+    st, need = ws_size(d)
+    assert L.bsa_plan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert L.bsa_plan(ctypes.byref(d), FAKE, FAKE, FAKE, None, need, None) == WS
+    assert L.bsa_plan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 16, need, None) == ALIGN
+    assert L.bsa_permute(ctypes.byref(d), 1, None, FAKE, None, bad, FAKE, None, 0, None) == ALIGN
+    assert L.bsa_permute(ctypes.byref(d), 0, None, FAKE + 1, None, None, None, None, 0, None) == ALIGN
+
+
+def test_too_many_tiles_for_plan():
+    # 8,320 tiles > the plan limit; permute and forward accept it
+    d = bsa.make_desc(1, 1, 64, (16, 128, 260), 10)
+    assert lib().bsa_plan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUP
+
+
+def test_empty_problems_are_no_ops():
+    L = lib()
+    for d in (cfg(batch=0), cfg(heads=0), bsa.make_desc(1, 2, 64, (0, 0, 0), 0)):
+        # nothing to do: success without touching any pointer or the GPU
+        assert L.bsa_forward(ctypes.byref(d), None, None, None, None, None, None, None, 0, None) == OK
+        assert L.bsa_plan(ctypes.byref(d), None, None, None, None, 0, None) == OK
+        assert L.bsa_permute(ctypes.byref(d), 1, None, None, None, None, None, None, 0, None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = cfg()
+    x = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsa.forward(d, x, x, x, x.view(torch.int32), x)
+
+
+def test_desc_layout_matches_header():
+    # field order and size of bsa_desc
+    fields = re.search(r"typedef struct bsa_desc \{(.*?)\} bsa_desc;", HEADER, re.S).group(1)
+    names = re.findall(r"(?:int32_t|float)\s+(\w+);", fields)
+    assert names == [n for n, _ in Desc._fields_]
+    assert ctypes.sizeof(Desc) == 4 * len(names)
+    assert np.dtype(np.int32).itemsize == 4

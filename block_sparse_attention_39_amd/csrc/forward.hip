@@ -64,6 +64,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte chunk (native vector, not HIP's uint4)
 
 constexpr float kRescaleLog2 = 8.0f;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left alone (gfx9 encoding)
+constexpr int kWaitVm0 = 0x0F70;
 constexpr int kGroups = 8;        // block groups of the grouped launch (one per XCD)
 constexpr int kMaxGroupSize = 64; // blocks per group the fence can track (one per lane)
 #ifndef BSA_FENCE_CHUNK
@@ -75,53 +77,53 @@ constexpr int kMaxSpin = 400;            // bounded wait per fence (x s_sleep 2)
 template <int D>
 struct Cfg {
     static constexpr int C = D / 8;                // 16-byte chunks in a K row
-    static constexpr int KSTR = 2 * D + 16;        // padded K row in LDS (bytes)
-    static constexpr int VSTR = 2 * kTile + 16;    // padded V^T row in LDS (bytes)
-    static constexpr int KB = kTile * KSTR;        // K tile in LDS
-    static constexpr int VB = D * VSTR;            // V^T tile in LDS
+    static constexpr int KB = kTile * D * 2;       // K tile in LDS (16 KB for D = 128)
+    static constexpr int VB = D * kTile * 2;       // V^T tile in LDS
     static constexpr int BUF = KB + VB;            // one LDS stage
-    static constexpr int NLD = kTile * C / 256;    // 16-byte chunks per thread, for K and for V^T
+    static constexpr int NK = kTile * C / 256;     // DMA instructions per wave for a K tile (and for V^T)
     static constexpr int SD = D / 16;              // MFMA steps over d for S^T
     static constexpr int OD = D / 32;              // 32-row d blocks of O^T
 };
 
-// Registers holding the next K/V^T tile while the current one is computed.
-// Named members (not arrays) so they stay in registers.
-struct Prefetch {
-    u32x4 k0, k1, k2, k3;  // K chunks (k2, k3 unused when D = 64)
-    u32x4 v0, v1, v2, v3;  // V^T chunks (v2, v3 unused when D = 64)
-};
-
+// LDS layout of a stage: the K tile as 64 rows of D bf16 and the V^T tile as D
+// rows of 64 bf16, unpadded, with the 16-byte chunks of every row permuted by
+// an XOR so that the 16 rows read by half a wave hit 16 different bank groups:
+//   K row r (C chunks):    physical chunk = c ^ kswz(r)
+//   V^T row d (8 chunks):  physical chunk = c ^ ((d >> 1) & 7)
 template <int D>
-__device__ inline void load_tile(Prefetch& pf, const u32x4* __restrict__ kt, const u32x4* __restrict__ vt,
-                                 int tid) {
-    pf.k0 = kt[tid];
-    pf.k1 = kt[tid + 256];
-    pf.v0 = vt[tid];
-    pf.v1 = vt[tid + 256];
-    if constexpr (Cfg<D>::NLD == 4) {
-        pf.k2 = kt[tid + 512];
-        pf.k3 = kt[tid + 768];
-        pf.v2 = vt[tid + 512];
-        pf.v3 = vt[tid + 768];
-    }
+__device__ inline int kswz(int r) {
+    return Cfg<D>::C == 16 ? (r & 15) : ((r >> 1) & 7);
 }
+__device__ inline int vswz(int d) { return (d >> 1) & 7; }
 
-// kw / vw: this thread's LDS write addresses for chunk 0 of the K and V^T tiles
-// of the target buffer; chunk i sits a fixed distance further.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Copy one key tile (K: 64 x D, V^T: D x 64, both contiguous in HBM) into an
+// LDS stage with direct-to-LDS loads: every wave-wide instruction fills 1 KB
+// of LDS, lane L the 16 bytes at offset 16 L; the lane fetches whichever
+// global chunk belongs there under the XOR layout.  No registers are staged;
+// completion is waited for with vmcnt before the stage is handed over.
 template <int D>
-__device__ inline void store_tile(const Prefetch& pf, uint8_t* kw, uint8_t* vw) {
-    constexpr int KSTEP = (256 / Cfg<D>::C) * Cfg<D>::KSTR;  // 256 chunks = this many K rows
-    constexpr int VSTEP = 32 * Cfg<D>::VSTR;                 // 256 chunks = 32 V^T rows
-    *(u32x4*)(kw) = pf.k0;
-    *(u32x4*)(kw + KSTEP) = pf.k1;
-    *(u32x4*)(vw) = pf.v0;
-    *(u32x4*)(vw + VSTEP) = pf.v1;
-    if constexpr (Cfg<D>::NLD == 4) {
-        *(u32x4*)(kw + 2 * KSTEP) = pf.k2;
-        *(u32x4*)(kw + 3 * KSTEP) = pf.k3;
-        *(u32x4*)(vw + 2 * VSTEP) = pf.v2;
-        *(u32x4*)(vw + 3 * VSTEP) = pf.v3;
+__device__ inline void dma_tile(const uint8_t* __restrict__ kt, const uint8_t* __restrict__ vt, uint8_t* stage,
+                                int wave, int lane) {
+    constexpr int C = Cfg<D>::C;
+#pragma unroll
+    for (int n = 0; n < Cfg<D>::NK; ++n) {
+        const int blk = n * 4 + wave;           // 1 KB block of the K region
+        const int p = blk * 64 + lane;          // 16-byte slot
+        const int r = p / C;
+        const int c = (p % C) ^ kswz<D>(r);
+        __builtin_amdgcn_global_load_lds((const void*)(kt + (r * C + c) * 16), (lds_ptr_t)(stage + blk * 1024),
+                                         16, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < Cfg<D>::NK; ++n) {
+        const int blk = n * 4 + wave;
+        const int p = blk * 64 + lane;
+        const int d = p / 8;
+        const int c = (p % 8) ^ vswz(d);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + (d * 8 + c) * 16),
+                                         (lds_ptr_t)(stage + Cfg<D>::KB + blk * 1024), 16, 0, 0);
     }
 }
 
@@ -161,8 +163,8 @@ __device__ inline void fence_enter(const Fence& f, int seq, int wave, int lane) 
 // One query tile, all four waves of the block.  `vi` < 0 marks a prefix
 // (dense) query tile.  With FENCED the block follows its group's key chunks.
 template <int D, bool FENCED>
-__device__ __attribute__((always_inline)) inline void attend_tile(const ForwardArgs& a, uint8_t* smem, int64_t bh,
-                                                                  int qt, int vi, Fence fence) {
+__device__ __attribute__((always_inline)) inline void attend_tile(const ForwardArgs& a, uint8_t* st0, uint8_t* st1,
+                                                                  int64_t bh, int qt, int vi, Fence fence) {
     using CF = Cfg<D>;
     constexpr int SD = CF::SD, OD = CF::OD;
 
@@ -176,9 +178,9 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     const int32_t* idx_row = dense ? nullptr : a.idx + (bh * a.nvt + vi) * a.keep;
     const int n_tiles = a.npt + a.nvt;
     const int64_t n_tot = (int64_t)n_tiles * kTile;
-    const u32x4* kb = (const u32x4*)(a.k + bh * n_tot * D);
-    const u32x4* vb = (const u32x4*)(a.vt + bh * n_tot * D);
-    constexpr int TCH = kTile * D / 8;  // 16-byte chunks per tile
+    const uint8_t* kb = (const uint8_t*)(a.k + bh * n_tot * D);
+    const uint8_t* vb = (const uint8_t*)(a.vt + bh * n_tot * D);
+    constexpr int TB = kTile * D * 2;  // bytes per tile
     // kept-tile numbers are clamped into range so a corrupt list cannot
     // address outside the tensors
     auto tile_of = [&](int j) -> int {
@@ -187,17 +189,17 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
         return a.npt + min(max(t, 0), a.nvt - 1);
     };
 
-    // per-lane LDS addresses (buffer 0; buffer 1 is CF::BUF further)
-    // writes: chunk tid of the K tile is row tid / C, chunk tid % C; of the
-    // V^T tile row tid / 8, chunk tid % 8
-    uint8_t* const kw0 = smem + (tid / CF::C) * CF::KSTR + (tid % CF::C) * 16;
-    uint8_t* const vw0 = smem + CF::KB + (tid / 8) * CF::VSTR + (tid % 8) * 16;
-    // S^T operand: K row 32*kh + (16-row group) + swapped position, chunk 2*s + hf
+    // Per-lane LDS byte offsets inside a stage.  S^T operand: K row
+    // R = 32*kh + (16-row group) + swapped position, logical chunk 2*s + hf;
+    // under the XOR layout the address of step s is koff ^ (s << 5).
     const int r16 = lr & 15;
     const int rsw = (r16 & 3) | ((r16 & 4) << 1) | ((r16 & 8) >> 1);
-    const uint8_t* const kr0 = smem + (32 * kh + (lr & 16) + rsw) * CF::KSTR + hf * 16;
-    // O^T operand: V^T row 32*i + lr, keys 32*kh + 16*c + 8*hf .. +7
-    const uint8_t* const vr0 = smem + CF::KB + lr * CF::VSTR + (32 * kh + 8 * hf) * 2;
+    const int R = 32 * kh + (lr & 16) + rsw;
+    const int koff = R * (D * 2) + ((hf ^ (kswz<D>(R) & 1)) << 4) + ((kswz<D>(R) >> 1) << 5);
+    // O^T operand: V^T row 32*i + lr, logical chunk 4*kh + 2*c + hf; the
+    // address is (voff ^ (c << 5)) + i * 32 rows
+    const int vy = vswz(lr);
+    const int voff = Cfg<D>::KB + lr * (kTile * 2) + (((4 * kh + hf) ^ vy) << 4);
 
     // Q^T operand: lane holds query 32*qh + lr, channels 16*s + 8*hf .. +7
     bf16x8 qf[SD];
@@ -231,10 +233,9 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     if (n_iter > 1) follow(1);
     __syncthreads();
     {
-        Prefetch pf0;
         const int t0 = tile_of(0);
-        load_tile<D>(pf0, kb + (int64_t)t0 * TCH, vb + (int64_t)t0 * TCH, tid);
-        store_tile<D>(pf0, kw0, vw0);
+        dma_tile<D>(kb + (int64_t)t0 * TB, vb + (int64_t)t0 * TB, st0, wave, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     __syncthreads();
 
@@ -246,22 +247,22 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
             const int j = j0 + cur;
             if (j < n_iter) {
                 const bool more = j + 1 < n_iter;
-                Prefetch pf;
+                uint8_t* const st = cur ? st1 : st0;  // this tile's stage
+                uint8_t* const nx = cur ? st0 : st1;  // the next tile's stage
                 if (more) {
                     const int tn = tile_of(j + 1);
-                    load_tile<D>(pf, kb + (int64_t)tn * TCH, vb + (int64_t)tn * TCH, tid);
+                    dma_tile<D>(kb + (int64_t)tn * TB, vb + (int64_t)tn * TB, nx, wave, lane);
                 }
-                const uint8_t* kr = kr0 + cur * CF::BUF;
-                const uint8_t* vr = vr0 + cur * CF::BUF;
 
                 // every operand read of the tile up front
                 bf16x8 kf[SD], vf[2 * OD];
 #pragma unroll
-                for (int s = 0; s < SD; ++s) kf[s] = *(const bf16x8*)(kr + 32 * s);
+                for (int s = 0; s < SD; ++s) kf[s] = *(const bf16x8*)(st + (koff ^ (s << 5)));
 #pragma unroll
                 for (int i = 0; i < OD; ++i)
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) vf[2 * i + c] = *(const bf16x8*)(vr + i * 32 * CF::VSTR + c * 32);
+                    for (int c = 0; c < 2; ++c)
+                        vf[2 * i + c] = *(const bf16x8*)(st + (voff ^ (c << 5)) + i * 32 * (kTile * 2));
 
                 // S^T (32 keys x 32 queries) = K Q^T
                 f32x16 s_acc = f32x16{};
@@ -305,7 +306,7 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
                     for (int c = 0; c < 2; ++c)
                         acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * i + c], pf16[c], acc_o[i], 0, 0, 0);
 
-                if (more) store_tile<D>(pf, kw0 + (1 - cur) * CF::BUF, vw0 + (1 - cur) * CF::BUF);
+                if (more) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of the next tile landed
                 if (j + 2 < n_iter) follow(j + 2);  // the tile requested at the start of the next step
                 __syncthreads();
             }
@@ -313,8 +314,8 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     }
 
     // ---- merge the two key halves of every query, normalise, store --------
-    float* comb = (float*)smem;                      // [2 qh][OD*16][64 lanes]
-    float* comb_m = comb + 2 * OD * 16 * 64;         // [2 qh][64]
+    float* comb = (float*)st0;                       // [2 qh][OD*16][64 lanes]
+    float* comb_m = (float*)st1;                     // [2 qh][64]
     float* comb_l = comb_m + 2 * 64;                 // [2 qh][64]
     uint16_t* stage = (uint16_t*)(comb_l + 2 * 64);  // [64][D + 8]
     constexpr int SROW = D + 8;
@@ -360,7 +361,7 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
         constexpr int C = CF::C;
         uint16_t* orow = a.o + (bh * n_tot + (int64_t)qt * kTile) * D;
 #pragma unroll
-        for (int i = 0; i < CF::NLD; ++i) {
+        for (int i = 0; i < CF::NK; ++i) {
             const int q = tid + 256 * i;
             const int r = q / C, c = q % C;
             *(u32x4*)(orow + r * D + c * 8) = *(const u32x4*)(stage + r * SROW + c * 8);
@@ -373,15 +374,16 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 sparse_fwd_kernel(ForwardArgs a, int64_t first) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg<D>::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[Cfg<D>::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[Cfg<D>::BUF];
     const int64_t g = first + blockIdx.x;
     const int64_t n_pref = (int64_t)a.BH * a.npt;
     if (g < n_pref) {
-        attend_tile<D, false>(a, smem, g / a.npt, (int)(g % a.npt), -1, Fence{});
+        attend_tile<D, false>(a, st0, st1, g / a.npt, (int)(g % a.npt), -1, Fence{});
     } else {
         const int64_t gv = g - n_pref;
         const int vi = (int)(gv % a.nvt);
-        attend_tile<D, false>(a, smem, gv / a.nvt, a.npt + vi, vi, Fence{});
+        attend_tile<D, false>(a, st0, st1, gv / a.nvt, a.npt + vi, vi, Fence{});
     }
 }
 
@@ -391,7 +393,8 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg<D>::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[Cfg<D>::BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[Cfg<D>::BUF];
     const int group = blockIdx.x % kGroups, slot = blockIdx.x / kGroups;
     const int S = gridDim.x / kGroups;
     const int64_t n_items = (int64_t)a.BH * a.nvt;
@@ -401,7 +404,7 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
         const int64_t item = (r * kGroups + group) * S + slot;
         if (item >= n_items) break;
         f.base = (int)(r * n_chunks);
-        attend_tile<D, true>(a, smem, item / a.nvt, a.npt + (int)(item % a.nvt), (int)(item % a.nvt), f);
+        attend_tile<D, true>(a, st0, st1, item / a.nvt, a.npt + (int)(item % a.nvt), (int)(item % a.nvt), f);
     }
     // done: never hold the rest of the group back
     if (threadIdx.x == 0) __hip_atomic_store(f.prog + slot, INT_MAX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -14,8 +14,9 @@ BSA_OK = 0
 STATUS_NAMES = {0: "BSA_OK", -1: "BSA_ERR_NULL", -2: "BSA_ERR_SHAPE", -3: "BSA_ERR_UNSUPPORTED",
                 -4: "BSA_ERR_ALIGN", -5: "BSA_ERR_WORKSPACE", -6: "BSA_ERR_LAUNCH", -7: "BSA_ERR_ARG"}
 TILE_STATIC, TILE_DYNAMIC = 0, 1
-PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_VT = 0, 1, 2, 3
+PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_KF, PERM_GATHER_VF = 0, 1, 2, 3, 4
 MAX_VIDEO_TILES = 8192
+MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
 EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_status_string", "bsa_version")
 

@@ -12,8 +12,8 @@ import math
 
 import torch
 
-from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_VT, PERM_SCATTER, TILE_DYNAMIC, TILE_STATIC, BsaError,
-                   Desc, lib)
+from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_VF, PERM_SCATTER, TILE_DYNAMIC,
+                   TILE_STATIC, BsaError, Desc, lib)
 
 
 def make_desc(batch: int, heads: int, head_dim: int, grid, keep_tiles: int, *, scale: float | None = None,
@@ -66,10 +66,17 @@ def gather(desc: Desc, src, dst, perm, stream=None):
                              _stream(stream)), "bsa_permute(GATHER)")
 
 
-def gather_vt(desc: Desc, src, dst, perm, stream=None):
-    """Raster V -> tiled order transposed inside every 64-token tile ([B, H, Ntot/64, D, 64])."""
-    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER_VT, None, _ptr(perm), None, _ptr(src), _ptr(dst), None,
-                             0, _stream(stream)), "bsa_permute(GATHER_VT)")
+def gather_kf(desc: Desc, src, dst, perm, stream=None):
+    """Raster K -> the K-fragment layout (the tiled order, each 64-token tile in
+    the attention kernel's operand order; same size as the tiled layout)."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER_KF, None, _ptr(perm), None, _ptr(src), _ptr(dst), None,
+                             0, _stream(stream)), "bsa_permute(GATHER_KF)")
+
+
+def gather_vf(desc: Desc, src, dst, perm, stream=None):
+    """Raster V -> the V-fragment layout (same size as the tiled layout)."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER_VF, None, _ptr(perm), None, _ptr(src), _ptr(dst), None,
+                             0, _stream(stream)), "bsa_permute(GATHER_VF)")
 
 
 def scatter(desc: Desc, src, dst, perm, stream=None):
@@ -77,17 +84,18 @@ def scatter(desc: Desc, src, dst, perm, stream=None):
                              _stream(stream)), "bsa_permute(SCATTER)")
 
 
-def plan(desc: Desc, q_tiled, k_tiled, block_idx, workspace, stream=None):
+def plan(desc: Desc, q_tiled, k_frag, block_idx, workspace, stream=None):
     ws = workspace.numel() * workspace.element_size()
-    _check(lib().bsa_plan(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_tiled), _ptr(block_idx), _ptr(workspace), ws,
+    _check(lib().bsa_plan(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), _ptr(block_idx), _ptr(workspace), ws,
                           _stream(stream)), "bsa_plan")
 
 
-def forward(desc: Desc, q_tiled, k_tiled, vt_tiled, block_idx, o_tiled, lse=None, workspace=None, stream=None):
-    """``vt_tiled`` is V in the per-tile transposed layout written by gather_vt.
-    With ``workspace`` the video query tiles run as the grouped persistent grid."""
+def forward(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, workspace=None, stream=None):
+    """``k_frag`` / ``v_frag`` are K and V in the fragment layouts written by
+    gather_kf / gather_vf.  With ``workspace`` the video query tiles run as the
+    grouped persistent grid."""
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().bsa_forward(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_tiled), _ptr(vt_tiled), _ptr(block_idx),
+    _check(lib().bsa_forward(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), _ptr(v_frag), _ptr(block_idx),
                              _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws, _stream(stream)), "bsa_forward")
 
 
@@ -122,9 +130,9 @@ class BlockSparseAttention:
         self.perm = torch.empty((B, max(self.n_video, 1)), dtype=torch.int32, device=device)
         regions = (desc.grid_t // 8) * (desc.grid_h // 8) * (desc.grid_w // 8)
         self.shape_map = torch.empty((B, max(regions, 1)), dtype=torch.uint8, device=device) if self.dynamic else None
-        self.q_t, self.k_t, self.o_t = (torch.empty((B, H, self.n_tot, D), dtype=bf, device=device)
-                                        for _ in range(3))
-        self.vt_t = torch.empty((B, H, self.n_tot // 64, D, 64), dtype=bf, device=device)
+        # q_t, o_t: tiled layout; k_f, v_f: the fragment layouts (same size)
+        self.q_t, self.k_f, self.v_f, self.o_t = (torch.empty((B, H, self.n_tot, D), dtype=bf, device=device)
+                                                  for _ in range(4))
         self.block_idx = torch.empty((B, H, max(self.nvt, 1), max(desc.keep_tiles, 1)), dtype=torch.int32,
                                      device=device)
         self.workspace = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device)
@@ -136,14 +144,14 @@ class BlockSparseAttention:
 
     def gather_qkv(self, q, k, v, stream=None):
         gather(self.desc, q, self.q_t, self.perm, stream)
-        gather(self.desc, k, self.k_t, self.perm, stream)
-        gather_vt(self.desc, v, self.vt_t, self.perm, stream)
+        gather_kf(self.desc, k, self.k_f, self.perm, stream)
+        gather_vf(self.desc, v, self.v_f, self.perm, stream)
 
     def plan(self, stream=None):
-        plan(self.desc, self.q_t, self.k_t, self.block_idx, self.workspace, stream)
+        plan(self.desc, self.q_t, self.k_f, self.block_idx, self.workspace, stream)
 
     def forward(self, stream=None):
-        forward(self.desc, self.q_t, self.k_t, self.vt_t, self.block_idx, self.o_t, self.lse,
+        forward(self.desc, self.q_t, self.k_f, self.v_f, self.block_idx, self.o_t, self.lse,
                 self.workspace if self.grouped else None, stream)
 
     def scatter_out(self, out, stream=None):

@@ -28,11 +28,15 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           # keep per-thread arrays in registers: LDS is budgeted by hand
           "-mllvm", "-disable-promote-alloca-to-lds",
           "-Wall", "-Wno-unused-result"]
+# per-file additions: the attention kernel keeps its MFMA accumulators in
+# ordinary VGPRs (its softmax rescales them with vector instructions, and the
+# accumulation registers then hold the operand fragments)
+EXTRA = {"forward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -128,7 +128,8 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
-    if (op != BSA_PERM_BUILD && op != BSA_PERM_GATHER && op != BSA_PERM_SCATTER && op != BSA_PERM_GATHER_VT)
+    if (op != BSA_PERM_BUILD && op != BSA_PERM_GATHER && op != BSA_PERM_SCATTER && op != BSA_PERM_GATHER_KF &&
+        op != BSA_PERM_GATHER_VF)
         return BSA_ERR_ARG;
     if (g.B == 0 || g.n_tot == 0) return BSA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -157,23 +158,26 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     if (g.H == 0) return BSA_OK;
     if (!src || !dst || (g.n_video > 0 && !perm)) return BSA_ERR_NULL;
     if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
-    if (op == BSA_PERM_GATHER_VT)
-        return launched(bsa::launch_gather_vt(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
+    if (op == BSA_PERM_GATHER_KF)
+        return launched(bsa::launch_gather_kf(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
+                                              (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s));
+    if (op == BSA_PERM_GATHER_VF)
+        return launched(bsa::launch_gather_vf(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
                                               (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s));
     return launched(bsa::launch_permute_copy(op == BSA_PERM_SCATTER, static_cast<const uint16_t*>(src),
                                              static_cast<uint16_t*>(dst), perm, (int)g.B, (int)g.H, (int)g.D,
                                              (int)g.npf, g.n_video, s));
 }
 
-bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_tiled, int32_t* block_idx, void* ws,
+bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_frag, int32_t* block_idx, void* ws,
                     size_t ws_bytes, void* stream) {
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
     if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
     if (g.empty || g.nvt == 0) return BSA_OK;
-    if (!q_tiled || !k_tiled || !block_idx) return BSA_ERR_NULL;
-    if (misaligned(q_tiled, 16) || misaligned(k_tiled, 16) || misaligned(block_idx, 4)) return BSA_ERR_ALIGN;
+    if (!q_tiled || !k_frag || !block_idx) return BSA_ERR_NULL;
+    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(block_idx, 4)) return BSA_ERR_ALIGN;
     const Layout L = layout(g);
     if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
     if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
@@ -182,7 +186,7 @@ bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_til
     float* qbar = reinterpret_cast<float*>(w + L.qbar);
     float* kbar = reinterpret_cast<float*>(w + L.kbar);
     float* scores = reinterpret_cast<float*>(w + L.scores);
-    hipError_t e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_tiled),
+    hipError_t e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag),
                                     qbar, kbar, (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s);
     for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
         const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
@@ -194,15 +198,16 @@ bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_til
     return launched(e);
 }
 
-bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_tiled, const void* vt_tiled,
+bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
                        const int32_t* block_idx, void* o_tiled, float* lse, void* ws, size_t ws_bytes,
                        void* stream) {
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
+    if (g.npt + g.nvt > BSA_MAX_TILES) return BSA_ERR_UNSUPPORTED;
     if (g.empty) return BSA_OK;
-    if (!q_tiled || !k_tiled || !vt_tiled || !o_tiled || (g.nvt > 0 && !block_idx)) return BSA_ERR_NULL;
-    if (misaligned(q_tiled, 16) || misaligned(k_tiled, 16) || misaligned(vt_tiled, 16) || misaligned(o_tiled, 16) ||
+    if (!q_tiled || !k_frag || !v_frag || !o_tiled || (g.nvt > 0 && !block_idx)) return BSA_ERR_NULL;
+    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(v_frag, 16) || misaligned(o_tiled, 16) ||
         misaligned(block_idx, 4) || misaligned(lse, 4))
         return BSA_ERR_ALIGN;
     int* progress = nullptr;
@@ -214,8 +219,8 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
     }
     bsa::ForwardArgs a;
     a.q = static_cast<const uint16_t*>(q_tiled);
-    a.k = static_cast<const uint16_t*>(k_tiled);
-    a.vt = static_cast<const uint16_t*>(vt_tiled);
+    a.k = static_cast<const uint16_t*>(k_frag);
+    a.v = static_cast<const uint16_t*>(v_frag);
     a.idx = block_idx;
     a.o = static_cast<uint16_t*>(o_tiled);
     a.lse = lse;

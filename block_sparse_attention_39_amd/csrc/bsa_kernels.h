@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "bsa.h"
+
 namespace bsa {
 
 constexpr int kTile = 64;  // tokens per tile
@@ -16,8 +18,12 @@ hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int t
 hipError_t launch_permute_copy(bool to_raster, const uint16_t* src, uint16_t* dst, const int32_t* perm,
                                int B, int H, int D, int n_prefix, int64_t n_video, hipStream_t s);
 
-// Raster [B][Ntot][H][D] -> per-tile transposed [B][H][Ntot/64][D][64] (the V operand layout).
-hipError_t launch_gather_vt(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
+// Raster [B][Ntot][H][D] -> the K-fragment and V-fragment layouts (kfrag, vfrag
+// of the C interface): the tiled order with every 64-token tile laid out in
+// the operand order of the attention kernel's MFMAs.
+hipError_t launch_gather_kf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
+                            int n_prefix, int64_t n_video, hipStream_t s);
+hipError_t launch_gather_vf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
                             int n_prefix, int64_t n_video, hipStream_t s);
 
 // Dynamic shapes: per-(b, region, head) partial |delta| sums, then shape choice
@@ -29,8 +35,9 @@ hipError_t launch_shape_choose(const double* partial, uint8_t* shape_map, int B,
 hipError_t launch_perm_dynamic(const uint8_t* shape_map, int32_t* perm, int B, int T, int Hg, int W,
                                hipStream_t s);
 
-// Mean of the 64 tokens of every video tile of Q and K -> float [BH][nvt][D].
-hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_tiled, float* qbar, float* kbar, int BH,
+// Mean of the 64 tokens of every video tile of Q (tiled) and K (K-fragment
+// layout) -> float [BH][nvt][D].
+hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
                        int n_prefix, int nvt, int D, hipStream_t s);
 
 // scores[bh][i][j] = qbar_i . kbar_j (float) for bh in [0, BH).
@@ -42,8 +49,8 @@ hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k
 
 struct ForwardArgs {
     const uint16_t* q;       // tiled [BH][Ntot][D]
-    const uint16_t* k;
-    const uint16_t* vt;      // per-tile transposed [BH][Ntot/64][D][64]
+    const uint16_t* k;       // K-fragment layout [BH][Ntot/64][2][D/16][64][8]
+    const uint16_t* v;       // V-fragment layout [BH][Ntot/64][2][D/32][2][64][8]
     const int32_t* idx;      // [BH][nvt][keep]
     uint16_t* o;             // tiled [BH][Ntot][D]
     float* lse;              // [BH][Ntot] or null

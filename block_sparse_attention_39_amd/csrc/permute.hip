@@ -64,18 +64,16 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
     }
 }
 
-// Raster V -> per-tile transposed layout [B][H][tile][D][64]: the 64 tokens of
-// a tile become the contiguous dimension, which is the operand layout of the
-// P V product in the attention kernel.  One block per (batch, tile); work item
-// = (head, group of 8 tokens, 8-channel chunk), chunk fastest: a thread reads
-// 8 token rows of 16 bytes (256-byte head rows across a wave), transposes the
-// 8 x 8 block of bf16 values in registers and writes 8 channel rows of 16
-// bytes (8 consecutive tokens each).
-__device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-__device__ inline uint32_t word_of(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
+// Raster K -> K-fragment layout [B][H][tile][kh][s][lane][8]: chunk
+// (kh, s, lane) of a tile holds channels 16 s + 8 (lane / 32) .. +7 of the
+// tile's token 32 kh + swap23(lane % 32) (bits 2 and 3 exchanged), i.e. the
+// A operand of v_mfma_f32_32x32x16_bf16 for the S^T = K Q^T products of the
+// attention kernel.  One block per (batch, tile); work item = (head, chunk),
+// chunk fastest, so a wave writes 1 KB contiguous and reads 32-byte runs of
+// the tile's raster rows.
+__device__ inline int swap23(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-__global__ __launch_bounds__(256) void gather_vt_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+__global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
                                                         int n_prefix, int64_t n_video, int64_t n_tot) {
     __shared__ int64_t tok[kTile];
@@ -88,7 +86,45 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const uint4* __restrict_
         tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
     }
     __syncthreads();
-    const int D = C * 8;
+    const int SD = C / 2;
+    const int per_head = kTile * C;
+    const int items = H * per_head;
+#pragma unroll 4
+    for (int it = threadIdx.x; it < items; it += 256) {
+        const int q = it % per_head, h = it / per_head;
+        const int lane = q & 63, s = (q >> 6) % SD, kh = (q >> 6) / SD;
+        const int r = 32 * kh + swap23(lane & 31);
+        const int cc = 2 * s + (lane >> 5);
+        dst[(((int64_t)b * H + h) * n_tiles + tile) * per_head + q] = src[(((int64_t)b * n_tot + tok[r]) * H + h) * C + cc];
+    }
+}
+
+// Raster V -> V-fragment layout [B][H][tile][kh][i][c][lane][8]: chunk
+// (kh, i, c, lane) of a tile holds channel 32 i + lane % 32 of the tile's
+// tokens 32 kh + 16 c + 8 (lane / 32) .. +7, i.e. the A operand of the
+// O^T = V^T P^T products.  One block per (batch, tile); work item = (head,
+// group of 8 tokens, 8-channel chunk): a thread reads 8 token rows of 16 bytes
+// (256-byte head rows across a wave), transposes the 8 x 8 block of bf16
+// values in registers and writes 8 chunks for 8 consecutive lanes (128 bytes
+// contiguous).
+__device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ inline uint32_t word_of(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
+
+__global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        const int32_t* __restrict__ perm, int H, int C,
+                                                        int n_prefix, int64_t n_video, int64_t n_tot) {
+    __shared__ int64_t tok[kTile];
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x;
+    const int64_t p0 = tile * kTile;
+    const int64_t n_tiles = n_tot / kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t p = p0 + threadIdx.x;
+        tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
+    }
+    __syncthreads();
+    const int OD = C / 4;  // 32-channel blocks
     const int items = H * 8 * C;
     for (int it = threadIdx.x; it < items; it += 256) {
         const int dc = it % C;
@@ -98,8 +134,11 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const uint4* __restrict_
         auto row = [&](int i) { return src[(((int64_t)b * n_tot + tok[8 * g + i]) * H + h) * C + dc]; };
         r0 = row(0); r1 = row(1); r2 = row(2); r3 = row(3);
         r4 = row(4); r5 = row(5); r6 = row(6); r7 = row(7);
-        // out[e] holds channel 8*dc + e of tokens 8*g .. 8*g + 7
-        uint4* out = dst + ((((int64_t)b * H + h) * n_tiles + tile) * D + 8 * dc) * (kTile / 8) + g;
+        // tokens 8 g .. 8 g + 7 = 32 kh + 16 c + 8 hf + e; channels 8 dc + e'
+        // = 32 i + 8 (dc % 4) + e' -> lane 32 hf + 8 (dc % 4) + e'
+        const int kh = g >> 2, c = (g >> 1) & 1, hf = g & 1, i = dc >> 2;
+        uint4* out = dst + (((int64_t)b * H + h) * n_tiles + tile) * (kTile * C) +
+                     ((kh * OD + i) * 2 + c) * 64 + 32 * hf + 8 * (dc & 3);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int w = e >> 1;
@@ -115,18 +154,27 @@ __global__ __launch_bounds__(256) void gather_vt_kernel(const uint4* __restrict_
                 o.z = lo_pair(word_of(r4, w), word_of(r5, w));
                 o.w = lo_pair(word_of(r6, w), word_of(r7, w));
             }
-            out[e * (kTile / 8)] = o;
+            out[e] = o;
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_gather_vt(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
+hipError_t launch_gather_kf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
                             int n_prefix, int64_t n_video, hipStream_t s) {
     const int64_t n_tot = n_prefix + n_video;
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_vt_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
+    hipLaunchKernelGGL(gather_kf_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
+                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_vf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
+                            int n_prefix, int64_t n_video, hipStream_t s) {
+    const int64_t n_tot = n_prefix + n_video;
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_vf_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
                        (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot);
     return hipGetLastError();
 }

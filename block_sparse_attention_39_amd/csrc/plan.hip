@@ -6,9 +6,9 @@
 // product of the pooled query and key vectors; equal scores go to the lower key
 // tile number; kept lists are written in ascending order.
 //
-// pool   : HBM-bound read of Q and K once; one wave per tile, 16-byte loads,
-//          double accumulation (exact for bf16 inputs), one rounding to float,
-//          cross-lane reduction with wave shuffles.
+// pool   : HBM-bound read of Q (tiled) and K (K-fragment layout) once; one
+//          wave per tile, 16-byte loads, double accumulation (exact for bf16
+//          inputs), one rounding to float, cross-lane reduction with shuffles.
 // scores : float GEMM per (batch, head) of the pooled vectors, 64x64 output
 //          blocks through LDS.
 // topk   : one block per row; 8-bit radix select on the order-preserving
@@ -24,15 +24,48 @@ __device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 // ---------------------------------------------------------------- pooling --
-// Block = 4 waves, one tile per wave.  Lane l reads chunk c = l % C of rows
-// r = l / C + i * (64 / C); the wave then folds the 64 / C lanes that share c.
+// Block = 4 waves, one tile per wave; the first B*H*nvt tiles are Q's (tiled
+// layout), the next ones K's (K-fragment layout).  Sums are exact in double
+// (64 bf16 values), so the order of summation does not matter.
+//  Q: lane l reads chunk c = l % C of rows r = l / C + i * (64 / C); the wave
+//     then folds the 64 / C lanes that share c.
+//  K: chunk (kh, s, lane) holds channels 16 s + 8 (lane / 32) .. +7 of token
+//     32 kh + swap23(lane % 32); lane l takes channel group (s, hf) =
+//     (l / LPG / 2, l / LPG % 2) and 64 / LPG of the tile's tokens, then the
+//     LPG lanes of a group fold their sums.
+__device__ inline void acc8(double (&acc)[8], const uint4& x) {
+    acc[0] += (double)bf_lo(x.x);
+    acc[1] += (double)bf_hi(x.x);
+    acc[2] += (double)bf_lo(x.y);
+    acc[3] += (double)bf_hi(x.y);
+    acc[4] += (double)bf_lo(x.z);
+    acc[5] += (double)bf_hi(x.z);
+    acc[6] += (double)bf_lo(x.w);
+    acc[7] += (double)bf_hi(x.w);
+}
+
+__device__ inline void store_mean8(float* dst, const double (&acc)[8]) {
+    float4 lo, hi;
+    lo.x = (float)(acc[0] * (1.0 / kTile));
+    lo.y = (float)(acc[1] * (1.0 / kTile));
+    lo.z = (float)(acc[2] * (1.0 / kTile));
+    lo.w = (float)(acc[3] * (1.0 / kTile));
+    hi.x = (float)(acc[4] * (1.0 / kTile));
+    hi.y = (float)(acc[5] * (1.0 / kTile));
+    hi.z = (float)(acc[6] * (1.0 / kTile));
+    hi.w = (float)(acc[7] * (1.0 / kTile));
+    ((float4*)dst)[0] = lo;
+    ((float4*)dst)[1] = hi;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                    float* __restrict__ qbar, float* __restrict__ kbar, int BH,
                                                    int n_prefix, int nvt) {
     constexpr int C = D / 8;         // 16-byte chunks per row
-    constexpr int RPI = 64 / C;      // rows covered by one wave-wide load
-    constexpr int ITER = kTile / RPI;
+    constexpr int SD = D / 16;       // K-fragment steps
+    constexpr int LPG = 64 / (2 * SD);  // lanes per channel group (K)
+    constexpr int TPL = kTile / LPG;    // tokens per lane (K)
     const int lane = threadIdx.x & 63;
     const int64_t tiles_per_tensor = (int64_t)BH * nvt;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -42,37 +75,31 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
     const int64_t bh = t / nvt, i = t % nvt;
     const int64_t n_tot = n_prefix + (int64_t)nvt * kTile;
     const uint4* src = (is_k ? k : q) + ((bh * n_tot + n_prefix + i * kTile) * C);
-    const int c = lane % C, r0 = lane / C;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (!is_k) {
+        constexpr int RPI = 64 / C;  // rows covered by one wave-wide load
+        const int c = lane % C, r0 = lane / C;
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-        const uint4 x = src[(r0 + it * RPI) * C + c];
-        acc[0] += (double)bf_lo(x.x);
-        acc[1] += (double)bf_hi(x.x);
-        acc[2] += (double)bf_lo(x.y);
-        acc[3] += (double)bf_hi(x.y);
-        acc[4] += (double)bf_lo(x.z);
-        acc[5] += (double)bf_hi(x.z);
-        acc[6] += (double)bf_lo(x.w);
-        acc[7] += (double)bf_hi(x.w);
-    }
+        for (int it = 0; it < kTile / RPI; ++it) acc8(acc, src[(r0 + it * RPI) * C + c]);
 #pragma unroll
-    for (int o = C; o < 64; o <<= 1)
+        for (int o = C; o < 64; o <<= 1)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
-    if (lane < C) {
-        float4 lo, hi;
-        lo.x = (float)(acc[0] * (1.0 / kTile));
-        lo.y = (float)(acc[1] * (1.0 / kTile));
-        lo.z = (float)(acc[2] * (1.0 / kTile));
-        lo.w = (float)(acc[3] * (1.0 / kTile));
-        hi.x = (float)(acc[4] * (1.0 / kTile));
-        hi.y = (float)(acc[5] * (1.0 / kTile));
-        hi.z = (float)(acc[6] * (1.0 / kTile));
-        hi.w = (float)(acc[7] * (1.0 / kTile));
-        float4* dst = (float4*)((is_k ? kbar : qbar) + t * D) + 2 * c;
-        dst[0] = lo;
-        dst[1] = hi;
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
+        if (lane < C) store_mean8(qbar + t * D + 8 * lane, acc);
+    } else {
+        const int grp = lane / LPG, part = lane % LPG;
+        const int s = grp >> 1, hf = grp & 1;
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+            const int tok = part * TPL + u;  // 32 kh + m
+            const int kh = tok >> 5, m = tok & 31;
+            acc8(acc, src[(kh * SD + s) * 64 + 32 * hf + m]);
+        }
+#pragma unroll
+        for (int o = 1; o < LPG; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
+        if (part == 0) store_mean8(kbar + t * D + 16 * s + 8 * hf, acc);
     }
 }
 
@@ -210,16 +237,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, 
 
 }  // namespace
 
-hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_tiled, float* qbar, float* kbar, int BH,
+hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
                        int n_prefix, int nvt, int D, hipStream_t s) {
     const int64_t tiles = 2LL * BH * nvt;
     if (tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((tiles + 3) / 4));
     if (D == 128)
-        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_tiled,
+        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag,
                            qbar, kbar, BH, n_prefix, nvt);
     else
-        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_tiled,
+        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag,
                            qbar, kbar, BH, n_prefix, nvt);
     return hipGetLastError();
 }

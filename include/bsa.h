@@ -19,9 +19,9 @@
  *   "조건 토큰은 왜 다르게 다루나": a conditioning prefix of segment-pure tiles is
  *   attended densely and never pruned; top-k applies to video key tiles only.
  *
- * A call sequence:  bsa_permute(BUILD) -> bsa_permute(GATHER) for Q and K,
- * bsa_permute(GATHER_VT) for V -> bsa_plan -> bsa_forward ->
- * bsa_permute(SCATTER) for O.
+ * A call sequence:  bsa_permute(BUILD) -> bsa_permute(GATHER) for Q,
+ * bsa_permute(GATHER_KF) for K, bsa_permute(GATHER_VF) for V -> bsa_plan ->
+ * bsa_forward -> bsa_permute(SCATTER) for O.
  *
  * Layouts (row-major, bf16 = IEEE bfloat16):
  *   raster  bf16 [B][Ntot][H][D]   the dense prefix first (n_prefix tokens, already
@@ -30,9 +30,20 @@
  *   tiled   bf16 [B][H][Ntot][D]   prefix unchanged, then the video tokens in tile
  *                                   order: tile 0's 64 tokens, tile 1's, ...; inside
  *                                   a tile, tokens in (t, h, w) raster order.
- *   tiled_t bf16 [B][H][Ntot/64][D][64]  the tiled order, transposed inside each
- *                                   64-token tile: channel-major, the tile's 64
- *                                   tokens contiguous (the V operand of bsa_forward).
+ *   kfrag   bf16 [B][H][Ntot/64][2][D/16][64][8]  K in the tiled order, each
+ *                                   64-token tile in the operand order of the
+ *                                   attention kernel's matrix instructions:
+ *                                   element [.][t][kh][s][l][e] is channel
+ *                                   16*s + 8*(l/32) + e of the tile's token
+ *                                   32*kh + swap23(l % 32), where swap23(m)
+ *                                   exchanges bits 2 and 3 of m.
+ *   vfrag   bf16 [B][H][Ntot/64][2][D/32][2][64][8]  V likewise: element
+ *                                   [.][t][kh][i][c][l][e] is channel
+ *                                   32*i + (l % 32) of token
+ *                                   32*kh + 16*c + 8*(l/32) + e of tile t.
+ *                                   (Both are plain permutations of the tiled
+ *                                   layout, same size; every 1 KB of them is one
+ *                                   wave-wide 16-byte-per-lane load.)
  *   perm    int32 [B][Nvideo]      tiled video slot -> raster video token index
  *                                   (0-based, not counting the prefix).
  *   block_idx int32 [B][H][nVT][k] per video query tile, the k kept video key tiles
@@ -72,10 +83,18 @@ typedef enum {
 } bsa_status;
 
 enum { BSA_TILE_STATIC = 0, BSA_TILE_DYNAMIC = 1 };
-enum { BSA_PERM_BUILD = 0, BSA_PERM_GATHER = 1, BSA_PERM_SCATTER = 2, BSA_PERM_GATHER_VT = 3 };
+enum {
+    BSA_PERM_BUILD = 0,
+    BSA_PERM_GATHER = 1,
+    BSA_PERM_SCATTER = 2,
+    BSA_PERM_GATHER_KF = 3,
+    BSA_PERM_GATHER_VF = 4
+};
 
 /* Largest number of video tiles per (batch, head) that bsa_plan accepts. */
 #define BSA_MAX_VIDEO_TILES 8192
+/* Largest number of tiles (prefix + video) per (batch, head) bsa_forward accepts. */
+#define BSA_MAX_TILES 16384
 
 typedef struct bsa_desc {
     int32_t batch;      /* B >= 0 (0: every call is a no-op returning BSA_OK)         */
@@ -121,7 +140,8 @@ bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
  *       regions' tile slots.  Uses the workspace; `src`/`dst` unused.
  *  op = BSA_PERM_GATHER: `src` raster -> `dst` tiled (Q, K or V).
  *  op = BSA_PERM_SCATTER: `src` tiled -> `dst` raster (the output).
- *  op = BSA_PERM_GATHER_VT: `src` raster -> `dst` tiled_t (V).
+ *  op = BSA_PERM_GATHER_KF: `src` raster -> `dst` kfrag (K).
+ *  op = BSA_PERM_GATHER_VF: `src` raster -> `dst` vfrag (V).
  * Gather and scatter read `perm` and copy bf16 values exactly; the prefix
  * tokens keep their positions.  Source and destination must not overlap.
  */
@@ -130,19 +150,20 @@ bsa_status bsa_permute(const bsa_desc *desc, int op, const void *q_raster, int32
                        size_t ws_bytes, void *stream);
 
 /*
- * Tile selection.  From the tiled Q and K (bf16): the mean of each video
+ * Tile selection.  From Q (tiled) and K (kfrag), bf16: the mean of each video
  * tile's 64 tokens (summed exactly, rounded once to float), the score
  * s_ij = sum_d qbar_i[d] kbar_j[d] (float), and per (b, h, video query tile i)
  * the keep_tiles video key tiles with the largest s_ij, equal scores going to
  * the lower tile number, written ascending to `block_idx`.  Prefix tiles are
  * never scored (they are always attended).  Uses the workspace.
  */
-bsa_status bsa_plan(const bsa_desc *desc, const void *q_tiled, const void *k_tiled,
+bsa_status bsa_plan(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
                     int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Attention over the kept tiles.  `q_tiled`, `k_tiled` and `o_tiled` are in the
- * tiled layout, `vt_tiled` in the tiled_t layout.  For each query token of video tile i the
+ * Attention over the kept tiles.  `q_tiled` and `o_tiled` are in the tiled
+ * layout, `k_frag` in the kfrag and `v_frag` in the vfrag layout; at most
+ * BSA_MAX_TILES tiles per (batch, head).  For each query token of video tile i the
  * keys are the prefix tokens and the tokens of the tiles block_idx[b][h][i][:];
  * prefix query tokens attend to every token.  o = softmax(scale * q K^T) V with
  * bf16 products accumulated in float, a float online softmax, and o rounded to
@@ -156,8 +177,8 @@ bsa_status bsa_plan(const bsa_desc *desc, const void *q_tiled, const void *k_til
  * results are the same either way.  Calls given the same workspace must not
  * run concurrently.
  */
-bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_tiled,
-                       const void *vt_tiled, const int32_t *block_idx, void *o_tiled, float *lse,
+bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
+                       const void *v_frag, const int32_t *block_idx, void *o_tiled, float *lse,
                        void *ws, size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
@@ -166,7 +187,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 300
+#define BSA_VERSION 400
 
 #ifdef __cplusplus
 }

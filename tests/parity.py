@@ -83,10 +83,39 @@ class GpuRun:
         return self.att.block_idx.cpu().numpy()[:, :, :self.wl.n_video_tiles, :self.wl.keep_tiles]
 
 
-def tile_transposed(x_tiled: np.ndarray) -> np.ndarray:
-    """Tiled [B, H, Ntot, D] -> per-tile transposed [B, H, Ntot/64, D, 64] (the V layout)."""
+def _swap23(m: np.ndarray) -> np.ndarray:
+    return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1)
+
+
+def kfrag_layout(x_tiled: np.ndarray) -> np.ndarray:
+    """Tiled [B, H, Ntot, D] -> the K-fragment layout [B, H, Ntot/64, 2, D/16, 64, 8]
+    as the C header defines it: element [t][kh][s][l][e] is channel
+    16 s + 8 (l // 32) + e of token 32 kh + swap23(l % 32) of tile t."""
     B, H, N, D = x_tiled.shape
-    return np.ascontiguousarray(x_tiled.reshape(B, H, N // 64, 64, D).transpose(0, 1, 2, 4, 3))
+    t = x_tiled.reshape(B, H, N // 64, 64, D)
+    kh = np.arange(2)[:, None, None, None]
+    s = np.arange(D // 16)[None, :, None, None]
+    lane = np.arange(64)[None, None, :, None]
+    e = np.arange(8)[None, None, None, :]
+    tok = 32 * kh + _swap23(lane % 32) + 0 * s + 0 * e
+    ch = 16 * s + 8 * (lane // 32) + e + 0 * kh
+    return np.ascontiguousarray(t[:, :, :, tok, ch])
+
+
+def vfrag_layout(x_tiled: np.ndarray) -> np.ndarray:
+    """Tiled [B, H, Ntot, D] -> the V-fragment layout [B, H, Ntot/64, 2, D/32, 2, 64, 8]:
+    element [t][kh][i][c][l][e] is channel 32 i + l % 32 of token
+    32 kh + 16 c + 8 (l // 32) + e of tile t."""
+    B, H, N, D = x_tiled.shape
+    t = x_tiled.reshape(B, H, N // 64, 64, D)
+    kh = np.arange(2)[:, None, None, None, None]
+    i = np.arange(D // 32)[None, :, None, None, None]
+    c = np.arange(2)[None, None, :, None, None]
+    lane = np.arange(64)[None, None, None, :, None]
+    e = np.arange(8)[None, None, None, None, :]
+    tok = 32 * kh + 16 * c + 8 * (lane // 32) + e + 0 * i
+    ch = 32 * i + lane % 32 + 0 * kh + 0 * c + 0 * e
+    return np.ascontiguousarray(t[:, :, :, tok, ch])
 
 
 def gamma(n: int) -> float:

@@ -148,6 +148,29 @@ def test_too_many_tiles_for_plan():
     assert lib().bsa_plan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUP
 
 
+def test_too_many_tiles_for_forward():
+    # prefix + video tiles above BSA_MAX_TILES: forward refuses before touching anything
+    m = re.search(r"#define BSA_MAX_TILES (\d+)", HEADER)
+    assert int(m.group(1)) == bsa._lib.MAX_TILES
+    d = bsa.make_desc(1, 1, 64, (16, 128, 260), 10, n_prefix=64 * (bsa._lib.MAX_TILES - 8320 + 1))
+    assert lib().bsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == UNSUP
+    d = bsa.make_desc(1, 1, 64, (16, 128, 260), 10, n_prefix=64 * (bsa._lib.MAX_TILES - 8320))
+    assert lib().bsa_forward(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == NULL
+
+
+def test_permute_ops_match_header():
+    for name, val in (("BUILD", bsa.PERM_BUILD), ("GATHER", bsa.PERM_GATHER), ("SCATTER", bsa.PERM_SCATTER),
+                      ("GATHER_KF", bsa.PERM_GATHER_KF), ("GATHER_VF", bsa.PERM_GATHER_VF)):
+        m = re.search(r"BSA_PERM_%s = (\d+)" % name, HEADER)
+        assert m and int(m.group(1)) == val
+    d = cfg()
+    for op in (bsa.PERM_GATHER_KF, bsa.PERM_GATHER_VF):
+        # accepted ops: a missing source is reported as such
+        assert lib().bsa_permute(ctypes.byref(d), op, None, FAKE, None, None, FAKE, None, 0, None) == NULL
+        assert lib().bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE + 8, FAKE, None, 0, None) == ALIGN
+    assert lib().bsa_permute(ctypes.byref(d), 5, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
+
+
 def test_empty_problems_are_no_ops():
     L = lib()
     for d in (cfg(batch=0), cfg(heads=0), bsa.make_desc(1, 2, 64, (0, 0, 0), 0)):

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synthetic as S
-from parity import GpuRun, check_lse, check_output, check_selection, tile_transposed, to_bits
+from parity import GpuRun, check_lse, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +40,8 @@ def check_sampled(g: GpuRun, q, k, v, perm, keep=None, sample_bh=SAMPLE_BH):
         h = min(h, wl.heads - 1)
         sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
         qt, kt, vt = (oracle.gather(sl(x), perm[b:b + 1], npf) for x in (q, k, v))
-        for ref, dev in ((qt, g.att.q_t), (kt, g.att.k_t), (tile_transposed(vt), g.att.vt_t)):
-            assert np.array_equal(to_bits(dev[b, h]), ref[0, 0])
+        for ref, dev in ((qt, g.att.q_t), (kfrag_layout(kt), g.att.k_f), (vfrag_layout(vt), g.att.v_f)):
+            assert np.array_equal(to_bits(dev[b, h]).reshape(ref.shape[2:]), ref[0, 0])
         qp, kp = oracle.pool(qt, npf), oracle.pool(kt, npf)
         assert np.array_equal(gq[b, h], qp[0, 0]) and np.array_equal(gk[b, h], kp[0, 0])
         n_exact, n_near = check_selection(gidx[b:b + 1, h:h + 1], qp, kp, keep)

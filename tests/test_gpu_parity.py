@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synthetic as S
-from parity import GpuRun, bits_to_f64, check_lse, check_output, check_selection, tile_transposed, to_bits
+from parity import GpuRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +59,8 @@ def test_path_matches_oracle(wl):
 
     # gather: exact copies
     qt, kt, vt = (oracle.gather(x, perm, npf) for x in (q, k, v))
-    for ref, dev in ((qt, g.att.q_t), (kt, g.att.k_t), (tile_transposed(vt), g.att.vt_t)):
-        assert np.array_equal(to_bits(dev), ref)
+    for ref, dev in ((qt, g.att.q_t), (kfrag_layout(kt), g.att.k_f), (vfrag_layout(vt), g.att.v_f)):
+        assert np.array_equal(to_bits(dev).reshape(ref.shape), ref)
 
     # plan: pooled means bit-exact, kept tiles exact outside near ties
     if wl.n_video:

@@ -17,7 +17,9 @@ the launch stream, and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -44,6 +46,24 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none or
+    the forward kernel's source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{re.sub(r'<.*', '', kernel)}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"sha256 \(first 16 hex\s+digits\): `([0-9a-f]{16})`", txt)
+    m_bytes = re.search(r"traffic_bytes_per_launch: (\d+)", txt)
+    if not (m_hash and m_bytes):
+        return None
+    src = os.path.join(ROOT, "block_sparse_attention_39_amd", "csrc", "forward.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != m_hash.group(1):
+        return None
+    return int(m_bytes.group(1))
 
 
 def cpu_baseline(wl, q, k, v, n_tiles: int):
@@ -159,6 +179,9 @@ def main():
     ms_step = float(np.mean(totals))
     F = wl.effective_flops()
     fwd_ms = float(np.mean(per_stage["forward"]))
+    # the forward stage is the attention kernel (plus a 4 us counter clear; a
+    # dense prefix adds the plain kernel for the prefix query tiles)
+    kernel = f"sparse_fwd_grouped_kernel<{wl.head_dim}>"
     achieved = F / (fwd_ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -178,9 +201,9 @@ def main():
                    "heads": wl.heads, "head_dim": wl.head_dim, "keep_tiles": wl.keep_tiles,
                    "tile": "dynamic" if wl.dynamic else "x".join(map(str, wl.tile)),
                    "effective_tflop_per_call": F / 1e12},
-        "roofline": {"bound": "mfma", "kernel": "sparse_fwd_kernel<128>" if wl.head_dim == 128 else
-                     "sparse_fwd_kernel<64>", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(kernel, wl.name)},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "skipped_tile_ratio": 1.0 - wl.keep_tiles / wl.n_video_tiles,

@@ -59,7 +59,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kRescaleLog2 = 8.0f;
+// A slice's weights are computed against the current reference maximum
+// without looking for the slice's own maximum; only when they add up to more
+// than 2^60 (some logit above the reference by ~60 in base 2, or the first
+// slice, whose reference is -1e30) is the true maximum taken, O and the
+// normaliser rescaled and the weights recomputed.  Weights up to 2^60 are exact
+// in float and bf16 and leave O and the normaliser far from overflow.
+constexpr float kOverflowSum = 1.152921504606846976e18f;  // 2^60
 constexpr int kGroups = 8;         // block groups of the grouped launch (one per XCD)
 constexpr int kMaxGroupSize = 64;  // blocks per group the start-of-round wait can track
 constexpr int kMaxSpin = 2000;     // bounded wait per round (x s_sleep 2)
@@ -142,9 +148,7 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
 
     bf16x8 kf[2][SD], vf[2][NV];
     f32x16 sacc[2];     // S^T of the slice the softmax works on next, per query half
-    bf16x8 pf[2][2];    // P^T of the previous slice, per query half and key half
-    bool need[2];
-    float alpha[2];
+    bf16x8 pf[2][2][2];  // P^T by step parity: [n & 1] holds P(n), per query half and key half
     f32x16 acc[OD][2];
 #pragma unroll
     for (int i = 0; i < OD; ++i) acc[i][0] = acc[i][1] = f32x16{};
@@ -163,7 +167,7 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
 #pragma unroll
         for (int s = 0; s < NV; ++s) vf[1][s] = bf16x8{};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pf[qb][0] = pf[qb][1] = bf16x8{};
+        for (int qb = 0; qb < 2; ++qb) pf[1][qb][0] = pf[1][qb][1] = bf16x8{};
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             sacc[qb] = f32x16{};
@@ -200,95 +204,99 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
             constexpr int NPV = 4 * OD;            // PV slots
             constexpr int NM = NPV + 2 * SD;       // all slots
             constexpr int QLEAD = 4;               // Q^T read lead, in slots
-            float mx[2], mt[2], neg_m[2], lrun[2];
+            constexpr int PPS = 8 / (2 * OD);      // weight pairs per PV slot: 1 (D = 128), 2 (D = 64)
+            constexpr int KEVERY = NPV / SD, VEVERY = 2 * SD / NV;
+            float neg_m[2], lrun[2];
             bf16x8 qv[2][SD];
             int qoff = lane * 16;
             asm("" : "+v"(qoff) : "s"(n));  // opaque: keeps the Q^T reads in the loop
 #pragma unroll
-            for (int g = 0; g < NM; ++g) {
-                // the Q^T fragment of the S MFMA QLEAD slots ahead
-                if (g + QLEAD >= NPV && g + QLEAD < NM) {
+            for (int qb = 0; qb < 2; ++qb) {
+                neg_m[qb] = vmask - m_ref[qb];
+                lrun[qb] = 0.f;
+            }
+            // PV slots: O[qb] += V(n-1) P(n-1)[qb], each MFMA followed by the
+            // next weights of S(n)[qb] (computed against the current reference
+            // maximum) and, every other slot, one fragment of K(n+2)
+#pragma unroll
+            for (int g = 0; g < NPV; ++g) {
+                if (g + QLEAD >= NPV) {
                     const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
                     qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
                 }
-                // the MFMA of this slot
-                if (g < NPV) {
-                    const int qb = g / (2 * OD), c = (g / OD) % 2, i = g % OD;
-                    acc[i][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[B ^ 1][2 * i + c], pf[qb][c],
-                                                                         acc[i][qb], 0, 0, 0);
-                } else {
-                    const int h = g - NPV, qb = h / SD, st = h % SD;
-                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ 1][st], qv[qb][st],
-                                                                       st == 0 ? f32x16{} : sacc[qb], 0, 0, 0);
-                }
-                // the softmax steps of this slot: 12 per query half, spread
-                // over the slots before the S products of that half
+                const int qb = g / (2 * OD), c = (g / OD) % 2, i = g % OD;
+                acc[i][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[B ^ 1][2 * i + c], pf[B ^ 1][qb][c],
+                                                                     acc[i][qb], 0, 0, 0);
 #pragma unroll
-                for (int u = 0; u < 24; ++u) {
-                    if ((u * (NPV + SD)) / 24 != g) continue;
-                    const int qb = u / 12, k = u % 12;
-                    const f32x16 sv = sacc[qb];
-                    if (k == 0) {
-                        float m = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-                        m = fmaxf(fmaxf(m, sv[3]), sv[4]);
-                        m = fmaxf(fmaxf(m, sv[5]), sv[6]);
-                        mx[qb] = fmaxf(fmaxf(m, sv[7]), sv[8]);
-                    } else if (k == 1) {
-                        float m = fmaxf(fmaxf(mx[qb], sv[9]), sv[10]);
-                        m = fmaxf(fmaxf(m, sv[11]), sv[12]);
-                        m = fmaxf(fmaxf(m, sv[13]), sv[14]);
-                        mx[qb] = fmaxf(m, sv[15]);
-                    } else if (k == 2) {
-                        mt[qb] = pair_max(mx[qb]) * c2 + vmask;
-                    } else if (k == 3) {
-                        need[qb] = __any(mt[qb] > m_ref[qb] + kRescaleLog2);
-                        const float m_new = need[qb] ? fmaxf(m_ref[qb], mt[qb]) : m_ref[qb];
-                        alpha[qb] = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-                        m_ref[qb] = m_new;
-                        neg_m[qb] = vmask - m_new;
-                        lrun[qb] = l_sum[qb] * alpha[qb];
-                    } else {
-                        const int r = 2 * (k - 4);
-                        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sv[r], c2, neg_m[qb])),
-                                          __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, neg_m[qb]))};
-                        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-                        lrun[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lrun[qb], false);
-                        pf[qb][r >> 3][r & 7] = pb[0];
-                        pf[qb][r >> 3][(r & 7) + 1] = pb[1];
-                        if (k == 11) {
-                            // keep the softmax here: without a use in this
-                            // block the compiler would sink it past the
-                            // rescale branch, away from the MFMAs
-                            asm("" : "+v"(pf[qb][0]), "+v"(pf[qb][1]), "+v"(lrun[qb]));
-                            l_sum[qb] = lrun[qb];
-                        }
-                    }
+                for (int j = 0; j < PPS; ++j) {
+                    const int r = 2 * (((g % (2 * OD)) * PPS) + j);
+                    const f32x16& sv = sacc[qb];
+                    const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sv[r], c2, neg_m[qb])),
+                                      __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, neg_m[qb]))};
+                    const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+                    lrun[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lrun[qb], false);
+                    pf[B][qb][r >> 3][r & 7] = pb[0];
+                    pf[B][qb][r >> 3][(r & 7) + 1] = pb[1];
                 }
-                // loads spread over the slots (a burst would stall the
-                // wave's issue): K(n+2) fragments into the buffer S(n) has
-                // finished with during the PV slots, V(n+1) into the buffer the
-                // PV products have finished with during the S slots
-                constexpr int KEVERY = NPV / SD, VEVERY = 2 * SD / NV;
-                if (g < NPV && g % KEVERY == 0) kf[B][g / KEVERY] = *(const bf16x8*)(kaddr + (g / KEVERY) * 1024);
-                if (g >= NPV && (g - NPV) % VEVERY == 0)
+                if (g % KEVERY == 0) kf[B][g / KEVERY] = *(const bf16x8*)(kaddr + (g / KEVERY) * 1024);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // overflow test per query half; rare: the slice's true maximum
+            // becomes the reference, O (all PV products of the half issued) and
+            // the normaliser are rescaled and the weights recomputed
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                // keep the weights above: without a use before the branch the
+                // compiler would sink them past it, away from the MFMAs
+                asm("" : "+v"(pf[B][qb][0]), "+v"(pf[B][qb][1]), "+v"(lrun[qb]));
+                int big = __builtin_amdgcn_readfirstlane((int)__any(!(lrun[qb] <= kOverflowSum)));
+                asm("" : "+s"(big));
+                if (big) {
+                    const f32x16& sv = sacc[qb];
+                    float m = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+                    for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, sv[e]), sv[e + 1]);
+                    m = fmaxf(m, sv[15]);
+                    const float m_new = fmaxf(m_ref[qb], pair_max(m) * c2 + vmask);
+                    const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+                    m_ref[qb] = m_new;
+                    l_sum[qb] *= alpha;
+#pragma unroll
+                    for (int i = 0; i < OD; ++i) acc[i][qb] *= alpha;
+                    const float nm = vmask - m_new;
+                    float l = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sv[r], c2, nm)),
+                                          __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, nm))};
+                        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+                        l = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l, false);
+                        pf[B][qb][r >> 3][r & 7] = pb[0];
+                        pf[B][qb][r >> 3][(r & 7) + 1] = pb[1];
+                    }
+                    lrun[qb] = l;
+                }
+                l_sum[qb] += lrun[qb];
+            }
+            // S slots: S(n+1)[qb] = K(n+1) Q^T[qb] (the weights of S(n) are
+            // done), Q^T fragments QLEAD slots ahead, V(n+1) into the buffer the
+            // PV products have finished with, every other slot
+#pragma unroll
+            for (int g = NPV; g < NM; ++g) {
+                if (g + QLEAD < NM) {
+                    const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
+                    qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
+                }
+                const int h = g - NPV, qb = h / SD, st = h % SD;
+                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ 1][st], qv[qb][st],
+                                                                   st == 0 ? f32x16{} : sacc[qb], 0, 0, 0);
+                if ((g - NPV) % VEVERY == 0)
                     vf[B ^ 1][(g - NPV) / VEVERY] = *(const bf16x8*)(vaddr + ((g - NPV) / VEVERY) * 1024);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
             t_v = t_k;
 
-            // rescale O (which now holds every slice up to n-1) to the new maxima
-            // (the branch tests an opaque copy of the flag so that the compiler
-            // does not merge the softmax's select on it into this branch)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                int nb = __builtin_amdgcn_readfirstlane((int)need[qb]);
-                asm("" : "+s"(nb));
-                if (nb) {
-#pragma unroll
-                    for (int i = 0; i < OD; ++i) acc[i][qb] *= alpha[qb];
-                }
-            }
         }
     }
 #undef TILE_AT

@@ -100,6 +100,38 @@ __device__ __attribute__((always_inline)) inline void load_frags(bf16x8 (&dst)[N
     for (int s = 0; s < N; ++s) dst[s] = *(const bf16x8*)(base + s * 1024);
 }
 
+// The rare path of the overflow test: the slice's true maximum (over the
+// lane pair that shares a query) becomes the reference, the accumulators of
+// the query half and its normaliser are rescaled, and the slice's weights are
+// recomputed.
+template <int OD>
+__device__ __attribute__((always_inline)) inline void rescale_slice(const f32x16& sv, float c2, float vmask,
+                                                                    float& m_ref, float& l_sum, f32x16 (&acc)[OD][2],
+                                                                    int qb, bf16x8 (&pf)[2], float& lrun,
+                                                                    bf16x2 ones) {
+    float m = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, sv[e]), sv[e + 1]);
+    m = fmaxf(m, sv[15]);
+    const float m_new = fmaxf(m_ref, pair_max(m) * c2 + vmask);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    l_sum *= alpha;
+#pragma unroll
+    for (int i = 0; i < OD; ++i) acc[i][qb] *= alpha;
+    const float nm = vmask - m_new;
+    float l = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sv[r], c2, nm)), __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, nm))};
+        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        l = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l, false);
+        pf[r >> 3][r & 7] = pb[0];
+        pf[r >> 3][(r & 7) + 1] = pb[1];
+    }
+    lrun = l;
+}
+
 // One query tile, all four waves of the block.  `vi` < 0 marks a prefix
 // (dense) query tile.
 template <int D>
@@ -177,13 +209,17 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
                     kf[0][s], *(const bf16x8*)(qlds + ((qb * SD + s) * 64 + lane) * 16), sacc[qb], 0, 0, 0);
         }
     }
-    int t_v = TILE_AT(1);  // tile whose V is loaded next
+    int t_v = TILE_AT(1);       // tile whose V is loaded next
+    int t_k_next = TILE_AT(2);  // tile whose K is loaded next
 
     for (int n0 = 0; n0 <= my_n; n0 += 2) {
 #pragma unroll
         for (int B = 0; B < 2; ++B) {
             const int n = n0 + B;
-            const int t_k = TILE_AT(n + 2);  // K(n+2) and, one step later, V(n+2)
+            const int t_k = t_k_next;  // K(n+2) and, one step later, V(n+2)
+            // the tile after it, read from LDS now and used at the end of the
+            // step (no wait for the read inside the step)
+            const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)];
             const uint8_t* const kaddr = kbh + (int64_t)t_k * TB;
             const uint8_t* const vaddr = vbh + (int64_t)t_v * TB;
 
@@ -241,48 +277,45 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
                 if (g % KEVERY == 0) kf[B][g / KEVERY] = *(const bf16x8*)(kaddr + (g / KEVERY) * 1024);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // overflow test per query half; rare: the slice's true maximum
-            // becomes the reference, O (all PV products of the half issued) and
-            // the normaliser are rescaled and the weights recomputed
+            // keep the weights above: without a use before the branches below
+            // the compiler would sink them past them, away from the MFMAs
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                // keep the weights above: without a use before the branch the
-                // compiler would sink them past it, away from the MFMAs
-                asm("" : "+v"(pf[B][qb][0]), "+v"(pf[B][qb][1]), "+v"(lrun[qb]));
-                int big = __builtin_amdgcn_readfirstlane((int)__any(!(lrun[qb] <= kOverflowSum)));
-                asm("" : "+s"(big));
-                if (big) {
-                    const f32x16& sv = sacc[qb];
-                    float m = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-                    for (int e = 3; e < 15; e += 2) m = fmaxf(fmaxf(m, sv[e]), sv[e + 1]);
-                    m = fmaxf(m, sv[15]);
-                    const float m_new = fmaxf(m_ref[qb], pair_max(m) * c2 + vmask);
-                    const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-                    m_ref[qb] = m_new;
-                    l_sum[qb] *= alpha;
-#pragma unroll
-                    for (int i = 0; i < OD; ++i) acc[i][qb] *= alpha;
-                    const float nm = vmask - m_new;
-                    float l = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sv[r], c2, nm)),
-                                          __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, nm))};
-                        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-                        l = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l, false);
-                        pf[B][qb][r >> 3][r & 7] = pb[0];
-                        pf[B][qb][r >> 3][(r & 7) + 1] = pb[1];
-                    }
-                    lrun[qb] = l;
-                }
-                l_sum[qb] += lrun[qb];
-            }
+            for (int qb = 0; qb < 2; ++qb) asm("" : "+v"(pf[B][qb][0]), "+v"(pf[B][qb][1]), "+v"(lrun[qb]));
+            // Overflow test of query half qb, just before the S products that
+            // overwrite its scores (for the second half, after the first half's
+            // S products: its weights are then long computed and the vote does
+            // not stall the wave).  Rare: the slice's true maximum becomes the
+            // reference, O (all PV products of the half issued) and the
+            // normaliser are rescaled and the weights recomputed.
+#define BSA_OVERFLOW_TEST(qb)                                                                              \
+    {                                                                                                      \
+        int big = __builtin_amdgcn_readfirstlane((int)__any(!(lrun[qb] <= kOverflowSum)));                 \
+        asm("" : "+s"(big));                                                                               \
+        if (big) rescale_slice<OD>(sacc[qb], c2, vmask, m_ref[qb], l_sum[qb], acc, qb, pf[B][qb], lrun[qb], ones); \
+        l_sum[qb] += lrun[qb];                                                                             \
+    }
+            BSA_OVERFLOW_TEST(0)
             // S slots: S(n+1)[qb] = K(n+1) Q^T[qb] (the weights of S(n) are
             // done), Q^T fragments QLEAD slots ahead, V(n+1) into the buffer the
             // PV products have finished with, every other slot
 #pragma unroll
-            for (int g = NPV; g < NM; ++g) {
+            for (int g = NPV; g < NPV + SD; ++g) {
+                if (g + QLEAD < NM) {
+                    const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
+                    qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
+                }
+                const int h = g - NPV, qb = h / SD, st = h % SD;
+                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ 1][st], qv[qb][st],
+                                                                   st == 0 ? f32x16{} : sacc[qb], 0, 0, 0);
+                if ((g - NPV) % VEVERY == 0)
+                    vf[B ^ 1][(g - NPV) / VEVERY] = *(const bf16x8*)(vaddr + ((g - NPV) / VEVERY) * 1024);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            BSA_OVERFLOW_TEST(1)
+#undef BSA_OVERFLOW_TEST
+#pragma unroll
+            for (int g = NPV + SD; g < NM; ++g) {
                 if (g + QLEAD < NM) {
                     const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
                     qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
@@ -296,6 +329,7 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
             }
 
             t_v = t_k;
+            t_k_next = __builtin_amdgcn_readfirstlane(t_after);
 
         }
     }

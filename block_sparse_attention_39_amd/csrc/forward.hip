@@ -132,43 +132,142 @@ __device__ __attribute__((always_inline)) inline void rescale_slice(const f32x16
     lrun = l;
 }
 
-// One query tile, all four waves of the block.  `vi` < 0 marks a prefix
-// (dense) query tile.
+// A query tile of the flattened work: (batch * heads + head, query tile
+// number counting the prefix tiles first, video tile number or -1 for a
+// prefix tile).
+struct Item {
+    int64_t bh;
+    int qt;
+    int vi;
+};
+
 template <int D>
-__device__ __attribute__((always_inline)) inline void attend_tile(const ForwardArgs& a, float* lds, int64_t bh,
-                                                                  int qt, int vi) {
+struct Regs {
+    static constexpr int QPT = 2 * Cfg<D>::SD * 64 / 256;  // Q^T fragment chunks per thread
+};
+constexpr int kListPre = 4;  // kept-list entries per thread fetched ahead of a tile
+
+// This wave's identity inside the block (the wave index is uniform).
+struct Wave {
+    int tid, wave, lane, par, kh, lr, hf;
+    __device__ Wave() {
+        tid = threadIdx.x;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        lane = tid & 63;
+        par = wave >> 1;
+        kh = wave & 1;
+        lr = lane & 31;
+        hf = lane >> 5;
+    }
+};
+
+__device__ inline int list_len(const ForwardArgs& a, const Item& it) {
+    return it.vi < 0 ? a.npt + a.nvt : a.npt + a.keep;
+}
+
+// The kept-list value behind list position j of a video query tile (read
+// from global memory; positions of the prefix read entry 0).
+__device__ inline int list_raw(const ForwardArgs& a, const Item& it, int j) {
+    if (it.vi < 0) return 0;  // prefix query tile: no list (and `idx` may be null)
+    return a.idx[(it.bh * a.nvt + it.vi) * (int64_t)a.keep + max(j - a.npt, 0)];
+}
+
+// Tile number of list position j given its raw kept-list value: prefix
+// tiles first (and every tile for a prefix query tile), kept video tiles
+// clamped into range so a corrupt list cannot address outside the tensors.
+__device__ inline int list_tile(const ForwardArgs& a, const Item& it, int j, int raw) {
+    return (it.vi < 0 || j < a.npt) ? j : a.npt + min(max(raw, 0), a.nvt - 1);
+}
+
+// Issue the loads a query tile starts with: this wave's K and V fragments of
+// its first slice and the K fragments of its second (tiles t0, t1), this
+// thread's chunks of the tile's Q^T fragments and its first kept-list entries.
+template <int D>
+__device__ __attribute__((always_inline)) inline void fetch_first(const ForwardArgs& a, const Item& it, int t0, int t1,
+                                                                  const Wave& w, bf16x8 (&kf)[2][Cfg<D>::SD],
+                                                                  bf16x8 (&vf)[2][Cfg<D>::NV],
+                                                                  u32x4 (&qpre)[Regs<D>::QPT], int (&lpre)[kListPre]) {
+    using CF = Cfg<D>;
+    constexpr int SD = CF::SD, TB = CF::TB;
+    const int n_tiles = a.npt + a.nvt;
+    const int64_t n_tot = (int64_t)n_tiles * kTile;
+    const uint8_t* kbh = (const uint8_t*)a.k + it.bh * (int64_t)n_tiles * TB + w.kh * CF::SLICE + w.lane * 16;
+    const uint8_t* vbh = (const uint8_t*)a.v + it.bh * (int64_t)n_tiles * TB + w.kh * CF::SLICE + w.lane * 16;
+    load_frags(kf[0], kbh + (int64_t)t0 * TB);
+    load_frags(vf[0], vbh + (int64_t)t0 * TB);
+    load_frags(kf[1], kbh + (int64_t)t1 * TB);
+    // Q^T operand fragment (query half qb, step s) of chunk f: lane holds
+    // query 32*qb + lr, channels 16*s + 8*hf .. +7
+#pragma unroll
+    for (int u = 0; u < Regs<D>::QPT; ++u) {
+        const int f = w.tid + 256 * u;
+        const int fl = f & 63, fs = (f >> 6) % SD, fq = f / (64 * SD);
+        const uint16_t* src =
+            a.q + (it.bh * n_tot + (int64_t)it.qt * kTile + 32 * fq + (fl & 31)) * D + 16 * fs + 8 * (fl >> 5);
+        qpre[u] = *(const u32x4*)src;
+    }
+#pragma unroll
+    for (int u = 0; u < kListPre; ++u) lpre[u] = 0;
+    if (it.vi >= 0) {
+        const int32_t* row = a.idx + (it.bh * a.nvt + it.vi) * (int64_t)a.keep;
+#pragma unroll
+        for (int u = 0; u < kListPre; ++u) {
+            const int e = w.tid + 256 * u;
+            if (e < a.keep) lpre[u] = row[e];
+        }
+    }
+}
+
+// One query tile, all four waves of the block, given the loads fetch_first
+// issued for it.  With `has_next`, the first loads of the block's next tile
+// `nx` are issued before this tile's epilogue, so that their latency overlaps
+// it.  `vi` < 0 marks a prefix (dense) query tile.
+template <int D>
+__device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs& a, float* lds, const Item& it,
+                                                               bool has_next, const Item& nx, const Wave& w,
+                                                               bf16x8 (&kf)[2][Cfg<D>::SD],
+                                                               bf16x8 (&vf)[2][Cfg<D>::NV],
+                                                               u32x4 (&qpre)[Regs<D>::QPT],
+                                                               int (&lpre)[kListPre]) {
     using CF = Cfg<D>;
     constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
-    const int par = wave >> 1, kh = wave & 1;
-    const int lr = lane & 31, hf = lane >> 5;
-
-    const bool dense = vi < 0;
-    const int n_iter = dense ? a.npt + a.nvt : a.npt + a.keep;
+    const int tid = w.tid, wave = w.wave, lane = w.lane, par = w.par, kh = w.kh, lr = w.lr, hf = w.hf;
+    const int64_t bh = it.bh;
+    const int qt = it.qt;
+    const bool dense = it.vi < 0;
+    const int n_iter = list_len(a, it);
     const int n_tiles = a.npt + a.nvt;
     const int64_t n_tot = (int64_t)n_tiles * kTile;
     int* list = (int*)lds;                            // key tile of every list position
     uint8_t* qlds = (uint8_t*)(lds + kMaxListTiles);  // Q^T fragments
 
+    // ---- stage the tile in LDS: its key-tile list and Q^T fragments ------
     __syncthreads();  // the previous query tile's epilogue is done with LDS
-    {
-        // prefix tiles first, then the kept video tiles (clamped into range so
-        // a corrupt list cannot address outside the tensors)
-        const int32_t* row = dense ? nullptr : a.idx + (bh * a.nvt + vi) * a.keep;
-        for (int j = tid; j < n_iter; j += 256)
-            list[j] = (dense || j < a.npt) ? j : a.npt + min(max(row[j - a.npt], 0), a.nvt - 1);
-        // Q^T operand fragment (query half qb, step s): lane holds query
-        // 32*qb + lr, channels 16*s + 8*hf .. +7
-        for (int f = tid; f < 2 * SD * 64; f += 256) {
-            const int fl = f & 63, fs = (f >> 6) % SD, fq = f / (64 * SD);
-            const uint16_t* src =
-                a.q + (bh * n_tot + (int64_t)qt * kTile + 32 * fq + (fl & 31)) * D + 16 * fs + 8 * (fl >> 5);
-            *(u32x4*)(qlds + f * 16) = *(const u32x4*)src;
+    if (dense) {
+        for (int j = tid; j < n_iter; j += 256) list[j] = j;
+    } else {
+        const int32_t* row = a.idx + (bh * a.nvt + it.vi) * (int64_t)a.keep;
+        for (int j = tid; j < a.npt; j += 256) list[j] = j;
+#pragma unroll
+        for (int u = 0; u < kListPre; ++u) {
+            const int e = tid + 256 * u;
+            if (e < a.keep) list[a.npt + e] = a.npt + min(max(lpre[u], 0), a.nvt - 1);
         }
+        for (int e = tid + 256 * kListPre; e < a.keep; e += 256)
+            list[a.npt + e] = a.npt + min(max(row[e], 0), a.nvt - 1);
     }
+#pragma unroll
+    for (int u = 0; u < Regs<D>::QPT; ++u) *(u32x4*)(qlds + (tid + 256 * u) * 16) = qpre[u];
     __syncthreads();
+
+    // the next tile's first two tile numbers for this wave, read now from
+    // global memory and used after the main loop
+    int n_iter_nx = 0, nraw0 = 0, nraw1 = 0;
+    if (has_next) {
+        n_iter_nx = list_len(a, nx);
+        nraw0 = list_raw(a, nx, min(par, n_iter_nx - 1));
+        nraw1 = list_raw(a, nx, min(par + 2, n_iter_nx - 1));
+    }
 
     const int my_n = (n_iter - par + 1) >> 1;  // slices of this wave
     // tile of this wave's slice n; positions past the end repeat the last one
@@ -178,8 +277,7 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     const uint8_t* kbh = (const uint8_t*)a.k + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
     const uint8_t* vbh = (const uint8_t*)a.v + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
 
-    bf16x8 kf[2][SD], vf[2][NV];
-    f32x16 sacc[2];     // S^T of the slice the softmax works on next, per query half
+    f32x16 sacc[2];      // S^T of the slice the softmax works on next, per query half
     bf16x8 pf[2][2][2];  // P^T by step parity: [n & 1] holds P(n), per query half and key half
     f32x16 acc[OD][2];
 #pragma unroll
@@ -189,25 +287,18 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     const float c2 = a.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // prologue: K(0), V(0), K(1) in flight; S(0); P(-1) = 0 against V(-1) = 0
-    {
-        const int t0 = TILE_AT(0);
-        const int t1 = TILE_AT(1);
-        load_frags(kf[0], kbh + (int64_t)t0 * TB);
-        load_frags(vf[0], vbh + (int64_t)t0 * TB);
-        load_frags(kf[1], kbh + (int64_t)t1 * TB);
+    // K(0), V(0), K(1) are in flight (fetch_first); S(0); P(-1) = 0 against V(-1) = 0
 #pragma unroll
-        for (int s = 0; s < NV; ++s) vf[1][s] = bf16x8{};
+    for (int s = 0; s < NV; ++s) vf[1][s] = bf16x8{};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pf[1][qb][0] = pf[1][qb][1] = bf16x8{};
+    for (int qb = 0; qb < 2; ++qb) pf[1][qb][0] = pf[1][qb][1] = bf16x8{};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            sacc[qb] = f32x16{};
+    for (int qb = 0; qb < 2; ++qb) {
+        sacc[qb] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < SD; ++s)
-                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    kf[0][s], *(const bf16x8*)(qlds + ((qb * SD + s) * 64 + lane) * 16), sacc[qb], 0, 0, 0);
-        }
+        for (int s = 0; s < SD; ++s)
+            sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                kf[0][s], *(const bf16x8*)(qlds + ((qb * SD + s) * 64 + lane) * 16), sacc[qb], 0, 0, 0);
     }
     int t_v = TILE_AT(1);       // tile whose V is loaded next
     int t_k_next = TILE_AT(2);  // tile whose K is loaded next
@@ -335,6 +426,14 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     }
 #undef TILE_AT
 
+
+    // ---- the next tile's first loads, in flight during this epilogue ------
+    if (has_next) {
+        const int t0 = list_tile(a, nx, min(par, n_iter_nx - 1), __builtin_amdgcn_readfirstlane(nraw0));
+        const int t1 = list_tile(a, nx, min(par + 2, n_iter_nx - 1), __builtin_amdgcn_readfirstlane(nraw1));
+        fetch_first<D>(a, nx, t0, t1, w, kf, vf, qpre, lpre);
+    }
+
     // ---- merge the four partial results of every query, normalise, store --
     float* merge = lds;                       // [4 waves][64 queries][MROW]
     float* mrow = lds + CF::MERGE;            // [4 waves][64] maxima
@@ -399,6 +498,21 @@ __device__ __attribute__((always_inline)) inline void attend_tile(const ForwardA
     }
 }
 
+// The first loads of a block's first tile (nothing to overlap them with).
+template <int D>
+__device__ __attribute__((always_inline)) inline void fetch_first_direct(const ForwardArgs& a, const Item& it,
+                                                                         const Wave& w,
+                                                                         bf16x8 (&kf)[2][Cfg<D>::SD],
+                                                                         bf16x8 (&vf)[2][Cfg<D>::NV],
+                                                                         u32x4 (&qpre)[Regs<D>::QPT],
+                                                                         int (&lpre)[kListPre]) {
+    const int n = list_len(a, it);
+    const int j0 = min(w.par, n - 1), j1 = min(w.par + 2, n - 1);
+    const int t0 = list_tile(a, it, j0, __builtin_amdgcn_readfirstlane(list_raw(a, it, j0)));
+    const int t1 = list_tile(a, it, j1, __builtin_amdgcn_readfirstlane(list_raw(a, it, j1)));
+    fetch_first<D>(a, it, t0, t1, w, kf, vf, qpre, lpre);
+}
+
 // Plain launch: block g handles query tile g of [prefix tiles of every (b,h)]
 // followed by [video tiles of every (b,h)], starting at tile `first`.
 template <int D>
@@ -407,13 +521,20 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
     __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::LDS_FLOATS];
     const int64_t g = first + blockIdx.x;
     const int64_t n_pref = (int64_t)a.BH * a.npt;
+    Item it;
     if (g < n_pref) {
-        attend_tile<D>(a, lds, g / a.npt, (int)(g % a.npt), -1);
+        it = Item{g / a.npt, (int)(g % a.npt), -1};
     } else {
         const int64_t gv = g - n_pref;
         const int vi = (int)(gv % a.nvt);
-        attend_tile<D>(a, lds, gv / a.nvt, a.npt + vi, vi);
+        it = Item{gv / a.nvt, a.npt + vi, vi};
     }
+    const Wave w;
+    bf16x8 kf[2][Cfg<D>::SD], vf[2][Cfg<D>::NV];
+    u32x4 qpre[Regs<D>::QPT];
+    int lpre[kListPre];
+    fetch_first_direct<D>(a, it, w, kf, vf, qpre, lpre);
+    run_tile<D>(a, lds, it, false, it, w, kf, vf, qpre, lpre);
 }
 
 // Grouped persistent launch over the video query tiles: block b belongs to
@@ -427,25 +548,39 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
     const int S = gridDim.x / kGroups;
     const int64_t n_items = (int64_t)a.BH * a.nvt;
     int* prog = progress + group * kMaxGroupSize;
-    for (int64_t r = 0;; ++r) {
-        const int64_t item = (r * kGroups + group) * S + slot;
-        if (item >= n_items) break;
-        // publish the round, then wait (bounded) until every block of the
-        // group has started it; the barrier at the start of the tile holds
-        // the other waves
-        if (threadIdx.x < 64) {
-            const int lane = threadIdx.x;
-            if (lane == 0) __hip_atomic_store(prog + slot, (int)r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int spin = 0; spin < kMaxSpin; ++spin) {
-                int v = INT_MAX;
-                if (lane < S) v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    auto item_of = [&](int64_t r) -> int64_t { return (r * kGroups + group) * S + slot; };
+    auto make = [&](int64_t item) -> Item {
+        return Item{item / a.nvt, a.npt + (int)(item % a.nvt), (int)(item % a.nvt)};
+    };
+    const Wave w;
+    bf16x8 kf[2][Cfg<D>::SD], vf[2][Cfg<D>::NV];
+    u32x4 qpre[Regs<D>::QPT];
+    int lpre[kListPre];
+    if (item_of(0) < n_items) {
+        Item cur = make(item_of(0));
+        fetch_first_direct<D>(a, cur, w, kf, vf, qpre, lpre);
+        for (int64_t r = 0;; ++r) {
+            // publish the round, then wait (bounded) until every block of the
+            // group has started it; the barrier at the start of the tile holds
+            // the other waves
+            if (threadIdx.x < 64) {
+                const int lane = threadIdx.x;
+                if (lane == 0) __hip_atomic_store(prog + slot, (int)r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int spin = 0; spin < kMaxSpin; ++spin) {
+                    int v = INT_MAX;
+                    if (lane < S) v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-                if (v >= (int)r) break;
-                __builtin_amdgcn_s_sleep(2);
+                    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+                    if (v >= (int)r) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
             }
+            const bool has_next = item_of(r + 1) < n_items;
+            const Item nx = has_next ? make(item_of(r + 1)) : cur;
+            run_tile<D>(a, lds, cur, has_next, nx, w, kf, vf, qpre, lpre);
+            if (!has_next) break;
+            cur = nx;
         }
-        attend_tile<D>(a, lds, item / a.nvt, a.npt + (int)(item % a.nvt), (int)(item % a.nvt));
     }
     // done: never hold the rest of the group back
     if (threadIdx.x == 0) __hip_atomic_store(prog + slot, INT_MAX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="prism720p")
     ap.add_argument("--keep", type=int, default=None, help="override kept tiles per query tile")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=96, help="query tiles in the CPU oracle sample")
+    ap.add_argument("--cpu-tiles", type=int, default=960, help="query tiles in the CPU oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()

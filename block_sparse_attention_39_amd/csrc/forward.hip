@@ -21,18 +21,23 @@
 //   V-fragment layouts of the C interface): every wave-wide 16-byte load reads
 //   1 KB contiguous and lands exactly in the operand registers, so K and V
 //   need no LDS; the Q^T fragments of the query tile are staged once in LDS.
-//   Each wave, one per SIMD, is software pipelined over its slices n:
-//     O += V(n-1) P(n-1) and S(n+1) = K(n+1) Q^T on the matrix cores while
-//     the softmax of S(n) -> P(n) runs on the vector ALU, with the loads of
-//     K(n+2) and V(n+1) spread over the step;
-//   the MFMAs and the softmax steps are issued alternately in a fixed order,
-//   since a single wave has no other wave on its SIMD to overlap with.
-//   The softmax works in base 2 (scale * log2 e folded into one FMA) and
-//   rescales the accumulators only when a row maximum grows by more than
-//   2^8, which is exact (the same reference maximum is used for O and for the
-//   normaliser).  The normaliser adds up the same bf16-rounded weights that
-//   enter the MFMA (v_dot2 with ones), so each output is a convex combination
-//   of V rows.
+//   Each wave, one per SIMD, is software pipelined over its slices n; a
+//   step is two windows of MFMA slots, one per query half h:
+//     window 0: O[1] += V(n-1) P(n-1)[1], S(n)[1] = K(n) Q^T[1], beside the
+//               softmax of S(n)[0] -> P(n)[0];
+//     window 1: O[0] += V(n) P(n)[0], S(n+1)[0] = K(n+1) Q^T[0], beside the
+//               softmax of S(n)[1] -> P(n)[1];
+//   with the loads of V(n+1) and K(n+2) in the S slots.  The MFMAs and the
+//   softmax instructions are issued alternately in a fixed order, since a
+//   single wave has no other wave on its SIMD to overlap with: one pair of
+//   weights per MFMA, its three stages (scaled logit, exp2, bf16 pair) in
+//   consecutive slots so that no instruction waits on the one before it.
+//   The softmax works in base 2 (scale * log2 e folded into one FMA).  Weights
+//   are taken against a running reference maximum and the accumulators are
+//   rescaled only when a slice's weights add up to more than 2^60 (exact: the
+//   same reference is used for O and for the normaliser).  The normaliser
+//   adds up the same bf16-rounded weights that enter the MFMA (v_dot2 with
+//   ones), so each output is a convex combination of V rows.
 //
 // Two launch forms:
 //   * plain: one block per query tile (prefix query tiles first: they are the
@@ -277,8 +282,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     const uint8_t* kbh = (const uint8_t*)a.k + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
     const uint8_t* vbh = (const uint8_t*)a.v + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
 
-    f32x16 sacc[2];      // S^T of the slice the softmax works on next, per query half
-    bf16x8 pf[2][2][2];  // P^T by step parity: [n & 1] holds P(n), per query half and key half
+    f32x16 sacc[2];   // S^T per query half: S(n)[0] and S(n)[1] in turn
+    bf16x8 pf[2][2];  // P^T per query half, by 16-key half
     f32x16 acc[OD][2];
 #pragma unroll
     for (int i = 0; i < OD; ++i) acc[i][0] = acc[i][1] = f32x16{};
@@ -287,19 +292,16 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     const float c2 = a.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // K(0), V(0), K(1) are in flight (fetch_first); S(0); P(-1) = 0 against V(-1) = 0
+    // K(0), V(0), K(1) are in flight (fetch_first).  S(0)[0] now; the first
+    // step's products with P(-1)[1] = 0 and V(-1) = 0 add nothing.
 #pragma unroll
     for (int s = 0; s < NV; ++s) vf[1][s] = bf16x8{};
+    pf[1][0] = pf[1][1] = bf16x8{};
+    sacc[0] = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) pf[1][qb][0] = pf[1][qb][1] = bf16x8{};
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < SD; ++s)
-            sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                kf[0][s], *(const bf16x8*)(qlds + ((qb * SD + s) * 64 + lane) * 16), sacc[qb], 0, 0, 0);
-    }
+    for (int s = 0; s < SD; ++s)
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s], *(const bf16x8*)(qlds + (s * 64 + lane) * 16),
+                                                          sacc[0], 0, 0, 0);
     int t_v = TILE_AT(1);       // tile whose V is loaded next
     int t_k_next = TILE_AT(2);  // tile whose K is loaded next
 
@@ -314,114 +316,132 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
             const uint8_t* const kaddr = kbh + (int64_t)t_k * TB;
             const uint8_t* const vaddr = vbh + (int64_t)t_v * TB;
 
-            // One step: 32 MFMA slots for D = 128 (16 for D = 64) in this
-            // order:
-            //   O[qb0] += V(n-1) P(n-1)[qb0];  O[qb1] += V(n-1) P(n-1)[qb1];
-            //   S(n+1)[qb0] = K(n+1) Q^T[qb0];  S(n+1)[qb1] = K(n+1) Q^T[qb1]
-            // and after every MFMA one step of the softmax of S(n) (first
-            // query half, then the second; each is done before the S(n+1)
-            // products that overwrite its input).  A scheduling fence after
-            // every slot keeps this order, so that the single wave of the SIMD
-            // feeds the matrix core and the vector ALU together.  The Q^T
+            // One step is two windows of 2*OD + SD MFMA slots (16 for
+            // D = 128), one per query half h of the softmax:
+            //   window 0: O[1] += V(n-1) P(n-1)[1];  S(n)[1] = K(n) Q^T[1]
+            //             (+ V(n+1) loads);  softmax of S(n)[0] -> P(n)[0]
+            //   window 1: O[0] += V(n) P(n)[0];      S(n+1)[0] = K(n+1) Q^T[0]
+            //             (+ K(n+2) loads);  softmax of S(n)[1] -> P(n)[1]
+            // so the softmax of a half runs beside products that neither
+            // write its scores nor read its weights, and P needs one buffer.
+            // The weights of a half go through three stages, a pair of
+            // elements at a time: scaled logit (FMA), exp2, and bf16 pair
+            // with the normaliser's dot product.  A pair's stages sit in
+            // consecutive slots, so no instruction waits on the one before
+            // it and the single wave of the SIMD keeps the matrix core busy.
+            // A scheduling fence after every slot holds this order; the Q^T
             // fragments are read from LDS a few slots ahead of their MFMA.
             // After the K-row order of the fragment layout, lane-half hf holds
             // keys 16*c + 8*hf + e of the slice at S[8*c + e].  Slices past
             // the end get -inf added to their logits (no branch).
             const float vmask = n < my_n ? 0.f : -INFINITY;
-            constexpr int NPV = 4 * OD;            // PV slots
-            constexpr int NM = NPV + 2 * SD;       // all slots
-            constexpr int QLEAD = 4;               // Q^T read lead, in slots
-            constexpr int PPS = 8 / (2 * OD);      // weight pairs per PV slot: 1 (D = 128), 2 (D = 64)
-            constexpr int KEVERY = NPV / SD, VEVERY = 2 * SD / NV;
-            float neg_m[2], lrun[2];
-            bf16x8 qv[2][SD];
+            constexpr int NPV = 2 * OD;           // PV slots of a window
+            constexpr int W = NPV + SD;           // slots of a window
+            constexpr int QLEAD = 4;              // Q^T read lead, in slots
+            constexpr int PPS = (8 + W - 4) / (W - 3);  // weight pairs per stage slot: 1 (D = 128), 2 (D = 64)
+            constexpr int NSA = 8 / PPS;          // stage slots of a window
+            constexpr int GSUM = NSA + 3;         // slot of the normaliser's dot products
+            static_assert(NPV >= QLEAD && NV == SD && NSA * PPS == 8 && GSUM < W, "window layout");
             int qoff = lane * 16;
             asm("" : "+v"(qoff) : "s"(n));  // opaque: keeps the Q^T reads in the loop
+            float lrun[2];
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                neg_m[qb] = vmask - m_ref[qb];
-                lrun[qb] = 0.f;
-            }
-            // PV slots: O[qb] += V(n-1) P(n-1)[qb], each MFMA followed by the
-            // next weights of S(n)[qb] (computed against the current reference
-            // maximum) and, every other slot, one fragment of K(n+2)
+            for (int h = 0; h < 2; ++h) {
+                // h = 0: PV of query half 1 and S of half 1 (this slice);
+                // h = 1: PV of half 0 and S of half 0 (next slice)
+                const int pq = 1 - h, sq = 1 - h;
+                const float neg_m = vmask - m_ref[h];
+                float xa[8][2], xe[8][2];
+                bf16x8 qv[SD];
 #pragma unroll
-            for (int g = 0; g < NPV; ++g) {
-                if (g + QLEAD >= NPV) {
-                    const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
-                    qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
+                for (int g = 0; g < W; ++g) {
+                    if (g + QLEAD >= NPV && g + QLEAD < W) {
+                        const int s2 = g + QLEAD - NPV;
+                        qv[s2] = *(const bf16x8*)(qlds + qoff + (sq * SD + s2) * 1024);
+                    }
+                    if (g < NPV) {
+                        const int c = g / OD, i = g % OD;
+                        // h = 0: V(n-1) in vf[B^1]; h = 1: V(n) in vf[B]
+                        acc[i][pq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[B ^ 1 ^ h][2 * i + c], pf[pq][c],
+                                                                             acc[i][pq], 0, 0, 0);
+                        asm volatile("" ::"v"(acc[i][pq][0]));  // keeps the MFMA in its slot
+                    } else {
+                        const int st = g - NPV;
+                        // h = 0: K(n) in kf[B]; h = 1: K(n+1) in kf[B^1]
+                        sacc[sq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ h][st], qv[st],
+                                                                           st == 0 ? f32x16{} : sacc[sq], 0, 0, 0);
+                        asm volatile("" ::"v"(sacc[sq][0]));
+                        if (h == 0)
+                            vf[B ^ 1][st] = *(const bf16x8*)(vaddr + st * 1024);  // V(n+1)
+                        else
+                            kf[B][st] = *(const bf16x8*)(kaddr + st * 1024);      // K(n+2)
+                    }
+                    // stage 1 (pairs of stage slot g-1): scaled logits of S(n)[h]
+                    if (g >= 1 && g - 1 < NSA) {
+#pragma unroll
+                        for (int u = 0; u < PPS; ++u) {
+                            const int p = (g - 1) * PPS + u, r = 2 * p;
+                            xa[p][0] = fmaf(sacc[h][r], c2, neg_m);
+                            xa[p][1] = fmaf(sacc[h][r + 1], c2, neg_m);
+                            asm volatile("" : "+v"(xa[p][0]), "+v"(xa[p][1]));
+                        }
+                    }
+                    // stage 2 (pairs of stage slot g-2): exp2
+                    if (g >= 2 && g - 2 < NSA) {
+#pragma unroll
+                        for (int u = 0; u < PPS; ++u) {
+                            const int p = (g - 2) * PPS + u;
+                            xe[p][0] = __builtin_amdgcn_exp2f(xa[p][0]);
+                            xe[p][1] = __builtin_amdgcn_exp2f(xa[p][1]);
+                            asm volatile("" : "+v"(xe[p][0]), "+v"(xe[p][1]));
+                        }
+                    }
+                    // stage 3 (pairs of stage slot g-3): the bf16 pair into P^T
+                    if (g >= 3 && g - 3 < NSA) {
+#pragma unroll
+                        for (int u = 0; u < PPS; ++u) {
+                            const int p = (g - 3) * PPS + u, r = 2 * p;
+                            const f32x2 pp = {xe[p][0], xe[p][1]};
+                            const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+                            pf[h][r >> 3][r & 7] = pb[0];
+                            pf[h][r >> 3][(r & 7) + 1] = pb[1];
+                            asm volatile("" : "+v"(pf[h][r >> 3]));
+                        }
+                    }
+                    // the normaliser: the same bf16 weights that enter the
+                    // MFMA, added up by v_dot2 with ones.  v_dot2 waits for the
+                    // matrix core to drain, so the eight of a half go together
+                    // in one slot (one wait, not eight).
+                    if (g == GSUM) {
+                        float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const int r = 2 * p;
+                            const bf16x2 pb = {pf[h][r >> 3][r & 7], pf[h][r >> 3][(r & 7) + 1]};
+                            if (p & 1)
+                                l1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l1, false);
+                            else
+                                l0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l0, false);
+                        }
+                        lrun[h] = l0 + l1;
+                        asm volatile("" : "+v"(lrun[h]));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                const int qb = g / (2 * OD), c = (g / OD) % 2, i = g % OD;
-                acc[i][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[B ^ 1][2 * i + c], pf[B ^ 1][qb][c],
-                                                                     acc[i][qb], 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < PPS; ++j) {
-                    const int r = 2 * (((g % (2 * OD)) * PPS) + j);
-                    const f32x16& sv = sacc[qb];
-                    const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sv[r], c2, neg_m[qb])),
-                                      __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, neg_m[qb]))};
-                    const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-                    lrun[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lrun[qb], false);
-                    pf[B][qb][r >> 3][r & 7] = pb[0];
-                    pf[B][qb][r >> 3][(r & 7) + 1] = pb[1];
-                }
-                if (g % KEVERY == 0) kf[B][g / KEVERY] = *(const bf16x8*)(kaddr + (g / KEVERY) * 1024);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // keep the weights above: without a use before the branches below
-            // the compiler would sink them past them, away from the MFMAs
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) asm("" : "+v"(pf[B][qb][0]), "+v"(pf[B][qb][1]), "+v"(lrun[qb]));
-            // Overflow test of query half qb, just before the S products that
-            // overwrite its scores (for the second half, after the first half's
-            // S products: its weights are then long computed and the vote does
-            // not stall the wave).  Rare: the slice's true maximum becomes the
-            // reference, O (all PV products of the half issued) and the
-            // normaliser are rescaled and the weights recomputed.
-#define BSA_OVERFLOW_TEST(qb)                                                                              \
-    {                                                                                                      \
-        int big = __builtin_amdgcn_readfirstlane((int)__any(!(lrun[qb] <= kOverflowSum)));                 \
-        asm("" : "+s"(big));                                                                               \
-        if (big) rescale_slice<OD>(sacc[qb], c2, vmask, m_ref[qb], l_sum[qb], acc, qb, pf[B][qb], lrun[qb], ones); \
-        l_sum[qb] += lrun[qb];                                                                             \
-    }
-            BSA_OVERFLOW_TEST(0)
-            // S slots: S(n+1)[qb] = K(n+1) Q^T[qb] (the weights of S(n) are
-            // done), Q^T fragments QLEAD slots ahead, V(n+1) into the buffer the
-            // PV products have finished with, every other slot
-#pragma unroll
-            for (int g = NPV; g < NPV + SD; ++g) {
-                if (g + QLEAD < NM) {
-                    const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
-                    qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
-                }
-                const int h = g - NPV, qb = h / SD, st = h % SD;
-                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ 1][st], qv[qb][st],
-                                                                   st == 0 ? f32x16{} : sacc[qb], 0, 0, 0);
-                if ((g - NPV) % VEVERY == 0)
-                    vf[B ^ 1][(g - NPV) / VEVERY] = *(const bf16x8*)(vaddr + ((g - NPV) / VEVERY) * 1024);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-
-            BSA_OVERFLOW_TEST(1)
-#undef BSA_OVERFLOW_TEST
-#pragma unroll
-            for (int g = NPV + SD; g < NM; ++g) {
-                if (g + QLEAD < NM) {
-                    const int h = g + QLEAD - NPV, q2 = h / SD, s2 = h % SD;
-                    qv[q2][s2] = *(const bf16x8*)(qlds + qoff + (q2 * SD + s2) * 1024);
-                }
-                const int h = g - NPV, qb = h / SD, st = h % SD;
-                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ 1][st], qv[qb][st],
-                                                                   st == 0 ? f32x16{} : sacc[qb], 0, 0, 0);
-                if ((g - NPV) % VEVERY == 0)
-                    vf[B ^ 1][(g - NPV) / VEVERY] = *(const bf16x8*)(vaddr + ((g - NPV) / VEVERY) * 1024);
-                __builtin_amdgcn_sched_barrier(0);
+                // Overflow test of half h before its weights are used (rare:
+                // the slice's true maximum becomes the reference, O of the
+                // half, all of whose products are issued, and the normaliser
+                // are rescaled and the weights recomputed).  The anchor keeps
+                // the weights ahead of the branch.
+                asm volatile("" : "+v"(pf[h][0]), "+v"(pf[h][1]), "+v"(lrun[h]));
+                int big = __builtin_amdgcn_readfirstlane((int)__any(!(lrun[h] <= kOverflowSum)));
+                asm("" : "+s"(big));
+                if (big) rescale_slice<OD>(sacc[h], c2, vmask, m_ref[h], l_sum[h], acc, h, pf[h], lrun[h], ones);
+                l_sum[h] += lrun[h];
             }
 
             t_v = t_k;
             t_k_next = __builtin_amdgcn_readfirstlane(t_after);
-
         }
     }
 #undef TILE_AT

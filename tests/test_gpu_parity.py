@@ -165,3 +165,38 @@ def test_grouped_and_plain_launch_agree(wl):
     g.run()
     assert np.array_equal(grouped[0], to_bits(g.att.o_t))
     assert np.array_equal(grouped[1], g.att.lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("growing", [True, False], ids=["growing", "shrinking"])
+def test_rescale_path_with_steep_logits(growing):
+    """Logits that change by ~50 (base 2) from one key tile to the next: with
+    growing logits nearly every slice of every wave overflows the running
+    reference and takes the rescale path; with shrinking ones the later
+    weights underflow to zero.  Both must match the exact fp64 oracle."""
+    wl = W("steep", 1, 2, 128, (8, 8, 16), 16, seed=41)
+    n, D = wl.n_video_tiles, wl.head_dim
+    perm = oracle.perm_static(wl.grid)
+    rng = np.random.default_rng(41)
+    qt = (1.0 + 0.1 * rng.standard_normal((1, 2, wl.n_video, D))).astype(np.float32)
+    tile_of_slot = np.arange(wl.n_video) // 64
+    ramp = 3.0 * (tile_of_slot if growing else (n - 1 - tile_of_slot))
+    kt = (ramp[None, None, :, None] + 0.1 * rng.standard_normal((1, 2, wl.n_video, D))).astype(np.float32)
+    vt = rng.standard_normal((1, 2, wl.n_video, D)).astype(np.float32)
+    # back to raster order so that the GPU gather produces exactly these tiles
+    def raster(x):
+        r = np.empty((1, wl.n_video, 2, D), np.float32)
+        r[0, perm] = x[0].transpose(1, 0, 2)
+        return S.to_bf16_bits(r)
+    q, k, v = raster(qt), raster(kt), raster(vt)
+    g = GpuRun(wl, q, k, v).run()
+    idx = g.block_idx()
+    assert np.all(idx == np.arange(n))  # k = n: every tile kept
+    qg, kg, vg = (oracle.gather(x, perm, 0) for x in (q, k, v))
+    got = to_bits(g.att.o_t)
+    lse = g.att.lse.cpu().numpy()
+    for h in range(2):
+        ref, ref_lse = oracle.attention(qg[0, h], kg[0, h], vg[0, h], 0, idx[0, h], float(np.float32(wl.scale)),
+                                        np.arange(n, dtype=np.int32))
+        check_output(got[0, h].reshape(n, 64, D), ref, f"h{h}")
+        check_lse(lse[0, h].reshape(n, 64), ref_lse, qg[0, h].reshape(n, 64, D), kg[0, h], float(np.float32(wl.scale)),
+                  f"lse h{h}")

@@ -68,6 +68,12 @@ def lib() -> ctypes.CDLL:
         L.orc_topk.restype = None
         L.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, f64, P, i32, P, P]
         L.orc_attention.restype = None
+        L.orc_attention_lse_delta.argtypes = [P, P, P, P, i32, i32, i32, i32, P, f64, P, P]
+        L.orc_attention_lse_delta.restype = None
+        L.orc_attention_backward_dq.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, f64, P, i32, P]
+        L.orc_attention_backward_dq.restype = None
+        L.orc_attention_backward_dkdv.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, f64, P, i32, P, P]
+        L.orc_attention_backward_dkdv.restype = None
         _lib = L
     return _lib
 
@@ -265,3 +271,65 @@ def reference(q_raster, k_raster, v_raster, *, grid, n_prefix: int, k: int, scal
     res.update(perm=perm, q_tiled=qt, k_tiled=kt, v_tiled=vt, qp=qp, kp=kp, idx=idx, s_k=s_k,
                s_k1=s_k1, mag=mag, o_tiled=o_t, lse=lse, o=o)
     return res
+
+
+def _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh):
+    q, kx, v, do = (_c(x, np.uint16) for x in (q_bh, k_bh, v_bh, do_bh))
+    Ntot, D = q.shape
+    nvt = (Ntot - n_prefix) // TILE
+    ix = _c(idx_bh, np.int32) if idx_bh is not None else np.zeros((0, 0), np.int32)
+    k = ix.shape[1] if ix.ndim == 2 else 0
+    return q, kx, v, do, Ntot, D, nvt, ix, k
+
+
+def lse_delta(q_bh, k_bh, v_bh, do_bh, n_prefix: int, idx_bh, scale: float):
+    """lse and Delta = dO . O of every query token of one (b,h) (tiled order):
+    ``(lse, delta)``, float64 ``[Ntot]`` each."""
+    q, kx, v, do, Ntot, D, nvt, ix, k = _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh)
+    lse = np.empty(Ntot, np.float64)
+    delta = np.empty(Ntot, np.float64)
+    lib().orc_attention_lse_delta(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), n_prefix, nvt, D, k, _ptr(ix),
+                                  float(scale), _ptr(lse), _ptr(delta))
+    return lse, delta
+
+
+def backward_dq(q_bh, k_bh, v_bh, do_bh, lse, delta, n_prefix: int, idx_bh, scale: float, qtiles):
+    """dQ of the query tiles ``qtiles`` of one (b,h): float64 ``[nq, 64, D]``."""
+    q, kx, v, do, Ntot, D, nvt, ix, k = _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh)
+    qt = _c(qtiles, np.int32)
+    out = np.empty((qt.shape[0], TILE, D), np.float64)
+    lib().orc_attention_backward_dq(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), _ptr(_c(lse, np.float64)),
+                                    _ptr(_c(delta, np.float64)), n_prefix, nvt, D, k, _ptr(ix), float(scale),
+                                    _ptr(qt), qt.shape[0], _ptr(out))
+    return out
+
+
+def backward_dkdv(q_bh, k_bh, v_bh, do_bh, lse, delta, n_prefix: int, idx_bh, scale: float, ktiles):
+    """dK and dV of the key tiles ``ktiles`` of one (b,h): two float64 ``[nk, 64, D]``."""
+    q, kx, v, do, Ntot, D, nvt, ix, k = _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh)
+    kt = _c(ktiles, np.int32)
+    dk = np.empty((kt.shape[0], TILE, D), np.float64)
+    dv = np.empty((kt.shape[0], TILE, D), np.float64)
+    lib().orc_attention_backward_dkdv(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), _ptr(_c(lse, np.float64)),
+                                      _ptr(_c(delta, np.float64)), n_prefix, nvt, D, k, _ptr(ix), float(scale),
+                                      _ptr(kt), kt.shape[0], _ptr(dk), _ptr(dv))
+    return dk, dv
+
+
+def backward_full(q_tiled, k_tiled, v_tiled, do_tiled, n_prefix: int, idx, scale: float):
+    """Gradients of every (b,h), tiled order: ``(dq, dk, dv)`` float64 ``[B,H,Ntot,D]``."""
+    B, H, Ntot, D = q_tiled.shape
+    tiles = np.arange(Ntot // TILE, dtype=np.int32)
+    dq = np.empty((B, H, Ntot, D), np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    for b in range(B):
+        for h in range(H):
+            ix = idx[b, h] if idx is not None else None
+            args = (q_tiled[b, h], k_tiled[b, h], v_tiled[b, h], do_tiled[b, h])
+            lse, delta = lse_delta(*args, n_prefix, ix, scale)
+            dq[b, h] = backward_dq(*args, lse, delta, n_prefix, ix, scale, tiles).reshape(Ntot, D)
+            gk, gv = backward_dkdv(*args, lse, delta, n_prefix, ix, scale, tiles)
+            dk[b, h] = gk.reshape(Ntot, D)
+            dv[b, h] = gv.reshape(Ntot, D)
+    return dq, dk, dv

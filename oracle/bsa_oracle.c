@@ -543,3 +543,179 @@ void orc_attention(const uint16_t *q, const uint16_t *kx, const uint16_t *v, int
         free(keys);
     }
 }
+
+/*
+ * Gradients of orc_attention's output with respect to q, k and v (one (b,h)),
+ * given dO = dL/dO.  This is the plain derivative of the function orc_attention
+ * computes (the pages give no backward; Prism's training speedup, in [Prism]
+ * section "같은 계산량 안에서 볼 곳을 고르는 Prism", needs it over the same kept
+ * lists).  For query q with key set S_q, z_qj = scale * (q . k_j),
+ * P_qj = exp(z_qj - lse_q), O_q = sum_j P_qj v_j:
+ *   Delta_q = dO_q . O_q,   dP_qj = dO_q . v_j,   dS_qj = P_qj (dP_qj - Delta_q),
+ *   dQ_q = scale * sum_{j in S_q} dS_qj k_j,
+ *   dK_j = scale * sum_{q : j in S_q} dS_qj q_q,
+ *   dV_j = sum_{q : j in S_q} P_qj dO_q.
+ */
+
+/* Key token list of query tile qt (as in orc_attention); returns the count. */
+static int64_t key_list(int qt, int n_prefix, int nvt, int k, const int32_t *idx, int64_t *keys)
+{
+    const int npt = n_prefix / TILE;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+    int64_t c = 0;
+    if (qt < npt) {
+        for (int64_t j = 0; j < Ntot; ++j)
+            keys[c++] = j;
+        return c;
+    }
+    const int i = qt - npt;
+    for (int64_t j = 0; j < n_prefix; ++j)
+        keys[c++] = j;
+    for (int t = 0; t < k; ++t) {
+        const int64_t base = n_prefix + (int64_t)idx[(int64_t)i * k + t] * TILE;
+        for (int r = 0; r < TILE; ++r)
+            keys[c++] = base + r;
+    }
+    return c;
+}
+
+/* Does query tile qt attend to key tile kt? */
+static int attends(int qt, int kt, int npt, int k, const int32_t *idx)
+{
+    if (qt < npt || kt < npt)
+        return 1;
+    const int32_t *row = idx + (int64_t)(qt - npt) * k;
+    for (int t = 0; t < k; ++t)
+        if (row[t] == kt - npt)
+            return 1;
+    return 0;
+}
+
+static double dot_bf16(const uint16_t *a, const uint16_t *b, int D)
+{
+    double s = 0.0;
+    for (int d = 0; d < D; ++d)
+        s += bf16_to_double(a[d]) * bf16_to_double(b[d]);
+    return s;
+}
+
+/*
+ * lse_q and Delta_q for every query token of one (b,h): O recomputed as in
+ * orc_attention.  lse, delta: [Ntot].
+ */
+void orc_attention_lse_delta(const uint16_t *q, const uint16_t *kx, const uint16_t *v, const uint16_t *dout,
+                             int n_prefix, int nvt, int D, int k, const int32_t *idx, double scale,
+                             double *lse, double *delta)
+{
+    const int npt = n_prefix / TILE;
+    const int ntiles = npt + nvt;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int qt = 0; qt < ntiles; ++qt) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)Ntot);
+        double *z = (double *)malloc(sizeof(double) * (size_t)Ntot);
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        const int64_t nk = key_list(qt, n_prefix, nvt, k, idx, keys);
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                z[j] = scale * dot_bf16(q + qi * D, kx + keys[j] * D, D);
+                if (z[j] > mx)
+                    mx = z[j];
+            }
+            double den = 0.0;
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const double w = exp(z[j] - mx);
+                den += w;
+                for (int d = 0; d < D; ++d)
+                    o[d] += w * bf16_to_double(v[keys[j] * D + d]);
+            }
+            double dl = 0.0;
+            for (int d = 0; d < D; ++d)
+                dl += bf16_to_double(dout[qi * D + d]) * (o[d] / den);
+            lse[qi] = mx + log(den);
+            delta[qi] = dl;
+        }
+        free(keys);
+        free(z);
+        free(o);
+    }
+}
+
+/*
+ * dQ of the query tiles qtiles[0..nq) (tiled tile numbers), given lse and
+ * Delta of every query token.  dq: [nq][64][D].
+ */
+void orc_attention_backward_dq(const uint16_t *q, const uint16_t *kx, const uint16_t *v, const uint16_t *dout,
+                               const double *lse, const double *delta, int n_prefix, int nvt, int D, int k,
+                               const int32_t *idx, double scale, const int32_t *qtiles, int nq, double *dq)
+{
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nq; ++a) {
+        const int qt = qtiles[a];
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)Ntot);
+        const int64_t nk = key_list(qt, n_prefix, nvt, k, idx, keys);
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            double *g = dq + ((int64_t)a * TILE + r) * D;
+            for (int d = 0; d < D; ++d)
+                g[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const uint16_t *kr = kx + keys[j] * D;
+                const double p = exp(scale * dot_bf16(q + qi * D, kr, D) - lse[qi]);
+                const double dp = dot_bf16(dout + qi * D, v + keys[j] * D, D);
+                const double ds = p * (dp - delta[qi]);
+                for (int d = 0; d < D; ++d)
+                    g[d] += ds * bf16_to_double(kr[d]);
+            }
+            for (int d = 0; d < D; ++d)
+                g[d] *= scale;
+        }
+        free(keys);
+    }
+}
+
+/*
+ * dK and dV of the key tiles ktiles[0..nk) (tiled tile numbers), given lse
+ * and Delta of every query token: every query of every query tile that
+ * attends the key tile contributes.  dk, dv: [nk][64][D].
+ */
+void orc_attention_backward_dkdv(const uint16_t *q, const uint16_t *kx, const uint16_t *v, const uint16_t *dout,
+                                 const double *lse, const double *delta, int n_prefix, int nvt, int D, int k,
+                                 const int32_t *idx, double scale, const int32_t *ktiles, int nk, double *dk,
+                                 double *dv)
+{
+    const int npt = n_prefix / TILE;
+    const int ntiles = npt + nvt;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nk; ++a) {
+        const int kt = ktiles[a];
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t kj = (int64_t)kt * TILE + r;
+            double *gk = dk + ((int64_t)a * TILE + r) * D;
+            double *gv = dv + ((int64_t)a * TILE + r) * D;
+            for (int d = 0; d < D; ++d)
+                gk[d] = gv[d] = 0.0;
+            for (int qt = 0; qt < ntiles; ++qt) {
+                if (!attends(qt, kt, npt, k, idx))
+                    continue;
+                for (int s = 0; s < TILE; ++s) {
+                    const int64_t qi = (int64_t)qt * TILE + s;
+                    const double p = exp(scale * dot_bf16(q + qi * D, kx + kj * D, D) - lse[qi]);
+                    const double dp = dot_bf16(dout + qi * D, v + kj * D, D);
+                    const double ds = p * (dp - delta[qi]);
+                    for (int d = 0; d < D; ++d) {
+                        gk[d] += ds * bf16_to_double(q[qi * D + d]);
+                        gv[d] += p * bf16_to_double(dout[qi * D + d]);
+                    }
+                }
+            }
+            for (int d = 0; d < D; ++d)
+                gk[d] *= scale;
+        }
+    }
+}

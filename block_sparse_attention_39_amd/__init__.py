@@ -8,11 +8,12 @@ ABI in ``include/bsa.h``; this package is the thin Python binding.
 """
 from ._lib import (EXPORTS, LIB_PATH, MAX_VIDEO_TILES, PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_VF, PERM_SCATTER,
                    TILE_DYNAMIC, TILE_STATIC, BsaError, Desc, lib)
-from .api import (BlockSparseAttention, forward, gather, gather_kf, gather_vf, make_desc, permute_build, plan, pooled_views,
-                  scatter, workspace_size)
+from .api import (BlockSparseAttention, backward, backward_workspace_size, forward, gather, gather_kf, gather_vf,
+                  make_desc, permute_build, plan, pooled_views, scatter, workspace_size)
 
 lib()  # fail at import if the HIP library was not built
 
-__all__ = ["BlockSparseAttention", "BsaError", "Desc", "EXPORTS", "LIB_PATH", "MAX_VIDEO_TILES", "forward",
+__all__ = ["BlockSparseAttention", "BsaError", "Desc", "EXPORTS", "LIB_PATH", "MAX_VIDEO_TILES", "backward",
+           "backward_workspace_size", "forward",
            "gather", "gather_kf", "gather_vf", "make_desc", "permute_build", "plan", "pooled_views", "scatter", "workspace_size",
            "PERM_BUILD", "PERM_GATHER", "PERM_GATHER_KF", "PERM_GATHER_VF", "PERM_SCATTER", "TILE_STATIC", "TILE_DYNAMIC"]

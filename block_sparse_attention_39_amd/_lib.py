@@ -18,7 +18,8 @@ PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_KF, PERM_GATHER_VF = 0, 1, 2,
 MAX_VIDEO_TILES = 8192
 MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
-EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_status_string", "bsa_version")
+EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_backward_workspace_size",
+           "bsa_backward", "bsa_status_string", "bsa_version")
 
 
 class Desc(ctypes.Structure):
@@ -54,10 +55,13 @@ def lib() -> ctypes.CDLL:
         L.bsa_permute.argtypes = [D, ctypes.c_int, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_plan.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_forward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.bsa_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        L.bsa_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_status_string.argtypes = [ctypes.c_int]
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_version.argtypes = []
-        for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_version"):
+        for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_backward_workspace_size",
+                  "bsa_backward", "bsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -99,6 +99,22 @@ def forward(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, w
                              _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws, _stream(stream)), "bsa_forward")
 
 
+def backward_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "bsa_backward_workspace_size")
+    return n.value
+
+
+def backward(desc: Desc, q, k, v, o, d_o, lse, perm, block_idx, dq, dk, dv, workspace, stream=None):
+    """Gradients of the forward: raster bf16 ``q, k, v, o, d_o`` ``[B, Ntot, H, D]``,
+    the forward's ``lse`` ``[B, H, Ntot]`` (tiled order), ``perm`` and ``block_idx``
+    -> raster bf16 ``dq, dk, dv``."""
+    ws = workspace.numel() * workspace.element_size()
+    _check(lib().bsa_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                              _ptr(perm), _ptr(block_idx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws,
+                              _stream(stream)), "bsa_backward")
+
+
 def pooled_views(desc: Desc, workspace):
     """(qbar, kbar) float views of the workspace after bsa_plan ([B, H, nVT, D])."""
     B, H, D = desc.batch, desc.heads, desc.head_dim

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
-SOURCES = ["bsa_api.cpp", "permute.hip", "shape.hip", "plan.hip", "forward.hip"]
+SOURCES = ["bsa_api.cpp", "permute.hip", "shape.hip", "plan.hip", "forward.hip", "backward.hip"]
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,7 +31,7 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 # per-file additions: the attention kernel keeps its MFMA accumulators in
 # ordinary VGPRs (its softmax rescales them with vector instructions, and the
 # accumulation registers then hold the operand fragments)
-EXTRA = {"forward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"forward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -1,0 +1,495 @@
+// Gradients of the kept-tile attention (dQ, dK, dV), bf16 MFMA on gfx950.
+//
+// What is differentiated: the function the forward computes ("Prism /
+// Kandinsky 6 speed ablation" page, section on Prism's block-sparse
+// attention, where the same sparsity also speeds up training; "Ref2VA VSA"
+// page, section on conditioning tokens, for the dense prefix).  For query q
+// with key set S_q, P_qj = exp(scale q.k_j - lse_q):
+//   Delta_q = dO_q . O_q,  dP_qj = dO_q . v_j,  dS_qj = P_qj (dP_qj - Delta_q),
+//   dQ_q = scale sum_j dS_qj k_j,  dK_j = scale sum_q dS_qj q_q,
+//   dV_j = sum_q P_qj dO_q.
+// P is recomputed from the forward's lse (no per-slice maximum is needed:
+// every exponent is at most 0).
+//
+// Work split (one block of 4 waves, one wave per SIMD, per tile):
+//   * dQ: one block per query tile, over its kept key tiles (the forward's
+//     list).  Wave (par, kh) takes list positions par, par + 2, ... and the
+//     32-key half kh of each; every wave holds all 64 queries.  Per slice:
+//       S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T (dP^T - Delta),
+//       dQ^T += K^T dS^T.
+//   * dK, dV: one block per key tile, over the query tiles that attend it (the
+//     prefix query tiles, and the video query tiles whose list holds the key
+//     tile: the transposed lists).  Wave (par, kh) takes list positions par,
+//     par + 2, ... and holds its 32-key half; per slice, for each 32-query half:
+//       S = Q K^T,  dP = dO V^T,  dS = P (dP - Delta),
+//       dV^T += dO^T P,  dK^T += Q^T dS.
+//   All products are v_mfma_f32_32x32x16_bf16 with the operands in the
+//   fragment layouts of the C interface (kfrag: rows of 32 tokens by 16
+//   channels; vfrag: 32 channels by 16 tokens), loaded straight into
+//   registers, 1 KB per wave-wide load; the stationary operand of a block is
+//   staged once in LDS.  The swap23 token order of the kfrag layout makes the
+//   accumulator rows a lane holds exactly the tokens it must supply as the
+//   next product's B operand, so P and dS go from accumulator to operand with
+//   a bf16 cast only.  The four waves' partial sums are added once per tile in
+//   LDS and written in raster order through the permutation.
+#include "bsa_kernels.h"
+
+namespace bsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxListTilesB = BSA_MAX_TILES;
+
+template <int D>
+struct BCfg {
+    static constexpr int SD = D / 16;         // kfrag loads (1 KB) of a 32-token half
+    static constexpr int OD = D / 32;         // 32-channel blocks
+    static constexpr int NV = 2 * OD;         // vfrag loads of a 32-token half
+    static constexpr int TB = kTile * D * 2;  // bytes of a tile in a fragment layout
+    static constexpr int HALF = TB / 2;       // bytes of a 32-token half
+    static constexpr int MROW = D + 4;        // merge row stride in floats
+    // stationary fragments: two operands x two 32-token halves x SD x 1 KB
+    static constexpr int STAT_FLOATS = 2 * 2 * SD * 256;
+    static constexpr int LOOP_FLOATS = kMaxListTilesB + STAT_FLOATS;
+    static constexpr int MERGE_FLOATS = 4 * 64 * MROW;
+    static constexpr int LDS_FLOATS = LOOP_FLOATS > MERGE_FLOATS ? LOOP_FLOATS : MERGE_FLOATS;
+};
+
+// token index l % 32 of a kfrag row (bits 2 and 3 exchanged)
+__device__ inline int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// raster token of tiled row `row` of batch b
+__device__ inline int64_t raster_token(const BackwardArgs& a, int b, int64_t row) {
+    return row < a.npf ? row : a.npf + a.perm[(int64_t)b * (a.n_tot - a.npf) + (row - a.npf)];
+}
+
+// one (batch, head) row of D bf16 channels, raster layout
+__device__ inline uint16_t* raster_row(uint16_t* base, const BackwardArgs& a, int64_t bh, int64_t tok, int D) {
+    const int64_t b = bh / a.H, h = bh % a.H;
+    return base + ((b * a.n_tot + tok) * a.H + h) * D;
+}
+
+// ---- Delta = dO . O and lse in base 2, per tiled row ----------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * n_tot + row
+    if (r >= (int64_t)a.BH * a.n_tot) return;
+    const int64_t bh = r / a.n_tot, row = r % a.n_tot;
+    const int b = (int)(bh / a.H);
+    const int64_t tok = raster_token(a, b, row);
+    const uint16_t* o = raster_row(const_cast<uint16_t*>(a.o), a, bh, tok, D);
+    const uint16_t* g = raster_row(const_cast<uint16_t*>(a.dout), a, bh, tok, D);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const bf16x8 x = *(const bf16x8*)(o + 8 * c), y = *(const bf16x8*)(g + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
+    }
+    a.delta[r] = s;
+    a.lse2[r] = a.lse[r] * kLog2e;
+}
+
+// ---- transposed lists: for each video key tile, the video query tiles that
+// kept it, ascending --------------------------------------------------------
+// bit j of row (bh, i): video query tile i kept video key tile j
+__global__ __launch_bounds__(256) void bwd_mask_kernel(BackwardArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * nvt + i
+    if (r >= (int64_t)a.BH * a.nvt) return;
+    uint32_t* row = a.mask + r * a.mwords;
+    for (int w = 0; w < a.mwords; ++w) row[w] = 0u;
+    const int32_t* ix = a.idx + r * a.keep;
+    for (int t = 0; t < a.keep; ++t) {
+        const int j = min(max(ix[t], 0), a.nvt - 1);
+        row[j >> 5] |= 1u << (j & 31);
+    }
+}
+
+// cnt[bh][j] = number of video query tiles that kept j
+__global__ __launch_bounds__(256) void bwd_tcount_kernel(BackwardArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * nvt + j
+    if (r >= (int64_t)a.BH * a.nvt) return;
+    const int64_t bh = r / a.nvt;
+    const int j = (int)(r % a.nvt);
+    const uint32_t* m = a.mask + bh * a.nvt * a.mwords + (j >> 5);
+    int c = 0;
+    for (int i = 0; i < a.nvt; ++i) c += (m[(int64_t)i * a.mwords] >> (j & 31)) & 1u;
+    a.cnt[r] = c;
+}
+
+// rowp[bh][0..nvt]: exclusive prefix sums of the counts (one block per bh)
+__global__ __launch_bounds__(256) void bwd_tscan_kernel(BackwardArgs a) {
+    __shared__ int part[256];
+    int* rp = a.rowp + (int64_t)blockIdx.x * (a.nvt + 1);
+    const int* cn = a.cnt + (int64_t)blockIdx.x * a.nvt;
+    const int t = threadIdx.x;
+    const int per = (a.nvt + 255) / 256;
+    const int lo = min(t * per, a.nvt), hi = min(lo + per, a.nvt);
+    int s = 0;
+    for (int j = lo; j < hi; ++j) s += cn[j];
+    part[t] = s;
+    __syncthreads();
+    if (t == 0) {
+        int run = 0;
+        for (int u = 0; u < 256; ++u) {
+            const int v = part[u];
+            part[u] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    int run = part[t];
+    for (int j = lo; j < hi; ++j) {
+        rp[j] = run;
+        run += cn[j];
+    }
+    if (t == 255) rp[a.nvt] = run;
+}
+
+__global__ __launch_bounds__(256) void bwd_tfill_kernel(BackwardArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * nvt + j
+    if (r >= (int64_t)a.BH * a.nvt) return;
+    const int64_t bh = r / a.nvt;
+    const int j = (int)(r % a.nvt);
+    const uint32_t* m = a.mask + bh * a.nvt * a.mwords + (j >> 5);
+    int32_t* out = a.tlist + bh * (int64_t)a.nvt * a.keep + a.rowp[bh * (a.nvt + 1) + j];
+    int p = 0;
+    for (int i = 0; i < a.nvt; ++i)
+        if ((m[(int64_t)i * a.mwords] >> (j & 31)) & 1u) out[p++] = i;
+}
+
+// ---- shared pieces of the two gradient kernels -----------------------------
+struct WaveId {
+    int tid, wave, lane, par, kh, lr, hf;
+    __device__ WaveId() {
+        tid = threadIdx.x;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        lane = tid & 63;
+        par = wave >> 1;
+        kh = wave & 1;
+        lr = lane & 31;
+        hf = lane >> 5;
+    }
+};
+
+template <int N>
+__device__ __attribute__((always_inline)) inline void load_n(bf16x8 (&dst)[N], const uint8_t* base) {
+#pragma unroll
+    for (int s = 0; s < N; ++s) dst[s] = *(const bf16x8*)(base + s * 1024);
+}
+
+// bf16 pair of accumulator elements r, r + 1 into a B-operand fragment pair
+__device__ inline void put_pair(bf16x8 (&f)[2], int r, float x, float y) {
+    const bf16x2 pb = __builtin_convertvector((f32x2){x, y}, bf16x2);
+    f[r >> 3][r & 7] = pb[0];
+    f[r >> 3][(r & 7) + 1] = pb[1];
+}
+
+// Adds the four waves' 32x32 fragments of a [64 rows][D] result through LDS
+// and writes it, times `mul`, as bf16 rows of the raster output.  acc[i][g]:
+// rows 32*i + (accumulator row) of the channels, column = token
+// 32*g + swap23(lr) for the given token-half owner map.  `own` gives, per wave
+// w, the token half (0/1) whose columns it holds in acc[.][0] (and 1 - own in
+// acc[.][1] when it holds both halves: both = true).
+template <int D>
+__device__ __attribute__((always_inline)) inline void merge_store(float* lds, const f32x16 (&acc)[D / 32][2],
+                                                                  bool both, const WaveId& w, float mul,
+                                                                  const BackwardArgs& a, int64_t bh, int tile,
+                                                                  uint16_t* out) {
+    constexpr int OD = D / 32, MROW = BCfg<D>::MROW;
+    float* merge = lds;  // [4 waves][64 tokens][MROW]
+    __syncthreads();     // everyone is done with the loop's LDS
+    {
+        float* mine = merge + w.wave * 64 * MROW;
+        // zero this wave's area when it holds only one half
+        if (!both)
+            for (int u = w.lane; u < 64 * MROW; u += 64) mine[u] = 0.f;
+        const int ng = both ? 2 : 1;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if (g >= ng) break;
+            const int half = both ? g : w.kh;
+            const int tok = 32 * half + swap23(w.lr);
+#pragma unroll
+            for (int i = 0; i < OD; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 v = {acc[i][g][4 * j], acc[i][g][4 * j + 1], acc[i][g][4 * j + 2], acc[i][g][4 * j + 3]};
+                    *(f32x4*)(mine + tok * MROW + 32 * i + 8 * j + 4 * w.hf) = v;
+                }
+        }
+    }
+    __syncthreads();
+    constexpr int C = D / 8;
+    const int b = (int)(bh / a.H);
+#pragma unroll
+    for (int u = 0; u < kTile * C / 256; ++u) {
+        const int cidx = w.tid + 256 * u;
+        const int r = cidx / C, c = cidx % C;
+        f32x4 s0 = *(const f32x4*)(merge + r * MROW + 8 * c);
+        f32x4 s1 = *(const f32x4*)(merge + r * MROW + 8 * c + 4);
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            s0 += *(const f32x4*)(merge + (q * 64 + r) * MROW + 8 * c);
+            s1 += *(const f32x4*)(merge + (q * 64 + r) * MROW + 8 * c + 4);
+        }
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const bf16x2 lo = __builtin_convertvector((f32x2){s0[2 * e] * mul, s0[2 * e + 1] * mul}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector((f32x2){s1[2 * e] * mul, s1[2 * e + 1] * mul}, bf16x2);
+            pk[e] = __builtin_bit_cast(uint32_t, lo);
+            pk[2 + e] = __builtin_bit_cast(uint32_t, hi);
+        }
+        const int64_t tok = raster_token(a, b, (int64_t)tile * kTile + r);
+        *(u32x4*)(raster_row(out, a, bh, tok, D) + 8 * c) = pk;
+    }
+}
+
+// ---- dQ ---------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(BackwardArgs a) {
+    using CF = BCfg<D>;
+    constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
+    __shared__ __attribute__((aligned(16))) float lds[CF::LDS_FLOATS];
+    const WaveId w;
+    const int n_tiles = a.npt + a.nvt;
+    const int64_t bh = blockIdx.x / n_tiles;
+    const int qt = (int)(blockIdx.x % n_tiles);
+    const bool dense = qt < a.npt;
+    const int n_iter = dense ? n_tiles : a.npt + a.keep;
+    int* list = (int*)lds;
+    uint8_t* qlds = (uint8_t*)(lds + kMaxListTilesB);   // Q^T fragments [2][SD][64][16 B]
+    uint8_t* glds = qlds + 2 * SD * 1024;                // dO^T fragments, same layout
+
+    // ---- stage: the key-tile list and the stationary Q^T, dO^T ---------------
+    if (dense) {
+        for (int j = w.tid; j < n_iter; j += 256) list[j] = j;
+    } else {
+        const int32_t* row = a.idx + (bh * a.nvt + (qt - a.npt)) * (int64_t)a.keep;
+        for (int j = w.tid; j < a.npt; j += 256) list[j] = j;
+        for (int e = w.tid; e < a.keep; e += 256) list[a.npt + e] = a.npt + min(max(row[e], 0), a.nvt - 1);
+    }
+    {
+        const uint8_t* qsrc = (const uint8_t*)a.q_kf + (bh * n_tiles + qt) * (int64_t)TB;
+        const uint8_t* gsrc = (const uint8_t*)a.do_kf + (bh * n_tiles + qt) * (int64_t)TB;
+        for (int u = w.tid; u < TB / 16; u += 256) {
+            *(u32x4*)(qlds + u * 16) = *(const u32x4*)(qsrc + u * 16);
+            *(u32x4*)(glds + u * 16) = *(const u32x4*)(gsrc + u * 16);
+        }
+    }
+    __syncthreads();
+
+    // this lane's queries: 32*qb + swap23(lr) (the Q^T column order of kfrag)
+    float lse2[2], dlt[2];
+    {
+        const int64_t base = bh * (int64_t)a.n_tot + (int64_t)qt * kTile;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            lse2[qb] = a.lse2[base + 32 * qb + swap23(w.lr)];
+            dlt[qb] = a.delta[base + 32 * qb + swap23(w.lr)];
+        }
+    }
+    const float c2 = a.scale_log2;
+    const int my_n = (n_iter - w.par + 1) >> 1;
+    const uint8_t* kkb = (const uint8_t*)a.k_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + w.lane * 16;
+    const uint8_t* vkb = (const uint8_t*)a.v_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + w.lane * 16;
+    const uint8_t* kvb = (const uint8_t*)a.k_vf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + w.lane * 16;
+    auto tile_at = [&](int n) { return __builtin_amdgcn_readfirstlane(list[min(w.par + 2 * n, n_iter - 1)]); };
+
+    f32x16 acc[OD][2];
+#pragma unroll
+    for (int i = 0; i < OD; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    bf16x8 kk[2][SD], vk[2][SD], kv[2][NV];
+    {
+        const int t0 = tile_at(0);
+        load_n(kk[0], kkb + (int64_t)t0 * TB);
+        load_n(vk[0], vkb + (int64_t)t0 * TB);
+        load_n(kv[0], kvb + (int64_t)t0 * TB);
+    }
+    for (int n0 = 0; n0 < my_n; n0 += 2) {
+#pragma unroll
+        for (int B = 0; B < 2; ++B) {
+            const int n = n0 + B;
+            if (B == 1 && n >= my_n) break;
+            {   // the next slice's operands into the other buffers
+                const int tn = tile_at(n + 1);
+                load_n(kk[B ^ 1], kkb + (int64_t)tn * TB);
+                load_n(vk[B ^ 1], vkb + (int64_t)tn * TB);
+                load_n(kv[B ^ 1], kvb + (int64_t)tn * TB);
+            }
+            bf16x8 dsf[2][2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                for (int st = 0; st < SD; ++st) {
+                    const bf16x8 qf = *(const bf16x8*)(qlds + ((qb * SD + st) * 64 + w.lane) * 16);
+                    const bf16x8 gf = *(const bf16x8*)(glds + ((qb * SD + st) * 64 + w.lane) * 16);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[B][st], qf, s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vk[B][st], gf, dp, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2[qb]));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -lse2[qb]));
+                    put_pair(dsf[qb], r, p0 * (dp[r] - dlt[qb]), p1 * (dp[r + 1] - dlt[qb]));
+                }
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int i = 0; i < OD; ++i)
+                        acc[i][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[B][2 * i + c], dsf[qb][c], acc[i][qb],
+                                                                             0, 0, 0);
+        }
+    }
+    merge_store<D>(lds, acc, true, w, a.scale, a, bh, qt, a.dq);
+}
+
+// ---- dK, dV -----------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BackwardArgs a) {
+    using CF = BCfg<D>;
+    constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
+    __shared__ __attribute__((aligned(16))) float lds[CF::LDS_FLOATS];
+    const WaveId w;
+    const int n_tiles = a.npt + a.nvt;
+    const int64_t bh = blockIdx.x / n_tiles;
+    const int kt = (int)(blockIdx.x % n_tiles);
+    int* list = (int*)lds;
+    uint8_t* klds = (uint8_t*)(lds + kMaxListTilesB);   // K fragments of the tile [2][SD][64][16 B]
+    uint8_t* vlds = klds + 2 * SD * 1024;                // V fragments, same layout
+
+    // ---- stage: the query-tile list and the stationary K, V fragments --------
+    int n_iter;
+    if (kt < a.npt) {
+        n_iter = n_tiles;
+        for (int j = w.tid; j < n_iter; j += 256) list[j] = j;
+    } else {
+        const int j = kt - a.npt;
+        const int lo = a.rowp[bh * (a.nvt + 1) + j], hi = a.rowp[bh * (a.nvt + 1) + j + 1];
+        const int32_t* tl = a.tlist + bh * (int64_t)a.nvt * a.keep;
+        n_iter = a.npt + (hi - lo);
+        for (int u = w.tid; u < a.npt; u += 256) list[u] = u;
+        for (int u = w.tid; u < hi - lo; u += 256) list[a.npt + u] = a.npt + min(max(tl[lo + u], 0), a.nvt - 1);
+    }
+    n_iter = __builtin_amdgcn_readfirstlane(n_iter);
+    {
+        const uint8_t* ksrc = (const uint8_t*)a.k_kf + (bh * n_tiles + kt) * (int64_t)TB;
+        const uint8_t* vsrc = (const uint8_t*)a.v_kf + (bh * n_tiles + kt) * (int64_t)TB;
+        for (int u = w.tid; u < TB / 16; u += 256) {
+            *(u32x4*)(klds + u * 16) = *(const u32x4*)(ksrc + u * 16);
+            *(u32x4*)(vlds + u * 16) = *(const u32x4*)(vsrc + u * 16);
+        }
+    }
+    __syncthreads();
+
+    const float c2 = a.scale_log2;
+    const int my_n = (n_iter - w.par + 1) >> 1;
+    const uint8_t* qkb = (const uint8_t*)a.q_kf + bh * (int64_t)n_tiles * TB + w.lane * 16;
+    const uint8_t* gkb = (const uint8_t*)a.do_kf + bh * (int64_t)n_tiles * TB + w.lane * 16;
+    const uint8_t* qvb = (const uint8_t*)a.q_vf + bh * (int64_t)n_tiles * TB + w.lane * 16;
+    const uint8_t* gvb = (const uint8_t*)a.do_vf + bh * (int64_t)n_tiles * TB + w.lane * 16;
+    auto tile_at = [&](int n) { return __builtin_amdgcn_readfirstlane(list[min(w.par + 2 * n, n_iter - 1)]); };
+
+    // this wave's key half kh: B-operand fragments of K^T and V^T from LDS
+    const uint8_t* kown = klds + (w.kh * SD * 64 + w.lane) * 16;
+    const uint8_t* vown = vlds + (w.kh * SD * 64 + w.lane) * 16;
+
+    f32x16 dk[OD][2], dv[OD][2];  // [.][0] used; [.][1] keeps merge_store's shape
+#pragma unroll
+    for (int i = 0; i < OD; ++i) dk[i][0] = dk[i][1] = dv[i][0] = dv[i][1] = f32x16{};
+
+    for (int n = 0; n < my_n; ++n) {
+        const int tq = tile_at(n);
+        const int64_t qrow = bh * (int64_t)a.n_tot + (int64_t)tq * kTile;
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+            const int64_t off = (int64_t)tq * TB + qh * CF::HALF;
+            bf16x8 qk[SD], gk[SD], qv[NV], gv[NV];
+            load_n(qk, qkb + off);
+            load_n(gk, gkb + off);
+            load_n(qv, qvb + off);
+            load_n(gv, gvb + off);
+            // lse and Delta of the rows this lane holds: queries
+            // 32*qh + 16*c + 8*hf + e, c = 0, 1, e = 0..7
+            float l2[16], dl[16];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int64_t r0 = qrow + 32 * qh + 16 * c + 8 * w.hf;
+                const f32x4 a0 = *(const f32x4*)(a.lse2 + r0), a1 = *(const f32x4*)(a.lse2 + r0 + 4);
+                const f32x4 d0 = *(const f32x4*)(a.delta + r0), d1 = *(const f32x4*)(a.delta + r0 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    l2[8 * c + e] = a0[e];
+                    l2[8 * c + 4 + e] = a1[e];
+                    dl[8 * c + e] = d0[e];
+                    dl[8 * c + 4 + e] = d1[e];
+                }
+            }
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int st = 0; st < SD; ++st) {
+                const bf16x8 kf = *(const bf16x8*)(kown + st * 1024);
+                const bf16x8 vf = *(const bf16x8*)(vown + st * 1024);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk[st], kf, s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gk[st], vf, dp, 0, 0, 0);
+            }
+            // accumulator element j holds query 32*qh + 16*(j/8) + 8*hf + j%8
+            bf16x8 pf[2], dsf[2];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[r]));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -l2[r + 1]));
+                put_pair(pf, r, p0, p1);
+                put_pair(dsf, r, p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < OD; ++i) {
+                    dv[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gv[2 * i + c], pf[c], dv[i][0], 0, 0, 0);
+                    dk[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[2 * i + c], dsf[c], dk[i][0], 0, 0, 0);
+                }
+        }
+    }
+    merge_store<D>(lds, dk, false, w, a.scale, a, bh, kt, a.dk);
+    merge_store<D>(lds, dv, false, w, 1.f, a, bh, kt, a.dv);
+}
+
+template <int D>
+hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.BH * a.n_tot;
+    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+    if (a.nvt > 0) {
+        const int64_t vt = (int64_t)a.BH * a.nvt;
+        const unsigned g = (unsigned)((vt + 255) / 256);
+        hipLaunchKernelGGL(bwd_mask_kernel, dim3(g), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_tcount_kernel, dim3(g), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_tscan_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_tfill_kernel, dim3(g), dim3(256), 0, s, a);
+    }
+    const int64_t tiles = (int64_t)a.BH * (a.npt + a.nvt);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, int D, hipStream_t s) {
+    if ((int64_t)a.BH * (a.npt + a.nvt) == 0) return hipSuccess;
+    return D == 128 ? launch_backward_d<128>(a, s) : launch_backward_d<64>(a, s);
+}
+
+}  // namespace bsa

@@ -94,6 +94,35 @@ Layout layout(const Geo& g) {
 
 bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LAUNCH; }
 
+// Workspace of bsa_backward: the seven fragment-layout copies, then the
+// per-row lse (base 2) and Delta, then the transposed lists.
+struct BwdLayout {
+    size_t frag[7], lse2, delta, mask, cnt, rowp, tlist, total;
+    int mwords;
+};
+
+BwdLayout bwd_layout(const Geo& g) {
+    BwdLayout L{};
+    const size_t t = align_up((size_t)g.BH * g.n_tot * g.D * 2);
+    size_t o = 0;
+    for (int i = 0; i < 7; ++i, o += t) L.frag[i] = o;
+    L.lse2 = o;
+    o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
+    L.delta = o;
+    o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
+    L.mwords = (int)((g.nvt + 31) / 32);
+    L.mask = o;
+    o += align_up((size_t)g.BH * g.nvt * L.mwords * sizeof(uint32_t));
+    L.cnt = o;
+    o += align_up((size_t)g.BH * g.nvt * sizeof(int32_t));
+    L.rowp = o;
+    o += align_up((size_t)g.BH * (g.nvt + 1) * sizeof(int32_t));
+    L.tlist = o;
+    o += align_up((size_t)g.BH * g.nvt * g.k * sizeof(int32_t));
+    L.total = o;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +259,83 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
     a.keep = (int)g.k;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+bsa_status bsa_backward_workspace_size(const bsa_desc* desc, size_t* bytes) {
+    if (!bytes) return BSA_ERR_NULL;
+    Geo g;
+    const bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    *bytes = bwd_layout(g).total;
+    return BSA_OK;
+}
+
+bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                        const void* d_o, const float* lse, const int32_t* perm, const int32_t* block_idx, void* dq,
+                        void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.npt + g.nvt > BSA_MAX_TILES || g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.empty) return BSA_OK;
+    if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return BSA_ERR_NULL;
+    if (g.nvt > 0 && (!perm || !block_idx)) return BSA_ERR_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(d_o, 16) ||
+        misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(lse, 4) ||
+        misaligned(perm, 4) || misaligned(block_idx, 4))
+        return BSA_ERR_ALIGN;
+    const BwdLayout L = bwd_layout(g);
+    if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+    if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    uint16_t* f[7];
+    for (int i = 0; i < 7; ++i) f[i] = reinterpret_cast<uint16_t*>(w + L.frag[i]);
+    // f: q_kf, do_kf, k_kf, v_kf (kfrag), k_vf, q_vf, do_vf (vfrag)
+    const uint16_t* src_kf[4] = {static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_o),
+                                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
+    const uint16_t* src_vf[3] = {static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(q),
+                                 static_cast<const uint16_t*>(d_o)};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 4 && e == hipSuccess; ++i)
+        e = bsa::launch_gather_kf(src_kf[i], f[i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s);
+    for (int i = 0; i < 3 && e == hipSuccess; ++i)
+        e = bsa::launch_gather_vf(src_vf[i], f[4 + i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video,
+                                  s);
+    if (e != hipSuccess) return launched(e);
+    bsa::BackwardArgs a{};
+    a.q_kf = f[0];
+    a.do_kf = f[1];
+    a.k_kf = f[2];
+    a.v_kf = f[3];
+    a.k_vf = f[4];
+    a.q_vf = f[5];
+    a.do_vf = f[6];
+    a.o = static_cast<const uint16_t*>(o);
+    a.dout = static_cast<const uint16_t*>(d_o);
+    a.lse = lse;
+    a.idx = block_idx;
+    a.perm = perm;
+    a.lse2 = reinterpret_cast<float*>(w + L.lse2);
+    a.delta = reinterpret_cast<float*>(w + L.delta);
+    a.mask = reinterpret_cast<uint32_t*>(w + L.mask);
+    a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
+    a.rowp = reinterpret_cast<int32_t*>(w + L.rowp);
+    a.tlist = reinterpret_cast<int32_t*>(w + L.tlist);
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.BH = (int)g.BH;
+    a.H = (int)g.H;
+    a.npt = (int)g.npt;
+    a.nvt = (int)g.nvt;
+    a.keep = (int)g.k;
+    a.mwords = L.mwords;
+    a.npf = g.npf;
+    a.n_tot = g.n_tot;
+    a.scale = desc->scale;
+    a.scale_log2 = desc->scale * 1.4426950408889634f;
+    return launched(bsa::launch_backward(a, (int)g.D, s));
 }
 
 }  // extern "C"

@@ -65,4 +65,21 @@ struct ForwardArgs {
 size_t forward_workspace_bytes();
 hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s);
 
+struct BackwardArgs {
+    // fragment layouts of the tiled tensors (kfrag / vfrag of the C interface)
+    const uint16_t *q_kf, *do_kf, *k_kf, *v_kf, *k_vf, *q_vf, *do_vf;
+    const uint16_t *o, *dout;  // raster [B][Ntot][H][D]
+    const float* lse;          // [BH][Ntot] natural log, tiled order
+    const int32_t* idx;        // [BH][nvt][keep]
+    const int32_t* perm;       // [B][Nvideo]
+    float *lse2, *delta;       // [BH][Ntot] scratch: lse * log2 e, dO . O
+    uint32_t* mask;            // [BH][nvt][mwords] scratch
+    int32_t *cnt, *rowp, *tlist;  // [BH][nvt], [BH][nvt + 1], [BH][nvt * keep] scratch
+    uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]
+    int BH, H, npt, nvt, keep, mwords;
+    int64_t npf, n_tot;
+    float scale, scale_log2;
+};
+hipError_t launch_backward(const BackwardArgs& a, int D, hipStream_t s);
+
 }  // namespace bsa

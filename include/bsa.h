@@ -21,7 +21,8 @@
  *
  * A call sequence:  bsa_permute(BUILD) -> bsa_permute(GATHER) for Q,
  * bsa_permute(GATHER_KF) for K, bsa_permute(GATHER_VF) for V -> bsa_plan ->
- * bsa_forward -> bsa_permute(SCATTER) for O.
+ * bsa_forward -> bsa_permute(SCATTER) for O; for training, bsa_backward with
+ * the raster tensors, the forward's lse and dL/dO.
  *
  * Layouts (row-major, bf16 = IEEE bfloat16):
  *   raster  bf16 [B][Ntot][H][D]   the dense prefix first (n_prefix tokens, already
@@ -181,13 +182,50 @@ bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_
                        const void *v_frag, const int32_t *block_idx, void *o_tiled, float *lse,
                        void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Bytes of device workspace that bsa_backward needs for `desc` (about seven
+ * times the size of one bf16 [B][H][Ntot][D] tensor: the fragment-layout
+ * copies of Q, K, V and dO the gradient kernels stream).  Host-only.
+ */
+bsa_status bsa_backward_workspace_size(const bsa_desc *desc, size_t *bytes);
+
+/*
+ * Gradients of bsa_forward's output.  The pages give no backward; Prism's
+ * page ("Prism / Kandinsky 6 speed ablation", section "같은 계산량 안에서 볼 곳을
+ * 고르는 Prism") reports that the same block sparsity speeds up training, which
+ * needs dQ, dK and dV over the same kept lists.  This is the exact derivative
+ * of the function bsa_forward computes: for query q with key set S_q (its
+ * kept tiles and the prefix; every token for a prefix query),
+ * P_qj = exp(scale q.k_j - lse_q), Delta_q = dO_q . O_q,
+ * dS_qj = P_qj (dO_q . v_j - Delta_q):
+ *   dQ_q = scale sum_{j in S_q} dS_qj k_j,
+ *   dK_j = scale sum_{q: j in S_q} dS_qj q_q,   dV_j = sum_{q: j in S_q} P_qj dO_q.
+ * Arguments:
+ *   q, k, v, o, d_o  bf16 raster [B][Ntot][H][D]: the forward's inputs, its
+ *                    output o and dL/do;
+ *   lse              float [B][H][Ntot] from bsa_forward (tiled order);
+ *   perm             int32 [B][Nvideo] from bsa_permute(BUILD);
+ *   block_idx        int32 [B][H][nVT][k] from bsa_plan (NULL only without video);
+ *   dq, dk, dv       bf16 raster [B][Ntot][H][D], overwritten;
+ *   ws               bsa_backward_workspace_size() bytes, 256-byte aligned.
+ * Products are bf16 MFMAs with float accumulation; P and dS are rounded to
+ * bf16 before their products, the gradients to bf16 at the end.  Tensors must
+ * be 16-byte aligned (lse, perm, block_idx 4-byte); at most BSA_MAX_TILES
+ * tiles and BSA_MAX_VIDEO_TILES video tiles per (batch, head).  Calls given the
+ * same workspace must not run concurrently.
+ */
+bsa_status bsa_backward(const bsa_desc *desc, const void *q, const void *k, const void *v,
+                        const void *o, const void *d_o, const float *lse, const int32_t *perm,
+                        const int32_t *block_idx, void *dq, void *dk, void *dv, void *ws,
+                        size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *bsa_status_string(bsa_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 400
+#define BSA_VERSION 500
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}  # "do": the output gradient of a backward pass
 
 
 @dataclasses.dataclass(frozen=True)

@@ -1,0 +1,85 @@
+"""GPU parity of the backward (dQ, dK, dV) against the CPU oracle's fp64
+gradients, on small workloads the oracle finishes in seconds: several tiles,
+ragged tile counts, k = 1, k = n, head dims 64 and 128, a dense prefix, a
+prefix with no video, and dynamic tile shapes.
+
+The forward runs first on the GPU (its selection, output and lse are checked
+by the forward parity tests); the backward gets the raster inputs, the GPU's
+output, a seeded dO and the forward's lse.  The oracle differentiates the same
+function exactly, with the GPU's selection.
+
+Tolerance, per gradient tensor: max |err| <= 2e-2 * max |ref| and
+mean |err| <= 1e-2 * mean |ref|.  The kernel rounds P and dS to bf16 (relative
+2^-9) before their products and each gradient to bf16 at the end (2^-9), and
+its Delta uses the bf16-rounded forward output; summed over many terms of
+mixed sign these stay a small multiple of 2^-9 of the tensor's scale.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_39_amd as bsa
+import oracle
+import synthetic as S
+from parity import GpuRun, bits_to_f64, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = S.Workload
+CASES = [
+    S.WORKLOADS["tiny"],
+    W("ragged", 2, 3, 128, (8, 8, 12), 5, seed=11),
+    W("prefix128", 1, 2, 128, (8, 8, 16), 3, seed=12, n_prefix=128),
+    W("prefix_d64", 2, 2, 64, (4, 8, 24), 2, seed=13, n_prefix=192),
+    W("dense_k_eq_n", 1, 2, 128, (8, 8, 8), 8, seed=14),
+    W("k1_d64", 1, 3, 64, (8, 8, 12), 1, seed=15),
+    W("prefix_only", 1, 2, 128, (0, 0, 0), 0, seed=17, n_prefix=256),
+    W("dynamic", 1, 2, 128, (16, 16, 16), 6, seed=18, dynamic=True, recipe="field"),
+]
+RTOL_MAX = 2e-2
+RTOL_MEAN = 1e-2
+
+
+def run_backward(wl):
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    dO = to_dev(do)
+    dq, dk, dv = (torch.empty_like(g.q) for _ in range(3))
+    ws = torch.empty(max(bsa.backward_workspace_size(g.desc), 256), dtype=torch.uint8, device="cuda")
+    bsa.backward(g.desc, g.q, g.k, g.v, g.out, dO, g.att.lse, g.att.perm, g.att.block_idx, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return (q, k, v, do), g, (dq, dk, dv)
+
+
+def check_grad(got, ref, what):
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    ref_mx, ref_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    print(f"[{what}] max|err| {mx:.3e} (ref max {ref_mx:.3e}), mean|err| {mean:.3e} (ref mean {ref_mean:.3e})",
+          flush=True)
+    assert np.isfinite(got).all(), what
+    assert mx <= RTOL_MAX * ref_mx + 1e-6, f"{what}: max {mx:.3e} vs {RTOL_MAX} x {ref_mx:.3e}"
+    assert mean <= RTOL_MEAN * ref_mean + 1e-7, f"{what}: mean {mean:.3e} vs {RTOL_MEAN} x {ref_mean:.3e}"
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_backward_matches_oracle(wl):
+    print(f"\n[case] {wl}", flush=True)
+    (q, k, v, do), g, grads = run_backward(wl)
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    perm = g.perm()
+    qt, kt, vt, dot = (oracle.gather(x, perm, npf) for x in (q, k, v, do))
+    gidx = g.block_idx() if wl.n_video else None
+    ref = oracle.backward_full(qt, kt, vt, dot, npf, gidx, scale)
+    for name, dev, r in zip(("dq", "dk", "dv"), grads, ref):
+        got = bits_to_f64(oracle.gather(to_bits(dev), perm, npf))
+        check_grad(got, r, name)
+
+
+def test_backward_is_deterministic():
+    wl = W("det", 1, 2, 128, (8, 8, 16), 5, seed=31, n_prefix=64)
+    _, _, a = run_backward(wl)
+    _, _, b = run_backward(wl)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

@@ -13,6 +13,13 @@ Prints one JSON line: effective TFLOP/s over the kept tiles (4*B*H*D * sum of
 attended key tokens per query) for the whole step, the forward kernel's
 roofline against the bf16 dense MFMA peak, per-stage times from HIP events on
 the launch stream, and the CPU oracle timed on a bounded sample.
+
+    python bench.py --backward [...]
+
+times the backward instead (bsa_backward: dQ, dK, dV from the forward's
+output and lse and a synthetic dO, inputs resident in HBM) and prints its own
+line: 2.5 x the forward's effective FLOPs (the five products of the gradient:
+S and dP recomputed, dV, dK, dQ) per second.
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (256 CUs x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective TFLOP/s (kept tiles) + ms/call, 122,880-token grid @25% keep, 1 GPU"
+METRIC_BWD = "backward effective TFLOP/s (2.5x forward FLOPs, kept tiles) + ms/call, 1 GPU"
 
 
 def parse():
@@ -43,6 +51,8 @@ def parse():
     ap.add_argument("--keep", type=int, default=None, help="override kept tiles per query tile")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tiles", type=int, default=960, help="query tiles in the CPU oracle sample")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass (bsa_backward)")
+    ap.add_argument("--cpu-bwd-tiles", type=int, default=120, help="query and key tiles in the backward CPU sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -107,6 +117,109 @@ def cpu_baseline(wl, q, k, v, n_tiles: int):
     }
 
 
+def cpu_baseline_backward(wl, q, k, v, do, n_tiles: int):
+    """The oracle's backward on one (batch, head) slice: lse, Delta and dQ of
+    `n_tiles` sampled query tiles, dK and dV of `n_tiles` sampled key tiles
+    (given lse and Delta of every query: the work does not depend on their
+    values), each extrapolated linearly over the head's tiles."""
+    import oracle
+    b, h = 0, 0
+    sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    perm = oracle.perm_static(wl.grid, wl.tile)[None]
+    qt, kt, vt, dt = (oracle.gather(sl(x), perm, wl.n_prefix)[0, 0] for x in (q, k, v, do))
+    t0 = time.perf_counter()
+    qp, kp = oracle.pool(qt[None, None], wl.n_prefix), oracle.pool(kt[None, None], wl.n_prefix)
+    idx, *_ = oracle.topk(qp, kp, wl.keep_tiles)
+    t_plan = time.perf_counter() - t0
+    nqt = wl.n_tokens // 64
+    rng = np.random.default_rng(4321)
+    tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
+    scale = float(np.float32(wl.scale))
+    t0 = time.perf_counter()
+    o, lse_s = oracle.attention(qt, kt, vt, wl.n_prefix, idx[0, 0], scale, tiles)
+    lse = np.zeros(wl.n_tokens)
+    delta = np.zeros(wl.n_tokens)
+    oracle.backward_dq(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], scale, tiles)
+    t_q = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.backward_dkdv(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], scale, tiles)
+    t_k = time.perf_counter() - t0
+    head_seconds = t_plan + (t_q + t_k) * nqt / len(tiles)
+    head_flops = 2.5 * wl.effective_flops() / (wl.batch * wl.heads)
+    return {
+        "value": head_flops / head_seconds / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "ms_per_call_extrapolated": head_seconds * wl.batch * wl.heads * 1e3,
+        "sample": (f"one (batch, head) slice of the same workload: plan over all rows ({t_plan:.2f} s), lse, "
+                   f"Delta and dQ of {len(tiles)} query tiles ({t_q:.2f} s) and dK, dV of {len(tiles)} key tiles "
+                   f"({t_k:.2f} s) of {nqt}, fp64, extrapolated linearly to the head and scaled by the head's "
+                   f"share of 2.5x the effective FLOPs"),
+    }
+
+
+def bench_backward(args, wl, q, k, v):
+    import torch
+
+    import block_sparse_attention_39_amd as bsa
+    import synthetic as S
+    do = S.tensor(wl, "do")
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+    att = bsa.BlockSparseAttention(desc, with_lse=True)
+    out = att(qd, kd, vd)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(max(bsa.backward_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+    call = lambda: bsa.backward(desc, qd, kd, vd, out, dod, att.lse, att.perm, att.block_idx, dq, dk, dv, ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_start = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(times))
+    F = 2.5 * wl.effective_flops()
+    achieved = F / (ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC_BWD,
+        "value": achieved,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid_thw": list(wl.grid), "tokens": wl.n_tokens,
+                   "video_tiles": wl.n_video_tiles, "prefix_tokens": wl.n_prefix, "batch": wl.batch,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "keep_tiles": wl.keep_tiles,
+                   "tile": "dynamic" if wl.dynamic else "x".join(map(str, wl.tile)),
+                   "backward_effective_tflop_per_call": F / 1e12},
+        "roofline": {"bound": "mfma", "kernel": "bsa_backward (all kernels of the call)", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline_backward(wl, q, k, v, do, args.cpu_bwd_tiles)
+        print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +240,12 @@ def main():
     print(f"[bench] {wl.name}: inputs generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     torch.cuda.set_device(0)
+    if args.backward:
+        if wl.dynamic:
+            print("bench.py --backward times static-tile workloads", file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args, wl, q, k, v)
+        return
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

@@ -357,93 +357,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---- dK, dV -----------------------------------------------------------------
+// The block walks the query tiles that attend its key tile one at a time.
+// Each query tile's four streamed operands (Q and dO in the kfrag and the
+// vfrag layout, 4 x 16 KB for D = 128) are copied once into LDS by direct
+// global-to-LDS loads, one tile ahead into the other of two stages; wave
+// (qh, kh) then reads its query half's fragments there and keeps the K and V
+// fragments of its key half in registers for the whole walk.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left alone (gfx9 encoding)
+constexpr int kWaitVm0 = 0x0F70;
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void dma_query_tile(const BackwardArgs& a, int64_t bh, int tq,
+                                                                     uint8_t* stage, const WaveId& w) {
+    constexpr int TB = BCfg<D>::TB, NB = TB / 1024;
+    const int n_tiles = a.npt + a.nvt;
+    const uint16_t* src[4] = {a.q_kf, a.do_kf, a.q_vf, a.do_vf};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint8_t* g = (const uint8_t*)src[u] + (bh * n_tiles + tq) * (int64_t)TB + w.lane * 16;
+#pragma unroll
+        for (int n = 0; n < NB / 4; ++n) {
+            const int blk = n * 4 + w.wave;
+            __builtin_amdgcn_global_load_lds((const void*)(g + blk * 1024), (lds_ptr_t)(stage + u * TB + blk * 1024),
+                                             16, 0, 0);
+        }
+    }
+}
+
+// lse (base 2) and Delta of the 16 query rows a lane holds in query half qh:
+// rows 32*qh + 16*c + 8*hf + e of the tile, c = 0, 1, e = 0..7
+__device__ __attribute__((always_inline)) inline void load_rows(const BackwardArgs& a, int64_t bh, int tq, int qh,
+                                                                int hf, float (&l2)[16], float (&dl)[16]) {
+    const int64_t q0 = bh * a.n_tot + (int64_t)tq * kTile + 32 * qh + 8 * hf;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const f32x4 a0 = *(const f32x4*)(a.lse2 + q0 + 16 * c), a1 = *(const f32x4*)(a.lse2 + q0 + 16 * c + 4);
+        const f32x4 d0 = *(const f32x4*)(a.delta + q0 + 16 * c), d1 = *(const f32x4*)(a.delta + q0 + 16 * c + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            l2[8 * c + e] = a0[e];
+            l2[8 * c + 4 + e] = a1[e];
+            dl[8 * c + e] = d0[e];
+            dl[8 * c + 4 + e] = d1[e];
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BackwardArgs a) {
     using CF = BCfg<D>;
     constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
-    __shared__ __attribute__((aligned(16))) float lds[CF::LDS_FLOATS];
+    constexpr int STAGE = 4 * TB;
+    constexpr int LDS_BYTES = 2 * STAGE > CF::MERGE_FLOATS * 4 ? 2 * STAGE : CF::MERGE_FLOATS * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
     const WaveId w;
+    const int qh = w.par;  // this wave's query half; w.kh its key half
     const int n_tiles = a.npt + a.nvt;
     const int64_t bh = blockIdx.x / n_tiles;
     const int kt = (int)(blockIdx.x % n_tiles);
-    int* list = (int*)lds;
-    uint8_t* klds = (uint8_t*)(lds + kMaxListTilesB);   // K fragments of the tile [2][SD][64][16 B]
-    uint8_t* vlds = klds + 2 * SD * 1024;                // V fragments, same layout
 
-    // ---- stage: the query-tile list and the stationary K, V fragments --------
-    int n_iter;
+    // the query tiles that attend key tile kt: every tile for a prefix key
+    // tile; the prefix tiles and then the transposed list for a video one
+    int n_iter, lo = 0;
+    const int32_t* tl = nullptr;
     if (kt < a.npt) {
         n_iter = n_tiles;
-        for (int j = w.tid; j < n_iter; j += 256) list[j] = j;
     } else {
         const int j = kt - a.npt;
-        const int lo = a.rowp[bh * (a.nvt + 1) + j], hi = a.rowp[bh * (a.nvt + 1) + j + 1];
-        const int32_t* tl = a.tlist + bh * (int64_t)a.nvt * a.keep;
-        n_iter = a.npt + (hi - lo);
-        for (int u = w.tid; u < a.npt; u += 256) list[u] = u;
-        for (int u = w.tid; u < hi - lo; u += 256) list[a.npt + u] = a.npt + min(max(tl[lo + u], 0), a.nvt - 1);
+        lo = a.rowp[bh * (a.nvt + 1) + j];
+        n_iter = a.npt + a.rowp[bh * (a.nvt + 1) + j + 1] - lo;
+        tl = a.tlist + bh * (int64_t)a.nvt * a.keep;
     }
     n_iter = __builtin_amdgcn_readfirstlane(n_iter);
+    auto tile_of = [&](int n) -> int {
+        if (n < a.npt || kt < a.npt) return n;
+        return a.npt + min(max(__builtin_amdgcn_readfirstlane(tl[lo + n - a.npt]), 0), a.nvt - 1);
+    };
+
+    // stationary: K and V fragments of key half kh (B operands: key = lane)
+    bf16x8 kreg[SD], vreg[SD];
     {
-        const uint8_t* ksrc = (const uint8_t*)a.k_kf + (bh * n_tiles + kt) * (int64_t)TB;
-        const uint8_t* vsrc = (const uint8_t*)a.v_kf + (bh * n_tiles + kt) * (int64_t)TB;
-        for (int u = w.tid; u < TB / 16; u += 256) {
-            *(u32x4*)(klds + u * 16) = *(const u32x4*)(ksrc + u * 16);
-            *(u32x4*)(vlds + u * 16) = *(const u32x4*)(vsrc + u * 16);
-        }
+        const int64_t off = (bh * n_tiles + kt) * (int64_t)TB + w.kh * CF::HALF + w.lane * 16;
+        load_n(kreg, (const uint8_t*)a.k_kf + off);
+        load_n(vreg, (const uint8_t*)a.v_kf + off);
     }
-    __syncthreads();
-
-    const float c2 = a.scale_log2;
-    const int my_n = (n_iter - w.par + 1) >> 1;
-    const uint8_t* qkb = (const uint8_t*)a.q_kf + bh * (int64_t)n_tiles * TB + w.lane * 16;
-    const uint8_t* gkb = (const uint8_t*)a.do_kf + bh * (int64_t)n_tiles * TB + w.lane * 16;
-    const uint8_t* qvb = (const uint8_t*)a.q_vf + bh * (int64_t)n_tiles * TB + w.lane * 16;
-    const uint8_t* gvb = (const uint8_t*)a.do_vf + bh * (int64_t)n_tiles * TB + w.lane * 16;
-    auto tile_at = [&](int n) { return __builtin_amdgcn_readfirstlane(list[min(w.par + 2 * n, n_iter - 1)]); };
-
-    // this wave's key half kh: B-operand fragments of K^T and V^T from LDS
-    const uint8_t* kown = klds + (w.kh * SD * 64 + w.lane) * 16;
-    const uint8_t* vown = vlds + (w.kh * SD * 64 + w.lane) * 16;
-
     f32x16 dk[OD][2], dv[OD][2];  // [.][0] used; [.][1] keeps merge_store's shape
 #pragma unroll
     for (int i = 0; i < OD; ++i) dk[i][0] = dk[i][1] = dv[i][0] = dv[i][1] = f32x16{};
+    const float c2 = a.scale_log2;
 
-    for (int n = 0; n < my_n; ++n) {
-        const int tq = tile_at(n);
-        const int64_t qrow = bh * (int64_t)a.n_tot + (int64_t)tq * kTile;
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-            const int64_t off = (int64_t)tq * TB + qh * CF::HALF;
-            bf16x8 qk[SD], gk[SD], qv[NV], gv[NV];
-            load_n(qk, qkb + off);
-            load_n(gk, gkb + off);
-            load_n(qv, qvb + off);
-            load_n(gv, gvb + off);
-            // lse and Delta of the rows this lane holds: queries
-            // 32*qh + 16*c + 8*hf + e, c = 0, 1, e = 0..7
-            float l2[16], dl[16];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int64_t r0 = qrow + 32 * qh + 16 * c + 8 * w.hf;
-                const f32x4 a0 = *(const f32x4*)(a.lse2 + r0), a1 = *(const f32x4*)(a.lse2 + r0 + 4);
-                const f32x4 d0 = *(const f32x4*)(a.delta + r0), d1 = *(const f32x4*)(a.delta + r0 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    l2[8 * c + e] = a0[e];
-                    l2[8 * c + 4 + e] = a1[e];
-                    dl[8 * c + e] = d0[e];
-                    dl[8 * c + 4 + e] = d1[e];
-                }
+    if (n_iter > 0) {
+        float l2[16], dl[16];
+        int tq = tile_of(0);
+        dma_query_tile<D>(a, bh, tq, smem, w);
+        load_rows(a, bh, tq, qh, w.hf, l2, dl);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+        for (int n = 0; n < n_iter; ++n) {
+            uint8_t* const st = smem + (n & 1) * STAGE;
+            const bool more = n + 1 < n_iter;
+            float nl2[16], ndl[16];
+            if (more) {  // the next query tile into the other stage (read by nobody since the last barrier)
+                const int tn = tile_of(n + 1);
+                dma_query_tile<D>(a, bh, tn, smem + ((n + 1) & 1) * STAGE, w);
+                load_rows(a, bh, tn, qh, w.hf, nl2, ndl);
             }
+            const uint8_t* qk = st + (qh * SD * 64 + w.lane) * 16;
+            const uint8_t* gk = st + TB + (qh * SD * 64 + w.lane) * 16;
+            const uint8_t* qv = st + 2 * TB + (qh * NV * 64 + w.lane) * 16;
+            const uint8_t* gv = st + 3 * TB + (qh * NV * 64 + w.lane) * 16;
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int st = 0; st < SD; ++st) {
-                const bf16x8 kf = *(const bf16x8*)(kown + st * 1024);
-                const bf16x8 vf = *(const bf16x8*)(vown + st * 1024);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk[st], kf, s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gk[st], vf, dp, 0, 0, 0);
+            for (int t = 0; t < SD; ++t) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qk + t * 1024), kreg[t], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gk + t * 1024), vreg[t], dp, 0, 0, 0);
             }
             // accumulator element j holds query 32*qh + 16*(j/8) + 8*hf + j%8
             bf16x8 pf[2], dsf[2];
@@ -458,13 +486,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int i = 0; i < OD; ++i) {
-                    dv[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gv[2 * i + c], pf[c], dv[i][0], 0, 0, 0);
-                    dk[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[2 * i + c], dsf[c], dk[i][0], 0, 0, 0);
+                    dv[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gv + (2 * i + c) * 1024),
+                                                                       pf[c], dv[i][0], 0, 0, 0);
+                    dk[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qv + (2 * i + c) * 1024),
+                                                                       dsf[c], dk[i][0], 0, 0, 0);
                 }
+            if (more) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of the next tile landed
+            __syncthreads();                                  // ... and everyone's; this stage is free again
+            if (more) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    l2[r] = nl2[r];
+                    dl[r] = ndl[r];
+                }
+            }
         }
     }
-    merge_store<D>(lds, dk, false, w, a.scale, a, bh, kt, a.dk);
-    merge_store<D>(lds, dv, false, w, 1.f, a, bh, kt, a.dv);
+    merge_store<D>((float*)smem, dk, false, w, a.scale, a, bh, kt, a.dk);
+    merge_store<D>((float*)smem, dv, false, w, 1.f, a, bh, kt, a.dv);
 }
 
 template <int D>

@@ -254,6 +254,17 @@ __device__ __attribute__((always_inline)) inline void merge_store(float* lds, co
 }
 
 // ---- dQ ---------------------------------------------------------------------
+// Software pipelined like the forward: a step over slice n is two windows of
+// 2*OD + SD + SD MFMA slots, one per query half h of the elementwise work:
+//   window 0: dQ^T[1] += K^T(n-1) dS^T(n-1)[1], S(n)[1] = K(n) Q^T[1],
+//             dP(n)[1] = V(n) dO^T[1];  beside them dS^T(n)[0] and the loads
+//             of K^T(n+1);
+//   window 1: dQ^T[0] += K^T(n) dS^T(n)[0], S(n+1)[0], dP(n+1)[0]; beside
+//             them dS^T(n)[1] and the loads of K(n+2), V(n+2).
+// A half's dS^T never shares a window with the products that overwrite its
+// scores or read it, so it needs one buffer.  Its pairs of elements go
+// through three stages in consecutive slots: P = exp2(S c - lse), then
+// P (dP - Delta), then the bf16 cast.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(BackwardArgs a) {
     using CF = BCfg<D>;
@@ -298,61 +309,131 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
     const float c2 = a.scale_log2;
-    const int my_n = (n_iter - w.par + 1) >> 1;
-    const uint8_t* kkb = (const uint8_t*)a.k_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + w.lane * 16;
-    const uint8_t* vkb = (const uint8_t*)a.v_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + w.lane * 16;
-    const uint8_t* kvb = (const uint8_t*)a.k_vf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + w.lane * 16;
-    auto tile_at = [&](int n) { return __builtin_amdgcn_readfirstlane(list[min(w.par + 2 * n, n_iter - 1)]); };
+    const int par = w.par, lane = w.lane;
+    const int my_n = (n_iter - par + 1) >> 1;
+    const uint8_t* kkb = (const uint8_t*)a.k_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
+    const uint8_t* vkb = (const uint8_t*)a.v_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
+    const uint8_t* kvb = (const uint8_t*)a.k_vf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
+#define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)])
 
     f32x16 acc[OD][2];
 #pragma unroll
     for (int i = 0; i < OD; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    f32x16 sacc[2], dpacc[2];
+    bf16x8 dsf[2][2];
     bf16x8 kk[2][SD], vk[2][SD], kv[2][NV];
     {
-        const int t0 = tile_at(0);
+        const int t0 = TILE_AT(0), t1 = TILE_AT(1);
         load_n(kk[0], kkb + (int64_t)t0 * TB);
         load_n(vk[0], vkb + (int64_t)t0 * TB);
         load_n(kv[0], kvb + (int64_t)t0 * TB);
+        load_n(kk[1], kkb + (int64_t)t1 * TB);
+        load_n(vk[1], vkb + (int64_t)t1 * TB);
     }
-    for (int n0 = 0; n0 < my_n; n0 += 2) {
+    // slice -1: K^T = 0 and dS^T[1] = 0 (the first window's dQ products add nothing)
+#pragma unroll
+    for (int f = 0; f < NV; ++f) kv[1][f] = bf16x8{};
+    dsf[1][0] = dsf[1][1] = bf16x8{};
+    // S(0)[0], dP(0)[0]
+    sacc[0] = dpacc[0] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < SD; ++st) {
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[0][st], *(const bf16x8*)(qlds + (st * 64 + lane) * 16),
+                                                          sacc[0], 0, 0, 0);
+        dpacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vk[0][st], *(const bf16x8*)(glds + (st * 64 + lane) * 16),
+                                                           dpacc[0], 0, 0, 0);
+    }
+    int t_v = TILE_AT(1);       // tile whose K^T fragments are loaded next
+    int t_k_next = TILE_AT(2);  // tile whose K, V fragments are loaded next
+
+    constexpr int NS = 2 * SD;         // S and dP slots of a window
+    constexpr int W = NS + 2 * OD;     // slots of a window
+    constexpr int QLEAD = 4;           // LDS read lead of the Q^T / dO^T fragments, in slots
+    constexpr int NG = W / 3;          // stage groups of a window
+    constexpr int PPG = 8 / NG;        // pairs of elements per stage group: 1 (D = 128), 2 (D = 64)
+    static_assert(NG * PPG == 8 && 2 * OD >= QLEAD && 2 * OD + NV <= W && 2 * SD <= W, "window layout");
+    int qoff = lane * 16;
+    bf16x8 qf[NS];
+
+    for (int n0 = 0; n0 <= my_n; n0 += 2) {
 #pragma unroll
         for (int B = 0; B < 2; ++B) {
             const int n = n0 + B;
-            if (B == 1 && n >= my_n) break;
-            {   // the next slice's operands into the other buffers
-                const int tn = tile_at(n + 1);
-                load_n(kk[B ^ 1], kkb + (int64_t)tn * TB);
-                load_n(vk[B ^ 1], vkb + (int64_t)tn * TB);
-                load_n(kv[B ^ 1], kvb + (int64_t)tn * TB);
-            }
-            bf16x8 dsf[2][2];
+            const int t_k = t_k_next;
+            const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)];
+            const uint8_t* const kaddr = kkb + (int64_t)t_k * TB;
+            const uint8_t* const vaddr = vkb + (int64_t)t_k * TB;
+            const uint8_t* const kvaddr = kvb + (int64_t)t_v * TB;
+            const float vmask = n < my_n ? 0.f : -INFINITY;
+            asm("" : "+v"(qoff) : "s"(n));  // opaque: keeps the LDS reads in the loop
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                f32x16 s = f32x16{}, dp = f32x16{};
+            for (int h = 0; h < 2; ++h) {
+                // h = 0: S, dP of half 1 (slice n), dQ of half 1 (slice n-1);
+                // h = 1: S, dP of half 0 (slice n+1), dQ of half 0 (slice n)
+                const int sq = 1 - h, pq = 1 - h;
+                const float neg = vmask - lse2[h];
+                float xe[8][2];
 #pragma unroll
-                for (int st = 0; st < SD; ++st) {
-                    const bf16x8 qf = *(const bf16x8*)(qlds + ((qb * SD + st) * 64 + w.lane) * 16);
-                    const bf16x8 gf = *(const bf16x8*)(glds + ((qb * SD + st) * 64 + w.lane) * 16);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[B][st], qf, s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vk[B][st], gf, dp, 0, 0, 0);
+                for (int g = 0; g < W; ++g) {
+                    // the Q^T / dO^T fragment of S/dP slot u, QLEAD slots ahead
+                    {
+                        const int u = g + QLEAD - 2 * OD;
+                        if (u >= 0 && u < NS)
+                            qf[u] = *(const bf16x8*)((u < SD ? qlds : glds) + qoff + (sq * SD + u % SD) * 1024);
+                    }
+                    if (g < 2 * OD) {
+                        const int c = g / OD, i = g % OD;
+                        acc[i][pq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[B ^ 1 ^ h][2 * i + c], dsf[pq][c],
+                                                                             acc[i][pq], 0, 0, 0);
+                        asm volatile("" ::"v"(acc[i][pq][0]));
+                    } else if (g < 2 * OD + SD) {
+                        const int st = g - 2 * OD;
+                        sacc[sq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[B ^ h][st], qf[st],
+                                                                           st == 0 ? f32x16{} : sacc[sq], 0, 0, 0);
+                        asm volatile("" ::"v"(sacc[sq][0]));
+                    } else {
+                        const int st = g - 2 * OD - SD;
+                        dpacc[sq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vk[B ^ h][st], qf[SD + st],
+                                                                            st == 0 ? f32x16{} : dpacc[sq], 0, 0, 0);
+                        asm volatile("" ::"v"(dpacc[sq][0]));
+                    }
+                    // window 0: K^T(n+1) once its buffer's dQ products are issued;
+                    // window 1: K(n+2), V(n+2); one fragment per slot
+                    if (h == 0) {
+                        const int f = g - 2 * OD;
+                        if (f >= 0 && f < NV) kv[B ^ 1][f] = *(const bf16x8*)(kvaddr + f * 1024);
+                    } else {
+                        if (g < SD) kk[B][g] = *(const bf16x8*)(kaddr + g * 1024);
+                        if (g >= SD && g < 2 * SD) vk[B][g - SD] = *(const bf16x8*)(vaddr + (g - SD) * 1024);
+                    }
+                    // dS^T of half h, stage group q = g / 3
+                    const int q = g / 3, stg = g % 3;
+                    if (q < NG) {
+#pragma unroll
+                        for (int u = 0; u < PPG; ++u) {
+                            const int p = q * PPG + u, r = 2 * p;
+                            if (stg == 0) {
+                                xe[p][0] = __builtin_amdgcn_exp2f(fmaf(sacc[h][r], c2, neg));
+                                xe[p][1] = __builtin_amdgcn_exp2f(fmaf(sacc[h][r + 1], c2, neg));
+                                asm volatile("" : "+v"(xe[p][0]), "+v"(xe[p][1]));
+                            } else if (stg == 1) {
+                                xe[p][0] *= dpacc[h][r] - dlt[h];
+                                xe[p][1] *= dpacc[h][r + 1] - dlt[h];
+                                asm volatile("" : "+v"(xe[p][0]), "+v"(xe[p][1]));
+                            } else {
+                                put_pair(dsf[h], r, xe[p][0], xe[p][1]);
+                                asm volatile("" : "+v"(dsf[h][r >> 3]));
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2[qb]));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -lse2[qb]));
-                    put_pair(dsf[qb], r, p0 * (dp[r] - dlt[qb]), p1 * (dp[r + 1] - dlt[qb]));
-                }
             }
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int i = 0; i < OD; ++i)
-                        acc[i][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[B][2 * i + c], dsf[qb][c], acc[i][qb],
-                                                                             0, 0, 0);
+            t_v = t_k;
+            t_k_next = __builtin_amdgcn_readfirstlane(t_after);
         }
     }
+#undef TILE_AT
     merge_store<D>(lds, acc, true, w, a.scale, a, bh, qt, a.dq);
 }
 

@@ -32,6 +32,8 @@
 //   next product's B operand, so P and dS go from accumulator to operand with
 //   a bf16 cast only.  The four waves' partial sums are added once per tile in
 //   LDS and written in raster order through the permutation.
+#include <climits>
+
 #include "bsa_kernels.h"
 
 namespace bsa {
@@ -266,14 +268,11 @@ __device__ __attribute__((always_inline)) inline void merge_store(float* lds, co
 // through three stages in consecutive slots: P = exp2(S c - lse), then
 // P (dP - Delta), then the bf16 cast.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(BackwardArgs a) {
+__device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs& a, float* lds, int64_t bh, int qt,
+                                                              const WaveId& w) {
     using CF = BCfg<D>;
     constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
-    __shared__ __attribute__((aligned(16))) float lds[CF::LDS_FLOATS];
-    const WaveId w;
     const int n_tiles = a.npt + a.nvt;
-    const int64_t bh = blockIdx.x / n_tiles;
-    const int qt = (int)(blockIdx.x % n_tiles);
     const bool dense = qt < a.npt;
     const int n_iter = dense ? n_tiles : a.npt + a.keep;
     int* list = (int*)lds;
@@ -281,6 +280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint8_t* glds = qlds + 2 * SD * 1024;                // dO^T fragments, same layout
 
     // ---- stage: the key-tile list and the stationary Q^T, dO^T ---------------
+    __syncthreads();  // the previous tile's epilogue is done with LDS
     if (dense) {
         for (int j = w.tid; j < n_iter; j += 256) list[j] = j;
     } else {
@@ -486,17 +486,21 @@ __device__ __attribute__((always_inline)) inline void load_rows(const BackwardAr
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BackwardArgs a) {
+struct DkdvLds {
+    static constexpr int STAGE = 4 * BCfg<D>::TB;
+    static constexpr int BYTES =
+        2 * STAGE > BCfg<D>::MERGE_FLOATS * 4 ? 2 * STAGE : BCfg<D>::MERGE_FLOATS * 4;
+};
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardArgs& a, uint8_t* smem, int64_t bh,
+                                                                int kt, const WaveId& w) {
     using CF = BCfg<D>;
     constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
-    constexpr int STAGE = 4 * TB;
-    constexpr int LDS_BYTES = 2 * STAGE > CF::MERGE_FLOATS * 4 ? 2 * STAGE : CF::MERGE_FLOATS * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
-    const WaveId w;
+    constexpr int STAGE = DkdvLds<D>::STAGE;
     const int qh = w.par;  // this wave's query half; w.kh its key half
     const int n_tiles = a.npt + a.nvt;
-    const int64_t bh = blockIdx.x / n_tiles;
-    const int kt = (int)(blockIdx.x % n_tiles);
+    __syncthreads();  // the previous tile's epilogue is done with LDS
 
     // the query tiles that attend key tile kt: every tile for a prefix key
     // tile; the prefix tiles and then the transposed list for a video one
@@ -548,30 +552,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const uint8_t* gk = st + TB + (qh * SD * 64 + w.lane) * 16;
             const uint8_t* qv = st + 2 * TB + (qh * NV * 64 + w.lane) * 16;
             const uint8_t* gv = st + 3 * TB + (qh * NV * 64 + w.lane) * 16;
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // 2*SD + 2*NV MFMA slots: S, dP, then dV and dK interleaved; the
+            // A operand of slot g is read from LDS LEAD slots ahead
+            constexpr int NSL = 2 * SD + 2 * NV, LEAD = 5;
+            auto a_src = [&](int g) -> const uint8_t* {
+                if (g < SD) return qk + g * 1024;
+                if (g < 2 * SD) return gk + (g - SD) * 1024;
+                const int j = g - 2 * SD, f = j >> 1;  // fragment 2i + c: c = f / OD, i = f % OD
+                const int frag = 2 * (f % OD) + f / OD;
+                return ((j & 1) ? qv : gv) + frag * 1024;
+            };
+            bf16x8 af[NSL];
 #pragma unroll
-            for (int t = 0; t < SD; ++t) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qk + t * 1024), kreg[t], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gk + t * 1024), vreg[t], dp, 0, 0, 0);
-            }
-            // accumulator element j holds query 32*qh + 16*(j/8) + 8*hf + j%8
+            for (int g = 0; g < LEAD; ++g) af[g] = *(const bf16x8*)a_src(g);
+            f32x16 s = f32x16{}, dp = f32x16{};
             bf16x8 pf[2], dsf[2];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[r]));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -l2[r + 1]));
-                put_pair(pf, r, p0, p1);
-                put_pair(dsf, r, p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
-            }
+            for (int g = 0; g < NSL; ++g) {
+                if (g + LEAD < NSL) af[g + LEAD] = *(const bf16x8*)a_src(g + LEAD);
+                if (g == 2 * SD) {
+                    // weights and dS of elements 0..7 (rows 32*qh + 8*hf + e) before
+                    // the products that read them
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int i = 0; i < OD; ++i) {
-                    dv[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(gv + (2 * i + c) * 1024),
-                                                                       pf[c], dv[i][0], 0, 0, 0);
-                    dk[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qv + (2 * i + c) * 1024),
-                                                                       dsf[c], dk[i][0], 0, 0, 0);
+                    for (int r = 0; r < 8; r += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[r]));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -l2[r + 1]));
+                        put_pair(pf, r, p0, p1);
+                        put_pair(dsf, r, p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
+                    }
                 }
+                if (g < SD) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], kreg[g], s, 0, 0, 0);
+                } else if (g < 2 * SD) {
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], vreg[g - SD], dp, 0, 0, 0);
+                } else {
+                    const int j = g - 2 * SD, f = j >> 1, c = f / OD, i = f % OD;
+                    if (j & 1)
+                        dk[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], dsf[c], dk[i][0], 0, 0, 0);
+                    else
+                        dv[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], pf[c], dv[i][0], 0, 0, 0);
+                    // elements 8..15 (rows 32*qh + 16 + 8*hf + e): four pairs spread
+                    // over the 2*OD slots of the first half (c = 0)
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) {
+                        if (pp * 2 * OD / 4 != j) continue;
+                        const int r = 8 + 2 * pp;
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[r]));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -l2[r + 1]));
+                        put_pair(pf, r, p0, p1);
+                        put_pair(dsf, r, p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (more) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of the next tile landed
             __syncthreads();                                  // ... and everyone's; this stage is free again
             if (more) {
@@ -587,6 +620,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     merge_store<D>((float*)smem, dv, false, w, 1.f, a, bh, kt, a.dv);
 }
 
+// Persistent launch of a per-tile body over the BH * (npt + nvt) tiles: block b
+// belongs to group b % 8 (the XCD the hardware dispatches it to, so a group
+// shares one L2); round r of group g covers tiles [(r*8 + g)*S, (r*8 + g + 1)*S)
+// of the (batch, head)-major order, consecutive tiles of one (batch, head).
+// The blocks of a group start each round together (bounded wait) and, with
+// similar work, walk their ascending lists in near lock-step, so an operand
+// tile is fetched into the XCD's L2 once for every block that needs it.  The
+// waits only shape the schedule; results do not depend on them.
+constexpr int kGroupsB = 8, kMaxGroupSizeB = 64, kMaxSpinB = 2000;
+
+template <typename Body>
+__device__ __attribute__((always_inline)) inline void grouped_rounds(const BackwardArgs& a, int* progress, Body body) {
+    const int group = blockIdx.x % kGroupsB, slot = blockIdx.x / kGroupsB;
+    const int S = gridDim.x / kGroupsB;
+    const int n_tiles = a.npt + a.nvt;
+    const int64_t n_items = (int64_t)a.BH * n_tiles;
+    int* prog = progress + group * kMaxGroupSizeB;
+    for (int64_t r = 0;; ++r) {
+        const int64_t item = (r * kGroupsB + group) * S + slot;
+        if (item >= n_items) break;
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            if (lane == 0) __hip_atomic_store(prog + slot, (int)r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int spin = 0; spin < kMaxSpinB; ++spin) {
+                int v = INT_MAX;
+                if (lane < S) v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+                if (v >= (int)r) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        body(item / n_tiles, (int)(item % n_tiles));
+    }
+    // done: never hold the rest of the group back
+    if (threadIdx.x == 0) __hip_atomic_store(prog + slot, INT_MAX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(BackwardArgs a,
+                                                                                              int* progress) {
+    __shared__ __attribute__((aligned(16))) float lds[BCfg<D>::LDS_FLOATS];
+    const WaveId w;
+    grouped_rounds(a, progress, [&](int64_t bh, int qt) { dq_tile<D>(a, lds, bh, qt, w); });
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BackwardArgs a,
+                                                                                                int* progress) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DkdvLds<D>::BYTES];
+    const WaveId w;
+    grouped_rounds(a, progress, [&](int64_t bh, int kt) { dkdv_tile<D>(a, smem, bh, kt, w); });
+}
+
+__global__ void bwd_clear_progress_kernel(int* progress, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) progress[i] = 0;
+}
+
+template <typename K>
+hipError_t grouped_grid(K kernel, int64_t work, int64_t* grid) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+    if (e != hipSuccess) return e;
+    int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    g = g / kGroupsB * kGroupsB;
+    if (g > (int64_t)kGroupsB * kMaxGroupSizeB) g = (int64_t)kGroupsB * kMaxGroupSizeB;
+    const int64_t need = (work + kGroupsB - 1) / kGroupsB * kGroupsB;
+    if (g > need) g = need;
+    if (g < kGroupsB) g = kGroupsB;
+    *grid = g;
+    return hipSuccess;
+}
+
 template <int D>
 hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.BH * a.n_tot;
@@ -600,8 +708,15 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(bwd_tfill_kernel, dim3(g), dim3(256), 0, s, a);
     }
     const int64_t tiles = (int64_t)a.BH * (a.npt + a.nvt);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)tiles), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    int64_t gq = 0, gk = 0;
+    hipError_t e = grouped_grid(bwd_dq_kernel<D>, tiles, &gq);
+    if (e == hipSuccess) e = grouped_grid(bwd_dkdv_kernel<D>, tiles, &gk);
+    if (e != hipSuccess) return e;
+    constexpr int NP = kGroupsB * kMaxGroupSizeB;
+    hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(256), 0, s, a, a.progress);
+    hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(256), 0, s, a, a.progress);
     return hipGetLastError();
 }
 

@@ -97,7 +97,7 @@ bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LA
 // Workspace of bsa_backward: the seven fragment-layout copies, then the
 // per-row lse (base 2) and Delta, then the transposed lists.
 struct BwdLayout {
-    size_t frag[7], lse2, delta, mask, cnt, rowp, tlist, total;
+    size_t frag[7], lse2, delta, mask, cnt, rowp, tlist, progress, total;
     int mwords;
 };
 
@@ -119,6 +119,8 @@ BwdLayout bwd_layout(const Geo& g) {
     o += align_up((size_t)g.BH * (g.nvt + 1) * sizeof(int32_t));
     L.tlist = o;
     o += align_up((size_t)g.BH * g.nvt * g.k * sizeof(int32_t));
+    L.progress = o;
+    o += align_up((size_t)bsa::backward_progress_ints() * sizeof(int));
     L.total = o;
     return L;
 }
@@ -322,6 +324,7 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
     a.rowp = reinterpret_cast<int32_t*>(w + L.rowp);
     a.tlist = reinterpret_cast<int32_t*>(w + L.tlist);
+    a.progress = reinterpret_cast<int*>(w + L.progress);
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);

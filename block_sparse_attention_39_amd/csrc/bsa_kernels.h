@@ -76,10 +76,12 @@ struct BackwardArgs {
     uint32_t* mask;            // [BH][nvt][mwords] scratch
     int32_t *cnt, *rowp, *tlist;  // [BH][nvt], [BH][nvt + 1], [BH][nvt * keep] scratch
     uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]
+    int* progress;             // backward_progress_ints() ints: grouped-launch round counters
     int BH, H, npt, nvt, keep, mwords;
     int64_t npf, n_tot;
     float scale, scale_log2;
 };
+constexpr int backward_progress_ints() { return 8 * 64; }
 hipError_t launch_backward(const BackwardArgs& a, int D, hipStream_t s);
 
 }  // namespace bsa

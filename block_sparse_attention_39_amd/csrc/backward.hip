@@ -438,69 +438,249 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
 }
 
 // ---- dK, dV -----------------------------------------------------------------
-// The block walks the query tiles that attend its key tile one at a time.
-// Each query tile's four streamed operands (Q and dO in the kfrag and the
-// vfrag layout, 4 x 16 KB for D = 128) are copied once into LDS by direct
-// global-to-LDS loads, one tile ahead into the other of two stages; wave
-// (qh, kh) then reads its query half's fragments there and keeps the K and V
-// fragments of its key half in registers for the whole walk.
+// The block walks the query tiles that attend its key tile.  Each query tile's
+// Q and dO rows (tiled layout, 2 x 16 KB for D = 128) and its 64 values of lse
+// and Delta are copied into LDS once, by direct global-to-LDS loads, two tiles
+// ahead into the third of three stages.  In LDS the rows are kept whole with
+// their 16-byte chunks XOR-swizzled by the row, so that both operand shapes
+// read without bank conflicts:
+//   * S = Q K^T and dP = dO V^T take Q and dO as A operands of 32 rows by 16
+//     channels: one 16-byte read per lane;
+//   * dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T, 32 channels by 16
+//     rows: two transposing reads (ds_read_b64_tr_b16) per lane, each giving a
+//     lane 4 consecutive rows of its channel.
+// Wave (qh, kh) takes query half qh of every tile and keeps the K and V
+// fragments of its key half kh in registers for the whole walk.
+//
+// The three stages are three LDS arrays and the walk is unrolled by three, so
+// that each step names its stages at compile time: the compiler can then tell
+// the reads of one stage from the direct loads into another and does not make
+// the reads wait for those loads.  The waits for the loads are explicit.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left alone (gfx9 encoding)
-constexpr int kWaitVm0 = 0x0F70;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left alone (gfx9 encoding)
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// a block barrier that does not wait for the direct-to-LDS loads in flight
+// (the waits before it are explicit); the empty asm keeps memory accesses on
+// their side of it
+__device__ __attribute__((always_inline)) inline void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// an int32 read through the scalar data cache (uniform address, data written
+// by an earlier launch), so that waiting for it does not wait for the vector
+// memory loads in flight
+__device__ inline int scalar_load(const int32_t* p) { return *(const_i32*)p; }
+
+template <int D>
+struct DkdvLds {
+    static constexpr int C = D / 8;                     // 16-byte chunks of a row
+    static constexpr int ROWS = kTile * D * 2;          // bytes of one tensor's rows
+    static constexpr int STAGE = 2 * ROWS + 512;        // Q rows, dO rows, lse (base 2), Delta
+    static constexpr int MERGE = kTile * BCfg<D>::MROW * 4;  // [64][MROW] floats
+    static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
+    static constexpr int OPS = C / 2 + 1;               // direct loads per wave per tile
+};
+
+// position of 16-byte chunk c of row r in LDS: c ^ rswz(r)
+template <int D>
+__device__ inline int rswz(int r) {
+    return (2 * (r & 3) | ((r >> 3) & 1) | (((r >> 2) & 1) << 3)) & (D / 8 - 1);
+}
 
 template <int D>
 __device__ __attribute__((always_inline)) inline void dma_query_tile(const BackwardArgs& a, int64_t bh, int tq,
                                                                      uint8_t* stage, const WaveId& w) {
-    constexpr int TB = BCfg<D>::TB, NB = TB / 1024;
-    const int n_tiles = a.npt + a.nvt;
-    const uint16_t* src[4] = {a.q_kf, a.do_kf, a.q_vf, a.do_vf};
+    using L = DkdvLds<D>;
+    constexpr int C = L::C;
+    const int64_t row0 = bh * a.n_tot + (int64_t)tq * kTile;
+    const uint16_t* src[2] = {a.q_t + row0 * D, a.do_t + row0 * D};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint8_t* g = (const uint8_t*)src[u] + (bh * n_tiles + tq) * (int64_t)TB + w.lane * 16;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int n = 0; n < NB / 4; ++n) {
-            const int blk = n * 4 + w.wave;
-            __builtin_amdgcn_global_load_lds((const void*)(g + blk * 1024), (lds_ptr_t)(stage + u * TB + blk * 1024),
-                                             16, 0, 0);
+        for (int n = 0; n < C / 4; ++n) {
+            const int blk = n * 4 + w.wave;   // 1 KB block of the region
+            const int p = blk * 64 + w.lane;  // its 16-byte slot
+            const int r = p / C;
+            const int c = (p % C) ^ rswz<D>(r);
+            __builtin_amdgcn_global_load_lds((const void*)(src[u] + (r * C + c) * 8),
+                                             (lds_ptr_t)(stage + u * L::ROWS + blk * 1024), 16, 0, 0);
         }
+    // lse (base 2) and Delta: wave w copies 32 of the 128 values
+    if (w.lane < 32) {
+        const float* g = (w.wave < 2 ? a.lse2 : a.delta) + row0 + 32 * (w.wave & 1) + w.lane;
+        __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)(stage + 2 * L::ROWS + w.wave * 128), 4, 0, 0);
     }
 }
 
-// lse (base 2) and Delta of the 16 query rows a lane holds in query half qh:
-// rows 32*qh + 16*c + 8*hf + e of the tile, c = 0, 1, e = 0..7
-__device__ __attribute__((always_inline)) inline void load_rows(const BackwardArgs& a, int64_t bh, int tq, int qh,
-                                                                int hf, float (&l2)[16], float (&dl)[16]) {
-    const int64_t q0 = bh * a.n_tot + (int64_t)tq * kTile + 32 * qh + 8 * hf;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const f32x4 a0 = *(const f32x4*)(a.lse2 + q0 + 16 * c), a1 = *(const f32x4*)(a.lse2 + q0 + 16 * c + 4);
-        const f32x4 d0 = *(const f32x4*)(a.delta + q0 + 16 * c), d1 = *(const f32x4*)(a.delta + q0 + 16 * c + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            l2[8 * c + e] = a0[e];
-            l2[8 * c + 4 + e] = a1[e];
-            dl[8 * c + e] = d0[e];
-            dl[8 * c + 4 + e] = d1[e];
-        }
-    }
-}
-
+// Sums the two query halves' partial dK^T (or dV^T) of key tile `tile` in one
+// [64 keys][MROW] float block of LDS and writes it, times `mul`, as bf16 rows
+// of the raster output.  Wave (qh, kh) holds key half kh: the qh = 1 waves
+// store, the qh = 0 waves add theirs in place, then all threads write rows.
 template <int D>
-struct DkdvLds {
-    static constexpr int STAGE = 4 * BCfg<D>::TB;
-    static constexpr int BYTES =
-        2 * STAGE > BCfg<D>::MERGE_FLOATS * 4 ? 2 * STAGE : BCfg<D>::MERGE_FLOATS * 4;
+__device__ __attribute__((always_inline)) inline void merge_halves(float* lds, const f32x16 (&acc)[D / 32],
+                                                                   const WaveId& w, float mul, const BackwardArgs& a,
+                                                                   int64_t bh, int tile, uint16_t* out) {
+    constexpr int OD = D / 32, MROW = BCfg<D>::MROW, C = D / 8;
+    const int tok = 32 * w.kh + swap23(w.lr);
+    float* mine = lds + tok * MROW + 4 * w.hf;
+    block_barrier();  // the previous user of the block is done
+    if (w.par == 1) {
+#pragma unroll
+        for (int i = 0; i < OD; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *(f32x4*)(mine + 32 * i + 8 * j) =
+                    f32x4{acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
+    }
+    __syncthreads();
+    if (w.par == 0) {
+#pragma unroll
+        for (int i = 0; i < OD; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4* p = (f32x4*)(mine + 32 * i + 8 * j);
+                *p = *p + f32x4{acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
+            }
+    }
+    __syncthreads();
+    const int b = (int)(bh / a.H);
+#pragma unroll
+    for (int u = 0; u < kTile * C / 256; ++u) {
+        const int cidx = w.tid + 256 * u;
+        const int r = cidx / C, c = cidx % C;
+        const f32x4 s0 = *(const f32x4*)(lds + r * MROW + 8 * c);
+        const f32x4 s1 = *(const f32x4*)(lds + r * MROW + 8 * c + 4);
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const bf16x2 lo = __builtin_convertvector((f32x2){s0[2 * e] * mul, s0[2 * e + 1] * mul}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector((f32x2){s1[2 * e] * mul, s1[2 * e + 1] * mul}, bf16x2);
+            pk[e] = __builtin_bit_cast(uint32_t, lo);
+            pk[2 + e] = __builtin_bit_cast(uint32_t, hi);
+        }
+        const int64_t tk = raster_token(a, b, (int64_t)tile * kTile + r);
+        *(u32x4*)(raster_row(out, a, bh, tk, D) + 8 * c) = pk;
+    }
+}
+
+// Per-lane constants of the dK/dV walk (see dkdv_tile).
+struct DkdvLane {
+    int qh, hf;  // query half of the wave, lane half
+    int qa, tb;  // LDS offsets of the two operand shapes
 };
+
+// One query tile of the dK/dV walk: the tile's Q and dO rows, lse and Delta
+// are in LDS at `st`; when `nx` is not null the tile after next is loaded into
+// it first.  The two pointers are declared not to alias: the compiler then
+// leaves the reads of `st` free of waits for the loads into `nx` (the caller
+// waits for those explicitly before their stage is read).
+template <int D>
+__device__ __attribute__((always_inline)) inline void dkdv_step(
+    const BackwardArgs& a, const uint8_t* __restrict__ st, uint8_t* __restrict__ nx, int64_t bh, int tq_next,
+    const WaveId& w, const DkdvLane& ln, const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
+    f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    using L = DkdvLds<D>;
+    constexpr int SD = D / 16, OD = D / 32, NV = 2 * OD, C = L::C;
+    const float c2 = a.scale_log2;
+    const int qh = ln.qh;
+    if (nx) dma_query_tile<D>(a, bh, tq_next, nx, w);
+    // fresh copies of the lane offsets for this step, so that the offsets
+    // derived from them are formed where they are used
+    int qa_s = ln.qa, tb_s = ln.tb;
+    asm volatile("" : "+v"(qa_s), "+v"(tb_s));
+    // lse (base 2) and Delta of this lane's rows: element r = 8*c + e of
+    // the accumulators is row 32*qh + 16*c + 8*hf + e
+    const float* lse_row = (const float*)(st + 2 * L::ROWS) + 32 * qh + 8 * w.hf;
+    // 2*SD + 2*NV MFMA slots: S, dP, then dV and dK interleaved; the
+    // A operand of slot g is read from LDS LEAD slots ahead
+    constexpr int NSL = 2 * SD + 2 * NV, LEAD = 3;
+    auto a_read = [&](int g) -> bf16x8 {
+        if (g < 2 * SD) {
+            const int s2 = g % SD;
+            return *(const bf16x8*)(st + (g < SD ? 0 : L::ROWS) + (qa_s ^ (32 * s2)));
+        }
+        const int j = g - 2 * SD, f = j >> 1;  // fragment 2i + c: c = f / OD, i = f % OD
+        const int i = f % OD, c = f / OD;
+        const uint8_t* base = st + ((j & 1) ? 0 : L::ROWS);  // dK: Q^T, dV: dO^T
+        v4i16 h[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+            h[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(base + (tb_s ^ (64 * ((i ^ 2 * h2) & (C / 4 - 1)))) + (16 * c + 4 * h2) * C * 16));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // pair q of accumulator elements (2q, 2q + 1) is turned into weights
+    // and dS at slot use_slot(q): pairs 0..3 at the first dV/dK slot,
+    // pairs 4..7 spread over the first 2*OD of those slots (the ones that
+    // read elements 0..7 only); their lse and Delta are read two slots ahead
+    auto use_slot = [](int q) { return 2 * SD + (q < 4 ? 0 : (q - 4) * 2 * OD / 4); };
+    bf16x8 af[NSL];
+#pragma unroll
+    for (int g = 0; g < LEAD; ++g) af[g] = a_read(g);
+    f32x16 sc = f32x16{}, dp = f32x16{};
+    bf16x8 pf[2], dsf[2];
+    f32x4 lo_l[2], lo_d[2];
+    f32x2 pl[8], pd[8];
+#pragma unroll
+    for (int g = 0; g < NSL; ++g) {
+        if (g + LEAD < NSL) af[g + LEAD] = a_read(g + LEAD);
+        if (g == use_slot(0) - 2) {
+            lo_l[0] = *(const f32x4*)lse_row;
+            lo_l[1] = *(const f32x4*)(lse_row + 4);
+            lo_d[0] = *(const f32x4*)(lse_row + 64);
+            lo_d[1] = *(const f32x4*)(lse_row + 68);
+        }
+#pragma unroll
+        for (int q = 4; q < 8; ++q)
+            if (g == use_slot(q) - 2) {
+                const int r = 2 * q;  // c = 1, e = r - 8
+                pl[q] = *(const f32x2*)(lse_row + 16 + (r - 8));
+                pd[q] = *(const f32x2*)(lse_row + 64 + 16 + (r - 8));
+            }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (g == use_slot(q)) {
+                const int r = 2 * q;
+                const float l0 = q < 4 ? lo_l[q >> 1][r & 3] : pl[q][0];
+                const float l1 = q < 4 ? lo_l[q >> 1][(r & 3) + 1] : pl[q][1];
+                const float d0 = q < 4 ? lo_d[q >> 1][r & 3] : pd[q][0];
+                const float d1 = q < 4 ? lo_d[q >> 1][(r & 3) + 1] : pd[q][1];
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -l0));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -l1));
+                put_pair(pf, r, p0, p1);
+                put_pair(dsf, r, p0 * (dp[r] - d0), p1 * (dp[r + 1] - d1));
+            }
+        if (g < SD) {
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], kreg[g], sc, 0, 0, 0);
+        } else if (g < 2 * SD) {
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], vreg[g - SD], dp, 0, 0, 0);
+        } else {
+            const int j = g - 2 * SD, f = j >> 1, c = f / OD, i = f % OD;
+            if (j & 1)
+                dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], dsf[c], dk[i], 0, 0, 0);
+            else
+                dv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], pf[c], dv[i], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
 template <int D>
 __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardArgs& a, uint8_t* smem, int64_t bh,
                                                                 int kt, const WaveId& w) {
     using CF = BCfg<D>;
-    constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
-    constexpr int STAGE = DkdvLds<D>::STAGE;
+    using L = DkdvLds<D>;
+    constexpr int SD = CF::SD, OD = CF::OD, TB = CF::TB, C = L::C;
     const int qh = w.par;  // this wave's query half; w.kh its key half
     const int n_tiles = a.npt + a.nvt;
-    __syncthreads();  // the previous tile's epilogue is done with LDS
+    block_barrier();       // the previous tile's epilogue is done with LDS
 
     // the query tiles that attend key tile kt: every tile for a prefix key
     // tile; the prefix tiles and then the transposed list for a video one
@@ -509,15 +689,14 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
     if (kt < a.npt) {
         n_iter = n_tiles;
     } else {
-        const int j = kt - a.npt;
-        lo = a.rowp[bh * (a.nvt + 1) + j];
-        n_iter = a.npt + a.rowp[bh * (a.nvt + 1) + j + 1] - lo;
-        tl = a.tlist + bh * (int64_t)a.nvt * a.keep;
+        const int32_t* rp = a.rowp + bh * (a.nvt + 1) + (kt - a.npt);
+        lo = scalar_load(rp);
+        n_iter = a.npt + scalar_load(rp + 1) - lo;
+        tl = a.tlist + bh * (int64_t)a.nvt * a.keep + lo - a.npt;
     }
-    n_iter = __builtin_amdgcn_readfirstlane(n_iter);
     auto tile_of = [&](int n) -> int {
         if (n < a.npt || kt < a.npt) return n;
-        return a.npt + min(max(__builtin_amdgcn_readfirstlane(tl[lo + n - a.npt]), 0), a.nvt - 1);
+        return a.npt + min(max(scalar_load(tl + n), 0), a.nvt - 1);
     };
 
     // stationary: K and V fragments of key half kh (B operands: key = lane)
@@ -527,97 +706,60 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
         load_n(kreg, (const uint8_t*)a.k_kf + off);
         load_n(vreg, (const uint8_t*)a.v_kf + off);
     }
-    f32x16 dk[OD][2], dv[OD][2];  // [.][0] used; [.][1] keeps merge_store's shape
+    f32x16 dk[OD], dv[OD];
 #pragma unroll
-    for (int i = 0; i < OD; ++i) dk[i][0] = dk[i][1] = dv[i][0] = dv[i][1] = f32x16{};
-    const float c2 = a.scale_log2;
+    for (int i = 0; i < OD; ++i) dk[i] = dv[i] = f32x16{};
+
+    // Per-lane LDS byte offsets inside a stage.  A row is C * 16 bytes and its
+    // chunk position is below that, so row + position = row ^ position.
+    // S / dP A operand (32 rows x 16 channels): row rq = 32*qh + swap23(lr),
+    // chunk 2*s + hf at position (2*s + hf) ^ rswz(rq):
+    //   offset = qa ^ (32 * s),  qa = rq*C*16 ^ ((hf ^ rswz(rq)) * 16)
+    // dV^T / dK^T A operand (32 channels x 16 rows), two transposing reads
+    // h2 = 0, 1 per fragment (i, c): input lane (G, ta, te) of 16-lane group G
+    // addresses row 32*qh + 16*c + 8*(G/2) + 4*h2 + te, chunk
+    // 4*i + 2*(G%2) + ta/2, bytes 8*(ta%2).  With rswz of that row,
+    //   offset = tb ^ (64 * ((i ^ 2*h2) & (C/4 - 1))) + (16*c + 4*h2) * C * 16
+    DkdvLane ln;
+    ln.qh = qh;
+    ln.hf = w.hf;
+    {
+        const int rq = 32 * qh + swap23(w.lr);
+        ln.qa = (rq * C * 16) ^ ((w.hf ^ rswz<D>(rq)) * 16);
+        const int G = w.lane >> 4, ta = w.lane & 3, te = (w.lane >> 2) & 3;
+        ln.tb = ((32 * qh + 8 * (G >> 1) + te) * C * 16) |
+                (((2 * (G & 1) + (ta >> 1)) ^ ((2 * te | (G >> 1)) & (C - 1))) * 16) | ((ta & 1) * 8);
+    }
 
     if (n_iter > 0) {
-        float l2[16], dl[16];
-        int tq = tile_of(0);
-        dma_query_tile<D>(a, bh, tq, smem, w);
-        load_rows(a, bh, tq, qh, w.hf, l2, dl);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __syncthreads();
+        dma_query_tile<D>(a, bh, tile_of(0), smem, w);
+        if (n_iter > 1) {
+            dma_query_tile<D>(a, bh, tile_of(1), smem + L::BYTES, w);
+            __builtin_amdgcn_s_waitcnt(wait_vm(L::OPS));
+        } else {
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        }
+        block_barrier();
+        int cur = 0;
         for (int n = 0; n < n_iter; ++n) {
-            uint8_t* const st = smem + (n & 1) * STAGE;
-            const bool more = n + 1 < n_iter;
-            float nl2[16], ndl[16];
-            if (more) {  // the next query tile into the other stage (read by nobody since the last barrier)
-                const int tn = tile_of(n + 1);
-                dma_query_tile<D>(a, bh, tn, smem + ((n + 1) & 1) * STAGE, w);
-                load_rows(a, bh, tn, qh, w.hf, nl2, ndl);
-            }
-            const uint8_t* qk = st + (qh * SD * 64 + w.lane) * 16;
-            const uint8_t* gk = st + TB + (qh * SD * 64 + w.lane) * 16;
-            const uint8_t* qv = st + 2 * TB + (qh * NV * 64 + w.lane) * 16;
-            const uint8_t* gv = st + 3 * TB + (qh * NV * 64 + w.lane) * 16;
-            // 2*SD + 2*NV MFMA slots: S, dP, then dV and dK interleaved; the
-            // A operand of slot g is read from LDS LEAD slots ahead
-            constexpr int NSL = 2 * SD + 2 * NV, LEAD = 5;
-            auto a_src = [&](int g) -> const uint8_t* {
-                if (g < SD) return qk + g * 1024;
-                if (g < 2 * SD) return gk + (g - SD) * 1024;
-                const int j = g - 2 * SD, f = j >> 1;  // fragment 2i + c: c = f / OD, i = f % OD
-                const int frag = 2 * (f % OD) + f / OD;
-                return ((j & 1) ? qv : gv) + frag * 1024;
-            };
-            bf16x8 af[NSL];
-#pragma unroll
-            for (int g = 0; g < LEAD; ++g) af[g] = *(const bf16x8*)a_src(g);
-            f32x16 s = f32x16{}, dp = f32x16{};
-            bf16x8 pf[2], dsf[2];
-#pragma unroll
-            for (int g = 0; g < NSL; ++g) {
-                if (g + LEAD < NSL) af[g + LEAD] = *(const bf16x8*)a_src(g + LEAD);
-                if (g == 2 * SD) {
-                    // weights and dS of elements 0..7 (rows 32*qh + 8*hf + e) before
-                    // the products that read them
-#pragma unroll
-                    for (int r = 0; r < 8; r += 2) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[r]));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -l2[r + 1]));
-                        put_pair(pf, r, p0, p1);
-                        put_pair(dsf, r, p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
-                    }
-                }
-                if (g < SD) {
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], kreg[g], s, 0, 0, 0);
-                } else if (g < 2 * SD) {
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], vreg[g - SD], dp, 0, 0, 0);
-                } else {
-                    const int j = g - 2 * SD, f = j >> 1, c = f / OD, i = f % OD;
-                    if (j & 1)
-                        dk[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], dsf[c], dk[i][0], 0, 0, 0);
-                    else
-                        dv[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], pf[c], dv[i][0], 0, 0, 0);
-                    // elements 8..15 (rows 32*qh + 16 + 8*hf + e): four pairs spread
-                    // over the 2*OD slots of the first half (c = 0)
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp) {
-                        if (pp * 2 * OD / 4 != j) continue;
-                        const int r = 8 + 2 * pp;
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[r]));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -l2[r + 1]));
-                        put_pair(pf, r, p0, p1);
-                        put_pair(dsf, r, p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (more) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's part of the next tile landed
-            __syncthreads();                                  // ... and everyone's; this stage is free again
-            if (more) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    l2[r] = nl2[r];
-                    dl[r] = ndl[r];
-                }
-            }
+            // tile n is in stage cur; the tile after next goes to the stage
+            // tile n - 1 used
+            const int nxt = cur == 0 ? 2 : cur - 1;
+            const bool ahead = n + 2 < n_iter;
+            dkdv_step<D>(a, smem + cur * L::BYTES, ahead ? smem + nxt * L::BYTES : nullptr, bh,
+                         ahead ? tile_of(n + 2) : 0, w, ln, kreg, vreg, dk, dv);
+            // the next tile landed (this wave's part; the tile after it may
+            // stay in flight), then everyone's, and this stage is free again
+            if (ahead)
+                __builtin_amdgcn_s_waitcnt(wait_vm(L::OPS));
+            else
+                __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            block_barrier();
+            cur = cur == 2 ? 0 : cur + 1;
         }
     }
-    merge_store<D>((float*)smem, dk, false, w, a.scale, a, bh, kt, a.dk);
-    merge_store<D>((float*)smem, dv, false, w, 1.f, a, bh, kt, a.dv);
+    merge_halves<D>((float*)smem, dk, w, a.scale, a, bh, kt, a.dk);
+    merge_halves<D>((float*)smem, dv, w, 1.f, a, bh, kt, a.dv);
 }
 
 // Persistent launch of a per-tile body over the BH * (npt + nvt) tiles: block b
@@ -669,7 +811,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BackwardArgs a,
                                                                                                 int* progress) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[DkdvLds<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[3 * DkdvLds<D>::BYTES];
     const WaveId w;
     grouped_rounds(a, progress, [&](int64_t bh, int kt) { dkdv_tile<D>(a, smem, bh, kt, w); });
 }

@@ -94,7 +94,7 @@ Layout layout(const Geo& g) {
 
 bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LAUNCH; }
 
-// Workspace of bsa_backward: the seven fragment-layout copies, then the
+// Workspace of bsa_backward: five fragment-layout and two tiled copies, then the
 // per-row lse (base 2) and Delta, then the transposed lists.
 struct BwdLayout {
     size_t frag[7], lse2, delta, mask, cnt, rowp, tlist, progress, total;
@@ -293,17 +293,19 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     char* w = static_cast<char*>(ws);
     uint16_t* f[7];
     for (int i = 0; i < 7; ++i) f[i] = reinterpret_cast<uint16_t*>(w + L.frag[i]);
-    // f: q_kf, do_kf, k_kf, v_kf (kfrag), k_vf, q_vf, do_vf (vfrag)
+    // f: q_kf, do_kf, k_kf, v_kf (kfrag), k_vf (vfrag), q_t, do_t (tiled)
     const uint16_t* src_kf[4] = {static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_o),
                                  static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
-    const uint16_t* src_vf[3] = {static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(q),
-                                 static_cast<const uint16_t*>(d_o)};
+    const uint16_t* src_t[2] = {static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_o)};
     hipError_t e = hipSuccess;
     for (int i = 0; i < 4 && e == hipSuccess; ++i)
         e = bsa::launch_gather_kf(src_kf[i], f[i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s);
-    for (int i = 0; i < 3 && e == hipSuccess; ++i)
-        e = bsa::launch_gather_vf(src_vf[i], f[4 + i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video,
-                                  s);
+    if (e == hipSuccess)
+        e = bsa::launch_gather_vf(static_cast<const uint16_t*>(k), f[4], perm, (int)g.B, (int)g.H, (int)g.D,
+                                  (int)g.npf, g.n_video, s);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
+        e = bsa::launch_permute_copy(false, src_t[i], f[5 + i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf,
+                                     g.n_video, s);
     if (e != hipSuccess) return launched(e);
     bsa::BackwardArgs a{};
     a.q_kf = f[0];
@@ -311,8 +313,8 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.k_kf = f[2];
     a.v_kf = f[3];
     a.k_vf = f[4];
-    a.q_vf = f[5];
-    a.do_vf = f[6];
+    a.q_t = f[5];
+    a.do_t = f[6];
     a.o = static_cast<const uint16_t*>(o);
     a.dout = static_cast<const uint16_t*>(d_o);
     a.lse = lse;

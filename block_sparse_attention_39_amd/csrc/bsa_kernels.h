@@ -67,7 +67,8 @@ hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_
 
 struct BackwardArgs {
     // fragment layouts of the tiled tensors (kfrag / vfrag of the C interface)
-    const uint16_t *q_kf, *do_kf, *k_kf, *v_kf, *k_vf, *q_vf, *do_vf;
+    const uint16_t *q_kf, *do_kf, *k_kf, *v_kf, *k_vf;
+    const uint16_t *q_t, *do_t;  // tiled [BH][Ntot][D]
     const uint16_t *o, *dout;  // raster [B][Ntot][H][D]
     const float* lse;          // [BH][Ntot] natural log, tiled order
     const int32_t* idx;        // [BH][nvt][keep]

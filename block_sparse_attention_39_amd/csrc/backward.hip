@@ -488,12 +488,29 @@ struct DkdvLds {
     static constexpr int OPS = C / 2 + 1;               // direct loads per wave per tile
 };
 
-// position of 16-byte chunk c of row r in LDS: c ^ rswz(r)
+// Position of 16-byte chunk c of row r in LDS: c ^ rswz(r).  LDS serves 64
+// banks of 4 bytes a cycle: 16 lanes of a 16-byte read or 32 lanes of an
+// 8-byte read.  rswz makes both operand reads of a stage conflict-free:
+//   * 16 lanes reading one chunk position of 16 distinct rows (rows
+//     swap23(0..15) + 16*m): rswz is a bijection on the bits that tell those
+//     rows apart within a bank row (all four low bits when a row is 256 bytes,
+//     bits 1..3 when two 128-byte rows share a bank row);
+//   * 32 lanes of a transposing read covering chunks 4*i .. 4*i + 3 of 4
+//     consecutive rows: the row's two low bits (D = 128; its bit 1 for D = 64,
+//     whose row parity picks the bank half) move the 4-chunk block.
 template <int D>
 __device__ inline int rswz(int r) {
-    return (2 * (r & 3) | ((r >> 3) & 1) | (((r >> 2) & 1) << 3)) & (D / 8 - 1);
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// Word 3 of a raw buffer resource (gfx9 family): 32-bit data format, no
+// swizzle; with stride 0 a lane's offset is checked against num_records.
+constexpr int kBufWord3 = 0x00020000;
+
+// Copies query tile tq's Q and dO rows (swizzled) and its lse (base 2) and
+// Delta into one LDS stage by direct buffer-to-LDS loads: C / 2 + 1 loads per
+// wave.  Buffer loads rather than global ones: the compiler treats a global
+// load into LDS as a flat access and then makes every LDS wait a full one.
 template <int D>
 __device__ __attribute__((always_inline)) inline void dma_query_tile(const BackwardArgs& a, int64_t bh, int tq,
                                                                      uint8_t* stage, const WaveId& w) {
@@ -502,20 +519,24 @@ __device__ __attribute__((always_inline)) inline void dma_query_tile(const Backw
     const int64_t row0 = bh * a.n_tot + (int64_t)tq * kTile;
     const uint16_t* src[2] = {a.q_t + row0 * D, a.do_t + row0 * D};
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src[u], 0, L::ROWS, kBufWord3);
 #pragma unroll
         for (int n = 0; n < C / 4; ++n) {
             const int blk = n * 4 + w.wave;   // 1 KB block of the region
             const int p = blk * 64 + w.lane;  // its 16-byte slot
             const int r = p / C;
             const int c = (p % C) ^ rswz<D>(r);
-            __builtin_amdgcn_global_load_lds((const void*)(src[u] + (r * C + c) * 8),
-                                             (lds_ptr_t)(stage + u * L::ROWS + blk * 1024), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + u * L::ROWS + blk * 1024), 16,
+                                                     (r * C + c) * 16, 0, 0, 0);
         }
+    }
     // lse (base 2) and Delta: wave w copies 32 of the 128 values
     if (w.lane < 32) {
-        const float* g = (w.wave < 2 ? a.lse2 : a.delta) + row0 + 32 * (w.wave & 1) + w.lane;
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)(stage + 2 * L::ROWS + w.wave * 128), 4, 0, 0);
+        const float* g = (w.wave < 2 ? a.lse2 : a.delta) + row0 + 32 * (w.wave & 1);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, 32 * 4, kBufWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + 2 * L::ROWS + w.wave * 128), 4, w.lane * 4, 0,
+                                                 0, 0);
     }
 }
 
@@ -598,75 +619,66 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
     // lse (base 2) and Delta of this lane's rows: element r = 8*c + e of
     // the accumulators is row 32*qh + 16*c + 8*hf + e
     const float* lse_row = (const float*)(st + 2 * L::ROWS) + 32 * qh + 8 * w.hf;
-    // 2*SD + 2*NV MFMA slots: S, dP, then dV and dK interleaved; the
-    // A operand of slot g is read from LDS LEAD slots ahead
+    // 2*SD + 2*NV MFMA slots: S (SD), dP (SD), dV (NV), dK (NV); the A
+    // operand of slot g is read from LDS LEAD slots ahead
     constexpr int NSL = 2 * SD + 2 * NV, LEAD = 3;
     auto a_read = [&](int g) -> bf16x8 {
         if (g < 2 * SD) {
             const int s2 = g % SD;
             return *(const bf16x8*)(st + (g < SD ? 0 : L::ROWS) + (qa_s ^ (32 * s2)));
         }
-        const int j = g - 2 * SD, f = j >> 1;  // fragment 2i + c: c = f / OD, i = f % OD
-        const int i = f % OD, c = f / OD;
-        const uint8_t* base = st + ((j & 1) ? 0 : L::ROWS);  // dK: Q^T, dV: dO^T
+        // dV (dO^T) then dK (Q^T), fragment i of query block c = j / OD
+        const int j = (g - 2 * SD) % NV, i = j % OD, c = j / OD;
+        const uint8_t* base = st + (g < 2 * SD + NV ? L::ROWS : 0);
         v4i16 h[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
             h[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16*)(base + (tb_s ^ (64 * ((i ^ 2 * h2) & (C / 4 - 1)))) + (16 * c + 4 * h2) * C * 16));
+                (lds_v4i16*)(base + (tb_s ^ (64 * i) ^ (16 * h2)) + (16 * c + 4 * h2) * C * 16));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // pair q of accumulator elements (2q, 2q + 1) is turned into weights
-    // and dS at slot use_slot(q): pairs 0..3 at the first dV/dK slot,
-    // pairs 4..7 spread over the first 2*OD of those slots (the ones that
-    // read elements 0..7 only); their lse and Delta are read two slots ahead
-    auto use_slot = [](int q) { return 2 * SD + (q < 4 ? 0 : (q - 4) * 2 * OD / 4); };
+    // The elementwise work is spread over the MFMA slots, one pair q of
+    // accumulator elements (2q, 2q + 1) at a time: its weights during the dP
+    // products (S is complete two slots after its last product), its dS during
+    // the dV products (likewise for dP); pairs 0..3 fill the first query block
+    // (c = 0) before the products that read it.  lse and Delta of a pair are
+    // read from LDS two slots before their use.
+    constexpr int PW = SD >= 8 ? 8 : SD - 2;
+    auto p_slot = [](int q) { return SD + 2 + q * PW / 8; };
+    auto ds_slot = [](int q) { return 2 * SD + 2 + q * PW / 8; };
     bf16x8 af[NSL];
 #pragma unroll
     for (int g = 0; g < LEAD; ++g) af[g] = a_read(g);
     f32x16 sc = f32x16{}, dp = f32x16{};
     bf16x8 pf[2], dsf[2];
-    f32x4 lo_l[2], lo_d[2];
-    f32x2 pl[8], pd[8];
+    float pw[16];      // weights P of the elements
+    f32x2 pl[8], pd[8];  // lse, Delta of pair q
 #pragma unroll
     for (int g = 0; g < NSL; ++g) {
         if (g + LEAD < NSL) af[g + LEAD] = a_read(g + LEAD);
-        if (g == use_slot(0) - 2) {
-            lo_l[0] = *(const f32x4*)lse_row;
-            lo_l[1] = *(const f32x4*)(lse_row + 4);
-            lo_d[0] = *(const f32x4*)(lse_row + 64);
-            lo_d[1] = *(const f32x4*)(lse_row + 68);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 2 * q, roff = 16 * (r >> 3) + (r & 7);  // row 32*qh + 8*hf + roff
+            if (g == p_slot(q) - 2) pl[q] = *(const f32x2*)(lse_row + roff);
+            if (g == ds_slot(q) - 2) pd[q] = *(const f32x2*)(lse_row + 64 + roff);
+            if (g == p_slot(q)) {
+                pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -pl[q][0]));
+                pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -pl[q][1]));
+                put_pair(pf, r, pw[r], pw[r + 1]);
+            }
+            if (g == ds_slot(q))
+                put_pair(dsf, r, pw[r] * (dp[r] - pd[q][0]), pw[r + 1] * (dp[r + 1] - pd[q][1]));
         }
-#pragma unroll
-        for (int q = 4; q < 8; ++q)
-            if (g == use_slot(q) - 2) {
-                const int r = 2 * q;  // c = 1, e = r - 8
-                pl[q] = *(const f32x2*)(lse_row + 16 + (r - 8));
-                pd[q] = *(const f32x2*)(lse_row + 64 + 16 + (r - 8));
-            }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (g == use_slot(q)) {
-                const int r = 2 * q;
-                const float l0 = q < 4 ? lo_l[q >> 1][r & 3] : pl[q][0];
-                const float l1 = q < 4 ? lo_l[q >> 1][(r & 3) + 1] : pl[q][1];
-                const float d0 = q < 4 ? lo_d[q >> 1][r & 3] : pd[q][0];
-                const float d1 = q < 4 ? lo_d[q >> 1][(r & 3) + 1] : pd[q][1];
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -l0));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -l1));
-                put_pair(pf, r, p0, p1);
-                put_pair(dsf, r, p0 * (dp[r] - d0), p1 * (dp[r + 1] - d1));
-            }
         if (g < SD) {
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], kreg[g], sc, 0, 0, 0);
         } else if (g < 2 * SD) {
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], vreg[g - SD], dp, 0, 0, 0);
         } else {
-            const int j = g - 2 * SD, f = j >> 1, c = f / OD, i = f % OD;
-            if (j & 1)
-                dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], dsf[c], dk[i], 0, 0, 0);
-            else
+            const int j = (g - 2 * SD) % NV, i = j % OD, c = j / OD;
+            if (g < 2 * SD + NV)
                 dv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], pf[c], dv[i], 0, 0, 0);
+            else
+                dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], dsf[c], dk[i], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -717,9 +729,9 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
     //   offset = qa ^ (32 * s),  qa = rq*C*16 ^ ((hf ^ rswz(rq)) * 16)
     // dV^T / dK^T A operand (32 channels x 16 rows), two transposing reads
     // h2 = 0, 1 per fragment (i, c): input lane (G, ta, te) of 16-lane group G
-    // addresses row 32*qh + 16*c + 8*(G/2) + 4*h2 + te, chunk
-    // 4*i + 2*(G%2) + ta/2, bytes 8*(ta%2).  With rswz of that row,
-    //   offset = tb ^ (64 * ((i ^ 2*h2) & (C/4 - 1))) + (16*c + 4*h2) * C * 16
+    // addresses row r = r0 + 16*c + 4*h2, r0 = 32*qh + 8*(G/2) + te, chunk
+    // 4*i + 2*(G%2) + ta/2, bytes 8*(ta%2).  rswz(r) = rswz(r0) ^ h2, so
+    //   offset = tb ^ (64 * i) ^ (16 * h2) + (16*c + 4*h2) * C * 16
     DkdvLane ln;
     ln.qh = qh;
     ln.hf = w.hf;
@@ -727,8 +739,8 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
         const int rq = 32 * qh + swap23(w.lr);
         ln.qa = (rq * C * 16) ^ ((w.hf ^ rswz<D>(rq)) * 16);
         const int G = w.lane >> 4, ta = w.lane & 3, te = (w.lane >> 2) & 3;
-        ln.tb = ((32 * qh + 8 * (G >> 1) + te) * C * 16) |
-                (((2 * (G & 1) + (ta >> 1)) ^ ((2 * te | (G >> 1)) & (C - 1))) * 16) | ((ta & 1) * 8);
+        const int r0 = 32 * qh + 8 * (G >> 1) + te;
+        ln.tb = (r0 * C * 16) | (((2 * (G & 1) + (ta >> 1)) ^ rswz<D>(r0)) * 16) | ((ta & 1) * 8);
     }
 
     if (n_iter > 0) {

@@ -79,6 +79,8 @@ __device__ inline uint16_t* raster_row(uint16_t* base, const BackwardArgs& a, in
 }
 
 // ---- Delta = dO . O and lse in base 2, per tiled row ----------------------
+// Also -lse / scale and -Delta: the dK/dV kernel starts its S and dP
+// accumulators from them, so that exp2(c2 * S') = P and P * dP' = dS.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * n_tot + row
@@ -97,6 +99,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
     }
     a.delta[r] = s;
     a.lse2[r] = a.lse[r] * kLog2e;
+    a.ndelta[r] = -s;
+    a.nlse[r] = -a.lse[r] / a.scale;
 }
 
 // ---- transposed lists: for each video key tile, the video query tiles that
@@ -482,7 +486,7 @@ template <int D>
 struct DkdvLds {
     static constexpr int C = D / 8;                     // 16-byte chunks of a row
     static constexpr int ROWS = kTile * D * 2;          // bytes of one tensor's rows
-    static constexpr int STAGE = 2 * ROWS + 512;        // Q rows, dO rows, lse (base 2), Delta
+    static constexpr int STAGE = 2 * ROWS + 512;        // Q rows, dO rows, -lse / scale, -Delta
     static constexpr int MERGE = kTile * BCfg<D>::MROW * 4;  // [64][MROW] floats
     static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
     static constexpr int OPS = C / 2 + 1;               // direct loads per wave per tile
@@ -507,8 +511,8 @@ __device__ inline int rswz(int r) {
 // swizzle; with stride 0 a lane's offset is checked against num_records.
 constexpr int kBufWord3 = 0x00020000;
 
-// Copies query tile tq's Q and dO rows (swizzled) and its lse (base 2) and
-// Delta into one LDS stage by direct buffer-to-LDS loads: C / 2 + 1 loads per
+// Copies query tile tq's Q and dO rows (swizzled) and its -lse / scale and
+// -Delta into one LDS stage by direct buffer-to-LDS loads: C / 2 + 1 loads per
 // wave.  Buffer loads rather than global ones: the compiler treats a global
 // load into LDS as a flat access and then makes every LDS wait a full one.
 template <int D>
@@ -533,7 +537,7 @@ __device__ __attribute__((always_inline)) inline void dma_query_tile(const Backw
     }
     // lse (base 2) and Delta: wave w copies 32 of the 128 values
     if (w.lane < 32) {
-        const float* g = (w.wave < 2 ? a.lse2 : a.delta) + row0 + 32 * (w.wave & 1);
+        const float* g = (w.wave < 2 ? a.nlse : a.ndelta) + row0 + 32 * (w.wave & 1);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, 32 * 4, kBufWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + 2 * L::ROWS + w.wave * 128), 4, w.lane * 4, 0,
                                                  0, 0);
@@ -616,9 +620,23 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
     // derived from them are formed where they are used
     int qa_s = ln.qa, tb_s = ln.tb;
     asm volatile("" : "+v"(qa_s), "+v"(tb_s));
-    // lse (base 2) and Delta of this lane's rows: element r = 8*c + e of
-    // the accumulators is row 32*qh + 16*c + 8*hf + e
-    const float* lse_row = (const float*)(st + 2 * L::ROWS) + 32 * qh + 8 * w.hf;
+    // S and dP start from -lse / scale and -Delta of their rows (accumulator
+    // element r = 8*c + e is row 32*qh + 16*c + 8*hf + e), so that the
+    // weights are exp2(c2 * S) and dS = P * dP
+    const float* init_row = (const float*)(st + 2 * L::ROWS) + 32 * qh + 8 * w.hf;
+    f32x16 sc, dp;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 x = *(const f32x4*)(init_row + 16 * c + 4 * h);
+            const f32x4 y = *(const f32x4*)(init_row + 64 + 16 * c + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sc[8 * c + 4 * h + e] = x[e];
+                dp[8 * c + 4 * h + e] = y[e];
+            }
+        }
     // 2*SD + 2*NV MFMA slots: S (SD), dP (SD), dV (NV), dK (NV); the A
     // operand of slot g is read from LDS LEAD slots ahead
     constexpr int NSL = 2 * SD + 2 * NV, LEAD = 3;
@@ -641,33 +659,27 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
     // accumulator elements (2q, 2q + 1) at a time: its weights during the dP
     // products (S is complete two slots after its last product), its dS during
     // the dV products (likewise for dP); pairs 0..3 fill the first query block
-    // (c = 0) before the products that read it.  lse and Delta of a pair are
-    // read from LDS two slots before their use.
+    // (c = 0) before the products that read it.
     constexpr int PW = SD >= 8 ? 8 : SD - 2;
     auto p_slot = [](int q) { return SD + 2 + q * PW / 8; };
     auto ds_slot = [](int q) { return 2 * SD + 2 + q * PW / 8; };
     bf16x8 af[NSL];
 #pragma unroll
     for (int g = 0; g < LEAD; ++g) af[g] = a_read(g);
-    f32x16 sc = f32x16{}, dp = f32x16{};
     bf16x8 pf[2], dsf[2];
-    float pw[16];      // weights P of the elements
-    f32x2 pl[8], pd[8];  // lse, Delta of pair q
+    float pw[16];  // weights P of the elements
 #pragma unroll
     for (int g = 0; g < NSL; ++g) {
         if (g + LEAD < NSL) af[g + LEAD] = a_read(g + LEAD);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int r = 2 * q, roff = 16 * (r >> 3) + (r & 7);  // row 32*qh + 8*hf + roff
-            if (g == p_slot(q) - 2) pl[q] = *(const f32x2*)(lse_row + roff);
-            if (g == ds_slot(q) - 2) pd[q] = *(const f32x2*)(lse_row + 64 + roff);
+            const int r = 2 * q;
             if (g == p_slot(q)) {
-                pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -pl[q][0]));
-                pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], c2, -pl[q][1]));
+                pw[r] = __builtin_amdgcn_exp2f(sc[r] * c2);
+                pw[r + 1] = __builtin_amdgcn_exp2f(sc[r + 1] * c2);
                 put_pair(pf, r, pw[r], pw[r + 1]);
             }
-            if (g == ds_slot(q))
-                put_pair(dsf, r, pw[r] * (dp[r] - pd[q][0]), pw[r + 1] * (dp[r + 1] - pd[q][1]));
+            if (g == ds_slot(q)) put_pair(dsf, r, pw[r] * dp[r], pw[r + 1] * dp[r + 1]);
         }
         if (g < SD) {
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], kreg[g], sc, 0, 0, 0);

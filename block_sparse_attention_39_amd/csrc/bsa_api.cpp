@@ -95,9 +95,10 @@ Layout layout(const Geo& g) {
 bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LAUNCH; }
 
 // Workspace of bsa_backward: five fragment-layout and two tiled copies, then the
-// per-row lse (base 2) and Delta, then the transposed lists.
+// per-row lse (base 2) and Delta and their negated forms, then the transposed
+// lists.
 struct BwdLayout {
-    size_t frag[7], lse2, delta, mask, cnt, rowp, tlist, progress, total;
+    size_t frag[7], lse2, delta, nlse, ndelta, mask, cnt, rowp, tlist, progress, total;
     int mwords;
 };
 
@@ -109,6 +110,10 @@ BwdLayout bwd_layout(const Geo& g) {
     L.lse2 = o;
     o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
     L.delta = o;
+    o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
+    L.nlse = o;
+    o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
+    L.ndelta = o;
     o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
     L.mwords = (int)((g.nvt + 31) / 32);
     L.mask = o;
@@ -322,6 +327,8 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.perm = perm;
     a.lse2 = reinterpret_cast<float*>(w + L.lse2);
     a.delta = reinterpret_cast<float*>(w + L.delta);
+    a.nlse = reinterpret_cast<float*>(w + L.nlse);
+    a.ndelta = reinterpret_cast<float*>(w + L.ndelta);
     a.mask = reinterpret_cast<uint32_t*>(w + L.mask);
     a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
     a.rowp = reinterpret_cast<int32_t*>(w + L.rowp);

@@ -74,6 +74,7 @@ struct BackwardArgs {
     const int32_t* idx;        // [BH][nvt][keep]
     const int32_t* perm;       // [B][Nvideo]
     float *lse2, *delta;       // [BH][Ntot] scratch: lse * log2 e, dO . O
+    float *nlse, *ndelta;      // [BH][Ntot] scratch: -lse / scale, -(dO . O)
     uint32_t* mask;            // [BH][nvt][mwords] scratch
     int32_t *cnt, *rowp, *tlist;  // [BH][nvt], [BH][nvt + 1], [BH][nvt * keep] scratch
     uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]

@@ -442,24 +442,26 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
 }
 
 // ---- dK, dV -----------------------------------------------------------------
-// The block walks the query tiles that attend its key tile.  Each query tile's
-// Q and dO rows (tiled layout, 2 x 16 KB for D = 128) and its 64 values of lse
-// and Delta are copied into LDS once, by direct global-to-LDS loads, two tiles
-// ahead into the third of three stages.  In LDS the rows are kept whole with
-// their 16-byte chunks XOR-swizzled by the row, so that both operand shapes
-// read without bank conflicts:
+// One block of 8 waves per key tile walks the query tiles that attend it.  The
+// waves form two quads; quad p takes the walk's tiles p, p + 2, p + 4, ... and
+// wave (p, qh, kh) of it query half qh of those tiles against key half kh.
+// Two waves share each SIMD, so that the vector, scalar and LDS instructions
+// of one issue while the other's matrix products run.  Each wave keeps the K
+// fragments of its key half in registers and reads V's from LDS (the key
+// tile's V, 16 KB for D = 128, staged once per key tile), and accumulates its
+// own partial dK^T and dV^T; the four partials of a key half are summed once
+// per key tile.
+//
+// Each query tile's Q and dO rows (tiled layout, 2 x 16 KB for D = 128) and
+// its 64 values of -lse / scale and -Delta are copied into LDS once, by direct
+// loads, one step ahead into the quad's other stage.  In LDS the rows are kept
+// whole with their 16-byte chunks XOR-swizzled by the row, so that both
+// operand shapes read without bank conflicts:
 //   * S = Q K^T and dP = dO V^T take Q and dO as A operands of 32 rows by 16
 //     channels: one 16-byte read per lane;
 //   * dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T, 32 channels by 16
 //     rows: two transposing reads (ds_read_b64_tr_b16) per lane, each giving a
 //     lane 4 consecutive rows of its channel.
-// Wave (qh, kh) takes query half qh of every tile and keeps the K and V
-// fragments of its key half kh in registers for the whole walk.
-//
-// The three stages are three LDS arrays and the walk is unrolled by three, so
-// that each step names its stages at compile time: the compiler can then tell
-// the reads of one stage from the direct loads into another and does not make
-// the reads wait for those loads.  The waits for the loads are explicit.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -482,14 +484,34 @@ __device__ __attribute__((always_inline)) inline void block_barrier() {
 // memory loads in flight
 __device__ inline int scalar_load(const int32_t* p) { return *(const_i32*)p; }
 
+constexpr int kDkdvThreads = 512;
+
 template <int D>
 struct DkdvLds {
-    static constexpr int C = D / 8;                     // 16-byte chunks of a row
-    static constexpr int ROWS = kTile * D * 2;          // bytes of one tensor's rows
-    static constexpr int STAGE = 2 * ROWS + 512;        // Q rows, dO rows, -lse / scale, -Delta
-    static constexpr int MERGE = kTile * BCfg<D>::MROW * 4;  // [64][MROW] floats
-    static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
-    static constexpr int OPS = C / 2 + 1;               // direct loads per wave per tile
+    static constexpr int C = D / 8;                          // 16-byte chunks of a row
+    static constexpr int ROWS = kTile * D * 2;               // bytes of one tensor's rows
+    static constexpr int STAGE = 2 * ROWS + 512;             // Q rows, dO rows, -lse / scale, -Delta
+    static constexpr int VB = kTile * D * 2;                 // the key tile's V (K-fragment layout)
+    static constexpr int MERGE = kTile * BCfg<D>::MROW * 4;  // [64][MROW] floats, over the stages
+    static constexpr int BYTES = VB + 4 * STAGE;             // V, then stages (buffer, quad)
+    static constexpr int OPS = C / 2 + 1;                    // direct loads per wave per tile
+    static_assert(4 * STAGE >= MERGE, "merge block must fit in the stages");
+};
+
+// wave (p, qh, kh) of the dK/dV block
+struct DkdvWave {
+    int tid, wave, lane, quad, qw, qh, kh, lr, hf;
+    __device__ DkdvWave() {
+        tid = threadIdx.x;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        lane = tid & 63;
+        quad = wave >> 2;
+        qw = wave & 3;  // wave within the quad
+        qh = (wave >> 1) & 1;
+        kh = wave & 1;
+        lr = lane & 31;
+        hf = lane >> 5;
+    }
 };
 
 // Position of 16-byte chunk c of row r in LDS: c ^ rswz(r).  LDS serves 64
@@ -512,73 +534,76 @@ __device__ inline int rswz(int r) {
 constexpr int kBufWord3 = 0x00020000;
 
 // Copies query tile tq's Q and dO rows (swizzled) and its -lse / scale and
-// -Delta into one LDS stage by direct buffer-to-LDS loads: C / 2 + 1 loads per
-// wave.  Buffer loads rather than global ones: the compiler treats a global
-// load into LDS as a flat access and then makes every LDS wait a full one.
+// -Delta into one LDS stage by direct buffer-to-LDS loads, shared by the four
+// waves of a quad: OPS = C / 2 + 1 loads per wave, which the caller issues one
+// at a time (op(k), k < OPS) spread over a step, so that they enter the memory
+// pipeline gradually.  Buffer loads rather than global ones: the compiler
+// treats a global load into LDS as a flat access and then makes every LDS wait
+// a full one.
 template <int D>
-__device__ __attribute__((always_inline)) inline void dma_query_tile(const BackwardArgs& a, int64_t bh, int tq,
-                                                                     uint8_t* stage, const WaveId& w) {
+struct QueryTileLoad {
     using L = DkdvLds<D>;
-    constexpr int C = L::C;
-    const int64_t row0 = bh * a.n_tot + (int64_t)tq * kTile;
-    const uint16_t* src[2] = {a.q_t + row0 * D, a.do_t + row0 * D};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src[u], 0, L::ROWS, kBufWord3);
-#pragma unroll
-        for (int n = 0; n < C / 4; ++n) {
-            const int blk = n * 4 + w.wave;   // 1 KB block of the region
-            const int p = blk * 64 + w.lane;  // its 16-byte slot
+    static constexpr int C = L::C;
+    __amdgpu_buffer_rsrc_t rs[2], rl;
+    uint8_t* stage;
+    int qw, lane;
+    __device__ __attribute__((always_inline)) QueryTileLoad(const BackwardArgs& a, int64_t bh, int tq, uint8_t* st,
+                                                            const DkdvWave& w)
+        : stage(st), qw(w.qw), lane(w.lane) {
+        const int64_t row0 = bh * a.n_tot + (int64_t)tq * kTile;
+        rs[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q_t + row0 * D), 0, L::ROWS, kBufWord3);
+        rs[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.do_t + row0 * D), 0, L::ROWS, kBufWord3);
+        // -lse / scale and -Delta: wave qw copies 32 of the 128 values
+        const float* g = (qw < 2 ? a.nlse : a.ndelta) + row0 + 32 * (qw & 1);
+        rl = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, 32 * 4, kBufWord3);
+    }
+    __device__ __attribute__((always_inline)) void op(int k) const {
+        if (k < C / 2) {
+            const int u = k / (C / 4), n = k % (C / 4);
+            const int blk = n * 4 + qw;     // 1 KB block of the region
+            const int p = blk * 64 + lane;  // its 16-byte slot
             const int r = p / C;
             const int c = (p % C) ^ rswz<D>(r);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + u * L::ROWS + blk * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[u], (lds_ptr_t)(stage + u * L::ROWS + blk * 1024), 16,
                                                      (r * C + c) * 16, 0, 0, 0);
+        } else if (lane < 32) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(stage + 2 * L::ROWS + qw * 128), 4, lane * 4, 0,
+                                                     0, 0);
         }
     }
-    // lse (base 2) and Delta: wave w copies 32 of the 128 values
-    if (w.lane < 32) {
-        const float* g = (w.wave < 2 ? a.nlse : a.ndelta) + row0 + 32 * (w.wave & 1);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, 0, 32 * 4, kBufWord3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + 2 * L::ROWS + w.wave * 128), 4, w.lane * 4, 0,
-                                                 0, 0);
-    }
-}
+};
 
-// Sums the two query halves' partial dK^T (or dV^T) of key tile `tile` in one
-// [64 keys][MROW] float block of LDS and writes it, times `mul`, as bf16 rows
-// of the raster output.  Wave (qh, kh) holds key half kh: the qh = 1 waves
-// store, the qh = 0 waves add theirs in place, then all threads write rows.
+// Sums the four partial dK^T (or dV^T) of each key half of key tile `tile` in
+// one [64 keys][MROW] float block of LDS, in a fixed order, and writes it,
+// times `mul`, as bf16 rows of the raster output.
 template <int D>
-__device__ __attribute__((always_inline)) inline void merge_halves(float* lds, const f32x16 (&acc)[D / 32],
-                                                                   const WaveId& w, float mul, const BackwardArgs& a,
-                                                                   int64_t bh, int tile, uint16_t* out) {
+__device__ __attribute__((always_inline)) inline void merge_partials(float* lds, const f32x16 (&acc)[D / 32],
+                                                                     const DkdvWave& w, float mul,
+                                                                     const BackwardArgs& a, int64_t bh, int tile,
+                                                                     uint16_t* out) {
     constexpr int OD = D / 32, MROW = BCfg<D>::MROW, C = D / 8;
     const int tok = 32 * w.kh + swap23(w.lr);
     float* mine = lds + tok * MROW + 4 * w.hf;
-    block_barrier();  // the previous user of the block is done
-    if (w.par == 1) {
+    const int order = 2 * w.quad + w.qh;  // 3 stores, 2, 1, 0 add in turn
+    block_barrier();                      // the previous user of the block is done
 #pragma unroll
-        for (int i = 0; i < OD; ++i)
+    for (int turn = 3; turn >= 0; --turn) {
+        if (order == turn) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *(f32x4*)(mine + 32 * i + 8 * j) =
-                    f32x4{acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
+            for (int i = 0; i < OD; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f32x4* p = (f32x4*)(mine + 32 * i + 8 * j);
+                    const f32x4 v = {acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
+                    *p = turn == 3 ? v : *p + v;
+                }
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    if (w.par == 0) {
-#pragma unroll
-        for (int i = 0; i < OD; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4* p = (f32x4*)(mine + 32 * i + 8 * j);
-                *p = *p + f32x4{acc[i][4 * j], acc[i][4 * j + 1], acc[i][4 * j + 2], acc[i][4 * j + 3]};
-            }
-    }
-    __syncthreads();
     const int b = (int)(bh / a.H);
 #pragma unroll
-    for (int u = 0; u < kTile * C / 256; ++u) {
-        const int cidx = w.tid + 256 * u;
+    for (int u = 0; u < kTile * C / kDkdvThreads; ++u) {
+        const int cidx = w.tid + kDkdvThreads * u;
         const int r = cidx / C, c = cidx % C;
         const f32x4 s0 = *(const f32x4*)(lds + r * MROW + 8 * c);
         const f32x4 s1 = *(const f32x4*)(lds + r * MROW + 8 * c + 4);
@@ -597,25 +622,26 @@ __device__ __attribute__((always_inline)) inline void merge_halves(float* lds, c
 
 // Per-lane constants of the dK/dV walk (see dkdv_tile).
 struct DkdvLane {
-    int qh, hf;  // query half of the wave, lane half
     int qa, tb;  // LDS offsets of the two operand shapes
 };
 
-// One query tile of the dK/dV walk: the tile's Q and dO rows, lse and Delta
-// are in LDS at `st`; when `nx` is not null the tile after next is loaded into
-// it first.  The two pointers are declared not to alias: the compiler then
-// leaves the reads of `st` free of waits for the loads into `nx` (the caller
-// waits for those explicitly before their stage is read).
+// One query tile of the dK/dV walk for one wave: the tile's Q and dO rows,
+// -lse / scale and -Delta are in LDS at `st`, the key tile's V at `vl`; when
+// `nx` is not null the quad's next tile is loaded into it first.  The
+// pointers are declared not to alias: the compiler then leaves the reads of
+// `st` and `vl` free of waits for the loads into `nx` (the caller waits for
+// those explicitly before their stage is read).
 template <int D>
 __device__ __attribute__((always_inline)) inline void dkdv_step(
-    const BackwardArgs& a, const uint8_t* __restrict__ st, uint8_t* __restrict__ nx, int64_t bh, int tq_next,
-    const WaveId& w, const DkdvLane& ln, const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
-    f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    const BackwardArgs& a, const uint8_t* __restrict__ st, const uint8_t* __restrict__ vl,
+    uint8_t* __restrict__ nx, int64_t bh, int tq_next, const DkdvWave& w, const DkdvLane& ln,
+    const bf16x8 (&kreg)[D / 16], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
     using L = DkdvLds<D>;
     constexpr int SD = D / 16, OD = D / 32, NV = 2 * OD, C = L::C;
     const float c2 = a.scale_log2;
-    const int qh = ln.qh;
-    if (nx) dma_query_tile<D>(a, bh, tq_next, nx, w);
+    const int qh = w.qh;
+    // the quad's next tile: one load in each of the first OPS slots
+    const QueryTileLoad<D> ld(a, bh, tq_next, nx, w);
     // fresh copies of the lane offsets for this step, so that the offsets
     // derived from them are formed where they are used
     int qa_s = ln.qa, tb_s = ln.tb;
@@ -638,8 +664,10 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
             }
         }
     // 2*SD + 2*NV MFMA slots: S (SD), dP (SD), dV (NV), dK (NV); the A
-    // operand of slot g is read from LDS LEAD slots ahead
+    // operand of slot g (and V's fragment for a dP slot) is read from LDS
+    // LEAD slots ahead
     constexpr int NSL = 2 * SD + 2 * NV, LEAD = 3;
+    const uint8_t* vh = vl + w.kh * (L::VB / 2) + w.lane * 16;
     auto a_read = [&](int g) -> bf16x8 {
         if (g < 2 * SD) {
             const int s2 = g % SD;
@@ -663,7 +691,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
     constexpr int PW = SD >= 8 ? 8 : SD - 2;
     auto p_slot = [](int q) { return SD + 2 + q * PW / 8; };
     auto ds_slot = [](int q) { return 2 * SD + 2 + q * PW / 8; };
-    bf16x8 af[NSL];
+    bf16x8 af[NSL], vf[SD];
 #pragma unroll
     for (int g = 0; g < LEAD; ++g) af[g] = a_read(g);
     bf16x8 pf[2], dsf[2];
@@ -671,6 +699,8 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
 #pragma unroll
     for (int g = 0; g < NSL; ++g) {
         if (g + LEAD < NSL) af[g + LEAD] = a_read(g + LEAD);
+        if (g + LEAD >= SD && g + LEAD < 2 * SD) vf[g + LEAD - SD] = *(const bf16x8*)(vh + (g + LEAD - SD) * 1024);
+        if (nx && g < L::OPS) ld.op(g);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = 2 * q;
@@ -684,7 +714,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
         if (g < SD) {
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], kreg[g], sc, 0, 0, 0);
         } else if (g < 2 * SD) {
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], vreg[g - SD], dp, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[g], vf[g - SD], dp, 0, 0, 0);
         } else {
             const int j = (g - 2 * SD) % NV, i = j % OD, c = j / OD;
             if (g < 2 * SD + NV)
@@ -698,13 +728,15 @@ __device__ __attribute__((always_inline)) inline void dkdv_step(
 
 template <int D>
 __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardArgs& a, uint8_t* smem, int64_t bh,
-                                                                int kt, const WaveId& w) {
+                                                                int kt, const DkdvWave& w) {
     using CF = BCfg<D>;
     using L = DkdvLds<D>;
     constexpr int SD = CF::SD, OD = CF::OD, TB = CF::TB, C = L::C;
-    const int qh = w.par;  // this wave's query half; w.kh its key half
+    const int qh = w.qh;
     const int n_tiles = a.npt + a.nvt;
-    block_barrier();       // the previous tile's epilogue is done with LDS
+    uint8_t* const vl = smem;            // the key tile's V
+    uint8_t* const stages = smem + L::VB;  // stage (buffer, quad) at (2 * buffer + quad) * STAGE
+    block_barrier();                     // the previous tile's epilogue is done with LDS
 
     // the query tiles that attend key tile kt: every tile for a prefix key
     // tile; the prefix tiles and then the transposed list for a video one
@@ -723,12 +755,20 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
         return a.npt + min(max(scalar_load(tl + n), 0), a.nvt - 1);
     };
 
-    // stationary: K and V fragments of key half kh (B operands: key = lane)
-    bf16x8 kreg[SD], vreg[SD];
+    // K fragments of key half kh in registers (B operands: key = lane); the
+    // key tile's V into LDS (2 KB per wave)
+    bf16x8 kreg[SD];
+    const int64_t tile_off = (bh * n_tiles + kt) * (int64_t)TB;
+    load_n(kreg, (const uint8_t*)a.k_kf + tile_off + w.kh * CF::HALF + w.lane * 16);
     {
-        const int64_t off = (bh * n_tiles + kt) * (int64_t)TB + w.kh * CF::HALF + w.lane * 16;
-        load_n(kreg, (const uint8_t*)a.k_kf + off);
-        load_n(vreg, (const uint8_t*)a.v_kf + off);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.v_kf + tile_off), 0, TB, kBufWord3);
+#pragma unroll
+        for (int j = 0; j < TB / 1024 / 8; ++j) {
+            const int blk = w.wave * (TB / 1024 / 8) + j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(vl + blk * 1024), 16, blk * 1024 + w.lane * 16,
+                                                     0, 0, 0);
+        }
     }
     f32x16 dk[OD], dv[OD];
 #pragma unroll
@@ -745,8 +785,6 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
     // 4*i + 2*(G%2) + ta/2, bytes 8*(ta%2).  rswz(r) = rswz(r0) ^ h2, so
     //   offset = tb ^ (64 * i) ^ (16 * h2) + (16*c + 4*h2) * C * 16
     DkdvLane ln;
-    ln.qh = qh;
-    ln.hf = w.hf;
     {
         const int rq = 32 * qh + swap23(w.lr);
         ln.qa = (rq * C * 16) ^ ((w.hf ^ rswz<D>(rq)) * 16);
@@ -755,35 +793,32 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
         ln.tb = (r0 * C * 16) | (((2 * (G & 1) + (ta >> 1)) ^ rswz<D>(r0)) * 16) | ((ta & 1) * 8);
     }
 
-    if (n_iter > 0) {
-        dma_query_tile<D>(a, bh, tile_of(0), smem, w);
-        if (n_iter > 1) {
-            dma_query_tile<D>(a, bh, tile_of(1), smem + L::BYTES, w);
-            __builtin_amdgcn_s_waitcnt(wait_vm(L::OPS));
-        } else {
-            __builtin_amdgcn_s_waitcnt(wait_vm(0));
-        }
-        block_barrier();
-        int cur = 0;
-        for (int n = 0; n < n_iter; ++n) {
-            // tile n is in stage cur; the tile after next goes to the stage
-            // tile n - 1 used
-            const int nxt = cur == 0 ? 2 : cur - 1;
-            const bool ahead = n + 2 < n_iter;
-            dkdv_step<D>(a, smem + cur * L::BYTES, ahead ? smem + nxt * L::BYTES : nullptr, bh,
-                         ahead ? tile_of(n + 2) : 0, w, ln, kreg, vreg, dk, dv);
-            // the next tile landed (this wave's part; the tile after it may
-            // stay in flight), then everyone's, and this stage is free again
-            if (ahead)
-                __builtin_amdgcn_s_waitcnt(wait_vm(L::OPS));
-            else
-                __builtin_amdgcn_s_waitcnt(wait_vm(0));
-            block_barrier();
-            cur = cur == 2 ? 0 : cur + 1;
-        }
+    // step m: quad p computes tile 2m + p from stage (m % 2, p) and loads tile
+    // 2m + 2 + p into stage ((m + 1) % 2, p)
+    const int n_steps = (n_iter + 1) / 2;
+    if (w.quad < n_iter) {
+        const QueryTileLoad<D> ld(a, bh, tile_of(w.quad), stages + w.quad * L::STAGE, w);
+#pragma unroll
+        for (int k = 0; k < L::OPS; ++k) ld.op(k);
     }
-    merge_halves<D>((float*)smem, dk, w, a.scale, a, bh, kt, a.dk);
-    merge_halves<D>((float*)smem, dv, w, 1.f, a, bh, kt, a.dv);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // K, V and the first tiles
+    block_barrier();
+    for (int m = 0; m < n_steps; ++m) {
+        const int t = 2 * m + w.quad, tn = t + 2;
+        const int buf = m & 1;
+        if (t < n_iter) {
+            dkdv_step<D>(a, stages + (2 * buf + w.quad) * L::STAGE, vl,
+                         tn < n_iter ? stages + (2 * (buf ^ 1) + w.quad) * L::STAGE : nullptr, bh,
+                         tn < n_iter ? tile_of(tn) : 0, w, ln, kreg, dk, dv);
+        }
+        // the quad's next tile has landed (this wave's part), then everyone's,
+        // and this step's stages are free again
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        block_barrier();
+    }
+    float* merge = (float*)stages;
+    merge_partials<D>(merge, dk, w, a.scale, a, bh, kt, a.dk);
+    merge_partials<D>(merge, dv, w, 1.f, a, bh, kt, a.dv);
 }
 
 // Persistent launch of a per-tile body over the BH * (npt + nvt) tiles: block b
@@ -833,10 +868,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BackwardArgs a,
-                                                                                                int* progress) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[3 * DkdvLds<D>::BYTES];
-    const WaveId w;
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
+    BackwardArgs a, int* progress) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DkdvLds<D>::BYTES];
+    const DkdvWave w;
     grouped_rounds(a, progress, [&](int64_t bh, int kt) { dkdv_tile<D>(a, smem, bh, kt, w); });
 }
 
@@ -845,11 +880,11 @@ __global__ void bwd_clear_progress_kernel(int* progress, int n) {
 }
 
 template <typename K>
-hipError_t grouped_grid(K kernel, int64_t work, int64_t* grid) {
+hipError_t grouped_grid(K kernel, int threads, int64_t work, int64_t* grid) {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
     if (e != hipSuccess) return e;
     int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     g = g / kGroupsB * kGroupsB;
@@ -875,14 +910,14 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     }
     const int64_t tiles = (int64_t)a.BH * (a.npt + a.nvt);
     int64_t gq = 0, gk = 0;
-    hipError_t e = grouped_grid(bwd_dq_kernel<D>, tiles, &gq);
-    if (e == hipSuccess) e = grouped_grid(bwd_dkdv_kernel<D>, tiles, &gk);
+    hipError_t e = grouped_grid(bwd_dq_kernel<D>, 256, tiles, &gq);
+    if (e == hipSuccess) e = grouped_grid(bwd_dkdv_kernel<D>, kDkdvThreads, tiles, &gk);
     if (e != hipSuccess) return e;
     constexpr int NP = kGroupsB * kMaxGroupSizeB;
     hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(256), 0, s, a, a.progress);
     hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(256), 0, s, a, a.progress);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kDkdvThreads), 0, s, a, a.progress);
     return hipGetLastError();
 }
 

@@ -20,6 +20,11 @@ times the backward instead (bsa_backward: dQ, dK, dV from the forward's
 output and lse and a synthetic dO, inputs resident in HBM) and prints its own
 line: 2.5 x the forward's effective FLOPs (the five products of the gradient:
 S and dP recomputed, dV, dK, dQ) per second.
+
+    python bench.py --varkeep 480,192,120,96 [...]
+
+times the variable-keep path instead (bsa_plan_csr / bsa_forward_csr): head h
+keeps the (h mod 4)-th count of the list; effective FLOPs from those counts.
 """
 from __future__ import annotations
 
@@ -40,6 +45,7 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (256 CUs x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective TFLOP/s (kept tiles) + ms/call, 122,880-token grid @25% keep, 1 GPU"
 METRIC_BWD = "backward effective TFLOP/s (2.5x forward FLOPs, kept tiles) + ms/call, 1 GPU"
+METRIC_VAR = "variable-keep effective TFLOP/s (kept tiles, per-head keep) + ms/call, 1 GPU"
 
 
 def parse():
@@ -53,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-tiles", type=int, default=960, help="query tiles in the CPU oracle sample")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (bsa_backward)")
     ap.add_argument("--cpu-bwd-tiles", type=int, default=120, help="query and key tiles in the backward CPU sample")
+    ap.add_argument("--varkeep", default=None,
+                    help="comma-separated keep counts cycled over the heads: time the CSR (variable keep) path")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -115,6 +123,132 @@ def cpu_baseline(wl, q, k, v, n_tiles: int):
                    f"({t_attn:.2f} s), extrapolated linearly to the head and scaled by the head's share of "
                    f"the effective FLOPs"),
     }
+
+
+def varkeep_flops(wl, keep_h):
+    """4 * B * D * sum over heads and query tokens of the keys attended, with
+    head h keeping keep_h[h] tiles per video query tile."""
+    pairs = 0
+    for kh in keep_h:
+        pairs += wl.n_prefix * wl.n_tokens + wl.n_video * (wl.n_prefix + kh * 64)
+    return 4.0 * wl.batch * wl.head_dim * pairs
+
+
+def cpu_baseline_varkeep(wl, q, k, v, keep_h, n_tiles: int):
+    """The oracle's variable-keep path on one (batch, head) slice per distinct
+    count: gather, pooling and the per-row top-k over all of the head's rows,
+    CSR attention on `n_tiles` sampled query tiles, extrapolated linearly over
+    the query tiles and scaled by the heads of each count."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    perm = oracle.perm_static(wl.grid, wl.tile)[None]
+    nqt = wl.n_tokens // 64
+    rng = np.random.default_rng(2468)
+    tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
+    scale = float(np.float32(wl.scale))
+    total_s, total_f, parts = 0.0, 0.0, []
+    for h, kh in enumerate(keep_h[:len(set(keep_h))]):
+        sl = lambda x: np.ascontiguousarray(x[0:1, :, h:h + 1])
+        t0 = time.perf_counter()
+        qt, kt, vt = (oracle.gather(sl(x), perm, wl.n_prefix) for x in (q, k, v))
+        qp, kp = oracle.pool(qt, wl.n_prefix), oracle.pool(kt, wl.n_prefix)
+        row_ptr, col = oracle.plan_csr(qp, kp, [kh])
+        t_plan = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.attention_csr(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, row_ptr, col, scale, tiles)
+        t_attn = time.perf_counter() - t0
+        heads = sum(1 for x in keep_h if x == kh) * wl.batch
+        total_s += (t_plan + t_attn * nqt / len(tiles)) * heads
+        total_f += varkeep_flops(wl, [kh]) / wl.batch * heads
+        parts.append(f"k={kh}: plan {t_plan:.2f} s, attention on {len(tiles)} tiles {t_attn:.2f} s")
+    return {
+        "value": total_f / total_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "ms_per_call_extrapolated": total_s * 1e3,
+        "sample": ("one (batch, head) slice per distinct keep count of the same workload (" + "; ".join(parts) +
+                   f"), fp64, extrapolated linearly over the {nqt} query tiles and over the heads of each count"),
+    }
+
+
+def bench_varkeep(args, wl, q, k, v):
+    import torch
+
+    import block_sparse_attention_39_amd as bsa
+    counts = [int(x) for x in args.varkeep.split(",")]
+    keep_h = [counts[h % len(counts)] for h in range(wl.heads)]
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, max(keep_h), scale=wl.scale,
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+    att = bsa.BlockSparseAttention(desc)
+    out = torch.empty_like(qd)
+    rows = wl.batch * wl.heads * wl.n_video_tiles
+    row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
+    col = torch.empty(bsa.csr_entries(desc, keep_h), dtype=torch.int32, device="cuda")
+    stages = ["build", "gather", "plan", "forward", "scatter"]
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        mark(0)
+        att.build(qd)
+        mark(1)
+        att.gather_qkv(qd, kd, vd)
+        mark(2)
+        bsa.plan_csr(desc, att.q_t, att.k_f, row_ptr, col, att.workspace, keep_per_head=keep_h)
+        mark(3)
+        bsa.forward_csr(desc, att.q_t, att.k_f, att.v_f, row_ptr, col, att.o_t, workspace=att.workspace)
+        mark(4)
+        att.scatter_out(out)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_stage = {s: [] for s in stages}
+    totals = []
+    for ev in events:
+        for j, s in enumerate(stages):
+            per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
+        totals.append(ev[0].elapsed_time(ev[5]))
+    ms_step = float(np.mean(totals))
+    F = varkeep_flops(wl, keep_h)
+    fwd_ms = float(np.mean(per_stage["forward"]))
+    achieved = F / (fwd_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC_VAR,
+        "value": F / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid_thw": list(wl.grid), "tokens": wl.n_tokens,
+                   "video_tiles": wl.n_video_tiles, "batch": wl.batch, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "keep_per_head": keep_h, "effective_tflop_per_call": F / 1e12},
+        "roofline": {"bound": "mfma", "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}> (CSR lists)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline_varkeep(wl, q, k, v, keep_h, 240)
+        print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline_backward(wl, q, k, v, do, n_tiles: int):
@@ -245,6 +379,12 @@ def main():
             print("bench.py --backward times static-tile workloads", file=sys.stderr)
             sys.exit(2)
         bench_backward(args, wl, q, k, v)
+        return
+    if args.varkeep:
+        if wl.dynamic:
+            print("bench.py --varkeep times static-tile workloads", file=sys.stderr)
+            sys.exit(2)
+        bench_varkeep(args, wl, q, k, v)
         return
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20

@@ -18,8 +18,9 @@ PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_KF, PERM_GATHER_VF = 0, 1, 2,
 MAX_VIDEO_TILES = 8192
 MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
-EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_backward_workspace_size",
-           "bsa_backward", "bsa_status_string", "bsa_version")
+EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_csr_entries", "bsa_plan_csr",
+           "bsa_forward_csr", "bsa_backward_workspace_size", "bsa_backward", "bsa_status_string", "bsa_version")
+MAX_CSR_HEADS = 256
 
 
 class Desc(ctypes.Structure):
@@ -55,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.bsa_permute.argtypes = [D, ctypes.c_int, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_plan.argtypes = [D, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_forward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        I64 = ctypes.c_int64
+        L.bsa_csr_entries.argtypes = [D, P, ctypes.POINTER(I64)]
+        L.bsa_plan_csr.argtypes = [D, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
+        L.bsa_forward_csr.argtypes = [D, P, P, P, P, P, I64, P, P, P, ctypes.c_size_t, P]
         L.bsa_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_status_string.argtypes = [ctypes.c_int]

@@ -99,6 +99,46 @@ def forward(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, w
                              _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws, _stream(stream)), "bsa_forward")
 
 
+def _keep_heads(desc: Desc, keep_per_head):
+    """Host int32 array of the per-head keep counts (or None)."""
+    if keep_per_head is None:
+        return None, None
+    arr = (ctypes.c_int32 * len(keep_per_head))(*[int(x) for x in keep_per_head])
+    if len(keep_per_head) != desc.heads:
+        raise ValueError("keep_per_head needs one count per head")
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def csr_entries(desc: Desc, keep_per_head=None) -> int:
+    """Entries the CSR column array needs: B * nVT * sum of the per-head keeps."""
+    _, kp = _keep_heads(desc, keep_per_head)
+    n = ctypes.c_int64(0)
+    _check(lib().bsa_csr_entries(ctypes.byref(desc), kp, ctypes.byref(n)), "bsa_csr_entries")
+    return n.value
+
+
+def plan_csr(desc: Desc, q_tiled, k_frag, row_ptr, col_idx, workspace, keep_per_head=None, keep_rows=None,
+             stream=None):
+    """Variable-keep selection: ``row_ptr`` int64 ``[B*H*nVT + 1]`` and ``col_idx``
+    int32 (at least csr_entries() entries) on the device; ``keep_per_head`` a
+    host sequence of H counts, ``keep_rows`` an optional device int32
+    ``[B, H, nVT]`` tensor of per-row counts (clamped to 1..keep_per_head[h])."""
+    arr, kp = _keep_heads(desc, keep_per_head)
+    ws = workspace.numel() * workspace.element_size()
+    _check(lib().bsa_plan_csr(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), kp, _ptr(keep_rows), _ptr(row_ptr),
+                              _ptr(col_idx), col_idx.numel(), _ptr(workspace), ws, _stream(stream)), "bsa_plan_csr")
+    del arr
+
+
+def forward_csr(desc: Desc, q_tiled, k_frag, v_frag, row_ptr, col_idx, o_tiled, lse=None, workspace=None,
+                stream=None):
+    """bsa_forward with the kept lists in CSR form (from plan_csr)."""
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().bsa_forward_csr(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), _ptr(v_frag), _ptr(row_ptr),
+                                 _ptr(col_idx), col_idx.numel(), _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws,
+                                 _stream(stream)), "bsa_forward_csr")
+
+
 def backward_workspace_size(desc: Desc) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().bsa_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "bsa_backward_workspace_size")

@@ -253,7 +253,7 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
-    bsa::ForwardArgs a;
+    bsa::ForwardArgs a{};
     a.q = static_cast<const uint16_t*>(q_tiled);
     a.k = static_cast<const uint16_t*>(k_frag);
     a.v = static_cast<const uint16_t*>(v_frag);
@@ -264,6 +264,115 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
     a.npt = (int)g.npt;
     a.nvt = (int)g.nvt;
     a.keep = (int)g.k;
+    a.scale_log2 = desc->scale * 1.4426950408889634f;
+    return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+// ---- variable keep (CSR lists) ----------------------------------------------
+
+namespace {
+
+// Per-head keep counts: keep_per_head (host, [H]) or desc->keep_tiles, each
+// in 1..nvt; fills kh and the number of list entries B * nvt * sum_h k_h.
+bsa_status csr_heads(const Geo& g, const int32_t* keep_per_head, bsa::CsrKeep* kh, int64_t* entries) {
+    if (g.H > BSA_MAX_CSR_HEADS) return BSA_ERR_UNSUPPORTED;
+    int64_t sum = 0;
+    for (int64_t h = 0; h < g.H; ++h) {
+        const int64_t k = keep_per_head ? keep_per_head[h] : g.k;
+        if (k < 1 || k > g.nvt) return BSA_ERR_SHAPE;
+        if (kh) kh->k[h] = (int32_t)k;
+        sum += k;
+    }
+    *entries = g.B * g.nvt * sum;
+    return BSA_OK;
+}
+
+}  // namespace
+
+bsa_status bsa_csr_entries(const bsa_desc* desc, const int32_t* keep_per_head, int64_t* entries) {
+    if (!entries) return BSA_ERR_NULL;
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.empty || g.nvt == 0) {
+        *entries = 0;
+        return BSA_OK;
+    }
+    return csr_heads(g, keep_per_head, nullptr, entries);
+}
+
+bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const int32_t* keep_per_head,
+                        const int32_t* keep_rows, int64_t* row_ptr, int32_t* col_idx, int64_t col_entries, void* ws,
+                        size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.empty || g.nvt == 0) return BSA_OK;
+    bsa::CsrKeep kh{};
+    int64_t need = 0;
+    st = csr_heads(g, keep_per_head, &kh, &need);
+    if (st != BSA_OK) return st;
+    if (!q_tiled || !k_frag || !row_ptr || !col_idx) return BSA_ERR_NULL;
+    if (col_entries < need) return BSA_ERR_SHAPE;
+    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(row_ptr, 8) || misaligned(col_idx, 4) ||
+        misaligned(keep_rows, 4))
+        return BSA_ERR_ALIGN;
+    const Layout L = layout(g);
+    if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+    if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    float* qbar = reinterpret_cast<float*>(w + L.qbar);
+    float* kbar = reinterpret_cast<float*>(w + L.kbar);
+    float* scores = reinterpret_cast<float*>(w + L.scores);
+    hipError_t e = bsa::launch_csr_rowptr(kh, keep_rows, (int)g.BH, (int)g.H, (int)g.nvt, row_ptr, s);
+    if (e == hipSuccess)
+        e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag), qbar, kbar,
+                             (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s);
+    for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
+        const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
+        e = bsa::launch_scores(qbar + b0 * g.nvt * g.D, kbar + b0 * g.nvt * g.D, scores, (int)cnt, (int)g.nvt,
+                               (int)g.D, s);
+        if (e == hipSuccess)
+            e = bsa::launch_topk_csr(scores, col_idx, row_ptr, b0 * g.nvt, (int)(cnt * g.nvt), (int)g.nvt, s);
+    }
+    return launched(e);
+}
+
+bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
+                           const int64_t* row_ptr, const int32_t* col_idx, int64_t col_entries, void* o_tiled,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.npt + g.nvt > BSA_MAX_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.empty) return BSA_OK;
+    if (!q_tiled || !k_frag || !v_frag || !o_tiled || (g.nvt > 0 && (!row_ptr || !col_idx))) return BSA_ERR_NULL;
+    if (g.nvt > 0 && col_entries < 1) return BSA_ERR_SHAPE;
+    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(v_frag, 16) || misaligned(o_tiled, 16) ||
+        misaligned(row_ptr, 8) || misaligned(col_idx, 4) || misaligned(lse, 4))
+        return BSA_ERR_ALIGN;
+    int* progress = nullptr;
+    if (ws) {
+        const Layout L = layout(g);
+        if (ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+        if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
+    }
+    bsa::ForwardArgs a{};
+    a.q = static_cast<const uint16_t*>(q_tiled);
+    a.k = static_cast<const uint16_t*>(k_frag);
+    a.v = static_cast<const uint16_t*>(v_frag);
+    a.idx = col_idx;
+    a.row_ptr = g.nvt > 0 ? row_ptr : nullptr;
+    a.col_entries = col_entries;
+    a.o = static_cast<uint16_t*>(o_tiled);
+    a.lse = lse;
+    a.BH = (int)g.BH;
+    a.npt = (int)g.npt;
+    a.nvt = (int)g.nvt;
+    a.keep = 1;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }

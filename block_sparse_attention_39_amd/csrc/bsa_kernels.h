@@ -47,11 +47,23 @@ hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, in
 // Per row: the k largest scores (lower index first on ties), ascending indices.
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s);
 
+// Variable keep: per-head keep counts (kernel argument), per-row counts
+// (device, optional), CSR row pointers and the per-row top-k.
+struct CsrKeep {
+    int32_t k[BSA_MAX_CSR_HEADS];
+};
+hipError_t launch_csr_rowptr(const CsrKeep& kh, const int32_t* keep_rows, int BH, int H, int nvt, int64_t* row_ptr,
+                             hipStream_t s);
+hipError_t launch_topk_csr(const float* scores, int32_t* col_idx, const int64_t* row_ptr, int64_t row0, int rows,
+                           int n, hipStream_t s);
+
 struct ForwardArgs {
     const uint16_t* q;       // tiled [BH][Ntot][D]
     const uint16_t* k;       // K-fragment layout [BH][Ntot/64][2][D/16][64][8]
     const uint16_t* v;       // V-fragment layout [BH][Ntot/64][2][D/32][2][64][8]
-    const int32_t* idx;      // [BH][nvt][keep]
+    const int32_t* idx;      // [BH][nvt][keep], or CSR column indices when row_ptr is set
+    const int64_t* row_ptr;  // CSR row pointers [BH * nvt + 1], or null (fixed keep)
+    int64_t col_entries;     // CSR: entries of idx (list bounds are clamped to it)
     uint16_t* o;             // tiled [BH][Ntot][D]
     float* lse;              // [BH][Ntot] or null
     int BH;

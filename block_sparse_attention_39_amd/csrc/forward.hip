@@ -166,15 +166,33 @@ struct Wave {
     }
 };
 
+typedef const __attribute__((address_space(4))) int64_t const_i64;
+
+// Start and length of the kept list of video query tile vi of (batch, head)
+// bh: fixed keep, or the CSR row (read through the scalar cache), clamped to
+// [0, col_entries) and to 1..nvt entries so that a corrupt row cannot address
+// outside the lists.
+__device__ inline int64_t row_begin(const ForwardArgs& a, int64_t bh, int vi) {
+    const int64_t r = bh * a.nvt + vi;
+    if (!a.row_ptr) return r * a.keep;
+    return min(max(((const_i64*)a.row_ptr)[r], (int64_t)0), a.col_entries - 1);
+}
+__device__ inline int row_len(const ForwardArgs& a, int64_t bh, int vi) {
+    if (!a.row_ptr) return a.keep;
+    const int64_t b = row_begin(a, bh, vi);
+    const int64_t e = min(((const_i64*)a.row_ptr)[bh * a.nvt + vi + 1], a.col_entries);
+    return (int)min(max(e - b, (int64_t)1), (int64_t)a.nvt);
+}
+
 __device__ inline int list_len(const ForwardArgs& a, const Item& it) {
-    return it.vi < 0 ? a.npt + a.nvt : a.npt + a.keep;
+    return it.vi < 0 ? a.npt + a.nvt : a.npt + row_len(a, it.bh, it.vi);
 }
 
 // The kept-list value behind list position j of a video query tile (read
 // from global memory; positions of the prefix read entry 0).
 __device__ inline int list_raw(const ForwardArgs& a, const Item& it, int j) {
     if (it.vi < 0) return 0;  // prefix query tile: no list (and `idx` may be null)
-    return a.idx[(it.bh * a.nvt + it.vi) * (int64_t)a.keep + max(j - a.npt, 0)];
+    return a.idx[row_begin(a, it.bh, it.vi) + min(max(j - a.npt, 0), row_len(a, it.bh, it.vi) - 1)];
 }
 
 // Tile number of list position j given its raw kept-list value: prefix
@@ -214,11 +232,12 @@ __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardA
 #pragma unroll
     for (int u = 0; u < kListPre; ++u) lpre[u] = 0;
     if (it.vi >= 0) {
-        const int32_t* row = a.idx + (it.bh * a.nvt + it.vi) * (int64_t)a.keep;
+        const int32_t* row = a.idx + row_begin(a, it.bh, it.vi);
+        const int len = row_len(a, it.bh, it.vi);
 #pragma unroll
         for (int u = 0; u < kListPre; ++u) {
             const int e = w.tid + 256 * u;
-            if (e < a.keep) lpre[u] = row[e];
+            if (e < len) lpre[u] = row[e];
         }
     }
 }
@@ -251,14 +270,15 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     if (dense) {
         for (int j = tid; j < n_iter; j += 256) list[j] = j;
     } else {
-        const int32_t* row = a.idx + (bh * a.nvt + it.vi) * (int64_t)a.keep;
+        const int32_t* row = a.idx + row_begin(a, bh, it.vi);
+        const int len = n_iter - a.npt;
         for (int j = tid; j < a.npt; j += 256) list[j] = j;
 #pragma unroll
         for (int u = 0; u < kListPre; ++u) {
             const int e = tid + 256 * u;
-            if (e < a.keep) list[a.npt + e] = a.npt + min(max(lpre[u], 0), a.nvt - 1);
+            if (e < len) list[a.npt + e] = a.npt + min(max(lpre[u], 0), a.nvt - 1);
         }
-        for (int e = tid + 256 * kListPre; e < a.keep; e += 256)
+        for (int e = tid + 256 * kListPre; e < len; e += 256)
             list[a.npt + e] = a.npt + min(max(row[e], 0), a.nvt - 1);
     }
 #pragma unroll

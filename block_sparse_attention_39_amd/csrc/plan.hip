@@ -181,14 +181,24 @@ __device__ inline int block_scan_256(int x, int* wsum, int* total) {
     return v + before;
 }
 
+// One block per row of scores.  Fixed keep: k per row, written at row * k.
+// Variable keep (row_ptr not null): row r0 + row keeps row_ptr[r + 1] -
+// row_ptr[r] tiles, written at row_ptr[r].
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, int32_t* __restrict__ idx, int n,
-                                                   int k) {
+                                                   int k_fixed, const int64_t* __restrict__ row_ptr, int64_t r0) {
     extern __shared__ uint32_t keys[];  // [n]
     __shared__ int hist[256];
     __shared__ int wsum[4];
     __shared__ int sel_digit, sel_above;
     const int64_t row = blockIdx.x;
     const float* s = S + row * n;
+    int k = k_fixed;
+    int32_t* out = idx + row * k_fixed;
+    if (row_ptr) {
+        const int64_t beg = row_ptr[r0 + row];
+        k = (int)(row_ptr[r0 + row + 1] - beg);
+        out = idx + beg;
+    }
     for (int j = threadIdx.x; j < n; j += 256) keys[j] = order_key(s[j]);
     uint32_t prefix = 0, mask = 0;
     int need = k;  // how many of the keys matching `prefix` are still to take
@@ -218,7 +228,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, 
     // prefix is now the key of the k-th largest score; `need` of the keys equal
     // to it are taken, lowest index first.
     const uint32_t thr = prefix;
-    int32_t* out = idx + row * k;
     int taken = 0, ties = 0;
     for (int j0 = 0; j0 < n; j0 += 256) {
         const int j = j0 + threadIdx.x;
@@ -235,7 +244,47 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, 
     }
 }
 
+// Row pointers of variable-keep lists: row (bh, i) keeps keep_rows[bh][i]
+// clamped to [1, keep_h[h]] tiles (keep_h[h] without keep_rows); row_ptr is
+// the exclusive prefix sum over rows in (bh, i) order.  One block: each
+// thread sums a contiguous run of rows, the runs are scanned, then written.
+__global__ __launch_bounds__(1024) void csr_rowptr_kernel(CsrKeep kh, const int32_t* __restrict__ keep_rows,
+                                                          int BH, int H, int nvt, int64_t* __restrict__ row_ptr) {
+    __shared__ int64_t part[1024];
+    const int64_t rows = (int64_t)BH * nvt;
+    const int64_t per = (rows + 1023) / 1024;
+    const int64_t r_lo = min((int64_t)threadIdx.x * per, rows), r_hi = min(r_lo + per, rows);
+    auto len = [&](int64_t r) -> int64_t {
+        const int h = (int)((r / nvt) % H);
+        const int cap = kh.k[h];
+        return keep_rows ? (int64_t)min(max(keep_rows[r], 1), cap) : (int64_t)cap;
+    };
+    int64_t sum = 0;
+    for (int64_t r = r_lo; r < r_hi; ++r) sum += len(r);
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    // inclusive scan of the 1024 partial sums (Hillis-Steele in LDS)
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int64_t add = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int64_t run = part[threadIdx.x] - sum;
+    for (int64_t r = r_lo; r < r_hi; ++r) {
+        row_ptr[r] = run;
+        run += len(r);
+    }
+    if (threadIdx.x == 1023) row_ptr[rows] = part[1023];
+}
+
 }  // namespace
+
+hipError_t launch_csr_rowptr(const CsrKeep& kh, const int32_t* keep_rows, int BH, int H, int nvt, int64_t* row_ptr,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(csr_rowptr_kernel, dim3(1), dim3(1024), 0, s, kh, keep_rows, BH, H, nvt, row_ptr);
+    return hipGetLastError();
+}
 
 hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
                        int n_prefix, int nvt, int D, hipStream_t s) {
@@ -262,7 +311,15 @@ hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, in
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), (size_t)n * sizeof(uint32_t), s, scores, idx,
-                       n, k);
+                       n, k, (const int64_t*)nullptr, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_csr(const float* scores, int32_t* col_idx, const int64_t* row_ptr, int64_t row0, int rows,
+                           int n, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), (size_t)n * sizeof(uint32_t), s, scores,
+                       col_idx, n, 0, row_ptr, row0);
     return hipGetLastError();
 }
 

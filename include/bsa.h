@@ -183,6 +183,44 @@ bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Variable keep: per-head and per-row keep counts with the kept lists in CSR
+ * form.  The pages keep a fixed share per call ("Prism / Kandinsky 6 speed
+ * ablation", section "같은 계산량 안에서 볼 곳을 고르는 Prism": sparsity s keeps
+ * (1 - s) of the key tiles); these entry points let that share differ per
+ * head or per query tile, with the same selection rule and the same
+ * attention kernel.
+ *
+ *   keep_per_head  host int32 [H], each in 1..nVT; NULL: desc->keep_tiles for
+ *                  every head.  At most BSA_MAX_CSR_HEADS heads.
+ *   keep_rows      device int32 [B][H][nVT] or NULL: video query tile i of
+ *                  (b, h) keeps min(max(keep_rows[b][h][i], 1), keep_per_head[h])
+ *                  tiles (keep_per_head[h] when NULL).
+ *   row_ptr        device int64 [B*H*nVT + 1]: row r = (b*H + h)*nVT + i holds
+ *                  col_idx[row_ptr[r] .. row_ptr[r+1]); row_ptr[0] = 0.
+ *   col_idx        device int32, col_entries entries: the kept video tiles of
+ *                  each row, ascending.
+ *
+ * bsa_csr_entries (host only) gives the entries col_idx needs at most:
+ * B * nVT * sum_h keep_per_head[h].
+ * bsa_plan_csr writes row_ptr and col_idx: the selection of bsa_plan with
+ * each row's own count (the largest scores, equal scores to the lower tile
+ * number); col_entries below bsa_csr_entries gives BSA_ERR_SHAPE.  Uses the
+ * workspace of bsa_workspace_size.
+ * bsa_forward_csr is bsa_forward with the lists read from row_ptr/col_idx;
+ * each row must hold 1..nVT entries (row bounds are clamped to that and to
+ * col_entries, so a corrupt row_ptr cannot address outside col_idx).
+ */
+#define BSA_MAX_CSR_HEADS 256
+bsa_status bsa_csr_entries(const bsa_desc *desc, const int32_t *keep_per_head, int64_t *entries);
+bsa_status bsa_plan_csr(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
+                        const int32_t *keep_per_head, const int32_t *keep_rows, int64_t *row_ptr,
+                        int32_t *col_idx, int64_t col_entries, void *ws, size_t ws_bytes, void *stream);
+bsa_status bsa_forward_csr(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
+                           const void *v_frag, const int64_t *row_ptr, const int32_t *col_idx,
+                           int64_t col_entries, void *o_tiled, float *lse, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
  * Bytes of device workspace that bsa_backward needs for `desc` (about seven
  * times the size of one bf16 [B][H][Ntot][D] tensor: the fragment-layout
  * copies of Q, K, V and dO the gradient kernels stream).  Host-only.
@@ -225,7 +263,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 500
+#define BSA_VERSION 600
 
 #ifdef __cplusplus
 }

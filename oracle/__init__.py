@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.orc_topk.restype = None
         L.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, f64, P, i32, P, P]
         L.orc_attention.restype = None
+        L.orc_attention_csr.argtypes = [P, P, P, i32, i32, i32, P, P, f64, P, i32, P, P]
+        L.orc_attention_csr.restype = None
         L.orc_attention_lse_delta.argtypes = [P, P, P, P, i32, i32, i32, i32, P, f64, P, P]
         L.orc_attention_lse_delta.restype = None
         L.orc_attention_backward_dq.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, f64, P, i32, P]
@@ -215,6 +217,52 @@ def attention(q_bh, k_bh, v_bh, n_prefix: int, idx_bh, scale: float, qtiles):
     lib().orc_attention(_ptr(q), _ptr(kx), _ptr(v), n_prefix, nvt, D, k, _ptr(ix), float(scale),
                         _ptr(qt), nq, _ptr(out), _ptr(lse))
     return out, lse
+
+
+def attention_csr(q_bh, k_bh, v_bh, n_prefix: int, row_ptr_bh, col, scale: float, qtiles):
+    """As ``attention``, with video query tile i keeping the video tiles
+    ``col[row_ptr_bh[i]:row_ptr_bh[i+1]]`` (variable keep, CSR lists).
+    ``row_ptr_bh``: int64 ``[nvt + 1]`` into ``col`` (int32)."""
+    q = _c(q_bh, np.uint16)
+    kx = _c(k_bh, np.uint16)
+    v = _c(v_bh, np.uint16)
+    Ntot, D = q.shape
+    nvt = (Ntot - n_prefix) // TILE
+    rp = _c(row_ptr_bh, np.int64)
+    cl = _c(col, np.int32) if len(col) else np.zeros(1, np.int32)
+    qt = _c(qtiles, np.int32)
+    nq = qt.shape[0]
+    out = np.empty((nq, TILE, D), np.float64)
+    lse = np.empty((nq, TILE), np.float64)
+    lib().orc_attention_csr(_ptr(q), _ptr(kx), _ptr(v), n_prefix, nvt, D, _ptr(rp), _ptr(cl), float(scale),
+                            _ptr(qt), nq, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def plan_csr(qp, kp, keep_per_head, keep_rows=None):
+    """Variable-keep selection from pooled ``qp, kp`` (float32 ``[B,H,nvt,D]``):
+    row (b,h,i) keeps ``min(max(keep_rows[b,h,i], 1), keep_per_head[h])`` tiles
+    (``keep_per_head[h]`` without ``keep_rows``), chosen by the same rule as
+    ``topk``.  Returns ``(row_ptr int64 [B*H*nvt + 1], col int32)`` with rows in
+    (b, h, i) order."""
+    B, H, n, _ = qp.shape
+    lens = np.empty((B, H, n), np.int64)
+    for h in range(H):
+        lens[:, h, :] = keep_per_head[h]
+    if keep_rows is not None:
+        lens = np.minimum(np.maximum(np.asarray(keep_rows, np.int64), 1), lens)
+    row_ptr = np.zeros(B * H * n + 1, np.int64)
+    row_ptr[1:] = np.cumsum(lens.reshape(-1))
+    col = np.empty(int(row_ptr[-1]), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for k in np.unique(lens[b, h]):
+                rows = np.nonzero(lens[b, h] == k)[0].astype(np.int32)
+                idx = topk(qp[b:b + 1, h:h + 1], kp[b:b + 1, h:h + 1], int(k), rows)[0]
+                for a, i in enumerate(rows):
+                    r = (b * H + h) * n + i
+                    col[row_ptr[r]:row_ptr[r + 1]] = idx[0, 0, a]
+    return row_ptr, col
 
 
 def plan(q_tiled, k_tiled, n_prefix: int, k: int):

@@ -545,6 +545,81 @@ void orc_attention(const uint16_t *q, const uint16_t *kx, const uint16_t *v, int
 }
 
 /*
+ * Attention with a kept list of its own length per video query tile (variable
+ * keep per head or per query tile, lists in CSR form): as orc_attention, with
+ * video query tile i attending to all prefix tokens and to the tokens of the
+ * video tiles col[row_ptr[i] .. row_ptr[i+1]).  row_ptr: [nvt + 1] of one
+ * (b,h); col: the entries it points into.
+ */
+void orc_attention_csr(const uint16_t *q, const uint16_t *kx, const uint16_t *v, int n_prefix,
+                       int nvt, int D, const int64_t *row_ptr, const int32_t *col, double scale,
+                       const int32_t *qtiles, int nq, double *out, double *lse)
+{
+    const int npt = n_prefix / TILE;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nq; ++a) {
+        const int qt = qtiles[a];
+        int64_t nkeys, c = 0;
+        int64_t *keys;
+        if (qt < npt) {
+            nkeys = Ntot;
+            keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)nkeys);
+            for (int64_t j = 0; j < Ntot; ++j)
+                keys[c++] = j;
+        } else {
+            const int i = qt - npt;
+            const int64_t b = row_ptr[i], e = row_ptr[i + 1];
+            nkeys = n_prefix + (e - b) * TILE;
+            keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nkeys > 0 ? nkeys : 1));
+            for (int64_t j = 0; j < n_prefix; ++j)
+                keys[c++] = j;
+            for (int64_t t = b; t < e; ++t) {
+                const int64_t base = n_prefix + (int64_t)col[t] * TILE;
+                for (int r = 0; r < TILE; ++r)
+                    keys[c++] = base + r;
+            }
+        }
+        double *z = (double *)malloc(sizeof(double) * (size_t)(nkeys > 0 ? nkeys : 1));
+        double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            for (int d = 0; d < D; ++d)
+                qd[d] = bf16_to_double(q[qi * D + d]);
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const uint16_t *kr = kx + keys[j] * D;
+                double s = 0.0;
+                for (int d = 0; d < D; ++d)
+                    s += qd[d] * bf16_to_double(kr[d]);
+                z[j] = s * scale;
+                if (z[j] > mx)
+                    mx = z[j];
+            }
+            double den = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc[d] = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const double w = exp(z[j] - mx);
+                den += w;
+                const uint16_t *vr = v + keys[j] * D;
+                for (int d = 0; d < D; ++d)
+                    acc[d] += w * bf16_to_double(vr[d]);
+            }
+            for (int d = 0; d < D; ++d)
+                out[((int64_t)a * TILE + r) * D + d] = acc[d] / den;
+            if (lse)
+                lse[(int64_t)a * TILE + r] = mx + log(den);
+        }
+        free(z);
+        free(qd);
+        free(acc);
+        free(keys);
+    }
+}
+
+/*
  * Gradients of orc_attention's output with respect to q, k and v (one (b,h)),
  * given dO = dL/dO.  This is the plain derivative of the function orc_attention
  * computes (the pages give no backward; Prism's training speedup, in [Prism]

@@ -1,0 +1,154 @@
+"""GPU parity of the variable-keep path (bsa_plan_csr, bsa_forward_csr): kept
+lists of their own length per head and per query tile, in CSR form.
+
+* Row pointers: bit-exact against the counts (per-head keep clamped by the
+  per-row keep) summed in (b, h, i) order.
+* Lists: per (b, h) and per count, the rules of the fixed-keep selection test
+  (bit-exact outside near ties, a valid top-k within the band on near ties).
+* Attention: the oracle's CSR attention run on the GPU's lists, with the
+  forward's output and lse tolerances.
+* With one count for every row the CSR path reproduces the fixed-keep plan
+  and forward bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_39_amd as bsa
+import oracle
+import synthetic as S
+from parity import GpuRun, check_lse, check_output, check_selection, to_bits
+
+pytestmark = pytest.mark.gpu
+
+W = S.Workload
+CASES = [
+    (W("csr_heads", 1, 3, 64, (8, 16, 16), 8, seed=21), [8, 3, 32], None),
+    (W("csr_rows", 2, 2, 128, (8, 8, 16), 6, seed=22), [6, 11], (-1, 13)),
+    (W("csr_prefix", 1, 2, 128, (8, 8, 12), 4, seed=23, n_prefix=128), [4, 1], (0, 5)),
+    (W("csr_dynamic", 1, 2, 128, (16, 16, 16), 6, seed=24, dynamic=True, recipe="field"), [6, 20], None),
+]
+
+
+def run_csr(g: GpuRun, keep_h, keep_rows_dev):
+    a, d = g.att, g.desc
+    wl = g.wl
+    rows = wl.batch * wl.heads * wl.n_video_tiles
+    row_ptr = torch.full((rows + 1,), -7, dtype=torch.int64, device="cuda")
+    col = torch.full((bsa.csr_entries(d, keep_h),), -7, dtype=torch.int32, device="cuda")
+    bsa.plan_csr(d, a.q_t, a.k_f, row_ptr, col, a.workspace, keep_per_head=keep_h, keep_rows=keep_rows_dev)
+    o = torch.empty_like(a.q_t)
+    lse = torch.empty_like(a.lse)
+    bsa.forward_csr(d, a.q_t, a.k_f, a.v_f, row_ptr, col, o, lse, workspace=a.workspace)
+    torch.cuda.synchronize()
+    return row_ptr.cpu().numpy(), col.cpu().numpy(), o, lse
+
+
+@pytest.mark.parametrize("wl,keep_h,rows_range", CASES, ids=[c[0].name for c in CASES])
+def test_csr_matches_oracle(wl, keep_h, rows_range):
+    print(f"\n[case] {wl} keep_per_head={keep_h} rows={rows_range}", flush=True)
+    q, k, v = S.qkv(wl)
+    g = GpuRun(wl, q, k, v).run()
+    n = wl.n_video_tiles
+    keep_rows = None
+    if rows_range is not None:
+        rng = np.random.default_rng(wl.seed + 100)
+        keep_rows = rng.integers(rows_range[0], rows_range[1] + 1, size=(wl.batch, wl.heads, n)).astype(np.int32)
+    kr_dev = None if keep_rows is None else torch.from_numpy(keep_rows).cuda()
+    row_ptr, col, o, lse = run_csr(g, keep_h, kr_dev)
+
+    lens = np.broadcast_to(np.array(keep_h)[None, :, None], (wl.batch, wl.heads, n)).astype(np.int64)
+    if keep_rows is not None:
+        lens = np.minimum(np.maximum(keep_rows.astype(np.int64), 1), lens)
+    ref_ptr = np.zeros(lens.size + 1, np.int64)
+    ref_ptr[1:] = np.cumsum(lens.reshape(-1))
+    assert np.array_equal(row_ptr, ref_ptr)
+
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    perm = g.perm()
+    nqt = wl.n_tokens // 64
+    o_t, lse_h = to_bits(o), lse.cpu().numpy()
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+            qt, kt, vt = (oracle.gather(sl(x), perm[b:b + 1], npf) for x in (q, k, v))
+            qp, kp = oracle.pool(qt, npf), oracle.pool(kt, npf)
+            r0 = (b * wl.heads + h) * n
+            for kk in np.unique(lens[b, h]):
+                rws = np.nonzero(lens[b, h] == kk)[0].astype(np.int32)
+                got = np.stack([col[row_ptr[r0 + i]:row_ptr[r0 + i + 1]] for i in rws])[None, None]
+                n_exact, n_near = check_selection(got, qp, kp, int(kk), rows=rws)
+                print(f"[plan b{b} h{h} k={kk}] rows {len(rws)}: exact {n_exact}, near ties {n_near}", flush=True)
+            rp = row_ptr[r0:r0 + n + 1] - row_ptr[r0]
+            cl = col[row_ptr[r0]:row_ptr[r0 + n]]
+            tiles = np.arange(nqt, dtype=np.int32)
+            ref, ref_lse = oracle.attention_csr(qt[0, 0], kt[0, 0], vt[0, 0], npf, rp, cl, scale, tiles)
+            mx, mean = check_output(o_t[b, h].reshape(nqt, 64, wl.head_dim), ref, f"b{b} h{h}")
+            check_lse(lse_h[b, h].reshape(nqt, 64), ref_lse, qt[0, 0].reshape(nqt, 64, -1), kt[0, 0], scale,
+                      f"lse b{b} h{h}")
+            print(f"[attention b{b} h{h}] max|err| {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+def test_uniform_csr_equals_fixed_keep():
+    wl = W("csr_uniform", 2, 3, 128, (8, 8, 16), 5, seed=25, n_prefix=64)
+    q, k, v = S.qkv(wl)
+    g = GpuRun(wl, q, k, v).run()
+    row_ptr, col, o, lse = run_csr(g, [wl.keep_tiles] * wl.heads, None)
+    fixed = g.att.block_idx.cpu().numpy()[:, :, :wl.n_video_tiles, :wl.keep_tiles]
+    assert np.array_equal(col, fixed.reshape(-1))
+    assert np.array_equal(to_bits(o), to_bits(g.att.o_t))
+    assert np.array_equal(lse.cpu().numpy(), g.att.lse.cpu().numpy())
+
+
+def test_csr_argument_checks():
+    wl = W("csr_args", 1, 2, 64, (4, 8, 8), 2, seed=26)
+    d = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles)
+    assert bsa.csr_entries(d, [2, 3]) == 1 * wl.n_video_tiles * 5
+    with pytest.raises(bsa.BsaError):
+        bsa.csr_entries(d, [0, 3])            # a head keeping nothing
+    with pytest.raises(bsa.BsaError):
+        bsa.csr_entries(d, [2, wl.n_video_tiles + 1])
+    q, k, v = S.qkv(wl)
+    g = GpuRun(wl, q, k, v).run()
+    row_ptr = torch.zeros(wl.n_video_tiles * 2 + 1, dtype=torch.int64, device="cuda")
+    small = torch.zeros(3, dtype=torch.int32, device="cuda")
+    with pytest.raises(bsa.BsaError):  # column array below bsa_csr_entries
+        bsa.plan_csr(d, g.att.q_t, g.att.k_f, row_ptr, small, g.att.workspace, keep_per_head=[2, 3])
+
+
+def test_prism720p_csr_sampled():
+    """Full size (grid 32x48x80, batch 2, 24 heads, head_dim 128) with the
+    heads keeping 480, 192, 120 and 96 tiles in turn: row pointers in full,
+    lists and attention on sampled (batch, head) slices and query tiles."""
+    wl = S.WORKLOADS["prism720p"]
+    keep_h = [(480, 192, 120, 96)[h % 4] for h in range(wl.heads)]
+    print(f"\n[case] {wl} keep_per_head={keep_h}", flush=True)
+    q, k, v = S.qkv(wl)
+    g = GpuRun(wl, q, k, v).run()
+    row_ptr, col, o, lse = run_csr(g, keep_h, None)
+    n = wl.n_video_tiles
+    lens = np.repeat(np.tile(np.array(keep_h, np.int64), wl.batch), n)
+    assert np.array_equal(np.diff(row_ptr), lens) and row_ptr[0] == 0
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    perm = g.perm()
+    nqt = wl.n_tokens // 64
+    rng = np.random.default_rng(77)
+    for b, h in [(0, 1), (1, 2), (0, 3), (1, 20)]:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        qt, kt, vt = (oracle.gather(sl(x), perm[b:b + 1], npf) for x in (q, k, v))
+        qp, kp = oracle.pool(qt, npf), oracle.pool(kt, npf)
+        r0 = (b * wl.heads + h) * n
+        kk = keep_h[h]
+        got = col[row_ptr[r0]:row_ptr[r0 + n]].reshape(1, 1, n, kk)
+        n_exact, n_near = check_selection(got, qp, kp, kk)
+        print(f"[plan b{b} h{h} k={kk}] exact rows {n_exact}, near ties {n_near}", flush=True)
+        tiles = np.sort(rng.choice(nqt, size=16, replace=False)).astype(np.int32)
+        rp = row_ptr[r0:r0 + n + 1] - row_ptr[r0]
+        ref, ref_lse = oracle.attention_csr(qt[0, 0], kt[0, 0], vt[0, 0], npf, rp, got.reshape(-1), scale, tiles)
+        ob = to_bits(o[b, h]).reshape(nqt, 64, wl.head_dim)[tiles]
+        mx, mean = check_output(ob, ref, f"b{b} h{h}")
+        check_lse(lse[b, h].cpu().numpy().reshape(nqt, 64)[tiles], ref_lse,
+                  qt[0, 0].reshape(nqt, 64, -1)[tiles], kt[0, 0], scale, f"lse b{b} h{h}")
+        print(f"[attention b{b} h{h} k={kk}] max|err| {mx:.2e} mean {mean:.2e}", flush=True)
+    del g, o, lse
+    torch.cuda.empty_cache()

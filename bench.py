@@ -21,6 +21,12 @@ output and lse and a synthetic dO, inputs resident in HBM) and prints its own
 line: 2.5 x the forward's effective FLOPs (the five products of the gradient:
 S and dP recomputed, dV, dK, dQ) per second.
 
+    python bench.py --structured 1,2 [...]
+
+times structured lists (bsa_plan_structured / bsa_forward_csr): even heads
+spatial (radius 1 tile-frame), odd heads temporal (radius 2 tiles); effective
+FLOPs from the lists' lengths.
+
     python bench.py --varkeep 480,192,120,96 [...]
 
 times the variable-keep path instead (bsa_plan_csr / bsa_forward_csr): head h
@@ -46,6 +52,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "effective TFLOP/s (kept tiles) + ms/call, 122,880-token grid @25% keep, 1 GPU"
 METRIC_BWD = "backward effective TFLOP/s (2.5x forward FLOPs, kept tiles) + ms/call, 1 GPU"
 METRIC_VAR = "variable-keep effective TFLOP/s (kept tiles, per-head keep) + ms/call, 1 GPU"
+METRIC_STRUCT = "structured-list effective TFLOP/s (spatial/temporal heads, kept tiles) + ms/call, 1 GPU"
 
 
 def parse():
@@ -59,6 +66,8 @@ def parse():
     ap.add_argument("--cpu-tiles", type=int, default=960, help="query tiles in the CPU oracle sample")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (bsa_backward)")
     ap.add_argument("--cpu-bwd-tiles", type=int, default=120, help="query and key tiles in the backward CPU sample")
+    ap.add_argument("--structured", default=None,
+                    help="RT,RS: time structured lists, even heads spatial (radius RT), odd heads temporal (RS)")
     ap.add_argument("--varkeep", default=None,
                     help="comma-separated keep counts cycled over the heads: time the CSR (variable keep) path")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -251,6 +260,87 @@ def bench_varkeep(args, wl, q, k, v):
     print(json.dumps(res), flush=True)
 
 
+def bench_structured(args, wl, q, k, v):
+    import torch
+
+    import block_sparse_attention_39_amd as bsa
+    rt, rs = (int(x) for x in args.structured.split(","))
+    mask = [h % 2 for h in range(wl.heads)]
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
+                         n_prefix=wl.n_prefix, tile=wl.tile)
+    att = bsa.BlockSparseAttention(desc)
+    out = torch.empty_like(qd)
+    rows = wl.batch * wl.heads * wl.n_video_tiles
+    row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
+    entries = bsa.structured_entries(desc, mask, rt, rs)
+    col = torch.empty(entries, dtype=torch.int32, device="cuda")
+    stages = ["build", "gather", "plan", "forward", "scatter"]
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        mark(0)
+        att.build(qd)
+        mark(1)
+        att.gather_qkv(qd, kd, vd)
+        mark(2)
+        bsa.plan_structured(desc, mask, rt, rs, row_ptr, col)
+        mark(3)
+        bsa.forward_csr(desc, att.q_t, att.k_f, att.v_f, row_ptr, col, att.o_t, workspace=att.workspace)
+        mark(4)
+        att.scatter_out(out)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_stage = {s: [] for s in stages}
+    totals = []
+    for ev in events:
+        for j, s in enumerate(stages):
+            per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
+        totals.append(ev[0].elapsed_time(ev[5]))
+    ms_step = float(np.mean(totals))
+    # every video query token attends the prefix and 64 keys per kept tile
+    pairs = wl.heads * wl.batch * (wl.n_prefix * wl.n_tokens + wl.n_video * wl.n_prefix)
+    pairs += entries * 64 * 64
+    F = 4.0 * wl.head_dim * pairs
+    fwd_ms = float(np.mean(per_stage["forward"]))
+    achieved = F / (fwd_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC_STRUCT,
+        "value": F / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid_thw": list(wl.grid), "tokens": wl.n_tokens,
+                   "video_tiles": wl.n_video_tiles, "batch": wl.batch, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "head_mask": "even spatial, odd temporal", "radius_t": rt,
+                   "radius_hw": rs, "kept_entries": entries,
+                   "mean_kept_tiles": entries / rows, "effective_tflop_per_call": F / 1e12},
+        "roofline": {"bound": "mfma", "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}> (CSR lists)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline_backward(wl, q, k, v, do, n_tiles: int):
     """The oracle's backward on one (batch, head) slice: lse, Delta and dQ of
     `n_tiles` sampled query tiles, dK and dV of `n_tiles` sampled key tiles
@@ -379,6 +469,12 @@ def main():
             print("bench.py --backward times static-tile workloads", file=sys.stderr)
             sys.exit(2)
         bench_backward(args, wl, q, k, v)
+        return
+    if args.structured:
+        if wl.dynamic:
+            print("bench.py --structured times static-tile workloads", file=sys.stderr)
+            sys.exit(2)
+        bench_structured(args, wl, q, k, v)
         return
     if args.varkeep:
         if wl.dynamic:

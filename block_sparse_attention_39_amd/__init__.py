@@ -6,14 +6,16 @@ by pooled score and attends exactly to them (plus an optional dense prefix).
 All of it runs in the hand-written HIP kernels of ``libbsa.so`` behind the C
 ABI in ``include/bsa.h``; this package is the thin Python binding.
 """
-from ._lib import (EXPORTS, LIB_PATH, MAX_CSR_HEADS, MAX_VIDEO_TILES, PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_VF, PERM_SCATTER,
+from ._lib import (EXPORTS, LIB_PATH, MASK_SPATIAL, MASK_TEMPORAL, MAX_CSR_HEADS, MAX_VIDEO_TILES, PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_VF, PERM_SCATTER,
                    TILE_DYNAMIC, TILE_STATIC, BsaError, Desc, lib)
 from .api import (BlockSparseAttention, backward, backward_workspace_size, csr_entries, forward, forward_csr, gather,
-                  gather_kf, gather_vf, make_desc, permute_build, plan, plan_csr, pooled_views, scatter, workspace_size)
+                  gather_kf, gather_vf, make_desc, permute_build, plan, plan_csr, plan_structured, pooled_views, scatter,
+                  structured_entries, workspace_size)
 
 lib()  # fail at import if the HIP library was not built
 
 __all__ = ["BlockSparseAttention", "BsaError", "Desc", "EXPORTS", "LIB_PATH", "MAX_CSR_HEADS", "MAX_VIDEO_TILES",
-           "backward", "backward_workspace_size", "csr_entries", "forward", "forward_csr", "plan_csr",
+           "backward", "backward_workspace_size", "csr_entries", "forward", "forward_csr", "plan_csr", "plan_structured",
+           "structured_entries", "MASK_SPATIAL", "MASK_TEMPORAL",
            "gather", "gather_kf", "gather_vf", "make_desc", "permute_build", "plan", "pooled_views", "scatter", "workspace_size",
            "PERM_BUILD", "PERM_GATHER", "PERM_GATHER_KF", "PERM_GATHER_VF", "PERM_SCATTER", "TILE_STATIC", "TILE_DYNAMIC"]

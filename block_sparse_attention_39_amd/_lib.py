@@ -19,7 +19,9 @@ MAX_VIDEO_TILES = 8192
 MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
 EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_csr_entries", "bsa_plan_csr",
-           "bsa_forward_csr", "bsa_backward_workspace_size", "bsa_backward", "bsa_status_string", "bsa_version")
+           "bsa_forward_csr", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
+           "bsa_backward", "bsa_status_string", "bsa_version")
+MASK_SPATIAL, MASK_TEMPORAL = 0, 1
 MAX_CSR_HEADS = 256
 
 
@@ -60,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.bsa_csr_entries.argtypes = [D, P, ctypes.POINTER(I64)]
         L.bsa_plan_csr.argtypes = [D, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
         L.bsa_forward_csr.argtypes = [D, P, P, P, P, P, I64, P, P, P, ctypes.c_size_t, P]
+        I32 = ctypes.c_int32
+        L.bsa_structured_entries.argtypes = [D, P, I32, I32, ctypes.POINTER(I64)]
+        L.bsa_plan_structured.argtypes = [D, P, I32, I32, P, P, I64, P]
         L.bsa_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_status_string.argtypes = [ctypes.c_int]

@@ -139,6 +139,31 @@ def forward_csr(desc: Desc, q_tiled, k_frag, v_frag, row_ptr, col_idx, o_tiled, 
                                  _stream(stream)), "bsa_forward_csr")
 
 
+def _head_mask(desc: Desc, head_mask):
+    if len(head_mask) != desc.heads:
+        raise ValueError("head_mask needs one entry per head")
+    arr = (ctypes.c_int32 * len(head_mask))(*[int(x) for x in head_mask])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def structured_entries(desc: Desc, head_mask, radius_t: int, radius_hw: int) -> int:
+    """Entries of the structured CSR lists (MASK_SPATIAL / MASK_TEMPORAL per head)."""
+    arr, hp = _head_mask(desc, head_mask)
+    n = ctypes.c_int64(0)
+    _check(lib().bsa_structured_entries(ctypes.byref(desc), hp, int(radius_t), int(radius_hw), ctypes.byref(n)),
+           "bsa_structured_entries")
+    return n.value
+
+
+def plan_structured(desc: Desc, head_mask, radius_t: int, radius_hw: int, row_ptr, col_idx, stream=None):
+    """Structured lists: spatial heads keep the tiles within radius_t tile-frames,
+    temporal heads the tiles within radius_hw in h and w at every time; CSR
+    output for forward_csr."""
+    arr, hp = _head_mask(desc, head_mask)
+    _check(lib().bsa_plan_structured(ctypes.byref(desc), hp, int(radius_t), int(radius_hw), _ptr(row_ptr),
+                                     _ptr(col_idx), col_idx.numel(), _stream(stream)), "bsa_plan_structured")
+
+
 def backward_workspace_size(desc: Desc) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().bsa_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "bsa_backward_workspace_size")

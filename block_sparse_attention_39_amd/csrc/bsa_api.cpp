@@ -4,6 +4,7 @@
 // rejected call enqueues nothing.
 #include "bsa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -375,6 +376,75 @@ bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void
     a.keep = 1;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+// ---- structured lists (spatial / temporal heads) ------------------------------
+
+namespace {
+
+// sum over x in [0, n) of the size of [x - r, x + r] clipped to [0, n)
+int64_t range_sum(int64_t n, int64_t r) {
+    int64_t s = 0;
+    for (int64_t x = 0; x < n; ++x) s += std::min(x + r, n - 1) - std::max(x - r, (int64_t)0) + 1;
+    return s;
+}
+
+bsa_status struct_rule(const bsa_desc* desc, const Geo& g, const int32_t* head_mask, int32_t radius_t,
+                       int32_t radius_hw, bsa::StructRule* sr, int64_t* entries) {
+    if (g.dynamic) return BSA_ERR_UNSUPPORTED;  // the rule needs the regular tile grid
+    if (g.H > BSA_MAX_CSR_HEADS) return BSA_ERR_UNSUPPORTED;
+    if (!head_mask) return BSA_ERR_NULL;
+    if (radius_t < 0 || radius_hw < 0) return BSA_ERR_ARG;
+    const int64_t Tt = g.T / desc->tile_t, Th = g.Hg / desc->tile_h, Tw = g.W / desc->tile_w;
+    const int64_t spatial = range_sum(Tt, radius_t) * Th * Tw * Th * Tw;
+    const int64_t temporal = Tt * Tt * range_sum(Th, radius_hw) * range_sum(Tw, radius_hw);
+    int64_t sum = 0;
+    for (int64_t h = 0; h < g.H; ++h) {
+        if (head_mask[h] != BSA_MASK_SPATIAL && head_mask[h] != BSA_MASK_TEMPORAL) return BSA_ERR_ARG;
+        if (sr) sr->kind[h] = head_mask[h];
+        sum += head_mask[h] == BSA_MASK_SPATIAL ? spatial : temporal;
+    }
+    if (sr) {
+        sr->Tt = (int)Tt;
+        sr->Th = (int)Th;
+        sr->Tw = (int)Tw;
+        sr->rt = radius_t;
+        sr->rs = radius_hw;
+    }
+    *entries = g.B * sum;
+    return BSA_OK;
+}
+
+}  // namespace
+
+bsa_status bsa_structured_entries(const bsa_desc* desc, const int32_t* head_mask, int32_t radius_t,
+                                  int32_t radius_hw, int64_t* entries) {
+    if (!entries) return BSA_ERR_NULL;
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.empty || g.nvt == 0) {
+        *entries = 0;
+        return BSA_OK;
+    }
+    return struct_rule(desc, g, head_mask, radius_t, radius_hw, nullptr, entries);
+}
+
+bsa_status bsa_plan_structured(const bsa_desc* desc, const int32_t* head_mask, int32_t radius_t, int32_t radius_hw,
+                               int64_t* row_ptr, int32_t* col_idx, int64_t col_entries, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.empty || g.nvt == 0) return BSA_OK;
+    bsa::StructRule sr{};
+    int64_t need = 0;
+    st = struct_rule(desc, g, head_mask, radius_t, radius_hw, &sr, &need);
+    if (st != BSA_OK) return st;
+    if (!row_ptr || !col_idx) return BSA_ERR_NULL;
+    if (col_entries < need) return BSA_ERR_SHAPE;
+    if (misaligned(row_ptr, 8) || misaligned(col_idx, 4)) return BSA_ERR_ALIGN;
+    return launched(bsa::launch_structured(sr, (int)g.BH, (int)g.H, row_ptr, col_idx, static_cast<hipStream_t>(stream)));
 }
 
 bsa_status bsa_backward_workspace_size(const bsa_desc* desc, size_t* bytes) {

@@ -57,6 +57,14 @@ hipError_t launch_csr_rowptr(const CsrKeep& kh, const int32_t* keep_rows, int BH
 hipError_t launch_topk_csr(const float* scores, int32_t* col_idx, const int64_t* row_ptr, int64_t row0, int rows,
                            int n, hipStream_t s);
 
+// Structured lists: per head a mask kind (BSA_MASK_*), the tile grid and the
+// radii; row pointers and the ascending lists of every row.
+struct StructRule {
+    int32_t kind[BSA_MAX_CSR_HEADS];
+    int Tt, Th, Tw, rt, rs;
+};
+hipError_t launch_structured(const StructRule& sr, int BH, int H, int64_t* row_ptr, int32_t* col, hipStream_t s);
+
 struct ForwardArgs {
     const uint16_t* q;       // tiled [BH][Ntot][D]
     const uint16_t* k;       // K-fragment layout [BH][Ntot/64][2][D/16][64][8]

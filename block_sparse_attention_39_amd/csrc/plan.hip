@@ -244,21 +244,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, 
     }
 }
 
-// Row pointers of variable-keep lists: row (bh, i) keeps keep_rows[bh][i]
-// clamped to [1, keep_h[h]] tiles (keep_h[h] without keep_rows); row_ptr is
-// the exclusive prefix sum over rows in (bh, i) order.  One block: each
-// thread sums a contiguous run of rows, the runs are scanned, then written.
-__global__ __launch_bounds__(1024) void csr_rowptr_kernel(CsrKeep kh, const int32_t* __restrict__ keep_rows,
-                                                          int BH, int H, int nvt, int64_t* __restrict__ row_ptr) {
+// Row pointers from per-row lengths: row_ptr is the exclusive prefix sum of
+// len(r) over rows 0..rows-1.  One block of 1,024 threads: each sums a
+// contiguous run of rows, the runs are scanned in LDS, then written.
+template <typename Len>
+__device__ void rowptr_scan(int64_t rows, Len len, int64_t* __restrict__ row_ptr) {
     __shared__ int64_t part[1024];
-    const int64_t rows = (int64_t)BH * nvt;
     const int64_t per = (rows + 1023) / 1024;
     const int64_t r_lo = min((int64_t)threadIdx.x * per, rows), r_hi = min(r_lo + per, rows);
-    auto len = [&](int64_t r) -> int64_t {
-        const int h = (int)((r / nvt) % H);
-        const int cap = kh.k[h];
-        return keep_rows ? (int64_t)min(max(keep_rows[r], 1), cap) : (int64_t)cap;
-    };
     int64_t sum = 0;
     for (int64_t r = r_lo; r < r_hi; ++r) sum += len(r);
     part[threadIdx.x] = sum;
@@ -278,11 +271,74 @@ __global__ __launch_bounds__(1024) void csr_rowptr_kernel(CsrKeep kh, const int3
     if (threadIdx.x == 1023) row_ptr[rows] = part[1023];
 }
 
+// Variable keep: row (bh, i) keeps keep_rows[bh][i] clamped to [1, keep_h[h]]
+// tiles (keep_h[h] without keep_rows).
+__global__ __launch_bounds__(1024) void csr_rowptr_kernel(CsrKeep kh, const int32_t* __restrict__ keep_rows,
+                                                          int BH, int H, int nvt, int64_t* __restrict__ row_ptr) {
+    auto len = [&](int64_t r) -> int64_t {
+        const int cap = kh.k[(int)((r / nvt) % H)];
+        return keep_rows ? (int64_t)min(max(keep_rows[r], 1), cap) : (int64_t)cap;
+    };
+    rowptr_scan((int64_t)BH * nvt, len, row_ptr);
+}
+
+// Structured lists: the box of key tiles a query tile keeps, in tile-grid
+// coordinates (raster tile order: tile (t, h, w) is number (t*Th + h)*Tw + w).
+// A spatial head keeps every tile within rt tile-frames of the query tile's;
+// a temporal head keeps, at every time, the tiles within rs in h and in w of
+// the query tile's position.
+struct TileBox {
+    int t0, t1, h0, h1, w0, w1;  // inclusive
+    __device__ int64_t count() const { return (int64_t)(t1 - t0 + 1) * (h1 - h0 + 1) * (w1 - w0 + 1); }
+};
+__device__ inline TileBox struct_box(const StructRule& sr, int kind, int i) {
+    const int wi = i % sr.Tw, hi = (i / sr.Tw) % sr.Th, ti = i / (sr.Tw * sr.Th);
+    TileBox b;
+    if (kind == BSA_MASK_SPATIAL) {
+        b = {max(ti - sr.rt, 0), min(ti + sr.rt, sr.Tt - 1), 0, sr.Th - 1, 0, sr.Tw - 1};
+    } else {
+        b = {0, sr.Tt - 1, max(hi - sr.rs, 0), min(hi + sr.rs, sr.Th - 1), max(wi - sr.rs, 0),
+             min(wi + sr.rs, sr.Tw - 1)};
+    }
+    return b;
+}
+
+__global__ __launch_bounds__(1024) void struct_rowptr_kernel(StructRule sr, int BH, int H,
+                                                             int64_t* __restrict__ row_ptr) {
+    const int nvt = sr.Tt * sr.Th * sr.Tw;
+    auto len = [&](int64_t r) -> int64_t {
+        return struct_box(sr, sr.kind[(int)((r / nvt) % H)], (int)(r % nvt)).count();
+    };
+    rowptr_scan((int64_t)BH * nvt, len, row_ptr);
+}
+
+// One 64-thread block per row writes the row's box of tiles, ascending.
+__global__ __launch_bounds__(64) void struct_fill_kernel(StructRule sr, int H, const int64_t* __restrict__ row_ptr,
+                                                         int32_t* __restrict__ col) {
+    const int nvt = sr.Tt * sr.Th * sr.Tw;
+    const int64_t r = blockIdx.x;
+    const TileBox b = struct_box(sr, sr.kind[(int)((r / nvt) % H)], (int)(r % nvt));
+    const int nh = b.h1 - b.h0 + 1, nw = b.w1 - b.w0 + 1;
+    const int64_t n = b.count(), beg = row_ptr[r];
+    for (int64_t e = threadIdx.x; e < n; e += 64) {
+        const int w = b.w0 + (int)(e % nw), h = b.h0 + (int)((e / nw) % nh), t = b.t0 + (int)(e / ((int64_t)nw * nh));
+        col[beg + e] = (t * sr.Th + h) * sr.Tw + w;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_csr_rowptr(const CsrKeep& kh, const int32_t* keep_rows, int BH, int H, int nvt, int64_t* row_ptr,
                              hipStream_t s) {
     hipLaunchKernelGGL(csr_rowptr_kernel, dim3(1), dim3(1024), 0, s, kh, keep_rows, BH, H, nvt, row_ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_structured(const StructRule& sr, int BH, int H, int64_t* row_ptr, int32_t* col, hipStream_t s) {
+    const int64_t rows = (int64_t)BH * sr.Tt * sr.Th * sr.Tw;
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(struct_rowptr_kernel, dim3(1), dim3(1024), 0, s, sr, BH, H, row_ptr);
+    hipLaunchKernelGGL(struct_fill_kernel, dim3((unsigned)rows), dim3(64), 0, s, sr, H, (const int64_t*)row_ptr, col);
     return hipGetLastError();
 }
 

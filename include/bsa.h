@@ -221,6 +221,32 @@ bsa_status bsa_forward_csr(const bsa_desc *desc, const void *q_tiled, const void
                            void *stream);
 
 /*
+ * Structured lists: kept tiles from a fixed spatial or temporal rule per head
+ * instead of scores.  "Sparse VideoGen TPU 최적화" (aibase.it), section
+ * "Sparse VideoGen의 핵심 아이디어": attention heads are mostly spatial (a
+ * query looks at patches of its own or nearby frames) or temporal (it follows
+ * its spatial position across frames); section "실무에서 배울 최적화 기준": with
+ * tokens permuted into tiles such masks select whole tiles.  Static tile mode
+ * only (BSA_ERR_UNSUPPORTED in dynamic mode).  In the tile grid (Tt x Th x Tw
+ * tiles, video tile (t, h, w) numbered (t*Th + h)*Tw + w), video query tile
+ * (ti, hi, wi) of a head keeps
+ *   BSA_MASK_SPATIAL:  every tile (t, h, w) with |t - ti| <= radius_t;
+ *   BSA_MASK_TEMPORAL: every tile (t, h, w) with |h - hi| <= radius_hw and
+ *                      |w - wi| <= radius_hw,
+ * ascending, written as CSR lists (row_ptr / col_idx as for bsa_plan_csr) for
+ * bsa_forward_csr; the prefix stays dense.  head_mask: host int32 [H] of
+ * BSA_MASK_* (at most BSA_MAX_CSR_HEADS heads); radii >= 0 (BSA_ERR_ARG
+ * otherwise).  bsa_structured_entries (host only) gives the exact entry count;
+ * a smaller col_entries gives BSA_ERR_SHAPE.  No workspace.
+ */
+enum { BSA_MASK_SPATIAL = 0, BSA_MASK_TEMPORAL = 1 };
+bsa_status bsa_structured_entries(const bsa_desc *desc, const int32_t *head_mask, int32_t radius_t,
+                                  int32_t radius_hw, int64_t *entries);
+bsa_status bsa_plan_structured(const bsa_desc *desc, const int32_t *head_mask, int32_t radius_t,
+                               int32_t radius_hw, int64_t *row_ptr, int32_t *col_idx,
+                               int64_t col_entries, void *stream);
+
+/*
  * Bytes of device workspace that bsa_backward needs for `desc` (about seven
  * times the size of one bf16 [B][H][Ntot][D] tensor: the fragment-layout
  * copies of Q, K, V and dO the gradient kernels stream).  Host-only.
@@ -263,7 +289,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 600
+#define BSA_VERSION 700
 
 #ifdef __cplusplus
 }

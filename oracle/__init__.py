@@ -265,6 +265,40 @@ def plan_csr(qp, kp, keep_per_head, keep_rows=None):
     return row_ptr, col
 
 
+def plan_structured(tile_grid, head_mask, radius_t: int, radius_hw: int, batch: int):
+    """Structured kept lists (Sparse VideoGen page, section on its key idea:
+    spatial heads look within nearby frames, temporal heads follow a position
+    across frames).  ``tile_grid`` = (Tt, Th, Tw) tiles; video tile (t, h, w)
+    is number (t*Th + h)*Tw + w.  For head h, query tile (ti, hi, wi) keeps
+    every tile with |t - ti| <= radius_t (head_mask 0, spatial) or with
+    |h - hi| <= radius_hw and |w - wi| <= radius_hw (1, temporal), ascending.
+    Returns ``(row_ptr int64 [batch*H*nvt + 1], col int32)``, rows in (b, h, i)
+    order."""
+    Tt, Th, Tw = tile_grid
+    nvt = Tt * Th * Tw
+    lists = {}
+    for kind in (0, 1):
+        rows = []
+        for i in range(nvt):
+            ti, hi, wi = i // (Th * Tw), (i // Tw) % Th, i % Tw
+            keep = []
+            for j in range(nvt):
+                tj, hj, wj = j // (Th * Tw), (j // Tw) % Th, j % Tw
+                if kind == 0:
+                    ok = abs(tj - ti) <= radius_t
+                else:
+                    ok = abs(hj - hi) <= radius_hw and abs(wj - wi) <= radius_hw
+                if ok:
+                    keep.append(j)
+            rows.append(np.array(keep, np.int32))
+        lists[kind] = rows
+    all_rows = [lists[int(m)][i] for _ in range(batch) for m in head_mask for i in range(nvt)]
+    row_ptr = np.zeros(len(all_rows) + 1, np.int64)
+    row_ptr[1:] = np.cumsum([len(r) for r in all_rows])
+    col = np.concatenate(all_rows).astype(np.int32) if all_rows else np.zeros(0, np.int32)
+    return row_ptr, col
+
+
 def plan(q_tiled, k_tiled, n_prefix: int, k: int):
     """Pool Q and K, score and select: ``(qp, kp, idx, s_k, s_k1, mag)``."""
     qp = pool(q_tiled, n_prefix)

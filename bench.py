@@ -103,21 +103,31 @@ def cpu_baseline(wl, q, k, v, n_tiles: int):
     qs, ks, vs = sl(q), sl(k), sl(v)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
-    if wl.dynamic:
-        st = oracle.shape_stats(qs, wl.n_prefix, wl.grid)
-        shape, _ = oracle.shape_choose(st, wl.grid, float(np.float32(wl.tau)))
-        perm = oracle.perm_dynamic(shape, wl.grid)
+    if wl.padded:
+        perm = oracle.perm_static_padded(wl.grid, wl.tile)[None]
+        qt, kt, vt = (oracle.gather_padded(x, perm, wl.n_prefix) for x in (qs, ks, vs))
+        qp, kp = oracle.pool_padded(qt, perm, wl.n_prefix), oracle.pool_padded(kt, perm, wl.n_prefix)
     else:
-        perm = oracle.perm_static(wl.grid, wl.tile)[None]
-    qt, kt, vt = (oracle.gather(x, perm, wl.n_prefix) for x in (qs, ks, vs))
-    qp, kp = oracle.pool(qt, wl.n_prefix), oracle.pool(kt, wl.n_prefix)
+        if wl.dynamic:
+            st = oracle.shape_stats(qs, wl.n_prefix, wl.grid)
+            shape, _ = oracle.shape_choose(st, wl.grid, float(np.float32(wl.tau)))
+            perm = oracle.perm_dynamic(shape, wl.grid)
+        else:
+            perm = oracle.perm_static(wl.grid, wl.tile)[None]
+        qt, kt, vt = (oracle.gather(x, perm, wl.n_prefix) for x in (qs, ks, vs))
+        qp, kp = oracle.pool(qt, wl.n_prefix), oracle.pool(kt, wl.n_prefix)
     idx, *_ = oracle.topk(qp, kp, wl.keep_tiles)
     t_plan = time.perf_counter() - t0
-    nqt = wl.n_tokens // 64
+    nqt = wl.n_tiled_tokens // 64
     rng = np.random.default_rng(1234)
     tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
+    scale = float(np.float32(wl.scale))
     t0 = time.perf_counter()
-    oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0], float(np.float32(wl.scale)), tiles)
+    if wl.padded:
+        oracle.attention_padded(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0],
+                                oracle.key_real(perm[0], wl.n_prefix), scale, tiles)
+    else:
+        oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0], scale, tiles)
     t_attn = time.perf_counter() - t0
     head_seconds = t_plan + t_attn * nqt / len(tiles)
     head_flops = wl.effective_flops() / (wl.batch * wl.heads)
@@ -494,7 +504,7 @@ def main():
     dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
-                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
     att = bsa.BlockSparseAttention(desc)
     out = torch.empty_like(qd)
     torch.cuda.synchronize()
@@ -536,7 +546,7 @@ def main():
     fwd_ms = float(np.mean(per_stage["forward"]))
     # the forward stage is the attention kernel (plus a 4 us counter clear; a
     # dense prefix adds the plain kernel for the prefix query tiles)
-    kernel = f"sparse_fwd_grouped_kernel<{wl.head_dim}>"
+    kernel = f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}>"
     achieved = F / (fwd_ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -555,6 +565,7 @@ def main():
                    "video_tiles": wl.n_video_tiles, "prefix_tokens": wl.n_prefix, "batch": wl.batch,
                    "heads": wl.heads, "head_dim": wl.head_dim, "keep_tiles": wl.keep_tiles,
                    "tile": "dynamic" if wl.dynamic else "x".join(map(str, wl.tile)),
+                   "padded_video_tokens": wl.n_video_slots if wl.padded else None,
                    "effective_tflop_per_call": F / 1e12},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,

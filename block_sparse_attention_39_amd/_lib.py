@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
 BSA_OK = 0
 STATUS_NAMES = {0: "BSA_OK", -1: "BSA_ERR_NULL", -2: "BSA_ERR_SHAPE", -3: "BSA_ERR_UNSUPPORTED",
                 -4: "BSA_ERR_ALIGN", -5: "BSA_ERR_WORKSPACE", -6: "BSA_ERR_LAUNCH", -7: "BSA_ERR_ARG"}
-TILE_STATIC, TILE_DYNAMIC = 0, 1
+TILE_STATIC, TILE_DYNAMIC, TILE_STATIC_PADDED = 0, 1, 2
 PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_KF, PERM_GATHER_VF = 0, 1, 2, 3, 4
 MAX_VIDEO_TILES = 8192
 MAX_TILES = 16384

@@ -13,15 +13,27 @@ import math
 import torch
 
 from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_VF, PERM_SCATTER, TILE_DYNAMIC,
-                   TILE_STATIC, BsaError, Desc, lib)
+                   TILE_STATIC, TILE_STATIC_PADDED, BsaError, Desc, lib)
 
 
 def make_desc(batch: int, heads: int, head_dim: int, grid, keep_tiles: int, *, scale: float | None = None,
-              n_prefix: int = 0, dynamic: bool = False, tile=(4, 4, 4), tau: float = 0.10) -> Desc:
+              n_prefix: int = 0, dynamic: bool = False, tile=(4, 4, 4), tau: float = 0.10,
+              padded: bool = False) -> Desc:
+    """``padded``: a ragged grid, rounded up to whole static tiles."""
     T, H, W = grid
-    return Desc(batch, heads, head_dim, T, H, W, n_prefix, TILE_DYNAMIC if dynamic else TILE_STATIC,
-                tile[0], tile[1], tile[2], keep_tiles,
+    mode = TILE_DYNAMIC if dynamic else (TILE_STATIC_PADDED if padded else TILE_STATIC)
+    return Desc(batch, heads, head_dim, T, H, W, n_prefix, mode, tile[0], tile[1], tile[2], keep_tiles,
                 1.0 / math.sqrt(head_dim) if scale is None else scale, tau)
+
+
+def video_slots(desc: Desc) -> int:
+    """Video tokens of the tiled layouts: the grid, or for a ragged grid the
+    grid rounded up to whole tiles."""
+    T, H, W = desc.grid_t, desc.grid_h, desc.grid_w
+    if desc.tile_mode != TILE_STATIC_PADDED:
+        return T * H * W
+    tt, th, tw = desc.tile_t, desc.tile_h, desc.tile_w
+    return -(-T // tt) * tt * (-(-H // th) * th) * (-(-W // tw) * tw)
 
 
 def _ptr(t):
@@ -183,7 +195,7 @@ def backward(desc: Desc, q, k, v, o, d_o, lse, perm, block_idx, dq, dk, dv, work
 def pooled_views(desc: Desc, workspace):
     """(qbar, kbar) float views of the workspace after bsa_plan ([B, H, nVT, D])."""
     B, H, D = desc.batch, desc.heads, desc.head_dim
-    nvt = desc.grid_t * desc.grid_h * desc.grid_w // 64
+    nvt = video_slots(desc) // 64
     n = B * H * nvt * D
     pooled_bytes = (n * 4 + 255) // 256 * 256
     f = workspace.view(torch.uint8)
@@ -203,7 +215,7 @@ class BlockSparseAttention:
     def __init__(self, desc: Desc, device="cuda", with_lse: bool = False, grouped: bool = True):
         self.desc = desc
         B, H, D = desc.batch, desc.heads, desc.head_dim
-        self.n_video = desc.grid_t * desc.grid_h * desc.grid_w
+        self.n_video = video_slots(desc)  # tiled video tokens (padding slots included)
         self.n_tot = desc.n_prefix + self.n_video
         self.nvt = self.n_video // 64
         self.dynamic = desc.tile_mode == TILE_DYNAMIC

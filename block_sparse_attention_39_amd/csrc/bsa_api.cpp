@@ -17,10 +17,16 @@ constexpr size_t kScoreChunkBytes = size_t(1) << 30;  // cap on the score buffer
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// n_video: video tokens of the tiled layouts (padding slots included);
+// n_ras: video tokens of the raster layouts.  They differ only for a ragged
+// grid padded to whole tiles, which `pad` then describes (pad.T == 0 otherwise).
 struct Geo {
-    int64_t B, H, D, T, Hg, W, npf, n_video, n_tot, nvt, npt, BH, k, regions;
+    int64_t B, H, D, T, Hg, W, npf, n_video, n_ras, n_tot, nvt, npt, BH, k, regions;
+    int64_t Tt, Th, Tw;  // static tile grid (tiles per axis)
     bool dynamic;
+    bool padded;
     bool empty;
+    bsa::PadGeo pad;
 };
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
@@ -39,12 +45,25 @@ bsa_status check_desc(const bsa_desc* d, Geo* g) {
     g->Hg = d->grid_h;
     g->W = d->grid_w;
     g->npf = d->n_prefix;
-    g->n_video = g->T * g->Hg * g->W;
-    if (d->tile_mode == BSA_TILE_STATIC) {
-        g->dynamic = false;
+    g->n_ras = g->T * g->Hg * g->W;
+    g->n_video = g->n_ras;
+    g->dynamic = g->padded = false;
+    g->pad = bsa::PadGeo{};
+    g->Tt = g->Th = g->Tw = 0;
+    if (d->tile_mode == BSA_TILE_STATIC || d->tile_mode == BSA_TILE_STATIC_PADDED) {
         if (d->tile_t < 1 || d->tile_h < 1 || d->tile_w < 1) return BSA_ERR_SHAPE;
         if ((int64_t)d->tile_t * d->tile_h * d->tile_w != bsa::kTile) return BSA_ERR_SHAPE;
-        if (g->T % d->tile_t || g->Hg % d->tile_h || g->W % d->tile_w) return BSA_ERR_SHAPE;
+        g->Tt = (g->T + d->tile_t - 1) / d->tile_t;
+        g->Th = (g->Hg + d->tile_h - 1) / d->tile_h;
+        g->Tw = (g->W + d->tile_w - 1) / d->tile_w;
+        if (d->tile_mode == BSA_TILE_STATIC) {
+            if (g->T % d->tile_t || g->Hg % d->tile_h || g->W % d->tile_w) return BSA_ERR_SHAPE;
+        } else {
+            g->n_video = g->Tt * g->Th * g->Tw * bsa::kTile;
+            g->padded = g->n_video != g->n_ras;
+            if (g->padded)
+                g->pad = bsa::make_pad_geo((int)g->T, (int)g->Hg, (int)g->W, d->tile_t, d->tile_h, d->tile_w);
+        }
     } else if (d->tile_mode == BSA_TILE_DYNAMIC) {
         g->dynamic = true;
         if (g->T % 8 || g->Hg % 8 || g->W % 8) return BSA_ERR_SHAPE;
@@ -171,7 +190,7 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     if (g.B == 0 || g.n_tot == 0) return BSA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (op == BSA_PERM_BUILD) {
-        if (g.n_video == 0) return BSA_OK;
+        if (g.n_ras == 0) return BSA_OK;
         if (!perm) return BSA_ERR_NULL;
         if (misaligned(perm, 4)) return BSA_ERR_ALIGN;
         if (!g.dynamic)
@@ -197,13 +216,13 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
     if (op == BSA_PERM_GATHER_KF)
         return launched(bsa::launch_gather_kf(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
-                                              (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s));
+                                              (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s, g.n_ras));
     if (op == BSA_PERM_GATHER_VF)
         return launched(bsa::launch_gather_vf(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
-                                              (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s));
+                                              (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s, g.n_ras));
     return launched(bsa::launch_permute_copy(op == BSA_PERM_SCATTER, static_cast<const uint16_t*>(src),
                                              static_cast<uint16_t*>(dst), perm, (int)g.B, (int)g.H, (int)g.D,
-                                             (int)g.npf, g.n_video, s));
+                                             (int)g.npf, g.n_video, s, g.n_ras));
 }
 
 bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_frag, int32_t* block_idx, void* ws,
@@ -224,7 +243,7 @@ bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_fra
     float* kbar = reinterpret_cast<float*>(w + L.kbar);
     float* scores = reinterpret_cast<float*>(w + L.scores);
     hipError_t e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag),
-                                    qbar, kbar, (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s);
+                                    qbar, kbar, (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s, g.pad);
     for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
         const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
         e = bsa::launch_scores(qbar + b0 * g.nvt * g.D, kbar + b0 * g.nvt * g.D, scores, (int)cnt, (int)g.nvt,
@@ -265,6 +284,7 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
     a.npt = (int)g.npt;
     a.nvt = (int)g.nvt;
     a.keep = (int)g.k;
+    a.pad = g.pad;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }
@@ -330,7 +350,7 @@ bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k
     hipError_t e = bsa::launch_csr_rowptr(kh, keep_rows, (int)g.BH, (int)g.H, (int)g.nvt, row_ptr, s);
     if (e == hipSuccess)
         e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag), qbar, kbar,
-                             (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s);
+                             (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s, g.pad);
     for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
         const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
         e = bsa::launch_scores(qbar + b0 * g.nvt * g.D, kbar + b0 * g.nvt * g.D, scores, (int)cnt, (int)g.nvt,
@@ -374,6 +394,7 @@ bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void
     a.npt = (int)g.npt;
     a.nvt = (int)g.nvt;
     a.keep = 1;
+    a.pad = g.pad;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }
@@ -395,7 +416,7 @@ bsa_status struct_rule(const bsa_desc* desc, const Geo& g, const int32_t* head_m
     if (g.H > BSA_MAX_CSR_HEADS) return BSA_ERR_UNSUPPORTED;
     if (!head_mask) return BSA_ERR_NULL;
     if (radius_t < 0 || radius_hw < 0) return BSA_ERR_ARG;
-    const int64_t Tt = g.T / desc->tile_t, Th = g.Hg / desc->tile_h, Tw = g.W / desc->tile_w;
+    const int64_t Tt = g.Tt, Th = g.Th, Tw = g.Tw;
     const int64_t spatial = range_sum(Tt, radius_t) * Th * Tw * Th * Tw;
     const int64_t temporal = Tt * Tt * range_sum(Th, radius_hw) * range_sum(Tw, radius_hw);
     int64_t sum = 0;
@@ -463,6 +484,7 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
     if (g.npt + g.nvt > BSA_MAX_TILES || g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.padded) return BSA_ERR_UNSUPPORTED;  // no key-padding masks in the backward kernels
     if (g.empty) return BSA_OK;
     if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return BSA_ERR_NULL;
     if (g.nvt > 0 && (!perm || !block_idx)) return BSA_ERR_NULL;

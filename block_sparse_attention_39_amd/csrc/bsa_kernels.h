@@ -10,21 +10,54 @@ namespace bsa {
 
 constexpr int kTile = 64;  // tokens per tile
 
+// A ragged video grid padded up to whole static tiles: the real extents, the
+// tile extents and the tile counts per axis.  T == 0: no padding (every tile
+// full).  Tile (ti, hi, wi) is video tile (ti*Th + hi)*Tw + wi; its token
+// (lt, lh, lw) (raster inside the tile) is real iff ti*tt + lt < T,
+// hi*th + lh < Hg and wi*tw + lw < W.  real[c]: bit j set iff token j of a
+// tile of boundary class c is real, class bit 2/1/0 meaning the tile is the
+// last along t/h/w on an axis cut short (make_pad_geo fills it).
+struct PadGeo {
+    int T, Hg, W;
+    int tt, th, tw;
+    int Tt, Th, Tw;
+    uint64_t real[8];
+};
+
+inline PadGeo make_pad_geo(int T, int Hg, int W, int tt, int th, int tw) {
+    PadGeo g{};
+    g.T = T, g.Hg = Hg, g.W = W, g.tt = tt, g.th = th, g.tw = tw;
+    g.Tt = (T + tt - 1) / tt, g.Th = (Hg + th - 1) / th, g.Tw = (W + tw - 1) / tw;
+    for (int c = 0; c < 8; ++c) {
+        const int nt = (c & 4) ? T - (g.Tt - 1) * tt : tt;
+        const int nh = (c & 2) ? Hg - (g.Th - 1) * th : th;
+        const int nw = (c & 1) ? W - (g.Tw - 1) * tw : tw;
+        for (int j = 0; j < kTile; ++j) {
+            const int lt = j / (th * tw), lh = (j / tw) % th, lw = j % tw;
+            if (lt < nt && lh < nh && lw < nw) g.real[c] |= uint64_t(1) << j;
+        }
+    }
+    return g;
+}
+
 // Static tile order: perm[b][p] for all b (the same closed form per batch).
 hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int tw, int32_t* perm,
                               hipStream_t s);
 
-// Raster [B][Ntot][H][D] <-> tiled [B][H][Ntot][D] through perm (prefix kept in place).
+// Raster [B][n_prefix + n_raster_video][H][D] <-> tiled [B][H][n_prefix + n_video][D]
+// through perm (prefix kept in place; perm -1 marks a padding slot: gathered
+// as zeros, not scattered).  n_raster_video < 0: the same as n_video.
 hipError_t launch_permute_copy(bool to_raster, const uint16_t* src, uint16_t* dst, const int32_t* perm,
-                               int B, int H, int D, int n_prefix, int64_t n_video, hipStream_t s);
+                               int B, int H, int D, int n_prefix, int64_t n_video, hipStream_t s,
+                               int64_t n_raster_video = -1);
 
 // Raster [B][Ntot][H][D] -> the K-fragment and V-fragment layouts (kfrag, vfrag
 // of the C interface): the tiled order with every 64-token tile laid out in
 // the operand order of the attention kernel's MFMAs.
 hipError_t launch_gather_kf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
-                            int n_prefix, int64_t n_video, hipStream_t s);
+                            int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video = -1);
 hipError_t launch_gather_vf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
-                            int n_prefix, int64_t n_video, hipStream_t s);
+                            int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video = -1);
 
 // Dynamic shapes: per-(b, region, head) partial |delta| sums, then shape choice
 // and the permutation.
@@ -37,8 +70,10 @@ hipError_t launch_perm_dynamic(const uint8_t* shape_map, int32_t* perm, int B, i
 
 // Mean of the 64 tokens of every video tile of Q (tiled) and K (K-fragment
 // layout) -> float [BH][nvt][D].
+// Tile means: the sum of the tile's real tokens / their number (64 unless
+// `pad` marks the tile as a padded boundary tile).
 hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
-                       int n_prefix, int nvt, int D, hipStream_t s);
+                       int n_prefix, int nvt, int D, hipStream_t s, const PadGeo& pad = PadGeo{});
 
 // scores[bh][i][j] = qbar_i . kbar_j (float) for bh in [0, BH).
 hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, int BH, int n, int D,
@@ -72,6 +107,7 @@ struct ForwardArgs {
     const int32_t* idx;      // [BH][nvt][keep], or CSR column indices when row_ptr is set
     const int64_t* row_ptr;  // CSR row pointers [BH * nvt + 1], or null (fixed keep)
     int64_t col_entries;     // CSR: entries of idx (list bounds are clamped to it)
+    PadGeo pad;              // ragged grid: padding keys of boundary tiles are masked
     uint16_t* o;             // tiled [BH][Ntot][D]
     float* lse;              // [BH][Ntot] or null
     int BH;

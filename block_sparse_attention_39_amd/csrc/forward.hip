@@ -184,6 +184,29 @@ __device__ inline int row_len(const ForwardArgs& a, int64_t bh, int vi) {
     return (int)min(max(e - b, (int64_t)1), (int64_t)a.nvt);
 }
 
+// Ragged grids: the LDS tile list carries, above the tile number, the
+// boundary class of a video key tile (0: no padding token), and the keys of a
+// padding slot get -inf logits.  Class bit 2/1/0: the tile is the last on the
+// t/h/w axis and that axis is cut short.
+constexpr int kTileBits = 0xFFFF;  // tile numbers are below BSA_MAX_TILES <= 2^16
+
+__device__ inline int pad_class(const PadGeo& g, int vt) {
+    const int wi = vt % g.Tw, hi = (vt / g.Tw) % g.Th, ti = vt / (g.Tw * g.Th);
+    return (((ti + 1) * g.tt > g.T) << 2 | ((hi + 1) * g.th > g.Hg) << 1 | ((wi + 1) * g.tw > g.W)) << 16;
+}
+
+// -inf for the padding keys in this lane's S^T elements, given the class's
+// 64-bit mask of real keys: element r = 8*c + e holds key 32*kh + 16*c + 8*hf + e.
+__device__ __attribute__((always_inline)) inline void mask_padding_keys(uint64_t real, int kh, int hf,
+                                                                        f32x16& sv) {
+    const uint32_t half = kh ? (uint32_t)(real >> 32) : (uint32_t)real;
+    const uint32_t x = half >> (8 * hf);
+    const uint32_t bits = (x & 0xffu) | ((x >> 8) & 0xff00u);  // bit r: element r is a real key
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (!((bits >> r) & 1u)) sv[r] = -INFINITY;
+}
+
 __device__ inline int list_len(const ForwardArgs& a, const Item& it) {
     return it.vi < 0 ? a.npt + a.nvt : a.npt + row_len(a, it.bh, it.vi);
 }
@@ -245,8 +268,9 @@ __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardA
 // One query tile, all four waves of the block, given the loads fetch_first
 // issued for it.  With `has_next`, the first loads of the block's next tile
 // `nx` are issued before this tile's epilogue, so that their latency overlaps
-// it.  `vi` < 0 marks a prefix (dense) query tile.
-template <int D>
+// it.  `vi` < 0 marks a prefix (dense) query tile.  kPad: a ragged grid, whose
+// boundary key tiles have padding keys to mask.
+template <int D, bool kPad>
 __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs& a, float* lds, const Item& it,
                                                                bool has_next, const Item& nx, const Wave& w,
                                                                bf16x8 (&kf)[2][Cfg<D>::SD],
@@ -268,7 +292,7 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     // ---- stage the tile in LDS: its key-tile list and Q^T fragments ------
     __syncthreads();  // the previous query tile's epilogue is done with LDS
     if (dense) {
-        for (int j = tid; j < n_iter; j += 256) list[j] = j;
+        for (int j = tid; j < n_iter; j += 256) list[j] = j | (kPad && j >= a.npt ? pad_class(a.pad, j - a.npt) : 0);
     } else {
         const int32_t* row = a.idx + row_begin(a, bh, it.vi);
         const int len = n_iter - a.npt;
@@ -276,10 +300,15 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
 #pragma unroll
         for (int u = 0; u < kListPre; ++u) {
             const int e = tid + 256 * u;
-            if (e < len) list[a.npt + e] = a.npt + min(max(lpre[u], 0), a.nvt - 1);
+            if (e < len) {
+                const int vt = min(max(lpre[u], 0), a.nvt - 1);
+                list[a.npt + e] = (a.npt + vt) | (kPad ? pad_class(a.pad, vt) : 0);
+            }
         }
-        for (int e = tid + 256 * kListPre; e < len; e += 256)
-            list[a.npt + e] = a.npt + min(max(row[e], 0), a.nvt - 1);
+        for (int e = tid + 256 * kListPre; e < len; e += 256) {
+            const int vt = min(max(row[e], 0), a.nvt - 1);
+            list[a.npt + e] = (a.npt + vt) | (kPad ? pad_class(a.pad, vt) : 0);
+        }
     }
 #pragma unroll
     for (int u = 0; u < Regs<D>::QPT; ++u) *(u32x4*)(qlds + (tid + 256 * u) * 16) = qpre[u];
@@ -297,7 +326,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     const int my_n = (n_iter - par + 1) >> 1;  // slices of this wave
     // tile of this wave's slice n; positions past the end repeat the last one
     // (their weights are forced to zero)
-#define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)])
+#define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)] & (kPad ? kTileBits : -1))
+#define CLASSED_AT(n_) (kPad ? __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)]) : 0)
 
     const uint8_t* kbh = (const uint8_t*)a.k + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
     const uint8_t* vbh = (const uint8_t*)a.v + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
@@ -324,6 +354,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                                                           sacc[0], 0, 0, 0);
     int t_v = TILE_AT(1);       // tile whose V is loaded next
     int t_k_next = TILE_AT(2);  // tile whose K is loaded next
+    int t_s = CLASSED_AT(0);    // ragged grid: slice n's list entry, with its boundary class
+    int t_s_next = CLASSED_AT(1);
 
     for (int n0 = 0; n0 <= my_n; n0 += 2) {
 #pragma unroll
@@ -332,7 +364,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
             const int t_k = t_k_next;  // K(n+2) and, one step later, V(n+2)
             // the tile after it, read from LDS now and used at the end of the
             // step (no wait for the read inside the step)
-            const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)];
+            const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)] & (kPad ? kTileBits : -1);
+            const int t_s_after = kPad ? list[min(par + 2 * (n + 2), n_iter - 1)] : 0;
             const uint8_t* const kaddr = kbh + (int64_t)t_k * TB;
             const uint8_t* const vaddr = vbh + (int64_t)t_v * TB;
 
@@ -371,6 +404,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                 // h = 1: PV of half 0 and S of half 0 (next slice)
                 const int pq = 1 - h, sq = 1 - h;
                 const float neg_m = vmask - m_ref[h];
+                // a slice of a boundary tile: its padding keys out
+                if (kPad && (t_s >> 16)) mask_padding_keys(a.pad.real[t_s >> 16], kh, hf, sacc[h]);
                 float xa[8][2], xe[8][2];
                 bf16x8 qv[SD];
 #pragma unroll
@@ -462,9 +497,14 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
 
             t_v = t_k;
             t_k_next = __builtin_amdgcn_readfirstlane(t_after);
+            if (kPad) {
+                t_s = t_s_next;
+                t_s_next = __builtin_amdgcn_readfirstlane(t_s_after);
+            }
         }
     }
 #undef TILE_AT
+#undef CLASSED_AT
 
 
     // ---- the next tile's first loads, in flight during this epilogue ------
@@ -555,7 +595,7 @@ __device__ __attribute__((always_inline)) inline void fetch_first_direct(const F
 
 // Plain launch: block g handles query tile g of [prefix tiles of every (b,h)]
 // followed by [video tiles of every (b,h)], starting at tile `first`.
-template <int D>
+template <int D, bool kPad>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 sparse_fwd_kernel(ForwardArgs a, int64_t first) {
     __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::LDS_FLOATS];
@@ -574,13 +614,13 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
     u32x4 qpre[Regs<D>::QPT];
     int lpre[kListPre];
     fetch_first_direct<D>(a, it, w, kf, vf, qpre, lpre);
-    run_tile<D>(a, lds, it, false, it, w, kf, vf, qpre, lpre);
+    run_tile<D, kPad>(a, lds, it, false, it, w, kf, vf, qpre, lpre);
 }
 
 // Grouped persistent launch over the video query tiles: block b belongs to
 // group b % 8; round r of group g covers video query tiles
 // [(r*8 + g)*S, (r*8 + g + 1)*S) of the flattened (b, h, tile) order.
-template <int D>
+template <int D, bool kPad>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
     __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::LDS_FLOATS];
@@ -617,7 +657,7 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
             }
             const bool has_next = item_of(r + 1) < n_items;
             const Item nx = has_next ? make(item_of(r + 1)) : cur;
-            run_tile<D>(a, lds, cur, has_next, nx, w, kf, vf, qpre, lpre);
+            run_tile<D, kPad>(a, lds, cur, has_next, nx, w, kf, vf, qpre, lpre);
             if (!has_next) break;
             cur = nx;
         }
@@ -630,17 +670,17 @@ __global__ void clear_progress_kernel(int* progress, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) progress[i] = 0;
 }
 
-template <int D>
+template <int D, bool kPad>
 hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) {
     const int64_t n_pref = (int64_t)a.BH * a.npt;
     const int64_t n_vid = (int64_t)a.BH * a.nvt;
     if (!progress) {
         if (n_pref + n_vid > 0)
-            hipLaunchKernelGGL(sparse_fwd_kernel<D>, dim3((unsigned)(n_pref + n_vid)), dim3(256), 0, s, a,
+            hipLaunchKernelGGL((sparse_fwd_kernel<D, kPad>), dim3((unsigned)(n_pref + n_vid)), dim3(256), 0, s, a,
                                (int64_t)0);
         return hipGetLastError();
     }
-    if (n_pref > 0) hipLaunchKernelGGL(sparse_fwd_kernel<D>, dim3((unsigned)n_pref), dim3(256), 0, s, a, (int64_t)0);
+    if (n_pref > 0) hipLaunchKernelGGL((sparse_fwd_kernel<D, kPad>), dim3((unsigned)n_pref), dim3(256), 0, s, a, (int64_t)0);
     if (n_vid == 0) return hipGetLastError();
     // persistent grid: the blocks that fit at once, a multiple of the group
     // count, at most kMaxGroupSize per group, and no more than the work
@@ -648,7 +688,7 @@ hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) 
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_fwd_grouped_kernel<D>, 256, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_fwd_grouped_kernel<D, kPad>, 256, 0);
     if (e != hipSuccess) return e;
     int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     grid = grid / kGroups * kGroups;
@@ -657,7 +697,7 @@ hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) 
     if (grid > need) grid = need;
     if (grid < kGroups) grid = kGroups;
     hipLaunchKernelGGL(clear_progress_kernel, dim3(1), dim3(512), 0, s, progress, kGroups * kMaxGroupSize);
-    hipLaunchKernelGGL(sparse_fwd_grouped_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, a, progress);
+    hipLaunchKernelGGL((sparse_fwd_grouped_kernel<D, kPad>), dim3((unsigned)grid), dim3(256), 0, s, a, progress);
     return hipGetLastError();
 }
 
@@ -667,7 +707,9 @@ size_t forward_workspace_bytes() { return (size_t)kGroups * kMaxGroupSize * size
 
 hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s) {
     if ((int64_t)a.BH * (a.npt + a.nvt) == 0) return hipSuccess;
-    return D == 128 ? launch_forward_d<128>(a, progress, s) : launch_forward_d<64>(a, progress, s);
+    if (a.pad.T != 0)
+        return D == 128 ? launch_forward_d<128, true>(a, progress, s) : launch_forward_d<64, true>(a, progress, s);
+    return D == 128 ? launch_forward_d<128, false>(a, progress, s) : launch_forward_d<64, false>(a, progress, s);
 }
 
 }  // namespace bsa

@@ -13,11 +13,13 @@ namespace {
 
 // Static tile order: tile id = raster index in the tile grid (t slowest),
 // tokens raster inside the tile ("Prism / Kandinsky 6 speed ablation" page,
-// section on Prism: the default 64-token tile is 4x4x4).
+// section on Prism: the default 64-token tile is 4x4x4).  The tile grid covers
+// T x Hg x W rounded up to whole tiles; a slot past the grid on some axis is
+// padding and gets -1.
 __global__ void perm_static_kernel(int T, int Hg, int W, int tt, int th, int tw, int64_t n_video, int B,
                                    int32_t* __restrict__ perm) {
     const int64_t total = n_video * B;
-    const int nbh = Hg / th, nbw = W / tw;
+    const int nbh = (Hg + th - 1) / th, nbw = (W + tw - 1) / tw;
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
          g += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = g % n_video;
@@ -29,25 +31,33 @@ __global__ void perm_static_kernel(int T, int Hg, int W, int tt, int th, int tw,
         const int x = r / (th * tw), y = (r / tw) % th, z = r % tw;
         const int64_t t = a * tt + x;
         const int h = bb * th + y, w = cc * tw + z;
-        perm[g] = (int32_t)((t * Hg + h) * W + w);
+        perm[g] = (t < T && h < Hg && w < W) ? (int32_t)((t * Hg + h) * W + w) : -1;
     }
+}
+
+// raster token of tiled slot p (prefix first), or -1 for a padding slot
+__device__ inline int64_t slot_token(const int32_t* __restrict__ perm, int b, int64_t n_video, int n_prefix,
+                                     int64_t p) {
+    if (p < n_prefix) return p;
+    const int32_t v = perm[(int64_t)b * n_video + (p - n_prefix)];
+    return v < 0 ? -1 : n_prefix + v;
 }
 
 // One block per (batch, 64-token tile of the tiled order); 256 threads.
 // Work item = (head, token in tile, 16-byte chunk), chunk fastest, so a wave
 // writes (gather) or reads (scatter) contiguous 256-byte head rows of the
 // tiled tensor and touches 256-byte head rows of the raster tensor.
+// n_tot: tiled rows (padding slots included); n_ras: raster rows.  Gather
+// writes zeros to padding slots, scatter skips them.
 template <bool kToRaster>
 __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                            const int32_t* __restrict__ perm, int H, int C,
-                                                           int n_prefix, int64_t n_video, int64_t n_tot) {
+                                                           int n_prefix, int64_t n_video, int64_t n_tot,
+                                                           int64_t n_ras) {
     __shared__ int64_t tok[kTile];
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x < kTile) {
-        const int64_t p = p0 + threadIdx.x;
-        tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
-    }
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
     __syncthreads();
     const int items = kTile * H * C;
 #pragma unroll 4
@@ -56,11 +66,13 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
         const int pl = (it / C) % kTile;
         const int h = it / (C * kTile);
         const int64_t tiled = (((int64_t)b * H + h) * n_tot + p0 + pl) * C + c;
-        const int64_t raster = (((int64_t)b * n_tot + tok[pl]) * H + h) * C + c;
-        if (kToRaster)
-            dst[raster] = src[tiled];
-        else
-            dst[tiled] = src[raster];
+        const int64_t t = tok[pl];
+        const int64_t raster = (((int64_t)b * n_ras + t) * H + h) * C + c;
+        if (kToRaster) {
+            if (t >= 0) dst[raster] = src[tiled];
+        } else {
+            dst[tiled] = t >= 0 ? src[raster] : make_uint4(0, 0, 0, 0);
+        }
     }
 }
 
@@ -75,16 +87,14 @@ __device__ inline int swap23(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m &
 
 __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
-                                                        int n_prefix, int64_t n_video, int64_t n_tot) {
+                                                        int n_prefix, int64_t n_video, int64_t n_tot,
+                                                        int64_t n_ras) {
     __shared__ int64_t tok[kTile];
     const int b = blockIdx.y;
     const int64_t tile = blockIdx.x;
     const int64_t p0 = tile * kTile;
     const int64_t n_tiles = n_tot / kTile;
-    if (threadIdx.x < kTile) {
-        const int64_t p = p0 + threadIdx.x;
-        tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
-    }
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
     __syncthreads();
     const int SD = C / 2;
     const int per_head = kTile * C;
@@ -95,7 +105,9 @@ __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict_
         const int lane = q & 63, s = (q >> 6) % SD, kh = (q >> 6) / SD;
         const int r = 32 * kh + swap23(lane & 31);
         const int cc = 2 * s + (lane >> 5);
-        dst[(((int64_t)b * H + h) * n_tiles + tile) * per_head + q] = src[(((int64_t)b * n_tot + tok[r]) * H + h) * C + cc];
+        const int64_t t = tok[r];
+        dst[(((int64_t)b * H + h) * n_tiles + tile) * per_head + q] =
+            t >= 0 ? src[(((int64_t)b * n_ras + t) * H + h) * C + cc] : make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -113,16 +125,14 @@ __device__ inline uint32_t word_of(const uint4& v, int w) { return w == 0 ? v.x 
 
 __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
-                                                        int n_prefix, int64_t n_video, int64_t n_tot) {
+                                                        int n_prefix, int64_t n_video, int64_t n_tot,
+                                                        int64_t n_ras) {
     __shared__ int64_t tok[kTile];
     const int b = blockIdx.y;
     const int64_t tile = blockIdx.x;
     const int64_t p0 = tile * kTile;
     const int64_t n_tiles = n_tot / kTile;
-    if (threadIdx.x < kTile) {
-        const int64_t p = p0 + threadIdx.x;
-        tok[threadIdx.x] = (p < n_prefix) ? p : n_prefix + perm[(int64_t)b * n_video + (p - n_prefix)];
-    }
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
     __syncthreads();
     const int OD = C / 4;  // 32-channel blocks
     const int items = H * 8 * C;
@@ -131,7 +141,10 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
         const int g = (it / C) % 8;
         const int h = it / (8 * C);
         uint4 r0, r1, r2, r3, r4, r5, r6, r7;
-        auto row = [&](int i) { return src[(((int64_t)b * n_tot + tok[8 * g + i]) * H + h) * C + dc]; };
+        auto row = [&](int i) {
+            const int64_t t = tok[8 * g + i];
+            return t >= 0 ? src[(((int64_t)b * n_ras + t) * H + h) * C + dc] : make_uint4(0, 0, 0, 0);
+        };
         r0 = row(0); r1 = row(1); r2 = row(2); r3 = row(3);
         r4 = row(4); r5 = row(5); r6 = row(6); r7 = row(7);
         // tokens 8 g .. 8 g + 7 = 32 kh + 16 c + 8 hf + e; channels 8 dc + e'
@@ -162,26 +175,28 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
 }  // namespace
 
 hipError_t launch_gather_kf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
-                            int n_prefix, int64_t n_video, hipStream_t s) {
+                            int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video) {
     const int64_t n_tot = n_prefix + n_video;
+    const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
     hipLaunchKernelGGL(gather_kf_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
-                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot);
+                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot, n_ras);
     return hipGetLastError();
 }
 
 hipError_t launch_gather_vf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
-                            int n_prefix, int64_t n_video, hipStream_t s) {
+                            int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video) {
     const int64_t n_tot = n_prefix + n_video;
+    const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
     hipLaunchKernelGGL(gather_vf_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
-                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot);
+                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot, n_ras);
     return hipGetLastError();
 }
 
 hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int tw, int32_t* perm,
                               hipStream_t s) {
-    const int64_t n_video = (int64_t)T * Hg * W;
+    const int64_t n_video = (int64_t)((T + tt - 1) / tt * tt) * ((Hg + th - 1) / th * th) * ((W + tw - 1) / tw * tw);
     const int64_t total = n_video * B;
     if (total == 0) return hipSuccess;
     const int threads = 256;
@@ -193,17 +208,18 @@ hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int t
 }
 
 hipError_t launch_permute_copy(bool to_raster, const uint16_t* src, uint16_t* dst, const int32_t* perm, int B,
-                               int H, int D, int n_prefix, int64_t n_video, hipStream_t s) {
+                               int H, int D, int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video) {
     const int64_t n_tot = n_prefix + n_video;
+    const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
     const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
     const int C = D / 8;
     if (to_raster)
         hipLaunchKernelGGL(permute_copy_kernel<true>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm,
-                           H, C, n_prefix, n_video, n_tot);
+                           H, C, n_prefix, n_video, n_tot, n_ras);
     else
         hipLaunchKernelGGL(permute_copy_kernel<false>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm,
-                           H, C, n_prefix, n_video, n_tot);
+                           H, C, n_prefix, n_video, n_tot, n_ras);
     return hipGetLastError();
 }
 

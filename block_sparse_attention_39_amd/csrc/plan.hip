@@ -44,24 +44,32 @@ __device__ inline void acc8(double (&acc)[8], const uint4& x) {
     acc[7] += (double)bf_hi(x.w);
 }
 
-__device__ inline void store_mean8(float* dst, const double (&acc)[8]) {
+// the exact sums divided by the tile's token count, rounded once to float
+__device__ inline void store_mean8(float* dst, const double (&acc)[8], double count) {
     float4 lo, hi;
-    lo.x = (float)(acc[0] * (1.0 / kTile));
-    lo.y = (float)(acc[1] * (1.0 / kTile));
-    lo.z = (float)(acc[2] * (1.0 / kTile));
-    lo.w = (float)(acc[3] * (1.0 / kTile));
-    hi.x = (float)(acc[4] * (1.0 / kTile));
-    hi.y = (float)(acc[5] * (1.0 / kTile));
-    hi.z = (float)(acc[6] * (1.0 / kTile));
-    hi.w = (float)(acc[7] * (1.0 / kTile));
+    lo.x = (float)(acc[0] / count);
+    lo.y = (float)(acc[1] / count);
+    lo.z = (float)(acc[2] / count);
+    lo.w = (float)(acc[3] / count);
+    hi.x = (float)(acc[4] / count);
+    hi.y = (float)(acc[5] / count);
+    hi.z = (float)(acc[6] / count);
+    hi.w = (float)(acc[7] / count);
     ((float4*)dst)[0] = lo;
     ((float4*)dst)[1] = hi;
+}
+
+// real tokens of video tile i (64 without padding)
+__device__ inline int tile_count(const PadGeo& g, int64_t i) {
+    if (g.T == 0) return kTile;
+    const int wi = (int)(i % g.Tw), hi = (int)((i / g.Tw) % g.Th), ti = (int)(i / ((int64_t)g.Tw * g.Th));
+    return min(g.tt, g.T - ti * g.tt) * min(g.th, g.Hg - hi * g.th) * min(g.tw, g.W - wi * g.tw);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                    float* __restrict__ qbar, float* __restrict__ kbar, int BH,
-                                                   int n_prefix, int nvt) {
+                                                   int n_prefix, int nvt, PadGeo pad) {
     constexpr int C = D / 8;         // 16-byte chunks per row
     constexpr int SD = D / 16;       // K-fragment steps
     constexpr int LPG = 64 / (2 * SD);  // lanes per channel group (K)
@@ -75,6 +83,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
     const int64_t bh = t / nvt, i = t % nvt;
     const int64_t n_tot = n_prefix + (int64_t)nvt * kTile;
     const uint4* src = (is_k ? k : q) + ((bh * n_tot + n_prefix + i * kTile) * C);
+    const double count = (double)tile_count(pad, i);  // padding tokens are zeros in the tiled tensors
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (!is_k) {
         constexpr int RPI = 64 / C;  // rows covered by one wave-wide load
@@ -85,7 +94,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
         for (int o = C; o < 64; o <<= 1)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
-        if (lane < C) store_mean8(qbar + t * D + 8 * lane, acc);
+        if (lane < C) store_mean8(qbar + t * D + 8 * lane, acc, count);
     } else {
         const int grp = lane / LPG, part = lane % LPG;
         const int s = grp >> 1, hf = grp & 1;
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
         for (int o = 1; o < LPG; o <<= 1)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
-        if (part == 0) store_mean8(kbar + t * D + 16 * s + 8 * hf, acc);
+        if (part == 0) store_mean8(kbar + t * D + 16 * s + 8 * hf, acc, count);
     }
 }
 
@@ -343,16 +352,16 @@ hipError_t launch_structured(const StructRule& sr, int BH, int H, int64_t* row_p
 }
 
 hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
-                       int n_prefix, int nvt, int D, hipStream_t s) {
+                       int n_prefix, int nvt, int D, hipStream_t s, const PadGeo& pad) {
     const int64_t tiles = 2LL * BH * nvt;
     if (tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((tiles + 3) / 4));
     if (D == 128)
         hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag,
-                           qbar, kbar, BH, n_prefix, nvt);
+                           qbar, kbar, BH, n_prefix, nvt, pad);
     else
         hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag,
-                           qbar, kbar, BH, n_prefix, nvt);
+                           qbar, kbar, BH, n_prefix, nvt, pad);
     return hipGetLastError();
 }
 

@@ -51,6 +51,20 @@
  *                                   (video tile numbers 0..nVT-1), ascending.
  * Ntot = n_prefix + Nvideo, Nvideo = grid_t*grid_h*grid_w, nVT = Nvideo/64.
  *
+ * Ragged grids (tile_mode BSA_TILE_STATIC_PADDED): the grid need not be a
+ * whole number of tiles on any axis.  The tile grid then covers it rounded up
+ * (ceil(T/tile_t) x ceil(H/tile_h) x ceil(W/tile_w) tiles); the slots of a
+ * boundary tile that fall outside the grid are padding.  The raster layout
+ * keeps the real token count (Nraster = grid_t*grid_h*grid_w); every tiled
+ * layout (tiled, kfrag, vfrag, perm, block_idx, lse, the pooled means) uses
+ * the padded count Nvideo = 64 * tiles, nVT = tiles.  perm holds -1 for a
+ * padding slot; gathers write zeros there and the scatter skips it.  A boundary
+ * tile's mean is taken over its real tokens only, and its padding keys get
+ * zero attention weight; padding query rows of the tiled output are not
+ * meaningful and are dropped by the scatter.  No page fixes these rules: they
+ * are the plain reading under which a ragged grid computes what the same
+ * grid would if its tiles could be cut to size.
+ *
  * Ownership and threading: the caller allocates every buffer (device memory),
  * including the workspace.  The library allocates nothing, frees nothing,
  * never synchronises and keeps no state: calls are reentrant.  All work is
@@ -83,7 +97,7 @@ typedef enum {
     BSA_ERR_ARG = -7          /* bad enum value or non-finite / non-positive scale */
 } bsa_status;
 
-enum { BSA_TILE_STATIC = 0, BSA_TILE_DYNAMIC = 1 };
+enum { BSA_TILE_STATIC = 0, BSA_TILE_DYNAMIC = 1, BSA_TILE_STATIC_PADDED = 2 };
 enum {
     BSA_PERM_BUILD = 0,
     BSA_PERM_GATHER = 1,
@@ -101,14 +115,14 @@ typedef struct bsa_desc {
     int32_t batch;      /* B >= 0 (0: every call is a no-op returning BSA_OK)         */
     int32_t heads;      /* H >= 0 (0: no-op)                                           */
     int32_t head_dim;   /* D, 64 or 128                                                */
-    int32_t grid_t;     /* video grid T x H x W, each >= 0; T*H*W a multiple of 64     */
+    int32_t grid_t;     /* video grid T x H x W, each >= 0 (see tile_mode)             */
     int32_t grid_h;
     int32_t grid_w;
     int32_t n_prefix;   /* dense prefix tokens, a multiple of 64, >= 0                 */
-    int32_t tile_mode;  /* BSA_TILE_STATIC or BSA_TILE_DYNAMIC                         */
+    int32_t tile_mode;  /* BSA_TILE_STATIC, BSA_TILE_DYNAMIC or BSA_TILE_STATIC_PADDED */
     int32_t tile_t;     /* static tile extents; product 64; must divide the grid       */
-    int32_t tile_h;     /*   (ignored in dynamic mode, where the grid must be a        */
-    int32_t tile_w;     /*    multiple of 8 on every axis)                             */
+    int32_t tile_h;     /*   (padded mode: any grid; ignored in dynamic mode, where    */
+    int32_t tile_w;     /*    the grid must be a multiple of 8 on every axis)          */
     int32_t keep_tiles; /* k: kept video key tiles per video query tile, 1..nVT        */
                         /*   (0 when there is no video)                                */
     float scale;        /* softmax scale applied to q.k, finite and > 0 (1/sqrt(D))    */
@@ -226,8 +240,9 @@ bsa_status bsa_forward_csr(const bsa_desc *desc, const void *q_tiled, const void
  * "Sparse VideoGen의 핵심 아이디어": attention heads are mostly spatial (a
  * query looks at patches of its own or nearby frames) or temporal (it follows
  * its spatial position across frames); section "실무에서 배울 최적화 기준": with
- * tokens permuted into tiles such masks select whole tiles.  Static tile mode
- * only (BSA_ERR_UNSUPPORTED in dynamic mode).  In the tile grid (Tt x Th x Tw
+ * tokens permuted into tiles such masks select whole tiles.  Static tile modes
+ * only (BSA_ERR_UNSUPPORTED in dynamic mode; a ragged grid uses its rounded-up
+ * tile grid).  In the tile grid (Tt x Th x Tw
  * tiles, video tile (t, h, w) numbered (t*Th + h)*Tw + w), video query tile
  * (ti, hi, wi) of a head keeps
  *   BSA_MASK_SPATIAL:  every tile (t, h, w) with |t - ti| <= radius_t;
@@ -276,7 +291,8 @@ bsa_status bsa_backward_workspace_size(const bsa_desc *desc, size_t *bytes);
  * bf16 before their products, the gradients to bf16 at the end.  Tensors must
  * be 16-byte aligned (lse, perm, block_idx 4-byte); at most BSA_MAX_TILES
  * tiles and BSA_MAX_VIDEO_TILES video tiles per (batch, head).  Calls given the
- * same workspace must not run concurrently.
+ * same workspace must not run concurrently.  A ragged grid
+ * (BSA_TILE_STATIC_PADDED with padding) returns BSA_ERR_UNSUPPORTED.
  */
 bsa_status bsa_backward(const bsa_desc *desc, const void *q, const void *k, const void *v,
                         const void *o, const void *d_o, const float *lse, const int32_t *perm,
@@ -289,7 +305,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 700
+#define BSA_VERSION 800
 
 #ifdef __cplusplus
 }

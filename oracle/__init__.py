@@ -76,6 +76,16 @@ def lib() -> ctypes.CDLL:
         L.orc_attention_backward_dq.restype = None
         L.orc_attention_backward_dkdv.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, f64, P, i32, P, P]
         L.orc_attention_backward_dkdv.restype = None
+        L.orc_perm_static_padded.argtypes = [i32, i32, i32, i32, i32, i32, P]
+        L.orc_perm_static_padded.restype = i32
+        L.orc_gather_padded.argtypes = [P, P, i32, i32, i64, i64, i32, i32, P]
+        L.orc_gather_padded.restype = None
+        L.orc_scatter_padded.argtypes = [P, P, i32, i32, i64, i64, i32, i32, P]
+        L.orc_scatter_padded.restype = None
+        L.orc_pool_padded.argtypes = [P, P, i32, i32, i32, i32, i32, P]
+        L.orc_pool_padded.restype = None
+        L.orc_attention_padded.argtypes = [P, P, P, i32, i32, i32, P, P, P, f64, P, i32, P, P]
+        L.orc_attention_padded.restype = None
         _lib = L
     return _lib
 
@@ -415,3 +425,89 @@ def backward_full(q_tiled, k_tiled, v_tiled, do_tiled, n_prefix: int, idx, scale
             dk[b, h] = gk.reshape(Ntot, D)
             dv[b, h] = gv.reshape(Ntot, D)
     return dq, dk, dv
+
+
+# ---- ragged grids: static tiles over the grid rounded up to whole tiles ------
+
+def padded_slots(grid, tile=(4, 4, 4)) -> int:
+    """Video slots of the tiled order: every axis rounded up to whole tiles."""
+    return int(np.prod([-(-g // t) * t for g, t in zip(grid, tile)]))
+
+
+def perm_static_padded(grid, tile=(4, 4, 4)) -> np.ndarray:
+    """Tiled video slot -> raster video index, -1 for a padding slot,
+    ``int32 [padded_slots]``."""
+    T, Hg, W = grid
+    out = np.empty(padded_slots(grid, tile), np.int32)
+    if lib().orc_perm_static_padded(T, Hg, W, *tile, _ptr(out)) != 0:
+        raise ValueError("tile is not 64 tokens")
+    return out
+
+
+def gather_padded(x_raster: np.ndarray, perm: np.ndarray, n_prefix: int) -> np.ndarray:
+    """Raster ``[B, n_prefix + Nras, H, D]`` -> tiled ``[B, H, n_prefix + Nslots, D]``
+    (``Nslots`` = perm's length; zeros in padding slots)."""
+    x = _c(x_raster, np.uint16)
+    B, Nr, H, D = x.shape
+    Ns = perm.shape[-1]
+    p = _perm_b(perm, B, Ns)
+    out = np.empty((B, H, n_prefix + Ns, D), np.uint16)
+    lib().orc_gather_padded(_ptr(x), _ptr(p), B, n_prefix, Nr - n_prefix, Ns, H, D, _ptr(out))
+    return out
+
+
+def scatter_padded(x_tiled: np.ndarray, perm: np.ndarray, n_prefix: int, n_raster_video: int) -> np.ndarray:
+    """Tiled ``[B, H, n_prefix + Nslots, D]`` -> raster ``[B, n_prefix + n_raster_video, H, D]``
+    (padding slots dropped)."""
+    x = _c(x_tiled, np.uint16)
+    B, H, Nt, D = x.shape
+    Ns = Nt - n_prefix
+    p = _perm_b(perm, B, Ns)
+    out = np.zeros((B, n_prefix + n_raster_video, H, D), np.uint16)
+    lib().orc_scatter_padded(_ptr(x), _ptr(p), B, n_prefix, n_raster_video, Ns, H, D, _ptr(out))
+    return out
+
+
+def pool_padded(x_tiled: np.ndarray, perm: np.ndarray, n_prefix: int) -> np.ndarray:
+    """Per video tile mean over its real tokens, ``float32 [B, H, nvt, D]``."""
+    x = _c(x_tiled, np.uint16)
+    B, H, Ntot, D = x.shape
+    nvt = (Ntot - n_prefix) // TILE
+    p = _perm_b(perm, B, nvt * TILE)
+    out = np.empty((B, H, nvt, D), np.float32)
+    lib().orc_pool_padded(_ptr(x), _ptr(p), B, H, n_prefix, nvt, D, _ptr(out))
+    return out
+
+
+def key_real(perm_b: np.ndarray, n_prefix: int) -> np.ndarray:
+    """uint8 [n_prefix + Nslots]: 1 for a real token of the tiled order
+    (prefix and perm >= 0), 0 for a padding slot."""
+    return np.concatenate([np.ones(n_prefix, np.uint8), (np.asarray(perm_b) >= 0).astype(np.uint8)])
+
+
+def attention_padded_csr(q_bh, k_bh, v_bh, n_prefix: int, row_ptr_bh, col, real, scale: float, qtiles):
+    """As ``attention_csr``, with only the real keys (``real`` from ``key_real``)."""
+    q = _c(q_bh, np.uint16)
+    kx = _c(k_bh, np.uint16)
+    v = _c(v_bh, np.uint16)
+    Ntot, D = q.shape
+    nvt = (Ntot - n_prefix) // TILE
+    rp = _c(row_ptr_bh, np.int64)
+    cl = _c(col, np.int32) if len(col) else np.zeros(1, np.int32)
+    kr = _c(real, np.uint8)
+    assert kr.shape == (Ntot,)
+    qt = _c(qtiles, np.int32)
+    nq = qt.shape[0]
+    out = np.empty((nq, TILE, D), np.float64)
+    lse = np.empty((nq, TILE), np.float64)
+    lib().orc_attention_padded(_ptr(q), _ptr(kx), _ptr(v), n_prefix, nvt, D, _ptr(rp), _ptr(cl), _ptr(kr),
+                               float(scale), _ptr(qt), nq, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def attention_padded(q_bh, k_bh, v_bh, n_prefix: int, idx_bh, real, scale: float, qtiles):
+    """As ``attention`` (fixed keep, ``idx_bh [nvt, k]``), with only the real keys."""
+    ix = _c(idx_bh, np.int32)
+    nvt, k = ix.shape
+    row_ptr = np.arange(nvt + 1, dtype=np.int64) * k
+    return attention_padded_csr(q_bh, k_bh, v_bh, n_prefix, row_ptr, ix.reshape(-1), real, scale, qtiles)

@@ -794,3 +794,183 @@ void orc_attention_backward_dkdv(const uint16_t *q, const uint16_t *kx, const ui
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Ragged grids: static tiles over a grid rounded up to whole tiles           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [SVG, section "이론적 sparsity와 물리적 sparsity의 차이"]: against a tile grid
+ * a tile is full, partly covered (a boundary tile, which needs an element
+ * mask) or empty.  [Prism, section "토큰 수의 제곱으로 느는 어텐션 비용"]: the
+ * 32 x 48 x 80 grid of the 720p clip counts padding tokens.  Reading: a grid
+ * that is not a whole number of tiles is covered by the tile grid rounded up
+ * on every axis; the slots of a boundary tile that fall outside the grid are
+ * padding.  Tile order and token order inside a tile are those of
+ * orc_perm_static; perm[p] = -1 marks a padding slot.  The padded slot count
+ * is ceil(T/tt)*tt * ceil(Hg/th)*th * ceil(W/tw)*tw.
+ * Returns 0, or -1 if the tile is not 64 tokens.
+ */
+int orc_perm_static_padded(int T, int Hg, int W, int tt, int th, int tw, int32_t *perm)
+{
+    if (tt < 1 || th < 1 || tw < 1 || tt * th * tw != TILE)
+        return -1;
+    const int Tt = (T + tt - 1) / tt, Th = (Hg + th - 1) / th, Tw = (W + tw - 1) / tw;
+    int64_t p = 0;
+    for (int a = 0; a < Tt; ++a)
+        for (int b = 0; b < Th; ++b)
+            for (int c = 0; c < Tw; ++c)
+                for (int x = 0; x < tt; ++x)
+                    for (int y = 0; y < th; ++y)
+                        for (int z = 0; z < tw; ++z) {
+                            int t = a * tt + x, h = b * th + y, w = c * tw + z;
+                            if (t < T && h < Hg && w < W)
+                                perm[p++] = (int32_t)(((int64_t)t * Hg + h) * W + w);
+                            else
+                                perm[p++] = -1;
+                        }
+    return 0;
+}
+
+/*
+ * Gather and scatter over a padded permutation: the raster tensor has
+ * n_prefix + Nras tokens, the tiled one n_prefix + Nslots.  A padding slot is
+ * gathered as zeros and not scattered.  perm: [B][Nslots].
+ */
+void orc_gather_padded(const uint16_t *src_raster, const int32_t *perm, int B, int n_prefix, int64_t Nras,
+                       int64_t Nslots, int H, int D, uint16_t *dst_tiled)
+{
+    const int64_t Nr = n_prefix + Nras, Nt = n_prefix + Nslots;
+#pragma omp parallel for collapse(2)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t p = 0; p < Nt; ++p) {
+                uint16_t *d = dst_tiled + (((int64_t)b * H + h) * Nt + p) * D;
+                const int64_t v = (p < n_prefix) ? p : perm[(int64_t)b * Nslots + (p - n_prefix)];
+                if (p >= n_prefix && v < 0) {
+                    memset(d, 0, (size_t)D * sizeof(uint16_t));
+                    continue;
+                }
+                const int64_t tok = (p < n_prefix) ? p : n_prefix + v;
+                memcpy(d, src_raster + (((int64_t)b * Nr + tok) * H + h) * D, (size_t)D * sizeof(uint16_t));
+            }
+}
+
+void orc_scatter_padded(const uint16_t *src_tiled, const int32_t *perm, int B, int n_prefix, int64_t Nras,
+                        int64_t Nslots, int H, int D, uint16_t *dst_raster)
+{
+    const int64_t Nr = n_prefix + Nras, Nt = n_prefix + Nslots;
+#pragma omp parallel for collapse(2)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t p = 0; p < Nt; ++p) {
+                const int64_t v = (p < n_prefix) ? p : perm[(int64_t)b * Nslots + (p - n_prefix)];
+                if (p >= n_prefix && v < 0)
+                    continue;
+                const int64_t tok = (p < n_prefix) ? p : n_prefix + v;
+                memcpy(dst_raster + (((int64_t)b * Nr + tok) * H + h) * D,
+                       src_tiled + (((int64_t)b * H + h) * Nt + p) * D, (size_t)D * sizeof(uint16_t));
+            }
+}
+
+/*
+ * Tile means over a padded permutation [Prism: a block is judged by the mean
+ * of its tokens]: the mean of a boundary tile is taken over its real tokens
+ * (perm >= 0) only -- the reading under which padding changes no score.
+ * Summed in double, divided by the count, rounded once to float.
+ * x_tiled: [B][H][n_prefix + nvt*64][D]; perm: [B][nvt*64]; out: [B][H][nvt][D].
+ */
+void orc_pool_padded(const uint16_t *x_tiled, const int32_t *perm, int B, int H, int n_prefix, int nvt, int D,
+                     float *out)
+{
+    const int64_t Nslots = (int64_t)nvt * TILE, Ntot = n_prefix + Nslots;
+#pragma omp parallel for collapse(2)
+    for (int bh = 0; bh < B * H; ++bh)
+        for (int i = 0; i < nvt; ++i) {
+            const int32_t *pt = perm + (int64_t)(bh / H) * Nslots + (int64_t)i * TILE;
+            for (int d = 0; d < D; ++d) {
+                double s = 0.0;
+                int count = 0;
+                for (int r = 0; r < TILE; ++r) {
+                    if (pt[r] < 0)
+                        continue;
+                    s += bf16_to_double(x_tiled[((int64_t)bh * Ntot + n_prefix + (int64_t)i * TILE + r) * D + d]);
+                    ++count;
+                }
+                out[((int64_t)bh * nvt + i) * D + d] = (float)(s / count);
+            }
+        }
+}
+
+/*
+ * Attention on a ragged grid: as orc_attention_csr, with the keys limited to
+ * the real tokens (key_real[j] != 0) -- the element mask of a boundary tile
+ * [SVG, section "이론적 sparsity와 물리적 sparsity의 차이"].  Every query row
+ * (padding rows included) gets an output; the caller keeps the real ones.
+ * key_real: [n_prefix + nvt*64] of one batch element's tiled order.
+ */
+void orc_attention_padded(const uint16_t *q, const uint16_t *kx, const uint16_t *v, int n_prefix, int nvt, int D,
+                          const int64_t *row_ptr, const int32_t *col, const uint8_t *key_real, double scale,
+                          const int32_t *qtiles, int nq, double *out, double *lse)
+{
+    const int npt = n_prefix / TILE;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nq; ++a) {
+        const int qt = qtiles[a];
+        int64_t c = 0;
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(Ntot > 0 ? Ntot : 1));
+        if (qt < npt) {
+            for (int64_t j = 0; j < Ntot; ++j)
+                if (key_real[j])
+                    keys[c++] = j;
+        } else {
+            const int i = qt - npt;
+            for (int64_t j = 0; j < n_prefix; ++j)
+                keys[c++] = j;
+            for (int64_t t = row_ptr[i]; t < row_ptr[i + 1]; ++t) {
+                const int64_t base = n_prefix + (int64_t)col[t] * TILE;
+                for (int r = 0; r < TILE; ++r)
+                    if (key_real[base + r])
+                        keys[c++] = base + r;
+            }
+        }
+        const int64_t nkeys = c;
+        double *z = (double *)malloc(sizeof(double) * (size_t)(nkeys > 0 ? nkeys : 1));
+        double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            for (int d = 0; d < D; ++d)
+                qd[d] = bf16_to_double(q[qi * D + d]);
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const uint16_t *kr = kx + keys[j] * D;
+                double s = 0.0;
+                for (int d = 0; d < D; ++d)
+                    s += qd[d] * bf16_to_double(kr[d]);
+                z[j] = s * scale;
+                if (z[j] > mx)
+                    mx = z[j];
+            }
+            double den = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc[d] = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const double w = exp(z[j] - mx);
+                den += w;
+                const uint16_t *vr = v + keys[j] * D;
+                for (int d = 0; d < D; ++d)
+                    acc[d] += w * bf16_to_double(vr[d]);
+            }
+            for (int d = 0; d < D; ++d)
+                out[((int64_t)a * TILE + r) * D + d] = acc[d] / den;
+            if (lse)
+                lse[(int64_t)a * TILE + r] = mx + log(den);
+        }
+        free(z);
+        free(qd);
+        free(acc);
+        free(keys);
+    }
+}

@@ -48,19 +48,34 @@ class Workload:
     tau: float = 0.10
     field_amp: float = 2.0
     field_period: float = 4.0
+    padded: bool = False   # ragged grid: static tiles over the grid rounded up
 
     @property
     def n_video(self) -> int:
+        """Video tokens of the raster tensors (the real grid)."""
         T, H, W = self.grid
         return T * H * W
 
     @property
     def n_tokens(self) -> int:
+        """Tokens of the raster tensors."""
         return self.n_prefix + self.n_video
 
     @property
+    def n_video_slots(self) -> int:
+        """Video tokens of the tiled order: the grid, or with ``padded`` the
+        grid rounded up to whole tiles on every axis."""
+        if not self.padded:
+            return self.n_video
+        return int(np.prod([-(-g // t) * t for g, t in zip(self.grid, self.tile)]))
+
+    @property
+    def n_tiled_tokens(self) -> int:
+        return self.n_prefix + self.n_video_slots
+
+    @property
     def n_video_tiles(self) -> int:
-        return self.n_video // 64
+        return self.n_video_slots // 64
 
     @property
     def n_prefix_tiles(self) -> int:
@@ -75,11 +90,12 @@ class Workload:
 
     def effective_flops(self) -> float:
         """4 * B * H * D * sum over query tokens of the keys it attends to
-        (two matrix products over the kept tiles and the prefix only)."""
-        npt, nvt = self.n_prefix_tiles, self.n_video_tiles
-        keys_prefix_q = self.n_tokens                           # prefix queries: dense
+        (two matrix products over the kept tiles and the prefix only).  On a
+        ragged grid every tile counts whole (padding slots included), as the
+        kernels compute them."""
+        keys_prefix_q = self.n_tiled_tokens                     # prefix queries: dense
         keys_video_q = self.n_prefix + self.keep_tiles * 64     # video queries
-        pairs = self.n_prefix * keys_prefix_q + self.n_video * keys_video_q
+        pairs = self.n_prefix * keys_prefix_q + self.n_video_slots * keys_video_q
         return 4.0 * self.batch * self.heads * self.head_dim * pairs
 
 
@@ -96,6 +112,9 @@ WORKLOADS = {
     "prism720p_dynamic": Workload("prism720p_dynamic", 2, 24, 128, (32, 48, 80), 480, seed=3,
                                   dynamic=True, recipe="field"),
     "prefix": Workload("prefix", 1, 24, 128, (24, 48, 84), 378, seed=4, n_prefix=2048),
+    # 121 frames of 720p through a 4x temporal / 16x spatial latent: 31 x 45 x 80
+    # tokens, padded to the 32 x 48 x 80 tile grid (1,920 tiles)
+    "prism720p_ragged": Workload("prism720p_ragged", 2, 24, 128, (31, 45, 80), 480, seed=5, padded=True),
 }
 KEEP_SWEEP = (480, 192, 120, 96)   # 25 %, 10 %, 6.25 %, 5 % of 1,920 tiles
 

@@ -46,7 +46,7 @@ def bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 def desc_for(wl: S.Workload):
     return bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
-                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
 
 
 class GpuRun:
@@ -70,7 +70,7 @@ class GpuRun:
         return self
 
     def perm(self):
-        return self.att.perm.cpu().numpy()[:, :self.wl.n_video]
+        return self.att.perm.cpu().numpy()[:, :self.wl.n_video_slots]
 
     def shape_map(self):
         return None if self.att.shape_map is None else self.att.shape_map.cpu().numpy()

@@ -195,3 +195,34 @@ def test_desc_layout_matches_header():
     assert names == [n for n, _ in Desc._fields_]
     assert ctypes.sizeof(Desc) == 4 * len(names)
     assert np.dtype(np.int32).itemsize == 4
+
+
+def test_padded_mode_host_checks():
+    """Ragged grids (BSA_TILE_STATIC_PADDED): the mode constant matches the
+    header; the workspace is sized on the padded tile count; the tile must
+    still be 64 tokens; the backward refuses a ragged grid; structured lists
+    count on the rounded-up tile grid."""
+    m = re.search(r"BSA_TILE_STATIC_PADDED = (\d+)", HEADER)
+    assert m and int(m.group(1)) == bsa.TILE_STATIC_PADDED
+    L = lib()
+    d = bsa.make_desc(2, 24, 128, (31, 45, 80), 480, padded=True)   # 32 x 48 x 80 tiles after padding
+    assert bsa.video_slots(d) == 32 * 48 * 80
+    assert ws_size(d) == ws_size(bsa.make_desc(2, 24, 128, (32, 48, 80), 480))
+    # the same grid in the plain static mode is not a whole number of tiles
+    assert ws_size(bsa.make_desc(2, 24, 128, (31, 45, 80), 480))[0] == SHAPE
+    assert ws_size(bsa.make_desc(1, 1, 64, (5, 6, 7), 3, padded=True, tile=(4, 4, 2)))[0] == SHAPE
+    assert ws_size(bsa.make_desc(1, 1, 64, (5, 6, 7), 9, padded=True))[0] == SHAPE   # 8 tiles
+    n = ctypes.c_size_t(0)
+    assert L.bsa_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert L.bsa_backward(ctypes.byref(d), *([None] * 11), None, 0, None) == UNSUP
+    # padded mode on a grid that divides: the plain static problem
+    dp = bsa.make_desc(1, 2, 64, (8, 8, 12), 5, padded=True)
+    assert bsa.video_slots(dp) == 768 and ws_size(dp) == ws_size(bsa.make_desc(1, 2, 64, (8, 8, 12), 5))
+    # structured lists over the 2 x 2 x 2 tile grid of a 5 x 6 x 7 grid
+    import oracle
+    ds = bsa.make_desc(1, 2, 64, (5, 6, 7), 3, padded=True)
+    mask = (ctypes.c_int32 * 2)(bsa.MASK_SPATIAL, bsa.MASK_TEMPORAL)
+    e = ctypes.c_int64(0)
+    assert L.bsa_structured_entries(ctypes.byref(ds), mask, 0, 0, ctypes.byref(e)) == OK
+    rp, _ = oracle.plan_structured((2, 2, 2), [0, 1], 0, 0, 1)
+    assert e.value == rp[-1]

@@ -200,7 +200,7 @@ def bench_varkeep(args, wl, q, k, v):
     dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, max(keep_h), scale=wl.scale,
-                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
     att = bsa.BlockSparseAttention(desc)
     out = torch.empty_like(qd)
     rows = wl.batch * wl.heads * wl.n_video_tiles
@@ -279,7 +279,7 @@ def bench_structured(args, wl, q, k, v):
     dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
-                         n_prefix=wl.n_prefix, tile=wl.tile)
+                         n_prefix=wl.n_prefix, tile=wl.tile, padded=wl.padded)
     att = bsa.BlockSparseAttention(desc)
     out = torch.empty_like(qd)
     rows = wl.batch * wl.heads * wl.n_video_tiles
@@ -360,24 +360,40 @@ def cpu_baseline_backward(wl, q, k, v, do, n_tiles: int):
     b, h = 0, 0
     sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    perm = oracle.perm_static(wl.grid, wl.tile)[None]
-    qt, kt, vt, dt = (oracle.gather(sl(x), perm, wl.n_prefix)[0, 0] for x in (q, k, v, do))
+    if wl.padded:
+        perm = oracle.perm_static_padded(wl.grid, wl.tile)[None]
+        qt, kt, vt, dt = (oracle.gather_padded(sl(x), perm, wl.n_prefix)[0, 0] for x in (q, k, v, do))
+        real = oracle.key_real(perm[0], wl.n_prefix)
+    else:
+        perm = oracle.perm_static(wl.grid, wl.tile)[None]
+        qt, kt, vt, dt = (oracle.gather(sl(x), perm, wl.n_prefix)[0, 0] for x in (q, k, v, do))
     t0 = time.perf_counter()
-    qp, kp = oracle.pool(qt[None, None], wl.n_prefix), oracle.pool(kt[None, None], wl.n_prefix)
+    if wl.padded:
+        qp = oracle.pool_padded(qt[None, None], perm, wl.n_prefix)
+        kp = oracle.pool_padded(kt[None, None], perm, wl.n_prefix)
+    else:
+        qp, kp = oracle.pool(qt[None, None], wl.n_prefix), oracle.pool(kt[None, None], wl.n_prefix)
     idx, *_ = oracle.topk(qp, kp, wl.keep_tiles)
     t_plan = time.perf_counter() - t0
-    nqt = wl.n_tokens // 64
+    nqt = wl.n_tiled_tokens // 64
     rng = np.random.default_rng(4321)
     tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
     scale = float(np.float32(wl.scale))
+    lse = np.zeros(wl.n_tiled_tokens)
+    delta = np.zeros(wl.n_tiled_tokens)
     t0 = time.perf_counter()
-    o, lse_s = oracle.attention(qt, kt, vt, wl.n_prefix, idx[0, 0], scale, tiles)
-    lse = np.zeros(wl.n_tokens)
-    delta = np.zeros(wl.n_tokens)
-    oracle.backward_dq(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], scale, tiles)
+    if wl.padded:
+        oracle.attention_padded(qt, kt, vt, wl.n_prefix, idx[0, 0], real, scale, tiles)
+        oracle.backward_dq_padded(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], real, scale, tiles)
+    else:
+        oracle.attention(qt, kt, vt, wl.n_prefix, idx[0, 0], scale, tiles)
+        oracle.backward_dq(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], scale, tiles)
     t_q = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.backward_dkdv(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], scale, tiles)
+    if wl.padded:
+        oracle.backward_dkdv_padded(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], real, scale, tiles)
+    else:
+        oracle.backward_dkdv(qt, kt, vt, dt, lse, delta, wl.n_prefix, idx[0, 0], scale, tiles)
     t_k = time.perf_counter() - t0
     head_seconds = t_plan + (t_q + t_k) * nqt / len(tiles)
     head_flops = 2.5 * wl.effective_flops() / (wl.batch * wl.heads)
@@ -403,7 +419,7 @@ def bench_backward(args, wl, q, k, v):
     dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
-                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau)
+                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
     att = bsa.BlockSparseAttention(desc, with_lse=True)
     out = att(qd, kd, vd)
     dq, dk, dv = (torch.empty_like(qd) for _ in range(3))

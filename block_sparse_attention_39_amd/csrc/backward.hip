@@ -67,15 +67,17 @@ struct BCfg {
 // token index l % 32 of a kfrag row (bits 2 and 3 exchanged)
 __device__ inline int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// raster token of tiled row `row` of batch b
+// raster token of tiled row `row` of batch b, or -1 for a padding slot
 __device__ inline int64_t raster_token(const BackwardArgs& a, int b, int64_t row) {
-    return row < a.npf ? row : a.npf + a.perm[(int64_t)b * (a.n_tot - a.npf) + (row - a.npf)];
+    if (row < a.npf) return row;
+    const int32_t v = a.perm[(int64_t)b * (a.n_tot - a.npf) + (row - a.npf)];
+    return v < 0 ? -1 : a.npf + v;
 }
 
 // one (batch, head) row of D bf16 channels, raster layout
 __device__ inline uint16_t* raster_row(uint16_t* base, const BackwardArgs& a, int64_t bh, int64_t tok, int D) {
-    const int64_t b = bh / a.H, h = bh % a.H;
-    return base + ((b * a.n_tot + tok) * a.H + h) * D;
+    const int b = (int)bh / a.H, h = (int)bh % a.H;  // bh < B*H <= INT32_MAX
+    return base + (((int64_t)b * a.n_ras + tok) * a.H + h) * D;
 }
 
 // ---- Delta = dO . O and lse in base 2, per tiled row ----------------------
@@ -88,14 +90,16 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
     const int64_t bh = r / a.n_tot, row = r % a.n_tot;
     const int b = (int)(bh / a.H);
     const int64_t tok = raster_token(a, b, row);
-    const uint16_t* o = raster_row(const_cast<uint16_t*>(a.o), a, bh, tok, D);
-    const uint16_t* g = raster_row(const_cast<uint16_t*>(a.dout), a, bh, tok, D);
-    float s = 0.f;
+    float s = 0.f;  // a padding row has dO = 0
+    if (tok >= 0) {
+        const uint16_t* o = raster_row(const_cast<uint16_t*>(a.o), a, bh, tok, D);
+        const uint16_t* g = raster_row(const_cast<uint16_t*>(a.dout), a, bh, tok, D);
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const bf16x8 x = *(const bf16x8*)(o + 8 * c), y = *(const bf16x8*)(g + 8 * c);
+        for (int c = 0; c < D / 8; ++c) {
+            const bf16x8 x = *(const bf16x8*)(o + 8 * c), y = *(const bf16x8*)(g + 8 * c);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
+            for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
+        }
     }
     a.delta[r] = s;
     a.lse2[r] = a.lse[r] * kLog2e;
@@ -255,7 +259,7 @@ __device__ __attribute__((always_inline)) inline void merge_store(float* lds, co
             pk[2 + e] = __builtin_bit_cast(uint32_t, hi);
         }
         const int64_t tok = raster_token(a, b, (int64_t)tile * kTile + r);
-        *(u32x4*)(raster_row(out, a, bh, tok, D) + 8 * c) = pk;
+        if (tok >= 0) *(u32x4*)(raster_row(out, a, bh, tok, D) + 8 * c) = pk;
     }
 }
 
@@ -270,8 +274,10 @@ __device__ __attribute__((always_inline)) inline void merge_store(float* lds, co
 // A half's dS^T never shares a window with the products that overwrite its
 // scores or read it, so it needs one buffer.  Its pairs of elements go
 // through three stages in consecutive slots: P = exp2(S c - lse), then
-// P (dP - Delta), then the bf16 cast.
-template <int D>
+// P (dP - Delta), then the bf16 cast.  kPad: a ragged grid; the padding keys
+// of boundary key tiles get -inf logits, so their dS is exactly 0 (their K
+// rows are zero, and 0 * inf must not arise).
+template <int D, bool kPad>
 __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs& a, float* lds, int64_t bh, int qt,
                                                               const WaveId& w) {
     using CF = BCfg<D>;
@@ -286,11 +292,14 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
     // ---- stage: the key-tile list and the stationary Q^T, dO^T ---------------
     __syncthreads();  // the previous tile's epilogue is done with LDS
     if (dense) {
-        for (int j = w.tid; j < n_iter; j += 256) list[j] = j;
+        for (int j = w.tid; j < n_iter; j += 256) list[j] = j | (kPad && j >= a.npt ? pad_class(a.pad, j - a.npt) : 0);
     } else {
         const int32_t* row = a.idx + (bh * a.nvt + (qt - a.npt)) * (int64_t)a.keep;
         for (int j = w.tid; j < a.npt; j += 256) list[j] = j;
-        for (int e = w.tid; e < a.keep; e += 256) list[a.npt + e] = a.npt + min(max(row[e], 0), a.nvt - 1);
+        for (int e = w.tid; e < a.keep; e += 256) {
+            const int vt = min(max(row[e], 0), a.nvt - 1);
+            list[a.npt + e] = (a.npt + vt) | (kPad ? pad_class(a.pad, vt) : 0);
+        }
     }
     {
         const uint8_t* qsrc = (const uint8_t*)a.q_kf + (bh * n_tiles + qt) * (int64_t)TB;
@@ -318,7 +327,8 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
     const uint8_t* kkb = (const uint8_t*)a.k_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
     const uint8_t* vkb = (const uint8_t*)a.v_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
     const uint8_t* kvb = (const uint8_t*)a.k_vf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
-#define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)])
+#define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)] & (kPad ? kTileBits : -1))
+#define CLASSED_AT(n_) (kPad ? __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)]) : 0)
 
     f32x16 acc[OD][2];
 #pragma unroll
@@ -349,6 +359,8 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
     }
     int t_v = TILE_AT(1);       // tile whose K^T fragments are loaded next
     int t_k_next = TILE_AT(2);  // tile whose K, V fragments are loaded next
+    int t_s = CLASSED_AT(0);    // ragged grid: slice n's list entry, with its boundary class
+    int t_s_next = CLASSED_AT(1);
 
     constexpr int NS = 2 * SD;         // S and dP slots of a window
     constexpr int W = NS + 2 * OD;     // slots of a window
@@ -364,7 +376,8 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
         for (int B = 0; B < 2; ++B) {
             const int n = n0 + B;
             const int t_k = t_k_next;
-            const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)];
+            const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)] & (kPad ? kTileBits : -1);
+            const int t_s_after = kPad ? list[min(par + 2 * (n + 2), n_iter - 1)] : 0;
             const uint8_t* const kaddr = kkb + (int64_t)t_k * TB;
             const uint8_t* const vaddr = vkb + (int64_t)t_k * TB;
             const uint8_t* const kvaddr = kvb + (int64_t)t_v * TB;
@@ -376,6 +389,8 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
                 // h = 1: S, dP of half 0 (slice n+1), dQ of half 0 (slice n)
                 const int sq = 1 - h, pq = 1 - h;
                 const float neg = vmask - lse2[h];
+                // a slice of a boundary tile: its padding keys out
+                if (kPad && (t_s >> 16)) mask_padding_keys(a.pad.real[t_s >> 16], w.kh, w.hf, sacc[h]);
                 float xe[8][2];
 #pragma unroll
                 for (int g = 0; g < W; ++g) {
@@ -435,9 +450,14 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
             }
             t_v = t_k;
             t_k_next = __builtin_amdgcn_readfirstlane(t_after);
+            if (kPad) {
+                t_s = t_s_next;
+                t_s_next = __builtin_amdgcn_readfirstlane(t_s_after);
+            }
         }
     }
 #undef TILE_AT
+#undef CLASSED_AT
     merge_store<D>(lds, acc, true, w, a.scale, a, bh, qt, a.dq);
 }
 
@@ -616,7 +636,7 @@ __device__ __attribute__((always_inline)) inline void merge_partials(float* lds,
             pk[2 + e] = __builtin_bit_cast(uint32_t, hi);
         }
         const int64_t tk = raster_token(a, b, (int64_t)tile * kTile + r);
-        *(u32x4*)(raster_row(out, a, bh, tk, D) + 8 * c) = pk;
+        if (tk >= 0) *(u32x4*)(raster_row(out, a, bh, tk, D) + 8 * c) = pk;
     }
 }
 
@@ -859,12 +879,12 @@ __device__ __attribute__((always_inline)) inline void grouped_rounds(const Backw
     if (threadIdx.x == 0) __hip_atomic_store(prog + slot, INT_MAX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D>
+template <int D, bool kPad>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(BackwardArgs a,
                                                                                               int* progress) {
     __shared__ __attribute__((aligned(16))) float lds[BCfg<D>::LDS_FLOATS];
     const WaveId w;
-    grouped_rounds(a, progress, [&](int64_t bh, int qt) { dq_tile<D>(a, lds, bh, qt, w); });
+    grouped_rounds(a, progress, [&](int64_t bh, int qt) { dq_tile<D, kPad>(a, lds, bh, qt, w); });
 }
 
 template <int D>
@@ -896,7 +916,7 @@ hipError_t grouped_grid(K kernel, int threads, int64_t work, int64_t* grid) {
     return hipSuccess;
 }
 
-template <int D>
+template <int D, bool kPad>
 hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.BH * a.n_tot;
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
@@ -910,12 +930,12 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     }
     const int64_t tiles = (int64_t)a.BH * (a.npt + a.nvt);
     int64_t gq = 0, gk = 0;
-    hipError_t e = grouped_grid(bwd_dq_kernel<D>, 256, tiles, &gq);
+    hipError_t e = grouped_grid(bwd_dq_kernel<D, kPad>, 256, tiles, &gq);
     if (e == hipSuccess) e = grouped_grid(bwd_dkdv_kernel<D>, kDkdvThreads, tiles, &gk);
     if (e != hipSuccess) return e;
     constexpr int NP = kGroupsB * kMaxGroupSizeB;
     hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(256), 0, s, a, a.progress);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kPad>), dim3((unsigned)gq), dim3(256), 0, s, a, a.progress);
     hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kDkdvThreads), 0, s, a, a.progress);
     return hipGetLastError();
@@ -925,7 +945,9 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
 
 hipError_t launch_backward(const BackwardArgs& a, int D, hipStream_t s) {
     if ((int64_t)a.BH * (a.npt + a.nvt) == 0) return hipSuccess;
-    return D == 128 ? launch_backward_d<128>(a, s) : launch_backward_d<64>(a, s);
+    if (a.pad.T != 0)
+        return D == 128 ? launch_backward_d<128, true>(a, s) : launch_backward_d<64, true>(a, s);
+    return D == 128 ? launch_backward_d<128, false>(a, s) : launch_backward_d<64, false>(a, s);
 }
 
 }  // namespace bsa

@@ -484,7 +484,6 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
     if (g.npt + g.nvt > BSA_MAX_TILES || g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
-    if (g.padded) return BSA_ERR_UNSUPPORTED;  // no key-padding masks in the backward kernels
     if (g.empty) return BSA_OK;
     if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return BSA_ERR_NULL;
     if (g.nvt > 0 && (!perm || !block_idx)) return BSA_ERR_NULL;
@@ -505,13 +504,14 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     const uint16_t* src_t[2] = {static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_o)};
     hipError_t e = hipSuccess;
     for (int i = 0; i < 4 && e == hipSuccess; ++i)
-        e = bsa::launch_gather_kf(src_kf[i], f[i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s);
+        e = bsa::launch_gather_kf(src_kf[i], f[i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s,
+                                  g.n_ras);
     if (e == hipSuccess)
         e = bsa::launch_gather_vf(static_cast<const uint16_t*>(k), f[4], perm, (int)g.B, (int)g.H, (int)g.D,
-                                  (int)g.npf, g.n_video, s);
+                                  (int)g.npf, g.n_video, s, g.n_ras);
     for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = bsa::launch_permute_copy(false, src_t[i], f[5 + i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf,
-                                     g.n_video, s);
+                                     g.n_video, s, g.n_ras);
     if (e != hipSuccess) return launched(e);
     bsa::BackwardArgs a{};
     a.q_kf = f[0];
@@ -546,6 +546,8 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.mwords = L.mwords;
     a.npf = g.npf;
     a.n_tot = g.n_tot;
+    a.n_ras = g.npf + g.n_ras;
+    a.pad = g.pad;
     a.scale = desc->scale;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_backward(a, (int)g.D, s));

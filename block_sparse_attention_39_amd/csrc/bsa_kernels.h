@@ -40,6 +40,31 @@ inline PadGeo make_pad_geo(int T, int Hg, int W, int tt, int th, int tw) {
     return g;
 }
 
+// Ragged grids in the attention kernels: a tile list staged in LDS carries,
+// above the tile number, the boundary class of a video key tile (0: no
+// padding slot), and the padding keys of a boundary tile get -inf logits.
+constexpr int kTileBits = 0xFFFF;  // tile numbers are below BSA_MAX_TILES <= 2^16
+
+// boundary class of video tile vt, shifted above the tile number
+__device__ inline int pad_class(const PadGeo& g, int vt) {
+    const int wi = vt % g.Tw, hi = (vt / g.Tw) % g.Th, ti = vt / (g.Tw * g.Th);
+    return (((ti + 1) * g.tt > g.T) << 2 | ((hi + 1) * g.th > g.Hg) << 1 | ((wi + 1) * g.tw > g.W)) << 16;
+}
+
+// -inf for the padding keys among one lane's 16 elements of an S^T
+// accumulator of a 32-key half kh, given the class's 64-bit mask of real
+// keys.  The kfrag token order (swap23) puts key 32*kh + 16*c + 8*hf + e at
+// element 8*c + e of lane-half hf.
+template <class V>
+__device__ __attribute__((always_inline)) inline void mask_padding_keys(uint64_t real, int kh, int hf, V& sv) {
+    const uint32_t half = kh ? (uint32_t)(real >> 32) : (uint32_t)real;
+    const uint32_t x = half >> (8 * hf);
+    const uint32_t bits = (x & 0xffu) | ((x >> 8) & 0xff00u);  // bit r: element r is a real key
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (!((bits >> r) & 1u)) sv[r] = -__builtin_inff();
+}
+
 // Static tile order: perm[b][p] for all b (the same closed form per batch).
 hipError_t launch_perm_static(int B, int T, int Hg, int W, int tt, int th, int tw, int32_t* perm,
                               hipStream_t s);
@@ -128,7 +153,7 @@ struct BackwardArgs {
     const uint16_t *o, *dout;  // raster [B][Ntot][H][D]
     const float* lse;          // [BH][Ntot] natural log, tiled order
     const int32_t* idx;        // [BH][nvt][keep]
-    const int32_t* perm;       // [B][Nvideo]
+    const int32_t* perm;       // [B][Nvideo], -1 for a padding slot
     float *lse2, *delta;       // [BH][Ntot] scratch: lse * log2 e, dO . O
     float *nlse, *ndelta;      // [BH][Ntot] scratch: -lse / scale, -(dO . O)
     uint32_t* mask;            // [BH][nvt][mwords] scratch
@@ -136,7 +161,9 @@ struct BackwardArgs {
     uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]
     int* progress;             // backward_progress_ints() ints: grouped-launch round counters
     int BH, H, npt, nvt, keep, mwords;
-    int64_t npf, n_tot;
+    int64_t npf, n_tot;        // tiled rows per (b, h): prefix + video slots
+    int64_t n_ras;             // raster rows per batch element (fewer on a ragged grid)
+    PadGeo pad;                // ragged grid (pad.T != 0): perm -1 marks padding slots
     float scale, scale_log2;
 };
 constexpr int backward_progress_ints() { return 8 * 64; }

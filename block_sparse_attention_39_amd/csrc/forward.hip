@@ -184,29 +184,6 @@ __device__ inline int row_len(const ForwardArgs& a, int64_t bh, int vi) {
     return (int)min(max(e - b, (int64_t)1), (int64_t)a.nvt);
 }
 
-// Ragged grids: the LDS tile list carries, above the tile number, the
-// boundary class of a video key tile (0: no padding token), and the keys of a
-// padding slot get -inf logits.  Class bit 2/1/0: the tile is the last on the
-// t/h/w axis and that axis is cut short.
-constexpr int kTileBits = 0xFFFF;  // tile numbers are below BSA_MAX_TILES <= 2^16
-
-__device__ inline int pad_class(const PadGeo& g, int vt) {
-    const int wi = vt % g.Tw, hi = (vt / g.Tw) % g.Th, ti = vt / (g.Tw * g.Th);
-    return (((ti + 1) * g.tt > g.T) << 2 | ((hi + 1) * g.th > g.Hg) << 1 | ((wi + 1) * g.tw > g.W)) << 16;
-}
-
-// -inf for the padding keys in this lane's S^T elements, given the class's
-// 64-bit mask of real keys: element r = 8*c + e holds key 32*kh + 16*c + 8*hf + e.
-__device__ __attribute__((always_inline)) inline void mask_padding_keys(uint64_t real, int kh, int hf,
-                                                                        f32x16& sv) {
-    const uint32_t half = kh ? (uint32_t)(real >> 32) : (uint32_t)real;
-    const uint32_t x = half >> (8 * hf);
-    const uint32_t bits = (x & 0xffu) | ((x >> 8) & 0xff00u);  // bit r: element r is a real key
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        if (!((bits >> r) & 1u)) sv[r] = -INFINITY;
-}
-
 __device__ inline int list_len(const ForwardArgs& a, const Item& it) {
     return it.vi < 0 ? a.npt + a.nvt : a.npt + row_len(a, it.bh, it.vi);
 }

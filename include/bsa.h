@@ -291,8 +291,10 @@ bsa_status bsa_backward_workspace_size(const bsa_desc *desc, size_t *bytes);
  * bf16 before their products, the gradients to bf16 at the end.  Tensors must
  * be 16-byte aligned (lse, perm, block_idx 4-byte); at most BSA_MAX_TILES
  * tiles and BSA_MAX_VIDEO_TILES video tiles per (batch, head).  Calls given the
- * same workspace must not run concurrently.  A ragged grid
- * (BSA_TILE_STATIC_PADDED with padding) returns BSA_ERR_UNSUPPORTED.
+ * same workspace must not run concurrently.  On a ragged grid
+ * (BSA_TILE_STATIC_PADDED) the gradients are those of the padded forward:
+ * padding keys take no weight, padding slots are neither read nor written
+ * (perm -1), and the lse is the forward's over the padded tiled order.
  */
 bsa_status bsa_backward(const bsa_desc *desc, const void *q, const void *k, const void *v,
                         const void *o, const void *d_o, const float *lse, const int32_t *perm,

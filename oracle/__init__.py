@@ -86,6 +86,13 @@ def lib() -> ctypes.CDLL:
         L.orc_pool_padded.restype = None
         L.orc_attention_padded.argtypes = [P, P, P, i32, i32, i32, P, P, P, f64, P, i32, P, P]
         L.orc_attention_padded.restype = None
+        L.orc_attention_lse_delta_padded.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, P]
+        L.orc_attention_lse_delta_padded.restype = None
+        L.orc_attention_backward_dq_padded.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i32, P]
+        L.orc_attention_backward_dq_padded.restype = None
+        L.orc_attention_backward_dkdv_padded.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i32, P,
+                                                          P]
+        L.orc_attention_backward_dkdv_padded.restype = None
         _lib = L
     return _lib
 
@@ -511,3 +518,62 @@ def attention_padded(q_bh, k_bh, v_bh, n_prefix: int, idx_bh, real, scale: float
     nvt, k = ix.shape
     row_ptr = np.arange(nvt + 1, dtype=np.int64) * k
     return attention_padded_csr(q_bh, k_bh, v_bh, n_prefix, row_ptr, ix.reshape(-1), real, scale, qtiles)
+
+
+def lse_delta_padded(q_bh, k_bh, v_bh, do_bh, n_prefix: int, idx_bh, real, scale: float):
+    """As ``lse_delta`` on a ragged grid (real keys only)."""
+    q, kx, v, do, Ntot, D, nvt, ix, k = _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh)
+    kr = _c(real, np.uint8)
+    assert kr.shape == (Ntot,)
+    lse = np.empty(Ntot, np.float64)
+    delta = np.empty(Ntot, np.float64)
+    lib().orc_attention_lse_delta_padded(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), n_prefix, nvt, D, k, _ptr(ix),
+                                         _ptr(kr), float(scale), _ptr(lse), _ptr(delta))
+    return lse, delta
+
+
+def backward_dq_padded(q_bh, k_bh, v_bh, do_bh, lse, delta, n_prefix: int, idx_bh, real, scale: float, qtiles):
+    """As ``backward_dq`` on a ragged grid (real keys only)."""
+    q, kx, v, do, Ntot, D, nvt, ix, k = _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh)
+    kr = _c(real, np.uint8)
+    qt = _c(qtiles, np.int32)
+    out = np.empty((qt.shape[0], TILE, D), np.float64)
+    lib().orc_attention_backward_dq_padded(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), _ptr(_c(lse, np.float64)),
+                                           _ptr(_c(delta, np.float64)), n_prefix, nvt, D, k, _ptr(ix), _ptr(kr),
+                                           float(scale), _ptr(qt), qt.shape[0], _ptr(out))
+    return out
+
+
+def backward_dkdv_padded(q_bh, k_bh, v_bh, do_bh, lse, delta, n_prefix: int, idx_bh, real, scale: float, ktiles):
+    """As ``backward_dkdv`` on a ragged grid: real keys, real queries; padding
+    key rows are zero."""
+    q, kx, v, do, Ntot, D, nvt, ix, k = _bh_args(q_bh, k_bh, v_bh, do_bh, n_prefix, idx_bh)
+    kr = _c(real, np.uint8)
+    kt = _c(ktiles, np.int32)
+    dk = np.empty((kt.shape[0], TILE, D), np.float64)
+    dv = np.empty((kt.shape[0], TILE, D), np.float64)
+    lib().orc_attention_backward_dkdv_padded(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), _ptr(_c(lse, np.float64)),
+                                             _ptr(_c(delta, np.float64)), n_prefix, nvt, D, k, _ptr(ix), _ptr(kr),
+                                             float(scale), _ptr(kt), kt.shape[0], _ptr(dk), _ptr(dv))
+    return dk, dv
+
+
+def backward_full_padded(q_tiled, k_tiled, v_tiled, do_tiled, n_prefix: int, idx, real, scale: float):
+    """Gradients of every (b,h) on a ragged grid, tiled order (padding rows
+    of dK, dV zero): ``(dq, dk, dv)`` float64 ``[B,H,Ntot,D]``.  ``real``:
+    ``key_real`` of each batch element, ``[B, Ntot]``."""
+    B, H, Ntot, D = q_tiled.shape
+    tiles = np.arange(Ntot // TILE, dtype=np.int32)
+    dq = np.empty((B, H, Ntot, D), np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    for b in range(B):
+        for h in range(H):
+            ix = idx[b, h] if idx is not None else None
+            args = (q_tiled[b, h], k_tiled[b, h], v_tiled[b, h], do_tiled[b, h])
+            lse, delta = lse_delta_padded(*args, n_prefix, ix, real[b], scale)
+            dq[b, h] = backward_dq_padded(*args, lse, delta, n_prefix, ix, real[b], scale, tiles).reshape(Ntot, D)
+            g_k, g_v = backward_dkdv_padded(*args, lse, delta, n_prefix, ix, real[b], scale, tiles)
+            dk[b, h] = g_k.reshape(Ntot, D)
+            dv[b, h] = g_v.reshape(Ntot, D)
+    return dq, dk, dv

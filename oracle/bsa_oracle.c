@@ -974,3 +974,134 @@ void orc_attention_padded(const uint16_t *q, const uint16_t *kx, const uint16_t 
         free(keys);
     }
 }
+
+/*
+ * Gradients on a ragged grid: the derivative of orc_attention_padded (keys
+ * limited to the real tokens, key_real[j] != 0), with the selection fixed.
+ * As orc_attention_lse_delta / orc_attention_backward_dq / _dkdv, with:
+ *   - every key list filtered to the real keys;
+ *   - dK, dV summed over the real queries only (a padding slot is not a token:
+ *     it carries no loss), and zero for a padding key row.
+ * Padding query rows still get lse and Delta (of their zero query), unused.
+ */
+static int64_t keep_real(const uint8_t *real, int64_t *keys, int64_t n)
+{
+    int64_t c = 0;
+    for (int64_t j = 0; j < n; ++j)
+        if (real[keys[j]])
+            keys[c++] = keys[j];
+    return c;
+}
+
+void orc_attention_lse_delta_padded(const uint16_t *q, const uint16_t *kx, const uint16_t *v,
+                                    const uint16_t *dout, int n_prefix, int nvt, int D, int k, const int32_t *idx,
+                                    const uint8_t *key_real, double scale, double *lse, double *delta)
+{
+    const int npt = n_prefix / TILE;
+    const int ntiles = npt + nvt;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int qt = 0; qt < ntiles; ++qt) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)Ntot);
+        double *z = (double *)malloc(sizeof(double) * (size_t)Ntot);
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        const int64_t nk = keep_real(key_real, keys, key_list(qt, n_prefix, nvt, k, idx, keys));
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                z[j] = scale * dot_bf16(q + qi * D, kx + keys[j] * D, D);
+                if (z[j] > mx)
+                    mx = z[j];
+            }
+            double den = 0.0;
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const double w = exp(z[j] - mx);
+                den += w;
+                for (int d = 0; d < D; ++d)
+                    o[d] += w * bf16_to_double(v[keys[j] * D + d]);
+            }
+            double dl = 0.0;
+            for (int d = 0; d < D; ++d)
+                dl += bf16_to_double(dout[qi * D + d]) * (o[d] / den);
+            lse[qi] = mx + log(den);
+            delta[qi] = dl;
+        }
+        free(keys);
+        free(z);
+        free(o);
+    }
+}
+
+void orc_attention_backward_dq_padded(const uint16_t *q, const uint16_t *kx, const uint16_t *v,
+                                      const uint16_t *dout, const double *lse, const double *delta, int n_prefix,
+                                      int nvt, int D, int k, const int32_t *idx, const uint8_t *key_real,
+                                      double scale, const int32_t *qtiles, int nq, double *dq)
+{
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nq; ++a) {
+        const int qt = qtiles[a];
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)Ntot);
+        const int64_t nk = keep_real(key_real, keys, key_list(qt, n_prefix, nvt, k, idx, keys));
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            double *g = dq + ((int64_t)a * TILE + r) * D;
+            for (int d = 0; d < D; ++d)
+                g[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const uint16_t *kr = kx + keys[j] * D;
+                const double p = exp(scale * dot_bf16(q + qi * D, kr, D) - lse[qi]);
+                const double dp = dot_bf16(dout + qi * D, v + keys[j] * D, D);
+                const double ds = p * (dp - delta[qi]);
+                for (int d = 0; d < D; ++d)
+                    g[d] += ds * bf16_to_double(kr[d]);
+            }
+            for (int d = 0; d < D; ++d)
+                g[d] *= scale;
+        }
+        free(keys);
+    }
+}
+
+void orc_attention_backward_dkdv_padded(const uint16_t *q, const uint16_t *kx, const uint16_t *v,
+                                        const uint16_t *dout, const double *lse, const double *delta, int n_prefix,
+                                        int nvt, int D, int k, const int32_t *idx, const uint8_t *key_real,
+                                        double scale, const int32_t *ktiles, int nk, double *dk, double *dv)
+{
+    const int npt = n_prefix / TILE;
+    const int ntiles = npt + nvt;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nk; ++a) {
+        const int kt = ktiles[a];
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t kj = (int64_t)kt * TILE + r;
+            double *gk = dk + ((int64_t)a * TILE + r) * D;
+            double *gv = dv + ((int64_t)a * TILE + r) * D;
+            for (int d = 0; d < D; ++d)
+                gk[d] = gv[d] = 0.0;
+            if (!key_real[kj])
+                continue;
+            for (int qt = 0; qt < ntiles; ++qt) {
+                if (!attends(qt, kt, npt, k, idx))
+                    continue;
+                for (int s = 0; s < TILE; ++s) {
+                    const int64_t qi = (int64_t)qt * TILE + s;
+                    if (!key_real[qi]) /* the same mask marks real query rows */
+                        continue;
+                    const double p = exp(scale * dot_bf16(q + qi * D, kx + kj * D, D) - lse[qi]);
+                    const double dp = dot_bf16(dout + qi * D, v + kj * D, D);
+                    const double ds = p * (dp - delta[qi]);
+                    for (int d = 0; d < D; ++d) {
+                        gk[d] += ds * bf16_to_double(q[qi * D + d]);
+                        gv[d] += p * bf16_to_double(dout[qi * D + d]);
+                    }
+                }
+            }
+            for (int d = 0; d < D; ++d)
+                gk[d] *= scale;
+        }
+    }
+}

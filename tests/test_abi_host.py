@@ -200,8 +200,8 @@ def test_desc_layout_matches_header():
 def test_padded_mode_host_checks():
     """Ragged grids (BSA_TILE_STATIC_PADDED): the mode constant matches the
     header; the workspace is sized on the padded tile count; the tile must
-    still be 64 tokens; the backward refuses a ragged grid; structured lists
-    count on the rounded-up tile grid."""
+    still be 64 tokens; the backward takes a ragged grid (a missing tensor is
+    reported as such); structured lists count on the rounded-up tile grid."""
     m = re.search(r"BSA_TILE_STATIC_PADDED = (\d+)", HEADER)
     assert m and int(m.group(1)) == bsa.TILE_STATIC_PADDED
     L = lib()
@@ -214,7 +214,7 @@ def test_padded_mode_host_checks():
     assert ws_size(bsa.make_desc(1, 1, 64, (5, 6, 7), 9, padded=True))[0] == SHAPE   # 8 tiles
     n = ctypes.c_size_t(0)
     assert L.bsa_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
-    assert L.bsa_backward(ctypes.byref(d), *([None] * 11), None, 0, None) == UNSUP
+    assert L.bsa_backward(ctypes.byref(d), *([None] * 11), None, 0, None) == NULL
     # padded mode on a grid that divides: the plain static problem
     dp = bsa.make_desc(1, 2, 64, (8, 8, 12), 5, padded=True)
     assert bsa.video_slots(dp) == 768 and ws_size(dp) == ws_size(bsa.make_desc(1, 2, 64, (8, 8, 12), 5))

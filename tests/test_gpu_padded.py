@@ -6,15 +6,20 @@ not a whole number of static tiles, covered by the tile grid rounded up.
 * kept tiles: the selection rules of the other parity tests;
 * attention over the real keys only (boundary tiles masked), on the real
   query rows, with the forward's output and lse tolerances;
-* on a grid that divides, padded mode is the plain static path bit for bit.
+* on a grid that divides, padded mode is the plain static path bit for bit;
+* dQ, dK, dV on the raster rows against the oracle's gradients of the padded
+  forward, with the backward's tolerances (small cases in full, the 720p clip
+  on sampled tiles).
 """
 import numpy as np
 import pytest
 import torch
 
+import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, check_lse, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
+from parity import (GpuRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, to_dev,
+                    vfrag_layout)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,4 +110,104 @@ def test_prism720p_ragged_sampled():
     tiles = np.unique(np.concatenate([boundary, rng.choice(nqt, size=12, replace=False)])).astype(np.int32)
     check_padded_path(wl, g, q, k, v, qtiles=tiles, bh=[(0, 0), (1, 13)])
     del g
+    torch.cuda.empty_cache()
+
+
+# ---- gradients on ragged grids ---------------------------------------------------
+
+BWD_CASES = [
+    W("bpad_5x6x7", 2, 2, 128, (5, 6, 7), 5, seed=51, n_prefix=64, padded=True),
+    W("bpad_d64", 1, 3, 64, (9, 13, 10), 7, seed=52, padded=True),
+    W("bpad_tile2x4x8", 1, 2, 128, (7, 9, 20), 4, seed=53, tile=(2, 4, 8), padded=True),
+    W("bpad_keep_all", 1, 1, 128, (6, 5, 9), 12, seed=54, n_prefix=128, padded=True),
+]
+
+
+def raster_to_tiled_rows(perm1, npf):
+    """tiled slot of every raster row (prefix first), for one batch element"""
+    real_slots = np.nonzero(perm1 >= 0)[0]
+    src = np.empty(npf + real_slots.size, np.int64)
+    src[:npf] = np.arange(npf)
+    src[npf + perm1[real_slots]] = npf + real_slots
+    return src
+
+
+def check_grad(got, ref, what):
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    ref_mx, ref_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    print(f"[{what}] max|err| {mx:.3e} (ref max {ref_mx:.3e}), mean|err| {mean:.3e} (ref mean {ref_mean:.3e})",
+          flush=True)
+    assert np.isfinite(got).all(), what
+    assert mx <= 2e-2 * ref_mx + 1e-6, what
+    assert mean <= 1e-2 * ref_mean + 1e-7, what
+
+
+def run_padded_backward(wl):
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    dq, dk, dv = (torch.empty_like(g.q) for _ in range(3))
+    ws = torch.empty(max(bsa.backward_workspace_size(g.desc), 256), dtype=torch.uint8, device="cuda")
+    bsa.backward(g.desc, g.q, g.k, g.v, g.out, to_dev(do), g.att.lse, g.att.perm, g.att.block_idx, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return (q, k, v, do), g, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("wl", BWD_CASES, ids=[c.name for c in BWD_CASES])
+def test_padded_backward_matches_oracle(wl):
+    """dQ, dK, dV on the raster rows against the oracle's gradients of the
+    padded forward (real keys, real queries), with the GPU's selection."""
+    print(f"\n[case] {wl}", flush=True)
+    (q, k, v, do), g, grads = run_padded_backward(wl)
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    p1 = oracle.perm_static_padded(wl.grid, wl.tile)
+    tiled = [oracle.gather_padded(x, p1, npf) for x in (q, k, v, do)]
+    real = np.broadcast_to(oracle.key_real(p1, npf), (wl.batch, npf + p1.size))
+    ref = oracle.backward_full_padded(*tiled, npf, g.block_idx(), real, scale)
+    src = raster_to_tiled_rows(p1, npf)
+    for name, dev, r in zip(("dq", "dk", "dv"), grads, ref):
+        got = bits_to_f64(to_bits(dev))                      # raster [B, Nras, H, D]
+        check_grad(got, r[:, :, src].transpose(0, 2, 1, 3), name)
+
+
+def test_prism720p_ragged_backward_sampled():
+    """Full size (31 x 45 x 80 padded to 32 x 48 x 80, batch 2, 24 heads,
+    head_dim 128, keep 480): dQ of sampled query tiles entirely from the
+    oracle; dK, dV of sampled key tiles from the oracle's derivative with the
+    GPU forward's lse and Delta = dO . O of the GPU's bf16 output (a key tile
+    gathers from about 480 query tiles).  Boundary tiles among the samples."""
+    wl = S.WORKLOADS["prism720p_ragged"]
+    print(f"\n[case] {wl}", flush=True)
+    (q, k, v, do), g, grads = run_padded_backward(wl)
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    p1 = oracle.perm_static_padded(wl.grid, wl.tile)
+    real = oracle.key_real(p1, npf)
+    nqt = wl.n_tiled_tokens // 64
+    gidx = g.block_idx()
+    lse_gpu = g.att.lse.cpu().numpy()
+    for b, h in [(0, 5), (1, 22)]:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        qt, kt, vt, dot = (oracle.gather_padded(sl(x), p1, npf)[0, 0] for x in (q, k, v, do))
+        ot = bits_to_f64(to_bits(g.att.o_t[b, h]))
+        gt = [bits_to_f64(oracle.gather_padded(to_bits(x[b:b + 1, :, h:h + 1]), p1, npf)[0, 0])
+              .reshape(nqt, 64, wl.head_dim) for x in grads]
+        rows = real.reshape(nqt, 64).astype(bool)
+        qtiles = np.array([5, 1919, 1900, 959], np.int32)   # 1919, 1900, 959: boundary tiles
+        o_ref, lse_ref = oracle.attention_padded(qt, kt, vt, npf, gidx[b, h], real, scale, qtiles)
+        lse = np.zeros(wl.n_tiled_tokens)
+        delta = np.zeros(wl.n_tiled_tokens)
+        qrows = (qtiles[:, None] * 64 + np.arange(64)).reshape(-1)
+        lse[qrows] = lse_ref.reshape(-1)
+        delta[qrows] = (o_ref.reshape(-1, wl.head_dim) * bits_to_f64(dot)[qrows]).sum(1)
+        ref_dq = oracle.backward_dq_padded(qt, kt, vt, dot, lse, delta, npf, gidx[b, h], real, scale, qtiles)
+        check_grad(gt[0][qtiles][rows[qtiles]], ref_dq[rows[qtiles]], f"dq b{b} h{h}")
+        lse_all = lse_gpu[b, h].astype(np.float64)
+        delta_all = (ot * bits_to_f64(dot)).sum(1)
+        ktiles = np.array([1919, 1000], np.int32)
+        ref_dk, ref_dv = oracle.backward_dkdv_padded(qt, kt, vt, dot, lse_all, delta_all, npf, gidx[b, h], real,
+                                                     scale, ktiles)
+        check_grad(gt[1][ktiles][rows[ktiles]], ref_dk[rows[ktiles]], f"dk b{b} h{h}")
+        check_grad(gt[2][ktiles][rows[ktiles]], ref_dv[rows[ktiles]], f"dv b{b} h{h}")
+    del g, grads
     torch.cuda.empty_cache()

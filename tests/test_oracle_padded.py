@@ -15,6 +15,10 @@ quadratic cost: the 720p grid counts padding tokens).
   contents; identical to the CSR attention without padding.  With every tile
   kept, the whole path (gather, attention, scatter) is dense attention over
   the real tokens in raster order.
+* Gradients: torch autograd of the same masked fp64 attention (loss = sum of
+  O * dO, dO zero on padding rows); zero dK, dV on padding key rows; real
+  rows unchanged by padding-slot contents; with every tile kept, autograd of
+  dense attention over the real tokens in raster order.
 """
 import numpy as np
 import pytest
@@ -172,3 +176,65 @@ def test_all_tiles_kept_is_dense_attention_on_real_tokens(orc):
     qq, kk, vv = (_f64(a[0, :, 0])[None, None] for a in x)
     ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=0.25)[0, 0]
     np.testing.assert_allclose(o_ras, ref.numpy(), rtol=0, atol=1e-12)
+
+
+# ---- gradients on a ragged grid ------------------------------------------------
+
+def _autograd(q, k, v, do, mask, scale):
+    qq, kk, vv = (_f64(x).requires_grad_(True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qq[None, None], kk[None, None], vv[None, None],
+                                                           attn_mask=None if mask is None else
+                                                           torch.from_numpy(mask)[None, None], scale=scale)[0, 0]
+    (out * _f64(do)).sum().backward()
+    return qq.grad.numpy(), kk.grad.numpy(), vv.grad.numpy()
+
+
+@pytest.mark.parametrize("grid,tile,npf,D,keep", [((5, 6, 7), (4, 4, 4), 64, 16, 3), ((9, 4, 13), (2, 4, 8), 0, 8, 2)])
+def test_gradients_match_masked_autograd(orc, grid, tile, npf, D, keep):
+    """Kept lists and real keys as an explicit token mask on the tiled order;
+    dO is zero on padding rows (they carry no loss), as the gathered dO is."""
+    rng = np.random.default_rng(86 + D)
+    p = orc.perm_static_padded(grid, tile)
+    nvt = p.size // 64
+    nr = int(np.prod(grid))
+    q, k, v, do = (orc.gather_padded(_rand_bits(rng, (1, npf + nr, 1, D), 1.5), p, npf)[0, 0] for _ in range(4))
+    idx = np.stack([np.sort(rng.choice(nvt, size=keep, replace=False)) for _ in range(nvt)]).astype(np.int32)
+    real = orc.key_real(p, npf)
+    scale = 0.3
+    dq, dk, dv = (x[0, 0] for x in orc.backward_full_padded(q[None, None], k[None, None], v[None, None],
+                                                             do[None, None], npf, idx[None, None], real[None], scale))
+    row_ptr = np.arange(nvt + 1, dtype=np.int64) * keep
+    m = _mask(npf, nvt, row_ptr, idx.reshape(-1), real)
+    rq, rk, rv = _autograd(q, k, v, do, m, scale)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    assert not dk[real == 0].any() and not dv[real == 0].any()
+    # padding-slot contents of Q, K, V do not change the real rows' gradients
+    pad = np.nonzero(real == 0)[0]
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for x in (q2, k2, v2):
+        x[pad] = _rand_bits(rng, (pad.size, D), 20.0)
+    g2 = [x[0, 0] for x in orc.backward_full_padded(q2[None, None], k2[None, None], v2[None, None], do[None, None],
+                                                    npf, idx[None, None], real[None], scale)]
+    r = real == 1
+    for a, b in zip((dq, dk, dv), g2):
+        assert np.array_equal(a[r], b[r])
+
+
+def test_all_tiles_kept_gradients_are_dense_autograd_on_real_tokens(orc):
+    rng = np.random.default_rng(87)
+    grid, tile, npf, D = (6, 5, 9), (4, 4, 4), 64, 16
+    nr = int(np.prod(grid))
+    x = [_rand_bits(rng, (1, npf + nr, 1, D), 1.5) for _ in range(4)]
+    p = orc.perm_static_padded(grid, tile)
+    nvt = p.size // 64
+    qt, kt, vt, dt = (orc.gather_padded(a, p, npf) for a in x)
+    idx = np.tile(np.arange(nvt, dtype=np.int32), (nvt, 1))
+    grads = orc.backward_full_padded(qt, kt, vt, dt, npf, idx[None, None], orc.key_real(p, npf)[None], 0.25)
+    ref = _autograd(*(a[0, :, 0] for a in x), None, 0.25)
+    real_slots = np.nonzero(p >= 0)[0]
+    for g, r in zip(grads, ref):
+        back = np.zeros((npf + nr, D))
+        back[:npf] = g[0, 0, :npf]
+        back[npf + p[real_slots]] = g[0, 0, npf + real_slots]
+        np.testing.assert_allclose(back, r, rtol=0, atol=1e-11)

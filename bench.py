@@ -31,6 +31,7 @@ FLOPs from the lists' lengths.
 
 times the variable-keep path instead (bsa_plan_csr / bsa_forward_csr): head h
 keeps the (h mod 4)-th count of the list; effective FLOPs from those counts.
+With --backward it times bsa_backward_csr over those lists.
 """
 from __future__ import annotations
 
@@ -149,7 +150,7 @@ def varkeep_flops(wl, keep_h):
     head h keeping keep_h[h] tiles per video query tile."""
     pairs = 0
     for kh in keep_h:
-        pairs += wl.n_prefix * wl.n_tokens + wl.n_video * (wl.n_prefix + kh * 64)
+        pairs += wl.n_prefix * wl.n_tiled_tokens + wl.n_video_slots * (wl.n_prefix + kh * 64)
     return 4.0 * wl.batch * wl.head_dim * pairs
 
 
@@ -418,13 +419,32 @@ def bench_backward(args, wl, q, k, v):
     do = S.tensor(wl, "do")
     dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
-    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
-                         n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
+    keep_h = None  # --varkeep: CSR lists, head h keeping keep_h[h] tiles
+    if args.varkeep:
+        counts = [int(x) for x in args.varkeep.split(",")]
+        keep_h = [counts[h % len(counts)] for h in range(wl.heads)]
+    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, max(keep_h) if keep_h else wl.keep_tiles,
+                         scale=wl.scale, n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau,
+                         padded=wl.padded)
     att = bsa.BlockSparseAttention(desc, with_lse=True)
-    out = att(qd, kd, vd)
     dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
-    ws = torch.empty(max(bsa.backward_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
-    call = lambda: bsa.backward(desc, qd, kd, vd, out, dod, att.lse, att.perm, att.block_idx, dq, dk, dv, ws)
+    if keep_h is None:
+        out = att(qd, kd, vd)
+        ws = torch.empty(max(bsa.backward_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+        call = lambda: bsa.backward(desc, qd, kd, vd, out, dod, att.lse, att.perm, att.block_idx, dq, dk, dv, ws)
+    else:
+        att.build(qd)
+        att.gather_qkv(qd, kd, vd)
+        row_ptr = torch.empty(wl.batch * wl.heads * wl.n_video_tiles + 1, dtype=torch.int64, device="cuda")
+        col = torch.empty(bsa.csr_entries(desc, keep_h), dtype=torch.int32, device="cuda")
+        bsa.plan_csr(desc, att.q_t, att.k_f, row_ptr, col, att.workspace, keep_per_head=keep_h)
+        bsa.forward_csr(desc, att.q_t, att.k_f, att.v_f, row_ptr, col, att.o_t, att.lse, workspace=att.workspace)
+        out = torch.empty_like(qd)
+        att.scatter_out(out)
+        ws = torch.empty(max(bsa.backward_csr_workspace_size(desc, col.numel()), 256), dtype=torch.uint8,
+                         device="cuda")
+        call = lambda: bsa.backward_csr(desc, qd, kd, vd, out, dod, att.lse, att.perm, row_ptr, col, dq, dk, dv,
+                                        ws)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -438,7 +458,7 @@ def bench_backward(args, wl, q, k, v):
     wall = time.perf_counter() - t_start
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = float(np.mean(times))
-    F = 2.5 * wl.effective_flops()
+    F = 2.5 * (varkeep_flops(wl, keep_h) if keep_h else wl.effective_flops())
     achieved = F / (ms * 1e-3) / 1e12
     res = {
         "metric": METRIC_BWD,
@@ -457,13 +477,15 @@ def bench_backward(args, wl, q, k, v):
                    "video_tiles": wl.n_video_tiles, "prefix_tokens": wl.n_prefix, "batch": wl.batch,
                    "heads": wl.heads, "head_dim": wl.head_dim, "keep_tiles": wl.keep_tiles,
                    "tile": "dynamic" if wl.dynamic else "x".join(map(str, wl.tile)),
+                   "keep_per_head": keep_h, "padded_video_tokens": wl.n_video_slots if wl.padded else None,
                    "backward_effective_tflop_per_call": F / 1e12},
-        "roofline": {"bound": "mfma", "kernel": "bsa_backward (all kernels of the call)", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "bsa_backward%s (all kernels of the call)" % ("_csr" if keep_h else ""),
+                     "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": None},
         "wall_ms_per_step": wall * 1e3 / args.steps,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and keep_h is None:
         t0 = time.perf_counter()
         res["cpu_baseline"] = cpu_baseline_backward(wl, q, k, v, do, args.cpu_bwd_tiles)
         print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)

@@ -1,6 +1,6 @@
 """ctypes loader for libbsa.so and the mirror of ``bsa_desc`` (include/bsa.h).
 
-The library is built in-tree by ``python -m block_sparse_attention_39_amd.build``;
+The library is built in-tree by ``python block_sparse_attention_39_amd/build.py``;
 importing this module without it raises at once: there is no fallback path.
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
 EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_csr_entries", "bsa_plan_csr",
            "bsa_forward_csr", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
-           "bsa_backward", "bsa_status_string", "bsa_version")
+           "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_status_string", "bsa_version")
 MASK_SPATIAL, MASK_TEMPORAL = 0, 1
 MAX_CSR_HEADS = 256
 
@@ -51,7 +51,7 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m block_sparse_attention_39_amd.build` (hipcc, gfx950)")
+                              "`python block_sparse_attention_39_amd/build.py` (hipcc, gfx950)")
         L = ctypes.CDLL(LIB_PATH)
         P, D = ctypes.c_void_p, ctypes.POINTER(Desc)
         L.bsa_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
@@ -67,11 +67,13 @@ def lib() -> ctypes.CDLL:
         L.bsa_plan_structured.argtypes = [D, P, I32, I32, P, P, I64, P]
         L.bsa_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.bsa_backward_csr_workspace_size.argtypes = [D, I64, ctypes.POINTER(ctypes.c_size_t)]
+        L.bsa_backward_csr.argtypes = [D, P, P, P, P, P, P, P, P, P, I64, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_status_string.argtypes = [ctypes.c_int]
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_version.argtypes = []
         for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_forward", "bsa_backward_workspace_size",
-                  "bsa_backward", "bsa_version"):
+                  "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -192,6 +192,21 @@ def backward(desc: Desc, q, k, v, o, d_o, lse, perm, block_idx, dq, dk, dv, work
                               _stream(stream)), "bsa_backward")
 
 
+def backward_csr_workspace_size(desc: Desc, col_entries: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_backward_csr_workspace_size(ctypes.byref(desc), int(col_entries), ctypes.byref(n)),
+           "bsa_backward_csr_workspace_size")
+    return n.value
+
+
+def backward_csr(desc: Desc, q, k, v, o, d_o, lse, perm, row_ptr, col_idx, dq, dk, dv, workspace, stream=None):
+    """As ``backward``, over the CSR lists of ``plan_csr`` / ``plan_structured``."""
+    ws = workspace.numel() * workspace.element_size()
+    _check(lib().bsa_backward_csr(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                  _ptr(perm), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(workspace), ws, _stream(stream)), "bsa_backward_csr")
+
+
 def pooled_views(desc: Desc, workspace):
     """(qbar, kbar) float views of the workspace after bsa_plan ([B, H, nVT, D])."""
     B, H, D = desc.batch, desc.heads, desc.head_dim

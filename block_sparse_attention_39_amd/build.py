@@ -1,6 +1,6 @@
 """Build libbsa.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_attention_39_amd.build
+    python block_sparse_attention_39_amd/build.py
 
 Every translation unit is compiled with hipcc (-O3, --offload-arch=gfx950) and
 with packed FP32 instructions disabled; the objects go to ``_build/`` and the

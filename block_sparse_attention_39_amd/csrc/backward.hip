@@ -107,6 +107,21 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
     a.nlse[r] = -a.lse[r] / a.scale;
 }
 
+// ---- kept lists -------------------------------------------------------------
+// First entry in idx and length of the kept list of video query tile row r =
+// bh * nvt + i: the fixed stride, or the CSR row clamped as the forward
+// clamps it (inside [0, col_entries), 1..nvt entries), so that both passes
+// see the same key sets.
+__device__ inline int64_t kept_begin(const BackwardArgs& a, int64_t r) {
+    if (!a.row_ptr) return r * a.keep;
+    return min(max(a.row_ptr[r], (int64_t)0), a.col_entries - 1);
+}
+__device__ inline int kept_len(const BackwardArgs& a, int64_t r) {
+    if (!a.row_ptr) return a.keep;
+    const int64_t e = min(a.row_ptr[r + 1], a.col_entries);
+    return (int)min(max(e - kept_begin(a, r), (int64_t)1), (int64_t)a.nvt);
+}
+
 // ---- transposed lists: for each video key tile, the video query tiles that
 // kept it, ascending --------------------------------------------------------
 // bit j of row (bh, i): video query tile i kept video key tile j
@@ -115,8 +130,9 @@ __global__ __launch_bounds__(256) void bwd_mask_kernel(BackwardArgs a) {
     if (r >= (int64_t)a.BH * a.nvt) return;
     uint32_t* row = a.mask + r * a.mwords;
     for (int w = 0; w < a.mwords; ++w) row[w] = 0u;
-    const int32_t* ix = a.idx + r * a.keep;
-    for (int t = 0; t < a.keep; ++t) {
+    const int32_t* ix = a.idx + kept_begin(a, r);
+    const int len = kept_len(a, r);
+    for (int t = 0; t < len; ++t) {
         const int j = min(max(ix[t], 0), a.nvt - 1);
         row[j >> 5] |= 1u << (j & 31);
     }
@@ -134,33 +150,33 @@ __global__ __launch_bounds__(256) void bwd_tcount_kernel(BackwardArgs a) {
     a.cnt[r] = c;
 }
 
-// rowp[bh][0..nvt]: exclusive prefix sums of the counts (one block per bh)
-__global__ __launch_bounds__(256) void bwd_tscan_kernel(BackwardArgs a) {
-    __shared__ int part[256];
-    int* rp = a.rowp + (int64_t)blockIdx.x * (a.nvt + 1);
-    const int* cn = a.cnt + (int64_t)blockIdx.x * a.nvt;
+// rowp[0..BH*nvt]: exclusive prefix sums of the counts over (bh, j), one
+// block: each thread sums a contiguous run, the runs are scanned in LDS
+__global__ __launch_bounds__(1024) void bwd_tscan_kernel(BackwardArgs a) {
+    __shared__ int64_t part[1024];
+    const int64_t n = (int64_t)a.BH * a.nvt;
     const int t = threadIdx.x;
-    const int per = (a.nvt + 255) / 256;
-    const int lo = min(t * per, a.nvt), hi = min(lo + per, a.nvt);
-    int s = 0;
-    for (int j = lo; j < hi; ++j) s += cn[j];
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t lo = min(t * per, n), hi = min(lo + per, n);
+    int64_t s = 0;
+    for (int64_t j = lo; j < hi; ++j) s += a.cnt[j];
     part[t] = s;
     __syncthreads();
     if (t == 0) {
-        int run = 0;
-        for (int u = 0; u < 256; ++u) {
-            const int v = part[u];
+        int64_t run = 0;
+        for (int u = 0; u < 1024; ++u) {
+            const int64_t v = part[u];
             part[u] = run;
             run += v;
         }
     }
     __syncthreads();
-    int run = part[t];
-    for (int j = lo; j < hi; ++j) {
-        rp[j] = run;
-        run += cn[j];
+    int64_t run = part[t];
+    for (int64_t j = lo; j < hi; ++j) {
+        a.rowp[j] = run;
+        run += a.cnt[j];
     }
-    if (t == 255) rp[a.nvt] = run;
+    if (t == 1023) a.rowp[n] = run;
 }
 
 __global__ __launch_bounds__(256) void bwd_tfill_kernel(BackwardArgs a) {
@@ -169,10 +185,13 @@ __global__ __launch_bounds__(256) void bwd_tfill_kernel(BackwardArgs a) {
     const int64_t bh = r / a.nvt;
     const int j = (int)(r % a.nvt);
     const uint32_t* m = a.mask + bh * a.nvt * a.mwords + (j >> 5);
-    int32_t* out = a.tlist + bh * (int64_t)a.nvt * a.keep + a.rowp[bh * (a.nvt + 1) + j];
-    int p = 0;
+    const int64_t o = a.rowp[r];
+    int64_t p = 0;
     for (int i = 0; i < a.nvt; ++i)
-        if ((m[(int64_t)i * a.mwords] >> (j & 31)) & 1u) out[p++] = i;
+        if ((m[(int64_t)i * a.mwords] >> (j & 31)) & 1u) {
+            if (o + p < a.tcap) a.tlist[o + p] = i;  // a list past the capacity is cut (malformed CSR only)
+            ++p;
+        }
 }
 
 // ---- shared pieces of the two gradient kernels -----------------------------
@@ -284,7 +303,8 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
     constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
     const int n_tiles = a.npt + a.nvt;
     const bool dense = qt < a.npt;
-    const int n_iter = dense ? n_tiles : a.npt + a.keep;
+    const int64_t krow = bh * a.nvt + (qt - a.npt);  // kept-list row of a video query tile
+    const int n_iter = dense ? n_tiles : a.npt + kept_len(a, krow);
     int* list = (int*)lds;
     uint8_t* qlds = (uint8_t*)(lds + kMaxListTilesB);   // Q^T fragments [2][SD][64][16 B]
     uint8_t* glds = qlds + 2 * SD * 1024;                // dO^T fragments, same layout
@@ -294,9 +314,9 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
     if (dense) {
         for (int j = w.tid; j < n_iter; j += 256) list[j] = j | (kPad && j >= a.npt ? pad_class(a.pad, j - a.npt) : 0);
     } else {
-        const int32_t* row = a.idx + (bh * a.nvt + (qt - a.npt)) * (int64_t)a.keep;
+        const int32_t* row = a.idx + kept_begin(a, krow);
         for (int j = w.tid; j < a.npt; j += 256) list[j] = j;
-        for (int e = w.tid; e < a.keep; e += 256) {
+        for (int e = w.tid; e < n_iter - a.npt; e += 256) {
             const int vt = min(max(row[e], 0), a.nvt - 1);
             list[a.npt + e] = (a.npt + vt) | (kPad ? pad_class(a.pad, vt) : 0);
         }
@@ -502,7 +522,9 @@ __device__ __attribute__((always_inline)) inline void block_barrier() {
 // an int32 read through the scalar data cache (uniform address, data written
 // by an earlier launch), so that waiting for it does not wait for the vector
 // memory loads in flight
+typedef const __attribute__((address_space(4))) int64_t const_i64;
 __device__ inline int scalar_load(const int32_t* p) { return *(const_i32*)p; }
+__device__ inline int64_t scalar_load(const int64_t* p) { return *(const_i64*)p; }
 
 constexpr int kDkdvThreads = 512;
 
@@ -760,15 +782,15 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
 
     // the query tiles that attend key tile kt: every tile for a prefix key
     // tile; the prefix tiles and then the transposed list for a video one
-    int n_iter, lo = 0;
+    int n_iter;
     const int32_t* tl = nullptr;
     if (kt < a.npt) {
         n_iter = n_tiles;
     } else {
-        const int32_t* rp = a.rowp + bh * (a.nvt + 1) + (kt - a.npt);
-        lo = scalar_load(rp);
-        n_iter = a.npt + scalar_load(rp + 1) - lo;
-        tl = a.tlist + bh * (int64_t)a.nvt * a.keep + lo - a.npt;
+        const int64_t* rp = a.rowp + bh * a.nvt + (kt - a.npt);
+        const int64_t b0 = min(scalar_load(rp), a.tcap), b1 = min(scalar_load(rp + 1), a.tcap);
+        n_iter = a.npt + (int)(b1 - b0);
+        tl = a.tlist + b0 - a.npt;
     }
     auto tile_of = [&](int n) -> int {
         if (n < a.npt || kt < a.npt) return n;
@@ -925,7 +947,7 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
         const unsigned g = (unsigned)((vt + 255) / 256);
         hipLaunchKernelGGL(bwd_mask_kernel, dim3(g), dim3(256), 0, s, a);
         hipLaunchKernelGGL(bwd_tcount_kernel, dim3(g), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(bwd_tscan_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_tscan_kernel, dim3(1), dim3(1024), 0, s, a);
         hipLaunchKernelGGL(bwd_tfill_kernel, dim3(g), dim3(256), 0, s, a);
     }
     const int64_t tiles = (int64_t)a.BH * (a.npt + a.nvt);

@@ -122,7 +122,9 @@ struct BwdLayout {
     int mwords;
 };
 
-BwdLayout bwd_layout(const Geo& g) {
+// tcap: entries of the transposed lists (B*H*nVT*k for fixed keep, the CSR
+// column count for variable lists)
+BwdLayout bwd_layout(const Geo& g, int64_t tcap) {
     BwdLayout L{};
     const size_t t = align_up((size_t)g.BH * g.n_tot * g.D * 2);
     size_t o = 0;
@@ -141,9 +143,9 @@ BwdLayout bwd_layout(const Geo& g) {
     L.cnt = o;
     o += align_up((size_t)g.BH * g.nvt * sizeof(int32_t));
     L.rowp = o;
-    o += align_up((size_t)g.BH * (g.nvt + 1) * sizeof(int32_t));
+    o += align_up((size_t)(g.BH * g.nvt + 1) * sizeof(int64_t));
     L.tlist = o;
-    o += align_up((size_t)g.BH * g.nvt * g.k * sizeof(int32_t));
+    o += align_up((size_t)tcap * sizeof(int32_t));
     L.progress = o;
     o += align_up((size_t)bsa::backward_progress_ints() * sizeof(int));
     L.total = o;
@@ -473,25 +475,41 @@ bsa_status bsa_backward_workspace_size(const bsa_desc* desc, size_t* bytes) {
     Geo g;
     const bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
-    *bytes = bwd_layout(g).total;
+    *bytes = bwd_layout(g, g.BH * g.nvt * g.k).total;
     return BSA_OK;
 }
 
-bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, const void* v, const void* o,
-                        const void* d_o, const float* lse, const int32_t* perm, const int32_t* block_idx, void* dq,
-                        void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+bsa_status bsa_backward_csr_workspace_size(const bsa_desc* desc, int64_t col_entries, size_t* bytes) {
+    if (!bytes) return BSA_ERR_NULL;
+    Geo g;
+    const bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (col_entries < 0) return BSA_ERR_SHAPE;
+    *bytes = bwd_layout(g, g.nvt > 0 ? col_entries : 0).total;
+    return BSA_OK;
+}
+
+namespace {
+
+// The backward over fixed-keep lists (row_ptr null) or CSR lists.
+bsa_status backward_impl(const bsa_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                         const void* d_o, const float* lse, const int32_t* perm, const int32_t* idx,
+                         const int64_t* row_ptr, int64_t col_entries, bool csr, void* dq, void* dk, void* dv,
+                         void* ws, size_t ws_bytes, void* stream) {
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
     if (g.npt + g.nvt > BSA_MAX_TILES || g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
     if (g.empty) return BSA_OK;
     if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return BSA_ERR_NULL;
-    if (g.nvt > 0 && (!perm || !block_idx)) return BSA_ERR_NULL;
+    if (g.nvt > 0 && (!perm || !idx || (csr && !row_ptr))) return BSA_ERR_NULL;
+    if (csr && g.nvt > 0 && col_entries < 1) return BSA_ERR_SHAPE;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(d_o, 16) ||
         misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(lse, 4) ||
-        misaligned(perm, 4) || misaligned(block_idx, 4))
+        misaligned(perm, 4) || misaligned(idx, 4) || misaligned(row_ptr, 8))
         return BSA_ERR_ALIGN;
-    const BwdLayout L = bwd_layout(g);
+    const int64_t tcap = g.nvt == 0 ? 0 : csr ? col_entries : g.BH * g.nvt * g.k;
+    const BwdLayout L = bwd_layout(g, tcap);
     if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
     if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -524,7 +542,9 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.o = static_cast<const uint16_t*>(o);
     a.dout = static_cast<const uint16_t*>(d_o);
     a.lse = lse;
-    a.idx = block_idx;
+    a.idx = idx;
+    a.row_ptr = csr && g.nvt > 0 ? row_ptr : nullptr;
+    a.col_entries = col_entries;
     a.perm = perm;
     a.lse2 = reinterpret_cast<float*>(w + L.lse2);
     a.delta = reinterpret_cast<float*>(w + L.delta);
@@ -532,8 +552,9 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.ndelta = reinterpret_cast<float*>(w + L.ndelta);
     a.mask = reinterpret_cast<uint32_t*>(w + L.mask);
     a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
-    a.rowp = reinterpret_cast<int32_t*>(w + L.rowp);
+    a.rowp = reinterpret_cast<int64_t*>(w + L.rowp);
     a.tlist = reinterpret_cast<int32_t*>(w + L.tlist);
+    a.tcap = tcap;
     a.progress = reinterpret_cast<int*>(w + L.progress);
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
@@ -551,6 +572,23 @@ bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, cons
     a.scale = desc->scale;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_backward(a, (int)g.D, s));
+}
+
+}  // namespace
+
+bsa_status bsa_backward(const bsa_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                        const void* d_o, const float* lse, const int32_t* perm, const int32_t* block_idx, void* dq,
+                        void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+    return backward_impl(desc, q, k, v, o, d_o, lse, perm, block_idx, nullptr, 0, false, dq, dk, dv, ws, ws_bytes,
+                         stream);
+}
+
+bsa_status bsa_backward_csr(const bsa_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                            const void* d_o, const float* lse, const int32_t* perm, const int64_t* row_ptr,
+                            const int32_t* col_idx, int64_t col_entries, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream) {
+    return backward_impl(desc, q, k, v, o, d_o, lse, perm, col_idx, row_ptr, col_entries, true, dq, dk, dv, ws,
+                         ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -152,12 +152,17 @@ struct BackwardArgs {
     const uint16_t *q_t, *do_t;  // tiled [BH][Ntot][D]
     const uint16_t *o, *dout;  // raster [B][Ntot][H][D]
     const float* lse;          // [BH][Ntot] natural log, tiled order
-    const int32_t* idx;        // [BH][nvt][keep]
+    const int32_t* idx;        // [BH][nvt][keep], or CSR column indices when row_ptr is set
+    const int64_t* row_ptr;    // CSR row pointers [BH * nvt + 1], or null (fixed keep)
+    int64_t col_entries;       // CSR: entries of idx (list bounds are clamped to it)
     const int32_t* perm;       // [B][Nvideo], -1 for a padding slot
     float *lse2, *delta;       // [BH][Ntot] scratch: lse * log2 e, dO . O
     float *nlse, *ndelta;      // [BH][Ntot] scratch: -lse / scale, -(dO . O)
     uint32_t* mask;            // [BH][nvt][mwords] scratch
-    int32_t *cnt, *rowp, *tlist;  // [BH][nvt], [BH][nvt + 1], [BH][nvt * keep] scratch
+    int32_t* cnt;              // [BH][nvt] scratch: query tiles that kept each key tile
+    int64_t* rowp;             // [BH * nvt + 1] scratch: exclusive prefix sums of cnt
+    int32_t* tlist;            // [tcap] scratch: the transposed lists, (bh, key tile) order
+    int64_t tcap;              // entries of tlist
     uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]
     int* progress;             // backward_progress_ints() ints: grouped-launch round counters
     int BH, H, npt, nvt, keep, mwords;

@@ -301,13 +301,32 @@ bsa_status bsa_backward(const bsa_desc *desc, const void *q, const void *k, cons
                         const int32_t *block_idx, void *dq, void *dk, void *dv, void *ws,
                         size_t ws_bytes, void *stream);
 
+/*
+ * The backward over CSR kept lists (bsa_plan_csr / bsa_plan_structured,
+ * consumed by bsa_forward_csr): the same gradients as bsa_backward, with
+ * video query tile i of (b, h) keeping the video tiles
+ * col_idx[row_ptr[r] .. row_ptr[r+1]), r = (b*H + h)*nVT + i, clamped as
+ * bsa_forward_csr clamps them.  The transposed lists take col_entries int32
+ * of workspace: bsa_backward_csr_workspace_size(desc, col_entries) gives the
+ * size.  row_ptr must be non-decreasing from 0 with distinct entries per row
+ * (as the planners write it); other lists stay memory-safe but their
+ * gradients are unspecified.  Other arguments, layouts and errors as
+ * bsa_backward (row_ptr 8-byte aligned; col_entries < 1 with video:
+ * BSA_ERR_SHAPE).
+ */
+bsa_status bsa_backward_csr_workspace_size(const bsa_desc *desc, int64_t col_entries, size_t *bytes);
+bsa_status bsa_backward_csr(const bsa_desc *desc, const void *q, const void *k, const void *v,
+                            const void *o, const void *d_o, const float *lse, const int32_t *perm,
+                            const int64_t *row_ptr, const int32_t *col_idx, int64_t col_entries,
+                            void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *bsa_status_string(bsa_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 800
+#define BSA_VERSION 900
 
 #ifdef __cplusplus
 }

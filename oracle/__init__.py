@@ -93,6 +93,12 @@ def lib() -> ctypes.CDLL:
         L.orc_attention_backward_dkdv_padded.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i32, P,
                                                           P]
         L.orc_attention_backward_dkdv_padded.restype = None
+        L.orc_attention_lse_delta_csr.argtypes = [P, P, P, P, i32, i32, i32, P, P, f64, P, P]
+        L.orc_attention_lse_delta_csr.restype = None
+        L.orc_attention_backward_dq_csr.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P, f64, P, i32, P]
+        L.orc_attention_backward_dq_csr.restype = None
+        L.orc_attention_backward_dkdv_csr.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P, f64, P, i32, P, P]
+        L.orc_attention_backward_dkdv_csr.restype = None
         _lib = L
     return _lib
 
@@ -574,6 +580,78 @@ def backward_full_padded(q_tiled, k_tiled, v_tiled, do_tiled, n_prefix: int, idx
             lse, delta = lse_delta_padded(*args, n_prefix, ix, real[b], scale)
             dq[b, h] = backward_dq_padded(*args, lse, delta, n_prefix, ix, real[b], scale, tiles).reshape(Ntot, D)
             g_k, g_v = backward_dkdv_padded(*args, lse, delta, n_prefix, ix, real[b], scale, tiles)
+            dk[b, h] = g_k.reshape(Ntot, D)
+            dv[b, h] = g_v.reshape(Ntot, D)
+    return dq, dk, dv
+
+
+# ---- gradients over CSR kept lists -------------------------------------------------
+
+def _csr_args(q_bh, k_bh, v_bh, do_bh, n_prefix, row_ptr_bh, col):
+    q, kx, v, do = (_c(x, np.uint16) for x in (q_bh, k_bh, v_bh, do_bh))
+    Ntot, D = q.shape
+    nvt = (Ntot - n_prefix) // TILE
+    rp = _c(row_ptr_bh, np.int64) if nvt else np.zeros(1, np.int64)
+    cl = _c(col, np.int32) if len(col) else np.zeros(1, np.int32)
+    return q, kx, v, do, Ntot, D, nvt, rp, cl
+
+
+def lse_delta_csr(q_bh, k_bh, v_bh, do_bh, n_prefix: int, row_ptr_bh, col, scale: float):
+    """As ``lse_delta`` over CSR lists of one (b,h) (``row_ptr_bh`` ``[nvt + 1]``
+    into ``col``)."""
+    q, kx, v, do, Ntot, D, nvt, rp, cl = _csr_args(q_bh, k_bh, v_bh, do_bh, n_prefix, row_ptr_bh, col)
+    lse = np.empty(Ntot, np.float64)
+    delta = np.empty(Ntot, np.float64)
+    lib().orc_attention_lse_delta_csr(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), n_prefix, nvt, D, _ptr(rp), _ptr(cl),
+                                      float(scale), _ptr(lse), _ptr(delta))
+    return lse, delta
+
+
+def backward_dq_csr(q_bh, k_bh, v_bh, do_bh, lse, delta, n_prefix: int, row_ptr_bh, col, scale: float, qtiles):
+    """As ``backward_dq`` over CSR lists of one (b,h)."""
+    q, kx, v, do, Ntot, D, nvt, rp, cl = _csr_args(q_bh, k_bh, v_bh, do_bh, n_prefix, row_ptr_bh, col)
+    qt = _c(qtiles, np.int32)
+    out = np.empty((qt.shape[0], TILE, D), np.float64)
+    lib().orc_attention_backward_dq_csr(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), _ptr(_c(lse, np.float64)),
+                                        _ptr(_c(delta, np.float64)), n_prefix, nvt, D, _ptr(rp), _ptr(cl),
+                                        float(scale), _ptr(qt), qt.shape[0], _ptr(out))
+    return out
+
+
+def backward_dkdv_csr(q_bh, k_bh, v_bh, do_bh, lse, delta, n_prefix: int, row_ptr_bh, col, scale: float, ktiles):
+    """As ``backward_dkdv`` over CSR lists of one (b,h)."""
+    q, kx, v, do, Ntot, D, nvt, rp, cl = _csr_args(q_bh, k_bh, v_bh, do_bh, n_prefix, row_ptr_bh, col)
+    kt = _c(ktiles, np.int32)
+    dk = np.empty((kt.shape[0], TILE, D), np.float64)
+    dv = np.empty((kt.shape[0], TILE, D), np.float64)
+    lib().orc_attention_backward_dkdv_csr(_ptr(q), _ptr(kx), _ptr(v), _ptr(do), _ptr(_c(lse, np.float64)),
+                                          _ptr(_c(delta, np.float64)), n_prefix, nvt, D, _ptr(rp), _ptr(cl),
+                                          float(scale), _ptr(kt), kt.shape[0], _ptr(dk), _ptr(dv))
+    return dk, dv
+
+
+def backward_full_csr(q_tiled, k_tiled, v_tiled, do_tiled, n_prefix: int, row_ptr, col, scale: float):
+    """Gradients of every (b,h) over CSR lists (``row_ptr`` int64 ``[B*H*nvt + 1]``
+    and ``col`` as ``plan_csr`` returns them), tiled order: ``(dq, dk, dv)``
+    float64 ``[B,H,Ntot,D]``."""
+    B, H, Ntot, D = q_tiled.shape
+    nvt = (Ntot - n_prefix) // TILE
+    tiles = np.arange(Ntot // TILE, dtype=np.int32)
+    dq = np.empty((B, H, Ntot, D), np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    for b in range(B):
+        for h in range(H):
+            r0 = (b * H + h) * nvt
+            if nvt:
+                rp = np.asarray(row_ptr[r0:r0 + nvt + 1], np.int64) - row_ptr[r0]
+                cl = col[row_ptr[r0]:row_ptr[r0 + nvt]]
+            else:
+                rp, cl = np.zeros(1, np.int64), np.zeros(0, np.int32)
+            args = (q_tiled[b, h], k_tiled[b, h], v_tiled[b, h], do_tiled[b, h])
+            lse, delta = lse_delta_csr(*args, n_prefix, rp, cl, scale)
+            dq[b, h] = backward_dq_csr(*args, lse, delta, n_prefix, rp, cl, scale, tiles).reshape(Ntot, D)
+            g_k, g_v = backward_dkdv_csr(*args, lse, delta, n_prefix, rp, cl, scale, tiles)
             dk[b, h] = g_k.reshape(Ntot, D)
             dv[b, h] = g_v.reshape(Ntot, D)
     return dq, dk, dv

@@ -1105,3 +1105,150 @@ void orc_attention_backward_dkdv_padded(const uint16_t *q, const uint16_t *kx, c
         }
     }
 }
+
+/*
+ * Gradients over CSR kept lists (variable keep per head or per query tile):
+ * the derivative of orc_attention_csr with the lists fixed, in the steps of
+ * orc_attention_lse_delta / orc_attention_backward_dq / _dkdv, with video
+ * query tile i keeping the video tiles col[row_ptr[i] .. row_ptr[i+1]).
+ */
+static int64_t key_list_csr(int qt, int n_prefix, int nvt, const int64_t *row_ptr, const int32_t *col,
+                            int64_t *keys)
+{
+    const int npt = n_prefix / TILE;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+    int64_t c = 0;
+    if (qt < npt) {
+        for (int64_t j = 0; j < Ntot; ++j)
+            keys[c++] = j;
+        return c;
+    }
+    const int i = qt - npt;
+    for (int64_t j = 0; j < n_prefix; ++j)
+        keys[c++] = j;
+    for (int64_t t = row_ptr[i]; t < row_ptr[i + 1]; ++t) {
+        const int64_t base = n_prefix + (int64_t)col[t] * TILE;
+        for (int r = 0; r < TILE; ++r)
+            keys[c++] = base + r;
+    }
+    return c;
+}
+
+static int attends_csr(int qt, int kt, int npt, const int64_t *row_ptr, const int32_t *col)
+{
+    if (qt < npt || kt < npt)
+        return 1;
+    for (int64_t t = row_ptr[qt - npt]; t < row_ptr[qt - npt + 1]; ++t)
+        if (col[t] == kt - npt)
+            return 1;
+    return 0;
+}
+
+void orc_attention_lse_delta_csr(const uint16_t *q, const uint16_t *kx, const uint16_t *v, const uint16_t *dout,
+                                 int n_prefix, int nvt, int D, const int64_t *row_ptr, const int32_t *col,
+                                 double scale, double *lse, double *delta)
+{
+    const int npt = n_prefix / TILE;
+    const int ntiles = npt + nvt;
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int qt = 0; qt < ntiles; ++qt) {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)Ntot);
+        double *z = (double *)malloc(sizeof(double) * (size_t)Ntot);
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+        const int64_t nk = key_list_csr(qt, n_prefix, nvt, row_ptr, col, keys);
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                z[j] = scale * dot_bf16(q + qi * D, kx + keys[j] * D, D);
+                if (z[j] > mx)
+                    mx = z[j];
+            }
+            double den = 0.0;
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const double w = exp(z[j] - mx);
+                den += w;
+                for (int d = 0; d < D; ++d)
+                    o[d] += w * bf16_to_double(v[keys[j] * D + d]);
+            }
+            double dl = 0.0;
+            for (int d = 0; d < D; ++d)
+                dl += bf16_to_double(dout[qi * D + d]) * (o[d] / den);
+            lse[qi] = mx + log(den);
+            delta[qi] = dl;
+        }
+        free(keys);
+        free(z);
+        free(o);
+    }
+}
+
+void orc_attention_backward_dq_csr(const uint16_t *q, const uint16_t *kx, const uint16_t *v, const uint16_t *dout,
+                                   const double *lse, const double *delta, int n_prefix, int nvt, int D,
+                                   const int64_t *row_ptr, const int32_t *col, double scale, const int32_t *qtiles,
+                                   int nq, double *dq)
+{
+    const int64_t Ntot = n_prefix + (int64_t)nvt * TILE;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nq; ++a) {
+        const int qt = qtiles[a];
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)Ntot);
+        const int64_t nk = key_list_csr(qt, n_prefix, nvt, row_ptr, col, keys);
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t qi = (int64_t)qt * TILE + r;
+            double *g = dq + ((int64_t)a * TILE + r) * D;
+            for (int d = 0; d < D; ++d)
+                g[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                const uint16_t *kr = kx + keys[j] * D;
+                const double p = exp(scale * dot_bf16(q + qi * D, kr, D) - lse[qi]);
+                const double dp = dot_bf16(dout + qi * D, v + keys[j] * D, D);
+                const double ds = p * (dp - delta[qi]);
+                for (int d = 0; d < D; ++d)
+                    g[d] += ds * bf16_to_double(kr[d]);
+            }
+            for (int d = 0; d < D; ++d)
+                g[d] *= scale;
+        }
+        free(keys);
+    }
+}
+
+void orc_attention_backward_dkdv_csr(const uint16_t *q, const uint16_t *kx, const uint16_t *v, const uint16_t *dout,
+                                     const double *lse, const double *delta, int n_prefix, int nvt, int D,
+                                     const int64_t *row_ptr, const int32_t *col, double scale,
+                                     const int32_t *ktiles, int nk, double *dk, double *dv)
+{
+    const int npt = n_prefix / TILE;
+    const int ntiles = npt + nvt;
+#pragma omp parallel for schedule(dynamic)
+    for (int a = 0; a < nk; ++a) {
+        const int kt = ktiles[a];
+        for (int r = 0; r < TILE; ++r) {
+            const int64_t kj = (int64_t)kt * TILE + r;
+            double *gk = dk + ((int64_t)a * TILE + r) * D;
+            double *gv = dv + ((int64_t)a * TILE + r) * D;
+            for (int d = 0; d < D; ++d)
+                gk[d] = gv[d] = 0.0;
+            for (int qt = 0; qt < ntiles; ++qt) {
+                if (!attends_csr(qt, kt, npt, row_ptr, col))
+                    continue;
+                for (int s = 0; s < TILE; ++s) {
+                    const int64_t qi = (int64_t)qt * TILE + s;
+                    const double p = exp(scale * dot_bf16(q + qi * D, kx + kj * D, D) - lse[qi]);
+                    const double dp = dot_bf16(dout + qi * D, v + kj * D, D);
+                    const double ds = p * (dp - delta[qi]);
+                    for (int d = 0; d < D; ++d) {
+                        gk[d] += ds * bf16_to_double(q[qi * D + d]);
+                        gv[d] += p * bf16_to_double(dout[qi * D + d]);
+                    }
+                }
+            }
+            for (int d = 0; d < D; ++d)
+                gk[d] *= scale;
+        }
+    }
+}

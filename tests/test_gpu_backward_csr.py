@@ -1,0 +1,177 @@
+"""GPU parity of the backward over CSR kept lists (bsa_backward_csr): lists
+of their own length per head and per query tile (bsa_plan_csr) and
+structured spatial / temporal lists (bsa_plan_structured), against the
+oracle's fp64 gradients over the same lists, with the backward's tolerances
+(max |err| <= 2e-2 max |ref|, mean |err| <= 1e-2 mean |ref| per tensor).
+A CSR call whose rows all keep k tiles reproduces bsa_backward bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_39_amd as bsa
+import oracle
+import synthetic as S
+from parity import GpuRun, bits_to_f64, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = S.Workload
+RTOL_MAX = 2e-2
+RTOL_MEAN = 1e-2
+
+
+def check_grad(got, ref, what):
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    ref_mx, ref_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    print(f"[{what}] max|err| {mx:.3e} (ref max {ref_mx:.3e}), mean|err| {mean:.3e} (ref mean {ref_mean:.3e})",
+          flush=True)
+    assert np.isfinite(got).all(), what
+    assert mx <= RTOL_MAX * ref_mx + 1e-6, what
+    assert mean <= RTOL_MEAN * ref_mean + 1e-7, what
+
+
+def csr_forward_backward(g, row_ptr, col, do):
+    """The CSR forward (for its lse and O) and the CSR backward, on the GPU."""
+    a, d = g.att, g.desc
+    o_t = torch.empty_like(a.q_t)
+    lse = torch.empty_like(a.lse)
+    bsa.forward_csr(d, a.q_t, a.k_f, a.v_f, row_ptr, col, o_t, lse, workspace=a.workspace)
+    out = torch.empty_like(g.q)
+    bsa.scatter(d, o_t, out, a.perm)
+    dq, dk, dv = (torch.empty_like(g.q) for _ in range(3))
+    ws = torch.empty(max(bsa.backward_csr_workspace_size(d, col.numel()), 256), dtype=torch.uint8, device="cuda")
+    bsa.backward_csr(d, g.q, g.k, g.v, out, to_dev(do), lse, a.perm, row_ptr, col, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+CASES = [
+    (W("bcsr_heads", 1, 3, 128, (8, 8, 16), 8, seed=61), [8, 3, 16], None),
+    (W("bcsr_rows_d64", 2, 2, 64, (8, 8, 12), 6, seed=62), [6, 11], (-1, 13)),
+    (W("bcsr_prefix", 1, 2, 128, (8, 8, 12), 4, seed=63, n_prefix=128), [4, 1], (0, 5)),
+]
+
+
+@pytest.mark.parametrize("wl,keep_h,rows_range", CASES, ids=[c[0].name for c in CASES])
+def test_backward_csr_matches_oracle(wl, keep_h, rows_range):
+    print(f"\n[case] {wl} keep_per_head={keep_h} rows={rows_range}", flush=True)
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    n = wl.n_video_tiles
+    keep_rows = None
+    if rows_range is not None:
+        rng = np.random.default_rng(wl.seed + 100)
+        keep_rows = torch.from_numpy(rng.integers(rows_range[0], rows_range[1] + 1,
+                                                  size=(wl.batch, wl.heads, n)).astype(np.int32)).cuda()
+    row_ptr = torch.empty(wl.batch * wl.heads * n + 1, dtype=torch.int64, device="cuda")
+    col = torch.empty(bsa.csr_entries(g.desc, keep_h), dtype=torch.int32, device="cuda")
+    bsa.plan_csr(g.desc, g.att.q_t, g.att.k_f, row_ptr, col, g.att.workspace, keep_per_head=keep_h,
+                 keep_rows=keep_rows)
+    grads = csr_forward_backward(g, row_ptr, col, do)
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    perm = g.perm()
+    tiled = [oracle.gather(x, perm, npf) for x in (q, k, v, do)]
+    ref = oracle.backward_full_csr(*tiled, npf, row_ptr.cpu().numpy(), col.cpu().numpy(), scale)
+    for name, dev, r in zip(("dq", "dk", "dv"), grads, ref):
+        check_grad(bits_to_f64(oracle.gather(to_bits(dev), perm, npf)), r, name)
+
+
+def test_backward_structured_matches_oracle():
+    wl = W("bcsr_structured", 1, 2, 128, (12, 8, 16), 4, seed=64, n_prefix=64)
+    print(f"\n[case] {wl} spatial/temporal radius 1/1", flush=True)
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    mask = [bsa.MASK_SPATIAL, bsa.MASK_TEMPORAL]
+    n_ent = bsa.structured_entries(g.desc, mask, 1, 1)
+    row_ptr = torch.empty(wl.batch * wl.heads * wl.n_video_tiles + 1, dtype=torch.int64, device="cuda")
+    col = torch.empty(n_ent, dtype=torch.int32, device="cuda")
+    bsa.plan_structured(g.desc, mask, 1, 1, row_ptr, col)
+    grads = csr_forward_backward(g, row_ptr, col, do)
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    perm = g.perm()
+    tiled = [oracle.gather(x, perm, npf) for x in (q, k, v, do)]
+    ref = oracle.backward_full_csr(*tiled, npf, row_ptr.cpu().numpy(), col.cpu().numpy(), scale)
+    for name, dev, r in zip(("dq", "dk", "dv"), grads, ref):
+        check_grad(bits_to_f64(oracle.gather(to_bits(dev), perm, npf)), r, name)
+
+
+def test_uniform_csr_backward_equals_fixed_keep():
+    wl = W("bcsr_uniform", 2, 2, 128, (8, 8, 16), 5, seed=65, n_prefix=64)
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    n = wl.n_video_tiles
+    idx = g.att.block_idx[:, :, :n, :wl.keep_tiles].contiguous()
+    row_ptr = (torch.arange(wl.batch * wl.heads * n + 1, dtype=torch.int64) * wl.keep_tiles).cuda()
+    col = idx.reshape(-1)
+    d_csr = csr_forward_backward(g, row_ptr, col, do)
+    d_fix = [torch.empty_like(g.q) for _ in range(3)]
+    ws = torch.empty(bsa.backward_workspace_size(g.desc), dtype=torch.uint8, device="cuda")
+    bsa.backward(g.desc, g.q, g.k, g.v, g.out, to_dev(do), g.att.lse, g.att.perm, g.att.block_idx, *d_fix, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(d_csr, d_fix):
+        assert np.array_equal(to_bits(a), to_bits(b))
+
+
+def test_prism720p_backward_csr_sampled():
+    """Full size (grid 32x48x80, batch 2, 24 heads, head_dim 128) with the
+    heads keeping 480, 192, 120 and 96 tiles in turn: dQ of sampled query
+    tiles from the oracle; dK, dV of sampled key tiles from the oracle's
+    derivative with the GPU forward's lse and Delta from its bf16 output."""
+    wl = S.WORKLOADS["prism720p"]
+    keep_h = [(480, 192, 120, 96)[h % 4] for h in range(wl.heads)]
+    print(f"\n[case] {wl} keep_per_head={keep_h}", flush=True)
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    a, d = g.att, g.desc
+    n = wl.n_video_tiles
+    row_ptr = torch.empty(wl.batch * wl.heads * n + 1, dtype=torch.int64, device="cuda")
+    col = torch.empty(bsa.csr_entries(d, keep_h), dtype=torch.int32, device="cuda")
+    bsa.plan_csr(d, a.q_t, a.k_f, row_ptr, col, a.workspace, keep_per_head=keep_h)
+    o_t = torch.empty_like(a.q_t)
+    lse = torch.empty_like(a.lse)
+    bsa.forward_csr(d, a.q_t, a.k_f, a.v_f, row_ptr, col, o_t, lse, workspace=a.workspace)
+    out = torch.empty_like(g.q)
+    bsa.scatter(d, o_t, out, a.perm)
+    grads = [torch.empty_like(g.q) for _ in range(3)]
+    ws = torch.empty(bsa.backward_csr_workspace_size(d, col.numel()), dtype=torch.uint8, device="cuda")
+    bsa.backward_csr(d, g.q, g.k, g.v, out, to_dev(do), lse, a.perm, row_ptr, col, *grads, ws)
+    torch.cuda.synchronize()
+    print("[gpu] backward done", flush=True)
+    del ws
+    npf, scale = wl.n_prefix, float(np.float32(wl.scale))
+    perm = g.perm()
+    nqt = wl.n_tokens // 64
+    rp_all, col_all = row_ptr.cpu().numpy(), col.cpu().numpy()
+    lse_gpu = lse.cpu().numpy()
+    rng = np.random.default_rng(92)
+    for b, h in [(0, 1), (1, 3)]:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        qt, kt, vt, dot = (oracle.gather(sl(x), perm[b:b + 1], npf)[0, 0] for x in (q, k, v, do))
+        ot = bits_to_f64(to_bits(o_t[b, h]))
+        gt = [bits_to_f64(oracle.gather(to_bits(x[b:b + 1, :, h:h + 1]), perm[b:b + 1], npf)[0, 0])
+              .reshape(nqt, 64, wl.head_dim) for x in grads]
+        r0 = (b * wl.heads + h) * n
+        rp = rp_all[r0:r0 + n + 1] - rp_all[r0]
+        cl = col_all[rp_all[r0]:rp_all[r0 + n]]
+        qtiles = np.sort(rng.choice(nqt, size=4, replace=False)).astype(np.int32)
+        o_ref, lse_ref = oracle.attention_csr(qt, kt, vt, npf, rp, cl, scale, qtiles)
+        lse_v = np.zeros(wl.n_tokens)
+        delta = np.zeros(wl.n_tokens)
+        rows = (qtiles[:, None] * 64 + np.arange(64)).reshape(-1)
+        lse_v[rows] = lse_ref.reshape(-1)
+        delta[rows] = (o_ref.reshape(-1, wl.head_dim) * bits_to_f64(dot)[rows]).sum(1)
+        ref_dq = oracle.backward_dq_csr(qt, kt, vt, dot, lse_v, delta, npf, rp, cl, scale, qtiles)
+        check_grad(gt[0][qtiles], ref_dq, f"dq b{b} h{h} k={keep_h[h]}")
+        ktiles = np.sort(rng.choice(nqt, size=2, replace=False)).astype(np.int32)
+        ref_dk, ref_dv = oracle.backward_dkdv_csr(qt, kt, vt, dot, lse_gpu[b, h].astype(np.float64),
+                                                  (ot * bits_to_f64(dot)).sum(1), npf, rp, cl, scale, ktiles)
+        check_grad(gt[1][ktiles], ref_dk, f"dk b{b} h{h}")
+        check_grad(gt[2][ktiles], ref_dv, f"dv b{b} h{h}")
+    del g, grads
+    torch.cuda.empty_cache()

@@ -6,6 +6,8 @@ query tile, in CSR form).
   scaled_dot_product_attention in float64 under an explicit token-by-token
   mask built from the lists (prefix rows dense, video rows see the prefix and
   their kept tiles -- Ref2VA VSA page, section on conditioning tokens).
+* Gradients: uniform rows give the fixed-keep gradients bit for bit; rows of
+  different lengths match torch autograd through the masked fp64 attention.
 * Selection: each row holds the k_row tiles a stable descending sort of its
   exact float64 scores puts first (lowest tile number first among equal
   scores -- the reading of the tie rule), ascending; the counts are the
@@ -119,3 +121,42 @@ def test_selection_ties_and_nesting(orc):
         lists[k] = [set(c[rp[i]:rp[i + 1]]) for i in range(16)]
     for a, b in ((1, 4), (4, 9), (9, 16)):
         assert all(x <= y for x, y in zip(lists[a], lists[b]))
+
+
+# ---- gradients over CSR lists ---------------------------------------------------
+
+def test_csr_gradients_uniform_rows_equal_fixed_keep(orc):
+    rng = np.random.default_rng(75)
+    B, H, D, npf, nvt, k = 1, 2, 16, 64, 5, 3
+    N = npf + nvt * 64
+    q, kx, v, do = (_rand(rng, B * H * N, D).reshape(B, H, N, D) for _ in range(4))
+    idx = np.stack([np.stack([np.sort(rng.choice(nvt, size=k, replace=False)) for _ in range(nvt)])
+                    for _ in range(B * H)]).reshape(B, H, nvt, k).astype(np.int32)
+    row_ptr = np.arange(B * H * nvt + 1, dtype=np.int64) * k
+    g1 = orc.backward_full(q, kx, v, do, npf, idx, 0.3)
+    g2 = orc.backward_full_csr(q, kx, v, do, npf, row_ptr, idx.reshape(-1), 0.3)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("D,npf,nvt", [(8, 0, 6), (16, 128, 4)])
+def test_csr_gradients_match_masked_autograd(orc, D, npf, nvt):
+    """Rows of different lengths: torch autograd through fp64 SDPA under the
+    token mask of the lists, loss = sum of O * dO."""
+    rng = np.random.default_rng(76 + D)
+    N = npf + nvt * 64
+    q, kx, v, do = (_rand(rng, N, D, 1.5) for _ in range(4))
+    lens = rng.integers(1, nvt + 1, size=nvt)
+    row_ptr = np.zeros(nvt + 1, np.int64)
+    row_ptr[1:] = np.cumsum(lens)
+    col = np.concatenate([np.sort(rng.choice(nvt, size=n, replace=False)) for n in lens]).astype(np.int32)
+    scale = 0.25
+    got = orc.backward_full_csr(q[None, None], kx[None, None], v[None, None], do[None, None], npf, row_ptr, col,
+                                scale)
+    m = torch.from_numpy(_csr_mask(npf, nvt, row_ptr, col))
+    qq, kk, vv = (_f64(x).requires_grad_(True) for x in (q, kx, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qq[None, None], kk[None, None], vv[None, None],
+                                                           attn_mask=m[None, None], scale=scale)[0, 0]
+    (out * _f64(do)).sum().backward()
+    for g, r in zip(got, (qq.grad, kk.grad, vv.grad)):
+        np.testing.assert_allclose(g[0, 0], r.numpy(), rtol=0, atol=1e-11)

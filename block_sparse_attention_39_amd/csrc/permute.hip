@@ -35,6 +35,19 @@ __global__ void perm_static_kernel(int T, int Hg, int W, int tt, int th, int tw,
     }
 }
 
+// x, or zeros when t < 0 (a padding slot), by a bit mask rather than a
+// select, so that the load is not moved under a branch: the row loads of a
+// thread stay unconditional and in flight together.
+// kPad false: a grid of whole tiles, no padding slot and no masking.
+template <bool kPad>
+__device__ inline uint4 zero_if_padding(uint4 x, int64_t t) {
+    if (!kPad) return x;
+    const uint32_t m = ~(uint32_t)(t >> 63);  // t < 0: 0; else all ones
+    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+template <bool kPad>
+__device__ inline int64_t row_or_zero(int64_t t) { return kPad ? max(t, (int64_t)0) : t; }
+
 // raster token of tiled slot p (prefix first), or -1 for a padding slot
 __device__ inline int64_t slot_token(const int32_t* __restrict__ perm, int b, int64_t n_video, int n_prefix,
                                      int64_t p) {
@@ -49,7 +62,7 @@ __device__ inline int64_t slot_token(const int32_t* __restrict__ perm, int b, in
 // tiled tensor and touches 256-byte head rows of the raster tensor.
 // n_tot: tiled rows (padding slots included); n_ras: raster rows.  Gather
 // writes zeros to padding slots, scatter skips them.
-template <bool kToRaster>
+template <bool kToRaster, bool kPad>
 __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                            const int32_t* __restrict__ perm, int H, int C,
                                                            int n_prefix, int64_t n_video, int64_t n_tot,
@@ -67,11 +80,12 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
         const int h = it / (C * kTile);
         const int64_t tiled = (((int64_t)b * H + h) * n_tot + p0 + pl) * C + c;
         const int64_t t = tok[pl];
-        const int64_t raster = (((int64_t)b * n_ras + t) * H + h) * C + c;
+        // a padding slot (t < 0) reads a valid row and writes zeros
+        const int64_t raster = (((int64_t)b * n_ras + row_or_zero<kPad>(t)) * H + h) * C + c;
         if (kToRaster) {
-            if (t >= 0) dst[raster] = src[tiled];
+            if (!kPad || t >= 0) dst[raster] = src[tiled];
         } else {
-            dst[tiled] = t >= 0 ? src[raster] : make_uint4(0, 0, 0, 0);
+            dst[tiled] = zero_if_padding<kPad>(src[raster], t);
         }
     }
 }
@@ -85,6 +99,7 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
 // the tile's raster rows.
 __device__ inline int swap23(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+template <bool kPad>
 __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
                                                         int n_prefix, int64_t n_video, int64_t n_tot,
@@ -107,7 +122,7 @@ __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict_
         const int cc = 2 * s + (lane >> 5);
         const int64_t t = tok[r];
         dst[(((int64_t)b * H + h) * n_tiles + tile) * per_head + q] =
-            t >= 0 ? src[(((int64_t)b * n_ras + t) * H + h) * C + cc] : make_uint4(0, 0, 0, 0);
+            zero_if_padding<kPad>(src[(((int64_t)b * n_ras + row_or_zero<kPad>(t)) * H + h) * C + cc], t);
     }
 }
 
@@ -123,6 +138,7 @@ __device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu
 __device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 __device__ inline uint32_t word_of(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
 
+template <bool kPad>
 __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
                                                         int n_prefix, int64_t n_video, int64_t n_tot,
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
         uint4 r0, r1, r2, r3, r4, r5, r6, r7;
         auto row = [&](int i) {
             const int64_t t = tok[8 * g + i];
-            return t >= 0 ? src[(((int64_t)b * n_ras + t) * H + h) * C + dc] : make_uint4(0, 0, 0, 0);
+            return zero_if_padding<kPad>(src[(((int64_t)b * n_ras + row_or_zero<kPad>(t)) * H + h) * C + dc], t);
         };
         r0 = row(0); r1 = row(1); r2 = row(2); r3 = row(3);
         r4 = row(4); r5 = row(5); r6 = row(6); r7 = row(7);
@@ -179,8 +195,13 @@ hipError_t launch_gather_kf(const uint16_t* src, uint16_t* dst, const int32_t* p
     const int64_t n_tot = n_prefix + n_video;
     const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_kf_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
-                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot, n_ras);
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    if (n_ras != n_tot)  // a ragged grid: padding slots
+        hipLaunchKernelGGL(gather_kf_kernel<true>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H,
+                           D / 8, n_prefix, n_video, n_tot, n_ras);
+    else
+        hipLaunchKernelGGL(gather_kf_kernel<false>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H,
+                           D / 8, n_prefix, n_video, n_tot, n_ras);
     return hipGetLastError();
 }
 
@@ -189,8 +210,13 @@ hipError_t launch_gather_vf(const uint16_t* src, uint16_t* dst, const int32_t* p
     const int64_t n_tot = n_prefix + n_video;
     const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_vf_kernel, dim3((unsigned)(n_tot / kTile), (unsigned)B), dim3(256), 0, s,
-                       (const uint4*)src, (uint4*)dst, perm, H, D / 8, n_prefix, n_video, n_tot, n_ras);
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    if (n_ras != n_tot)
+        hipLaunchKernelGGL(gather_vf_kernel<true>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H,
+                           D / 8, n_prefix, n_video, n_tot, n_ras);
+    else
+        hipLaunchKernelGGL(gather_vf_kernel<false>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H,
+                           D / 8, n_prefix, n_video, n_tot, n_ras);
     return hipGetLastError();
 }
 
@@ -214,12 +240,11 @@ hipError_t launch_permute_copy(bool to_raster, const uint16_t* src, uint16_t* ds
     if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
     const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
     const int C = D / 8;
-    if (to_raster)
-        hipLaunchKernelGGL(permute_copy_kernel<true>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm,
-                           H, C, n_prefix, n_video, n_tot, n_ras);
-    else
-        hipLaunchKernelGGL(permute_copy_kernel<false>, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm,
-                           H, C, n_prefix, n_video, n_tot, n_ras);
+    const bool pad = n_ras != n_tot;
+    auto kernel = to_raster ? (pad ? permute_copy_kernel<true, true> : permute_copy_kernel<true, false>)
+                            : (pad ? permute_copy_kernel<false, true> : permute_copy_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H, C, n_prefix, n_video,
+                       n_tot, n_ras);
     return hipGetLastError();
 }
 

@@ -320,7 +320,7 @@ def bench_structured(args, wl, q, k, v):
         totals.append(ev[0].elapsed_time(ev[5]))
     ms_step = float(np.mean(totals))
     # every video query token attends the prefix and 64 keys per kept tile
-    pairs = wl.heads * wl.batch * (wl.n_prefix * wl.n_tokens + wl.n_video * wl.n_prefix)
+    pairs = wl.heads * wl.batch * (wl.n_prefix * wl.n_tiled_tokens + wl.n_video_slots * wl.n_prefix)
     pairs += entries * 64 * 64
     F = 4.0 * wl.head_dim * pairs
     fwd_ms = float(np.mean(per_stage["forward"]))
@@ -343,13 +343,67 @@ def bench_structured(args, wl, q, k, v):
                    "head_dim": wl.head_dim, "head_mask": "even spatial, odd temporal", "radius_t": rt,
                    "radius_hw": rs, "kept_entries": entries,
                    "mean_kept_tiles": entries / rows, "effective_tflop_per_call": F / 1e12},
-        "roofline": {"bound": "mfma", "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}> (CSR lists)",
+        "roofline": {"bound": "mfma",
+                     "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}> (CSR lists)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
         "wall_ms_per_step": wall * 1e3 / args.steps,
     }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        res["cpu_baseline"] = cpu_baseline_structured(wl, q, k, v, rt, rs, args.cpu_tiles)
+        print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_structured(wl, q, k, v, rt: int, rs: int, n_tiles: int):
+    """The oracle's structured path on one spatial and one temporal (batch,
+    head) slice: the lists over the whole tile grid, CSR attention on
+    `n_tiles` sampled query tiles, extrapolated linearly over the query tiles
+    and over the heads of each kind."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if wl.padded:
+        perm = oracle.perm_static_padded(wl.grid, wl.tile)[None]
+        gather = lambda x: oracle.gather_padded(x, perm, wl.n_prefix)
+    else:
+        perm = oracle.perm_static(wl.grid, wl.tile)[None]
+        gather = lambda x: oracle.gather(x, perm, wl.n_prefix)
+    tgrid = tuple(-(-g // t) for g, t in zip(wl.grid, wl.tile))
+    nqt = wl.n_tiled_tokens // 64
+    rng = np.random.default_rng(1357)
+    tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
+    scale = float(np.float32(wl.scale))
+    total_s, total_f, parts = 0.0, 0.0, []
+    for h, kind in ((0, 0), (1, 1)):
+        sl = lambda x: np.ascontiguousarray(x[0:1, :, h:h + 1])
+        t0 = time.perf_counter()
+        qt, kt, vt = (gather(sl(x)) for x in (q, k, v))
+        row_ptr, col = oracle.plan_structured(tgrid, [kind], rt, rs, 1)
+        t_plan = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        if wl.padded:
+            oracle.attention_padded_csr(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, row_ptr, col,
+                                        oracle.key_real(perm[0], wl.n_prefix), scale, tiles)
+        else:
+            oracle.attention_csr(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, row_ptr, col, scale, tiles)
+        t_attn = time.perf_counter() - t0
+        heads = sum(1 for x in range(wl.heads) if x % 2 == kind) * wl.batch
+        pairs = wl.n_prefix * wl.n_tiled_tokens + wl.n_video_slots * wl.n_prefix + int(row_ptr[-1]) * 64 * 64
+        total_s += (t_plan + t_attn * nqt / len(tiles)) * heads
+        total_f += 4.0 * wl.head_dim * pairs * heads
+        parts.append(f"{('spatial', 'temporal')[kind]}: lists {t_plan:.2f} s, attention on {len(tiles)} tiles "
+                     f"{t_attn:.2f} s")
+    return {
+        "value": total_f / total_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "ms_per_call_extrapolated": total_s * 1e3,
+        "sample": ("one spatial and one temporal (batch, head) slice of the same workload (" + "; ".join(parts) +
+                   f"), fp64, extrapolated linearly over the {nqt} query tiles and over the heads of each kind"),
+    }
 
 
 def cpu_baseline_backward(wl, q, k, v, do, n_tiles: int):

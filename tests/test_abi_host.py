@@ -226,3 +226,33 @@ def test_padded_mode_host_checks():
     assert L.bsa_structured_entries(ctypes.byref(ds), mask, 0, 0, ctypes.byref(e)) == OK
     rp, _ = oracle.plan_structured((2, 2, 2), [0, 1], 0, 0, 1)
     assert e.value == rp[-1]
+
+
+def test_backward_csr_host_checks():
+    """bsa_backward_csr: workspace sized on the CSR column count; missing
+    lists, an empty column array and a short workspace are refused before
+    anything is enqueued."""
+    L = lib()
+    d = cfg()                                   # 2 x 3 heads, 12 video tiles, k = 5
+    n = ctypes.c_size_t(0)
+    assert L.bsa_backward_csr_workspace_size(ctypes.byref(d), 100, ctypes.byref(n)) == OK
+    small = n.value
+    assert L.bsa_backward_csr_workspace_size(ctypes.byref(d), 1000, ctypes.byref(n)) == OK
+    assert n.value - small == (1000 * 4 + 255) // 256 * 256 - (100 * 4 + 255) // 256 * 256
+    assert L.bsa_backward_csr_workspace_size(ctypes.byref(d), -1, ctypes.byref(n)) == SHAPE
+    # with the fixed-keep count the two backward workspaces agree
+    fixed = ctypes.c_size_t(0)
+    assert L.bsa_backward_workspace_size(ctypes.byref(d), ctypes.byref(fixed)) == OK
+    assert L.bsa_backward_csr_workspace_size(ctypes.byref(d), 2 * 3 * 12 * 5, ctypes.byref(n)) == OK
+    assert n.value == fixed.value
+    ptrs = [FAKE] * 8                           # q k v o d_o lse perm | row_ptr col
+    assert L.bsa_backward_csr(ctypes.byref(d), *ptrs[:7], None, FAKE, 100, FAKE, FAKE, FAKE, FAKE, small,
+                              None) == NULL
+    assert L.bsa_backward_csr(ctypes.byref(d), *ptrs[:7], FAKE, None, 100, FAKE, FAKE, FAKE, FAKE, small,
+                              None) == NULL
+    assert L.bsa_backward_csr(ctypes.byref(d), *ptrs[:7], FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, small,
+                              None) == SHAPE
+    assert L.bsa_backward_csr(ctypes.byref(d), *ptrs[:7], FAKE + 4, FAKE, 100, FAKE, FAKE, FAKE, FAKE, small,
+                              None) == ALIGN
+    assert L.bsa_backward_csr(ctypes.byref(d), *ptrs[:7], FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, small - 1,
+                              None) == WS

@@ -88,8 +88,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
     if (!is_k) {
         constexpr int RPI = 64 / C;  // rows covered by one wave-wide load
         const int c = lane % C, r0 = lane / C;
+        uint4 x[kTile / RPI];  // every load in flight before the first sum
 #pragma unroll
-        for (int it = 0; it < kTile / RPI; ++it) acc8(acc, src[(r0 + it * RPI) * C + c]);
+        for (int it = 0; it < kTile / RPI; ++it) x[it] = src[(r0 + it * RPI) * C + c];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < kTile / RPI; ++it) acc8(acc, x[it]);
 #pragma unroll
         for (int o = C; o < 64; o <<= 1)
 #pragma unroll
@@ -98,12 +102,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
     } else {
         const int grp = lane / LPG, part = lane % LPG;
         const int s = grp >> 1, hf = grp & 1;
+        uint4 x[TPL];
 #pragma unroll
         for (int u = 0; u < TPL; ++u) {
             const int tok = part * TPL + u;  // 32 kh + m
             const int kh = tok >> 5, m = tok & 31;
-            acc8(acc, src[(kh * SD + s) * 64 + 32 * hf + m]);
+            x[u] = src[(kh * SD + s) * 64 + 32 * hf + m];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) acc8(acc, x[u]);
 #pragma unroll
         for (int o = 1; o < LPG; o <<= 1)
 #pragma unroll

@@ -243,21 +243,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, 
         __syncthreads();
     }
     // prefix is now the key of the k-th largest score; `need` of the keys equal
-    // to it are taken, lowest index first.
+    // to it are taken, lowest index first.  Each thread owns a contiguous run
+    // of indices, so two block scans (ties before the run, selected entries
+    // before the run) place its selections in ascending order.
     const uint32_t thr = prefix;
-    int taken = 0, ties = 0;
-    for (int j0 = 0; j0 < n; j0 += 256) {
-        const int j = j0 + threadIdx.x;
-        const uint32_t key = (j < n) ? keys[j] : 0u;
-        const int is_tie = (j < n && key == thr) ? 1 : 0;
-        int tie_tot;
-        const int tie_rank = block_scan_256(is_tie, wsum, &tie_tot) - is_tie + ties;
-        const int sel = (j < n) && (key > thr || (is_tie && tie_rank < need));
-        int sel_tot;
-        const int pos = block_scan_256(sel, wsum, &sel_tot) - sel + taken;
-        if (sel) out[pos] = j;
-        taken += sel_tot;
-        ties += tie_tot;
+    const int per = (n + 255) / 256;
+    const int j_lo = min((int)threadIdx.x * per, n), j_hi = min(j_lo + per, n);
+    int my_above = 0, my_ties = 0;
+    for (int j = j_lo; j < j_hi; ++j) {
+        const uint32_t key = keys[j];
+        my_above += key > thr;
+        my_ties += key == thr;
+    }
+    int tot;
+    const int ties_before = block_scan_256(my_ties, wsum, &tot) - my_ties;
+    const int my_take = my_above + min(max(need - ties_before, 0), my_ties);
+    int pos = block_scan_256(my_take, wsum, &tot) - my_take;
+    int tie_rank = ties_before;
+    for (int j = j_lo; j < j_hi; ++j) {
+        const uint32_t key = keys[j];
+        const bool tie = key == thr;
+        if (key > thr || (tie && tie_rank < need)) out[pos++] = j;
+        tie_rank += tie;
     }
 }
 

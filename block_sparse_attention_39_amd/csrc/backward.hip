@@ -102,9 +102,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
         }
     }
     a.delta[r] = s;
-    a.lse2[r] = a.lse[r] * kLog2e;
     a.ndelta[r] = -s;
-    a.nlse[r] = -a.lse[r] / a.scale;
+    if (tok >= 0) {
+        a.lse2[r] = a.lse[r] * kLog2e;
+        a.nlse[r] = -a.lse[r] / a.scale;
+    } else {  // a padding row carries no loss: every weight of it is exactly 0
+        a.lse2[r] = __builtin_inff();
+        a.nlse[r] = -__builtin_inff();
+    }
 }
 
 // ---- kept lists -------------------------------------------------------------

@@ -601,16 +601,16 @@ def main():
     out = torch.empty_like(qd)
     torch.cuda.synchronize()
 
-    stages = ["build", "gather", "plan", "forward", "scatter"]
+    stages = ["build", "gather_qk", "gather_v+plan", "forward", "scatter"]
 
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         mark(0)
         att.build(qd)
         mark(1)
-        att.gather_qkv(qd, kd, vd)
+        att.gather_qk(qd, kd)
         mark(2)
-        att.plan()
+        att.gather_v_and_plan(vd)  # the V gather on a side stream, beside the plan
         mark(3)
         att.forward()
         mark(4)

@@ -225,9 +225,12 @@ class BlockSparseAttention:
 
     ``__call__(q, k, v)`` takes raster bf16 tensors ``[B, Ntot, H, D]`` on the
     GPU and returns the raster output.  Buffers are allocated once, through
-    torch, in the constructor."""
+    torch, in the constructor.  With ``overlap`` the V gather runs on a side
+    stream (default priority) while the plan runs on the caller's stream: the
+    plan does not read V, and the forward waits for both."""
 
-    def __init__(self, desc: Desc, device="cuda", with_lse: bool = False, grouped: bool = True):
+    def __init__(self, desc: Desc, device="cuda", with_lse: bool = False, grouped: bool = True,
+                 overlap: bool = True):
         self.desc = desc
         B, H, D = desc.batch, desc.heads, desc.head_dim
         self.n_video = video_slots(desc)  # tiled video tokens (padding slots included)
@@ -246,14 +249,34 @@ class BlockSparseAttention:
         self.workspace = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device)
         self.lse = torch.empty((B, H, self.n_tot), dtype=torch.float32, device=device) if with_lse else None
         self.grouped = grouped
+        self.side = torch.cuda.Stream(device=device) if overlap else None
 
     def build(self, q, stream=None):
         permute_build(self.desc, self.perm, self.shape_map, q if self.dynamic else None, self.workspace, stream)
 
     def gather_qkv(self, q, k, v, stream=None):
+        self.gather_qk(q, k, stream)
+        self.gather_v(v, stream)
+
+    def gather_qk(self, q, k, stream=None):
         gather(self.desc, q, self.q_t, self.perm, stream)
         gather_kf(self.desc, k, self.k_f, self.perm, stream)
+
+    def gather_v(self, v, stream=None):
         gather_vf(self.desc, v, self.v_f, self.perm, stream)
+
+    def gather_v_and_plan(self, v, stream=None):
+        """The V gather and the plan, overlapped on the side stream when there
+        is one and ``stream`` is a torch stream or None."""
+        if self.side is None or not (stream is None or isinstance(stream, torch.cuda.Stream)):
+            self.gather_v(v, stream)
+            self.plan(stream)
+            return
+        cur = torch.cuda.current_stream() if stream is None else stream
+        self.side.wait_stream(cur)
+        self.gather_v(v, self.side)
+        self.plan(cur)
+        cur.wait_stream(self.side)
 
     def plan(self, stream=None):
         plan(self.desc, self.q_t, self.k_f, self.block_idx, self.workspace, stream)
@@ -269,8 +292,8 @@ class BlockSparseAttention:
         if out is None:
             out = torch.empty_like(q)
         self.build(q, stream)
-        self.gather_qkv(q, k, v, stream)
-        self.plan(stream)
+        self.gather_qk(q, k, stream)
+        self.gather_v_and_plan(v, stream)
         self.forward(stream)
         self.scatter_out(out, stream)
         return out

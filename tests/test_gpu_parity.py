@@ -200,3 +200,17 @@ def test_rescale_path_with_steep_logits(growing):
         check_output(got[0, h].reshape(n, 64, D), ref, f"h{h}")
         check_lse(lse[0, h].reshape(n, 64), ref_lse, qg[0, h].reshape(n, 64, D), kg[0, h], float(np.float32(wl.scale)),
                   f"lse h{h}")
+
+
+def test_overlapped_call_equals_sequential_steps():
+    """BlockSparseAttention.__call__ gathers V on a side stream beside the
+    plan; the result equals the step-by-step path bit for bit, call after
+    call (the side stream's work is ordered before the forward each time)."""
+    wl = W("overlap", 2, 3, 128, (8, 16, 16), 6, seed=33, n_prefix=64)
+    q, k, v = S.qkv(wl)
+    g = GpuRun(wl, q, k, v).run()
+    ref = to_bits(g.out).copy()
+    for it in range(3):
+        out = g.att(g.q, g.k, g.v)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(out), ref), f"call {it}"

@@ -94,6 +94,22 @@ def measured_traffic(kernel: str, workload: str):
     return int(m_bytes.group(1))
 
 
+def step_stats(times):
+    """Median, min and 90th percentile of the per-step times (ms)."""
+    t = np.asarray(times, np.float64)
+    return {"median": float(np.median(t)), "min": float(t.min()), "p90": float(np.percentile(t, 90))}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, q, k, v, n_tiles: int):
     """The oracle on one (batch, head) slice: gather, pooling and top-k over all
     of the head's rows, attention on `n_tiles` sampled query tiles; the head's
@@ -136,6 +152,7 @@ def cpu_baseline(wl, q, k, v, n_tiles: int):
         "value": head_flops / head_seconds / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "ms_per_call_extrapolated": head_seconds * wl.batch * wl.heads * 1e3,
         "sample": (f"one (batch, head) slice of the same workload: gather + pool + top-k over all {wl.n_video_tiles} "
@@ -185,6 +202,7 @@ def cpu_baseline_varkeep(wl, q, k, v, keep_h, n_tiles: int):
         "value": total_f / total_s / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "ms_per_call_extrapolated": total_s * 1e3,
         "sample": ("one (batch, head) slice per distinct keep count of the same workload (" + "; ".join(parts) +
@@ -263,6 +281,7 @@ def bench_varkeep(args, wl, q, k, v):
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step_stats": step_stats(totals),
     }
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -349,6 +368,7 @@ def bench_structured(args, wl, q, k, v):
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step_stats": step_stats(totals),
     }
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -399,6 +419,7 @@ def cpu_baseline_structured(wl, q, k, v, rt: int, rs: int, n_tiles: int):
         "value": total_f / total_s / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "ms_per_call_extrapolated": total_s * 1e3,
         "sample": ("one spatial and one temporal (batch, head) slice of the same workload (" + "; ".join(parts) +
@@ -456,6 +477,7 @@ def cpu_baseline_backward(wl, q, k, v, do, n_tiles: int):
         "value": head_flops / head_seconds / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "ms_per_call_extrapolated": head_seconds * wl.batch * wl.heads * 1e3,
         "sample": (f"one (batch, head) slice of the same workload: plan over all rows ({t_plan:.2f} s), lse, "
@@ -538,6 +560,7 @@ def bench_backward(args, wl, q, k, v):
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": None},
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step_stats": step_stats(times),
     }
     if not args.no_cpu_baseline and keep_h is None:
         t0 = time.perf_counter()
@@ -664,6 +687,7 @@ def main():
                      "traffic": measured_traffic(kernel, wl.name)},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step_stats": step_stats(totals),
         "skipped_tile_ratio": 1.0 - wl.keep_tiles / wl.n_video_tiles,
     }
     if not args.no_cpu_baseline:

@@ -7,8 +7,9 @@ benchmark times, on sampled outputs the oracle computes one by one:
 * dense prefix of 2,048 tokens before a 24x48x84 video grid (1,512 tiles),
   378 kept video tiles.
 
-Permutation and shape maps are compared in full; gather, pooling, selection,
-attention and scatter on sampled (batch, head) pairs and query tiles.
+Permutation and shape maps are compared in full, and at 720p the pooled means
+and kept lists of every row of every (batch, head); gather, attention and
+scatter on sampled (batch, head) pairs and query tiles.
 """
 import numpy as np
 import pytest
@@ -82,6 +83,29 @@ def test_prism720p_sampled(prism):
     first = to_bits(g.out)
     g.run()
     assert np.array_equal(first, to_bits(g.out))
+
+
+def test_prism720p_plan_every_row(prism):
+    """The plan at full size on every (batch, head): pooled means of every tile
+    bit-exact, kept lists of every row exact outside near ties (a valid top-k
+    within the band on near ties)."""
+    wl, q, k, v, g = prism
+    npf = wl.n_prefix
+    perm = np.ascontiguousarray(np.broadcast_to(oracle.perm_static(wl.grid), (wl.batch, wl.n_video)))
+    gq, gk = g.pooled()
+    gidx = g.block_idx()
+    n_exact = n_near = 0
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+            qt, kt = (oracle.gather(sl(x), perm[b:b + 1], npf) for x in (q, k))
+            qp, kp = oracle.pool(qt, npf), oracle.pool(kt, npf)
+            assert np.array_equal(gq[b, h], qp[0, 0]) and np.array_equal(gk[b, h], kp[0, 0]), f"b{b} h{h}"
+            e, n = check_selection(gidx[b:b + 1, h:h + 1], qp, kp, wl.keep_tiles)
+            n_exact += e
+            n_near += n
+    print(f"[plan, every row] exact rows {n_exact}, near-tie rows {n_near}", flush=True)
+    assert n_exact + n_near == wl.batch * wl.heads * wl.n_video_tiles
 
 
 @pytest.mark.parametrize("keep", [192, 120, 96])

@@ -20,7 +20,8 @@
 //   K and V are stored in HBM in the MFMA fragment order (K-fragment and
 //   V-fragment layouts of the C interface): every wave-wide 16-byte load reads
 //   1 KB contiguous and lands exactly in the operand registers, so K and V
-//   need no LDS; the Q^T fragments of the query tile are staged once in LDS.
+//   need no LDS; the Q^T fragments of the query tile are staged once in LDS
+//   and read from there once per tile into registers (64 per lane for D = 128).
 //   Each wave, one per SIMD, is software pipelined over its slices n; a
 //   step is two windows of MFMA slots, one per query half h:
 //     window 0: O[1] += V(n-1) P(n-1)[1], S(n)[1] = K(n) Q^T[1], beside the
@@ -329,6 +330,12 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     for (int s = 0; s < SD; ++s)
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][s], *(const bf16x8*)(qlds + (s * 64 + lane) * 16),
                                                           sacc[0], 0, 0, 0);
+    // Q^T fragments of both query halves held in registers for the whole tile
+    bf16x8 qreg[2][SD];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int s = 0; s < SD; ++s) qreg[h2][s] = *(const bf16x8*)(qlds + lane * 16 + (h2 * SD + s) * 1024);
     int t_v = TILE_AT(1);       // tile whose V is loaded next
     int t_k_next = TILE_AT(2);  // tile whose K is loaded next
     int t_s = CLASSED_AT(0);    // ragged grid: slice n's list entry, with its boundary class
@@ -360,20 +367,17 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
             // consecutive slots, so no instruction waits on the one before
             // it and the single wave of the SIMD keeps the matrix core busy.
             // A scheduling fence after every slot holds this order; the Q^T
-            // fragments are read from LDS a few slots ahead of their MFMA.
+            // fragments stay in registers for the whole tile.
             // After the K-row order of the fragment layout, lane-half hf holds
             // keys 16*c + 8*hf + e of the slice at S[8*c + e].  Slices past
             // the end get -inf added to their logits (no branch).
             const float vmask = n < my_n ? 0.f : -INFINITY;
             constexpr int NPV = 2 * OD;           // PV slots of a window
             constexpr int W = NPV + SD;           // slots of a window
-            constexpr int QLEAD = 4;              // Q^T read lead, in slots
             constexpr int PPS = (8 + W - 4) / (W - 3);  // weight pairs per stage slot: 1 (D = 128), 2 (D = 64)
             constexpr int NSA = 8 / PPS;          // stage slots of a window
             constexpr int GSUM = NSA + 3;         // slot of the normaliser's dot products
-            static_assert(NPV >= QLEAD && NV == SD && NSA * PPS == 8 && GSUM < W, "window layout");
-            int qoff = lane * 16;
-            asm("" : "+v"(qoff) : "s"(n));  // opaque: keeps the Q^T reads in the loop
+            static_assert(NV == SD && NSA * PPS == 8 && GSUM < W, "window layout");
             float lrun[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -384,13 +388,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                 // a slice of a boundary tile: its padding keys out
                 if (kPad && (t_s >> 16)) mask_padding_keys(a.pad.real[t_s >> 16], kh, hf, sacc[h]);
                 float xa[8][2], xe[8][2];
-                bf16x8 qv[SD];
 #pragma unroll
                 for (int g = 0; g < W; ++g) {
-                    if (g + QLEAD >= NPV && g + QLEAD < W) {
-                        const int s2 = g + QLEAD - NPV;
-                        qv[s2] = *(const bf16x8*)(qlds + qoff + (sq * SD + s2) * 1024);
-                    }
                     if (g < NPV) {
                         const int c = g / OD, i = g % OD;
                         // h = 0: V(n-1) in vf[B^1]; h = 1: V(n) in vf[B]
@@ -400,7 +399,7 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                     } else {
                         const int st = g - NPV;
                         // h = 0: K(n) in kf[B]; h = 1: K(n+1) in kf[B^1]
-                        sacc[sq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ h][st], qv[st],
+                        sacc[sq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[B ^ h][st], qreg[sq][st],
                                                                            st == 0 ? f32x16{} : sacc[sq], 0, 0, 0);
                         asm volatile("" ::"v"(sacc[sq][0]));
                         if (h == 0)

@@ -211,3 +211,81 @@ def test_prism720p_ragged_backward_sampled():
         check_grad(gt[2][ktiles][rows[ktiles]], ref_dv[rows[ktiles]], f"dv b{b} h{h}")
     del g, grads
     torch.cuda.empty_cache()
+
+
+def test_padded_csr_and_structured_lists():
+    """Ragged grid with CSR lists (per-head keeps) and with structured lists
+    (spatial radius 0, temporal radius 2 on a 2 x 3 x 3 tile grid): the CSR
+    forward against the oracle's masked CSR attention on the real rows, and
+    the CSR backward against the oracle's masked gradients (each head's rows
+    have one length, so they are fixed-keep lists for the oracle)."""
+    wl = W("pad_csr", 1, 2, 128, (7, 9, 10), 5, seed=48, n_prefix=64, padded=True)
+    q, k, v = S.qkv(wl)
+    do = S.tensor(wl, "do")
+    g = GpuRun(wl, q, k, v).run()
+    a, d = g.att, g.desc
+    npf, scale, D = wl.n_prefix, float(np.float32(wl.scale)), wl.head_dim
+    p1 = oracle.perm_static_padded(wl.grid, wl.tile)
+    real = oracle.key_real(p1, npf)
+    tiled = [oracle.gather_padded(x, p1, npf) for x in (q, k, v, do)]
+    qt, kt, vt, dot = tiled
+    n = wl.n_video_tiles
+    nqt = wl.n_tiled_tokens // 64
+    rows_real = real.reshape(nqt, 64).astype(bool)
+    tiles = np.arange(nqt, dtype=np.int32)
+    src = raster_to_tiled_rows(p1, npf)
+    lists = {}
+    row_ptr = torch.empty(wl.batch * wl.heads * n + 1, dtype=torch.int64, device="cuda")
+    col = torch.empty(bsa.csr_entries(d, [5, 2]), dtype=torch.int32, device="cuda")
+    bsa.plan_csr(d, a.q_t, a.k_f, row_ptr, col, a.workspace, keep_per_head=[5, 2])
+    lists["csr"] = (row_ptr, col)
+    mask = [bsa.MASK_SPATIAL, bsa.MASK_TEMPORAL]
+    rp2 = torch.empty_like(row_ptr)
+    col2 = torch.empty(bsa.structured_entries(d, mask, 0, 2), dtype=torch.int32, device="cuda")
+    bsa.plan_structured(d, mask, 0, 2, rp2, col2)  # full rows: one length per head
+    lists["structured"] = (rp2, col2)
+    for name, (rp, cl) in lists.items():
+        print(f"\n[case] {wl} {name} lists", flush=True)
+        o_t = torch.empty_like(a.q_t)
+        lse = torch.empty_like(a.lse)
+        bsa.forward_csr(d, a.q_t, a.k_f, a.v_f, rp, cl, o_t, lse, workspace=a.workspace)
+        out = torch.empty_like(g.q)
+        bsa.scatter(d, o_t, out, a.perm)
+        dq, dk, dv = (torch.empty_like(g.q) for _ in range(3))
+        ws = torch.empty(bsa.backward_csr_workspace_size(d, cl.numel()), dtype=torch.uint8, device="cuda")
+        bsa.backward_csr(d, g.q, g.k, g.v, out, to_dev(do), lse, a.perm, rp, cl, dq, dk, dv, ws)
+        torch.cuda.synchronize()
+        rp_h, cl_h = rp.cpu().numpy(), cl.cpu().numpy()
+        o_bits, lse_h = to_bits(o_t), lse.cpu().numpy()
+        for h in range(wl.heads):
+            r0 = h * n
+            rph = rp_h[r0:r0 + n + 1] - rp_h[r0]
+            clh = cl_h[rp_h[r0]:rp_h[r0 + n]]
+            ref, ref_lse = oracle.attention_padded_csr(qt[0, h], kt[0, h], vt[0, h], npf, rph, clh, real, scale,
+                                                       tiles)
+            check_output(o_bits[0, h].reshape(nqt, 64, D)[rows_real], ref[rows_real], f"{name} h{h}")
+            check_lse(lse_h[0, h].reshape(nqt, 64)[rows_real], ref_lse[rows_real],
+                      qt[0, h].reshape(nqt, 64, D)[rows_real], kt[0, h], scale, f"{name} lse h{h}")
+        grads_ref = padded_csr_gradients(qt, kt, vt, dot, npf, rp_h, cl_h, real, scale, wl.heads, n)
+        for gname, dev, r in zip(("dq", "dk", "dv"), (dq, dk, dv), grads_ref):
+            check_grad(bits_to_f64(to_bits(dev)), r[:, :, src].transpose(0, 2, 1, 3), f"{name} {gname}")
+    del g
+    torch.cuda.empty_cache()
+
+
+def padded_csr_gradients(qt, kt, vt, dot, npf, row_ptr, col, real, scale, H, n):
+    """The oracle's masked gradients over CSR lists whose rows are of one
+    length per head (per-head keeps, or structured rules that keep full
+    rows): each head's rows are a fixed-keep list."""
+    B, _, Ntot, D = qt.shape
+    out = [np.zeros((B, H, Ntot, D)) for _ in range(3)]
+    for h in range(H):
+        r0 = h * n
+        lens = np.diff(row_ptr[r0:r0 + n + 1])
+        assert (lens == lens[0]).all()
+        idx = col[row_ptr[r0]:row_ptr[r0 + n]].reshape(n, int(lens[0]))
+        g = oracle.backward_full_padded(qt[:, h:h + 1], kt[:, h:h + 1], vt[:, h:h + 1], dot[:, h:h + 1], npf,
+                                        idx[None, None], real[None], scale)
+        for o, x in zip(out, g):
+            o[:, h] = x[:, 0]
+    return out

@@ -135,7 +135,8 @@ typedef struct bsa_desc {
  * all three on one stream.  Host-only; enqueues nothing.  After bsa_plan's
  * work has run, the workspace starts with the pooled tile means
  *   float qbar[B][H][nVT][D], then float kbar[B][H][nVT][D]
- * (each the mean of the tile's 64 tokens), each region 256-byte aligned;
+ * (each the mean of the tile's 64 tokens, or of its real tokens on a ragged
+ * grid), each region 256-byte aligned;
  * bsa_forward does not overwrite them.
  */
 bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
@@ -166,7 +167,8 @@ bsa_status bsa_permute(const bsa_desc *desc, int op, const void *q_raster, int32
 
 /*
  * Tile selection.  From Q (tiled) and K (kfrag), bf16: the mean of each video
- * tile's 64 tokens (summed exactly, rounded once to float), the score
+ * tile's 64 tokens (of its real tokens on a ragged grid; summed exactly,
+ * divided by the count, rounded once to float), the score
  * s_ij = sum_d qbar_i[d] kbar_j[d] (float), and per (b, h, video query tile i)
  * the keep_tiles video key tiles with the largest s_ij, equal scores going to
  * the lower tile number, written ascending to `block_idx`.  Prefix tiles are

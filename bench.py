@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--workload", default="prism720p")
     ap.add_argument("--keep", type=int, default=None, help="override kept tiles per query tile")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=960, help="query tiles in the CPU oracle sample")
+    ap.add_argument("--cpu-tiles", type=int, default=4096, help="query tiles in the CPU oracle sample")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (bsa_backward)")
     ap.add_argument("--cpu-bwd-tiles", type=int, default=120, help="query and key tiles in the backward CPU sample")
     ap.add_argument("--structured", default=None,
@@ -110,56 +110,87 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, q, k, v, n_tiles: int):
-    """The oracle on one (batch, head) slice: gather, pooling and top-k over all
-    of the head's rows, attention on `n_tiles` sampled query tiles; the head's
-    time is extrapolated linearly over its query tiles."""
+CPU_SAMPLE_BH = ((0, 0), (1, 23), (0, 13), (1, 5))
+
+
+def cpu_baseline(wl, q, k, v, n_tiles: int, gpu_idx=None):
+    """The oracle on a few (batch, head) slices: gather, pooling and top-k
+    over all of each head's rows, attention on `n_tiles` sampled query tiles
+    split over the slices; extrapolated linearly over the query tiles and
+    heads.  With `gpu_idx` (the GPU's block_idx, [B, H, nVT, k]) the GPU's
+    kept lists of those heads are compared with the oracle's on every row, and
+    the rows in the contract's near-tie band (relative k-th / (k+1)-th gap
+    below 1e-4) and in the float rounding band are counted."""
     import oracle
-    b, h = 0, 0
-    sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
-    qs, ks, vs = sl(q), sl(k), sl(v)
+    pairs = [(b % wl.batch, h % wl.heads) for b, h in CPU_SAMPLE_BH]
+    pairs = list(dict.fromkeys(pairs))
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    if wl.padded:
-        perm = oracle.perm_static_padded(wl.grid, wl.tile)[None]
-        qt, kt, vt = (oracle.gather_padded(x, perm, wl.n_prefix) for x in (qs, ks, vs))
-        qp, kp = oracle.pool_padded(qt, perm, wl.n_prefix), oracle.pool_padded(kt, perm, wl.n_prefix)
-    else:
-        if wl.dynamic:
-            st = oracle.shape_stats(qs, wl.n_prefix, wl.grid)
-            shape, _ = oracle.shape_choose(st, wl.grid, float(np.float32(wl.tau)))
-            perm = oracle.perm_dynamic(shape, wl.grid)
-        else:
-            perm = oracle.perm_static(wl.grid, wl.tile)[None]
-        qt, kt, vt = (oracle.gather(x, perm, wl.n_prefix) for x in (qs, ks, vs))
-        qp, kp = oracle.pool(qt, wl.n_prefix), oracle.pool(kt, wl.n_prefix)
-    idx, *_ = oracle.topk(qp, kp, wl.keep_tiles)
-    t_plan = time.perf_counter() - t0
     nqt = wl.n_tiled_tokens // 64
+    per = max(1, min(nqt, n_tiles // len(pairs)))
     rng = np.random.default_rng(1234)
-    tiles = np.sort(rng.choice(nqt, size=min(n_tiles, nqt), replace=False)).astype(np.int32)
     scale = float(np.float32(wl.scale))
-    t0 = time.perf_counter()
-    if wl.padded:
-        oracle.attention_padded(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0],
-                                oracle.key_real(perm[0], wl.n_prefix), scale, tiles)
-    else:
-        oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0], scale, tiles)
-    t_attn = time.perf_counter() - t0
-    head_seconds = t_plan + t_attn * nqt / len(tiles)
+    t_plan = t_attn = 0.0
+    sel = {"rows": 0, "mismatch_rows": 0, "near_tie_rows": 0, "float_band_rows": 0}
+    for b, h in pairs:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
+        qs, ks, vs = sl(q), sl(k), sl(v)
+        t0 = time.perf_counter()
+        if wl.padded:
+            perm = oracle.perm_static_padded(wl.grid, wl.tile)[None]
+            qt, kt, vt = (oracle.gather_padded(x, perm, wl.n_prefix) for x in (qs, ks, vs))
+            qp, kp = oracle.pool_padded(qt, perm, wl.n_prefix), oracle.pool_padded(kt, perm, wl.n_prefix)
+        else:
+            if wl.dynamic:
+                st = oracle.shape_stats(qs, wl.n_prefix, wl.grid)
+                shape, _ = oracle.shape_choose(st, wl.grid, float(np.float32(wl.tau)))
+                perm = oracle.perm_dynamic(shape, wl.grid)
+            else:
+                perm = oracle.perm_static(wl.grid, wl.tile)[None]
+            qt, kt, vt = (oracle.gather(x, perm, wl.n_prefix) for x in (qs, ks, vs))
+            qp, kp = oracle.pool(qt, wl.n_prefix), oracle.pool(kt, wl.n_prefix)
+        idx, s_k, s_k1, mag = oracle.topk(qp, kp, wl.keep_tiles)
+        t_plan += time.perf_counter() - t0
+        if gpu_idx is not None and wl.n_video_tiles:
+            # the dynamic shapes of a slice follow the GPU's choice only where
+            # the statistic is clear of a threshold; static grids compare fully
+            gi = gpu_idx[b, h]
+            sel["rows"] += gi.shape[0]
+            sel["mismatch_rows"] += int(np.any(gi != idx[0, 0], axis=-1).sum())
+            gap = s_k - s_k1
+            den = np.maximum(np.abs(s_k), np.abs(s_k1))
+            ok = ~np.isnan(s_k1)
+            sel["near_tie_rows"] += int((ok & ((den == 0) | (gap < 1e-4 * den))).sum())
+            u = 2.0 ** -24
+            gam = wl.head_dim * u / (1 - wl.head_dim * u)
+            sel["float_band_rows"] += int((ok & (gap <= 2 * gam * mag)).sum())
+        tiles = np.sort(rng.choice(nqt, size=per, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        if wl.padded:
+            oracle.attention_padded(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0],
+                                    oracle.key_real(perm[0], wl.n_prefix), scale, tiles)
+        else:
+            oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], wl.n_prefix, idx[0, 0], scale, tiles)
+        t_attn += time.perf_counter() - t0
+    n_s = len(pairs)
+    head_seconds = (t_plan + t_attn * nqt / per) / n_s
     head_flops = wl.effective_flops() / (wl.batch * wl.heads)
-    return {
+    res = {
         "value": head_flops / head_seconds / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "cpu_model": cpu_model(),
         "kind": "oracle",
         "ms_per_call_extrapolated": head_seconds * wl.batch * wl.heads * 1e3,
-        "sample": (f"one (batch, head) slice of the same workload: gather + pool + top-k over all {wl.n_video_tiles} "
-                   f"query tiles ({t_plan:.2f} s) and fp64 attention on {len(tiles)} of {nqt} query tiles "
-                   f"({t_attn:.2f} s), extrapolated linearly to the head and scaled by the head's share of "
-                   f"the effective FLOPs"),
+        "sample": (f"{n_s} (batch, head) slices {pairs} of the same workload: gather + pool + top-k over all "
+                   f"{wl.n_video_tiles} query tiles of each ({t_plan:.2f} s) and fp64 attention on {per} sampled "
+                   f"query tiles of each, {per * n_s} of the call's {nqt * wl.batch * wl.heads} "
+                   f"({100.0 * per * n_s / (nqt * wl.batch * wl.heads):.1f}%) ({t_attn:.2f} s), extrapolated "
+                   f"linearly over the query tiles and heads"),
     }
+    if gpu_idx is not None:
+        sel["sample"] = f"every row of the {n_s} (batch, head) slices of the CPU sample, against the oracle"
+        res["selection_check"] = sel
+    return res
 
 
 def varkeep_flops(wl, keep_h):
@@ -220,7 +251,7 @@ def bench_varkeep(args, wl, q, k, v):
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, max(keep_h), scale=wl.scale,
                          n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
-    att = bsa.BlockSparseAttention(desc)
+    att = bsa.BlockSparseAttention(desc, pool_in_gather=False)   # the CSR planners pool for themselves
     out = torch.empty_like(qd)
     rows = wl.batch * wl.heads * wl.n_video_tiles
     row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
@@ -300,7 +331,7 @@ def bench_structured(args, wl, q, k, v):
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
                          n_prefix=wl.n_prefix, tile=wl.tile, padded=wl.padded)
-    att = bsa.BlockSparseAttention(desc)
+    att = bsa.BlockSparseAttention(desc, pool_in_gather=False)   # the CSR planners pool for themselves
     out = torch.empty_like(qd)
     rows = wl.batch * wl.heads * wl.n_video_tiles
     row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
@@ -659,6 +690,8 @@ def main():
     ms_step = float(np.mean(totals))
     F = wl.effective_flops()
     fwd_ms = float(np.mean(per_stage["forward"]))
+    gave_up, rounds = bsa.forward_stats(desc, att.workspace)   # of the last timed step's forward
+    kernels = kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out)
     # the forward stage is the attention kernel (plus a 4 us counter clear; a
     # dense prefix adds the plain kernel for the prefix query tiles)
     kernel = f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}>"
@@ -688,13 +721,81 @@ def main():
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "ms_per_step_stats": step_stats(totals),
+        "non_forward_ms": ms_step - fwd_ms,
         "skipped_tile_ratio": 1.0 - wl.keep_tiles / wl.n_video_tiles,
+        "lockstep": {"rounds": rounds, "waits_gave_up": gave_up,
+                     "note": "rounds of the grouped forward launch (last timed step) whose bounded start wait gave "
+                             "up before every block of its XCD group arrived"},
+        "kernels": kernels,
     }
+    if wl.dynamic:
+        hist = np.bincount(att.shape_map.cpu().numpy().reshape(-1), minlength=9)
+        res["shape_histogram"] = {"order": SHAPE_NAMES, "regions": hist.tolist()}
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_tiles)
+        gidx = None if wl.dynamic else att.block_idx.cpu().numpy()
+        res["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_tiles, gidx)
         print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
+
+
+SHAPE_NAMES = ["4x4x4", "2x4x8", "2x8x4", "8x4x2", "4x2x8", "4x8x2", "8x2x4", "2x2x16", "16x2x2"]
+
+
+def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, reps: int = 5):
+    """Each stage of the step alone on the stream (HIP events, mean of `reps`
+    calls after one untimed call), with its HBM bytes and rate against 8 TB/s:
+    the pooling gathers of Q and K, the plain gathers they replace, the V
+    gather, the selection, bsa_plan's own pooling + selection (the unfused
+    path) and the output scatter.  plan_ms: what the plan adds to the step
+    (the pooling gathers' time above the plain gathers, plus the selection),
+    against the plan's roofline: reading Q and K once and writing the lists."""
+    import torch
+    cur = torch.cuda.current_stream()
+    bf = 2 * wl.batch * wl.heads * wl.n_tiled_tokens * wl.head_dim   # one bf16 tiled tensor, bytes
+    pooled = wl.batch * wl.heads * wl.n_video_tiles * wl.head_dim * 4
+    idx_bytes = wl.batch * wl.heads * wl.n_video_tiles * wl.keep_tiles * 4
+    q_t2, k_f2 = torch.empty_like(att.q_t), torch.empty_like(att.k_f)
+
+    def t(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(cur)
+        for _ in range(reps):
+            fn()
+        ev[1].record(cur)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    ms = {
+        "gather_pool_q": t(lambda: bsa.gather_pool(desc, qd, att.q_t, att.perm, att.workspace)),
+        "gather_kf_pool_k": t(lambda: bsa.gather_kf_pool(desc, kd, att.k_f, att.perm, att.workspace)),
+        "gather_q_plain": t(lambda: bsa.gather(desc, qd, q_t2, att.perm)),
+        "gather_kf_k_plain": t(lambda: bsa.gather_kf(desc, kd, k_f2, att.perm)),
+        "gather_vf_v": t(lambda: att.gather_v(vd)),
+        "select": t(lambda: bsa.select(desc, att.block_idx, att.workspace)),
+        "plan_unfused": t(lambda: bsa.plan(desc, att.q_t, att.k_f, att.block_idx, att.workspace)),
+        "scatter_o": t(lambda: att.scatter_out(out)),
+    }
+    moved = {"gather_pool_q": 2 * bf + pooled, "gather_kf_pool_k": 2 * bf + pooled, "gather_q_plain": 2 * bf,
+             "gather_kf_k_plain": 2 * bf, "gather_vf_v": 2 * bf, "scatter_o": 2 * bf}
+    res = {"note": "each stage alone on the stream, mean of %d calls; hbm = algorithmic bytes moved / time" % reps}
+    for k_, v_ in ms.items():
+        e = {"ms": v_}
+        if k_ in moved:
+            gbs = moved[k_] / (v_ * 1e-3) / 1e9
+            e.update({"bytes": moved[k_], "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS})
+        res[k_] = e
+    pool_extra = max(0.0, ms["gather_pool_q"] + ms["gather_kf_pool_k"] - ms["gather_q_plain"]
+                     - ms["gather_kf_k_plain"])
+    plan_ms = pool_extra + ms["select"]
+    roof_ms = (2 * bf + idx_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3
+    res["plan"] = {"pool_in_gathers_extra_ms": pool_extra, "select_ms": ms["select"], "plan_ms": plan_ms,
+                   "roofline_ms": roof_ms, "frac": roof_ms / plan_ms if plan_ms > 0 else None,
+                   "roofline": "read Q and K once (pooling) and write the kept lists, at 8 TB/s",
+                   "unfused_plan_ms": ms["plan_unfused"],
+                   "unfused_frac": roof_ms / ms["plan_unfused"]}
+    return res
 
 
 if __name__ == "__main__":

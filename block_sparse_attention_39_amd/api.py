@@ -12,8 +12,9 @@ import math
 
 import torch
 
-from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_VF, PERM_SCATTER, TILE_DYNAMIC,
-                   TILE_STATIC, TILE_STATIC_PADDED, BsaError, Desc, lib)
+from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_KF_POOL, PERM_GATHER_POOL, PERM_GATHER_VF,
+                   PERM_SCATTER, PERM_TILED_TO_KF, PERM_TILED_TO_VF, TILE_DYNAMIC, TILE_STATIC, TILE_STATIC_PADDED,
+                   BsaError, Desc, lib)
 
 
 def make_desc(batch: int, heads: int, head_dim: int, grid, keep_tiles: int, *, scale: float | None = None,
@@ -91,6 +92,35 @@ def gather_vf(desc: Desc, src, dst, perm, stream=None):
                              0, _stream(stream)), "bsa_permute(GATHER_VF)")
 
 
+def _ws(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def gather_pool(desc: Desc, src, dst, perm, workspace, stream=None):
+    """Raster Q -> tiled, with the tile means of Q written into the workspace."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER_POOL, None, _ptr(perm), None, _ptr(src), _ptr(dst),
+                             _ptr(workspace), _ws(workspace), _stream(stream)), "bsa_permute(GATHER_POOL)")
+
+
+def gather_kf_pool(desc: Desc, src, dst, perm, workspace, stream=None):
+    """Raster K -> the K-fragment layout, with the tile means of K written into
+    the workspace."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_GATHER_KF_POOL, None, _ptr(perm), None, _ptr(src), _ptr(dst),
+                             _ptr(workspace), _ws(workspace), _stream(stream)), "bsa_permute(GATHER_KF_POOL)")
+
+
+def tiled_to_kf(desc: Desc, src, dst, stream=None):
+    """Tiled K -> the K-fragment layout."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_TILED_TO_KF, None, None, None, _ptr(src), _ptr(dst), None, 0,
+                             _stream(stream)), "bsa_permute(TILED_TO_KF)")
+
+
+def tiled_to_vf(desc: Desc, src, dst, stream=None):
+    """Tiled V -> the V-fragment layout."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_TILED_TO_VF, None, None, None, _ptr(src), _ptr(dst), None, 0,
+                             _stream(stream)), "bsa_permute(TILED_TO_VF)")
+
+
 def scatter(desc: Desc, src, dst, perm, stream=None):
     _check(lib().bsa_permute(ctypes.byref(desc), PERM_SCATTER, None, _ptr(perm), None, _ptr(src), _ptr(dst), None, 0,
                              _stream(stream)), "bsa_permute(SCATTER)")
@@ -100,6 +130,29 @@ def plan(desc: Desc, q_tiled, k_frag, block_idx, workspace, stream=None):
     ws = workspace.numel() * workspace.element_size()
     _check(lib().bsa_plan(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), _ptr(block_idx), _ptr(workspace), ws,
                           _stream(stream)), "bsa_plan")
+
+
+def select(desc: Desc, block_idx, workspace, stream=None):
+    """Scores and top-k from the tile means already in the workspace (written
+    by gather_pool / gather_kf_pool or an earlier plan)."""
+    _check(lib().bsa_select(ctypes.byref(desc), _ptr(block_idx), _ptr(workspace), _ws(workspace), _stream(stream)),
+           "bsa_select")
+
+
+def forward_stats_offset(desc: Desc) -> int:
+    """Byte offset in the workspace of the forward's int32 statistics: rounds
+    whose start wait gave up, rounds started (of the last grouped call)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_forward_stats_offset(ctypes.byref(desc), ctypes.byref(n)), "bsa_forward_stats_offset")
+    return n.value
+
+
+def forward_stats(desc: Desc, workspace):
+    """(rounds whose start wait gave up, rounds started) of the last grouped
+    forward call on this workspace (a device read: synchronises the stream)."""
+    off = forward_stats_offset(desc)
+    v = workspace.view(torch.uint8)[off:off + 8].view(torch.int32).cpu().tolist()
+    return int(v[0]), int(v[1])
 
 
 def forward(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, workspace=None, stream=None):
@@ -227,10 +280,13 @@ class BlockSparseAttention:
     GPU and returns the raster output.  Buffers are allocated once, through
     torch, in the constructor.  With ``overlap`` the V gather runs on a side
     stream (default priority) while the plan runs on the caller's stream: the
-    plan does not read V, and the forward waits for both."""
+    plan does not read V, and the forward waits for both.  With
+    ``pool_in_gather`` (default) the Q and K gathers also take the tile means
+    (bsa_permute GATHER_POOL / GATHER_KF_POOL) and the plan is bsa_select;
+    otherwise plain gathers and bsa_plan, which reads Q and K again."""
 
     def __init__(self, desc: Desc, device="cuda", with_lse: bool = False, grouped: bool = True,
-                 overlap: bool = True):
+                 overlap: bool = True, pool_in_gather: bool = True):
         self.desc = desc
         B, H, D = desc.batch, desc.heads, desc.head_dim
         self.n_video = video_slots(desc)  # tiled video tokens (padding slots included)
@@ -249,6 +305,7 @@ class BlockSparseAttention:
         self.workspace = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device)
         self.lse = torch.empty((B, H, self.n_tot), dtype=torch.float32, device=device) if with_lse else None
         self.grouped = grouped
+        self.pool_in_gather = pool_in_gather
         self.side = torch.cuda.Stream(device=device) if overlap else None
 
     def build(self, q, stream=None):
@@ -259,8 +316,12 @@ class BlockSparseAttention:
         self.gather_v(v, stream)
 
     def gather_qk(self, q, k, stream=None):
-        gather(self.desc, q, self.q_t, self.perm, stream)
-        gather_kf(self.desc, k, self.k_f, self.perm, stream)
+        if self.pool_in_gather:
+            gather_pool(self.desc, q, self.q_t, self.perm, self.workspace, stream)
+            gather_kf_pool(self.desc, k, self.k_f, self.perm, self.workspace, stream)
+        else:
+            gather(self.desc, q, self.q_t, self.perm, stream)
+            gather_kf(self.desc, k, self.k_f, self.perm, stream)
 
     def gather_v(self, v, stream=None):
         gather_vf(self.desc, v, self.v_f, self.perm, stream)
@@ -279,7 +340,10 @@ class BlockSparseAttention:
         cur.wait_stream(self.side)
 
     def plan(self, stream=None):
-        plan(self.desc, self.q_t, self.k_f, self.block_idx, self.workspace, stream)
+        if self.pool_in_gather:
+            select(self.desc, self.block_idx, self.workspace, stream)
+        else:
+            plan(self.desc, self.q_t, self.k_f, self.block_idx, self.workspace, stream)
 
     def forward(self, stream=None):
         forward(self.desc, self.q_t, self.k_f, self.v_f, self.block_idx, self.o_t, self.lse,

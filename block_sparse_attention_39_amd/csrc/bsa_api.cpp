@@ -13,7 +13,6 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kScoreChunkBytes = size_t(1) << 30;  // cap on the score buffer
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -86,22 +85,35 @@ bsa_status check_desc(const bsa_desc* d, Geo* g) {
 }
 
 struct Layout {
-    size_t qbar, kbar, scores, partial, fwd, total;
-    int64_t chunk_bh;  // (batch, head) pairs scored per pass
+    size_t qbar, kbar, qsplit, ksplit, qnorm, knorm, sel, partial, fwd, total;
 };
 
+// Workspace of bsa_plan / bsa_select / bsa_forward / the pooling gathers:
+// the float means of Q and K (documented at the front), their bf16 hi/lo
+// split in MFMA operand order and their norms, the selection's fallback
+// scratch, then the forward's group counters and statistics.  The dynamic
+// BUILD's partial sums reuse the front (they are consumed within BUILD).
 Layout layout(const Geo& g) {
     Layout L{};
     const size_t pooled = align_up((size_t)g.BH * g.nvt * g.D * sizeof(float));
-    L.qbar = 0;
-    L.kbar = pooled;
-    L.scores = 2 * pooled;
-    const size_t per_bh = (size_t)g.nvt * g.nvt * sizeof(float);
-    int64_t chunk = per_bh ? (int64_t)(kScoreChunkBytes / per_bh) : 1;
-    if (chunk < 1) chunk = 1;
-    if (chunk > g.BH) chunk = g.BH;
-    L.chunk_bh = chunk;
-    const size_t plan_bytes = (g.nvt > 0 && g.BH > 0) ? L.scores + align_up((size_t)chunk * per_bh) : 0;
+    const size_t split = align_up((size_t)g.BH * ((g.nvt + 15) / 16) * 16 * g.D * 2 * sizeof(uint16_t));
+    const size_t norms = align_up((size_t)g.BH * g.nvt * sizeof(float));
+    size_t o = 0;
+    L.qbar = o;
+    o += pooled;
+    L.kbar = o;
+    o += pooled;
+    L.qsplit = o;
+    o += split;
+    L.ksplit = o;
+    o += split;
+    L.qnorm = o;
+    o += norms;
+    L.knorm = o;
+    o += norms;
+    L.sel = o;
+    o += align_up(g.nvt > 0 ? bsa::select_scratch_bytes((int)g.nvt) : 0);
+    const size_t plan_bytes = (g.nvt > 0 && g.BH > 0) ? o : 0;
     const size_t build_bytes = g.dynamic ? align_up((size_t)g.B * g.regions * g.H * 3 * sizeof(double)) : 0;
     L.partial = 0;
     // the forward's block-group progress counters sit after the plan's region,
@@ -110,6 +122,37 @@ Layout layout(const Geo& g) {
     const size_t fwd_end = L.fwd + align_up(bsa::forward_workspace_bytes());
     L.total = fwd_end > build_bytes ? fwd_end : build_bytes;
     return L;
+}
+
+struct PoolPair {
+    bsa::PoolOut q, k;
+};
+PoolPair pool_outs(const Layout& L, void* ws) {
+    char* w = static_cast<char*>(ws);
+    PoolPair p;
+    p.q = {reinterpret_cast<float*>(w + L.qbar), reinterpret_cast<uint16_t*>(w + L.qsplit),
+           reinterpret_cast<float*>(w + L.qnorm)};
+    p.k = {reinterpret_cast<float*>(w + L.kbar), reinterpret_cast<uint16_t*>(w + L.ksplit),
+           reinterpret_cast<float*>(w + L.knorm)};
+    return p;
+}
+
+bsa::SelectArgs select_args(const Geo& g, const Layout& L, void* ws, int32_t* idx, const int64_t* row_ptr) {
+    const PoolPair p = pool_outs(L, ws);
+    bsa::SelectArgs a{};
+    a.qbar = p.q.mean;
+    a.kbar = p.k.mean;
+    a.qsplit = p.q.split;
+    a.ksplit = p.k.split;
+    a.qnorm = p.q.norm;
+    a.knorm = p.k.norm;
+    a.idx = idx;
+    a.row_ptr = row_ptr;
+    a.k_fixed = (int)g.k;
+    a.BH = (int)g.BH;
+    a.nvt = (int)g.nvt;
+    a.scratch = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + L.sel);
+    return a;
 }
 
 bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LAUNCH; }
@@ -186,9 +229,7 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
-    if (op != BSA_PERM_BUILD && op != BSA_PERM_GATHER && op != BSA_PERM_SCATTER && op != BSA_PERM_GATHER_KF &&
-        op != BSA_PERM_GATHER_VF)
-        return BSA_ERR_ARG;
+    if (op < BSA_PERM_BUILD || op > BSA_PERM_TILED_TO_VF) return BSA_ERR_ARG;
     if (g.B == 0 || g.n_tot == 0) return BSA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (op == BSA_PERM_BUILD) {
@@ -214,8 +255,26 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
         return launched(e);
     }
     if (g.H == 0) return BSA_OK;
+    if (op == BSA_PERM_TILED_TO_KF || op == BSA_PERM_TILED_TO_VF) {
+        if (!src || !dst) return BSA_ERR_NULL;
+        if (misaligned(src, 16) || misaligned(dst, 16)) return BSA_ERR_ALIGN;
+        return launched(bsa::launch_tiled_to_frag(op == BSA_PERM_TILED_TO_KF, static_cast<const uint16_t*>(src),
+                                                  static_cast<uint16_t*>(dst), (int)g.B, (int)g.H, (int)g.D,
+                                                  g.n_tot, s));
+    }
     if (!src || !dst || (g.n_video > 0 && !perm)) return BSA_ERR_NULL;
     if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
+    if (op == BSA_PERM_GATHER_POOL || op == BSA_PERM_GATHER_KF_POOL) {
+        if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+        const Layout L = layout(g);
+        if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+        if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        const PoolPair p = pool_outs(L, ws);
+        const bool kf = op == BSA_PERM_GATHER_KF_POOL;
+        return launched(bsa::launch_gather_pool(kf, static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
+                                                perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video,
+                                                kf ? p.k : p.q, s, g.n_ras));
+    }
     if (op == BSA_PERM_GATHER_KF)
         return launched(bsa::launch_gather_kf(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
                                               (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s, g.n_ras));
@@ -240,20 +299,35 @@ bsa_status bsa_plan(const bsa_desc* desc, const void* q_tiled, const void* k_fra
     if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
     if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    char* w = static_cast<char*>(ws);
-    float* qbar = reinterpret_cast<float*>(w + L.qbar);
-    float* kbar = reinterpret_cast<float*>(w + L.kbar);
-    float* scores = reinterpret_cast<float*>(w + L.scores);
+    const PoolPair p = pool_outs(L, ws);
     hipError_t e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag),
-                                    qbar, kbar, (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s, g.pad);
-    for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
-        const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
-        e = bsa::launch_scores(qbar + b0 * g.nvt * g.D, kbar + b0 * g.nvt * g.D, scores, (int)cnt, (int)g.nvt,
-                               (int)g.D, s);
-        if (e == hipSuccess)
-            e = bsa::launch_topk(scores, block_idx + b0 * g.nvt * g.k, (int)(cnt * g.nvt), (int)g.nvt, (int)g.k, s);
-    }
+                                    p.q, p.k, (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s, g.pad);
+    if (e == hipSuccess) e = bsa::launch_select(select_args(g, L, ws, block_idx, nullptr), (int)g.D, s);
     return launched(e);
+}
+
+bsa_status bsa_select(const bsa_desc* desc, int32_t* block_idx, void* ws, size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g.empty || g.nvt == 0) return BSA_OK;
+    if (!block_idx) return BSA_ERR_NULL;
+    if (misaligned(block_idx, 4)) return BSA_ERR_ALIGN;
+    const Layout L = layout(g);
+    if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+    if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+    return launched(bsa::launch_select(select_args(g, L, ws, block_idx, nullptr), (int)g.D,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+bsa_status bsa_forward_stats_offset(const bsa_desc* desc, size_t* offset) {
+    if (!offset) return BSA_ERR_NULL;
+    Geo g;
+    const bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    *offset = layout(g).fwd + bsa::forward_stats_offset();
+    return BSA_OK;
 }
 
 bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
@@ -345,21 +419,12 @@ bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k
     if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
     if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    char* w = static_cast<char*>(ws);
-    float* qbar = reinterpret_cast<float*>(w + L.qbar);
-    float* kbar = reinterpret_cast<float*>(w + L.kbar);
-    float* scores = reinterpret_cast<float*>(w + L.scores);
+    const PoolPair p = pool_outs(L, ws);
     hipError_t e = bsa::launch_csr_rowptr(kh, keep_rows, (int)g.BH, (int)g.H, (int)g.nvt, row_ptr, s);
     if (e == hipSuccess)
-        e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag), qbar, kbar,
+        e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag), p.q, p.k,
                              (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s, g.pad);
-    for (int64_t b0 = 0; e == hipSuccess && b0 < g.BH; b0 += L.chunk_bh) {
-        const int64_t cnt = (g.BH - b0 < L.chunk_bh) ? g.BH - b0 : L.chunk_bh;
-        e = bsa::launch_scores(qbar + b0 * g.nvt * g.D, kbar + b0 * g.nvt * g.D, scores, (int)cnt, (int)g.nvt,
-                               (int)g.D, s);
-        if (e == hipSuccess)
-            e = bsa::launch_topk_csr(scores, col_idx, row_ptr, b0 * g.nvt, (int)(cnt * g.nvt), (int)g.nvt, s);
-    }
+    if (e == hipSuccess) e = bsa::launch_select(select_args(g, L, ws, col_idx, row_ptr), (int)g.D, s);
     return launched(e);
 }
 

@@ -93,19 +93,93 @@ hipError_t launch_shape_choose(const double* partial, uint8_t* shape_map, int B,
 hipError_t launch_perm_dynamic(const uint8_t* shape_map, int32_t* perm, int B, int T, int Hg, int W,
                                hipStream_t s);
 
-// Mean of the 64 tokens of every video tile of Q (tiled) and K (K-fragment
-// layout) -> float [BH][nvt][D].
-// Tile means: the sum of the tile's real tokens / their number (64 unless
-// `pad` marks the tile as a padded boundary tile).
-hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
+// Pooled tile means and what the selection reads of them.  For every video
+// tile i of every (batch, head) bh:
+//   mean  float [BH][nvt][D]: the mean of the tile's tokens (of its real tokens
+//         on a ragged grid), the exact sum rounded once to float;
+//   split bf16 [BH][ceil(nvt/16)][D/32][2][64][8]: the same means as a pair of
+//         bf16 values (hi = bf16(m), lo = bf16(m - hi)), in the operand order of
+//         v_mfma_f32_16x16x32_bf16: in the 1 KB chunk (bh, row block i/16, k-step
+//         s, part), lane i%16 + 16*g holds channels 32*s + 8*g .. +7 of row i;
+//   norm  float [BH][nvt]: the Euclidean norm of the float mean.
+struct PoolOut {
+    float* mean;
+    uint16_t* split;
+    float* norm;
+};
+
+__device__ inline uint32_t bf16_rne_bits(float x) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const bf2 b = __builtin_convertvector((f2){x, x}, bf2);
+    return __builtin_bit_cast(uint32_t, b) & 0xffffu;
+}
+
+// Store the means of channels 8c .. 8c+7 of video tile i of bh: float, the
+// bf16 hi/lo split, and return the sum of their squares (for the norm).
+__device__ inline float store_pooled8(const PoolOut& po, int64_t bh, int nvt, int D, int64_t i, int c,
+                                      const float (&m)[8]) {
+    float4* mp = (float4*)(po.mean + (bh * nvt + i) * D + 8 * c);
+    mp[0] = make_float4(m[0], m[1], m[2], m[3]);
+    mp[1] = make_float4(m[4], m[5], m[6], m[7]);
+    uint32_t hi[4], lo[4];
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const uint32_t h0 = bf16_rne_bits(m[e]), h1 = bf16_rne_bits(m[e + 1]);
+        const uint32_t l0 = bf16_rne_bits(m[e] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = bf16_rne_bits(m[e + 1] - __uint_as_float(h1 << 16));
+        hi[e / 2] = h0 | (h1 << 16);
+        lo[e / 2] = l0 | (l1 << 16);
+        sq = fmaf(m[e], m[e], sq);
+        sq = fmaf(m[e + 1], m[e + 1], sq);
+    }
+    const int64_t nb = (nvt + 15) / 16, sd = D / 32;
+    const int64_t chunk = ((bh * nb + i / 16) * sd + c / 4) * 2 * 64 + (i % 16) + 16 * (c % 4);
+    uint4* sp = (uint4*)po.split;
+    sp[chunk] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    sp[chunk + 64] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    return sq;
+}
+
+// Mean of the tokens of every video tile of Q (tiled) and K (K-fragment
+// layout): the exact sum of the tile's real tokens / their number (64 unless
+// `pad` marks the tile as a padded boundary tile), into PoolOut q and k.
+hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, const PoolOut& q, const PoolOut& k, int BH,
                        int n_prefix, int nvt, int D, hipStream_t s, const PadGeo& pad = PadGeo{});
 
-// scores[bh][i][j] = qbar_i . kbar_j (float) for bh in [0, BH).
-hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, int BH, int n, int D,
-                         hipStream_t s);
+// Gather with pooling: raster [B][Ntot][H][D] -> tiled (kfrag false) or the
+// K-fragment layout (kfrag true) through perm, and the tile means of every
+// video tile into `po` (as launch_pool writes them).
+hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H,
+                              int D, int n_prefix, int64_t n_video, const PoolOut& po, hipStream_t s,
+                              int64_t n_raster_video = -1);
 
-// Per row: the k largest scores (lower index first on ties), ascending indices.
-hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s);
+// Tiled [B][H][Ntot][D] -> the K-fragment (kfrag true) or V-fragment layout.
+hipError_t launch_tiled_to_frag(bool kfrag, const uint16_t* src, uint16_t* dst, int B, int H, int D, int64_t n_tot,
+                                hipStream_t s);
+
+// Selection from the pooled means: per row (bh, i), the k video key tiles j of
+// largest s_ij = qbar_i . kbar_j (the sum taken in double), lower j first on
+// equal scores, ascending.  Fixed keep (row_ptr null): k_fixed entries per row
+// at idx + row * k_fixed; CSR: row r keeps row_ptr[r+1] - row_ptr[r] entries
+// written at idx + row_ptr[r].  `scratch`: select_scratch_bytes(nvt) bytes.
+struct SelectArgs {
+    const float* qbar;
+    const float* kbar;
+    const uint16_t* qsplit;
+    const uint16_t* ksplit;
+    const float* qnorm;
+    const float* knorm;
+    int32_t* idx;
+    const int64_t* row_ptr;
+    int k_fixed;
+    int BH;
+    int nvt;
+    uint64_t* scratch;
+};
+size_t select_scratch_bytes(int nvt);
+hipError_t launch_select(const SelectArgs& a, int D, hipStream_t s);
 
 // Variable keep: per-head keep counts (kernel argument), per-row counts
 // (device, optional), CSR row pointers and the per-row top-k.
@@ -114,8 +188,6 @@ struct CsrKeep {
 };
 hipError_t launch_csr_rowptr(const CsrKeep& kh, const int32_t* keep_rows, int BH, int H, int nvt, int64_t* row_ptr,
                              hipStream_t s);
-hipError_t launch_topk_csr(const float* scores, int32_t* col_idx, const int64_t* row_ptr, int64_t row0, int rows,
-                           int n, hipStream_t s);
 
 // Structured lists: per head a mask kind (BSA_MASK_*), the tile grid and the
 // radii; row pointers and the ascending lists of every row.
@@ -143,7 +215,10 @@ struct ForwardArgs {
 };
 // progress: forward_workspace_bytes() of device memory for the grouped launch
 // of the video query tiles, or null for one block per query tile.
+// After the counters: int stats[2] (rounds whose start wait gave up, rounds
+// started), cleared with them at the start of every grouped launch.
 size_t forward_workspace_bytes();
+size_t forward_stats_offset();
 hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s);
 
 struct BackwardArgs {

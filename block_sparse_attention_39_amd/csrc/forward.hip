@@ -75,6 +75,7 @@ constexpr float kOverflowSum = 1.152921504606846976e18f;  // 2^60
 constexpr int kGroups = 8;         // block groups of the grouped launch (one per XCD)
 constexpr int kMaxGroupSize = 64;  // blocks per group the start-of-round wait can track
 constexpr int kMaxSpin = 2000;     // bounded wait per round (x s_sleep 2)
+constexpr int kStatInts = 4;       // after the counters: rounds whose wait gave up, rounds started
 constexpr int kMaxListTiles = BSA_MAX_TILES;  // key tiles one query tile can visit (prefix + video)
 
 template <int D>
@@ -598,7 +599,7 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
 // [(r*8 + g)*S, (r*8 + g + 1)*S) of the flattened (b, h, tile) order.
 template <int D, bool kPad>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
+sparse_fwd_grouped_kernel(ForwardArgs a, int* progress, int* stats) {
     __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::LDS_FLOATS];
     const int group = blockIdx.x % kGroups, slot = blockIdx.x / kGroups;
     const int S = gridDim.x / kGroups;
@@ -622,13 +623,22 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress) {
             if (threadIdx.x < 64) {
                 const int lane = threadIdx.x;
                 if (lane == 0) __hip_atomic_store(prog + slot, (int)r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bool met = false;
                 for (int spin = 0; spin < kMaxSpin; ++spin) {
                     int v = INT_MAX;
                     if (lane < S) v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
                     for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-                    if (v >= (int)r) break;
+                    if (v >= (int)r) {
+                        met = true;
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
+                }
+                // statistics: rounds started, and rounds whose wait gave up
+                if (lane == 0) {
+                    __hip_atomic_fetch_add(stats + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (!met) __hip_atomic_fetch_add(stats, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             const bool has_next = item_of(r + 1) < n_items;
@@ -672,14 +682,17 @@ hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) 
     const int64_t need = (n_vid + kGroups - 1) / kGroups * kGroups;
     if (grid > need) grid = need;
     if (grid < kGroups) grid = kGroups;
-    hipLaunchKernelGGL(clear_progress_kernel, dim3(1), dim3(512), 0, s, progress, kGroups * kMaxGroupSize);
-    hipLaunchKernelGGL((sparse_fwd_grouped_kernel<D, kPad>), dim3((unsigned)grid), dim3(256), 0, s, a, progress);
+    int* stats = progress + kGroups * kMaxGroupSize;
+    hipLaunchKernelGGL(clear_progress_kernel, dim3(1), dim3(512), 0, s, progress, kGroups * kMaxGroupSize + kStatInts);
+    hipLaunchKernelGGL((sparse_fwd_grouped_kernel<D, kPad>), dim3((unsigned)grid), dim3(256), 0, s, a, progress,
+                       stats);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t forward_workspace_bytes() { return (size_t)kGroups * kMaxGroupSize * sizeof(int); }
+size_t forward_workspace_bytes() { return (size_t)(kGroups * kMaxGroupSize + kStatInts) * sizeof(int); }
+size_t forward_stats_offset() { return (size_t)kGroups * kMaxGroupSize * sizeof(int); }
 
 hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s) {
     if ((int64_t)a.BH * (a.npt + a.nvt) == 0) return hipSuccess;

@@ -90,16 +90,26 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
     }
 }
 
+// One 16-byte chunk (channels 8 cc .. +7) of token row t of head h: from the
+// raster layout (t: raster row, < 0 for a padding slot, read as zeros) or,
+// with kTiled, from the tiled layout (t: tiled row).
+template <bool kTiled, bool kPad>
+__device__ inline uint4 src_chunk(const uint4* __restrict__ src, int b, int h, int H, int C, int cc, int64_t t,
+                                  int64_t n_ras, int64_t n_tot) {
+    if (kTiled) return src[(((int64_t)b * H + h) * n_tot + t) * C + cc];
+    return zero_if_padding<kPad>(src[(((int64_t)b * n_ras + row_or_zero<kPad>(t)) * H + h) * C + cc], t);
+}
+
 // Raster K -> K-fragment layout [B][H][tile][kh][s][lane][8]: chunk
 // (kh, s, lane) of a tile holds channels 16 s + 8 (lane / 32) .. +7 of the
 // tile's token 32 kh + swap23(lane % 32) (bits 2 and 3 exchanged), i.e. the
 // A operand of v_mfma_f32_32x32x16_bf16 for the S^T = K Q^T products of the
 // attention kernel.  One block per (batch, tile); work item = (head, chunk),
 // chunk fastest, so a wave writes 1 KB contiguous and reads 32-byte runs of
-// the tile's raster rows.
+// the tile's raster rows.  kTiled: the source is the tiled layout instead.
 __device__ inline int swap23(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <bool kPad>
+template <bool kPad, bool kTiled = false>
 __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
                                                         int n_prefix, int64_t n_video, int64_t n_tot,
@@ -109,7 +119,8 @@ __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict_
     const int64_t tile = blockIdx.x;
     const int64_t p0 = tile * kTile;
     const int64_t n_tiles = n_tot / kTile;
-    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    if (threadIdx.x < kTile)
+        tok[threadIdx.x] = kTiled ? p0 + threadIdx.x : slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
     __syncthreads();
     const int SD = C / 2;
     const int per_head = kTile * C;
@@ -120,9 +131,8 @@ __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict_
         const int lane = q & 63, s = (q >> 6) % SD, kh = (q >> 6) / SD;
         const int r = 32 * kh + swap23(lane & 31);
         const int cc = 2 * s + (lane >> 5);
-        const int64_t t = tok[r];
         dst[(((int64_t)b * H + h) * n_tiles + tile) * per_head + q] =
-            zero_if_padding<kPad>(src[(((int64_t)b * n_ras + row_or_zero<kPad>(t)) * H + h) * C + cc], t);
+            src_chunk<kTiled, kPad>(src, b, h, H, C, cc, tok[r], n_ras, n_tot);
     }
 }
 
@@ -133,12 +143,12 @@ __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict_
 // group of 8 tokens, 8-channel chunk): a thread reads 8 token rows of 16 bytes
 // (256-byte head rows across a wave), transposes the 8 x 8 block of bf16
 // values in registers and writes 8 chunks for 8 consecutive lanes (128 bytes
-// contiguous).
+// contiguous).  kTiled: the source is the tiled layout instead.
 __device__ inline uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
 __device__ inline uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 __device__ inline uint32_t word_of(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
 
-template <bool kPad>
+template <bool kPad, bool kTiled = false>
 __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         const int32_t* __restrict__ perm, int H, int C,
                                                         int n_prefix, int64_t n_video, int64_t n_tot,
@@ -148,7 +158,8 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
     const int64_t tile = blockIdx.x;
     const int64_t p0 = tile * kTile;
     const int64_t n_tiles = n_tot / kTile;
-    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    if (threadIdx.x < kTile)
+        tok[threadIdx.x] = kTiled ? p0 + threadIdx.x : slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
     __syncthreads();
     const int OD = C / 4;  // 32-channel blocks
     const int items = H * 8 * C;
@@ -157,10 +168,7 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
         const int g = (it / C) % 8;
         const int h = it / (8 * C);
         uint4 r0, r1, r2, r3, r4, r5, r6, r7;
-        auto row = [&](int i) {
-            const int64_t t = tok[8 * g + i];
-            return zero_if_padding<kPad>(src[(((int64_t)b * n_ras + row_or_zero<kPad>(t)) * H + h) * C + dc], t);
-        };
+        auto row = [&](int i) { return src_chunk<kTiled, kPad>(src, b, h, H, C, dc, tok[8 * g + i], n_ras, n_tot); };
         r0 = row(0); r1 = row(1); r2 = row(2); r3 = row(3);
         r4 = row(4); r5 = row(5); r6 = row(6); r7 = row(7);
         // tokens 8 g .. 8 g + 7 = 32 kh + 16 c + 8 hf + e; channels 8 dc + e'
@@ -188,7 +196,195 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
     }
 }
 
+// Q gather with pooling.  One block per (batch, 64-token tile); thread =
+// (head, 16-byte chunk c), which loops over the tile's 64 tokens: it reads the
+// chunk of each token's raster row (a block reads whole 6 KB rows for 24 heads
+// of D = 128), writes it to the tiled layout, and for a video tile adds it up
+// in double (exact for 64 bf16 values), so the tile means cost no second read
+// of the tensor.  The C threads of a head are adjacent lanes of one wave: they
+// fold the sum of squares of the means for the norm.
+template <bool kPad>
+__global__ __launch_bounds__(1024) void gather_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           const int32_t* __restrict__ perm, int H, int C,
+                                                           int n_prefix, int64_t n_video, int64_t n_tot,
+                                                           int64_t n_ras, PoolOut po) {
+    __shared__ int64_t tok[kTile];
+    __shared__ int real;
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x, p0 = tile * kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        tok[threadIdx.x] = t;
+        const int nr = __popcll(__ballot(t >= 0));
+        if (threadIdx.x == 0) real = nr;
+    }
+    __syncthreads();
+    const bool pool = p0 >= n_prefix;
+    const int nvt = (int)(n_video / kTile);
+    const int64_t vt = (p0 - n_prefix) / kTile;
+    const double count = kPad ? (double)real : (double)kTile;
+    for (int pr = threadIdx.x; pr < H * C; pr += blockDim.x) {
+        const int h = pr / C, c = pr % C;
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int pl0 = 0; pl0 < kTile; pl0 += 8) {
+            uint4 x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = src_chunk<false, kPad>(src, b, h, H, C, c, tok[pl0 + e], n_ras, n_tot);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                dst[(((int64_t)b * H + h) * n_tot + p0 + pl0 + e) * C + c] = x[e];
+                if (pool) {
+                    acc[0] += (double)__uint_as_float(x[e].x << 16);
+                    acc[1] += (double)__uint_as_float(x[e].x & 0xffff0000u);
+                    acc[2] += (double)__uint_as_float(x[e].y << 16);
+                    acc[3] += (double)__uint_as_float(x[e].y & 0xffff0000u);
+                    acc[4] += (double)__uint_as_float(x[e].z << 16);
+                    acc[5] += (double)__uint_as_float(x[e].z & 0xffff0000u);
+                    acc[6] += (double)__uint_as_float(x[e].w << 16);
+                    acc[7] += (double)__uint_as_float(x[e].w & 0xffff0000u);
+                }
+            }
+        }
+        if (pool) {
+            float m[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m[e] = (float)(acc[e] / count);
+            const int64_t bh = (int64_t)b * H + h;
+            float sq = store_pooled8(po, bh, nvt, 8 * C, vt, c, m);
+            for (int o = 1; o < C; o <<= 1) sq += __shfl_xor(sq, o);
+            if (c == 0) po.norm[bh * nvt + vt] = sqrtf(sq);
+        }
+    }
+}
+
+// K gather with pooling, its stores in 256-byte runs.  One block of 256
+// threads per (batch, tile).  Lane l of a wave takes token offset tq = l % 16
+// and chunk group cg = l / 16; the C / 4 waves of a head cover its C chunks
+// (c = 4 (wave mod C/4) + cg), and 16 / C heads go per pass.  A lane moves
+// tokens tq, tq + 16, tq + 32, tq + 48 of its chunk: one 16-byte load from the
+// token's raster row and one store into the K-fragment layout each, where the
+// 16 lanes of a chunk (16 consecutive tokens, which swap23 keeps within their
+// aligned group of 16) write 256 contiguous bytes.  The lane adds its 4 values
+// in double, the 16 lanes of a chunk fold theirs (shuffles over the low four
+// lane bits), the chunk's lane tq = 0 stores the means, and the squares for the
+// norm are folded over the head's chunks through LDS in a fixed order.
+template <bool kPad>
+__global__ __launch_bounds__(256) void gather_kf_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                             const int32_t* __restrict__ perm, int H, int C,
+                                                             int n_prefix, int64_t n_video, int64_t n_tot,
+                                                             int64_t n_ras, PoolOut po) {
+    __shared__ int64_t tok[kTile];
+    __shared__ int real;
+    __shared__ float sqp[4];
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x, p0 = tile * kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        tok[threadIdx.x] = t;
+        const int nr = __popcll(__ballot(t >= 0));
+        if (threadIdx.x == 0) real = nr;
+    }
+    __syncthreads();
+    const bool pool = p0 >= n_prefix;
+    const int nvt = (int)(n_video / kTile);
+    const int64_t vt = (p0 - n_prefix) / kTile;
+    const double count = kPad ? (double)real : (double)kTile;
+    const int64_t n_tiles = n_tot / kTile;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tq = lane & 15, cg = lane >> 4;
+    const int wph = C / 4, hpp = 4 / wph;  // waves per head, heads per pass
+    const int hl = wave / wph;
+    const int c = 4 * (wave % wph) + cg;
+    for (int h0 = 0; h0 < H; h0 += hpp) {
+        const int h = h0 + hl;
+        float sq = 0.f;
+        if (h < H) {
+            uint4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = src_chunk<false, kPad>(src, b, h, H, C, c, tok[tq + 16 * u], n_ras, n_tot);
+            uint4* dh = dst + (((int64_t)b * H + h) * n_tiles + tile) * (kTile * C) + (c >> 1) * 64 + 32 * (c & 1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int pl = tq + 16 * u;
+                dh[(pl >> 5) * (C / 2) * 64 + swap23(pl & 31)] = x[u];
+            }
+            if (pool) {
+                double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc[0] += (double)__uint_as_float(x[u].x << 16);
+                    acc[1] += (double)__uint_as_float(x[u].x & 0xffff0000u);
+                    acc[2] += (double)__uint_as_float(x[u].y << 16);
+                    acc[3] += (double)__uint_as_float(x[u].y & 0xffff0000u);
+                    acc[4] += (double)__uint_as_float(x[u].z << 16);
+                    acc[5] += (double)__uint_as_float(x[u].z & 0xffff0000u);
+                    acc[6] += (double)__uint_as_float(x[u].w << 16);
+                    acc[7] += (double)__uint_as_float(x[u].w & 0xffff0000u);
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
+                if (tq == 0) {
+                    float m[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) m[e] = (float)(acc[e] / count);
+                    sq = store_pooled8(po, (int64_t)b * H + h, nvt, 8 * C, vt, c, m);
+                }
+            }
+        }
+        if (pool) {
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            __syncthreads();  // the previous pass has read sqp
+            if (lane == 0) sqp[wave] = sq;
+            __syncthreads();
+            if (h < H && lane == 0 && wave % wph == 0) {
+                float t = 0.f;
+                for (int w2 = 0; w2 < wph; ++w2) t += sqp[wave + w2];
+                po.norm[((int64_t)b * H + h) * nvt + vt] = sqrtf(t);
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H,
+                              int D, int n_prefix, int64_t n_video, const PoolOut& po, hipStream_t s,
+                              int64_t n_raster_video) {
+    const int64_t n_tot = n_prefix + n_video;
+    const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    const int C = D / 8;
+    const bool pad = n_ras != n_tot;
+    if (kfrag) {
+        auto kernel = pad ? gather_kf_pool_kernel<true> : gather_kf_pool_kernel<false>;
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H, C, n_prefix,
+                           n_video, n_tot, n_ras, po);
+        return hipGetLastError();
+    }
+    const int pairs = H * C;
+    const int threads = pairs >= 1024 ? 1024 : (pairs + 63) / 64 * 64;
+    auto kernel = pad ? gather_pool_kernel<true> : gather_pool_kernel<false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, (const uint4*)src, (uint4*)dst, perm, H, C, n_prefix,
+                       n_video, n_tot, n_ras, po);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiled_to_frag(bool kfrag, const uint16_t* src, uint16_t* dst, int B, int H, int D, int64_t n_tot,
+                                hipStream_t s) {
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    if (kfrag)
+        hipLaunchKernelGGL((gather_kf_kernel<false, true>), grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst,
+                           (const int32_t*)nullptr, H, D / 8, 0, n_tot, n_tot, n_tot);
+    else
+        hipLaunchKernelGGL((gather_vf_kernel<false, true>), grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst,
+                           (const int32_t*)nullptr, H, D / 8, 0, n_tot, n_tot, n_tot);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather_kf(const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H, int D,
                             int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video) {

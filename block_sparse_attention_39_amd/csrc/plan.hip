@@ -9,16 +9,24 @@
 // pool   : HBM-bound read of Q (tiled) and K (K-fragment layout) once; one
 //          wave per tile, 16-byte loads, double accumulation (exact for bf16
 //          inputs), one rounding to float, cross-lane reduction with shuffles.
-// scores : float GEMM per (batch, head) of the pooled vectors, 64x64 output
-//          blocks through LDS.
-// topk   : one block per row; 8-bit radix select on the order-preserving
-//          integer image of the float scores (4 passes, LDS histogram), then an
-//          index-ordered compaction that takes every score above the threshold
-//          and the lowest-numbered ties.
+//          Besides the float means it writes each mean as a bf16 hi/lo pair in
+//          MFMA operand order, and each mean's norm.
+// select : one persistent block of 4 waves per CU; a work item is R query rows
+//          of one (batch, head).  The R x nvt scores are computed on bf16 MFMA
+//          from the hi/lo pairs (hi*hi + hi*lo + lo*hi, float accumulation)
+//          into LDS; no score matrix goes to memory.  Then one wave per row
+//          brackets the k-th largest float score by counts (a sorted sample,
+//          then halving) and settles every key whose float score lies within
+//          the float error bound of the bracket by recomputing its score in
+//          double, in the order of the channels, so that the kept set is
+//          exactly the top k of the double scores.
 #include "bsa_kernels.h"
 
 namespace bsa {
 namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -45,18 +53,9 @@ __device__ inline void acc8(double (&acc)[8], const uint4& x) {
 }
 
 // the exact sums divided by the tile's token count, rounded once to float
-__device__ inline void store_mean8(float* dst, const double (&acc)[8], double count) {
-    float4 lo, hi;
-    lo.x = (float)(acc[0] / count);
-    lo.y = (float)(acc[1] / count);
-    lo.z = (float)(acc[2] / count);
-    lo.w = (float)(acc[3] / count);
-    hi.x = (float)(acc[4] / count);
-    hi.y = (float)(acc[5] / count);
-    hi.z = (float)(acc[6] / count);
-    hi.w = (float)(acc[7] / count);
-    ((float4*)dst)[0] = lo;
-    ((float4*)dst)[1] = hi;
+__device__ inline void mean8(float (&m)[8], const double (&acc)[8], double count) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = (float)(acc[e] / count);
 }
 
 // real tokens of video tile i (64 without padding)
@@ -68,8 +67,8 @@ __device__ inline int tile_count(const PadGeo& g, int64_t i) {
 
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
-                                                   float* __restrict__ qbar, float* __restrict__ kbar, int BH,
-                                                   int n_prefix, int nvt, PadGeo pad) {
+                                                   PoolOut qo, PoolOut ko, int BH, int n_prefix, int nvt,
+                                                   PadGeo pad) {
     constexpr int C = D / 8;         // 16-byte chunks per row
     constexpr int SD = D / 16;       // K-fragment steps
     constexpr int LPG = 64 / (2 * SD);  // lanes per channel group (K)
@@ -85,6 +84,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
     const uint4* src = (is_k ? k : q) + ((bh * n_tot + n_prefix + i * kTile) * C);
     const double count = (double)tile_count(pad, i);  // padding tokens are zeros in the tiled tensors
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float m[8];
     if (!is_k) {
         constexpr int RPI = 64 / C;  // rows covered by one wave-wide load
         const int c = lane % C, r0 = lane / C;
@@ -98,7 +98,13 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
         for (int o = C; o < 64; o <<= 1)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
-        if (lane < C) store_mean8(qbar + t * D + 8 * lane, acc, count);
+        // every lane holds the sums of its chunk c = lane % C
+        mean8(m, acc, count);
+        float sq = 0.f;
+        if (lane < C) sq = store_pooled8(qo, bh, nvt, D, i, c, m);
+#pragma unroll
+        for (int o = 1; o < C; o <<= 1) sq += __shfl_xor(sq, o);
+        if (lane == 0) qo.norm[t] = sqrtf(sq);
     } else {
         const int grp = lane / LPG, part = lane % LPG;
         const int s = grp >> 1, hf = grp & 1;
@@ -106,8 +112,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
 #pragma unroll
         for (int u = 0; u < TPL; ++u) {
             const int tok = part * TPL + u;  // 32 kh + m
-            const int kh = tok >> 5, m = tok & 31;
-            x[u] = src[(kh * SD + s) * 64 + 32 * hf + m];
+            const int kh = tok >> 5, mm = tok & 31;
+            x[u] = src[(kh * SD + s) * 64 + 32 * hf + mm];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -116,155 +122,561 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ q, 
         for (int o = 1; o < LPG; o <<= 1)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o);
-        if (part == 0) store_mean8(kbar + t * D + 16 * s + 8 * hf, acc, count);
+        // the LPG lanes of group grp hold the sums of channels 8 * grp .. +7
+        mean8(m, acc, count);
+        float sq = 0.f;
+        if (part == 0) sq = store_pooled8(ko, bh, nvt, D, i, grp, m);
+#pragma unroll
+        for (int o = LPG; o < 64; o <<= 1) sq += __shfl_xor(sq, o);
+        if (lane == 0) ko.norm[t] = sqrtf(sq);
     }
 }
 
-// ----------------------------------------------------------------- scores --
-// S[bh][i][j] = sum_d A[bh][i][d] B[bh][j][d], float.  Block = 256 threads,
-// 64x64 output block; thread (ty, tx) computes rows 4ty..4ty+3, cols 4tx..4tx+3.
-// Operands are staged transposed in LDS ([d][row]) in slabs of 32 channels.
-__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ A, const float* __restrict__ Bm,
-                                                     float* __restrict__ S, int n, int D) {
-    constexpr int KS = 32;
-    __shared__ float4 As[KS][16 + 1];
-    __shared__ float4 Bs[KS][16 + 1];
-    const int bh = blockIdx.z;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const float* Ab = A + (int64_t)bh * n * D;
-    const float* Bb = Bm + (int64_t)bh * n * D;
-    float acc[4][4] = {};
-    for (int d0 = 0; d0 < D; d0 += KS) {
-        // load 64 rows x 32 channels of A and B: 2048 floats each, 8 per thread
-        for (int e = threadIdx.x; e < 64 * KS; e += 256) {
-            const int row = e / KS, dd = e % KS;
-            const float a = (i0 + row < n) ? Ab[(int64_t)(i0 + row) * D + d0 + dd] : 0.f;
-            const float b = (j0 + row < n) ? Bb[(int64_t)(j0 + row) * D + d0 + dd] : 0.f;
-            reinterpret_cast<float*>(&As[dd][row >> 2])[row & 3] = a;
-            reinterpret_cast<float*>(&Bs[dd][row >> 2])[row & 3] = b;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < KS; ++dd) {
-            const float4 a = As[dd][ty];
-            const float4 b = Bs[dd][tx];
-            const float av[4] = {a.x, a.y, a.z, a.w};
-            const float bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
-        }
-        __syncthreads();
-    }
-    float* Sb = S + (int64_t)bh * n * n;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = i0 + 4 * ty + u;
-        if (i >= n) continue;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int j = j0 + 4 * tx + v;
-            if (j < n) Sb[(int64_t)i * n + j] = acc[u][v];
-        }
-    }
+// ----------------------------------------------------------------- select --
+constexpr int kSelWaves = 8;   // two waves per SIMD: one's latencies hide under the other's work
+constexpr int kSelBlocks = 256;  // persistent blocks: one per CU of the MI355X
+// per-wave scratch, in 32-bit words: two query rows in double (256 words each
+// for D = 128); a lone row's radix counts take the first 256 words, its query
+// row the second 256
+constexpr int kWaveScratch = 512;
+constexpr int kCandidates = 40;  // bracket search stops at this many scores inside the bracket
+enum : uint32_t { kTagOut = 0, kTagIn = 1, kTagMember = 2 };
+
+// |float score - double score| <= coef(D) |qbar| |kbar| + tiny: the hi/lo
+// split leaves at most 3.1 * 2^-16 |q_d k_d| per product (the dropped lo*lo
+// term and the two splits' remainders), and the float accumulation of the
+// 3D exact bf16 products (in up to 3D + 2 additions, each allowed a relative
+// 2^-23 whatever the MFMA's internal rounding) adds at most
+// (3D + 2) 2^-23 (1 + 2^-7)^2 sum_d |q_d k_d|; sum_d |q_d k_d| <= |q| |k|.  The
+// factor 2 covers the float norms' own rounding with a wide margin.
+template <int D>
+__host__ __device__ constexpr float select_coef() {
+    return 2.0f * (3.1f / 65536.f + 1.05f * (3 * D + 2) / 8388608.f);
 }
 
-// ------------------------------------------------------------------ top-k --
-// Order-preserving unsigned image of a float (larger float -> larger key);
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ inline float wave_min(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+// Wave-wide max / min through DPP: butterflies inside each quad, mirrors
+// inside each row of 16 lanes, then row broadcasts; lane 63 ends with the
+// result, which readlane makes uniform.
+template <int CTRL, int ROWS>
+__device__ inline float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+__device__ inline float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f<0xB1, 0xf>(v));   // quad_perm 1,0,3,2
+    v = fmaxf(v, dpp_f<0x4E, 0xf>(v));   // quad_perm 2,3,0,1
+    v = fmaxf(v, dpp_f<0x141, 0xf>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f<0x140, 0xf>(v));  // row_mirror
+    v = fmaxf(v, dpp_f<0x142, 0xa>(v));  // row_bcast15 into rows 1, 3
+    v = fmaxf(v, dpp_f<0x143, 0xc>(v));  // row_bcast31 into rows 2, 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+template <int CTRL, int ROWS>
+__device__ inline int dpp_i(int v) {  // rows outside ROWS read 0
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+__device__ inline int wave_sum_dpp(int v) {
+    v += dpp_i<0xB1, 0xf>(v);
+    v += dpp_i<0x4E, 0xf>(v);
+    v += dpp_i<0x141, 0xf>(v);
+    v += dpp_i<0x140, 0xf>(v);
+    v += dpp_i<0x142, 0xa>(v);
+    v += dpp_i<0x143, 0xc>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ inline float wave_min_dpp(float v) {
+    v = fminf(v, dpp_f<0xB1, 0xf>(v));
+    v = fminf(v, dpp_f<0x4E, 0xf>(v));
+    v = fminf(v, dpp_f<0x141, 0xf>(v));
+    v = fminf(v, dpp_f<0x140, 0xf>(v));
+    v = fminf(v, dpp_f<0x142, 0xa>(v));
+    v = fminf(v, dpp_f<0x143, 0xc>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ inline int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+__device__ inline int popc(uint64_t m) { return __popcll(m); }
+__device__ inline double readlane_d(double x, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Order-preserving unsigned image of a double (larger value -> larger key);
 // -0 is folded onto +0 so that equal scores give equal keys.
-__device__ inline uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+__device__ inline uint64_t order_key64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x + 0.0);
+    return (u >> 63) ? ~u : (u | (1ull << 63));
 }
 
-// Inclusive scan over a block of 256 threads (4 waves); returns the inclusive
-// prefix and writes the block total to *total.
-__device__ inline int block_scan_256(int x, int* wsum, int* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int v = x;
+// sum_d q[d] k[d] in double, channel by channel in increasing order: every
+// product of two floats is exact in double, so this is the plain sequential
+// double sum of the exact products.  q: the query row, already widened to
+// double in LDS; the key row's loads are all issued before the first product
+// (one memory latency per call).
+template <int D>
+__device__ inline double exact_score(const double* __restrict__ q, const float* __restrict__ k) {
+    float4 kv[D / 4];
+#pragma unroll
+    for (int d = 0; d < D / 4; ++d) kv[d] = ((const float4*)k)[d];
+    double s = 0.0;
+#pragma unroll
+    for (int d = 0; d < D / 4; ++d) {
+        s = fma(q[4 * d], (double)kv[d].x, s);
+        s = fma(q[4 * d + 1], (double)kv[d].y, s);
+        s = fma(q[4 * d + 2], (double)kv[d].z, s);
+        s = fma(q[4 * d + 3], (double)kv[d].w, s);
+    }
+    return s;
+}
+
+// A query row widened to double into the wave's scratch (lanes 0 .. D/2-1).
+template <int D>
+__device__ inline void stage_query(double* dst, const float* __restrict__ q, int lane) {
+    if (lane < D / 2) {
+        const float2 v = ((const float2*)q)[lane];
+        dst[2 * lane] = (double)v.x;
+        dst[2 * lane + 1] = (double)v.y;
+    }
+}
+
+// Threshold digit of a histogram scanned from the top: with lane l holding
+// the W counts of digits top - W*l - 0 .. top - W*l - (W-1) in h, the digit
+// at which the running count from the top reaches `need`, and the count of
+// the digits above it.  Returns false if no lane reaches `need`.
+template <int W>
+__device__ inline bool top_digit(const int (&h)[W], int top, int need, int lane, int& digit, int& above) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < W; ++q) c += h[q];
+    int incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o);
-        if (lane >= o) v += y;
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
     }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    return v + before;
+    const int excl = incl - c;
+    const uint64_t cm = __ballot(excl < need && incl >= need);
+    if (cm == 0) return false;
+    const int cl = __ffsll((long long)cm) - 1;
+    int d = 0, run = excl;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+        if (!found && run + h[q] >= need) {
+            d = top - W * lane - q;
+            found = true;
+        } else if (!found) {
+            run += h[q];
+        }
+    }
+    digit = __builtin_amdgcn_readlane(d, cl);
+    above = __builtin_amdgcn_readlane(run, cl);
+    return true;
 }
 
-// One block per row of scores.  Fixed keep: k per row, written at row * k.
-// Variable keep (row_ptr not null): row r0 + row keeps row_ptr[r + 1] -
-// row_ptr[r] tiles, written at row_ptr[r].
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ S, int32_t* __restrict__ idx, int n,
-                                                   int k_fixed, const int64_t* __restrict__ row_ptr, int64_t r0) {
-    extern __shared__ uint32_t keys[];  // [n]
-    __shared__ int hist[256];
-    __shared__ int wsum[4];
-    __shared__ int sel_digit, sel_above;
-    const int64_t row = blockIdx.x;
-    const float* s = S + row * n;
-    int k = k_fixed;
-    int32_t* out = idx + row * k_fixed;
-    if (row_ptr) {
-        const int64_t beg = row_ptr[r0 + row];
-        k = (int)(row_ptr[r0 + row + 1] - beg);
-        out = idx + beg;
+// The selection of one row by one wave, in three stages.  The row's n float
+// scores are read from LDS into registers (key j = lane + 64 p in x[p]); the
+// LDS row is then reused for the members' verdicts and the output.
+//  1. classify_row: a bracket lo <= T <= hi of the k-th largest float score
+//     T, from the row's extremes and counts (fewer than k scores above hi, at
+//     least k at or above lo), narrowed by interpolation until at most
+//     kCandidates scores lie in between.  With e bounding |float score -
+//     double score|: a key with float score above hi + 2e has a double score
+//     above that of every key whose float score is at most T, and at most
+//     k - 1 keys have a float score above T, so it is among the top k; a key
+//     below lo - 2e is beaten by the (at least k) keys with float scores >= T,
+//     so it is not.  The keys in between are the members.
+//  2. resolve: the members are scored again in double (both rows of a wave
+//     in one pass when their members fit in 64 lanes) and the best
+//     k - (keys above) of them by (-double score, index) complete the set;
+//     many members go through an 8-bit radix select of the double scores.
+//  3. output_row: the kept keys compacted in ascending order and written out.
+template <int P>
+struct RowState {
+    static constexpr int NW = (P + 31) / 32;
+    uint32_t inb[NW], memb[NW];  // this lane's keys above the band / inside it
+    int32_t* out;
+    int64_t rid;
+    float* row;
+    int k, nu, nm, need, my_mem, taken;
+    bool ok, uniform, done;
+};
+
+template <int D, int P>
+__device__ void classify_row(RowState<P>& st, const SelectArgs& a, float* row, int64_t bh, int i, float kmax,
+                             int lane) {
+    constexpr int NW = RowState<P>::NW;
+    const int n = a.nvt;
+    st.row = row;
+    st.rid = bh * n + i;
+    if (a.row_ptr) {
+        const int64_t b0 = a.row_ptr[st.rid];
+        st.k = (int)(a.row_ptr[st.rid + 1] - b0);
+        st.out = a.idx + b0;
+    } else {
+        st.k = a.k_fixed;
+        st.out = a.idx + st.rid * a.k_fixed;
     }
-    for (int j = threadIdx.x; j < n; j += 256) keys[j] = order_key(s[j]);
-    uint32_t prefix = 0, mask = 0;
-    int need = k;  // how many of the keys matching `prefix` are still to take
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[threadIdx.x] = 0;
-        __syncthreads();
-        for (int j = threadIdx.x; j < n; j += 256) {
-            const uint32_t key = keys[j];
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    const int k = st.k = min(max(st.k, 0), n);
+    st.done = k == 0 || k == n;
+    st.nu = st.nm = st.need = st.my_mem = st.taken = 0;
+    st.ok = true;
+    st.uniform = true;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) st.inb[w] = st.memb[w] = 0u;
+    if (st.done) {
+        if (k == n)  // every key
+            for (int j = lane; j < n; j += 64) st.out[j] = j;
+        return;
+    }
+    // keys past n read as NaN: every ordered comparison below is false for them
+    float x[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) x[p] = lane + 64 * p < n ? row[lane + 64 * p] : __builtin_nanf("");
+    const float qn = a.qnorm[st.rid];
+    const float e = select_coef<D>() * qn * kmax + 0x1p-110f * (1.f + qn + kmax);
+    const float e2 = 2.f * e;
+    // counts over the row: per-lane counters in four independent chains,
+    // then one DPP sum
+    auto count_gt = [&](float t) {
+        int c[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < P; ++p) c[p & 3] += x[p] > t ? 1 : 0;
+        return wave_sum_dpp(c[0] + c[1] + c[2] + c[3]);
+    };
+    auto count_ge = [&](float t) {
+        int c[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < P; ++p) c[p & 3] += x[p] >= t ? 1 : 0;
+        return wave_sum_dpp(c[0] + c[1] + c[2] + c[3]);
+    };
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        mn = fminf(mn, x[p]);
+        mx = fmaxf(mx, x[p]);
+    }
+    mn = wave_min_dpp(mn);
+    mx = wave_max_dpp(mx);
+    // the bracket: steps cut it where a straight line through the two counts
+    // reaches k (at least a twentieth of the width off either end)
+    float lo = mn, hi = mx;
+    int gl = count_ge(lo), gh = 0;
+    for (int it = 0; it < 48 && gl - gh > kCandidates; ++it) {
+        const float w = hi - lo;
+        const float f = fminf(fmaxf((float)(k - gh) / (float)(gl - gh), 0.05f), 0.95f);
+        const float mid = hi - w * f;
+        if (!(mid > lo && mid < hi)) break;
+        const int c = count_gt(mid);
+        if (c < k) {
+            hi = mid;
+            gh = c;
+        } else {
+            lo = mid;
+            gl = c;  // #{x > mid}: a lower bound of #{x >= lo}, enough to steer
+        }
+    }
+    st.ok = gl >= k && count_gt(hi) < k;
+    const float hi_v = hi + e2, lo_v = lo - e2;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const bool in = x[p] > hi_v;
+        const bool mem = !in && x[p] >= lo_v;
+        st.inb[p / 32] |= in ? 1u << (p % 32) : 0u;
+        st.memb[p / 32] |= mem ? 1u << (p % 32) : 0u;
+    }
+    int my_in = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        my_in += __popc(st.inb[w]);
+        st.my_mem += __popc(st.memb[w]);
+    }
+    st.nu = wave_sum_dpp(my_in);
+    st.nm = wave_sum_dpp(st.my_mem);
+    st.need = k - st.nu;
+    st.ok = st.ok && st.need >= 0 && st.need <= st.nm;
+    st.uniform = st.need == 0 || st.need == st.nm;  // members all out or all in
+    st.taken = st.uniform ? st.need : 0;
+}
+
+// List a row's members into ml[base ..] (lane by lane: lane l's run starts
+// after the members of the lanes below, a prefix sum from the ballots of the
+// count's bits).
+template <int P>
+__device__ inline void list_members(const RowState<P>& st, int* ml, int base, int lane) {
+    int first = base;
+#pragma unroll
+    for (int b = 0; b < 7; ++b) first += lanes_below(__ballot((st.my_mem >> b) & 1)) << b;
+#pragma unroll
+    for (int w = 0; w < RowState<P>::NW; ++w) {
+        uint32_t bits = st.memb[w];
+        while (bits) {
+            const int p = 32 * w + __builtin_ctz(bits);
+            bits &= bits - 1;
+            ml[first++] = lane + 64 * p;
+        }
+    }
+}
+
+// Members of one row (at most 64) or of two rows (together at most 64) in
+// lanes 0 .. nm0 + nm1 - 1: each scored in double, ranked within its row by
+// (-double score, index), the verdict written to its row's LDS area.
+template <int D, int P>
+__device__ void resolve_lanes(RowState<P>& s0, RowState<P>& s1, bool two, const SelectArgs& a, int64_t bh,
+                              int lane, double* qd, int* ml) {
+    const int n = a.nvt;
+    const int nm0 = s0.nm, ntot = nm0 + (two ? s1.nm : 0);
+    list_members(s0, ml, 0, lane);
+    if (two) list_members(s1, ml, nm0, lane);
+    stage_query<D>(qd, a.qbar + s0.rid * D, lane);
+    if (two) stage_query<D>(qd + D, a.qbar + s1.rid * D, lane);
+    const bool first = lane < nm0;
+    const int jm = lane < ntot ? ml[lane] : 0;
+    const double s = lane < ntot ? exact_score<D>(first ? qd : qd + D, a.kbar + (bh * n + jm) * D) : 0.0;
+    const int m_lo = first ? 0 : nm0, m_hi = first ? nm0 : ntot;
+    int rank = 0;
+    for (int m2 = 0; m2 < ntot; ++m2) {
+        const double s2 = readlane_d(s, m2);
+        const int j2 = __builtin_amdgcn_readlane(jm, m2);
+        rank += (m2 >= m_lo && m2 < m_hi && ((s2 > s) || (s2 == s && j2 < jm))) ? 1 : 0;
+    }
+    const bool sel = lane < ntot && rank < (first ? s0.need : s1.need);
+    if (lane < ntot) ((uint32_t*)(first ? s0.row : s1.row))[jm] = sel ? 1u : 0u;
+    s0.taken = popc(__ballot(sel && first));
+    if (two) s1.taken = popc(__ballot(sel && !first));
+}
+
+// Many members: flagged in the LDS row, their double scores as order keys in
+// the wave's scratch (indexed by key), then an 8-bit radix select of the
+// need-th largest key; equal keys go to the lower index.  (A rare path:
+// loops, not unrolled code.)
+template <int D, int P>
+__device__ void resolve_radix(RowState<P>& st, const SelectArgs& a, int64_t bh, int lane, uint32_t* hw,
+                              uint64_t* fb) {
+    const int n = a.nvt;
+    uint32_t* verdict = (uint32_t*)st.row;
+    double* qd = (double*)(hw + 256);
+    stage_query<D>(qd, a.qbar + st.rid * D, lane);
+    auto mem_p = [&](int p) { return ((st.memb[p / 32] >> (p % 32)) & 1u) != 0u; };
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (lane + 64 * p < n) verdict[lane + 64 * p] = mem_p(p) ? 2u : 0u;
+    for (int j = lane; j < n; j += 64)
+        if (verdict[j] == 2u)
+            __hip_atomic_store(fb + j, order_key64(exact_score<D>(qd, a.kbar + (bh * n + j) * D)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+    uint64_t prefix = 0, pmask = 0;
+    int rem = st.need;
+    bool ok = true;
+    for (int shift = 56; ok && shift >= 0; shift -= 8) {
+        for (int b = lane; b < 256; b += 64) hw[b] = 0u;
+        for (int j = lane; j < n; j += 64)
+            if (verdict[j] == 2u) {
+                const uint64_t key = __hip_atomic_load(fb + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255u], 1u);
+            }
+        int h4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h4[q] = (int)hw[255 - 4 * lane - q];
+        int digit = 0, ab = 0;
+        ok = top_digit(h4, 255, rem, lane, digit, ab);
+        rem -= ab;
+        prefix |= (uint64_t)(uint32_t)digit << shift;
+        pmask |= 0xffull << shift;
+    }
+    int ties = 0;
+    st.taken = 0;
+    for (int j0 = 0; ok && j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        const bool mem = j < n && verdict[j] == 2u;
+        const uint64_t key = mem ? __hip_atomic_load(fb + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        const bool eq = mem && key == prefix;
+        const uint64_t em = __ballot(eq);
+        const bool sel = mem && (key > prefix || (eq && ties + lanes_below(em) < rem));
+        if (mem) verdict[j] = sel ? 1u : 0u;
+        ties += popc(em);
+        st.taken += popc(__ballot(sel));
+    }
+    st.ok = st.ok && ok;
+}
+
+// Exactly k keys must be kept (always so for finite scores; otherwise, e.g.
+// with NaN scores, the first k keys keep the list well formed).  A lane reads
+// the verdicts of its own members, then the kept keys are compacted into the
+// LDS row (a write lands at a position below 64 (p + 1), whose verdicts have
+// been read) and copied out in order.
+template <int P>
+__device__ void output_row(const RowState<P>& st, int n, int lane) {
+    constexpr int NW = RowState<P>::NW;
+    const bool degenerate = !st.ok || st.nu + st.taken != st.k;
+    const uint32_t* verdict = (const uint32_t*)st.row;
+    uint32_t selb[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        selb[w] = st.inb[w] | (st.uniform && st.need > 0 ? st.memb[w] : 0u);
+        if (!st.uniform) {
+            uint32_t bits = st.memb[w];
+            while (bits) {
+                const int b = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (verdict[lane + 64 * (32 * w + b)] != 0u) selb[w] |= 1u << b;
+            }
+        }
+    }
+    int* outl = (int*)st.row;
+    int pos = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int j = lane + 64 * p;
+        const bool sel = degenerate ? j < st.k : ((selb[p / 32] >> (p % 32)) & 1u) != 0u;
+        const uint64_t sm = __ballot(sel);
+        if (sel) outl[pos + lanes_below(sm)] = j;
+        pos += popc(sm);
+    }
+    for (int q = lane; q < st.k; q += 64) st.out[q] = outl[q];
+}
+
+// The rows r0 (and r1 when two) of an item, by one wave.
+template <int D, int P>
+__device__ void select_rows(const SelectArgs& a, float* row0, float* row1, int i0, int i1, bool two, int64_t bh,
+                            float kmax, int lane, uint32_t* hw, int* ml, uint64_t* fb) {
+    RowState<P> s0, s1;
+    classify_row<D, P>(s0, a, row0, bh, i0, kmax, lane);
+    if (two) classify_row<D, P>(s1, a, row1, bh, i1, kmax, lane);
+    const bool act0 = !s0.done && s0.ok && !s0.uniform;
+    const bool act1 = two && !s1.done && s1.ok && !s1.uniform;
+    double* qd = (double*)hw;
+    if (act0 && act1 && s0.nm + s1.nm <= 64) {
+        resolve_lanes<D, P>(s0, s1, true, a, bh, lane, qd, ml);
+    } else {
+        if (act0) {
+            if (s0.nm <= 64)
+                resolve_lanes<D, P>(s0, s0, false, a, bh, lane, qd, ml);
+            else
+                resolve_radix<D, P>(s0, a, bh, lane, hw, fb);
+        }
+        if (act1) {
+            if (s1.nm <= 64)
+                resolve_lanes<D, P>(s1, s1, false, a, bh, lane, qd, ml);
+            else
+                resolve_radix<D, P>(s1, a, bh, lane, hw, fb);
+        }
+    }
+    if (!s0.done) output_row<P>(s0, a.nvt, lane);
+    if (two && !s1.done) output_row<P>(s1, a.nvt, lane);
+}
+
+// Persistent grid of at most kSelBlocks blocks of 8 waves; item = R
+// consecutive query rows of one (batch, head).  Phase 1: every wave takes
+// every eighth block of 16 keys and computes the 16 x 16 float scores of the rows' 16-row block with
+// three v_mfma_f32_16x16x32_bf16 per 32 channels (hi*hi, hi*lo, lo*hi), its
+// next key block's operands in flight; the R wanted rows go to LDS.  Phase 2:
+// one wave per row (select_row).  R * (NMAX + 4) floats of LDS hold the rows.
+template <int D, int R, int NMAX>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void select_kernel(SelectArgs a) {
+    constexpr int SD = D / 32;          // 32-channel k-steps
+    constexpr int STRIDE = NMAX + 4;    // row stride: the 4 row groups of a store land on distinct banks
+    __shared__ __attribute__((aligned(16))) float sc[R * STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kSelWaves][kWaveScratch];
+    __shared__ int mlist[kSelWaves][64];
+    __shared__ float red[kSelWaves];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = a.nvt;
+    const int nb = (n + 15) / 16;
+    const int per_bh = (n + R - 1) / R;
+    const int64_t items = (int64_t)a.BH * per_bh;
+    uint64_t* fb = a.scratch + ((int64_t)blockIdx.x * kSelWaves + wave) * n;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t bh = it / per_bh;
+        const int i0 = (int)(it % per_bh) * R;
+        __syncthreads();  // the previous item's rows and red[] are no longer read
+        float km = 0.f;
+        for (int j = tid; j < n; j += 64 * kSelWaves) km = fmaxf(km, a.knorm[bh * n + j]);
+        km = wave_max_dpp(km);
+        if (lane == 0) red[wave] = km;
+        {
+            const int roff = i0 % 16;
+            const uint4* qs = (const uint4*)a.qsplit + (bh * nb + i0 / 16) * SD * 128 + lane;
+            const uint4* ks = (const uint4*)a.ksplit + bh * nb * SD * 128 + lane;
+            bf16x8 qa[SD][2], ka[SD][2], kb[SD][2];
+#pragma unroll
+            for (int s2 = 0; s2 < SD; ++s2)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) qa[s2][p] = __builtin_bit_cast(bf16x8, qs[(2 * s2 + p) * 64]);
+            auto load = [&](bf16x8 (&dst)[SD][2], int jb) {
+#pragma unroll
+                for (int s2 = 0; s2 < SD; ++s2)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        dst[s2][p] = __builtin_bit_cast(bf16x8, ks[((int64_t)jb * SD + s2) * 128 + p * 64]);
+            };
+            auto score = [&](const bf16x8 (&kv)[SD][2], int jb) {
+                f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < SD; ++s2) {
+                    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2][0], kv[s2][0], c0, 0, 0, 0);
+                    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2][0], kv[s2][1], c1, 0, 0, 0);
+                    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2][1], kv[s2][0], c1, 0, 0, 0);
+                }
+                const f32x4 c = c0 + c1;
+                // lane l holds key 16 jb + l % 16 of rows 4 (l / 16) .. +3
+                const int col = 16 * jb + (lane & 15);
+                if (col < n) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 4 * (lane >> 4) + r - roff;
+                        if (row >= 0 && row < R) sc[row * STRIDE + col] = c[r];
+                    }
+                }
+            };
+            // the next key block's operands are loaded while this one is
+            // scored; past the last block the loads repeat it (unconditional
+            // loads keep the wait counts exact)
+            int jb = wave;
+            load(ka, min(jb, nb - 1));
+            while (jb < nb) {
+                int jn = jb + kSelWaves;
+                load(kb, min(jn, nb - 1));
+                score(ka, jb);
+                jb = jn;
+                if (jb >= nb) break;
+                jn = jb + kSelWaves;
+                load(ka, min(jn, nb - 1));
+                score(kb, jb);
+                jb = jn;
+            }
         }
         __syncthreads();
-        // counts from the top digit down: thread t holds digit 255 - t
-        const int cnt = hist[255 - threadIdx.x];
-        int tot;
-        const int incl = block_scan_256(cnt, wsum, &tot);
-        const int excl = incl - cnt;
-        if (excl < need && incl >= need) {
-            sel_digit = 255 - threadIdx.x;
-            sel_above = excl;
+        float kmax = red[0];
+#pragma unroll
+        for (int w = 1; w < kSelWaves; ++w) kmax = fmaxf(kmax, red[w]);
+        // one wave per row, or per pair of rows (R = 16: rows w and w + 8)
+        const int r0 = wave, r1 = wave + kSelWaves;
+        if (r0 < R && i0 + r0 < n) {
+            const bool two = r1 < R && i0 + r1 < n;
+            select_rows<D, NMAX / 64>(a, sc + r0 * STRIDE, sc + (two ? r1 : r0) * STRIDE, i0 + r0, i0 + r1, two, bh,
+                                      kmax, lane, hist[wave], mlist[wave], fb);
         }
-        __syncthreads();
-        need -= sel_above;
-        prefix |= (uint32_t)sel_digit << shift;
-        mask |= 255u << shift;
-        __syncthreads();
-    }
-    // prefix is now the key of the k-th largest score; `need` of the keys equal
-    // to it are taken, lowest index first.  Each thread owns a contiguous run
-    // of indices, so two block scans (ties before the run, selected entries
-    // before the run) place its selections in ascending order.
-    const uint32_t thr = prefix;
-    const int per = (n + 255) / 256;
-    const int j_lo = min((int)threadIdx.x * per, n), j_hi = min(j_lo + per, n);
-    int my_above = 0, my_ties = 0;
-    for (int j = j_lo; j < j_hi; ++j) {
-        const uint32_t key = keys[j];
-        my_above += key > thr;
-        my_ties += key == thr;
-    }
-    int tot;
-    const int ties_before = block_scan_256(my_ties, wsum, &tot) - my_ties;
-    const int my_take = my_above + min(max(need - ties_before, 0), my_ties);
-    int pos = block_scan_256(my_take, wsum, &tot) - my_take;
-    int tie_rank = ties_before;
-    for (int j = j_lo; j < j_hi; ++j) {
-        const uint32_t key = keys[j];
-        const bool tie = key == thr;
-        if (key > thr || (tie && tie_rank < need)) out[pos++] = j;
-        tie_rank += tie;
     }
 }
 
@@ -366,41 +778,39 @@ hipError_t launch_structured(const StructRule& sr, int BH, int H, int64_t* row_p
     return hipGetLastError();
 }
 
-hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, float* qbar, float* kbar, int BH,
+hipError_t launch_pool(const uint16_t* q_tiled, const uint16_t* k_frag, const PoolOut& q, const PoolOut& k, int BH,
                        int n_prefix, int nvt, int D, hipStream_t s, const PadGeo& pad) {
     const int64_t tiles = 2LL * BH * nvt;
     if (tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((tiles + 3) / 4));
     if (D == 128)
-        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag,
-                           qbar, kbar, BH, n_prefix, nvt, pad);
+        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag, q,
+                           k, BH, n_prefix, nvt, pad);
     else
-        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag,
-                           qbar, kbar, BH, n_prefix, nvt, pad);
+        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, (const uint4*)q_tiled, (const uint4*)k_frag, q,
+                           k, BH, n_prefix, nvt, pad);
     return hipGetLastError();
 }
 
-hipError_t launch_scores(const float* qbar, const float* kbar, float* scores, int BH, int n, int D,
-                         hipStream_t s) {
-    if (BH == 0 || n == 0) return hipSuccess;
-    const dim3 grid((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64), (unsigned)BH);
-    hipLaunchKernelGGL(scores_kernel, grid, dim3(256), 0, s, qbar, kbar, scores, n, D);
-    return hipGetLastError();
+size_t select_scratch_bytes(int nvt) { return (size_t)kSelBlocks * kSelWaves * (size_t)nvt * sizeof(uint64_t); }
+
+template <int D>
+static hipError_t launch_select_d(const SelectArgs& a, hipStream_t s) {
+    // rows per item: as many as LDS holds for this many keys
+    auto go = [&](auto kern, int R) {
+        const int64_t items = (int64_t)a.BH * ((a.nvt + R - 1) / R);
+        const unsigned grid = (unsigned)(items < kSelBlocks ? items : kSelBlocks);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kSelWaves), 0, s, a);
+        return hipGetLastError();
+    };
+    if (a.nvt <= 2176) return go(select_kernel<D, 16, 2176>, 16);
+    if (a.nvt <= 4352) return go(select_kernel<D, 8, 4352>, 8);
+    return go(select_kernel<D, 4, 8704>, 4);
 }
 
-hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s) {
-    if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), (size_t)n * sizeof(uint32_t), s, scores, idx,
-                       n, k, (const int64_t*)nullptr, (int64_t)0);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_csr(const float* scores, int32_t* col_idx, const int64_t* row_ptr, int64_t row0, int rows,
-                           int n, hipStream_t s) {
-    if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(256), (size_t)n * sizeof(uint32_t), s, scores,
-                       col_idx, n, 0, row_ptr, row0);
-    return hipGetLastError();
+hipError_t launch_select(const SelectArgs& a, int D, hipStream_t s) {
+    if ((int64_t)a.BH * a.nvt == 0) return hipSuccess;
+    return D == 128 ? launch_select_d<128>(a, s) : launch_select_d<64>(a, s);
 }
 
 }  // namespace bsa

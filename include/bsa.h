@@ -22,7 +22,11 @@
  * A call sequence:  bsa_permute(BUILD) -> bsa_permute(GATHER) for Q,
  * bsa_permute(GATHER_KF) for K, bsa_permute(GATHER_VF) for V -> bsa_plan ->
  * bsa_forward -> bsa_permute(SCATTER) for O; for training, bsa_backward with
- * the raster tensors, the forward's lse and dL/dO.
+ * the raster tensors, the forward's lse and dL/dO.  The same result with the
+ * tile means taken during the gathers (no second read of Q and K):
+ * bsa_permute(GATHER_POOL) for Q and bsa_permute(GATHER_KF_POOL) for K, then
+ * bsa_select in place of bsa_plan.  A caller holding K and V already in the
+ * tiled layout converts them with bsa_permute(TILED_TO_KF / TILED_TO_VF).
  *
  * Layouts (row-major, bf16 = IEEE bfloat16):
  *   raster  bf16 [B][Ntot][H][D]   the dense prefix first (n_prefix tokens, already
@@ -103,7 +107,11 @@ enum {
     BSA_PERM_GATHER = 1,
     BSA_PERM_SCATTER = 2,
     BSA_PERM_GATHER_KF = 3,
-    BSA_PERM_GATHER_VF = 4
+    BSA_PERM_GATHER_VF = 4,
+    BSA_PERM_GATHER_POOL = 5,
+    BSA_PERM_GATHER_KF_POOL = 6,
+    BSA_PERM_TILED_TO_KF = 7,
+    BSA_PERM_TILED_TO_VF = 8
 };
 
 /* Largest number of video tiles per (batch, head) that bsa_plan accepts. */
@@ -130,14 +138,17 @@ typedef struct bsa_desc {
 } bsa_desc;
 
 /*
- * Bytes of device workspace that bsa_plan, bsa_forward and
- * bsa_permute(BUILD, dynamic) need for `desc`; one buffer of this size serves
- * all three on one stream.  Host-only; enqueues nothing.  After bsa_plan's
- * work has run, the workspace starts with the pooled tile means
+ * Bytes of device workspace that bsa_plan, bsa_select, bsa_forward and
+ * bsa_permute (BUILD in dynamic mode, GATHER_POOL, GATHER_KF_POOL) need for
+ * `desc`; one buffer of this size serves all of them on one stream.
+ * Host-only; enqueues nothing.  After bsa_plan's work (or the two pooling
+ * gathers) has run, the workspace starts with the pooled tile means
  *   float qbar[B][H][nVT][D], then float kbar[B][H][nVT][D]
  * (each the mean of the tile's 64 tokens, or of its real tokens on a ragged
- * grid), each region 256-byte aligned;
- * bsa_forward does not overwrite them.
+ * grid), each region 256-byte aligned; bsa_forward does not overwrite them.
+ * About 4 * B*H*nVT*D floats (the means of Q and K and their bf16 hi/lo
+ * pairs) plus 16 KB per video tile of selection scratch: 221 MB for the 720p
+ * grid with B = 2, H = 24, D = 128 (nVT = 1,920).
  */
 bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
 
@@ -158,24 +169,50 @@ bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
  *  op = BSA_PERM_SCATTER: `src` tiled -> `dst` raster (the output).
  *  op = BSA_PERM_GATHER_KF: `src` raster -> `dst` kfrag (K).
  *  op = BSA_PERM_GATHER_VF: `src` raster -> `dst` vfrag (V).
+ *  op = BSA_PERM_GATHER_POOL: as GATHER (Q), and the tile means of Q as
+ *       bsa_plan computes them, written into the workspace (required) for
+ *       bsa_select.
+ *  op = BSA_PERM_GATHER_KF_POOL: as GATHER_KF (K), and the tile means of K
+ *       into the workspace.
+ *  op = BSA_PERM_TILED_TO_KF: `src` tiled -> `dst` kfrag (no perm needed).
+ *  op = BSA_PERM_TILED_TO_VF: `src` tiled -> `dst` vfrag.
  * Gather and scatter read `perm` and copy bf16 values exactly; the prefix
  * tokens keep their positions.  Source and destination must not overlap.
+ * The fragment layouts are what bsa_plan and bsa_forward read K and V in:
+ * each 1 KB of them is one 16-byte-per-lane load into matrix-instruction
+ * operand registers.  A gather writes them straight from the raster layout
+ * (as cheap as a tiled gather); TILED_TO_KF / TILED_TO_VF serve callers that
+ * already hold tiled tensors, for one more read and write of the tensor.
  */
 bsa_status bsa_permute(const bsa_desc *desc, int op, const void *q_raster, int32_t *perm,
                        uint8_t *shape_map, const void *src, void *dst, void *ws,
                        size_t ws_bytes, void *stream);
 
 /*
- * Tile selection.  From Q (tiled) and K (kfrag), bf16: the mean of each video
- * tile's 64 tokens (of its real tokens on a ragged grid; summed exactly,
- * divided by the count, rounded once to float), the score
- * s_ij = sum_d qbar_i[d] kbar_j[d] (float), and per (b, h, video query tile i)
- * the keep_tiles video key tiles with the largest s_ij, equal scores going to
- * the lower tile number, written ascending to `block_idx`.  Prefix tiles are
- * never scored (they are always attended).  Uses the workspace.
+ * Tile selection ("Prism / Kandinsky 6 speed ablation", section "같은 계산량
+ * 안에서 볼 곳을 고르는 Prism": each query tile keeps the key tiles whose
+ * 64-token means score highest).  From Q (tiled) and K (kfrag), bf16: the mean
+ * of each video tile's 64 tokens (of its real tokens on a ragged grid; summed
+ * exactly, divided by the count, rounded once to float), the score
+ * s_ij = sum_d qbar_i[d] kbar_j[d] of the float means, and per (b, h, video
+ * query tile i) the keep_tiles video key tiles with the largest s_ij, equal
+ * scores going to the lower tile number, written ascending to `block_idx`
+ * [B][H][nVT][keep_tiles].  The kept set is exactly the top k of the scores
+ * summed in double in channel order (candidates near the threshold are
+ * re-scored that way), so it does not depend on float rounding.  Prefix
+ * tiles are never scored (they are always attended).  Uses the workspace
+ * (bsa_workspace_size); no score matrix is written to memory.
  */
 bsa_status bsa_plan(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
                     int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The scoring and top-k of bsa_plan alone, from the tile means that
+ * bsa_permute(GATHER_POOL) and bsa_permute(GATHER_KF_POOL) (or an earlier
+ * bsa_plan) left in the workspace.  Same output and errors as bsa_plan.
+ */
+bsa_status bsa_select(const bsa_desc *desc, int32_t *block_idx, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /*
  * Attention over the kept tiles.  `q_tiled` and `o_tiled` are in the tiled
@@ -193,10 +230,27 @@ bsa_status bsa_plan(const bsa_desc *desc, const void *q_tiled, const void *k_fra
  * XCD's L2 for all of them; without it (NULL), one block per query tile.  The
  * results are the same either way.  Calls given the same workspace must not
  * run concurrently.
+ * The grouped launch relies on two things the hardware does but no API
+ * promises: the blocks of one launch are dispatched to the 8 XCDs round-robin
+ * (block b to XCD b mod 8), and all of its blocks (one per CU) are resident at
+ * once.  The wait at the start of each round is bounded, so results never
+ * depend on either; if one fails, rounds start out of step and the run is
+ * slower.  The workspace then records, per call, how many rounds' start
+ * waits gave up (see bsa_forward_stats_offset).
  */
 bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
                        const void *v_frag, const int32_t *block_idx, void *o_tiled, float *lse,
                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Byte offset, inside the workspace of bsa_workspace_size(desc), of the
+ * forward's statistics: int32 stats[2], cleared at the start of every
+ * bsa_forward / bsa_forward_csr call given a workspace and, when its work has
+ * run, stats[0] = rounds of the grouped launch whose bounded start wait gave
+ * up before every block of the group had arrived (0 when the lock step held),
+ * stats[1] = rounds started.  Host-only.
+ */
+bsa_status bsa_forward_stats_offset(const bsa_desc *desc, size_t *offset);
 
 /*
  * Variable keep: per-head and per-row keep counts with the kept lists in CSR
@@ -328,7 +382,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 900
+#define BSA_VERSION 1000
 
 #ifdef __cplusplus
 }

@@ -61,14 +61,21 @@ def test_workspace_size_formula():
     d = bsa.make_desc(2, 24, 128, (32, 48, 80), 480)
     st, n = ws_size(d)
     assert st == OK
-    pooled = 2 * 24 * 1920 * 128 * 4
-    fwd = 8 * 64 * 4   # block-group progress counters of the forward
-    assert n == 2 * pooled + 48 * 1920 * 1920 * 4 + fwd
+    pooled = 2 * 24 * 1920 * 128 * 4          # float means of Q, and of K
+    split = 2 * 24 * 1920 * 128 * 2 * 2       # their bf16 hi/lo pairs (1,920 rows: whole 16-row blocks)
+    norms = 2 * 24 * 1920 * 4                 # their norms
+    select_scratch = 256 * 8 * 1920 * 8       # the selection's fallback scratch: one row per wave of the grid
+    fwd = (8 * 64 + 4) * 4                    # block-group progress counters and statistics of the forward
+    al = lambda x: (x + 255) // 256 * 256
+    assert n == 2 * pooled + 2 * split + 2 * norms + select_scratch + al(fwd)
+    # no score matrix: the workspace is a few percent of one input tensor's size per head
+    assert n < 2 * 24 * 122880 * 128 * 2 // 5
+    assert bsa.forward_stats_offset(d) == n - al(fwd) + 8 * 64 * 4
     # dynamic mode also covers the per-(batch, region, head) statistic
     dd = bsa.make_desc(2, 24, 128, (32, 48, 80), 480, dynamic=True)
     assert ws_size(dd)[1] >= 2 * 240 * 24 * 3 * 8
     # no video: nothing to plan, only the forward's counters
-    assert ws_size(bsa.make_desc(1, 2, 64, (0, 0, 0), 0, n_prefix=128)) == (OK, fwd)
+    assert ws_size(bsa.make_desc(1, 2, 64, (0, 0, 0), 0, n_prefix=128)) == (OK, al(fwd))
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -102,6 +109,7 @@ def test_bad_tile_mode_and_op():
     assert ws_size(d)[0] == ARG
     d = cfg()
     assert lib().bsa_permute(ctypes.byref(d), 9, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
+    assert lib().bsa_permute(ctypes.byref(d), -1, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
 
 
 def test_null_pointers():
@@ -160,15 +168,51 @@ def test_too_many_tiles_for_forward():
 
 def test_permute_ops_match_header():
     for name, val in (("BUILD", bsa.PERM_BUILD), ("GATHER", bsa.PERM_GATHER), ("SCATTER", bsa.PERM_SCATTER),
-                      ("GATHER_KF", bsa.PERM_GATHER_KF), ("GATHER_VF", bsa.PERM_GATHER_VF)):
+                      ("GATHER_KF", bsa.PERM_GATHER_KF), ("GATHER_VF", bsa.PERM_GATHER_VF),
+                      ("GATHER_POOL", bsa.PERM_GATHER_POOL), ("GATHER_KF_POOL", bsa.PERM_GATHER_KF_POOL),
+                      ("TILED_TO_KF", bsa.PERM_TILED_TO_KF), ("TILED_TO_VF", bsa.PERM_TILED_TO_VF)):
         m = re.search(r"BSA_PERM_%s = (\d+)" % name, HEADER)
         assert m and int(m.group(1)) == val
     d = cfg()
-    for op in (bsa.PERM_GATHER_KF, bsa.PERM_GATHER_VF):
+    L = lib()
+    for op in (bsa.PERM_GATHER_KF, bsa.PERM_GATHER_VF, bsa.PERM_GATHER_POOL, bsa.PERM_GATHER_KF_POOL,
+               bsa.PERM_TILED_TO_KF, bsa.PERM_TILED_TO_VF):
         # accepted ops: a missing source is reported as such
-        assert lib().bsa_permute(ctypes.byref(d), op, None, FAKE, None, None, FAKE, None, 0, None) == NULL
-        assert lib().bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE + 8, FAKE, None, 0, None) == ALIGN
-    assert lib().bsa_permute(ctypes.byref(d), 5, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
+        assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, None, FAKE, None, 0, None) == NULL
+        assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE + 8, FAKE, None, 0, None) == ALIGN
+    # the pooling gathers write into the workspace: it must be there and large enough
+    st, need = ws_size(d)
+    for op in (bsa.PERM_GATHER_POOL, bsa.PERM_GATHER_KF_POOL):
+        assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE, None, 0, None) == WS
+        assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == WS
+        assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE, FAKE + 16, need, None) == ALIGN
+        assert L.bsa_permute(ctypes.byref(d), op, None, None, None, FAKE, FAKE, FAKE, need, None) == NULL
+    # the tiled -> fragment conversions need no permutation
+    for op in (bsa.PERM_TILED_TO_KF, bsa.PERM_TILED_TO_VF):
+        assert L.bsa_permute(ctypes.byref(d), op, None, None, None, FAKE, None, None, 0, None) == NULL
+
+
+def test_select_host_checks():
+    """bsa_select: the kept lists and a full workspace are required; sizes and
+    alignment are checked before anything is enqueued."""
+    L = lib()
+    d = cfg()
+    st, need = ws_size(d)
+    assert L.bsa_select(None, FAKE, FAKE, need, None) == NULL
+    assert L.bsa_select(ctypes.byref(d), None, FAKE, need, None) == NULL
+    assert L.bsa_select(ctypes.byref(d), FAKE + 2, FAKE, need, None) == ALIGN
+    assert L.bsa_select(ctypes.byref(d), FAKE, None, need, None) == WS
+    assert L.bsa_select(ctypes.byref(d), FAKE, FAKE, need - 1, None) == WS
+    assert L.bsa_select(ctypes.byref(d), FAKE, FAKE + 16, need, None) == ALIGN
+    big = bsa.make_desc(1, 1, 64, (16, 128, 260), 10)   # 8,320 tiles > the plan limit
+    assert L.bsa_select(ctypes.byref(big), FAKE, FAKE, 1 << 40, None) == UNSUP
+    for e in (cfg(batch=0), bsa.make_desc(1, 2, 64, (0, 0, 0), 0)):
+        assert L.bsa_select(ctypes.byref(e), None, None, 0, None) == OK
+    n = ctypes.c_size_t(0)
+    assert L.bsa_forward_stats_offset(None, ctypes.byref(n)) == NULL
+    assert L.bsa_forward_stats_offset(ctypes.byref(d), None) == NULL
+    assert L.bsa_forward_stats_offset(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value % 4 == 0 and n.value + 8 <= need
 
 
 def test_empty_problems_are_no_ops():

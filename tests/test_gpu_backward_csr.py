@@ -12,7 +12,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, bits_to_f64, to_bits, to_dev
+from parity import GpuRun, attending_tiles, bits_to_f64, check_lse, oracle_lse_delta_rows, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -153,7 +153,6 @@ def test_prism720p_backward_csr_sampled():
     for b, h in [(0, 1), (1, 3)]:
         sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
         qt, kt, vt, dot = (oracle.gather(sl(x), perm[b:b + 1], npf)[0, 0] for x in (q, k, v, do))
-        ot = bits_to_f64(to_bits(o_t[b, h]))
         gt = [bits_to_f64(oracle.gather(to_bits(x[b:b + 1, :, h:h + 1]), perm[b:b + 1], npf)[0, 0])
               .reshape(nqt, 64, wl.head_dim) for x in grads]
         r0 = (b * wl.heads + h) * n
@@ -169,8 +168,12 @@ def test_prism720p_backward_csr_sampled():
         ref_dq = oracle.backward_dq_csr(qt, kt, vt, dot, lse_v, delta, npf, rp, cl, scale, qtiles)
         check_grad(gt[0][qtiles], ref_dq, f"dq b{b} h{h} k={keep_h[h]}")
         ktiles = np.sort(rng.choice(nqt, size=2, replace=False)).astype(np.int32)
-        ref_dk, ref_dv = oracle.backward_dkdv_csr(qt, kt, vt, dot, lse_gpu[b, h].astype(np.float64),
-                                                  (ot * bits_to_f64(dot)).sum(1), npf, rp, cl, scale, ktiles)
+        need = attending_tiles(ktiles, wl.n_prefix_tiles, n, row_ptr=rp, col=cl)
+        lse_all, delta_all, rr = oracle_lse_delta_rows(
+            lambda t: oracle.attention_csr(qt, kt, vt, npf, rp, cl, scale, t), need, dot, wl.n_tokens, wl.head_dim)
+        check_lse(lse_gpu[b, h].reshape(nqt, 64)[need], lse_all[rr].reshape(-1, 64), qt.reshape(nqt, 64, -1)[need],
+                  kt, scale, f"lse b{b} h{h} (extra check)")
+        ref_dk, ref_dv = oracle.backward_dkdv_csr(qt, kt, vt, dot, lse_all, delta_all, npf, rp, cl, scale, ktiles)
         check_grad(gt[1][ktiles], ref_dk, f"dk b{b} h{h}")
         check_grad(gt[2][ktiles], ref_dv, f"dv b{b} h{h}")
     del g, grads

@@ -5,12 +5,11 @@ computes one by one:
 
 * dQ of sampled query tiles: entirely from the oracle (its lse and output of
   those tiles give Delta), with the GPU's selection;
-* dK and dV of sampled key tiles: a key tile collects from the ~480 query
-  tiles that keep it, too many rows to run the oracle's forward on, so these
-  take the lse of the GPU forward (itself checked per query against the
-  oracle by the forward's full-size test) and Delta = dO . O from the GPU's
-  bf16 output, summed in float64 here.  The derivative itself is the
-  oracle's.
+* dK and dV of sampled key tiles: also entirely from the oracle.  A key
+  tile collects from the query tiles that keep it (about 480 each); the
+  oracle's forward runs on exactly those query tiles for their lse and
+  Delta = dO . O.  The GPU forward's lse on the same rows is compared with
+  the oracle's as an extra check.
 
 Tolerance as at the small sizes: max |err| <= 2e-2 * max |ref| and
 mean |err| <= 1e-2 * mean |ref| over the sampled tiles of a tensor.
@@ -22,7 +21,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, bits_to_f64, to_bits, to_dev
+from parity import GpuRun, attending_tiles, bits_to_f64, check_lse, oracle_lse_delta_rows, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +29,7 @@ RTOL_MAX = 2e-2
 RTOL_MEAN = 1e-2
 SAMPLE_BH = [(0, 0), (1, 17)]
 N_QTILES = 6
-N_KTILES = 3
+N_KTILES = 2
 
 
 def check(got, ref, what):
@@ -66,7 +65,6 @@ def test_prism720p_backward_sampled():
     for b, h in SAMPLE_BH:
         sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
         qt, kt, vt, dot = (oracle.gather(sl(x), perm[b:b + 1], npf)[0, 0] for x in (q, k, v, do))
-        ot = oracle.gather(to_bits(g.out[b:b + 1, :, h:h + 1]), perm[b:b + 1], npf)[0, 0]
         grads = [bits_to_f64(oracle.gather(to_bits(x[b:b + 1, :, h:h + 1]), perm[b:b + 1], npf)[0, 0])
                  .reshape(nqt, 64, wl.head_dim) for x in (dq, dk, dv)]
 
@@ -81,10 +79,17 @@ def test_prism720p_backward_sampled():
         ref_dq = oracle.backward_dq(qt, kt, vt, dot, lse, delta, npf, gidx[b, h], scale, qtiles)
         check(grads[0][qtiles], ref_dq, f"dq b{b} h{h} tiles {qtiles.tolist()}")
 
-        # dK, dV: the GPU forward's lse and output for the many rows involved
-        lse_all = lse_gpu[b, h].astype(np.float64)
-        delta_all = (bits_to_f64(ot) * bits_to_f64(dot)).sum(1)
+        # dK, dV: lse and Delta of every query tile that attends a sampled key
+        # tile, from the oracle's forward on those tiles
         ktiles = np.sort(rng.choice(nqt, size=N_KTILES, replace=False)).astype(np.int32)
+        need = attending_tiles(ktiles, wl.n_prefix_tiles, wl.n_video_tiles, idx=gidx[b, h])
+        lse_all, delta_all, rows = oracle_lse_delta_rows(
+            lambda t: oracle.attention(qt, kt, vt, npf, gidx[b, h], scale, t), need, dot, wl.n_tokens,
+            wl.head_dim)
+        print(f"[dk/dv b{b} h{h}] oracle forward on the {need.size} query tiles that attend {ktiles.tolist()}",
+              flush=True)
+        check_lse(lse_gpu[b, h].reshape(nqt, 64)[need], lse_all[rows].reshape(-1, 64),
+                  qt.reshape(nqt, 64, -1)[need], kt, scale, f"lse b{b} h{h} (extra check)")
         ref_dk, ref_dv = oracle.backward_dkdv(qt, kt, vt, dot, lse_all, delta_all, npf, gidx[b, h], scale,
                                               ktiles)
         check(grads[1][ktiles], ref_dk, f"dk b{b} h{h} tiles {ktiles.tolist()}")

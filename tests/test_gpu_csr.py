@@ -77,7 +77,7 @@ def test_csr_matches_oracle(wl, keep_h, rows_range):
             for kk in np.unique(lens[b, h]):
                 rws = np.nonzero(lens[b, h] == kk)[0].astype(np.int32)
                 got = np.stack([col[row_ptr[r0 + i]:row_ptr[r0 + i + 1]] for i in rws])[None, None]
-                n_exact, n_near = check_selection(got, qp, kp, int(kk), rows=rws)
+                n_exact, n_near, n_gamma = check_selection(got, qp, kp, int(kk), rows=rws)
                 print(f"[plan b{b} h{h} k={kk}] rows {len(rws)}: exact {n_exact}, near ties {n_near}", flush=True)
             rp = row_ptr[r0:r0 + n + 1] - row_ptr[r0]
             cl = col[row_ptr[r0]:row_ptr[r0 + n]]
@@ -140,7 +140,7 @@ def test_prism720p_csr_sampled():
         r0 = (b * wl.heads + h) * n
         kk = keep_h[h]
         got = col[row_ptr[r0]:row_ptr[r0 + n]].reshape(1, 1, n, kk)
-        n_exact, n_near = check_selection(got, qp, kp, kk)
+        n_exact, n_near, n_gamma = check_selection(got, qp, kp, kk)
         print(f"[plan b{b} h{h} k={kk}] exact rows {n_exact}, near ties {n_near}", flush=True)
         tiles = np.sort(rng.choice(nqt, size=16, replace=False)).astype(np.int32)
         rp = row_ptr[r0:r0 + n + 1] - row_ptr[r0]

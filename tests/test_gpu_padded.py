@@ -18,7 +18,8 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import (GpuRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, to_dev,
+from parity import (GpuRun, attending_tiles, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout,
+                    oracle_lse_delta_rows, to_bits, to_dev,
                     vfrag_layout)
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +58,7 @@ def check_padded_path(wl, g, q, k, v, qtiles=None, bh=None):
         assert np.array_equal(to_bits(g.att.v_f[b:b + 1, h:h + 1]).reshape(-1), vfrag_layout(vt).reshape(-1))
         qp, kp = oracle.pool_padded(qt, p1, npf), oracle.pool_padded(kt, p1, npf)
         assert np.array_equal(gq[b:b + 1, h:h + 1], qp) and np.array_equal(gk[b:b + 1, h:h + 1], kp)
-        n_exact, n_near = check_selection(gidx[b:b + 1, h:h + 1], qp, kp, wl.keep_tiles)
+        n_exact, n_near, n_gamma = check_selection(gidx[b:b + 1, h:h + 1], qp, kp, wl.keep_tiles)
         tiles = np.arange(nqt, dtype=np.int32) if qtiles is None else qtiles
         ref, ref_lse = oracle.attention_padded(qt[0, 0], kt[0, 0], vt[0, 0], npf, gidx[b, h], real, scale, tiles)
         rows = real.reshape(nqt, 64)[tiles].astype(bool)  # real query rows of the sampled tiles
@@ -174,9 +175,9 @@ def test_padded_backward_matches_oracle(wl):
 def test_prism720p_ragged_backward_sampled():
     """Full size (31 x 45 x 80 padded to 32 x 48 x 80, batch 2, 24 heads,
     head_dim 128, keep 480): dQ of sampled query tiles entirely from the
-    oracle; dK, dV of sampled key tiles from the oracle's derivative with the
-    GPU forward's lse and Delta = dO . O of the GPU's bf16 output (a key tile
-    gathers from about 480 query tiles).  Boundary tiles among the samples."""
+    oracle; dK, dV of sampled key tiles also entirely from the oracle (its
+    forward on the query tiles that attend them, about 480 per key tile, for
+    their lse and Delta = dO . O).  Boundary tiles among the samples."""
     wl = S.WORKLOADS["prism720p_ragged"]
     print(f"\n[case] {wl}", flush=True)
     (q, k, v, do), g, grads = run_padded_backward(wl)
@@ -189,7 +190,6 @@ def test_prism720p_ragged_backward_sampled():
     for b, h in [(0, 5), (1, 22)]:
         sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
         qt, kt, vt, dot = (oracle.gather_padded(sl(x), p1, npf)[0, 0] for x in (q, k, v, do))
-        ot = bits_to_f64(to_bits(g.att.o_t[b, h]))
         gt = [bits_to_f64(oracle.gather_padded(to_bits(x[b:b + 1, :, h:h + 1]), p1, npf)[0, 0])
               .reshape(nqt, 64, wl.head_dim) for x in grads]
         rows = real.reshape(nqt, 64).astype(bool)
@@ -202,9 +202,15 @@ def test_prism720p_ragged_backward_sampled():
         delta[qrows] = (o_ref.reshape(-1, wl.head_dim) * bits_to_f64(dot)[qrows]).sum(1)
         ref_dq = oracle.backward_dq_padded(qt, kt, vt, dot, lse, delta, npf, gidx[b, h], real, scale, qtiles)
         check_grad(gt[0][qtiles][rows[qtiles]], ref_dq[rows[qtiles]], f"dq b{b} h{h}")
-        lse_all = lse_gpu[b, h].astype(np.float64)
-        delta_all = (ot * bits_to_f64(dot)).sum(1)
         ktiles = np.array([1919, 1000], np.int32)
+        need = attending_tiles(ktiles, wl.n_prefix_tiles, wl.n_video_tiles, idx=gidx[b, h])
+        lse_all, delta_all, rr = oracle_lse_delta_rows(
+            lambda t: oracle.attention_padded(qt, kt, vt, npf, gidx[b, h], real, scale, t), need, dot,
+            wl.n_tiled_tokens, wl.head_dim)
+        lrows = rows[need].reshape(-1)   # the real query rows among them
+        check_lse(lse_gpu[b, h].reshape(nqt, 64)[need].reshape(-1)[lrows], lse_all[rr][lrows],
+                  qt.reshape(nqt, 64, -1)[need].reshape(-1, wl.head_dim)[lrows], kt, scale,
+                  f"lse b{b} h{h} (extra check)")
         ref_dk, ref_dv = oracle.backward_dkdv_padded(qt, kt, vt, dot, lse_all, delta_all, npf, gidx[b, h], real,
                                                      scale, ktiles)
         check_grad(gt[1][ktiles][rows[ktiles]], ref_dk[rows[ktiles]], f"dk b{b} h{h}")

@@ -68,7 +68,7 @@ def test_path_matches_oracle(wl):
         gq, gk = g.pooled()
         assert np.array_equal(gq, qp) and np.array_equal(gk, kp)
         gidx = g.block_idx()
-        n_exact, n_near = check_selection(gidx, qp, kp, wl.keep_tiles)
+        n_exact, n_near, n_gamma = check_selection(gidx, qp, kp, wl.keep_tiles)
         print(f"[plan] rows exact {n_exact}, near ties {n_near}", flush=True)
     else:
         gidx = np.zeros((wl.batch, wl.heads, 0, 0), np.int32)

@@ -20,6 +20,7 @@ MAX_VIDEO_TILES = 8192
 MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
 EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_forward", "bsa_forward_stats_offset",
+           "bsa_forward_noalloc",
            "bsa_csr_entries", "bsa_plan_csr",
            "bsa_forward_csr", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
            "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_status_string", "bsa_version")
@@ -62,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.bsa_select.argtypes = [D, P, P, ctypes.c_size_t, P]
         L.bsa_forward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_forward_stats_offset.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        L.bsa_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P]
         I64 = ctypes.c_int64
         L.bsa_csr_entries.argtypes = [D, P, ctypes.POINTER(I64)]
         L.bsa_plan_csr.argtypes = [D, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
@@ -77,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_version.argtypes = []
         for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_forward",
-                  "bsa_forward_stats_offset", "bsa_backward_workspace_size",
+                  "bsa_forward_stats_offset", "bsa_forward_noalloc", "bsa_backward_workspace_size",
                   "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L

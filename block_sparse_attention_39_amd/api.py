@@ -164,6 +164,14 @@ def forward(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, w
                              _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws, _stream(stream)), "bsa_forward")
 
 
+def forward_noalloc(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, stream=None):
+    """bsa_forward's grouped launch without a workspace: for callers that
+    cannot allocate device memory (the library keeps its round counters in a
+    static per-GPU array; calls that overlap on one GPU race)."""
+    _check(lib().bsa_forward_noalloc(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), _ptr(v_frag), _ptr(block_idx),
+                                     _ptr(o_tiled), _ptr(lse), _stream(stream)), "bsa_forward_noalloc")
+
+
 def _keep_heads(desc: Desc, keep_per_head):
     """Host int32 array of the per-head keep counts (or None)."""
     if keep_per_head is None:

@@ -330,18 +330,45 @@ bsa_status bsa_forward_stats_offset(const bsa_desc* desc, size_t* offset) {
     return BSA_OK;
 }
 
+namespace {
+
+// Checks shared by bsa_forward and bsa_forward_noalloc; fills the kernel
+// arguments.
+bsa_status forward_args(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
+                        const int32_t* block_idx, void* o_tiled, float* lse, Geo* g, bsa::ForwardArgs* a) {
+    bsa_status st = check_desc(desc, g);
+    if (st != BSA_OK) return st;
+    if (g->npt + g->nvt > BSA_MAX_TILES) return BSA_ERR_UNSUPPORTED;
+    if (g->empty) return BSA_OK;
+    if (!q_tiled || !k_frag || !v_frag || !o_tiled || (g->nvt > 0 && !block_idx)) return BSA_ERR_NULL;
+    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(v_frag, 16) || misaligned(o_tiled, 16) ||
+        misaligned(block_idx, 4) || misaligned(lse, 4))
+        return BSA_ERR_ALIGN;
+    *a = bsa::ForwardArgs{};
+    a->q = static_cast<const uint16_t*>(q_tiled);
+    a->k = static_cast<const uint16_t*>(k_frag);
+    a->v = static_cast<const uint16_t*>(v_frag);
+    a->idx = block_idx;
+    a->o = static_cast<uint16_t*>(o_tiled);
+    a->lse = lse;
+    a->BH = (int)g->BH;
+    a->npt = (int)g->npt;
+    a->nvt = (int)g->nvt;
+    a->keep = (int)g->k;
+    a->pad = g->pad;
+    a->scale_log2 = desc->scale * 1.4426950408889634f;
+    return BSA_OK;
+}
+
+}  // namespace
+
 bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
                        const int32_t* block_idx, void* o_tiled, float* lse, void* ws, size_t ws_bytes,
                        void* stream) {
     Geo g;
-    bsa_status st = check_desc(desc, &g);
-    if (st != BSA_OK) return st;
-    if (g.npt + g.nvt > BSA_MAX_TILES) return BSA_ERR_UNSUPPORTED;
-    if (g.empty) return BSA_OK;
-    if (!q_tiled || !k_frag || !v_frag || !o_tiled || (g.nvt > 0 && !block_idx)) return BSA_ERR_NULL;
-    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(v_frag, 16) || misaligned(o_tiled, 16) ||
-        misaligned(block_idx, 4) || misaligned(lse, 4))
-        return BSA_ERR_ALIGN;
+    bsa::ForwardArgs a;
+    const bsa_status st = forward_args(desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse, &g, &a);
+    if (st != BSA_OK || g.empty) return st;
     int* progress = nullptr;
     if (ws) {
         const Layout L = layout(g);
@@ -349,20 +376,17 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
-    bsa::ForwardArgs a{};
-    a.q = static_cast<const uint16_t*>(q_tiled);
-    a.k = static_cast<const uint16_t*>(k_frag);
-    a.v = static_cast<const uint16_t*>(v_frag);
-    a.idx = block_idx;
-    a.o = static_cast<uint16_t*>(o_tiled);
-    a.lse = lse;
-    a.BH = (int)g.BH;
-    a.npt = (int)g.npt;
-    a.nvt = (int)g.nvt;
-    a.keep = (int)g.k;
-    a.pad = g.pad;
-    a.scale_log2 = desc->scale * 1.4426950408889634f;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+bsa_status bsa_forward_noalloc(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
+                               const int32_t* block_idx, void* o_tiled, float* lse, void* stream) {
+    Geo g;
+    bsa::ForwardArgs a;
+    const bsa_status st = forward_args(desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse, &g, &a);
+    if (st != BSA_OK || g.empty) return st;
+    if (bsa::forward_workspace_bytes() > bsa::forward_scratch_bytes()) return BSA_ERR_UNSUPPORTED;
+    return launched(bsa::launch_forward_noalloc(a, (int)g.D, static_cast<hipStream_t>(stream)));
 }
 
 // ---- variable keep (CSR lists) ----------------------------------------------

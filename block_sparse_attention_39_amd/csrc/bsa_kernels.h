@@ -220,6 +220,10 @@ struct ForwardArgs {
 size_t forward_workspace_bytes();
 size_t forward_stats_offset();
 hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s);
+// The grouped launch with its counters in a file-scope device array (one per
+// GPU, forward_scratch_bytes() long) instead of a workspace: allocates nothing.
+size_t forward_scratch_bytes();
+hipError_t launch_forward_noalloc(const ForwardArgs& a, int D, hipStream_t s);
 
 struct BackwardArgs {
     // fragment layouts of the tiled tensors (kfrag / vfrag of the C interface)

@@ -52,6 +52,7 @@
 //     the group's L2 once and read there by every block that kept it.  The
 //     waits only shape the schedule; results do not depend on them.
 #include <climits>
+#include <mutex>
 
 #include "bsa_kernels.h"
 
@@ -691,6 +692,54 @@ hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) 
 
 }  // namespace
 
+// ---- the forward without a caller workspace ---------------------------------
+// For callers that cannot allocate device memory: the grouped launch's round
+// counters and statistics live in this file-scope array, one copy per GPU,
+// instead of in a workspace.  On the host its name is only a stand-in for the
+// device array; kernels get the device address that hipGetSymbolAddress
+// returns, looked up once per device with that device current.  The clear
+// kernel zeroes it at the start of every call; calls that overlap on one GPU
+// share it and race.
+constexpr int kScratchInts = 1024;  // 4 KB
+static __device__ __align__(256) int scratch[kScratchInts];
+static_assert(kGroups * kMaxGroupSize + kStatInts <= kScratchInts, "grouped-launch counters exceed the scratch array");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of stream s (the current device
+// for the null stream).
+hipError_t scratch_pointer(hipStream_t s, int** out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (s) {
+        e = hipStreamGetDevice(s, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<int*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+size_t forward_scratch_bytes() { return sizeof(scratch); }
+
 size_t forward_workspace_bytes() { return (size_t)(kGroups * kMaxGroupSize + kStatInts) * sizeof(int); }
 size_t forward_stats_offset() { return (size_t)kGroups * kMaxGroupSize * sizeof(int); }
 
@@ -699,6 +748,14 @@ hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_
     if (a.pad.T != 0)
         return D == 128 ? launch_forward_d<128, true>(a, progress, s) : launch_forward_d<64, true>(a, progress, s);
     return D == 128 ? launch_forward_d<128, false>(a, progress, s) : launch_forward_d<64, false>(a, progress, s);
+}
+
+hipError_t launch_forward_noalloc(const ForwardArgs& a, int D, hipStream_t s) {
+    if ((int64_t)a.BH * (a.npt + a.nvt) == 0) return hipSuccess;
+    int* p = nullptr;
+    const hipError_t e = scratch_pointer(s, &p);
+    if (e != hipSuccess) return e;
+    return launch_forward(a, D, p, s);
 }
 
 }  // namespace bsa

@@ -243,6 +243,21 @@ bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * bsa_forward's grouped launch without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The launch's round counters (2 KB)
+ * live in a file-scope device array of the library (4 KB, one copy per GPU,
+ * held until the process ends) instead of a workspace; this entry point
+ * calls no allocator.  Arguments, layouts, results and errors as bsa_forward
+ * (every problem size bsa_forward accepts fits the array; BSA_ERR_UNSUPPORTED
+ * otherwise).  Every call on a GPU shares that GPU's array, which each call
+ * clears on its stream first: calls that overlap on one GPU race.
+ */
+bsa_status bsa_forward_noalloc(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
+                               const void *v_frag, const int32_t *block_idx, void *o_tiled,
+                               float *lse, void *stream);
+
+/*
  * Byte offset, inside the workspace of bsa_workspace_size(desc), of the
  * forward's statistics: int32 stats[2], cleared at the start of every
  * bsa_forward / bsa_forward_csr call given a workspace and, when its work has

@@ -723,9 +723,10 @@ def main():
         "ms_per_step_stats": step_stats(totals),
         "non_forward_ms": ms_step - fwd_ms,
         "skipped_tile_ratio": 1.0 - wl.keep_tiles / wl.n_video_tiles,
-        "lockstep": {"rounds": rounds, "waits_gave_up": gave_up,
-                     "note": "rounds of the grouped forward launch (last timed step) whose bounded start wait gave "
-                             "up before every block of its XCD group arrived"},
+        "lockstep": {"block_rounds": rounds, "waits_gave_up": gave_up,
+                     "note": "block rounds of the grouped forward launch in the last timed step (one per video "
+                             "query tile), and those whose bounded start wait gave up before every block of its "
+                             "XCD group arrived"},
         "kernels": kernels,
     }
     if wl.dynamic:

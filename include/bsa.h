@@ -153,7 +153,11 @@ typedef struct bsa_desc {
 bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
 
 /*
- * Token permutation between raster and tiled order.
+ * Token permutation between raster and tiled order ("Sparse VideoGen TPU
+ * 최적화", section "실무에서 배울 최적화 기준": the tokens are reordered first so
+ * that every tile is contiguous and a kept tile is read whole; "Prism /
+ * Kandinsky 6 speed ablation", section "같은 계산량 안에서 볼 곳을 고르는 Prism":
+ * the tile's shape may follow how fast each axis of a region varies).
  *  op = BSA_PERM_BUILD: write `perm` [B][Nvideo].  Static mode: the closed-form
  *       tile order (tiles in raster order of the tile grid).  Dynamic mode: read
  *       `q_raster` (bf16 raster, the queries), for every batch element and 8x8x8
@@ -215,7 +219,13 @@ bsa_status bsa_select(const bsa_desc *desc, int32_t *block_idx, void *ws, size_t
                       void *stream);
 
 /*
- * Attention over the kept tiles.  `q_tiled` and `o_tiled` are in the tiled
+ * Attention over the kept tiles ("Sparse VideoGen TPU 최적화", section
+ * "이론적 sparsity와 물리적 sparsity의 차이": a skipped tile costs no work and a
+ * kept tile is computed whole, unmasked; "RTX 4090에서 5초 영상 72초: Ref2VA
+ * VSA", section "조건 토큰은 왜 다르게 다루나": the conditioning prefix is
+ * attended densely by every query and attends to everything; "Prism /
+ * Kandinsky 6 speed ablation", section "같은 계산량 안에서 볼 곳을 고르는 Prism":
+ * the attention itself stays exact over what is kept).  `q_tiled` and `o_tiled` are in the tiled
  * layout, `k_frag` in the kfrag and `v_frag` in the vfrag layout; at most
  * BSA_MAX_TILES tiles per (batch, head).  For each query token of video tile i the
  * keys are the prefix tokens and the tokens of the tiles block_idx[b][h][i][:];
@@ -261,9 +271,10 @@ bsa_status bsa_forward_noalloc(const bsa_desc *desc, const void *q_tiled, const 
  * Byte offset, inside the workspace of bsa_workspace_size(desc), of the
  * forward's statistics: int32 stats[2], cleared at the start of every
  * bsa_forward / bsa_forward_csr call given a workspace and, when its work has
- * run, stats[0] = rounds of the grouped launch whose bounded start wait gave
- * up before every block of the group had arrived (0 when the lock step held),
- * stats[1] = rounds started.  Host-only.
+ * run, stats[0] = block rounds of the grouped launch (one per video query
+ * tile) whose bounded start wait gave up before every block of the group had
+ * arrived (0 when the lock step held), stats[1] = block rounds started.
+ * Host-only.
  */
 bsa_status bsa_forward_stats_offset(const bsa_desc *desc, size_t *offset);
 

@@ -17,7 +17,9 @@ Comparison rules:
   oracle run with the GPU's own selection (identical to the oracle's on every
   row that is not a near tie);
 * log-sum-exp: per query |err| <= 2^-8 (the bf16 rounding of the weights moves
-  the normaliser by at most 2^-9 relative) + 2 * scale * gamma_D * |q| max_j |k_j|
+  the normaliser by at most 2^-8 relative: bf16 keeps 8 significant bits, and
+  |log(1 + x)| <= |x| for x >= 0, 1.004 |x| just below 0, covered by the
+  second term's slack) + 2 * scale * gamma_D * |q| max_j |k_j|
   (float accumulation of the logits).
 """
 from __future__ import annotations

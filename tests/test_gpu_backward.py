@@ -10,9 +10,10 @@ function exactly, with the GPU's selection.
 
 Tolerance, per gradient tensor: max |err| <= 2e-2 * max |ref| and
 mean |err| <= 1e-2 * mean |ref|.  The kernel rounds P and dS to bf16 (relative
-2^-9) before their products and each gradient to bf16 at the end (2^-9), and
-its Delta uses the bf16-rounded forward output; summed over many terms of
-mixed sign these stay a small multiple of 2^-9 of the tensor's scale.
+at most 2^-8: 8 significant bits) before their products and each gradient to
+bf16 at the end (2^-8), and its Delta uses the bf16-rounded forward output;
+summed over many terms of mixed sign these stay a small multiple of 2^-8 of
+the tensor's scale.
 """
 import numpy as np
 import pytest

@@ -139,7 +139,7 @@ constexpr int kSelBlocks = 256;  // persistent blocks: one per CU of the MI355X
 // for D = 128); a lone row's radix counts take the first 256 words, its query
 // row the second 256
 constexpr int kWaveScratch = 512;
-constexpr int kCandidates = 40;  // bracket search stops at this many scores inside the bracket
+constexpr int kCandidates = 12;  // bracket search stops at this many scores inside the bracket
 enum : uint32_t { kTagOut = 0, kTagIn = 1, kTagMember = 2 };
 
 // |float score - double score| <= coef(D) |qbar| |kbar| + tiny: the hi/lo
@@ -212,12 +212,6 @@ __device__ inline int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 __device__ inline int popc(uint64_t m) { return __popcll(m); }
-__device__ inline double readlane_d(double x, int l) {
-    const uint64_t u = (uint64_t)__double_as_longlong(x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
 
 // Order-preserving unsigned image of a double (larger value -> larger key);
 // -0 is folded onto +0 so that equal scores give equal keys.
@@ -320,10 +314,11 @@ struct RowState {
     bool ok, uniform, done;
 };
 
-template <int D, int P>
-__device__ void classify_row(RowState<P>& st, const SelectArgs& a, float* row, int64_t bh, int i, float kmax,
-                             int lane) {
-    constexpr int NW = RowState<P>::NW;
+// The kept count and output of row i; a row keeping none or all of its keys
+// is done here (all: written out when `write`).
+template <int P>
+__device__ inline void row_setup(RowState<P>& st, const SelectArgs& a, float* row, int64_t bh, int i, int lane,
+                                 bool write) {
     const int n = a.nvt;
     st.row = row;
     st.rid = bh * n + i;
@@ -341,80 +336,140 @@ __device__ void classify_row(RowState<P>& st, const SelectArgs& a, float* row, i
     st.ok = true;
     st.uniform = true;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) st.inb[w] = st.memb[w] = 0u;
-    if (st.done) {
-        if (k == n)  // every key
-            for (int j = lane; j < n; j += 64) st.out[j] = j;
-        return;
-    }
-    // keys past n read as NaN: every ordered comparison below is false for them
-    float x[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) x[p] = lane + 64 * p < n ? row[lane + 64 * p] : __builtin_nanf("");
-    const float qn = a.qnorm[st.rid];
-    const float e = select_coef<D>() * qn * kmax + 0x1p-110f * (1.f + qn + kmax);
-    const float e2 = 2.f * e;
-    // counts over the row: per-lane counters in four independent chains,
-    // then one DPP sum
-    auto count_gt = [&](float t) {
-        int c[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int p = 0; p < P; ++p) c[p & 3] += x[p] > t ? 1 : 0;
-        return wave_sum_dpp(c[0] + c[1] + c[2] + c[3]);
-    };
-    auto count_ge = [&](float t) {
-        int c[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int p = 0; p < P; ++p) c[p & 3] += x[p] >= t ? 1 : 0;
-        return wave_sum_dpp(c[0] + c[1] + c[2] + c[3]);
-    };
-    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int w = 0; w < RowState<P>::NW; ++w) st.inb[w] = st.memb[w] = 0u;
+    if (st.done && k == n && write)  // every key
+        for (int j = lane; j < n; j += 64) st.out[j] = j;
+}
+
+// Both rows of a wave go through the bracket search together: each counting
+// pass counts both rows, so the two chains of wave reductions overlap.  A
+// lone row (two = false) runs as row 0 only.
+template <int D, int P>
+__device__ void classify_pair(RowState<P>& s0, RowState<P>& s1, bool two, const SelectArgs& a, float* row0,
+                              float* row1, int64_t bh, int i0, int i1, float kmax, int lane) {
+    constexpr int NW = RowState<P>::NW;
+    const int n = a.nvt;
+    row_setup<P>(s0, a, row0, bh, i0, lane, true);
+    row_setup<P>(s1, a, two ? row1 : row0, bh, two ? i1 : i0, lane, two);
+    if (!two) s1.done = true;
+    if (s0.done && s1.done) return;
+    // keys past n (and rows that are done) read as NaN: every ordered
+    // comparison below is false for them
+    float x0[P], x1[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        mn = fminf(mn, x[p]);
-        mx = fmaxf(mx, x[p]);
+        const bool in = lane + 64 * p < n;
+        x0[p] = in && !s0.done ? row0[lane + 64 * p] : __builtin_nanf("");
+        x1[p] = in && !s1.done ? row1[lane + 64 * p] : __builtin_nanf("");
     }
-    mn = wave_min_dpp(mn);
-    mx = wave_max_dpp(mx);
-    // the bracket: steps cut it where a straight line through the two counts
-    // reaches k (at least a twentieth of the width off either end)
-    float lo = mn, hi = mx;
-    int gl = count_ge(lo), gh = 0;
-    for (int it = 0; it < 48 && gl - gh > kCandidates; ++it) {
-        const float w = hi - lo;
-        const float f = fminf(fmaxf((float)(k - gh) / (float)(gl - gh), 0.05f), 0.95f);
-        const float mid = hi - w * f;
-        if (!(mid > lo && mid < hi)) break;
-        const int c = count_gt(mid);
-        if (c < k) {
-            hi = mid;
-            gh = c;
-        } else {
-            lo = mid;
-            gl = c;  // #{x > mid}: a lower bound of #{x >= lo}, enough to steer
+    const float qn0 = a.qnorm[s0.rid], qn1 = a.qnorm[s1.rid];
+    const float e0 = select_coef<D>() * qn0 * kmax + 0x1p-110f * (1.f + qn0 + kmax);
+    const float e1 = select_coef<D>() * qn1 * kmax + 0x1p-110f * (1.f + qn1 + kmax);
+    // #{x > t} of both rows: per-lane counters in two chains per row, then
+    // one DPP sum per row
+    auto count_gt2 = [&](float t0, float t1, int& c0, int& c1) {
+        int a0[2] = {0, 0}, a1[2] = {0, 0};
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            a0[p & 1] += x0[p] > t0 ? 1 : 0;
+            a1[p & 1] += x1[p] > t1 ? 1 : 0;
         }
-    }
-    st.ok = gl >= k && count_gt(hi) < k;
-    const float hi_v = hi + e2, lo_v = lo - e2;
+        c0 = wave_sum_dpp(a0[0] + a0[1]);
+        c1 = wave_sum_dpp(a1[0] + a1[1]);
+    };
+    float mn0 = __builtin_inff(), mx0 = -__builtin_inff(), mn1 = __builtin_inff(), mx1 = -__builtin_inff();
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        const bool in = x[p] > hi_v;
-        const bool mem = !in && x[p] >= lo_v;
-        st.inb[p / 32] |= in ? 1u << (p % 32) : 0u;
-        st.memb[p / 32] |= mem ? 1u << (p % 32) : 0u;
+        mn0 = fminf(mn0, x0[p]);
+        mx0 = fmaxf(mx0, x0[p]);
+        mn1 = fminf(mn1, x1[p]);
+        mx1 = fmaxf(mx1, x1[p]);
     }
-    int my_in = 0;
+    mn0 = wave_min_dpp(mn0);
+    mx0 = wave_max_dpp(mx0);
+    mn1 = wave_min_dpp(mn1);
+    mx1 = wave_max_dpp(mx1);
+    // the brackets: steps cut them where a straight line through the two
+    // counts reaches k (at least a twentieth of the width off either end)
+    float lo0 = mn0, hi0 = mx0, lo1 = mn1, hi1 = mx1;
+    int gl0, gl1, gh0 = 0, gh1 = 0;
+    {
+        // #{x >= min} = the row's finite keys
+        int a0 = 0, a1 = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            a0 += x0[p] >= mn0 ? 1 : 0;
+            a1 += x1[p] >= mn1 ? 1 : 0;
+        }
+        gl0 = wave_sum_dpp(a0);
+        gl1 = wave_sum_dpp(a1);
+    }
+    const int k0 = s0.k, k1 = s1.k;
+    bool act0 = !s0.done && gl0 - gh0 > kCandidates, act1 = !s1.done && gl1 - gh1 > kCandidates;
+    for (int it = 0; it < 48 && (act0 || act1); ++it) {
+        const float f0 = fminf(fmaxf((float)(k0 - gh0) / (float)(gl0 - gh0), 0.05f), 0.95f);
+        const float f1 = fminf(fmaxf((float)(k1 - gh1) / (float)(gl1 - gh1), 0.05f), 0.95f);
+        const float mid0 = hi0 - (hi0 - lo0) * f0, mid1 = hi1 - (hi1 - lo1) * f1;
+        act0 = act0 && mid0 > lo0 && mid0 < hi0;
+        act1 = act1 && mid1 > lo1 && mid1 < hi1;
+        int c0, c1;
+        count_gt2(mid0, mid1, c0, c1);
+        if (act0) {
+            if (c0 < k0) {
+                hi0 = mid0;
+                gh0 = c0;
+            } else {
+                lo0 = mid0;
+                gl0 = c0;  // #{x > mid}: a lower bound of #{x >= lo}, enough to steer
+            }
+        }
+        if (act1) {
+            if (c1 < k1) {
+                hi1 = mid1;
+                gh1 = c1;
+            } else {
+                lo1 = mid1;
+                gl1 = c1;
+            }
+        }
+        act0 = act0 && gl0 - gh0 > kCandidates;
+        act1 = act1 && gl1 - gh1 > kCandidates;
+    }
+    int ch0, ch1;
+    count_gt2(hi0, hi1, ch0, ch1);
+    s0.ok = gl0 >= k0 && ch0 < k0;
+    s1.ok = gl1 >= k1 && ch1 < k1;
+    // the band of each row: keys above it in, keys inside it members
+    const float hv0 = hi0 + 2.f * e0, lv0 = lo0 - 2.f * e0, hv1 = hi1 + 2.f * e1, lv1 = lo1 - 2.f * e1;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const bool in0 = x0[p] > hv0, m0 = !in0 && x0[p] >= lv0;
+        const bool in1 = x1[p] > hv1, m1 = !in1 && x1[p] >= lv1;
+        s0.inb[p / 32] |= in0 ? 1u << (p % 32) : 0u;
+        s0.memb[p / 32] |= m0 ? 1u << (p % 32) : 0u;
+        s1.inb[p / 32] |= in1 ? 1u << (p % 32) : 0u;
+        s1.memb[p / 32] |= m1 ? 1u << (p % 32) : 0u;
+    }
+    int in0 = 0, in1 = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        my_in += __popc(st.inb[w]);
-        st.my_mem += __popc(st.memb[w]);
+        in0 += __popc(s0.inb[w]);
+        s0.my_mem += __popc(s0.memb[w]);
+        in1 += __popc(s1.inb[w]);
+        s1.my_mem += __popc(s1.memb[w]);
     }
-    st.nu = wave_sum_dpp(my_in);
-    st.nm = wave_sum_dpp(st.my_mem);
-    st.need = k - st.nu;
-    st.ok = st.ok && st.need >= 0 && st.need <= st.nm;
-    st.uniform = st.need == 0 || st.need == st.nm;  // members all out or all in
-    st.taken = st.uniform ? st.need : 0;
+    s0.nu = wave_sum_dpp(in0);
+    s0.nm = wave_sum_dpp(s0.my_mem);
+    s1.nu = wave_sum_dpp(in1);
+    s1.nm = wave_sum_dpp(s1.my_mem);
+    s0.need = k0 - s0.nu;
+    s1.need = k1 - s1.nu;
+    s0.ok = s0.ok && s0.need >= 0 && s0.need <= s0.nm;
+    s1.ok = s1.ok && s1.need >= 0 && s1.need <= s1.nm;
+    s0.uniform = s0.need == 0 || s0.need == s0.nm;  // members all out or all in
+    s1.uniform = s1.need == 0 || s1.need == s1.nm;
+    s0.taken = s0.uniform ? s0.need : 0;
+    s1.taken = s1.uniform ? s1.need : 0;
 }
 
 // List a row's members into ml[base ..] (lane by lane: lane l's run starts
@@ -436,6 +491,54 @@ __device__ inline void list_members(const RowState<P>& st, int* ml, int base, in
     }
 }
 
+// The r0 lanes of mask c0 with the largest keys, equal keys going to the
+// lower index j, and likewise r1 of c1 (a second row's lanes), by an MSB-first
+// radix select over the 64-bit keys with one ballot per bit: the lanes whose
+// bit is set are taken whole while fewer than the remaining count, else the
+// search narrows to them.  Equal keys left at the end are chosen the same way
+// over the bits of j, zero side first.  Masks and counts stay uniform.
+__device__ inline void best_members(uint64_t c0, int r0, uint64_t c1, int r1, uint64_t key, int j, uint64_t& sel0,
+                                    uint64_t& sel1) {
+    uint64_t t0 = 0, t1 = 0;
+    const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
+    auto step = [](uint64_t h, uint64_t all, uint64_t& c, int& r, uint64_t& t) {
+        const int n = popc(h);
+        if (n >= r) {
+            c = h;
+        } else {
+            r -= n;
+            t |= h;
+            c &= ~all;
+        }
+    };
+    for (int b = 63; b >= 0; --b) {
+        if ((r0 <= 0 || popc(c0) == r0) && (r1 <= 0 || popc(c1) == r1)) break;
+        const uint64_t ones = __ballot(((b >= 32 ? khi : klo) >> (b & 31)) & 1u);
+        step(c0 & ones, ones, c0, r0, t0);
+        step(c1 & ones, ones, c1, r1, t1);
+    }
+    // equal keys: the r lowest j of c (j < 2^14)
+    auto ties = [&](uint64_t c, int r) -> uint64_t {
+        if (r <= 0) return 0ull;
+        if (popc(c) <= r) return c;
+        uint64_t chosen = 0;
+        for (int b = 13; b >= 0; --b) {
+            const uint64_t zero = c & ~__ballot((j >> b) & 1);
+            const int nz = popc(zero);
+            if (nz >= r) {
+                c = zero;
+            } else {
+                r -= nz;
+                chosen |= zero;
+                c &= ~zero;
+            }
+        }
+        return chosen | c;
+    };
+    sel0 = t0 | ties(c0, r0);
+    sel1 = t1 | ties(c1, r1);
+}
+
 // Members of one row (at most 64) or of two rows (together at most 64) in
 // lanes 0 .. nm0 + nm1 - 1: each scored in double, ranked within its row by
 // (-double score, index), the verdict written to its row's LDS area.
@@ -451,17 +554,14 @@ __device__ void resolve_lanes(RowState<P>& s0, RowState<P>& s1, bool two, const 
     const bool first = lane < nm0;
     const int jm = lane < ntot ? ml[lane] : 0;
     const double s = lane < ntot ? exact_score<D>(first ? qd : qd + D, a.kbar + (bh * n + jm) * D) : 0.0;
-    const int m_lo = first ? 0 : nm0, m_hi = first ? nm0 : ntot;
-    int rank = 0;
-    for (int m2 = 0; m2 < ntot; ++m2) {
-        const double s2 = readlane_d(s, m2);
-        const int j2 = __builtin_amdgcn_readlane(jm, m2);
-        rank += (m2 >= m_lo && m2 < m_hi && ((s2 > s) || (s2 == s && j2 < jm))) ? 1 : 0;
-    }
-    const bool sel = lane < ntot && rank < (first ? s0.need : s1.need);
+    // each row's best need members by (-double score, index), as masks of lanes
+    const uint64_t m0 = __ballot(first), m1 = two ? __ballot(lane >= nm0 && lane < ntot) : 0ull;
+    uint64_t sel0, sel1;
+    best_members(m0, s0.need, m1, two ? s1.need : 0, lane < ntot ? order_key64(s) : 0ull, jm, sel0, sel1);
+    const bool sel = ((sel0 | sel1) >> lane) & 1ull;
     if (lane < ntot) ((uint32_t*)(first ? s0.row : s1.row))[jm] = sel ? 1u : 0u;
-    s0.taken = popc(__ballot(sel && first));
-    if (two) s1.taken = popc(__ballot(sel && !first));
+    s0.taken = popc(sel0);
+    if (two) s1.taken = popc(sel1);
 }
 
 // Many members: flagged in the LDS row, their double scores as order keys in
@@ -560,8 +660,7 @@ template <int D, int P>
 __device__ void select_rows(const SelectArgs& a, float* row0, float* row1, int i0, int i1, bool two, int64_t bh,
                             float kmax, int lane, uint32_t* hw, int* ml, uint64_t* fb) {
     RowState<P> s0, s1;
-    classify_row<D, P>(s0, a, row0, bh, i0, kmax, lane);
-    if (two) classify_row<D, P>(s1, a, row1, bh, i1, kmax, lane);
+    classify_pair<D, P>(s0, s1, two, a, row0, row1, bh, i0, i1, kmax, lane);
     const bool act0 = !s0.done && s0.ok && !s0.uniform;
     const bool act1 = two && !s1.done && s1.ok && !s1.uniform;
     double* qd = (double*)hw;

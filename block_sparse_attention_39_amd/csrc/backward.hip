@@ -218,6 +218,15 @@ __device__ __attribute__((always_inline)) inline void load_n(bf16x8 (&dst)[N], c
 #pragma unroll
     for (int s = 0; s < N; ++s) dst[s] = *(const bf16x8*)(base + s * 1024);
 }
+// One (batch, head)'s tiles of a fragment-layout tensor as a buffer resource:
+// loads take a fixed lane offset and the tile's offset in a scalar register.
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int64_t bh, int n_tiles, int tb) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + bh * (int64_t)n_tiles * tb), 0,
+                                             n_tiles * tb, 0x00020000);
+}
+__device__ inline bf16x8 frag_load(__amdgpu_buffer_rsrc_t rs, int lane_ofs, int ofs) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_ofs, ofs, 0));
+}
 
 // bf16 pair of accumulator elements r, r + 1 into a B-operand fragment pair
 __device__ inline void put_pair(bf16x8 (&f)[2], int r, float x, float y) {
@@ -352,6 +361,9 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
     const uint8_t* kkb = (const uint8_t*)a.k_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
     const uint8_t* vkb = (const uint8_t*)a.v_kf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
     const uint8_t* kvb = (const uint8_t*)a.k_vf + bh * (int64_t)n_tiles * TB + w.kh * CF::HALF + lane * 16;
+    const __amdgpu_buffer_rsrc_t kkr = head_rsrc(a.k_kf, bh, n_tiles, TB), vkr = head_rsrc(a.v_kf, bh, n_tiles, TB),
+                                 kvr = head_rsrc(a.k_vf, bh, n_tiles, TB);
+    const int lofs = w.kh * CF::HALF + lane * 16;
 #define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)] & (kPad ? kTileBits : -1))
 #define CLASSED_AT(n_) (kPad ? __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)]) : 0)
 
@@ -403,9 +415,7 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
             const int t_k = t_k_next;
             const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)] & (kPad ? kTileBits : -1);
             const int t_s_after = kPad ? list[min(par + 2 * (n + 2), n_iter - 1)] : 0;
-            const uint8_t* const kaddr = kkb + (int64_t)t_k * TB;
-            const uint8_t* const vaddr = vkb + (int64_t)t_k * TB;
-            const uint8_t* const kvaddr = kvb + (int64_t)t_v * TB;
+            const int kofs = t_k * TB, kvofs = t_v * TB;
             const float vmask = n < my_n ? 0.f : -INFINITY;
             asm("" : "+v"(qoff) : "s"(n));  // opaque: keeps the LDS reads in the loop
 #pragma unroll
@@ -445,10 +455,10 @@ __device__ __attribute__((always_inline)) inline void dq_tile(const BackwardArgs
                     // window 1: K(n+2), V(n+2); one fragment per slot
                     if (h == 0) {
                         const int f = g - 2 * OD;
-                        if (f >= 0 && f < NV) kv[B ^ 1][f] = *(const bf16x8*)(kvaddr + f * 1024);
+                        if (f >= 0 && f < NV) kv[B ^ 1][f] = frag_load(kvr, lofs, kvofs + f * 1024);
                     } else {
-                        if (g < SD) kk[B][g] = *(const bf16x8*)(kaddr + g * 1024);
-                        if (g >= SD && g < 2 * SD) vk[B][g - SD] = *(const bf16x8*)(vaddr + (g - SD) * 1024);
+                        if (g < SD) kk[B][g] = frag_load(kkr, lofs, kofs + g * 1024);
+                        if (g >= SD && g < 2 * SD) vk[B][g - SD] = frag_load(vkr, lofs, kofs + (g - SD) * 1024);
                     }
                     // dS^T of half h, stage group q = g / 3
                     const int q = g / 3, stg = g % 3;

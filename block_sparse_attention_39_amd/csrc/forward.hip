@@ -102,10 +102,23 @@ __device__ inline float pair_max(float x) {
     return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
+// K or V of one (batch, head) as a buffer resource: the loads then take one
+// fixed lane offset in a vector register and the tile's offset in a scalar
+// one (no 64-bit address arithmetic per load).  Its size is the (batch, head)'s
+// whole range, so every load of a valid tile is in bounds.
+constexpr int kBufWord3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int64_t bh, int n_tiles, int tb) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + bh * (int64_t)n_tiles * tb), 0,
+                                             n_tiles * tb, kBufWord3);
+}
+__device__ inline bf16x8 frag_load(__amdgpu_buffer_rsrc_t rs, int lane_ofs, int ofs) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_ofs, ofs, 0));
+}
 template <int N>
-__device__ __attribute__((always_inline)) inline void load_frags(bf16x8 (&dst)[N], const uint8_t* base) {
+__device__ __attribute__((always_inline)) inline void load_frags(bf16x8 (&dst)[N], __amdgpu_buffer_rsrc_t rs,
+                                                                 int lane_ofs, int ofs) {
 #pragma unroll
-    for (int s = 0; s < N; ++s) dst[s] = *(const bf16x8*)(base + s * 1024);
+    for (int s = 0; s < N; ++s) dst[s] = frag_load(rs, lane_ofs, ofs + s * 1024);
 }
 
 // The rare path of the overflow test: the slice's true maximum (over the
@@ -217,11 +230,11 @@ __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardA
     constexpr int SD = CF::SD, TB = CF::TB;
     const int n_tiles = a.npt + a.nvt;
     const int64_t n_tot = (int64_t)n_tiles * kTile;
-    const uint8_t* kbh = (const uint8_t*)a.k + it.bh * (int64_t)n_tiles * TB + w.kh * CF::SLICE + w.lane * 16;
-    const uint8_t* vbh = (const uint8_t*)a.v + it.bh * (int64_t)n_tiles * TB + w.kh * CF::SLICE + w.lane * 16;
-    load_frags(kf[0], kbh + (int64_t)t0 * TB);
-    load_frags(vf[0], vbh + (int64_t)t0 * TB);
-    load_frags(kf[1], kbh + (int64_t)t1 * TB);
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k, it.bh, n_tiles, TB), vrs = head_rsrc(a.v, it.bh, n_tiles, TB);
+    const int lofs = w.kh * CF::SLICE + w.lane * 16;
+    load_frags(kf[0], krs, lofs, t0 * TB);
+    load_frags(vf[0], vrs, lofs, t0 * TB);
+    load_frags(kf[1], krs, lofs, t1 * TB);
     // Q^T operand fragment (query half qb, step s) of chunk f: lane holds
     // query 32*qb + lr, channels 16*s + 8*hf .. +7
 #pragma unroll
@@ -309,8 +322,8 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
 #define TILE_AT(n_) __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)] & (kPad ? kTileBits : -1))
 #define CLASSED_AT(n_) (kPad ? __builtin_amdgcn_readfirstlane(list[min(par + 2 * (n_), n_iter - 1)]) : 0)
 
-    const uint8_t* kbh = (const uint8_t*)a.k + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
-    const uint8_t* vbh = (const uint8_t*)a.v + bh * (int64_t)n_tiles * TB + kh * CF::SLICE + lane * 16;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k, bh, n_tiles, TB), vrs = head_rsrc(a.v, bh, n_tiles, TB);
+    const int lofs = kh * CF::SLICE + lane * 16;
 
     f32x16 sacc[2];   // S^T per query half: S(n)[0] and S(n)[1] in turn
     bf16x8 pf[2][2];  // P^T per query half, by 16-key half
@@ -352,8 +365,7 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
             // step (no wait for the read inside the step)
             const int t_after = list[min(par + 2 * (n + 3), n_iter - 1)] & (kPad ? kTileBits : -1);
             const int t_s_after = kPad ? list[min(par + 2 * (n + 2), n_iter - 1)] : 0;
-            const uint8_t* const kaddr = kbh + (int64_t)t_k * TB;
-            const uint8_t* const vaddr = vbh + (int64_t)t_v * TB;
+            const int kofs = t_k * TB, vofs = t_v * TB;
 
             // One step is two windows of 2*OD + SD MFMA slots (16 for
             // D = 128), one per query half h of the softmax:
@@ -405,9 +417,9 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                                                                            st == 0 ? f32x16{} : sacc[sq], 0, 0, 0);
                         asm volatile("" ::"v"(sacc[sq][0]));
                         if (h == 0)
-                            vf[B ^ 1][st] = *(const bf16x8*)(vaddr + st * 1024);  // V(n+1)
+                            vf[B ^ 1][st] = frag_load(vrs, lofs, vofs + st * 1024);  // V(n+1)
                         else
-                            kf[B][st] = *(const bf16x8*)(kaddr + st * 1024);      // K(n+2)
+                            kf[B][st] = frag_load(krs, lofs, kofs + st * 1024);      // K(n+2)
                     }
                     // stage 1 (pairs of stage slot g-1): scaled logits of S(n)[h]
                     if (g >= 1 && g - 1 < NSA) {

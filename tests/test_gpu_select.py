@@ -21,7 +21,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, check_selection, desc_for, to_bits, to_dev
+from parity import GpuRun, check_output, check_selection, desc_for, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -168,11 +168,13 @@ def test_forward_stats_count_rounds():
     assert gave_up == 0
 
 
-@pytest.mark.parametrize("grid,keep", [((32, 48, 96), 301), ((32, 64, 160), 640)], ids=["n2304", "n5120"])
+@pytest.mark.parametrize("grid,keep", [((32, 48, 96), 301), ((32, 64, 160), 640), ((32, 64, 256), 300)],
+                         ids=["n2304", "n5120", "n8192_max"])
 def test_large_tile_counts(grid, keep):
     """More video tiles than 16 rows of scores fit in LDS: 8 rows per item
-    (2,304 tiles) and 4 rows per item (5,120 tiles); lists against the oracle
-    on every row, including the pooled means."""
+    (2,304 tiles) and 4 rows per item (5,120 tiles, and the largest video
+    tile count the library accepts, 8,192); lists against the oracle on every
+    row, including the pooled means."""
     wl = W(f"n{grid}", 1, 1, 64, grid, keep, seed=71)
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
@@ -190,3 +192,34 @@ def test_large_tile_counts(grid, keep):
     assert np.array_equal(gq.cpu().numpy(), qp) and np.array_equal(gk.cpu().numpy(), kp)
     n_clear, n_near, n_gamma = check_selection(att.block_idx.cpu().numpy(), qp, kp, keep)
     print(f"[plan] rows {n_clear} clear, {n_near} near ties, {n_gamma} in the float band", flush=True)
+
+
+def test_maximum_total_tiles_whole_path():
+    """The most tiles per (batch, head) the library accepts: 8,192 prefix
+    tiles and 8,192 video tiles (16,384, a million tokens).  Permutation,
+    gathers and scatter are bit-exact on every row; the lists against the
+    oracle on every row; attention of a prefix query tile (every key) and a
+    video query tile (the prefix plus its kept tiles) against the oracle."""
+    wl = W("max_tiles", 1, 1, 64, (32, 64, 256), 16, seed=72, n_prefix=8192 * 64)
+    print(f"\n[case] {wl}", flush=True)
+    assert wl.n_tokens // 64 == bsa.MAX_VIDEO_TILES * 2 and wl.n_video_tiles == bsa.MAX_VIDEO_TILES
+    q, k, v = S.qkv(wl)
+    g = GpuRun(wl, q, k, v).run()
+    perm = oracle.perm_static(wl.grid)[None]
+    assert np.array_equal(g.perm(), perm)
+    npf = wl.n_prefix
+    qt, kt, vt = (oracle.gather(x, perm, npf) for x in (q, k, v))
+    assert np.array_equal(to_bits(g.att.q_t).reshape(qt.shape), qt)
+    qp, kp = oracle.pool(qt, npf), oracle.pool(kt, npf)
+    gq, gk = g.pooled()
+    assert np.array_equal(gq, qp) and np.array_equal(gk, kp)
+    idx = g.block_idx()
+    n_clear, n_near, n_gamma = check_selection(idx, qp, kp, wl.keep_tiles)
+    print(f"[plan] rows {n_clear} clear, {n_near} near ties, {n_gamma} in the float band", flush=True)
+    tiles = np.array([3, wl.n_prefix_tiles + 4321], dtype=np.int32)
+    ref, _ = oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], npf, idx[0, 0], float(np.float32(wl.scale)), tiles)
+    got = to_bits(g.att.o_t[0, 0]).reshape(-1, 64, wl.head_dim)[tiles]
+    mx, mean = check_output(got, ref, "max tiles")
+    print(f"[forward] max|err| {mx:.2e} mean {mean:.2e}", flush=True)
+    sc = oracle.scatter(to_bits(g.att.o_t), perm, npf)
+    assert np.array_equal(to_bits(g.out), sc)

@@ -565,6 +565,8 @@ def bench_backward(args, wl, q, k, v):
     wall = time.perf_counter() - t_start
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = float(np.mean(times))
+    # of the last timed call
+    dq_gave_up, dq_rounds, kv_gave_up, kv_rounds = bsa.backward_stats(desc, ws, col.numel() if keep_h else 0)
     F = 2.5 * (varkeep_flops(wl, keep_h) if keep_h else wl.effective_flops())
     achieved = F / (ms * 1e-3) / 1e12
     res = {
@@ -592,6 +594,11 @@ def bench_backward(args, wl, q, k, v):
                      "traffic": None},
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "ms_per_step_stats": step_stats(times),
+        "lockstep": {"dq": {"block_rounds": dq_rounds, "waits_gave_up": dq_gave_up},
+                     "dkdv": {"block_rounds": kv_rounds, "waits_gave_up": kv_gave_up},
+                     "note": "block rounds of the grouped dQ and dK/dV launches in the last timed call (one per "
+                             "query tile, one per key tile), and those whose bounded start wait gave up before "
+                             "every block of its XCD group arrived"},
     }
     if not args.no_cpu_baseline and keep_h is None:
         t0 = time.perf_counter()

@@ -23,7 +23,8 @@ EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_f
            "bsa_forward_noalloc",
            "bsa_csr_entries", "bsa_plan_csr",
            "bsa_forward_csr", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
-           "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_status_string", "bsa_version")
+           "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_backward_stats_offset",
+           "bsa_status_string", "bsa_version")
 MASK_SPATIAL, MASK_TEMPORAL = 0, 1
 MAX_CSR_HEADS = 256
 
@@ -75,12 +76,14 @@ def lib() -> ctypes.CDLL:
         L.bsa_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_backward_csr_workspace_size.argtypes = [D, I64, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_backward_csr.argtypes = [D, P, P, P, P, P, P, P, P, P, I64, P, P, P, P, ctypes.c_size_t, P]
+        L.bsa_backward_stats_offset.argtypes = [D, I64, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_status_string.argtypes = [ctypes.c_int]
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_version.argtypes = []
         for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_forward",
                   "bsa_forward_stats_offset", "bsa_forward_noalloc", "bsa_backward_workspace_size",
-                  "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_version"):
+                  "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_backward_stats_offset",
+                  "bsa_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib

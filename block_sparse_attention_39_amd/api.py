@@ -253,6 +253,23 @@ def backward(desc: Desc, q, k, v, o, d_o, lse, perm, block_idx, dq, dk, dv, work
                               _stream(stream)), "bsa_backward")
 
 
+def backward_stats_offset(desc: Desc, col_entries: int = 0) -> int:
+    """Byte offset in the backward workspace (col_entries 0: the fixed-keep
+    one; else the CSR one of that many columns) of int32 stats[4]."""
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_backward_stats_offset(ctypes.byref(desc), int(col_entries), ctypes.byref(n)),
+           "bsa_backward_stats_offset")
+    return n.value
+
+
+def backward_stats(desc: Desc, workspace, col_entries: int = 0):
+    """(dQ waits that gave up, dQ rounds, dK/dV waits that gave up, dK/dV
+    rounds) of the last backward call on this workspace (a device read:
+    synchronises the stream)."""
+    off = backward_stats_offset(desc, col_entries)
+    return tuple(int(x) for x in workspace.view(torch.uint8)[off:off + 16].view(torch.int32).cpu().tolist())
+
+
 def backward_csr_workspace_size(desc: Desc, col_entries: int) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().bsa_backward_csr_workspace_size(ctypes.byref(desc), int(col_entries), ctypes.byref(n)),

@@ -888,8 +888,11 @@ __device__ __attribute__((always_inline)) inline void dkdv_tile(const BackwardAr
 // waits only shape the schedule; results do not depend on them.
 constexpr int kGroupsB = 8, kMaxGroupSizeB = 64, kMaxSpinB = 2000;
 
+// stats[0] counts the block rounds whose bounded wait gave up before every
+// block of the group had arrived, stats[1] the block rounds started.
 template <typename Body>
-__device__ __attribute__((always_inline)) inline void grouped_rounds(const BackwardArgs& a, int* progress, Body body) {
+__device__ __attribute__((always_inline)) inline void grouped_rounds(const BackwardArgs& a, int* progress, int* stats,
+                                                                     Body body) {
     const int group = blockIdx.x % kGroupsB, slot = blockIdx.x / kGroupsB;
     const int S = gridDim.x / kGroupsB;
     const int n_tiles = a.npt + a.nvt;
@@ -901,13 +904,21 @@ __device__ __attribute__((always_inline)) inline void grouped_rounds(const Backw
         if (threadIdx.x < 64) {
             const int lane = threadIdx.x;
             if (lane == 0) __hip_atomic_store(prog + slot, (int)r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool met = false;
             for (int spin = 0; spin < kMaxSpinB; ++spin) {
                 int v = INT_MAX;
                 if (lane < S) v = __hip_atomic_load(prog + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-                if (v >= (int)r) break;
+                if (v >= (int)r) {
+                    met = true;
+                    break;
+                }
                 __builtin_amdgcn_s_sleep(2);
+            }
+            if (lane == 0) {
+                __hip_atomic_fetch_add(stats + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!met) __hip_atomic_fetch_add(stats, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         body(item / n_tiles, (int)(item % n_tiles));
@@ -921,7 +932,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                                                               int* progress) {
     __shared__ __attribute__((aligned(16))) float lds[BCfg<D>::LDS_FLOATS];
     const WaveId w;
-    grouped_rounds(a, progress, [&](int64_t bh, int qt) { dq_tile<D, kPad>(a, lds, bh, qt, w); });
+    grouped_rounds(a, progress, progress + backward_stats_ints(),
+                   [&](int64_t bh, int qt) { dq_tile<D, kPad>(a, lds, bh, qt, w); });
 }
 
 template <int D>
@@ -929,7 +941,8 @@ __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2,
     BackwardArgs a, int* progress) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[DkdvLds<D>::BYTES];
     const DkdvWave w;
-    grouped_rounds(a, progress, [&](int64_t bh, int kt) { dkdv_tile<D>(a, smem, bh, kt, w); });
+    grouped_rounds(a, progress, progress + backward_stats_ints() + 2,
+                   [&](int64_t bh, int kt) { dkdv_tile<D>(a, smem, bh, kt, w); });
 }
 
 __global__ void bwd_clear_progress_kernel(int* progress, int n) {
@@ -971,7 +984,9 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     if (e == hipSuccess) e = grouped_grid(bwd_dkdv_kernel<D>, kDkdvThreads, tiles, &gk);
     if (e != hipSuccess) return e;
     constexpr int NP = kGroupsB * kMaxGroupSizeB;
-    hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
+    static_assert(NP == backward_stats_ints(), "statistics follow the round counters");
+    // the first clear takes the statistics too, the second only the counters
+    hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, backward_progress_ints());
     hipLaunchKernelGGL((bwd_dq_kernel<D, kPad>), dim3((unsigned)gq), dim3(256), 0, s, a, a.progress);
     hipLaunchKernelGGL(bwd_clear_progress_kernel, dim3(1), dim3(512), 0, s, a.progress, NP);
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kDkdvThreads), 0, s, a, a.progress);

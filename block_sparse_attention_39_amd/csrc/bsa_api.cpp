@@ -578,6 +578,17 @@ bsa_status bsa_backward_csr_workspace_size(const bsa_desc* desc, int64_t col_ent
     return BSA_OK;
 }
 
+bsa_status bsa_backward_stats_offset(const bsa_desc* desc, int64_t col_entries, size_t* offset) {
+    if (!offset) return BSA_ERR_NULL;
+    Geo g;
+    const bsa_status st = check_desc(desc, &g);
+    if (st != BSA_OK) return st;
+    if (col_entries < 0) return BSA_ERR_SHAPE;
+    const int64_t tcap = col_entries == 0 ? g.BH * g.nvt * g.k : (g.nvt > 0 ? col_entries : 0);
+    *offset = bwd_layout(g, tcap).progress + (size_t)bsa::backward_stats_ints() * sizeof(int);
+    return BSA_OK;
+}
+
 namespace {
 
 // The backward over fixed-keep lists (row_ptr null) or CSR lists.

@@ -243,14 +243,19 @@ struct BackwardArgs {
     int32_t* tlist;            // [tcap] scratch: the transposed lists, (bh, key tile) order
     int64_t tcap;              // entries of tlist
     uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]
-    int* progress;             // backward_progress_ints() ints: grouped-launch round counters
+    int* progress;             // backward_progress_ints() ints: grouped-launch round counters,
+                               // then 4 statistics (backward_stats_ints())
     int BH, H, npt, nvt, keep, mwords;
     int64_t npf, n_tot;        // tiled rows per (b, h): prefix + video slots
     int64_t n_ras;             // raster rows per batch element (fewer on a ragged grid)
     PadGeo pad;                // ragged grid (pad.T != 0): perm -1 marks padding slots
     float scale, scale_log2;
 };
-constexpr int backward_progress_ints() { return 8 * 64; }
+// the round counters of the grouped gradient launches (8 groups of up to 64
+// blocks), then int32 stats[4]: dQ round-start waits that gave up, dQ block
+// rounds started, the same two for dK/dV
+constexpr int backward_stats_ints() { return 8 * 64; }
+constexpr int backward_progress_ints() { return 8 * 64 + 4; }
 hipError_t launch_backward(const BackwardArgs& a, int D, hipStream_t s);
 
 }  // namespace bsa

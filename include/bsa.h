@@ -402,13 +402,27 @@ bsa_status bsa_backward_csr(const bsa_desc *desc, const void *q, const void *k, 
                             const int64_t *row_ptr, const int32_t *col_idx, int64_t col_entries,
                             void *dq, void *dk, void *dv, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Byte offset of the gradient launches' statistics inside the backward
+ * workspace: int32 stats[4], cleared at the start of every bsa_backward /
+ * bsa_backward_csr call and, when its work has run, stats[0] = block rounds
+ * of the grouped dQ launch whose bounded start wait gave up before every
+ * block of its XCD group arrived, stats[1] = block rounds started (one per
+ * query tile), stats[2], stats[3] = the same for the dK/dV launch (one round
+ * per key tile).  col_entries = 0: the workspace of bsa_backward_workspace_size;
+ * > 0: that of bsa_backward_csr_workspace_size(desc, col_entries).  Like the
+ * forward's, the waits only shape the schedule (results never depend on
+ * them).  Host-only.
+ */
+bsa_status bsa_backward_stats_offset(const bsa_desc *desc, int64_t col_entries, size_t *offset);
+
 /* Static text for a status code. */
 const char *bsa_status_string(bsa_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 1000
+#define BSA_VERSION 1001
 
 #ifdef __cplusplus
 }

@@ -272,6 +272,25 @@ def test_padded_mode_host_checks():
     assert e.value == rp[-1]
 
 
+def test_backward_stats_offset():
+    """The backward's statistics sit at the end of either backward workspace,
+    after the 2 KB of round counters: the last 16 bytes of the 256-byte
+    aligned region of (8 * 64 + 4) ints.  Host-only."""
+    L = lib()
+    d = cfg()                                   # 2 x 3 heads, 12 video tiles, k = 5
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    region = (8 * 64 + 4) * 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert L.bsa_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert L.bsa_backward_stats_offset(ctypes.byref(d), 0, ctypes.byref(off)) == OK
+    assert off.value == n.value - al(region) + 8 * 64 * 4
+    assert L.bsa_backward_csr_workspace_size(ctypes.byref(d), 1000, ctypes.byref(n)) == OK
+    assert L.bsa_backward_stats_offset(ctypes.byref(d), 1000, ctypes.byref(off)) == OK
+    assert off.value == n.value - al(region) + 8 * 64 * 4
+    assert L.bsa_backward_stats_offset(ctypes.byref(d), -1, ctypes.byref(off)) == SHAPE
+    assert L.bsa_backward_stats_offset(ctypes.byref(d), 0, None) == NULL
+
+
 def test_backward_csr_host_checks():
     """bsa_backward_csr: workspace sized on the CSR column count; missing
     lists, an empty column array and a short workspace are refused before

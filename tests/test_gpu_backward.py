@@ -50,6 +50,7 @@ def run_backward(wl):
     ws = torch.empty(max(bsa.backward_workspace_size(g.desc), 256), dtype=torch.uint8, device="cuda")
     bsa.backward(g.desc, g.q, g.k, g.v, g.out, dO, g.att.lse, g.att.perm, g.att.block_idx, dq, dk, dv, ws)
     torch.cuda.synchronize()
+    g.bwd_ws = ws
     return (q, k, v, do), g, (dq, dk, dv)
 
 
@@ -84,3 +85,17 @@ def test_backward_is_deterministic():
     _, _, b = run_backward(wl)
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_stats_count_rounds():
+    """The grouped dQ and dK/dV launches record one block round per query
+    tile and per key tile (prefix tiles included); on an idle GPU with one
+    block per CU no round's start wait gives up."""
+    wl = W("bstats", 2, 4, 128, (16, 16, 32), 12, seed=63, n_prefix=128)
+    _, g, _ = run_backward(wl)
+    dq_gave_up, dq_rounds, kv_gave_up, kv_rounds = bsa.backward_stats(g.desc, g.bwd_ws)
+    tiles = wl.batch * wl.heads * (wl.n_prefix_tiles + wl.n_video_tiles)
+    print(f"[stats] dQ rounds {dq_rounds} (gave up {dq_gave_up}), dK/dV rounds {kv_rounds} (gave up {kv_gave_up})",
+          flush=True)
+    assert dq_rounds == tiles and kv_rounds == tiles
+    assert dq_gave_up == 0 and kv_gave_up == 0

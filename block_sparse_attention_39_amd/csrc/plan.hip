@@ -11,15 +11,15 @@
 //          inputs), one rounding to float, cross-lane reduction with shuffles.
 //          Besides the float means it writes each mean as a bf16 hi/lo pair in
 //          MFMA operand order, and each mean's norm.
-// select : one persistent block of 4 waves per CU; a work item is R query rows
+// select : one persistent block of 8 waves per CU; a work item is R query rows
 //          of one (batch, head).  The R x nvt scores are computed on bf16 MFMA
 //          from the hi/lo pairs (hi*hi + hi*lo + lo*hi, float accumulation)
-//          into LDS; no score matrix goes to memory.  Then one wave per row
-//          brackets the k-th largest float score by counts (a sorted sample,
-//          then halving) and settles every key whose float score lies within
-//          the float error bound of the bracket by recomputing its score in
-//          double, in the order of the channels, so that the kept set is
-//          exactly the top k of the double scores.
+//          into LDS; no score matrix goes to memory.  Then each wave takes two
+//          rows: it brackets the k-th largest float score of both by counts
+//          (interpolation steps) and settles every key whose float score lies
+//          within the float error bound of the bracket by recomputing its
+//          score in double, in the order of the channels, so that the kept set
+//          is exactly the top k of the double scores.
 #include "bsa_kernels.h"
 
 namespace bsa {
@@ -286,10 +286,11 @@ __device__ inline bool top_digit(const int (&h)[W], int top, int need, int lane,
     return true;
 }
 
-// The selection of one row by one wave, in three stages.  The row's n float
-// scores are read from LDS into registers (key j = lane + 64 p in x[p]); the
-// LDS row is then reused for the members' verdicts and the output.
-//  1. classify_row: a bracket lo <= T <= hi of the k-th largest float score
+// The selection of a row by one wave (two rows per wave, side by side), in
+// three stages.  The row's n float scores are read from LDS into registers
+// (key j = lane + 64 p in x[p]); the LDS row is then reused for the members'
+// verdicts and the output.
+//  1. classify_pair: a bracket lo <= T <= hi of the k-th largest float score
 //     T, from the row's extremes and counts (fewer than k scores above hi, at
 //     least k at or above lo), narrowed by interpolation until at most
 //     kCandidates scores lie in between.  With e bounding |float score -
@@ -300,8 +301,10 @@ __device__ inline bool top_digit(const int (&h)[W], int top, int need, int lane,
 //     so it is not.  The keys in between are the members.
 //  2. resolve: the members are scored again in double (both rows of a wave
 //     in one pass when their members fit in 64 lanes) and the best
-//     k - (keys above) of them by (-double score, index) complete the set;
-//     many members go through an 8-bit radix select of the double scores.
+//     k - (keys above) of them by (-double score, index) complete the set,
+//     found by a ballot radix select over the double scores' order keys
+//     (best_members); more than 64 members go through an 8-bit radix select
+//     through LDS and the workspace.
 //  3. output_row: the kept keys compacted in ascending order and written out.
 template <int P>
 struct RowState {

@@ -305,7 +305,7 @@ __device__ inline bool top_digit(const int (&h)[W], int top, int need, int lane,
 //     found by a ballot radix select over the double scores' order keys
 //     (best_members); more than 64 members go through an 8-bit radix select
 //     through LDS and the workspace.
-//  3. output_row: the kept keys compacted in ascending order and written out.
+//  3. output_row: the kept keys written out in ascending order.
 template <int P>
 struct RowState {
     static constexpr int NW = (P + 31) / 32;
@@ -624,9 +624,8 @@ __device__ void resolve_radix(RowState<P>& st, const SelectArgs& a, int64_t bh, 
 
 // Exactly k keys must be kept (always so for finite scores; otherwise, e.g.
 // with NaN scores, the first k keys keep the list well formed).  A lane reads
-// the verdicts of its own members, then the kept keys are compacted into the
-// LDS row (a write lands at a position below 64 (p + 1), whose verdicts have
-// been read) and copied out in order.
+// the verdicts of its own members, then the kept keys are written out in
+// ascending order, 64 keys per ballot.
 template <int P>
 __device__ void output_row(const RowState<P>& st, int n, int lane) {
     constexpr int NW = RowState<P>::NW;
@@ -645,17 +644,17 @@ __device__ void output_row(const RowState<P>& st, int n, int lane) {
             }
         }
     }
-    int* outl = (int*)st.row;
+    // each ballot's kept keys take consecutive places: stores straight to the
+    // output list, coalesced
     int pos = 0;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int j = lane + 64 * p;
         const bool sel = degenerate ? j < st.k : ((selb[p / 32] >> (p % 32)) & 1u) != 0u;
         const uint64_t sm = __ballot(sel);
-        if (sel) outl[pos + lanes_below(sm)] = j;
+        if (sel) st.out[pos + lanes_below(sm)] = j;
         pos += popc(sm);
     }
-    for (int q = lane; q < st.k; q += 64) st.out[q] = outl[q];
 }
 
 // The rows r0 (and r1 when two) of an item, by one wave.

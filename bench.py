@@ -71,6 +71,9 @@ def parse():
                     help="RT,RS: time structured lists, even heads spatial (radius RT), odd heads temporal (RS)")
     ap.add_argument("--varkeep", default=None,
                     help="comma-separated keep counts cycled over the heads: time the CSR (variable keep) path")
+    ap.add_argument("--tiled-io", action="store_true",
+                    help="time the path through tiled Q and O (gather, forward, scatter) instead of the raster-I/O "
+                         "forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -286,7 +289,7 @@ def bench_varkeep(args, wl, q, k, v):
     for ev in events:
         for j, s in enumerate(stages):
             per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
-        totals.append(ev[0].elapsed_time(ev[5]))
+        totals.append(ev[0].elapsed_time(ev[len(stages)]))
     ms_step = float(np.mean(totals))
     F = varkeep_flops(wl, keep_h)
     fwd_ms = float(np.mean(per_stage["forward"]))
@@ -367,7 +370,7 @@ def bench_structured(args, wl, q, k, v):
     for ev in events:
         for j, s in enumerate(stages):
             per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
-        totals.append(ev[0].elapsed_time(ev[5]))
+        totals.append(ev[0].elapsed_time(ev[len(stages)]))
     ms_step = float(np.mean(totals))
     # every video query token attends the prefix and 64 keys per kept tile
     pairs = wl.heads * wl.batch * (wl.n_prefix * wl.n_tiled_tokens + wl.n_video_slots * wl.n_prefix)
@@ -658,21 +661,34 @@ def main():
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
                          n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
-    att = bsa.BlockSparseAttention(desc)
+    raster = not args.tiled_io
+    att = bsa.BlockSparseAttention(desc, raster_io=raster)
     out = torch.empty_like(qd)
     torch.cuda.synchronize()
 
-    stages = ["build", "gather_qk", "gather_v+plan", "forward", "scatter"]
+    if raster:
+        # Q's means alone, K gathered with its means; the forward reads raster
+        # Q and writes raster O itself
+        stages = ["build", "pool_q+gather_k", "gather_v+plan", "forward"]
+    else:
+        stages = ["build", "gather_qk", "gather_v+plan", "forward", "scatter"]
 
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         mark(0)
         att.build(qd)
         mark(1)
-        att.gather_qk(qd, kd)
+        if raster:
+            att.pool_qk(qd, kd)
+        else:
+            att.gather_qk(qd, kd)
         mark(2)
         att.gather_v_and_plan(vd)  # the V gather on a side stream, beside the plan
         mark(3)
+        if raster:
+            att.forward_raster(qd, out)
+            mark(4)
+            return
         att.forward()
         mark(4)
         att.scatter_out(out)
@@ -681,7 +697,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    n_ev = len(stages) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -693,15 +710,15 @@ def main():
     for ev in events:
         for j, s in enumerate(stages):
             per_stage[s].append(ev[j].elapsed_time(ev[j + 1]))
-        totals.append(ev[0].elapsed_time(ev[5]))
+        totals.append(ev[0].elapsed_time(ev[len(stages)]))
     ms_step = float(np.mean(totals))
     F = wl.effective_flops()
     fwd_ms = float(np.mean(per_stage["forward"]))
     gave_up, rounds = bsa.forward_stats(desc, att.workspace)   # of the last timed step's forward
-    kernels = kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out)
+    kernels = kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, raster)
     # the forward stage is the attention kernel (plus a 4 us counter clear; a
     # dense prefix adds the plain kernel for the prefix query tiles)
-    kernel = f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}>"
+    kernel = f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}, {str(raster).lower()}>"
     achieved = F / (fwd_ms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -721,6 +738,7 @@ def main():
                    "heads": wl.heads, "head_dim": wl.head_dim, "keep_tiles": wl.keep_tiles,
                    "tile": "dynamic" if wl.dynamic else "x".join(map(str, wl.tile)),
                    "padded_video_tokens": wl.n_video_slots if wl.padded else None,
+                   "io": "raster Q and O (bsa_forward_raster)" if raster else "tiled Q and O (gather, scatter)",
                    "effective_tflop_per_call": F / 1e12},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
@@ -750,14 +768,16 @@ def main():
 SHAPE_NAMES = ["4x4x4", "2x4x8", "2x8x4", "8x4x2", "4x2x8", "4x8x2", "8x2x4", "2x2x16", "16x2x2"]
 
 
-def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, reps: int = 5):
+def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, raster: bool, reps: int = 5):
     """Each stage of the step alone on the stream (HIP events, mean of `reps`
     calls after one untimed call), with its HBM bytes and rate against 8 TB/s:
-    the pooling gathers of Q and K, the plain gathers they replace, the V
-    gather, the selection, bsa_plan's own pooling + selection (the unfused
-    path) and the output scatter.  plan_ms: what the plan adds to the step
-    (the pooling gathers' time above the plain gathers, plus the selection),
-    against the plan's roofline: reading Q and K once and writing the lists."""
+    Q's means alone (the raster-I/O path), the pooling gathers of Q and K, the
+    plain gathers they replace, the V gather, the selection, bsa_plan's own
+    pooling + selection (the unfused path) and the output scatter.  plan_ms:
+    what the plan adds to the step, against the plan's roofline (reading Q and
+    K once and writing the lists): on the raster-I/O path Q's means plus the
+    K gather's time above the plain one plus the selection; on the tiled path
+    the pooling gathers' time above the plain gathers plus the selection."""
     import torch
     cur = torch.cuda.current_stream()
     bf = 2 * wl.batch * wl.heads * wl.n_tiled_tokens * wl.head_dim   # one bf16 tiled tensor, bytes
@@ -776,6 +796,7 @@ def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, reps: int = 5):
         return ev[0].elapsed_time(ev[1]) / reps
 
     ms = {
+        "pool_q": t(lambda: bsa.pool(desc, qd, att.perm, att.workspace)),
         "gather_pool_q": t(lambda: bsa.gather_pool(desc, qd, att.q_t, att.perm, att.workspace)),
         "gather_kf_pool_k": t(lambda: bsa.gather_kf_pool(desc, kd, att.k_f, att.perm, att.workspace)),
         "gather_q_plain": t(lambda: bsa.gather(desc, qd, q_t2, att.perm)),
@@ -785,7 +806,7 @@ def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, reps: int = 5):
         "plan_unfused": t(lambda: bsa.plan(desc, att.q_t, att.k_f, att.block_idx, att.workspace)),
         "scatter_o": t(lambda: att.scatter_out(out)),
     }
-    moved = {"gather_pool_q": 2 * bf + pooled, "gather_kf_pool_k": 2 * bf + pooled, "gather_q_plain": 2 * bf,
+    moved = {"pool_q": bf + pooled, "gather_pool_q": 2 * bf + pooled, "gather_kf_pool_k": 2 * bf + pooled, "gather_q_plain": 2 * bf,
              "gather_kf_k_plain": 2 * bf, "gather_vf_v": 2 * bf, "scatter_o": 2 * bf}
     res = {"note": "each stage alone on the stream, mean of %d calls; hbm = algorithmic bytes moved / time" % reps}
     for k_, v_ in ms.items():
@@ -794,13 +815,18 @@ def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, reps: int = 5):
             gbs = moved[k_] / (v_ * 1e-3) / 1e9
             e.update({"bytes": moved[k_], "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS})
         res[k_] = e
-    pool_extra = max(0.0, ms["gather_pool_q"] + ms["gather_kf_pool_k"] - ms["gather_q_plain"]
-                     - ms["gather_kf_k_plain"])
-    plan_ms = pool_extra + ms["select"]
+    k_extra = max(0.0, ms["gather_kf_pool_k"] - ms["gather_kf_k_plain"])
+    q_extra = max(0.0, ms["gather_pool_q"] - ms["gather_q_plain"])
+    pool_ms = ms["pool_q"] + k_extra if raster else q_extra + k_extra
+    plan_ms = pool_ms + ms["select"]
+    tiled_plan_ms = q_extra + k_extra + ms["select"]
     roof_ms = (2 * bf + idx_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3
-    res["plan"] = {"pool_in_gathers_extra_ms": pool_extra, "select_ms": ms["select"], "plan_ms": plan_ms,
+    res["plan"] = {"pooling_ms": pool_ms, "select_ms": ms["select"], "plan_ms": plan_ms,
+                   "pooling": "Q's means alone plus the K gather's extra" if raster else
+                              "the pooling gathers' extra over the plain gathers",
                    "roofline_ms": roof_ms, "frac": roof_ms / plan_ms if plan_ms > 0 else None,
                    "roofline": "read Q and K once (pooling) and write the kept lists, at 8 TB/s",
+                   "tiled_path_plan_ms": tiled_plan_ms,
                    "unfused_plan_ms": ms["plan_unfused"],
                    "unfused_frac": roof_ms / ms["plan_unfused"]}
     return res

@@ -15,12 +15,12 @@ STATUS_NAMES = {0: "BSA_OK", -1: "BSA_ERR_NULL", -2: "BSA_ERR_SHAPE", -3: "BSA_E
                 -4: "BSA_ERR_ALIGN", -5: "BSA_ERR_WORKSPACE", -6: "BSA_ERR_LAUNCH", -7: "BSA_ERR_ARG"}
 TILE_STATIC, TILE_DYNAMIC, TILE_STATIC_PADDED = 0, 1, 2
 PERM_BUILD, PERM_GATHER, PERM_SCATTER, PERM_GATHER_KF, PERM_GATHER_VF = 0, 1, 2, 3, 4
-PERM_GATHER_POOL, PERM_GATHER_KF_POOL, PERM_TILED_TO_KF, PERM_TILED_TO_VF = 5, 6, 7, 8
+PERM_GATHER_POOL, PERM_GATHER_KF_POOL, PERM_TILED_TO_KF, PERM_TILED_TO_VF, PERM_POOL = 5, 6, 7, 8, 9
 MAX_VIDEO_TILES = 8192
 MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
 EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_forward", "bsa_forward_stats_offset",
-           "bsa_forward_noalloc",
+           "bsa_forward_noalloc", "bsa_forward_raster",
            "bsa_csr_entries", "bsa_plan_csr",
            "bsa_forward_csr", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
            "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_backward_stats_offset",
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.bsa_forward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.bsa_forward_stats_offset.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P]
+        L.bsa_forward_raster.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         I64 = ctypes.c_int64
         L.bsa_csr_entries.argtypes = [D, P, ctypes.POINTER(I64)]
         L.bsa_plan_csr.argtypes = [D, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
@@ -81,7 +82,8 @@ def lib() -> ctypes.CDLL:
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_version.argtypes = []
         for f in ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_forward",
-                  "bsa_forward_stats_offset", "bsa_forward_noalloc", "bsa_backward_workspace_size",
+                  "bsa_forward_stats_offset", "bsa_forward_noalloc", "bsa_forward_raster",
+                  "bsa_backward_workspace_size",
                   "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_backward_stats_offset",
                   "bsa_version"):
             getattr(L, f).restype = ctypes.c_int

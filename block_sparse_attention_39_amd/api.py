@@ -13,7 +13,7 @@ import math
 import torch
 
 from ._lib import (PERM_BUILD, PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_KF_POOL, PERM_GATHER_POOL, PERM_GATHER_VF,
-                   PERM_SCATTER, PERM_TILED_TO_KF, PERM_TILED_TO_VF, TILE_DYNAMIC, TILE_STATIC, TILE_STATIC_PADDED,
+                   PERM_POOL, PERM_SCATTER, PERM_TILED_TO_KF, PERM_TILED_TO_VF, TILE_DYNAMIC, TILE_STATIC, TILE_STATIC_PADDED,
                    BsaError, Desc, lib)
 
 
@@ -109,6 +109,13 @@ def gather_kf_pool(desc: Desc, src, dst, perm, workspace, stream=None):
                              _ptr(workspace), _ws(workspace), _stream(stream)), "bsa_permute(GATHER_KF_POOL)")
 
 
+def pool(desc: Desc, src, perm, workspace, stream=None):
+    """The tile means of raster Q alone (no tiled copy) into the workspace, as
+    gather_pool writes them: for forward_raster, which reads raster Q."""
+    _check(lib().bsa_permute(ctypes.byref(desc), PERM_POOL, None, _ptr(perm), None, _ptr(src), None,
+                             _ptr(workspace), _ws(workspace), _stream(stream)), "bsa_permute(POOL)")
+
+
 def tiled_to_kf(desc: Desc, src, dst, stream=None):
     """Tiled K -> the K-fragment layout."""
     _check(lib().bsa_permute(ctypes.byref(desc), PERM_TILED_TO_KF, None, None, None, _ptr(src), _ptr(dst), None, 0,
@@ -162,6 +169,15 @@ def forward(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, w
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().bsa_forward(ctypes.byref(desc), _ptr(q_tiled), _ptr(k_frag), _ptr(v_frag), _ptr(block_idx),
                              _ptr(o_tiled), _ptr(lse), _ptr(workspace), ws, _stream(stream)), "bsa_forward")
+
+
+def forward_raster(desc: Desc, q_raster, perm, k_frag, v_frag, block_idx, o_raster, lse=None, workspace=None,
+                   stream=None):
+    """forward with Q read from and O written to the raster layout through
+    ``perm`` (the same values as gather, forward and scatter)."""
+    _check(lib().bsa_forward_raster(ctypes.byref(desc), _ptr(q_raster), _ptr(perm), _ptr(k_frag), _ptr(v_frag),
+                                    _ptr(block_idx), _ptr(o_raster), _ptr(lse), _ptr(workspace), _ws(workspace),
+                                    _stream(stream)), "bsa_forward_raster")
 
 
 def forward_noalloc(desc: Desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse=None, stream=None):
@@ -303,17 +319,22 @@ class BlockSparseAttention:
 
     ``__call__(q, k, v)`` takes raster bf16 tensors ``[B, Ntot, H, D]`` on the
     GPU and returns the raster output.  Buffers are allocated once, through
-    torch, in the constructor.  With ``overlap`` the V gather runs on a side
-    stream (default priority) while the plan runs on the caller's stream: the
-    plan does not read V, and the forward waits for both.  With
-    ``pool_in_gather`` (default) the Q and K gathers also take the tile means
-    (bsa_permute GATHER_POOL / GATHER_KF_POOL) and the plan is bsa_select;
-    otherwise plain gathers and bsa_plan, which reads Q and K again."""
+    torch: the fragment-layout K and V, the lists and the workspace in the
+    constructor, the tiled Q and O (``q_t``, ``o_t``) on first use.  With
+    ``overlap`` the V gather runs on a side stream (default priority) while the
+    plan runs on the caller's stream: the plan does not read V, and the forward
+    waits for both.  With ``pool_in_gather`` (default) the Q and K gathers also
+    take the tile means (bsa_permute GATHER_POOL / GATHER_KF_POOL) and the plan
+    is bsa_select; otherwise plain gathers and bsa_plan, which reads Q and K
+    again.  With ``raster_io`` (default; needs ``pool_in_gather``) ``__call__``
+    skips the tiled Q and O: Q's means come from bsa_permute(POOL) and
+    bsa_forward_raster reads raster Q and writes raster O itself."""
 
     def __init__(self, desc: Desc, device="cuda", with_lse: bool = False, grouped: bool = True,
-                 overlap: bool = True, pool_in_gather: bool = True):
+                 overlap: bool = True, pool_in_gather: bool = True, raster_io: bool = True):
         self.desc = desc
         B, H, D = desc.batch, desc.heads, desc.head_dim
+        self.device = device
         self.n_video = video_slots(desc)  # tiled video tokens (padding slots included)
         self.n_tot = desc.n_prefix + self.n_video
         self.nvt = self.n_video // 64
@@ -322,16 +343,35 @@ class BlockSparseAttention:
         self.perm = torch.empty((B, max(self.n_video, 1)), dtype=torch.int32, device=device)
         regions = (desc.grid_t // 8) * (desc.grid_h // 8) * (desc.grid_w // 8)
         self.shape_map = torch.empty((B, max(regions, 1)), dtype=torch.uint8, device=device) if self.dynamic else None
-        # q_t, o_t: tiled layout; k_f, v_f: the fragment layouts (same size)
-        self.q_t, self.k_f, self.v_f, self.o_t = (torch.empty((B, H, self.n_tot, D), dtype=bf, device=device)
-                                                  for _ in range(4))
+        # k_f, v_f: the fragment layouts (the size of the tiled layout)
+        self.k_f, self.v_f = (torch.empty((B, H, self.n_tot, D), dtype=bf, device=device) for _ in range(2))
+        self._q_t = self._o_t = None
         self.block_idx = torch.empty((B, H, max(self.nvt, 1), max(desc.keep_tiles, 1)), dtype=torch.int32,
                                      device=device)
         self.workspace = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device)
         self.lse = torch.empty((B, H, self.n_tot), dtype=torch.float32, device=device) if with_lse else None
         self.grouped = grouped
         self.pool_in_gather = pool_in_gather
+        self.raster_io = raster_io and pool_in_gather
         self.side = torch.cuda.Stream(device=device) if overlap else None
+
+    def _tiled(self):
+        d = self.desc
+        return torch.empty((d.batch, d.heads, self.n_tot, d.head_dim), dtype=torch.bfloat16, device=self.device)
+
+    @property
+    def q_t(self):
+        """Tiled Q [B, H, Ntot, D] (allocated on first use)."""
+        if self._q_t is None:
+            self._q_t = self._tiled()
+        return self._q_t
+
+    @property
+    def o_t(self):
+        """Tiled O [B, H, Ntot, D] (allocated on first use)."""
+        if self._o_t is None:
+            self._o_t = self._tiled()
+        return self._o_t
 
     def build(self, q, stream=None):
         permute_build(self.desc, self.perm, self.shape_map, q if self.dynamic else None, self.workspace, stream)
@@ -347,6 +387,12 @@ class BlockSparseAttention:
         else:
             gather(self.desc, q, self.q_t, self.perm, stream)
             gather_kf(self.desc, k, self.k_f, self.perm, stream)
+
+    def pool_qk(self, q, k, stream=None):
+        """The raster-I/O path's first step: Q's tile means (no tiled copy) and
+        the K gather with K's means."""
+        pool(self.desc, q, self.perm, self.workspace, stream)
+        gather_kf_pool(self.desc, k, self.k_f, self.perm, self.workspace, stream)
 
     def gather_v(self, v, stream=None):
         gather_vf(self.desc, v, self.v_f, self.perm, stream)
@@ -374,6 +420,11 @@ class BlockSparseAttention:
         forward(self.desc, self.q_t, self.k_f, self.v_f, self.block_idx, self.o_t, self.lse,
                 self.workspace if self.grouped else None, stream)
 
+    def forward_raster(self, q, out, stream=None):
+        """The forward from raster Q straight into raster ``out``."""
+        forward_raster(self.desc, q, self.perm, self.k_f, self.v_f, self.block_idx, out, self.lse,
+                       self.workspace if self.grouped else None, stream)
+
     def scatter_out(self, out, stream=None):
         scatter(self.desc, self.o_t, out, self.perm, stream)
 
@@ -381,6 +432,11 @@ class BlockSparseAttention:
         if out is None:
             out = torch.empty_like(q)
         self.build(q, stream)
+        if self.raster_io:
+            self.pool_qk(q, k, stream)
+            self.gather_v_and_plan(v, stream)
+            self.forward_raster(q, out, stream)
+            return out
         self.gather_qk(q, k, stream)
         self.gather_v_and_plan(v, stream)
         self.forward(stream)

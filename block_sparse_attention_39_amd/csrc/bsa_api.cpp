@@ -229,7 +229,7 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
-    if (op < BSA_PERM_BUILD || op > BSA_PERM_TILED_TO_VF) return BSA_ERR_ARG;
+    if (op < BSA_PERM_BUILD || op > BSA_PERM_POOL) return BSA_ERR_ARG;
     if (g.B == 0 || g.n_tot == 0) return BSA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (op == BSA_PERM_BUILD) {
@@ -261,6 +261,17 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
         return launched(bsa::launch_tiled_to_frag(op == BSA_PERM_TILED_TO_KF, static_cast<const uint16_t*>(src),
                                                   static_cast<uint16_t*>(dst), (int)g.B, (int)g.H, (int)g.D,
                                                   g.n_tot, s));
+    }
+    if (op == BSA_PERM_POOL) {
+        if (g.n_video == 0) return BSA_OK;
+        if (!src || !perm) return BSA_ERR_NULL;
+        if (misaligned(src, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
+        if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
+        const Layout L = layout(g);
+        if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+        if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        return launched(bsa::launch_pool_raster(static_cast<const uint16_t*>(src), perm, (int)g.B, (int)g.H,
+                                                (int)g.D, (int)g.npf, g.n_video, pool_outs(L, ws).q, s, g.n_ras));
     }
     if (!src || !dst || (g.n_video > 0 && !perm)) return BSA_ERR_NULL;
     if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
@@ -369,6 +380,32 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
     bsa::ForwardArgs a;
     const bsa_status st = forward_args(desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse, &g, &a);
     if (st != BSA_OK || g.empty) return st;
+    int* progress = nullptr;
+    if (ws) {
+        const Layout L = layout(g);
+        if (ws_bytes < L.total) return BSA_ERR_WORKSPACE;
+        if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
+    }
+    return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+bsa_status bsa_forward_raster(const bsa_desc* desc, const void* q_raster, const int32_t* perm, const void* k_frag,
+                              const void* v_frag, const int32_t* block_idx, void* o_raster, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+    Geo g;
+    bsa::ForwardArgs a;
+    const bsa_status st = forward_args(desc, q_raster, k_frag, v_frag, block_idx, o_raster, lse, &g, &a);
+    if (st != BSA_OK || g.empty) return st;
+    if (g.n_video > 0 && !perm) return BSA_ERR_NULL;
+    if (misaligned(perm, 4)) return BSA_ERR_ALIGN;
+    // raster rows: prefix + real video tokens, whose raster and slot numbers
+    // the kernel keeps in int
+    if (g.npf + g.n_ras > INT32_MAX / 2) return BSA_ERR_UNSUPPORTED;
+    a.raster = true;
+    a.perm = perm;  // read for video slots only
+    a.n_ras = g.npf + g.n_ras;
+    a.H = (int)g.H;
     int* progress = nullptr;
     if (ws) {
         const Layout L = layout(g);

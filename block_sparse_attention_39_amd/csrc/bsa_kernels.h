@@ -155,6 +155,11 @@ hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, co
                               int D, int n_prefix, int64_t n_video, const PoolOut& po, hipStream_t s,
                               int64_t n_raster_video = -1);
 
+// The tile means of the video tiles of raster Q alone (no copy), read through
+// perm, into `po` exactly as launch_gather_pool writes them.
+hipError_t launch_pool_raster(const uint16_t* src, const int32_t* perm, int B, int H, int D, int n_prefix,
+                              int64_t n_video, const PoolOut& po, hipStream_t s, int64_t n_raster_video = -1);
+
 // Tiled [B][H][Ntot][D] -> the K-fragment (kfrag true) or V-fragment layout.
 hipError_t launch_tiled_to_frag(bool kfrag, const uint16_t* src, uint16_t* dst, int B, int H, int D, int64_t n_tot,
                                 hipStream_t s);
@@ -198,15 +203,20 @@ struct StructRule {
 hipError_t launch_structured(const StructRule& sr, int BH, int H, int64_t* row_ptr, int32_t* col, hipStream_t s);
 
 struct ForwardArgs {
-    const uint16_t* q;       // tiled [BH][Ntot][D]
+    const uint16_t* q;       // tiled [BH][Ntot][D], or raster [B][n_ras][H][D] (raster)
     const uint16_t* k;       // K-fragment layout [BH][Ntot/64][2][D/16][64][8]
     const uint16_t* v;       // V-fragment layout [BH][Ntot/64][2][D/32][2][64][8]
     const int32_t* idx;      // [BH][nvt][keep], or CSR column indices when row_ptr is set
     const int64_t* row_ptr;  // CSR row pointers [BH * nvt + 1], or null (fixed keep)
     int64_t col_entries;     // CSR: entries of idx (list bounds are clamped to it)
     PadGeo pad;              // ragged grid: padding keys of boundary tiles are masked
-    uint16_t* o;             // tiled [BH][Ntot][D]
+    uint16_t* o;             // tiled [BH][Ntot][D], or raster [B][n_ras][H][D] (raster)
     float* lse;              // [BH][Ntot] or null
+    bool raster;             // Q and O in the raster layout, through perm
+    const int32_t* perm;     // raster: tiled video slot -> raster video token [B][nvt*64]
+                             // (-1: padding slot)
+    int64_t n_ras;           // raster rows per batch element (prefix + real video tokens)
+    int H;                   // heads (the raster layout interleaves them)
     int BH;
     int npt;                 // prefix tiles
     int nvt;                 // video tiles

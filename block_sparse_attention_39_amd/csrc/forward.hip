@@ -94,6 +94,11 @@ struct Cfg {
     static constexpr int QFRAG = 2 * SD * 64 * 4;          // floats
     static constexpr int LOOP_ALL = kMaxListTiles + QFRAG;
     static constexpr int LDS_FLOATS = MERGE_ALL > LOOP_ALL ? MERGE_ALL : LOOP_ALL;
+    // raster Q and O: the raster row of each of the tile's 64 tokens, past
+    // both areas (written at staging, read by the epilogue's stores)
+    static constexpr int ROWS = LDS_FLOATS;
+    template <bool kRas>
+    static constexpr int lds_floats() { return LDS_FLOATS + (kRas ? kTile : 0); }
 };
 
 // max of x over lane l and lane l ^ 32
@@ -218,14 +223,26 @@ __device__ inline int list_tile(const ForwardArgs& a, const Item& it, int j, int
     return (it.vi < 0 || j < a.npt) ? j : a.npt + min(max(raw, 0), a.nvt - 1);
 }
 
+// Raster Q and O: the raster row (inside its batch element) of token `tok` of
+// query tile `it`.  Prefix tokens keep their positions; a video slot maps
+// through perm, and a padding slot gives -1.
+__device__ inline int raster_row(const ForwardArgs& a, const Item& it, int tok) {
+    const int p = it.qt * kTile + tok, np = a.npt * kTile;
+    if (p < np) return p;
+    const int v = a.perm[(it.bh / a.H) * ((int64_t)a.nvt * kTile) + (p - np)];
+    return v < 0 ? -1 : np + v;
+}
+
 // Issue the loads a query tile starts with: this wave's K and V fragments of
 // its first slice and the K fragments of its second (tiles t0, t1), this
 // thread's chunks of the tile's Q^T fragments and its first kept-list entries.
-template <int D>
+// kRas: Q is raster; lane l's `rowq` is the raster row of the tile's token l.
+template <int D, bool kRas>
 __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardArgs& a, const Item& it, int t0, int t1,
                                                                   const Wave& w, bf16x8 (&kf)[2][Cfg<D>::SD],
                                                                   bf16x8 (&vf)[2][Cfg<D>::NV],
-                                                                  u32x4 (&qpre)[Regs<D>::QPT], int (&lpre)[kListPre]) {
+                                                                  u32x4 (&qpre)[Regs<D>::QPT], int (&lpre)[kListPre],
+                                                                  int rowq) {
     using CF = Cfg<D>;
     constexpr int SD = CF::SD, TB = CF::TB;
     const int n_tiles = a.npt + a.nvt;
@@ -237,13 +254,28 @@ __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardA
     load_frags(kf[1], krs, lofs, t1 * TB);
     // Q^T operand fragment (query half qb, step s) of chunk f: lane holds
     // query 32*qb + lr, channels 16*s + 8*hf .. +7
+    if constexpr (kRas) {
+        // token row r of this (batch, head) at qh + r * H * D; a padding
+        // slot loads row 0 and is zeroed
+        const int64_t b = it.bh / a.H, h = it.bh % a.H;
+        const uint16_t* qh = a.q + (b * a.n_ras * a.H + h) * D;
 #pragma unroll
-    for (int u = 0; u < Regs<D>::QPT; ++u) {
-        const int f = w.tid + 256 * u;
-        const int fl = f & 63, fs = (f >> 6) % SD, fq = f / (64 * SD);
-        const uint16_t* src =
-            a.q + (it.bh * n_tot + (int64_t)it.qt * kTile + 32 * fq + (fl & 31)) * D + 16 * fs + 8 * (fl >> 5);
-        qpre[u] = *(const u32x4*)src;
+        for (int u = 0; u < Regs<D>::QPT; ++u) {
+            const int f = w.tid + 256 * u;
+            const int fl = f & 63, fs = (f >> 6) % SD, fq = f / (64 * SD);
+            const int r = __shfl(rowq, 32 * fq + (fl & 31));
+            const u32x4 x = *(const u32x4*)(qh + (int64_t)max(r, 0) * a.H * D + 16 * fs + 8 * (fl >> 5));
+            qpre[u] = r < 0 ? u32x4{} : x;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < Regs<D>::QPT; ++u) {
+            const int f = w.tid + 256 * u;
+            const int fl = f & 63, fs = (f >> 6) % SD, fq = f / (64 * SD);
+            const uint16_t* src =
+                a.q + (it.bh * n_tot + (int64_t)it.qt * kTile + 32 * fq + (fl & 31)) * D + 16 * fs + 8 * (fl >> 5);
+            qpre[u] = *(const u32x4*)src;
+        }
     }
 #pragma unroll
     for (int u = 0; u < kListPre; ++u) lpre[u] = 0;
@@ -262,14 +294,16 @@ __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardA
 // issued for it.  With `has_next`, the first loads of the block's next tile
 // `nx` are issued before this tile's epilogue, so that their latency overlaps
 // it.  `vi` < 0 marks a prefix (dense) query tile.  kPad: a ragged grid, whose
-// boundary key tiles have padding keys to mask.
-template <int D, bool kPad>
+// boundary key tiles have padding keys to mask.  kRas: raster Q and O; `rowq`
+// holds this tile's raster rows (lane l: token l) on entry and the next
+// tile's on exit.
+template <int D, bool kPad, bool kRas>
 __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs& a, float* lds, const Item& it,
                                                                bool has_next, const Item& nx, const Wave& w,
                                                                bf16x8 (&kf)[2][Cfg<D>::SD],
                                                                bf16x8 (&vf)[2][Cfg<D>::NV],
                                                                u32x4 (&qpre)[Regs<D>::QPT],
-                                                               int (&lpre)[kListPre]) {
+                                                               int (&lpre)[kListPre], int& rowq) {
     using CF = Cfg<D>;
     constexpr int SD = CF::SD, OD = CF::OD, NV = CF::NV, TB = CF::TB;
     const int tid = w.tid, wave = w.wave, lane = w.lane, par = w.par, kh = w.kh, lr = w.lr, hf = w.hf;
@@ -305,7 +339,11 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     }
 #pragma unroll
     for (int u = 0; u < Regs<D>::QPT; ++u) *(u32x4*)(qlds + (tid + 256 * u) * 16) = qpre[u];
+    if (kRas && tid < kTile) ((int*)(lds + CF::ROWS))[tid] = rowq;
     __syncthreads();
+    // raster Q and O: the next tile's raster rows, read now and used by its
+    // first loads in this tile's epilogue
+    if (kRas && has_next) rowq = raster_row(a, nx, lane);
 
     // the next tile's first two tile numbers for this wave, read now from
     // global memory and used after the main loop
@@ -501,7 +539,7 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     if (has_next) {
         const int t0 = list_tile(a, nx, min(par, n_iter_nx - 1), __builtin_amdgcn_readfirstlane(nraw0));
         const int t1 = list_tile(a, nx, min(par + 2, n_iter_nx - 1), __builtin_amdgcn_readfirstlane(nraw1));
-        fetch_first<D>(a, nx, t0, t1, w, kf, vf, qpre, lpre);
+        fetch_first<D, kRas>(a, nx, t0, t1, w, kf, vf, qpre, lpre, rowq);
     }
 
     // ---- merge the four partial results of every query, normalise, store --
@@ -544,6 +582,9 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     {
         constexpr int C = D / 8;
         uint16_t* orow = a.o + (bh * n_tot + (int64_t)qt * kTile) * D;
+        // raster O: token row r of this (batch, head) at oh + r * H * D
+        uint16_t* oh = kRas ? a.o + ((bh / a.H) * a.n_ras * a.H + bh % a.H) * D : nullptr;
+        const int* rows = (const int*)(lds + CF::ROWS);
 #pragma unroll
         for (int u = 0; u < kTile * C / 256; ++u) {
             const int cidx = tid + 256 * u;
@@ -563,32 +604,38 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                 pk[e] = __builtin_bit_cast(uint32_t, lo);
                 pk[2 + e] = __builtin_bit_cast(uint32_t, hi);
             }
-            *(u32x4*)(orow + r * D + 8 * c) = pk;
+            if constexpr (kRas) {
+                const int row = rows[r];  // -1: a padding slot, not stored
+                if (row >= 0) *(u32x4*)(oh + (int64_t)row * a.H * D + 8 * c) = pk;
+            } else {
+                *(u32x4*)(orow + r * D + 8 * c) = pk;
+            }
         }
     }
 }
 
 // The first loads of a block's first tile (nothing to overlap them with).
-template <int D>
+template <int D, bool kRas>
 __device__ __attribute__((always_inline)) inline void fetch_first_direct(const ForwardArgs& a, const Item& it,
                                                                          const Wave& w,
                                                                          bf16x8 (&kf)[2][Cfg<D>::SD],
                                                                          bf16x8 (&vf)[2][Cfg<D>::NV],
                                                                          u32x4 (&qpre)[Regs<D>::QPT],
-                                                                         int (&lpre)[kListPre]) {
+                                                                         int (&lpre)[kListPre], int& rowq) {
     const int n = list_len(a, it);
     const int j0 = min(w.par, n - 1), j1 = min(w.par + 2, n - 1);
     const int t0 = list_tile(a, it, j0, __builtin_amdgcn_readfirstlane(list_raw(a, it, j0)));
     const int t1 = list_tile(a, it, j1, __builtin_amdgcn_readfirstlane(list_raw(a, it, j1)));
-    fetch_first<D>(a, it, t0, t1, w, kf, vf, qpre, lpre);
+    if (kRas) rowq = raster_row(a, it, w.lane);
+    fetch_first<D, kRas>(a, it, t0, t1, w, kf, vf, qpre, lpre, rowq);
 }
 
 // Plain launch: block g handles query tile g of [prefix tiles of every (b,h)]
 // followed by [video tiles of every (b,h)], starting at tile `first`.
-template <int D, bool kPad>
+template <int D, bool kPad, bool kRas>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 sparse_fwd_kernel(ForwardArgs a, int64_t first) {
-    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::template lds_floats<kRas>()];
     const int64_t g = first + blockIdx.x;
     const int64_t n_pref = (int64_t)a.BH * a.npt;
     Item it;
@@ -603,17 +650,18 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
     bf16x8 kf[2][Cfg<D>::SD], vf[2][Cfg<D>::NV];
     u32x4 qpre[Regs<D>::QPT];
     int lpre[kListPre];
-    fetch_first_direct<D>(a, it, w, kf, vf, qpre, lpre);
-    run_tile<D, kPad>(a, lds, it, false, it, w, kf, vf, qpre, lpre);
+    int rowq = 0;
+    fetch_first_direct<D, kRas>(a, it, w, kf, vf, qpre, lpre, rowq);
+    run_tile<D, kPad, kRas>(a, lds, it, false, it, w, kf, vf, qpre, lpre, rowq);
 }
 
 // Grouped persistent launch over the video query tiles: block b belongs to
 // group b % 8; round r of group g covers video query tiles
 // [(r*8 + g)*S, (r*8 + g + 1)*S) of the flattened (b, h, tile) order.
-template <int D, bool kPad>
+template <int D, bool kPad, bool kRas>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 sparse_fwd_grouped_kernel(ForwardArgs a, int* progress, int* stats) {
-    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::template lds_floats<kRas>()];
     const int group = blockIdx.x % kGroups, slot = blockIdx.x / kGroups;
     const int S = gridDim.x / kGroups;
     const int64_t n_items = (int64_t)a.BH * a.nvt;
@@ -626,9 +674,10 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress, int* stats) {
     bf16x8 kf[2][Cfg<D>::SD], vf[2][Cfg<D>::NV];
     u32x4 qpre[Regs<D>::QPT];
     int lpre[kListPre];
+    int rowq = 0;
     if (item_of(0) < n_items) {
         Item cur = make(item_of(0));
-        fetch_first_direct<D>(a, cur, w, kf, vf, qpre, lpre);
+        fetch_first_direct<D, kRas>(a, cur, w, kf, vf, qpre, lpre, rowq);
         for (int64_t r = 0;; ++r) {
             // publish the round, then wait (bounded) until every block of the
             // group has started it; the barrier at the start of the tile holds
@@ -656,7 +705,7 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress, int* stats) {
             }
             const bool has_next = item_of(r + 1) < n_items;
             const Item nx = has_next ? make(item_of(r + 1)) : cur;
-            run_tile<D, kPad>(a, lds, cur, has_next, nx, w, kf, vf, qpre, lpre);
+            run_tile<D, kPad, kRas>(a, lds, cur, has_next, nx, w, kf, vf, qpre, lpre, rowq);
             if (!has_next) break;
             cur = nx;
         }
@@ -669,17 +718,17 @@ __global__ void clear_progress_kernel(int* progress, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) progress[i] = 0;
 }
 
-template <int D, bool kPad>
+template <int D, bool kPad, bool kRas>
 hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) {
     const int64_t n_pref = (int64_t)a.BH * a.npt;
     const int64_t n_vid = (int64_t)a.BH * a.nvt;
     if (!progress) {
         if (n_pref + n_vid > 0)
-            hipLaunchKernelGGL((sparse_fwd_kernel<D, kPad>), dim3((unsigned)(n_pref + n_vid)), dim3(256), 0, s, a,
+            hipLaunchKernelGGL((sparse_fwd_kernel<D, kPad, kRas>), dim3((unsigned)(n_pref + n_vid)), dim3(256), 0, s, a,
                                (int64_t)0);
         return hipGetLastError();
     }
-    if (n_pref > 0) hipLaunchKernelGGL((sparse_fwd_kernel<D, kPad>), dim3((unsigned)n_pref), dim3(256), 0, s, a, (int64_t)0);
+    if (n_pref > 0) hipLaunchKernelGGL((sparse_fwd_kernel<D, kPad, kRas>), dim3((unsigned)n_pref), dim3(256), 0, s, a, (int64_t)0);
     if (n_vid == 0) return hipGetLastError();
     // persistent grid: the blocks that fit at once, a multiple of the group
     // count, at most kMaxGroupSize per group, and no more than the work
@@ -687,7 +736,7 @@ hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) 
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_fwd_grouped_kernel<D, kPad>, 256, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_fwd_grouped_kernel<D, kPad, kRas>, 256, 0);
     if (e != hipSuccess) return e;
     int64_t grid = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     grid = grid / kGroups * kGroups;
@@ -697,7 +746,7 @@ hipError_t launch_forward_d(const ForwardArgs& a, int* progress, hipStream_t s) 
     if (grid < kGroups) grid = kGroups;
     int* stats = progress + kGroups * kMaxGroupSize;
     hipLaunchKernelGGL(clear_progress_kernel, dim3(1), dim3(512), 0, s, progress, kGroups * kMaxGroupSize + kStatInts);
-    hipLaunchKernelGGL((sparse_fwd_grouped_kernel<D, kPad>), dim3((unsigned)grid), dim3(256), 0, s, a, progress,
+    hipLaunchKernelGGL((sparse_fwd_grouped_kernel<D, kPad, kRas>), dim3((unsigned)grid), dim3(256), 0, s, a, progress,
                        stats);
     return hipGetLastError();
 }
@@ -755,11 +804,20 @@ size_t forward_scratch_bytes() { return sizeof(scratch); }
 size_t forward_workspace_bytes() { return (size_t)(kGroups * kMaxGroupSize + kStatInts) * sizeof(int); }
 size_t forward_stats_offset() { return (size_t)kGroups * kMaxGroupSize * sizeof(int); }
 
+namespace {
+template <bool kRas>
+hipError_t launch_forward_r(const ForwardArgs& a, int D, int* progress, hipStream_t s) {
+    if (a.pad.T != 0)
+        return D == 128 ? launch_forward_d<128, true, kRas>(a, progress, s)
+                        : launch_forward_d<64, true, kRas>(a, progress, s);
+    return D == 128 ? launch_forward_d<128, false, kRas>(a, progress, s)
+                    : launch_forward_d<64, false, kRas>(a, progress, s);
+}
+}  // namespace
+
 hipError_t launch_forward(const ForwardArgs& a, int D, int* progress, hipStream_t s) {
     if ((int64_t)a.BH * (a.npt + a.nvt) == 0) return hipSuccess;
-    if (a.pad.T != 0)
-        return D == 128 ? launch_forward_d<128, true>(a, progress, s) : launch_forward_d<64, true>(a, progress, s);
-    return D == 128 ? launch_forward_d<128, false>(a, progress, s) : launch_forward_d<64, false>(a, progress, s);
+    return a.raster ? launch_forward_r<true>(a, D, progress, s) : launch_forward_r<false>(a, D, progress, s);
 }
 
 hipError_t launch_forward_noalloc(const ForwardArgs& a, int D, hipStream_t s) {

@@ -25,8 +25,12 @@
  * the raster tensors, the forward's lse and dL/dO.  The same result with the
  * tile means taken during the gathers (no second read of Q and K):
  * bsa_permute(GATHER_POOL) for Q and bsa_permute(GATHER_KF_POOL) for K, then
- * bsa_select in place of bsa_plan.  A caller holding K and V already in the
- * tiled layout converts them with bsa_permute(TILED_TO_KF / TILED_TO_VF).
+ * bsa_select in place of bsa_plan.  The shortest sequence also skips the
+ * tiled copies of Q and O: bsa_permute(POOL) for Q's means,
+ * bsa_permute(GATHER_KF_POOL) for K, bsa_permute(GATHER_VF) for V,
+ * bsa_select, then bsa_forward_raster, which reads raster Q and writes raster
+ * O itself.  A caller holding K and V already in the tiled layout converts
+ * them with bsa_permute(TILED_TO_KF / TILED_TO_VF).
  *
  * Layouts (row-major, bf16 = IEEE bfloat16):
  *   raster  bf16 [B][Ntot][H][D]   the dense prefix first (n_prefix tokens, already
@@ -111,7 +115,8 @@ enum {
     BSA_PERM_GATHER_POOL = 5,
     BSA_PERM_GATHER_KF_POOL = 6,
     BSA_PERM_TILED_TO_KF = 7,
-    BSA_PERM_TILED_TO_VF = 8
+    BSA_PERM_TILED_TO_VF = 8,
+    BSA_PERM_POOL = 9
 };
 
 /* Largest number of video tiles per (batch, head) that bsa_plan accepts. */
@@ -180,6 +185,10 @@ bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
  *       into the workspace.
  *  op = BSA_PERM_TILED_TO_KF: `src` tiled -> `dst` kfrag (no perm needed).
  *  op = BSA_PERM_TILED_TO_VF: `src` tiled -> `dst` vfrag.
+ *  op = BSA_PERM_POOL: the tile means of Q alone, read from `src` (raster)
+ *       through `perm` into the workspace (required), the same values
+ *       GATHER_POOL writes, without the tiled copy; `dst` unused.  For
+ *       bsa_forward_raster, which reads Q in the raster layout itself.
  * Gather and scatter read `perm` and copy bf16 values exactly; the prefix
  * tokens keep their positions.  Source and destination must not overlap.
  * The fragment layouts are what bsa_plan and bsa_forward read K and V in:
@@ -266,6 +275,24 @@ bsa_status bsa_forward(const bsa_desc *desc, const void *q_tiled, const void *k_
 bsa_status bsa_forward_noalloc(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
                                const void *v_frag, const int32_t *block_idx, void *o_tiled,
                                float *lse, void *stream);
+
+/*
+ * bsa_forward with Q read from, and O written to, the raster layout through
+ * `perm` (bsa_permute(BUILD)), the token permutation applied inside the
+ * kernel ("Sparse VideoGen TPU 최적화", section "실무에서 배울 최적화 기준":
+ * the reordering is a cost of its own, to be kept small).  The result equals
+ * bsa_permute(GATHER) of Q, bsa_forward, then bsa_permute(SCATTER) of O, bit
+ * for bit, without the tiled copies of Q and O: each query tile's 64 token
+ * rows are read and its 64 output rows written (256-byte head rows for
+ * D = 128) at their raster positions.  Padding slots of a ragged grid read
+ * zeros and are not written.  `q_raster` and `o_raster` bf16 [B][Ntot][H][D]
+ * (Ntot counting the real tokens), `perm` int32 [B][Nvideo]; `k_frag`,
+ * `v_frag`, `block_idx`, `lse` (tiled [B][H][Ntot], padding slots included),
+ * `ws` and the errors as bsa_forward.  o_raster must not overlap q_raster.
+ */
+bsa_status bsa_forward_raster(const bsa_desc *desc, const void *q_raster, const int32_t *perm,
+                              const void *k_frag, const void *v_frag, const int32_t *block_idx,
+                              void *o_raster, float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Byte offset, inside the workspace of bsa_workspace_size(desc), of the
@@ -422,7 +449,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 1001
+#define BSA_VERSION 1002
 
 #ifdef __cplusplus
 }

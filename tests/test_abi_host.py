@@ -108,7 +108,7 @@ def test_bad_tile_mode_and_op():
     d.tile_mode = 7
     assert ws_size(d)[0] == ARG
     d = cfg()
-    assert lib().bsa_permute(ctypes.byref(d), 9, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
+    assert lib().bsa_permute(ctypes.byref(d), 10, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
     assert lib().bsa_permute(ctypes.byref(d), -1, None, FAKE, None, FAKE, FAKE, None, 0, None) == ARG
 
 
@@ -170,7 +170,8 @@ def test_permute_ops_match_header():
     for name, val in (("BUILD", bsa.PERM_BUILD), ("GATHER", bsa.PERM_GATHER), ("SCATTER", bsa.PERM_SCATTER),
                       ("GATHER_KF", bsa.PERM_GATHER_KF), ("GATHER_VF", bsa.PERM_GATHER_VF),
                       ("GATHER_POOL", bsa.PERM_GATHER_POOL), ("GATHER_KF_POOL", bsa.PERM_GATHER_KF_POOL),
-                      ("TILED_TO_KF", bsa.PERM_TILED_TO_KF), ("TILED_TO_VF", bsa.PERM_TILED_TO_VF)):
+                      ("TILED_TO_KF", bsa.PERM_TILED_TO_KF), ("TILED_TO_VF", bsa.PERM_TILED_TO_VF),
+                      ("POOL", bsa.PERM_POOL)):
         m = re.search(r"BSA_PERM_%s = (\d+)" % name, HEADER)
         assert m and int(m.group(1)) == val
     d = cfg()
@@ -187,6 +188,18 @@ def test_permute_ops_match_header():
         assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == WS
         assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE, FAKE + 16, need, None) == ALIGN
         assert L.bsa_permute(ctypes.byref(d), op, None, None, None, FAKE, FAKE, FAKE, need, None) == NULL
+    # the pooling alone reads raster Q through perm into the workspace; no destination
+    P = bsa.PERM_POOL
+    assert L.bsa_permute(ctypes.byref(d), P, None, FAKE, None, None, None, FAKE, need, None) == NULL
+    assert L.bsa_permute(ctypes.byref(d), P, None, None, None, FAKE, None, FAKE, need, None) == NULL
+    assert L.bsa_permute(ctypes.byref(d), P, None, FAKE, None, FAKE + 8, None, FAKE, need, None) == ALIGN
+    assert L.bsa_permute(ctypes.byref(d), P, None, FAKE + 2, None, FAKE, None, FAKE, need, None) == ALIGN
+    assert L.bsa_permute(ctypes.byref(d), P, None, FAKE, None, FAKE, None, None, 0, None) == WS
+    assert L.bsa_permute(ctypes.byref(d), P, None, FAKE, None, FAKE, None, FAKE, need - 1, None) == WS
+    assert L.bsa_permute(ctypes.byref(d), P, None, FAKE, None, FAKE, None, FAKE + 16, need, None) == ALIGN
+    # no video: nothing to pool
+    dp = bsa.make_desc(1, 2, 128, (0, 0, 0), 0, n_prefix=128)
+    assert L.bsa_permute(ctypes.byref(dp), P, None, None, None, None, None, None, 0, None) == 0
     # the tiled -> fragment conversions need no permutation
     for op in (bsa.PERM_TILED_TO_KF, bsa.PERM_TILED_TO_VF):
         assert L.bsa_permute(ctypes.byref(d), op, None, None, None, FAKE, None, None, 0, None) == NULL
@@ -319,3 +332,34 @@ def test_backward_csr_host_checks():
                               None) == ALIGN
     assert L.bsa_backward_csr(ctypes.byref(d), *ptrs[:7], FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, small - 1,
                               None) == WS
+
+
+def test_forward_raster_host_checks():
+    """bsa_forward_raster's argument checks (host only, nothing launched):
+    the tensors and perm are required (perm not without video), aligned, the
+    workspace optional but whole and aligned, and the tile limit is
+    bsa_forward's."""
+    L = lib()
+    d = cfg()
+    F = L.bsa_forward_raster
+    # q, perm, k, v, block_idx, o
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert F(ctypes.byref(d), *args, None, None, 0, None) == NULL
+    assert F(None, *([FAKE] * 6), None, None, 0, None) == NULL
+    assert F(ctypes.byref(d), FAKE + 8, *([FAKE] * 5), None, None, 0, None) == ALIGN
+    assert F(ctypes.byref(d), FAKE, FAKE + 2, *([FAKE] * 4), None, None, 0, None) == ALIGN
+    assert F(ctypes.byref(d), *([FAKE] * 5), FAKE + 8, None, None, 0, None) == ALIGN
+    assert F(ctypes.byref(d), *([FAKE] * 6), FAKE + 1, None, 0, None) == ALIGN
+    st, need = ws_size(d)
+    assert F(ctypes.byref(d), *([FAKE] * 6), None, FAKE, need - 1, None) == WS
+    assert F(ctypes.byref(d), *([FAKE] * 6), None, FAKE + 16, need, None) == ALIGN
+    # prefix only: the tensors are still required
+    dp = bsa.make_desc(1, 2, 128, (0, 0, 0), 0, n_prefix=128)
+    assert F(ctypes.byref(dp), None, None, FAKE, FAKE, None, FAKE, None, None, 0, None) == NULL
+    # too many tiles, as bsa_forward
+    big = bsa.make_desc(1, 1, 64, (16, 128, 260), 10, n_prefix=64 * (bsa._lib.MAX_TILES - 8320 + 1))
+    assert F(ctypes.byref(big), *([FAKE] * 6), None, None, 0, None) == UNSUP
+    # empty problems are no-ops
+    assert F(ctypes.byref(bsa.make_desc(0, 2, 128, (8, 8, 8), 2)), *([None] * 6), None, None, 0, None) == 0

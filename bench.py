@@ -773,7 +773,8 @@ def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, raster: bool, reps: in
     calls after one untimed call), with its HBM bytes and rate against 8 TB/s:
     Q's means alone (the raster-I/O path), the pooling gathers of Q and K, the
     plain gathers they replace, the V gather, the selection, bsa_plan's own
-    pooling + selection (the unfused path) and the output scatter.  plan_ms:
+    pooling + selection (the unfused path), the output scatter, and the
+    attention kernel with tiled and with raster Q and O.  plan_ms:
     what the plan adds to the step, against the plan's roofline (reading Q and
     K once and writing the lists): on the raster-I/O path Q's means plus the
     K gather's time above the plain one plus the selection; on the tiled path
@@ -805,6 +806,12 @@ def kernel_breakdown(bsa, att, desc, wl, qd, kd, vd, out, raster: bool, reps: in
         "select": t(lambda: bsa.select(desc, att.block_idx, att.workspace)),
         "plan_unfused": t(lambda: bsa.plan(desc, att.q_t, att.k_f, att.block_idx, att.workspace)),
         "scatter_o": t(lambda: att.scatter_out(out)),
+        # the attention kernel in both forms, same process (after the gathers above
+        # filled the tiled Q)
+        "forward_tiled_io": t(lambda: bsa.forward(desc, att.q_t, att.k_f, att.v_f, att.block_idx, att.o_t,
+                                                  workspace=att.workspace)),
+        "forward_raster_io": t(lambda: bsa.forward_raster(desc, qd, att.perm, att.k_f, att.v_f, att.block_idx, out,
+                                                          workspace=att.workspace)),
     }
     moved = {"pool_q": bf + pooled, "gather_pool_q": 2 * bf + pooled, "gather_kf_pool_k": 2 * bf + pooled, "gather_q_plain": 2 * bf,
              "gather_kf_k_plain": 2 * bf, "gather_vf_v": 2 * bf, "scatter_o": 2 * bf}

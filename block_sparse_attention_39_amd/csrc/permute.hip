@@ -196,28 +196,27 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
     }
 }
 
-// Q gather with pooling (kStore), or the pooling alone (!kStore: only the
-// video tiles, nothing copied).  One block of 256 threads per (batch, 64-token
+// Q gather with pooling.  One block of 256 threads per (batch, 64-token
 // tile); wave w takes heads w, w + 4, ...  Lane l takes chunk c = l % C (16
 // bytes) and token offset ts = l / C of a head, so one wave load reads the
-// head rows (256 bytes for D = 128) of 64 / C tokens and, in the gather, one
-// wave store writes those 64 / C consecutive tokens of the tiled layout, 1 KB
-// contiguous.  A lane moves tokens ts, ts + 64/C, ... of its chunk and, for a
-// video tile, adds them up in double (exact unless a tile's values span more
-// than 2^39 in magnitude), so the means cost no second read of the tensor.
-// The lanes of a chunk fold their sums (shuffles over the high lane bits); the
-// C lanes with ts = 0 store the chunk's means and fold the sum of their
-// squares for the norm.
-template <bool kPad, bool kStore>
+// head rows (256 bytes for D = 128) of 64 / C tokens and one wave store writes
+// those 64 / C consecutive tokens of the tiled layout, 1 KB contiguous.  A
+// lane moves tokens ts, ts + 64/C, ... of its chunk and, for a video tile,
+// adds them up in double (exact unless a tile's values span more than 2^39 in
+// magnitude), so the means cost no second read of the tensor.  The lanes of a
+// chunk fold their sums (shuffles over the high lane bits); the C lanes with
+// ts = 0 store the chunk's means and fold the sum of their squares for the
+// norm.
+template <bool kPad>
 __global__ __launch_bounds__(256) void gather_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                           const int32_t* __restrict__ perm, int H, int C,
                                                           int n_prefix, int64_t n_video, int64_t n_tot,
                                                           int64_t n_ras, PoolOut po) {
-    constexpr int U = kStore ? 4 : 8;  // loads in flight per lane
+    constexpr int U = 4;  // loads in flight per lane
     __shared__ int64_t tok[kTile];
     __shared__ int real;
     const int b = blockIdx.y;
-    const int64_t p0 = kStore ? (int64_t)blockIdx.x * kTile : n_prefix + (int64_t)blockIdx.x * kTile;
+    const int64_t p0 = (int64_t)blockIdx.x * kTile;
     if (threadIdx.x < kTile) {
         const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
         tok[threadIdx.x] = t;
@@ -233,7 +232,7 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(const uint4* __restric
     const int c = lane % C, ts = lane / C, tpw = 64 / C;  // tpw: tokens per wave access
     for (int h = wave; h < H; h += 4) {
         const int64_t bh = (int64_t)b * H + h;
-        uint4* dh = kStore ? dst + (bh * n_tot + p0) * C + c : nullptr;
+        uint4* dh = dst + (bh * n_tot + p0) * C + c;
         double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int pl0 = 0; pl0 < kTile; pl0 += U * tpw) {
             uint4 x[U];
@@ -242,7 +241,7 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(const uint4* __restric
                 x[u] = src_chunk<false, kPad>(src, b, h, H, C, c, tok[pl0 + ts + tpw * u], n_ras, n_tot);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (kStore) dh[(int64_t)(pl0 + ts + tpw * u) * C] = x[u];
+                dh[(int64_t)(pl0 + ts + tpw * u) * C] = x[u];
                 if (pool) {
                     acc[0] += (double)__uint_as_float(x[u].x << 16);
                     acc[1] += (double)__uint_as_float(x[u].x & 0xffff0000u);
@@ -363,6 +362,59 @@ __global__ __launch_bounds__(256) void gather_kf_pool_kernel(const uint4* __rest
     }
 }
 
+// Q's means alone (no copy), for the forward that reads raster Q itself.  One
+// block per (batch, video tile); thread = (head, 16-byte chunk), chunk
+// fastest, so a wave load reads one token's rows of 64 / C heads, 1 KB
+// contiguous.  A thread adds up its chunk over the tile's 64 tokens in double,
+// eight loads in flight, in token order, and stores the means as the gather
+// does.
+template <bool kPad>
+__global__ __launch_bounds__(1024) void pool_raster_kernel(const uint4* __restrict__ src,
+                                                           const int32_t* __restrict__ perm, int H, int C,
+                                                           int n_prefix, int64_t n_video, int64_t n_ras, PoolOut po) {
+    constexpr int U = 8;  // loads in flight per thread
+    __shared__ int64_t tok[kTile];
+    __shared__ int real;
+    const int b = blockIdx.y;
+    const int64_t vt = blockIdx.x, p0 = n_prefix + vt * kTile;
+    if (threadIdx.x < kTile) {
+        const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        tok[threadIdx.x] = t;
+        const int nr = __popcll(__ballot(t >= 0));
+        if (threadIdx.x == 0) real = nr;
+    }
+    __syncthreads();
+    const int nvt = (int)(n_video / kTile);
+    const double count = kPad ? (double)real : (double)kTile;
+    for (int pr = threadIdx.x; pr < H * C; pr += blockDim.x) {
+        const int h = pr / C, c = pr % C;
+        double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int pl0 = 0; pl0 < kTile; pl0 += U) {
+            uint4 x[U];
+#pragma unroll
+            for (int e = 0; e < U; ++e) x[e] = src_chunk<false, kPad>(src, b, h, H, C, c, tok[pl0 + e], n_ras, 0);
+#pragma unroll
+            for (int e = 0; e < U; ++e) {
+                acc[0] += (double)__uint_as_float(x[e].x << 16);
+                acc[1] += (double)__uint_as_float(x[e].x & 0xffff0000u);
+                acc[2] += (double)__uint_as_float(x[e].y << 16);
+                acc[3] += (double)__uint_as_float(x[e].y & 0xffff0000u);
+                acc[4] += (double)__uint_as_float(x[e].z << 16);
+                acc[5] += (double)__uint_as_float(x[e].z & 0xffff0000u);
+                acc[6] += (double)__uint_as_float(x[e].w << 16);
+                acc[7] += (double)__uint_as_float(x[e].w & 0xffff0000u);
+            }
+        }
+        float m[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = (float)(acc[e] / count);
+        const int64_t bh = (int64_t)b * H + h;
+        float sq = store_pooled8(po, bh, nvt, 8 * C, vt, c, m);
+        for (int o = 1; o < C; o <<= 1) sq += __shfl_xor(sq, o);
+        if (c == 0) po.norm[bh * nvt + vt] = sqrtf(sq);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, const int32_t* perm, int B, int H,
@@ -380,7 +432,7 @@ hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, co
                            n_video, n_tot, n_ras, po);
         return hipGetLastError();
     }
-    auto kernel = pad ? gather_pool_kernel<true, true> : gather_pool_kernel<false, true>;
+    auto kernel = pad ? gather_pool_kernel<true> : gather_pool_kernel<false>;
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H, C, n_prefix,
                        n_video, n_tot, n_ras, po);
     return hipGetLastError();
@@ -392,9 +444,11 @@ hipError_t launch_pool_raster(const uint16_t* src, const int32_t* perm, int B, i
     const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
     if (B == 0 || H == 0 || n_video == 0) return hipSuccess;
     const dim3 grid((unsigned)(n_video / kTile), (unsigned)B);
-    auto kernel = n_ras != n_tot ? gather_pool_kernel<true, false> : gather_pool_kernel<false, false>;
-    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)nullptr, perm, H, D / 8,
-                       n_prefix, n_video, n_tot, n_ras, po);
+    const int pairs = H * (D / 8);
+    const int threads = pairs >= 1024 ? 1024 : (pairs + 63) / 64 * 64;
+    auto kernel = n_ras != n_tot ? pool_raster_kernel<true> : pool_raster_kernel<false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, (const uint4*)src, perm, H, D / 8, n_prefix, n_video,
+                       n_ras, po);
     return hipGetLastError();
 }
 

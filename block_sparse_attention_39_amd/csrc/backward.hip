@@ -129,18 +129,27 @@ __device__ inline int kept_len(const BackwardArgs& a, int64_t r) {
 
 // ---- transposed lists: for each video key tile, the video query tiles that
 // kept it, ascending --------------------------------------------------------
-// bit j of row (bh, i): video query tile i kept video key tile j
+// The query tiles in chunks of 64: mask[bh][chunk][j] has bit q set when video
+// query tile 64*chunk + q kept video key tile j.  One block per (bh, chunk)
+// ORs its 64 kept lists into LDS (a wave per query tile, lanes over its
+// entries), then writes the chunk's nvt words.
 __global__ __launch_bounds__(256) void bwd_mask_kernel(BackwardArgs a) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * nvt + i
-    if (r >= (int64_t)a.BH * a.nvt) return;
-    uint32_t* row = a.mask + r * a.mwords;
-    for (int w = 0; w < a.mwords; ++w) row[w] = 0u;
-    const int32_t* ix = a.idx + kept_begin(a, r);
-    const int len = kept_len(a, r);
-    for (int t = 0; t < len; ++t) {
-        const int j = min(max(ix[t], 0), a.nvt - 1);
-        row[j >> 5] |= 1u << (j & 31);
+    extern __shared__ unsigned long long mw[];  // [nvt]
+    const int64_t bh = blockIdx.x / a.mchunks;
+    const int chunk = (int)(blockIdx.x % a.mchunks);
+    for (int j = threadIdx.x; j < a.nvt; j += 256) mw[j] = 0ull;
+    __syncthreads();
+    const int q0 = chunk * 64, nq = min(64, a.nvt - q0);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int q = wave; q < nq; q += 4) {
+        const int64_t r = bh * a.nvt + q0 + q;
+        const int32_t* ix = a.idx + kept_begin(a, r);
+        const int len = kept_len(a, r);
+        for (int t = lane; t < len; t += 64) atomicOr(&mw[min(max(ix[t], 0), a.nvt - 1)], 1ull << q);
     }
+    __syncthreads();
+    unsigned long long* out = a.mask + (bh * a.mchunks + chunk) * a.nvt;
+    for (int j = threadIdx.x; j < a.nvt; j += 256) out[j] = mw[j];
 }
 
 // cnt[bh][j] = number of video query tiles that kept j
@@ -149,54 +158,65 @@ __global__ __launch_bounds__(256) void bwd_tcount_kernel(BackwardArgs a) {
     if (r >= (int64_t)a.BH * a.nvt) return;
     const int64_t bh = r / a.nvt;
     const int j = (int)(r % a.nvt);
-    const uint32_t* m = a.mask + bh * a.nvt * a.mwords + (j >> 5);
+    const unsigned long long* m = a.mask + bh * a.mchunks * a.nvt + j;
     int c = 0;
-    for (int i = 0; i < a.nvt; ++i) c += (m[(int64_t)i * a.mwords] >> (j & 31)) & 1u;
+    for (int ch = 0; ch < a.mchunks; ++ch) c += __popcll(m[(int64_t)ch * a.nvt]);
     a.cnt[r] = c;
 }
 
 // rowp[0..BH*nvt]: exclusive prefix sums of the counts over (bh, j), one
-// block: each thread sums a contiguous run, the runs are scanned in LDS
+// block walking the counts 1,024 at a time: a shuffle scan per wave, the 16
+// wave totals through LDS, and a running carry
 __global__ __launch_bounds__(1024) void bwd_tscan_kernel(BackwardArgs a) {
-    __shared__ int64_t part[1024];
+    __shared__ int wsum[16];
     const int64_t n = (int64_t)a.BH * a.nvt;
-    const int t = threadIdx.x;
-    const int64_t per = (n + 1023) / 1024;
-    const int64_t lo = min(t * per, n), hi = min(lo + per, n);
-    int64_t s = 0;
-    for (int64_t j = lo; j < hi; ++j) s += a.cnt[j];
-    part[t] = s;
-    __syncthreads();
-    if (t == 0) {
-        int64_t run = 0;
-        for (int u = 0; u < 1024; ++u) {
-            const int64_t v = part[u];
-            part[u] = run;
-            run += v;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int64_t carry = 0;
+    for (int64_t base = 0; base < n; base += 1024) {
+        const int64_t j = base + t;
+        const int v = j < n ? a.cnt[j] : 0;  // each at most nvt: a tile's sum fits in int
+        int x = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
         }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int below = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int sw = wsum[w];
+            below += w < wave ? sw : 0;
+            total += sw;
+        }
+        if (j < n) a.rowp[j] = carry + below + x - v;
+        carry += total;
+        __syncthreads();  // wsum is rewritten by the next tile
     }
-    __syncthreads();
-    int64_t run = part[t];
-    for (int64_t j = lo; j < hi; ++j) {
-        a.rowp[j] = run;
-        run += a.cnt[j];
-    }
-    if (t == 1023) a.rowp[n] = run;
+    if (t == 0) a.rowp[n] = carry;
 }
 
+// tlist[rowp[bh][j] ..]: the video query tiles that kept j, ascending.  A wave
+// per (bh, j) walks the chunk words in order; lane q writes query tile
+// 64*chunk + q at its rank among the word's set bits.
 __global__ __launch_bounds__(256) void bwd_tfill_kernel(BackwardArgs a) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * nvt + j
+    const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;  // bh * nvt + j (whole waves)
     if (r >= (int64_t)a.BH * a.nvt) return;
+    const int lane = threadIdx.x & 63;
     const int64_t bh = r / a.nvt;
     const int j = (int)(r % a.nvt);
-    const uint32_t* m = a.mask + bh * a.nvt * a.mwords + (j >> 5);
-    const int64_t o = a.rowp[r];
-    int64_t p = 0;
-    for (int i = 0; i < a.nvt; ++i)
-        if ((m[(int64_t)i * a.mwords] >> (j & 31)) & 1u) {
-            if (o + p < a.tcap) a.tlist[o + p] = i;  // a list past the capacity is cut (malformed CSR only)
-            ++p;
+    const unsigned long long* m = a.mask + bh * a.mchunks * a.nvt + j;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int64_t o = a.rowp[r];
+    for (int ch = 0; ch < a.mchunks; ++ch) {
+        const unsigned long long w = m[(int64_t)ch * a.nvt];
+        if ((w >> lane) & 1ull) {
+            const int64_t p = o + __popcll(w & below);
+            if (p < a.tcap) a.tlist[p] = ch * 64 + lane;  // a list past the capacity is cut (malformed CSR only)
         }
+        o += __popcll(w);
+    }
 }
 
 // ---- shared pieces of the two gradient kernels -----------------------------
@@ -973,10 +993,11 @@ hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
     if (a.nvt > 0) {
         const int64_t vt = (int64_t)a.BH * a.nvt;
         const unsigned g = (unsigned)((vt + 255) / 256);
-        hipLaunchKernelGGL(bwd_mask_kernel, dim3(g), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)((int64_t)a.BH * a.mchunks)), dim3(256),
+                           (size_t)a.nvt * sizeof(unsigned long long), s, a);
         hipLaunchKernelGGL(bwd_tcount_kernel, dim3(g), dim3(256), 0, s, a);
         hipLaunchKernelGGL(bwd_tscan_kernel, dim3(1), dim3(1024), 0, s, a);
-        hipLaunchKernelGGL(bwd_tfill_kernel, dim3(g), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_tfill_kernel, dim3((unsigned)((vt * 64 + 255) / 256)), dim3(256), 0, s, a);
     }
     const int64_t tiles = (int64_t)a.BH * (a.npt + a.nvt);
     int64_t gq = 0, gk = 0;

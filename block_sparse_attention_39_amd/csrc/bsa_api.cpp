@@ -162,7 +162,7 @@ bsa_status launched(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_LA
 // lists.
 struct BwdLayout {
     size_t frag[7], lse2, delta, nlse, ndelta, mask, cnt, rowp, tlist, progress, total;
-    int mwords;
+    int mchunks;
 };
 
 // tcap: entries of the transposed lists (B*H*nVT*k for fixed keep, the CSR
@@ -180,9 +180,9 @@ BwdLayout bwd_layout(const Geo& g, int64_t tcap) {
     o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
     L.ndelta = o;
     o += align_up((size_t)g.BH * g.n_tot * sizeof(float));
-    L.mwords = (int)((g.nvt + 31) / 32);
+    L.mchunks = (int)((g.nvt + 63) / 64);
     L.mask = o;
-    o += align_up((size_t)g.BH * g.nvt * L.mwords * sizeof(uint32_t));
+    o += align_up((size_t)g.BH * L.mchunks * g.nvt * sizeof(uint64_t));
     L.cnt = o;
     o += align_up((size_t)g.BH * g.nvt * sizeof(int32_t));
     L.rowp = o;
@@ -687,7 +687,7 @@ bsa_status backward_impl(const bsa_desc* desc, const void* q, const void* k, con
     a.delta = reinterpret_cast<float*>(w + L.delta);
     a.nlse = reinterpret_cast<float*>(w + L.nlse);
     a.ndelta = reinterpret_cast<float*>(w + L.ndelta);
-    a.mask = reinterpret_cast<uint32_t*>(w + L.mask);
+    a.mask = reinterpret_cast<unsigned long long*>(w + L.mask);
     a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
     a.rowp = reinterpret_cast<int64_t*>(w + L.rowp);
     a.tlist = reinterpret_cast<int32_t*>(w + L.tlist);
@@ -701,7 +701,7 @@ bsa_status backward_impl(const bsa_desc* desc, const void* q, const void* k, con
     a.npt = (int)g.npt;
     a.nvt = (int)g.nvt;
     a.keep = (int)g.k;
-    a.mwords = L.mwords;
+    a.mchunks = L.mchunks;
     a.npf = g.npf;
     a.n_tot = g.n_tot;
     a.n_ras = g.npf + g.n_ras;

@@ -247,7 +247,7 @@ struct BackwardArgs {
     const int32_t* perm;       // [B][Nvideo], -1 for a padding slot
     float *lse2, *delta;       // [BH][Ntot] scratch: lse * log2 e, dO . O
     float *nlse, *ndelta;      // [BH][Ntot] scratch: -lse / scale, -(dO . O)
-    uint32_t* mask;            // [BH][nvt][mwords] scratch
+    unsigned long long* mask;  // [BH][mchunks][nvt] scratch: bit q of [bh][c][j]: query tile 64c + q kept j
     int32_t* cnt;              // [BH][nvt] scratch: query tiles that kept each key tile
     int64_t* rowp;             // [BH * nvt + 1] scratch: exclusive prefix sums of cnt
     int32_t* tlist;            // [tcap] scratch: the transposed lists, (bh, key tile) order
@@ -255,7 +255,7 @@ struct BackwardArgs {
     uint16_t *dq, *dk, *dv;    // raster [B][Ntot][H][D]
     int* progress;             // backward_progress_ints() ints: grouped-launch round counters,
                                // then 4 statistics (backward_stats_ints())
-    int BH, H, npt, nvt, keep, mwords;
+    int BH, H, npt, nvt, keep, mchunks;
     int64_t npf, n_tot;        // tiled rows per (b, h): prefix + video slots
     int64_t n_ras;             // raster rows per batch element (fewer on a ragged grid)
     PadGeo pad;                // ragged grid (pad.T != 0): perm -1 marks padding slots

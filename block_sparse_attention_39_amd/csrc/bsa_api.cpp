@@ -30,6 +30,12 @@ struct Geo {
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
+// true when the byte ranges [p, p + pb) and [q, q + qb) intersect
+bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return pb > 0 && qb > 0 && a < b + qb && b < a + pb;
+}
+
 bsa_status check_desc(const bsa_desc* d, Geo* g) {
     if (!d) return BSA_ERR_NULL;
     if (d->batch < 0 || d->heads < 0 || d->grid_t < 0 || d->grid_h < 0 || d->grid_w < 0 || d->n_prefix < 0)
@@ -255,9 +261,12 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
         return launched(e);
     }
     if (g.H == 0) return BSA_OK;
+    const size_t tiled = (size_t)g.BH * g.n_tot * g.D * 2;
+    const size_t raster = (size_t)g.B * (g.npf + g.n_ras) * g.H * g.D * 2;
     if (op == BSA_PERM_TILED_TO_KF || op == BSA_PERM_TILED_TO_VF) {
         if (!src || !dst) return BSA_ERR_NULL;
         if (misaligned(src, 16) || misaligned(dst, 16)) return BSA_ERR_ALIGN;
+        if (overlaps(src, tiled, dst, tiled)) return BSA_ERR_ARG;
         return launched(bsa::launch_tiled_to_frag(op == BSA_PERM_TILED_TO_KF, static_cast<const uint16_t*>(src),
                                                   static_cast<uint16_t*>(dst), (int)g.B, (int)g.H, (int)g.D,
                                                   g.n_tot, s));
@@ -275,17 +284,20 @@ bsa_status bsa_permute(const bsa_desc* desc, int op, const void* q_raster, int32
     }
     if (!src || !dst || (g.n_video > 0 && !perm)) return BSA_ERR_NULL;
     if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(perm, 4)) return BSA_ERR_ALIGN;
+    const bool overlap = op == BSA_PERM_SCATTER ? overlaps(src, tiled, dst, raster) : overlaps(src, raster, dst, tiled);
     if (op == BSA_PERM_GATHER_POOL || op == BSA_PERM_GATHER_KF_POOL) {
         if (g.nvt > BSA_MAX_VIDEO_TILES) return BSA_ERR_UNSUPPORTED;
         const Layout L = layout(g);
         if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+        if (overlap) return BSA_ERR_ARG;
         const PoolPair p = pool_outs(L, ws);
         const bool kf = op == BSA_PERM_GATHER_KF_POOL;
         return launched(bsa::launch_gather_pool(kf, static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst),
                                                 perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video,
                                                 kf ? p.k : p.q, s, g.n_ras));
     }
+    if (overlap) return BSA_ERR_ARG;
     if (op == BSA_PERM_GATHER_KF)
         return launched(bsa::launch_gather_kf(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), perm,
                                               (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s, g.n_ras));
@@ -343,6 +355,15 @@ bsa_status bsa_forward_stats_offset(const bsa_desc* desc, size_t* offset) {
 
 namespace {
 
+// The forward's output must not overlap an input that other blocks still
+// read (the last check before a launch): Q and O raster (raster) or tiled,
+// K and V in the fragment layouts (the tiled size).
+bool forward_io_overlap(const Geo& g, const void* q, const void* k, const void* v, const void* o, bool raster) {
+    const size_t tiled = (size_t)g.BH * g.n_tot * g.D * 2;
+    const size_t io = raster ? (size_t)g.B * (g.npf + g.n_ras) * g.H * g.D * 2 : tiled;
+    return overlaps(o, io, q, io) || overlaps(o, io, k, tiled) || overlaps(o, io, v, tiled);
+}
+
 // Checks shared by bsa_forward and bsa_forward_noalloc; fills the kernel
 // arguments.
 bsa_status forward_args(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
@@ -387,6 +408,7 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
+    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false)) return BSA_ERR_ARG;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }
 
@@ -413,6 +435,7 @@ bsa_status bsa_forward_raster(const bsa_desc* desc, const void* q_raster, const 
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
+    if (forward_io_overlap(g, q_raster, k_frag, v_frag, o_raster, true)) return BSA_ERR_ARG;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }
 
@@ -423,6 +446,7 @@ bsa_status bsa_forward_noalloc(const bsa_desc* desc, const void* q_tiled, const 
     const bsa_status st = forward_args(desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse, &g, &a);
     if (st != BSA_OK || g.empty) return st;
     if (bsa::forward_workspace_bytes() > bsa::forward_scratch_bytes()) return BSA_ERR_UNSUPPORTED;
+    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false)) return BSA_ERR_ARG;
     return launched(bsa::launch_forward_noalloc(a, (int)g.D, static_cast<hipStream_t>(stream)));
 }
 
@@ -509,6 +533,7 @@ bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
+    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false)) return BSA_ERR_ARG;
     bsa::ForwardArgs a{};
     a.q = static_cast<const uint16_t*>(q_tiled);
     a.k = static_cast<const uint16_t*>(k_frag);

@@ -102,7 +102,8 @@ typedef enum {
     BSA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
     BSA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than bsa_workspace_size() */
     BSA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch */
-    BSA_ERR_ARG = -7          /* bad enum value or non-finite / non-positive scale */
+    BSA_ERR_ARG = -7          /* bad enum value, non-finite / non-positive scale, or an
+                                 output buffer overlapping an input of the same call */
 } bsa_status;
 
 enum { BSA_TILE_STATIC = 0, BSA_TILE_DYNAMIC = 1, BSA_TILE_STATIC_PADDED = 2 };
@@ -190,7 +191,8 @@ bsa_status bsa_workspace_size(const bsa_desc *desc, size_t *bytes);
  *       GATHER_POOL writes, without the tiled copy; `dst` unused.  For
  *       bsa_forward_raster, which reads Q in the raster layout itself.
  * Gather and scatter read `perm` and copy bf16 values exactly; the prefix
- * tokens keep their positions.  Source and destination must not overlap.
+ * tokens keep their positions.  Source and destination must not overlap
+ * (BSA_ERR_ARG when their byte ranges intersect).
  * The fragment layouts are what bsa_plan and bsa_forward read K and V in:
  * each 1 KB of them is one 16-byte-per-lane load into matrix-instruction
  * operand registers.  A gather writes them straight from the raster layout
@@ -242,7 +244,8 @@ bsa_status bsa_select(const bsa_desc *desc, int32_t *block_idx, void *ws, size_t
  * bf16 products accumulated in float, a float online softmax, and o rounded to
  * bf16 (`o_tiled`, tiled layout).  `lse` (optional, NULL to skip) receives
  * float [B][H][Ntot]: the natural log of sum_j exp(scale * q.k_j) per query.
- * `block_idx` may be NULL only when there is no video.
+ * `block_idx` may be NULL only when there is no video.  `o_tiled` must not
+ * overlap `q_tiled`, `k_frag` or `v_frag` (BSA_ERR_ARG).
  * `ws` (optional): a workspace of bsa_workspace_size() bytes, 256-byte aligned.
  * With it, the video query tiles run as a persistent grid whose blocks, per
  * XCD, sweep the key tiles in step so that a key tile is fetched once into the
@@ -288,7 +291,8 @@ bsa_status bsa_forward_noalloc(const bsa_desc *desc, const void *q_tiled, const 
  * zeros and are not written.  `q_raster` and `o_raster` bf16 [B][Ntot][H][D]
  * (Ntot counting the real tokens), `perm` int32 [B][Nvideo]; `k_frag`,
  * `v_frag`, `block_idx`, `lse` (tiled [B][H][Ntot], padding slots included),
- * `ws` and the errors as bsa_forward.  o_raster must not overlap q_raster.
+ * `ws` and the errors as bsa_forward.  o_raster must not overlap q_raster,
+ * k_frag or v_frag (BSA_ERR_ARG).
  */
 bsa_status bsa_forward_raster(const bsa_desc *desc, const void *q_raster, const int32_t *perm,
                               const void *k_frag, const void *v_frag, const int32_t *block_idx,

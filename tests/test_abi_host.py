@@ -363,3 +363,33 @@ def test_forward_raster_host_checks():
     assert F(ctypes.byref(big), *([FAKE] * 6), None, None, 0, None) == UNSUP
     # empty problems are no-ops
     assert F(ctypes.byref(bsa.make_desc(0, 2, 128, (8, 8, 8), 2)), *([None] * 6), None, None, 0, None) == 0
+
+
+def test_overlapping_output_is_rejected():
+    """An output whose byte range meets an input of the same call is refused
+    on the host (BSA_ERR_ARG), before anything is enqueued: forward (tiled,
+    raster, CSR) and the permutation copies."""
+    L = lib()
+    d = cfg()
+    B, H, D = d.batch, d.heads, d.head_dim
+    n_tot = d.n_prefix + d.grid_t * d.grid_h * d.grid_w
+    tiled = B * H * n_tot * D * 2
+    far = FAKE + 4 * tiled + (1 << 20)  # a second region clear of the first
+    far -= far % 256
+    # forward: o inside q, o just past q (allowed: ranges touch but do not meet)
+    assert L.bsa_forward(ctypes.byref(d), FAKE, far, far + 2 * tiled, FAKE, FAKE + tiled - 256, None, None, 0,
+                         None) == ARG
+    st = L.bsa_forward(ctypes.byref(d), FAKE, far, far + 2 * tiled, FAKE, FAKE, None, None, 0, None)
+    assert st == ARG  # in place
+    # o overlapping k_frag
+    assert L.bsa_forward(ctypes.byref(d), FAKE, far, far + 2 * tiled, FAKE, far + 256, None, None, 0, None) == ARG
+    # raster: o_raster on q_raster
+    F = L.bsa_forward_raster
+    assert F(ctypes.byref(d), FAKE, FAKE, far, far + 2 * tiled, FAKE, FAKE, None, None, 0, None) == ARG
+    # CSR forward
+    assert L.bsa_forward_csr(ctypes.byref(d), FAKE, far, far + 2 * tiled, FAKE, FAKE, 1, FAKE, None, None, 0,
+                             None) == ARG
+    # permute: gather in place, scatter in place, tiled -> fragment in place
+    for op in (bsa.PERM_GATHER, bsa.PERM_GATHER_KF, bsa.PERM_GATHER_VF, bsa.PERM_SCATTER, bsa.PERM_TILED_TO_KF,
+               bsa.PERM_TILED_TO_VF):
+        assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE + 256, None, 0, None) == ARG, op

@@ -27,6 +27,36 @@ def make_desc(batch: int, heads: int, head_dim: int, grid, keep_tiles: int, *, s
                 1.0 / math.sqrt(head_dim) if scale is None else scale, tau)
 
 
+def keep_tiles_for(sparsity: float, n_video_tiles: int) -> int:
+    """Kept key tiles per query tile for a sparsity s in [0, 1]: the (1 - s)
+    share of the n video tiles, rounded to nearest, at least one and at most
+    all of them ("Prism / Kandinsky 6 speed ablation" page, section on Prism's
+    block-sparse attention: s = 0.75 keeps a quarter of the key blocks, 480 of
+    1,920 per query block).  The C interface takes the integer count."""
+    s = float(sparsity)
+    if not 0.0 <= s <= 1.0:
+        raise ValueError(f"sparsity {sparsity} outside [0, 1]")
+    n = int(n_video_tiles)
+    if n <= 0:
+        return 0
+    return min(max(int(math.floor((1.0 - s) * n + 0.5)), 1), n)
+
+
+# Below this many tokens a call stays dense ("倍速で回した一晩" page, section
+# "같은 방식을 직접 해보려면": the sparse attention node leaves calls with
+# fewer tokens than its minimum, 12,288 there, dense).
+DENSE_BELOW_TOKENS = 12288
+
+
+def keep_for_call(sparsity: float, n_video_tiles: int, n_tokens: int,
+                  dense_below: int = DENSE_BELOW_TOKENS) -> int:
+    """keep_tiles_for, except that a call with fewer than ``dense_below``
+    tokens keeps every tile (k = n runs the same kernels densely)."""
+    if n_tokens < dense_below:
+        return max(int(n_video_tiles), 0)
+    return keep_tiles_for(sparsity, n_video_tiles)
+
+
 def video_slots(desc: Desc) -> int:
     """Video tokens of the tiled layouts: the grid, or for a ragged grid the
     grid rounded up to whole tiles."""

@@ -393,3 +393,28 @@ def test_overlapping_output_is_rejected():
     for op in (bsa.PERM_GATHER, bsa.PERM_GATHER_KF, bsa.PERM_GATHER_VF, bsa.PERM_SCATTER, bsa.PERM_TILED_TO_KF,
                bsa.PERM_TILED_TO_VF):
         assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE + 256, None, 0, None) == ARG, op
+
+
+def test_keep_from_sparsity():
+    """The sparsity -> kept-tiles helper against the pages' worked figures:
+    sparsity 0.75 keeps 480 of 1,920 key tiles per query tile (Prism page,
+    section on Prism's block-sparse attention); 0.9375 (the CLI default the
+    same page names) keeps 120; rounding to nearest, clamped to [1, n]; and
+    calls under the 12,288-token minimum of the ComfyUI node ("倍速で回した一晩",
+    section "같은 방식을 직접 해보려면") stay dense."""
+    assert bsa.keep_tiles_for(0.75, 1920) == 480
+    assert bsa.keep_tiles_for(0.9375, 1920) == 120
+    assert bsa.keep_tiles_for(0.9, 1920) == 192 and bsa.keep_tiles_for(0.95, 1920) == 96
+    assert bsa.keep_tiles_for(0.93, 1920) == 134  # 134.4 rounds down
+    assert bsa.keep_tiles_for(0.0, 32) == 32 and bsa.keep_tiles_for(1.0, 32) == 1
+    assert bsa.keep_tiles_for(0.99, 32) == 1      # never zero tiles
+    assert bsa.keep_tiles_for(0.75, 1512) == 378  # the prefix workload's video tiles
+    assert bsa.keep_tiles_for(0.75, 0) == 0
+    for bad in (-0.1, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            bsa.keep_tiles_for(bad, 100)
+    assert bsa.DENSE_BELOW_TOKENS == 12288
+    assert bsa.keep_for_call(0.75, 32, 2048) == 32            # small call: dense
+    assert bsa.keep_for_call(0.75, 1920, 122880) == 480
+    assert bsa.keep_for_call(0.75, 192, 12288) == 48          # at the minimum: sparse
+    assert bsa.keep_for_call(0.75, 192, 12288, dense_below=0) == 48

@@ -199,7 +199,8 @@ def test_maximum_total_tiles_whole_path():
     tiles and 8,192 video tiles (16,384, a million tokens).  Permutation,
     gathers and scatter are bit-exact on every row; the lists against the
     oracle on every row; attention of a prefix query tile (every key) and a
-    video query tile (the prefix plus its kept tiles) against the oracle."""
+    video query tile (the prefix plus its kept tiles) against the oracle; the
+    raster-I/O path equal to the tiled one bit for bit."""
     wl = W("max_tiles", 1, 1, 64, (32, 64, 256), 16, seed=72, n_prefix=8192 * 64)
     print(f"\n[case] {wl}", flush=True)
     assert wl.n_tokens // 64 == bsa.MAX_VIDEO_TILES * 2 and wl.n_video_tiles == bsa.MAX_VIDEO_TILES
@@ -223,3 +224,11 @@ def test_maximum_total_tiles_whole_path():
     print(f"[forward] max|err| {mx:.2e} mean {mean:.2e}", flush=True)
     sc = oracle.scatter(to_bits(g.att.o_t), perm, npf)
     assert np.array_equal(to_bits(g.out), sc)
+    # the raster-I/O path at the same size (raster rows past 2^19 and slot
+    # numbers up to 2^20 - 1): the same output and lse bit for bit
+    att = bsa.BlockSparseAttention(g.desc, with_lse=True)
+    out = torch.full_like(g.q.view(torch.int16), 0x7FC1).view(torch.bfloat16)
+    att(g.q, g.k, g.v, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), g.out.view(torch.int16))
+    assert torch.equal(att.lse, g.att.lse)

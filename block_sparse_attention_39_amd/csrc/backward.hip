@@ -46,7 +46,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxListTilesB = BSA_MAX_TILES;
 
 template <int D>
@@ -78,38 +77,6 @@ __device__ inline int64_t raster_token(const BackwardArgs& a, int b, int64_t row
 __device__ inline uint16_t* raster_row(uint16_t* base, const BackwardArgs& a, int64_t bh, int64_t tok, int D) {
     const int b = (int)bh / a.H, h = (int)bh % a.H;  // bh < B*H <= INT32_MAX
     return base + (((int64_t)b * a.n_ras + tok) * a.H + h) * D;
-}
-
-// ---- Delta = dO . O and lse in base 2, per tiled row ----------------------
-// Also -lse / scale and -Delta: the dK/dV kernel starts its S and dP
-// accumulators from them, so that exp2(c2 * S') = P and P * dP' = dS.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardArgs a) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;  // bh * n_tot + row
-    if (r >= (int64_t)a.BH * a.n_tot) return;
-    const int64_t bh = r / a.n_tot, row = r % a.n_tot;
-    const int b = (int)(bh / a.H);
-    const int64_t tok = raster_token(a, b, row);
-    float s = 0.f;  // a padding row has dO = 0
-    if (tok >= 0) {
-        const uint16_t* o = raster_row(const_cast<uint16_t*>(a.o), a, bh, tok, D);
-        const uint16_t* g = raster_row(const_cast<uint16_t*>(a.dout), a, bh, tok, D);
-#pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const bf16x8 x = *(const bf16x8*)(o + 8 * c), y = *(const bf16x8*)(g + 8 * c);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
-        }
-    }
-    a.delta[r] = s;
-    a.ndelta[r] = -s;
-    if (tok >= 0) {
-        a.lse2[r] = a.lse[r] * kLog2e;
-        a.nlse[r] = -a.lse[r] / a.scale;
-    } else {  // a padding row carries no loss: every weight of it is exactly 0
-        a.lse2[r] = __builtin_inff();
-        a.nlse[r] = -__builtin_inff();
-    }
 }
 
 // ---- kept lists -------------------------------------------------------------
@@ -988,8 +955,6 @@ hipError_t grouped_grid(K kernel, int threads, int64_t work, int64_t* grid) {
 
 template <int D, bool kPad>
 hipError_t launch_backward_d(const BackwardArgs& a, hipStream_t s) {
-    const int64_t rows = (int64_t)a.BH * a.n_tot;
-    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
     if (a.nvt > 0) {
         const int64_t vt = (int64_t)a.BH * a.nvt;
         const unsigned g = (unsigned)((vt + 255) / 256);

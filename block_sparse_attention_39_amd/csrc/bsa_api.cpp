@@ -678,20 +678,25 @@ bsa_status backward_impl(const bsa_desc* desc, const void* q, const void* k, con
     char* w = static_cast<char*>(ws);
     uint16_t* f[7];
     for (int i = 0; i < 7; ++i) f[i] = reinterpret_cast<uint16_t*>(w + L.frag[i]);
-    // f: q_kf, do_kf, k_kf, v_kf (kfrag), k_vf (vfrag), q_t, do_t (tiled)
-    const uint16_t* src_kf[4] = {static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_o),
-                                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
-    const uint16_t* src_t[2] = {static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(d_o)};
-    hipError_t e = hipSuccess;
-    for (int i = 0; i < 4 && e == hipSuccess; ++i)
-        e = bsa::launch_gather_kf(src_kf[i], f[i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf, g.n_video, s,
-                                  g.n_ras);
+    // f: q_kf, do_kf, k_kf, v_kf (kfrag), k_vf (vfrag), q_t, do_t (tiled).
+    // Q, dO and K are read once each for both of their layouts; the dO
+    // gather also takes Delta = dO . O and the lse forms per row.
+    float* lse2 = reinterpret_cast<float*>(w + L.lse2);
+    float* delta = reinterpret_cast<float*>(w + L.delta);
+    float* nlse = reinterpret_cast<float*>(w + L.nlse);
+    float* ndelta = reinterpret_cast<float*>(w + L.ndelta);
+    const bsa::DeltaOut dl{static_cast<const uint16_t*>(o), lse, delta, ndelta, lse2, nlse, desc->scale};
+    const int B = (int)g.B, H = (int)g.H, D = (int)g.D, npf = (int)g.npf;
+    hipError_t e = bsa::launch_gather_kf_tiled(static_cast<const uint16_t*>(q), f[0], f[5], perm, B, H, D, npf,
+                                               g.n_video, s, g.n_ras, nullptr);
     if (e == hipSuccess)
-        e = bsa::launch_gather_vf(static_cast<const uint16_t*>(k), f[4], perm, (int)g.B, (int)g.H, (int)g.D,
-                                  (int)g.npf, g.n_video, s, g.n_ras);
-    for (int i = 0; i < 2 && e == hipSuccess; ++i)
-        e = bsa::launch_permute_copy(false, src_t[i], f[5 + i], perm, (int)g.B, (int)g.H, (int)g.D, (int)g.npf,
-                                     g.n_video, s, g.n_ras);
+        e = bsa::launch_gather_kf_tiled(static_cast<const uint16_t*>(d_o), f[1], f[6], perm, B, H, D, npf, g.n_video,
+                                        s, g.n_ras, &dl);
+    if (e == hipSuccess)
+        e = bsa::launch_gather_kf_vf(static_cast<const uint16_t*>(k), f[2], f[4], perm, B, H, D, npf, g.n_video, s,
+                                     g.n_ras);
+    if (e == hipSuccess)
+        e = bsa::launch_gather_kf(static_cast<const uint16_t*>(v), f[3], perm, B, H, D, npf, g.n_video, s, g.n_ras);
     if (e != hipSuccess) return launched(e);
     bsa::BackwardArgs a{};
     a.q_kf = f[0];
@@ -701,17 +706,14 @@ bsa_status backward_impl(const bsa_desc* desc, const void* q, const void* k, con
     a.k_vf = f[4];
     a.q_t = f[5];
     a.do_t = f[6];
-    a.o = static_cast<const uint16_t*>(o);
-    a.dout = static_cast<const uint16_t*>(d_o);
-    a.lse = lse;
     a.idx = idx;
     a.row_ptr = csr && g.nvt > 0 ? row_ptr : nullptr;
     a.col_entries = col_entries;
     a.perm = perm;
-    a.lse2 = reinterpret_cast<float*>(w + L.lse2);
-    a.delta = reinterpret_cast<float*>(w + L.delta);
-    a.nlse = reinterpret_cast<float*>(w + L.nlse);
-    a.ndelta = reinterpret_cast<float*>(w + L.ndelta);
+    a.lse2 = lse2;
+    a.delta = delta;
+    a.nlse = nlse;
+    a.ndelta = ndelta;
     a.mask = reinterpret_cast<unsigned long long*>(w + L.mask);
     a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
     a.rowp = reinterpret_cast<int64_t*>(w + L.rowp);

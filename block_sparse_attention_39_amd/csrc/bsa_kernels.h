@@ -160,6 +160,25 @@ hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, co
 hipError_t launch_pool_raster(const uint16_t* src, const int32_t* perm, int B, int H, int D, int n_prefix,
                               int64_t n_video, const PoolOut& po, hipStream_t s, int64_t n_raster_video = -1);
 
+// The backward's per-row quantities, taken while dO is gathered: Delta =
+// dO . O (O raster), and the forward's lse as lse * log2 e and -lse / scale
+// (+inf and -inf on a padding row, whose Delta is 0), all [B*H][Ntot] in the
+// tiled row order.
+struct DeltaOut {
+    const uint16_t* o;
+    const float* lse;
+    float *delta, *ndelta, *lse2, *nlse;
+    float scale;
+};
+// Raster -> the K-fragment layout and the tiled layout in one read (Q, or dO
+// with `dl` set: then also the per-row quantities above).
+hipError_t launch_gather_kf_tiled(const uint16_t* src, uint16_t* dst_kf, uint16_t* dst_t, const int32_t* perm, int B,
+                                  int H, int D, int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video,
+                                  const DeltaOut* dl);
+// Raster -> the K-fragment and the V-fragment layouts in one read (K).
+hipError_t launch_gather_kf_vf(const uint16_t* src, uint16_t* dst_kf, uint16_t* dst_vf, const int32_t* perm, int B,
+                               int H, int D, int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video);
+
 // Tiled [B][H][Ntot][D] -> the K-fragment (kfrag true) or V-fragment layout.
 hipError_t launch_tiled_to_frag(bool kfrag, const uint16_t* src, uint16_t* dst, int B, int H, int D, int64_t n_tot,
                                 hipStream_t s);
@@ -239,8 +258,6 @@ struct BackwardArgs {
     // fragment layouts of the tiled tensors (kfrag / vfrag of the C interface)
     const uint16_t *q_kf, *do_kf, *k_kf, *v_kf, *k_vf;
     const uint16_t *q_t, *do_t;  // tiled [BH][Ntot][D]
-    const uint16_t *o, *dout;  // raster [B][Ntot][H][D]
-    const float* lse;          // [BH][Ntot] natural log, tiled order
     const int32_t* idx;        // [BH][nvt][keep], or CSR column indices when row_ptr is set
     const int64_t* row_ptr;    // CSR row pointers [BH * nvt + 1], or null (fixed keep)
     int64_t col_entries;       // CSR: entries of idx (list bounds are clamped to it)

@@ -196,6 +196,174 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
     }
 }
 
+// ---- the backward's gathers: two layouts from one read ---------------------
+// Position of chunk (token pl, 16-byte chunk c) of a tile in the K-fragment
+// layout: chunk (kh, s, lane) holds channels 16 s + 8 (lane / 32) .. +7 of
+// token 32 kh + swap23(lane % 32), and swap23 is its own inverse.
+__device__ inline int kfrag_pos(int pl, int c, int SD) {
+    return ((pl >> 5) * SD + (c >> 1)) * 64 + 32 * (c & 1) + swap23(pl & 31);
+}
+
+// Raster -> tiled and K-fragment layouts (Q, dO), each written 1 KB per wave
+// store.  One block of 4 waves per (batch, tile); a pass takes two heads, wave
+// w the token half w % 2 (32 tokens: K-fragment half kh) of head 2 p + w / 2.
+// A wave loads its rows as the plain gather does (lane = (token, 16-byte
+// chunk), chunk fastest: 1 KB of 256-byte head rows per load), stores them to
+// the tiled layout and into its own 8 KB of LDS (chunk c of token r at
+// c ^ (r % C): conflict-free both ways), then writes its half of the
+// K-fragment tile from there, 1 KB per store.  No wave reads another's rows.
+// kDelta (dO): the same chunk of O is read and the C lanes of a token add up
+// their products into Delta, with the row's lse forms beside it.
+template <bool kPad, bool kDelta>
+__global__ __launch_bounds__(256) void gather_kf_tiled_kernel(const uint4* __restrict__ src,
+                                                              uint4* __restrict__ dst_kf, uint4* __restrict__ dst_t,
+                                                              const int32_t* __restrict__ perm, int H, int C,
+                                                              int n_prefix, int64_t n_video, int64_t n_tot,
+                                                              int64_t n_ras, DeltaOut dl) {
+    __shared__ int64_t tok[kTile];
+    __shared__ uint4 stage[4][32 * 16];  // per wave: 32 tokens x up to 16 chunks
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x, p0 = tile * kTile, n_tiles = n_tot / kTile;
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kh = wave & 1;
+    const int SD = C / 2, tpi = 64 / C;  // tpi: tokens per wave load
+    const int c = lane % C, ts = lane / C;
+    uint4* st = stage[wave];
+    for (int hp = 0; hp < H; hp += 2) {
+        const int h = hp + (wave >> 1);
+        if (h < H) {
+            const int64_t bh = (int64_t)b * H + h;
+            uint4* dt = dst_t + (bh * n_tot + p0) * C;
+#pragma unroll
+            for (int i = 0; i < 32 / tpi; ++i) {
+                const int r = i * tpi + ts, pl = 32 * kh + r;  // r: token within the half
+                const int64_t t = tok[pl];
+                const uint4 x = src_chunk<false, kPad>(src, b, h, H, C, c, t, n_ras, n_tot);
+                dt[pl * C + c] = x;
+                st[r * C + (c ^ (r % C))] = x;
+                if (kDelta) {
+                    const uint4 y = src_chunk<false, kPad>((const uint4*)dl.o, b, h, H, C, c, t, n_ras, n_tot);
+                    float d = 0.f;  // a padding row reads zeros: Delta 0
+                    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        d = fmaf(__uint_as_float(ys[w] << 16), __uint_as_float(xs[w] << 16), d);
+                        d = fmaf(__uint_as_float(ys[w] & 0xffff0000u), __uint_as_float(xs[w] & 0xffff0000u), d);
+                    }
+                    for (int o = 1; o < C; o <<= 1) d += __shfl_xor(d, o);
+                    if (c == 0) {
+                        const int64_t rr = bh * n_tot + p0 + pl;
+                        dl.delta[rr] = d;
+                        dl.ndelta[rr] = -d;
+                        if (t >= 0) {
+                            dl.lse2[rr] = dl.lse[rr] * 1.4426950408889634f;
+                            dl.nlse[rr] = -dl.lse[rr] / dl.scale;
+                        } else {  // a padding row carries no loss: every weight of it is exactly 0
+                            dl.lse2[rr] = __builtin_inff();
+                            dl.nlse[rr] = -__builtin_inff();
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the stage is complete (and the tok reads done)
+        if (h < H) {
+            const int64_t bh = (int64_t)b * H + h;
+            // K-fragment half kh: chunk (kh, s, lane) = channels 16 s + 8 (lane / 32)
+            // of token 32 kh + swap23(lane % 32)
+            uint4* dk = dst_kf + (bh * n_tiles + tile) * (kTile * C) + kh * SD * 64 + lane;
+            const int r = swap23(lane & 31);
+#pragma unroll 4
+            for (int s2 = 0; s2 < SD; ++s2) {
+                const int cc = 2 * s2 + (lane >> 5);
+                dk[s2 * 64] = st[r * C + (cc ^ (r % C))];
+            }
+        }
+        __syncthreads();  // before the next pass overwrites the stage
+    }
+}
+
+// Raster -> K-fragment and V-fragment layouts (K), each written 128 bytes or
+// more per lane group.  The V-fragment gather's mapping: a thread reads 8
+// token rows of one 16-byte chunk and writes their 8 x 8 transpose; a wave
+// covers 32 tokens (D = 128: two waves per head, wave = K-fragment half) or
+// all 64 (D = 64).  It also puts the chunks into its own LDS (chunk c of its
+// token r at c ^ (r % C)) and then writes its K-fragment chunks from there,
+// 1 KB per store.  No wave reads another's rows.
+template <bool kPad>
+__global__ __launch_bounds__(256) void gather_kf_vf_kernel(const uint4* __restrict__ src,
+                                                           uint4* __restrict__ dst_kf, uint4* __restrict__ dst_vf,
+                                                           const int32_t* __restrict__ perm, int H, int C,
+                                                           int n_prefix, int64_t n_video, int64_t n_tot,
+                                                           int64_t n_ras) {
+    __shared__ int64_t tok[kTile];
+    __shared__ uint4 stage[4][512];  // per wave: 32 tokens x 16 chunks, or 64 x 8
+    const int b = blockIdx.y;
+    const int64_t tile = blockIdx.x, p0 = tile * kTile, n_tiles = n_tot / kTile;
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int OD = C / 4, SD = C / 2;
+    const int halves = C == 16 ? 1 : 2;  // K-fragment halves a wave holds
+    const int items = H * 8 * C;
+    uint4* st = stage[wave];
+    for (int base = 0; base < items; base += 256) {
+        const int it = base + threadIdx.x;
+        const int h = it / (8 * C);  // uniform over a wave (8 C is a multiple of 64)
+        const bool on = it < items;
+        const int dc = it % C, g = (it / C) % 8;
+        const int g0 = ((base + wave * 64) / C) % 8;  // the wave's first token group
+        const int kh0 = g0 >> 2;
+        if (on) {
+            uint4 rw[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                rw[i] = src_chunk<false, kPad>(src, b, h, H, C, dc, tok[8 * g + i], n_ras, n_tot);
+            const int64_t tbase = (((int64_t)b * H + h) * n_tiles + tile) * (kTile * C);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * (g - g0) + i;  // token within the wave's range
+                st[r * C + (dc ^ (r % C))] = rw[i];
+            }
+            const int kh = g >> 2, c = (g >> 1) & 1, hf = g & 1, ib = dc >> 2;
+            uint4* out = dst_vf + tbase + ((kh * OD + ib) * 2 + c) * 64 + 32 * hf + 8 * (dc & 3);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int w = e >> 1;
+                uint4 o;
+                if (e & 1) {
+                    o.x = hi_pair(word_of(rw[0], w), word_of(rw[1], w));
+                    o.y = hi_pair(word_of(rw[2], w), word_of(rw[3], w));
+                    o.z = hi_pair(word_of(rw[4], w), word_of(rw[5], w));
+                    o.w = hi_pair(word_of(rw[6], w), word_of(rw[7], w));
+                } else {
+                    o.x = lo_pair(word_of(rw[0], w), word_of(rw[1], w));
+                    o.y = lo_pair(word_of(rw[2], w), word_of(rw[3], w));
+                    o.z = lo_pair(word_of(rw[4], w), word_of(rw[5], w));
+                    o.w = lo_pair(word_of(rw[6], w), word_of(rw[7], w));
+                }
+                out[e] = o;
+            }
+        }
+        __syncthreads();  // the stage is complete
+        if (on) {
+            const int64_t tbase = (((int64_t)b * H + h) * n_tiles + tile) * (kTile * C);
+            for (int hh = 0; hh < halves; ++hh) {
+                const int kh = kh0 + hh;
+                const int r = 32 * hh + swap23(lane & 31);
+                uint4* dk = dst_kf + tbase + kh * SD * 64 + lane;
+#pragma unroll 4
+                for (int s2 = 0; s2 < SD; ++s2) {
+                    const int cc = 2 * s2 + (lane >> 5);
+                    dk[s2 * 64] = st[r * C + (cc ^ (r % C))];
+                }
+            }
+        }
+        __syncthreads();  // before the next pass overwrites the stage
+    }
+}
+
 // Q gather with pooling.  One block of 256 threads per (batch, 64-token
 // tile); wave w takes heads w, w + 4, ...  Lane l takes chunk c = l % C (16
 // bytes) and token offset ts = l / C of a head, so one wave load reads the
@@ -435,6 +603,34 @@ hipError_t launch_gather_pool(bool kfrag, const uint16_t* src, uint16_t* dst, co
     auto kernel = pad ? gather_pool_kernel<true> : gather_pool_kernel<false>;
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst, perm, H, C, n_prefix,
                        n_video, n_tot, n_ras, po);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_kf_tiled(const uint16_t* src, uint16_t* dst_kf, uint16_t* dst_t, const int32_t* perm, int B,
+                                  int H, int D, int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video,
+                                  const DeltaOut* dl) {
+    const int64_t n_tot = n_prefix + n_video;
+    const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    const bool pad = n_ras != n_tot;
+    const DeltaOut d = dl ? *dl : DeltaOut{};
+    auto kernel = dl ? (pad ? gather_kf_tiled_kernel<true, true> : gather_kf_tiled_kernel<false, true>)
+                     : (pad ? gather_kf_tiled_kernel<true, false> : gather_kf_tiled_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst_kf, (uint4*)dst_t, perm, H, D / 8,
+                       n_prefix, n_video, n_tot, n_ras, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_kf_vf(const uint16_t* src, uint16_t* dst_kf, uint16_t* dst_vf, const int32_t* perm, int B,
+                               int H, int D, int n_prefix, int64_t n_video, hipStream_t s, int64_t n_raster_video) {
+    const int64_t n_tot = n_prefix + n_video;
+    const int64_t n_ras = n_prefix + (n_raster_video < 0 ? n_video : n_raster_video);
+    if (B == 0 || H == 0 || n_tot == 0) return hipSuccess;
+    const dim3 grid((unsigned)(n_tot / kTile), (unsigned)B);
+    auto kernel = n_ras != n_tot ? gather_kf_vf_kernel<true> : gather_kf_vf_kernel<false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint4*)src, (uint4*)dst_kf, (uint4*)dst_vf, perm, H,
+                       D / 8, n_prefix, n_video, n_tot, n_ras);
     return hipGetLastError();
 }
 

@@ -254,18 +254,32 @@ def bench_varkeep(args, wl, q, k, v):
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, max(keep_h), scale=wl.scale,
                          n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
-    att = bsa.BlockSparseAttention(desc, pool_in_gather=False)   # the CSR planners pool for themselves
+    raster = not args.tiled_io
+    att = bsa.BlockSparseAttention(desc, pool_in_gather=raster)
     out = torch.empty_like(qd)
     rows = wl.batch * wl.heads * wl.n_video_tiles
     row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
     col = torch.empty(bsa.csr_entries(desc, keep_h), dtype=torch.int32, device="cuda")
-    stages = ["build", "gather", "plan", "forward", "scatter"]
+    # raster I/O: Q's means alone, K and V gathered (K with its means), the CSR
+    # selection from the means, the forward reading raster Q and writing raster
+    # O; tiled: the three gathers, bsa_plan_csr (its own pooling), the tiled
+    # forward and the scatter
+    stages = ["build", "gather", "plan", "forward"] if raster else ["build", "gather", "plan", "forward", "scatter"]
 
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         mark(0)
         att.build(qd)
         mark(1)
+        if raster:
+            att.pool_qk(qd, kd)
+            att.gather_v(vd)
+            mark(2)
+            bsa.select_csr(desc, row_ptr, col, att.workspace, keep_per_head=keep_h)
+            mark(3)
+            bsa.forward_csr_raster(desc, qd, att.perm, att.k_f, att.v_f, row_ptr, col, out, workspace=att.workspace)
+            mark(4)
+            return
         att.gather_qkv(qd, kd, vd)
         mark(2)
         bsa.plan_csr(desc, att.q_t, att.k_f, row_ptr, col, att.workspace, keep_per_head=keep_h)
@@ -278,7 +292,7 @@ def bench_varkeep(args, wl, q, k, v):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
@@ -309,8 +323,11 @@ def bench_varkeep(args, wl, q, k, v):
         "data": "synthetic",
         "config": {"workload": wl.name, "grid_thw": list(wl.grid), "tokens": wl.n_tokens,
                    "video_tiles": wl.n_video_tiles, "batch": wl.batch, "heads": wl.heads,
-                   "head_dim": wl.head_dim, "keep_per_head": keep_h, "effective_tflop_per_call": F / 1e12},
-        "roofline": {"bound": "mfma", "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}> (CSR lists)",
+                   "head_dim": wl.head_dim, "keep_per_head": keep_h, "effective_tflop_per_call": F / 1e12,
+                   "io": "raster Q and O (bsa_forward_csr_raster)" if raster else "tiled Q and O (gather, scatter)"},
+        "roofline": {"bound": "mfma",
+                     "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}, "
+                               f"{str(raster).lower()}> (CSR lists)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},
@@ -334,23 +351,34 @@ def bench_structured(args, wl, q, k, v):
     qd, kd, vd = dev(q), dev(k), dev(v)
     desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
                          n_prefix=wl.n_prefix, tile=wl.tile, padded=wl.padded)
-    att = bsa.BlockSparseAttention(desc, pool_in_gather=False)   # the CSR planners pool for themselves
+    raster = not args.tiled_io
+    att = bsa.BlockSparseAttention(desc, pool_in_gather=False)   # structured lists need no tile means
     out = torch.empty_like(qd)
     rows = wl.batch * wl.heads * wl.n_video_tiles
     row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")
     entries = bsa.structured_entries(desc, mask, rt, rs)
     col = torch.empty(entries, dtype=torch.int32, device="cuda")
-    stages = ["build", "gather", "plan", "forward", "scatter"]
+    # raster I/O: only K and V are gathered, the forward reads raster Q and
+    # writes raster O; tiled: the three gathers, the tiled forward, the scatter
+    stages = ["build", "gather", "plan", "forward"] if raster else ["build", "gather", "plan", "forward", "scatter"]
 
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         mark(0)
         att.build(qd)
         mark(1)
-        att.gather_qkv(qd, kd, vd)
+        if raster:
+            bsa.gather_kf(desc, kd, att.k_f, att.perm)
+            att.gather_v(vd)
+        else:
+            att.gather_qkv(qd, kd, vd)
         mark(2)
         bsa.plan_structured(desc, mask, rt, rs, row_ptr, col)
         mark(3)
+        if raster:
+            bsa.forward_csr_raster(desc, qd, att.perm, att.k_f, att.v_f, row_ptr, col, out, workspace=att.workspace)
+            mark(4)
+            return
         bsa.forward_csr(desc, att.q_t, att.k_f, att.v_f, row_ptr, col, att.o_t, workspace=att.workspace)
         mark(4)
         att.scatter_out(out)
@@ -359,7 +387,7 @@ def bench_structured(args, wl, q, k, v):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
@@ -395,9 +423,11 @@ def bench_structured(args, wl, q, k, v):
                    "video_tiles": wl.n_video_tiles, "batch": wl.batch, "heads": wl.heads,
                    "head_dim": wl.head_dim, "head_mask": "even spatial, odd temporal", "radius_t": rt,
                    "radius_hw": rs, "kept_entries": entries,
-                   "mean_kept_tiles": entries / rows, "effective_tflop_per_call": F / 1e12},
+                   "mean_kept_tiles": entries / rows, "effective_tflop_per_call": F / 1e12,
+                   "io": "raster Q and O (bsa_forward_csr_raster)" if raster else "tiled Q and O (gather, scatter)"},
         "roofline": {"bound": "mfma",
-                     "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}> (CSR lists)",
+                     "kernel": f"sparse_fwd_grouped_kernel<{wl.head_dim}, {str(wl.padded).lower()}, "
+                               f"{str(raster).lower()}> (CSR lists)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
         "stages_ms": {s: float(np.mean(per_stage[s])) for s in stages},

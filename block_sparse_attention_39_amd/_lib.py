@@ -21,8 +21,8 @@ MAX_TILES = 16384
 # the exported entry points, in the order include/bsa.h declares them
 EXPORTS = ("bsa_workspace_size", "bsa_permute", "bsa_plan", "bsa_select", "bsa_forward", "bsa_forward_stats_offset",
            "bsa_forward_noalloc", "bsa_forward_raster",
-           "bsa_csr_entries", "bsa_plan_csr",
-           "bsa_forward_csr", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
+           "bsa_csr_entries", "bsa_plan_csr", "bsa_select_csr",
+           "bsa_forward_csr", "bsa_forward_csr_raster", "bsa_structured_entries", "bsa_plan_structured", "bsa_backward_workspace_size",
            "bsa_backward", "bsa_backward_csr_workspace_size", "bsa_backward_csr", "bsa_backward_stats_offset",
            "bsa_status_string", "bsa_version")
 MASK_SPATIAL, MASK_TEMPORAL = 0, 1
@@ -69,7 +69,9 @@ def lib() -> ctypes.CDLL:
         I64 = ctypes.c_int64
         L.bsa_csr_entries.argtypes = [D, P, ctypes.POINTER(I64)]
         L.bsa_plan_csr.argtypes = [D, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
+        L.bsa_select_csr.argtypes = [D, P, P, P, P, I64, P, ctypes.c_size_t, P]
         L.bsa_forward_csr.argtypes = [D, P, P, P, P, P, I64, P, P, P, ctypes.c_size_t, P]
+        L.bsa_forward_csr_raster.argtypes = [D, P, P, P, P, P, P, I64, P, P, P, ctypes.c_size_t, P]
         I32 = ctypes.c_int32
         L.bsa_structured_entries.argtypes = [D, P, I32, I32, ctypes.POINTER(I64)]
         L.bsa_plan_structured.argtypes = [D, P, I32, I32, P, P, I64, P]

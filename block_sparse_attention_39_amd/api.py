@@ -249,6 +249,25 @@ def plan_csr(desc: Desc, q_tiled, k_frag, row_ptr, col_idx, workspace, keep_per_
     del arr
 
 
+def select_csr(desc: Desc, row_ptr, col_idx, workspace, keep_per_head=None, keep_rows=None, stream=None):
+    """plan_csr's row pointers and selection alone, from the tile means the
+    pooling permutes (pool / gather_pool, gather_kf_pool) left in the
+    workspace."""
+    arr, kp = _keep_heads(desc, keep_per_head)
+    _check(lib().bsa_select_csr(ctypes.byref(desc), kp, _ptr(keep_rows), _ptr(row_ptr), _ptr(col_idx),
+                                col_idx.numel(), _ptr(workspace), _ws(workspace), _stream(stream)), "bsa_select_csr")
+    del arr
+
+
+def forward_csr_raster(desc: Desc, q_raster, perm, k_frag, v_frag, row_ptr, col_idx, o_raster, lse=None,
+                       workspace=None, stream=None):
+    """forward_csr with Q read from and O written to the raster layout through
+    ``perm`` (the same values as gather, forward_csr and scatter)."""
+    _check(lib().bsa_forward_csr_raster(ctypes.byref(desc), _ptr(q_raster), _ptr(perm), _ptr(k_frag), _ptr(v_frag),
+                                        _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(o_raster), _ptr(lse),
+                                        _ptr(workspace), _ws(workspace), _stream(stream)), "bsa_forward_csr_raster")
+
+
 def forward_csr(desc: Desc, q_tiled, k_frag, v_frag, row_ptr, col_idx, o_tiled, lse=None, workspace=None,
                 stream=None):
     """bsa_forward with the kept lists in CSR form (from plan_csr)."""

@@ -483,9 +483,13 @@ bsa_status bsa_csr_entries(const bsa_desc* desc, const int32_t* keep_per_head, i
     return csr_heads(g, keep_per_head, nullptr, entries);
 }
 
-bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const int32_t* keep_per_head,
-                        const int32_t* keep_rows, int64_t* row_ptr, int32_t* col_idx, int64_t col_entries, void* ws,
-                        size_t ws_bytes, void* stream) {
+namespace {
+
+// bsa_plan_csr (pool = true: the tile means from q_tiled and k_frag first) and
+// bsa_select_csr (the means already in the workspace).
+bsa_status plan_csr_impl(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const int32_t* keep_per_head,
+                         const int32_t* keep_rows, int64_t* row_ptr, int32_t* col_idx, int64_t col_entries, void* ws,
+                         size_t ws_bytes, void* stream, bool pool) {
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
@@ -495,7 +499,7 @@ bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k
     int64_t need = 0;
     st = csr_heads(g, keep_per_head, &kh, &need);
     if (st != BSA_OK) return st;
-    if (!q_tiled || !k_frag || !row_ptr || !col_idx) return BSA_ERR_NULL;
+    if ((pool && (!q_tiled || !k_frag)) || !row_ptr || !col_idx) return BSA_ERR_NULL;
     if (col_entries < need) return BSA_ERR_SHAPE;
     if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(row_ptr, 8) || misaligned(col_idx, 4) ||
         misaligned(keep_rows, 4))
@@ -506,26 +510,48 @@ bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k
     hipStream_t s = static_cast<hipStream_t>(stream);
     const PoolPair p = pool_outs(L, ws);
     hipError_t e = bsa::launch_csr_rowptr(kh, keep_rows, (int)g.BH, (int)g.H, (int)g.nvt, row_ptr, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && pool)
         e = bsa::launch_pool(static_cast<const uint16_t*>(q_tiled), static_cast<const uint16_t*>(k_frag), p.q, p.k,
                              (int)g.BH, (int)g.npf, (int)g.nvt, (int)g.D, s, g.pad);
     if (e == hipSuccess) e = bsa::launch_select(select_args(g, L, ws, col_idx, row_ptr), (int)g.D, s);
     return launched(e);
 }
 
-bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
-                           const int64_t* row_ptr, const int32_t* col_idx, int64_t col_entries, void* o_tiled,
-                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // namespace
+
+bsa_status bsa_plan_csr(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const int32_t* keep_per_head,
+                        const int32_t* keep_rows, int64_t* row_ptr, int32_t* col_idx, int64_t col_entries, void* ws,
+                        size_t ws_bytes, void* stream) {
+    return plan_csr_impl(desc, q_tiled, k_frag, keep_per_head, keep_rows, row_ptr, col_idx, col_entries, ws, ws_bytes,
+                         stream, true);
+}
+
+bsa_status bsa_select_csr(const bsa_desc* desc, const int32_t* keep_per_head, const int32_t* keep_rows,
+                          int64_t* row_ptr, int32_t* col_idx, int64_t col_entries, void* ws, size_t ws_bytes,
+                          void* stream) {
+    return plan_csr_impl(desc, nullptr, nullptr, keep_per_head, keep_rows, row_ptr, col_idx, col_entries, ws,
+                         ws_bytes, stream, false);
+}
+
+namespace {
+
+// bsa_forward_csr and bsa_forward_csr_raster: q / o tiled, or raster through
+// perm (raster).
+bsa_status forward_csr_impl(const bsa_desc* desc, const void* q, const int32_t* perm, const void* k_frag,
+                            const void* v_frag, const int64_t* row_ptr, const int32_t* col_idx, int64_t col_entries,
+                            void* o, float* lse, void* ws, size_t ws_bytes, void* stream, bool raster) {
     Geo g;
     bsa_status st = check_desc(desc, &g);
     if (st != BSA_OK) return st;
     if (g.npt + g.nvt > BSA_MAX_TILES) return BSA_ERR_UNSUPPORTED;
     if (g.empty) return BSA_OK;
-    if (!q_tiled || !k_frag || !v_frag || !o_tiled || (g.nvt > 0 && (!row_ptr || !col_idx))) return BSA_ERR_NULL;
+    if (!q || !k_frag || !v_frag || !o || (g.nvt > 0 && (!row_ptr || !col_idx))) return BSA_ERR_NULL;
+    if (raster && g.n_video > 0 && !perm) return BSA_ERR_NULL;
     if (g.nvt > 0 && col_entries < 1) return BSA_ERR_SHAPE;
-    if (misaligned(q_tiled, 16) || misaligned(k_frag, 16) || misaligned(v_frag, 16) || misaligned(o_tiled, 16) ||
-        misaligned(row_ptr, 8) || misaligned(col_idx, 4) || misaligned(lse, 4))
+    if (misaligned(q, 16) || misaligned(k_frag, 16) || misaligned(v_frag, 16) || misaligned(o, 16) ||
+        misaligned(row_ptr, 8) || misaligned(col_idx, 4) || misaligned(lse, 4) || misaligned(perm, 4))
         return BSA_ERR_ALIGN;
+    if (raster && g.npf + g.n_ras > INT32_MAX / 2) return BSA_ERR_UNSUPPORTED;
     int* progress = nullptr;
     if (ws) {
         const Layout L = layout(g);
@@ -533,15 +559,15 @@ bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
-    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false)) return BSA_ERR_ARG;
+    if (forward_io_overlap(g, q, k_frag, v_frag, o, raster)) return BSA_ERR_ARG;
     bsa::ForwardArgs a{};
-    a.q = static_cast<const uint16_t*>(q_tiled);
+    a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k_frag);
     a.v = static_cast<const uint16_t*>(v_frag);
     a.idx = col_idx;
     a.row_ptr = g.nvt > 0 ? row_ptr : nullptr;
     a.col_entries = col_entries;
-    a.o = static_cast<uint16_t*>(o_tiled);
+    a.o = static_cast<uint16_t*>(o);
     a.lse = lse;
     a.BH = (int)g.BH;
     a.npt = (int)g.npt;
@@ -549,7 +575,30 @@ bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void
     a.keep = 1;
     a.pad = g.pad;
     a.scale_log2 = desc->scale * 1.4426950408889634f;
+    if (raster) {
+        a.raster = true;
+        a.perm = perm;
+        a.n_ras = g.npf + g.n_ras;
+        a.H = (int)g.H;
+    }
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+bsa_status bsa_forward_csr(const bsa_desc* desc, const void* q_tiled, const void* k_frag, const void* v_frag,
+                           const int64_t* row_ptr, const int32_t* col_idx, int64_t col_entries, void* o_tiled,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
+    return forward_csr_impl(desc, q_tiled, nullptr, k_frag, v_frag, row_ptr, col_idx, col_entries, o_tiled, lse, ws,
+                            ws_bytes, stream, false);
+}
+
+bsa_status bsa_forward_csr_raster(const bsa_desc* desc, const void* q_raster, const int32_t* perm,
+                                  const void* k_frag, const void* v_frag, const int64_t* row_ptr,
+                                  const int32_t* col_idx, int64_t col_entries, void* o_raster, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    return forward_csr_impl(desc, q_raster, perm, k_frag, v_frag, row_ptr, col_idx, col_entries, o_raster, lse, ws,
+                            ws_bytes, stream, true);
 }
 
 // ---- structured lists (spatial / temporal heads) ------------------------------

@@ -342,10 +342,29 @@ bsa_status bsa_csr_entries(const bsa_desc *desc, const int32_t *keep_per_head, i
 bsa_status bsa_plan_csr(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
                         const int32_t *keep_per_head, const int32_t *keep_rows, int64_t *row_ptr,
                         int32_t *col_idx, int64_t col_entries, void *ws, size_t ws_bytes, void *stream);
+/*
+ * The row pointers, scoring and top-k of bsa_plan_csr alone, from the tile
+ * means that bsa_permute(POOL or GATHER_POOL) and bsa_permute(GATHER_KF_POOL)
+ * (or an earlier plan) left in the workspace: the CSR counterpart of
+ * bsa_select.  Same output and errors as bsa_plan_csr.
+ */
+bsa_status bsa_select_csr(const bsa_desc *desc, const int32_t *keep_per_head, const int32_t *keep_rows,
+                          int64_t *row_ptr, int32_t *col_idx, int64_t col_entries, void *ws, size_t ws_bytes,
+                          void *stream);
 bsa_status bsa_forward_csr(const bsa_desc *desc, const void *q_tiled, const void *k_frag,
                            const void *v_frag, const int64_t *row_ptr, const int32_t *col_idx,
                            int64_t col_entries, void *o_tiled, float *lse, void *ws, size_t ws_bytes,
                            void *stream);
+/*
+ * bsa_forward_csr with Q read from, and O written to, the raster layout
+ * through `perm`, as bsa_forward_raster does for fixed keep: the same result
+ * bit for bit as GATHER -> bsa_forward_csr -> SCATTER, without the tiled
+ * copies.  Arguments and errors as bsa_forward_csr and bsa_forward_raster.
+ */
+bsa_status bsa_forward_csr_raster(const bsa_desc *desc, const void *q_raster, const int32_t *perm,
+                                  const void *k_frag, const void *v_frag, const int64_t *row_ptr,
+                                  const int32_t *col_idx, int64_t col_entries, void *o_raster, float *lse,
+                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Structured lists: kept tiles from a fixed spatial or temporal rule per head
@@ -453,7 +472,7 @@ const char *bsa_status_string(bsa_status status);
 /* ABI version of this header (major * 100 + minor). */
 int bsa_version(void);
 
-#define BSA_VERSION 1002
+#define BSA_VERSION 1003
 
 #ifdef __cplusplus
 }

@@ -418,3 +418,32 @@ def test_keep_from_sparsity():
     assert bsa.keep_for_call(0.75, 1920, 122880) == 480
     assert bsa.keep_for_call(0.75, 192, 12288) == 48          # at the minimum: sparse
     assert bsa.keep_for_call(0.75, 192, 12288, dense_below=0) == 48
+
+
+def test_csr_select_and_raster_forward_host_checks():
+    """bsa_select_csr (the CSR selection from the means in the workspace) and
+    bsa_forward_csr_raster reject bad arguments on the host."""
+    L = lib()
+    d = cfg()
+    st, need = ws_size(d)
+    n_entries = ctypes.c_int64()
+    assert L.bsa_csr_entries(ctypes.byref(d), None, ctypes.byref(n_entries)) == OK
+    E = n_entries.value
+    S_ = L.bsa_select_csr
+    assert S_(ctypes.byref(d), None, None, None, FAKE, E, FAKE, need, None) == NULL        # row_ptr
+    assert S_(ctypes.byref(d), None, None, FAKE, None, E, FAKE, need, None) == NULL        # col_idx
+    assert S_(ctypes.byref(d), None, None, FAKE, FAKE, E - 1, FAKE, need, None) == SHAPE   # too few entries
+    assert S_(ctypes.byref(d), None, None, FAKE, FAKE, E, None, 0, None) == WS
+    assert S_(ctypes.byref(d), None, None, FAKE, FAKE, E, FAKE, need - 1, None) == WS
+    assert S_(ctypes.byref(d), None, None, FAKE + 4, FAKE, E, FAKE, need, None) == ALIGN
+    F = L.bsa_forward_csr_raster
+    # q, perm, k, v, row_ptr, col_idx
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert F(ctypes.byref(d), *args, E, FAKE, None, None, 0, None) == NULL, i
+    assert F(ctypes.byref(d), *([FAKE] * 6), E, None, None, None, 0, None) == NULL        # o
+    assert F(ctypes.byref(d), *([FAKE] * 6), 0, FAKE, None, None, 0, None) == SHAPE       # no entries
+    assert F(ctypes.byref(d), FAKE, FAKE + 2, *([FAKE] * 4), E, FAKE, None, None, 0, None) == ALIGN
+    assert F(ctypes.byref(d), *([FAKE] * 6), E, FAKE, None, FAKE, need - 1, None) == WS
+    assert F(ctypes.byref(d), *([FAKE] * 6), E, FAKE, None, None, 0, None) == ARG         # o on q

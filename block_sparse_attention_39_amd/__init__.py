@@ -10,7 +10,7 @@ from ._lib import (EXPORTS, LIB_PATH, MASK_SPATIAL, MASK_TEMPORAL, MAX_CSR_HEADS
                    PERM_GATHER, PERM_GATHER_KF, PERM_GATHER_KF_POOL, PERM_GATHER_POOL, PERM_GATHER_VF, PERM_POOL,
                    PERM_SCATTER, PERM_TILED_TO_KF, PERM_TILED_TO_VF, TILE_DYNAMIC, TILE_STATIC, TILE_STATIC_PADDED, BsaError, Desc,
                    lib)
-from .api import (DENSE_BELOW_TOKENS, BlockSparseAttention, backward, backward_csr, backward_csr_workspace_size, backward_stats,
+from .api import (DENSE_BELOW_TOKENS, BlockSparseAttention, attention, backward, backward_csr, backward_csr_workspace_size, backward_stats,
                   backward_stats_offset, backward_workspace_size,
                   csr_entries, forward, forward_csr, forward_csr_raster, forward_noalloc, forward_raster, forward_stats, forward_stats_offset, gather, gather_kf,
                   gather_kf_pool, gather_pool, gather_vf, keep_for_call, keep_tiles_for, make_desc, permute_build, plan, plan_csr, plan_structured,
@@ -19,7 +19,7 @@ from .api import (DENSE_BELOW_TOKENS, BlockSparseAttention, backward, backward_c
 
 lib()  # fail at import if the HIP library was not built
 
-__all__ = ["DENSE_BELOW_TOKENS", "keep_for_call", "keep_tiles_for", "BlockSparseAttention", "BsaError", "Desc", "EXPORTS", "LIB_PATH", "MAX_CSR_HEADS", "MAX_VIDEO_TILES",
+__all__ = ["attention", "DENSE_BELOW_TOKENS", "keep_for_call", "keep_tiles_for", "BlockSparseAttention", "BsaError", "Desc", "EXPORTS", "LIB_PATH", "MAX_CSR_HEADS", "MAX_VIDEO_TILES",
            "backward", "backward_csr", "backward_csr_workspace_size", "backward_stats", "backward_stats_offset",
            "backward_workspace_size", "csr_entries",
            "forward", "forward_csr", "forward_csr_raster", "forward_noalloc", "forward_raster", "forward_stats", "forward_stats_offset", "plan_csr", "plan_structured",

@@ -469,6 +469,12 @@ class BlockSparseAttention:
         forward(self.desc, self.q_t, self.k_f, self.v_f, self.block_idx, self.o_t, self.lse,
                 self.workspace if self.grouped else None, stream)
 
+    def backward_workspace(self):
+        """The bsa_backward workspace for this problem size (allocated on first use)."""
+        if getattr(self, "_bwd_ws", None) is None:
+            self._bwd_ws = torch.empty(backward_workspace_size(self.desc), dtype=torch.uint8, device=self.device)
+        return self._bwd_ws
+
     def forward_raster(self, q, out, stream=None):
         """The forward from raster Q straight into raster ``out``."""
         forward_raster(self.desc, q, self.perm, self.k_f, self.v_f, self.block_idx, out, self.lse,
@@ -491,3 +497,40 @@ class BlockSparseAttention:
         self.forward(stream)
         self.scatter_out(out, stream)
         return out
+
+
+class _Attention(torch.autograd.Function):
+    """The op as a differentiable torch function: forward through the raster
+    path of a BlockSparseAttention, backward through bsa_backward with the
+    forward's own permutation, kept lists and lse (the selection is held
+    fixed: the gradient is that of exact attention over the kept tiles)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, att):
+        out = torch.empty_like(q)
+        att(q, k, v, out)
+        # this call's permutation, lists and lse: the next call through the
+        # same object overwrites its buffers
+        ctx.save_for_backward(q, k, v, out, att.perm.clone(), att.block_idx.clone(), att.lse.clone())
+        ctx.att = att
+        return out
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, out, perm, block_idx, lse = ctx.saved_tensors
+        att = ctx.att
+        d_o = d_o.to(torch.bfloat16).contiguous()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        backward(att.desc, q, k, v, out, d_o, lse, perm, block_idx, dq, dk, dv, att.backward_workspace())
+        return dq, dk, dv, None
+
+
+def attention(q, k, v, att: "BlockSparseAttention"):
+    """Block-sparse attention of raster bf16 ``q, k, v`` ``[B, Ntot, H, D]`` (on
+    the GPU, contiguous) as a differentiable operation: returns the raster
+    output; its gradient runs bsa_backward with this call's own selection.
+    ``att`` owns the buffers for ``q``'s size (``BlockSparseAttention(desc)``);
+    one object can serve several calls (layers), each saving its lists."""
+    if att.lse is None:
+        att.lse = torch.empty((att.desc.batch, att.desc.heads, att.n_tot), dtype=torch.float32, device=q.device)
+    return _Attention.apply(q, k, v, att)

@@ -99,3 +99,35 @@ def test_backward_stats_count_rounds():
           flush=True)
     assert dq_rounds == tiles and kv_rounds == tiles
     assert dq_gave_up == 0 and kv_gave_up == 0
+
+
+def test_autograd_attention_matches_direct_calls():
+    """bsa.attention as a torch autograd function: its output and the
+    gradients that loss.backward() produces equal the raster forward and
+    bsa_backward called directly, bit for bit; two calls through one
+    BlockSparseAttention before either backward each keep their own
+    selection and lse."""
+    wl = W("autograd", 1, 2, 128, (8, 8, 16), 4, seed=91, n_prefix=64)
+    desc = bsa.make_desc(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.keep_tiles, scale=wl.scale,
+                         n_prefix=wl.n_prefix)
+    att = bsa.BlockSparseAttention(desc)
+    inputs = []
+    for seed in (91, 92):
+        wk = W("autograd", 1, 2, 128, (8, 8, 16), 4, seed=seed, n_prefix=64)
+        q, k, v = S.qkv(wk)
+        inputs.append(([to_dev(x).requires_grad_() for x in (q, k, v)], to_dev(S.tensor(wk, "do"))))
+    outs = [bsa.attention(*qkv, att) for qkv, _ in inputs]
+    for out, (_, do) in zip(outs, inputs):
+        (out.float() * do.float()).sum().backward()
+    torch.cuda.synchronize()
+    ws = torch.empty(bsa.backward_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    for out, (qkv, do) in zip(outs, inputs):
+        q, k, v = (x.detach() for x in qkv)
+        ref = bsa.BlockSparseAttention(desc, with_lse=True)
+        o2 = ref(q, k, v)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        bsa.backward(desc, q, k, v, o2, do, ref.lse, ref.perm, ref.block_idx, dq, dk, dv, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(out.detach()), to_bits(o2))
+        for got, want in zip((x.grad for x in qkv), (dq, dk, dv)):
+            assert np.array_equal(to_bits(got), to_bits(want))

@@ -5,7 +5,8 @@ tiles (padded mode), with or without a dense prefix, one or two batch
 elements and up to three heads, keep from 1 to every tile.  The rules are
 those of the other parity tests: permutation, gathers, means and scatter
 bit-exact, lists exact outside near ties, attention and gradients within the
-forward's and the backward's tolerances."""
+forward's and the backward's tolerances; the raster-I/O path (Q's means
+alone, bsa_forward_raster) equal to the tiled one bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -78,6 +79,15 @@ def test_random_problem(seed):
             check_lse(lse[b, h].reshape(nqt, 64)[rows], ref_lse[rows], qt[b, h].reshape(nqt, 64, D)[rows],
                       kt[b, h], scale, f"lse b{b} h{h}")
     assert np.array_equal(to_bits(g.out), oracle.scatter_padded(o_t, p1, npf, wl.n_video))
+    # the raster-I/O path: the same means, lists, output and lse bit for bit
+    ra = bsa.BlockSparseAttention(g.desc, with_lse=True)
+    rout = torch.full_like(g.q.view(torch.int16), 0x7FC1).view(torch.bfloat16)
+    ra(g.q, g.k, g.v, rout)
+    torch.cuda.synchronize()
+    rq, rk = bsa.pooled_views(g.desc, ra.workspace)
+    assert np.array_equal(rq.cpu().numpy(), gq) and np.array_equal(rk.cpu().numpy(), gk)
+    assert torch.equal(ra.block_idx, g.att.block_idx)
+    assert torch.equal(rout.view(torch.int16), g.out.view(torch.int16)) and torch.equal(ra.lse, g.att.lse)
     # gradients
     dq, dk, dv = (torch.empty_like(g.q) for _ in range(3))
     ws = torch.empty(max(bsa.backward_workspace_size(g.desc), 256), dtype=torch.uint8, device="cuda")

@@ -70,7 +70,9 @@ __device__ inline int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 
 __device__ inline int64_t raster_token(const BackwardArgs& a, int b, int64_t row) {
     if (row < a.npf) return row;
     const int32_t v = a.perm[(int64_t)b * (a.n_tot - a.npf) + (row - a.npf)];
-    return v < 0 ? -1 : a.npf + v;
+    // a value past the raster rows is clamped into them (a corrupt perm cannot
+    // address outside the gradients)
+    return v < 0 ? -1 : a.npf + min((int64_t)v, a.n_ras - a.npf - 1);
 }
 
 // one (batch, head) row of D bf16 channels, raster layout

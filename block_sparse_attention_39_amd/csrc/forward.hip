@@ -230,7 +230,9 @@ __device__ inline int raster_row(const ForwardArgs& a, const Item& it, int tok) 
     const int p = it.qt * kTile + tok, np = a.npt * kTile;
     if (p < np) return p;
     const int v = a.perm[(it.bh / a.H) * ((int64_t)a.nvt * kTile) + (p - np)];
-    return v < 0 ? -1 : np + v;
+    // a value past the raster rows is clamped into them (a corrupt perm cannot
+    // address outside Q or O)
+    return v < 0 ? -1 : np + min(v, (int)(a.n_ras - np) - 1);
 }
 
 // Issue the loads a query tile starts with: this wave's K and V fragments of

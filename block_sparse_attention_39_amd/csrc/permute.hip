@@ -48,12 +48,17 @@ __device__ inline uint4 zero_if_padding(uint4 x, int64_t t) {
 template <bool kPad>
 __device__ inline int64_t row_or_zero(int64_t t) { return kPad ? max(t, (int64_t)0) : t; }
 
-// raster token of tiled slot p (prefix first), or -1 for a padding slot
+// Raster row (prefix first) of tiled slot p, or -1 for a padding slot (kPad:
+// a ragged grid).  A video value outside the raster's n_ras - n_prefix rows
+// is clamped into them (below 0 to row 0 without padding), so that a corrupt
+// perm cannot address outside the tensors.
+template <bool kPad>
 __device__ inline int64_t slot_token(const int32_t* __restrict__ perm, int b, int64_t n_video, int n_prefix,
-                                     int64_t p) {
+                                     int64_t n_ras, int64_t p) {
     if (p < n_prefix) return p;
     const int32_t v = perm[(int64_t)b * n_video + (p - n_prefix)];
-    return v < 0 ? -1 : n_prefix + v;
+    if (kPad && v < 0) return -1;
+    return n_prefix + min(max((int64_t)v, (int64_t)0), n_ras - n_prefix - 1);
 }
 
 // One block per (batch, 64-token tile of the tiled order); 256 threads.
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
     __shared__ int64_t tok[kTile];
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
     __syncthreads();
     const int items = kTile * H * C;
 #pragma unroll 4
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256) void gather_kf_kernel(const uint4* __restrict_
     const int64_t p0 = tile * kTile;
     const int64_t n_tiles = n_tot / kTile;
     if (threadIdx.x < kTile)
-        tok[threadIdx.x] = kTiled ? p0 + threadIdx.x : slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        tok[threadIdx.x] = kTiled ? p0 + threadIdx.x : slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
     __syncthreads();
     const int SD = C / 2;
     const int per_head = kTile * C;
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256) void gather_vf_kernel(const uint4* __restrict_
     const int64_t p0 = tile * kTile;
     const int64_t n_tiles = n_tot / kTile;
     if (threadIdx.x < kTile)
-        tok[threadIdx.x] = kTiled ? p0 + threadIdx.x : slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        tok[threadIdx.x] = kTiled ? p0 + threadIdx.x : slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
     __syncthreads();
     const int OD = C / 4;  // 32-channel blocks
     const int items = H * 8 * C;
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(256) void gather_kf_tiled_kernel(const uint4* __res
     __shared__ uint4 stage[4][32 * 16];  // per wave: 32 tokens x up to 16 chunks
     const int b = blockIdx.y;
     const int64_t tile = blockIdx.x, p0 = tile * kTile, n_tiles = n_tot / kTile;
-    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kh = wave & 1;
     const int SD = C / 2, tpi = 64 / C;  // tpi: tokens per wave load
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(256) void gather_kf_vf_kernel(const uint4* __restri
     __shared__ uint4 stage[4][512];  // per wave: 32 tokens x 16 chunks, or 64 x 8
     const int b = blockIdx.y;
     const int64_t tile = blockIdx.x, p0 = tile * kTile, n_tiles = n_tot / kTile;
-    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+    if (threadIdx.x < kTile) tok[threadIdx.x] = slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int OD = C / 4, SD = C / 2;
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(const uint4* __restric
     const int b = blockIdx.y;
     const int64_t p0 = (int64_t)blockIdx.x * kTile;
     if (threadIdx.x < kTile) {
-        const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        const int64_t t = slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
         tok[threadIdx.x] = t;
         const int nr = __popcll(__ballot(t >= 0));
         if (threadIdx.x == 0) real = nr;
@@ -461,7 +466,7 @@ __global__ __launch_bounds__(256) void gather_kf_pool_kernel(const uint4* __rest
     const int b = blockIdx.y;
     const int64_t tile = blockIdx.x, p0 = tile * kTile;
     if (threadIdx.x < kTile) {
-        const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        const int64_t t = slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
         tok[threadIdx.x] = t;
         const int nr = __popcll(__ballot(t >= 0));
         if (threadIdx.x == 0) real = nr;
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(1024) void pool_raster_kernel(const uint4* __restri
     const int b = blockIdx.y;
     const int64_t vt = blockIdx.x, p0 = n_prefix + vt * kTile;
     if (threadIdx.x < kTile) {
-        const int64_t t = slot_token(perm, b, n_video, n_prefix, p0 + threadIdx.x);
+        const int64_t t = slot_token<kPad>(perm, b, n_video, n_prefix, n_ras, p0 + threadIdx.x);
         tok[threadIdx.x] = t;
         const int nr = __popcll(__ballot(t >= 0));
         if (threadIdx.x == 0) real = nr;

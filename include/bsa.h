@@ -54,7 +54,12 @@
  *                                   layout, same size; every 1 KB of them is one
  *                                   wave-wide 16-byte-per-lane load.)
  *   perm    int32 [B][Nvideo]      tiled video slot -> raster video token index
- *                                   (0-based, not counting the prefix).
+ *                                   (0-based, not counting the prefix).  The
+ *                                   kernels clamp a value past the raster's
+ *                                   video rows into them (and, without padding,
+ *                                   a negative one to 0), so a corrupt perm
+ *                                   gives wrong rows but no access outside the
+ *                                   tensors.
  *   block_idx int32 [B][H][nVT][k] per video query tile, the k kept video key tiles
  *                                   (video tile numbers 0..nVT-1), ascending.
  * Ntot = n_prefix + Nvideo, Nvideo = grid_t*grid_h*grid_w, nVT = Nvideo/64.

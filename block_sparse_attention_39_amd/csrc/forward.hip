@@ -229,10 +229,19 @@ __device__ inline int list_tile(const ForwardArgs& a, const Item& it, int j, int
 __device__ inline int raster_row(const ForwardArgs& a, const Item& it, int tok) {
     const int p = it.qt * kTile + tok, np = a.npt * kTile;
     if (p < np) return p;
-    const int v = a.perm[(it.bh / a.H) * ((int64_t)a.nvt * kTile) + (p - np)];
+    const int v = a.perm[(int64_t)((int)it.bh / a.H) * (a.nvt * kTile) + (p - np)];
     // a value past the raster rows is clamped into them (a corrupt perm cannot
     // address outside Q or O)
     return v < 0 ? -1 : np + min(v, (int)(a.n_ras - np) - 1);
+}
+
+// Raster Q and O: offset of (batch, head) bh's token row 0, in elements;
+// token row r of that head sits r * H * D further on.  bh < 2^31 (the
+// descriptor checks bound B * H * tiles), so the split is 32-bit.
+template <int D>
+__device__ inline int64_t raster_head(const ForwardArgs& a, int64_t bh) {
+    const int b = (int)bh / a.H, h = (int)bh - b * a.H;
+    return ((int64_t)b * a.n_ras * a.H + h) * D;
 }
 
 // Issue the loads a query tile starts with: this wave's K and V fragments of
@@ -259,8 +268,7 @@ __device__ __attribute__((always_inline)) inline void fetch_first(const ForwardA
     if constexpr (kRas) {
         // token row r of this (batch, head) at qh + r * H * D; a padding
         // slot loads row 0 and is zeroed
-        const int64_t b = it.bh / a.H, h = it.bh % a.H;
-        const uint16_t* qh = a.q + (b * a.n_ras * a.H + h) * D;
+        const uint16_t* qh = a.q + raster_head<D>(a, it.bh);
 #pragma unroll
         for (int u = 0; u < Regs<D>::QPT; ++u) {
             const int f = w.tid + 256 * u;
@@ -585,7 +593,7 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
         constexpr int C = D / 8;
         uint16_t* orow = a.o + (bh * n_tot + (int64_t)qt * kTile) * D;
         // raster O: token row r of this (batch, head) at oh + r * H * D
-        uint16_t* oh = kRas ? a.o + ((bh / a.H) * a.n_ras * a.H + bh % a.H) * D : nullptr;
+        uint16_t* oh = kRas ? a.o + raster_head<D>(a, bh) : nullptr;
         const int* rows = (const int*)(lds + CF::ROWS);
 #pragma unroll
         for (int u = 0; u < kTile * C / 256; ++u) {

@@ -216,7 +216,7 @@ const char* bsa_status_string(bsa_status s) {
         case BSA_ERR_ALIGN: return "a tensor pointer is not suitably aligned";
         case BSA_ERR_WORKSPACE: return "workspace missing or too small";
         case BSA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
-        case BSA_ERR_ARG: return "invalid argument (enum value, scale or tau)";
+        case BSA_ERR_ARG: return "invalid argument (enum value, scale, tau or radius; or an output overlapping an input)";
     }
     return "unknown status";
 }

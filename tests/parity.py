@@ -53,7 +53,7 @@ def desc_for(wl: S.Workload):
                          n_prefix=wl.n_prefix, dynamic=wl.dynamic, tile=wl.tile, tau=wl.tau, padded=wl.padded)
 
 
-class GpuRun:
+class DeviceRun:
     """The whole path on the GPU, every intermediate kept for inspection."""
 
     def __init__(self, wl: S.Workload, q, k, v, with_lse=True):

@@ -12,7 +12,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, attending_tiles, bits_to_f64, check_lse, oracle_lse_delta_rows, to_bits, to_dev
+from parity import DeviceRun, attending_tiles, bits_to_f64, check_lse, oracle_lse_delta_rows, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_backward_csr_matches_oracle(wl, keep_h, rows_range):
     print(f"\n[case] {wl} keep_per_head={keep_h} rows={rows_range}", flush=True)
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     n = wl.n_video_tiles
     keep_rows = None
     if rows_range is not None:
@@ -84,7 +84,7 @@ def test_backward_structured_matches_oracle():
     print(f"\n[case] {wl} spatial/temporal radius 1/1", flush=True)
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     mask = [bsa.MASK_SPATIAL, bsa.MASK_TEMPORAL]
     n_ent = bsa.structured_entries(g.desc, mask, 1, 1)
     row_ptr = torch.empty(wl.batch * wl.heads * wl.n_video_tiles + 1, dtype=torch.int64, device="cuda")
@@ -103,7 +103,7 @@ def test_uniform_csr_backward_equals_fixed_keep():
     wl = W("bcsr_uniform", 2, 2, 128, (8, 8, 16), 5, seed=65, n_prefix=64)
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     n = wl.n_video_tiles
     idx = g.att.block_idx[:, :, :n, :wl.keep_tiles].contiguous()
     row_ptr = (torch.arange(wl.batch * wl.heads * n + 1, dtype=torch.int64) * wl.keep_tiles).cuda()
@@ -127,7 +127,7 @@ def test_prism720p_backward_csr_sampled():
     print(f"\n[case] {wl} keep_per_head={keep_h}", flush=True)
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     a, d = g.att, g.desc
     n = wl.n_video_tiles
     row_ptr = torch.empty(wl.batch * wl.heads * n + 1, dtype=torch.int64, device="cuda")

@@ -17,7 +17,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, check_lse, check_output, check_selection, to_bits
+from parity import DeviceRun, check_lse, check_output, check_selection, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,7 @@ CASES = [
 ]
 
 
-def run_csr(g: GpuRun, keep_h, keep_rows_dev):
+def run_csr(g: DeviceRun, keep_h, keep_rows_dev):
     a, d = g.att, g.desc
     wl = g.wl
     rows = wl.batch * wl.heads * wl.n_video_tiles
@@ -48,7 +48,7 @@ def run_csr(g: GpuRun, keep_h, keep_rows_dev):
 def test_csr_matches_oracle(wl, keep_h, rows_range):
     print(f"\n[case] {wl} keep_per_head={keep_h} rows={rows_range}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     n = wl.n_video_tiles
     keep_rows = None
     if rows_range is not None:
@@ -92,7 +92,7 @@ def test_csr_matches_oracle(wl, keep_h, rows_range):
 def test_uniform_csr_equals_fixed_keep():
     wl = W("csr_uniform", 2, 3, 128, (8, 8, 16), 5, seed=25, n_prefix=64)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     row_ptr, col, o, lse = run_csr(g, [wl.keep_tiles] * wl.heads, None)
     fixed = g.att.block_idx.cpu().numpy()[:, :, :wl.n_video_tiles, :wl.keep_tiles]
     assert np.array_equal(col, fixed.reshape(-1))
@@ -109,7 +109,7 @@ def test_csr_argument_checks():
     with pytest.raises(bsa.BsaError):
         bsa.csr_entries(d, [2, wl.n_video_tiles + 1])
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     row_ptr = torch.zeros(wl.n_video_tiles * 2 + 1, dtype=torch.int64, device="cuda")
     small = torch.zeros(3, dtype=torch.int32, device="cuda")
     with pytest.raises(bsa.BsaError):  # column array below bsa_csr_entries
@@ -124,7 +124,7 @@ def test_prism720p_csr_sampled():
     keep_h = [(480, 192, 120, 96)[h % 4] for h in range(wl.heads)]
     print(f"\n[case] {wl} keep_per_head={keep_h}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     row_ptr, col, o, lse = run_csr(g, keep_h, None)
     n = wl.n_video_tiles
     lens = np.repeat(np.tile(np.array(keep_h, np.int64), wl.batch), n)

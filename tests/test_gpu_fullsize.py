@@ -21,7 +21,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, bits_to_f64, check_lse, gamma, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
+from parity import DeviceRun, bits_to_f64, check_lse, gamma, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def check_against_rounded(got, ref, qt, kt, vt, npf, idx, tiles, scale, what):
     assert rerr.mean() < 0.5 * rnd.mean(), what
 
 
-def check_sampled(g: GpuRun, q, k, v, perm, keep=None, sample_bh=SAMPLE_BH, vs_rounded=False):
+def check_sampled(g: DeviceRun, q, k, v, perm, keep=None, sample_bh=SAMPLE_BH, vs_rounded=False):
     """vs_rounded: also compare with the oracle's output rounded to bf16."""
     wl = g.wl
     keep = keep or wl.keep_tiles
@@ -135,7 +135,7 @@ def check_sampled(g: GpuRun, q, k, v, perm, keep=None, sample_bh=SAMPLE_BH, vs_r
         assert np.array_equal(to_bits(out[b, :, h]), sc[0, :, 0])
 
 
-def assert_raster_io_equals_tiled(g: GpuRun):
+def assert_raster_io_equals_tiled(g: DeviceRun):
     """The raster-I/O path on g's inputs (bsa_permute(POOL), the pooling K
     gather, the V gather beside the selection, bsa_forward_raster; grouped
     launch): Q's means, every kept list, the whole raster output and the lse
@@ -161,7 +161,7 @@ def prism():
     wl = S.WORKLOADS["prism720p"]
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     yield wl, q, k, v, g
     del g
     torch.cuda.empty_cache()
@@ -213,7 +213,7 @@ def test_prism720p_keep_sweep_sampled(prism, keep):
     wl, q, k, v, _ = prism
     wk = wl.with_keep(keep)
     print(f"\n[case] {wk}", flush=True)
-    g = GpuRun(wk, q, k, v).run()
+    g = DeviceRun(wk, q, k, v).run()
     perm = np.ascontiguousarray(np.broadcast_to(oracle.perm_static(wl.grid), (wl.batch, wl.n_video)))
     check_sampled(g, q, k, v, perm, sample_bh=[(1, 5)])
     del g
@@ -224,7 +224,7 @@ def test_prefix_sampled():
     wl = S.WORKLOADS["prefix"]
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     perm = np.ascontiguousarray(np.broadcast_to(oracle.perm_static(wl.grid), (wl.batch, wl.n_video)))
     assert np.array_equal(g.perm(), perm)
     check_sampled(g, q, k, v, perm, sample_bh=[(0, 0), (0, 17)])
@@ -237,7 +237,7 @@ def test_dynamic_sampled():
     wl = S.WORKLOADS["prism720p_dynamic"]
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     st = oracle.shape_stats(q, wl.n_prefix, wl.grid)
     shape_o, near = oracle.shape_choose(st, wl.grid, float(np.float32(wl.tau)))
     gs = g.shape_map()

@@ -18,7 +18,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import (GpuRun, attending_tiles, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout,
+from parity import (DeviceRun, attending_tiles, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout,
                     oracle_lse_delta_rows, to_bits, to_dev,
                     vfrag_layout)
 
@@ -76,7 +76,7 @@ def check_padded_path(wl, g, q, k, v, qtiles=None, bh=None):
 def test_padded_path_matches_oracle(wl):
     print(f"\n[case] {wl} slots {wl.n_video_slots} tiles {wl.n_video_tiles}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     perm, worst = check_padded_path(wl, g, q, k, v)
     # scatter: the real rows back to raster order, padding slots dropped
     ref_out = oracle.scatter_padded(to_bits(g.att.o_t), perm, wl.n_prefix, wl.n_video)
@@ -87,8 +87,8 @@ def test_padded_path_matches_oracle(wl):
 def test_padded_mode_on_divisible_grid_is_static_path():
     base = W("pad_div", 2, 2, 128, (8, 8, 12), 5, seed=47, n_prefix=64)
     q, k, v = S.qkv(base)
-    g1 = GpuRun(base, q, k, v).run()
-    g2 = GpuRun(W("pad_div", 2, 2, 128, (8, 8, 12), 5, seed=47, n_prefix=64, padded=True), q, k, v).run()
+    g1 = DeviceRun(base, q, k, v).run()
+    g2 = DeviceRun(W("pad_div", 2, 2, 128, (8, 8, 12), 5, seed=47, n_prefix=64, padded=True), q, k, v).run()
     assert np.array_equal(g1.perm(), g2.perm())
     assert np.array_equal(g1.block_idx(), g2.block_idx())
     assert np.array_equal(to_bits(g1.out), to_bits(g2.out))
@@ -103,7 +103,7 @@ def test_prism720p_ragged_sampled():
     wl = S.WORKLOADS["prism720p_ragged"]
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     nqt = wl.n_tiled_tokens // 64
     rng = np.random.default_rng(91)
     # tiles of the last t-layer and last h-row are boundary tiles (31 = 7*4 + 3, 45 = 11*4 + 1)
@@ -147,7 +147,7 @@ def check_grad(got, ref, what):
 def run_padded_backward(wl):
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     dq, dk, dv = (torch.empty_like(g.q) for _ in range(3))
     ws = torch.empty(max(bsa.backward_workspace_size(g.desc), 256), dtype=torch.uint8, device="cuda")
     bsa.backward(g.desc, g.q, g.k, g.v, g.out, to_dev(do), g.att.lse, g.att.perm, g.att.block_idx, dq, dk, dv, ws)
@@ -228,7 +228,7 @@ def test_padded_csr_and_structured_lists():
     wl = W("pad_csr", 1, 2, 128, (7, 9, 10), 5, seed=48, n_prefix=64, padded=True)
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     a, d = g.att, g.desc
     npf, scale, D = wl.n_prefix, float(np.float32(wl.scale)), wl.head_dim
     p1 = oracle.perm_static_padded(wl.grid, wl.tile)

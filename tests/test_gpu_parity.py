@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synthetic as S
-from parity import GpuRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
+from parity import DeviceRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, vfrag_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def reference_perm(wl, q, g):
 def test_path_matches_oracle(wl):
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     npf, scale = wl.n_prefix, float(np.float32(wl.scale))
 
     # permutation
@@ -99,7 +99,7 @@ def test_path_matches_oracle(wl):
 def test_outputs_are_deterministic():
     wl = W("det", 2, 2, 128, (8, 8, 16), 5, seed=31, n_prefix=64)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     first = (to_bits(g.out).copy(), g.block_idx().copy())
     g.run()
     assert np.array_equal(first[0], to_bits(g.out))
@@ -126,7 +126,7 @@ def test_planted_selection_and_ties_on_gpu():
     kr[0, perm] = kt[0].transpose(1, 0, 2)
     q, k = S.to_bf16_bits(qr), S.to_bf16_bits(kr)
     v = S.to_bf16_bits(np.ones_like(qr))
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     idx = g.block_idx()
     assert np.all(idx[0, 0] == np.arange(n - 5, n))
     assert np.all(idx[0, 1] == np.arange(5))
@@ -142,7 +142,7 @@ def test_large_logits_stay_finite():
     qf = S.bf16_bits_to_f32(q) * 6.0
     kf = S.bf16_bits_to_f32(k) * 6.0
     q, k = S.to_bf16_bits(qf), S.to_bf16_bits(kf)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     perm = oracle.perm_static(wl.grid)
     qt, kt, vt = (oracle.gather(x, perm, 0) for x in (q, k, v))
     ref, _ = oracle.attention(qt[0, 0], kt[0, 0], vt[0, 0], 0, g.block_idx()[0, 0], float(np.float32(wl.scale)),
@@ -159,7 +159,7 @@ def test_grouped_and_plain_launch_agree(wl):
     in which query tiles are scheduled: outputs are bit-identical to one block
     per query tile."""
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     grouped = to_bits(g.att.o_t).copy(), g.att.lse.cpu().numpy().copy()
     g.att.grouped = False
     g.run()
@@ -188,7 +188,7 @@ def test_rescale_path_with_steep_logits(growing):
         r[0, perm] = x[0].transpose(1, 0, 2)
         return S.to_bf16_bits(r)
     q, k, v = raster(qt), raster(kt), raster(vt)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     idx = g.block_idx()
     assert np.all(idx == np.arange(n))  # k = n: every tile kept
     qg, kg, vg = (oracle.gather(x, perm, 0) for x in (q, k, v))
@@ -208,7 +208,7 @@ def test_overlapped_call_equals_sequential_steps():
     call (the side stream's work is ordered before the forward each time)."""
     wl = W("overlap", 2, 3, 128, (8, 16, 16), 6, seed=33, n_prefix=64)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     ref = to_bits(g.out).copy()
     for it in range(3):
         out = g.att(g.q, g.k, g.v)

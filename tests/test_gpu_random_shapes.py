@@ -14,7 +14,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import (GpuRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, to_dev,
+from parity import (DeviceRun, bits_to_f64, check_lse, check_output, check_selection, kfrag_layout, to_bits, to_dev,
                     vfrag_layout)
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_random_problem(seed):
     print(f"\n[case] {wl} slots {wl.n_video_slots}", flush=True)
     q, k, v = S.qkv(wl)
     do = S.tensor(wl, "do")
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     npf, scale, D = wl.n_prefix, float(np.float32(wl.scale)), wl.head_dim
     p1 = oracle.perm_static_padded(wl.grid, wl.tile)
     perm = np.ascontiguousarray(np.broadcast_to(p1, (wl.batch, p1.size)))

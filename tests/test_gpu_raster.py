@@ -19,7 +19,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, check_output, desc_for, to_bits
+from parity import DeviceRun, check_output, desc_for, to_bits
 from test_gpu_padded import CASES as PADDED_CASES
 from test_gpu_parity import CASES as PARITY_CASES
 
@@ -29,7 +29,7 @@ NAN_BITS = 0x7FC1  # a quiet NaN in bf16
 
 
 def raster_run(wl, g, grouped=True):
-    """The raster path on the inputs of GpuRun g, into a NaN-filled output."""
+    """The raster path on the inputs of DeviceRun g, into a NaN-filled output."""
     att = bsa.BlockSparseAttention(g.desc, with_lse=True, grouped=grouped)
     out = torch.full_like(g.q.view(torch.int16), NAN_BITS).view(torch.bfloat16)
     att(g.q, g.k, g.v, out)
@@ -48,7 +48,7 @@ CASES = PARITY_CASES + PADDED_CASES
 def test_raster_path_equals_tiled_path(wl):
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     for grouped in (True, False):
         att, out = raster_run(wl, g, grouped)
         n = wl.n_video_slots
@@ -70,7 +70,7 @@ ORACLE_CASES = [PARITY_CASES[1], PARITY_CASES[3], PARITY_CASES[10], PADDED_CASES
 def test_raster_path_matches_oracle(wl):
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v)  # inputs and descriptor only
+    g = DeviceRun(wl, q, k, v)  # inputs and descriptor only
     att, out = raster_run(wl, g)
     npf, scale = wl.n_prefix, float(np.float32(wl.scale))
     perm = att.perm.cpu().numpy()[:, :wl.n_video_slots]
@@ -128,7 +128,7 @@ def test_csr_raster_equals_tiled(wl, keep_h, rows_range):
     for bit (output first filled with NaN), lse included; grouped and plain."""
     print(f"\n[case] {wl} keep_per_head={keep_h} rows={rows_range}", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     d, a = g.desc, g.att
     n = wl.n_video_tiles
     kr = None
@@ -177,7 +177,7 @@ def test_structured_raster_equals_tiled(wl, mask, rt, rs):
     for bit."""
     print(f"\n[case] {wl} mask={mask} radii=({rt}, {rs})", flush=True)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     d, a = g.desc, g.att
     rows = wl.batch * wl.heads * wl.n_video_tiles
     row_ptr = torch.empty(rows + 1, dtype=torch.int64, device="cuda")

@@ -21,7 +21,7 @@ import torch
 import block_sparse_attention_39_amd as bsa
 import oracle
 import synthetic as S
-from parity import GpuRun, check_output, check_selection, desc_for, to_bits, to_dev
+from parity import DeviceRun, check_output, check_selection, desc_for, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -40,11 +40,11 @@ CASES = [
 def test_pooling_gathers_equal_plan(wl):
     print(f"\n[case] {wl}", flush=True)
     q, k, v = S.qkv(wl)
-    fused = GpuRun(wl, q, k, v).run()
+    fused = DeviceRun(wl, q, k, v).run()
     means = [x.copy() for x in fused.pooled()]
     idx, out = fused.block_idx().copy(), to_bits(fused.out).copy()
     q_t, k_f = to_bits(fused.att.q_t).copy(), to_bits(fused.att.k_f).copy()
-    plain = GpuRun(wl, q, k, v)
+    plain = DeviceRun(wl, q, k, v)
     plain.att.pool_in_gather = False
     plain.run()
     for a, b in zip(means, plain.pooled()):
@@ -87,7 +87,7 @@ def cancelling_inputs(wl, equal_head: bool):
 def test_cancelling_channels_select_exactly(wl):
     print(f"\n[case] {wl}", flush=True)
     q, k, v = cancelling_inputs(wl, equal_head=True)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     perm = oracle.perm_static(wl.grid)[None]
     qt, kt = oracle.gather(q, perm, 0), oracle.gather(k, perm, 0)
     qp, kp = oracle.pool(qt, 0), oracle.pool(kt, 0)
@@ -126,7 +126,7 @@ def test_equal_scores_everywhere_fallback():
     wl = W("zeros", 1, 2, 64, (8, 16, 40), 23, seed=54)
     q, k, v = S.qkv(wl)
     q = np.zeros_like(q)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     assert np.all(g.block_idx() == np.arange(23))
 
 
@@ -136,7 +136,7 @@ def test_tiled_inputs_convert_to_fragment_layouts():
     same lists and output bit for bit."""
     wl = W("tiled_in", 2, 3, 128, (8, 8, 12), 5, seed=61, n_prefix=64)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     desc, att = g.desc, g.att
     k_t, v_t = torch.empty_like(att.q_t), torch.empty_like(att.q_t)
     bsa.gather(desc, g.k, k_t, att.perm)
@@ -161,7 +161,7 @@ def test_forward_stats_count_rounds():
     per CU no round's start wait gives up."""
     wl = W("stats", 2, 4, 128, (16, 16, 32), 12, seed=62)
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     gave_up, rounds = bsa.forward_stats(g.desc, g.att.workspace)
     print(f"[stats] rounds {rounds}, waits that gave up {gave_up}", flush=True)
     assert rounds >= wl.batch * wl.heads * wl.n_video_tiles // 256
@@ -205,7 +205,7 @@ def test_maximum_total_tiles_whole_path():
     print(f"\n[case] {wl}", flush=True)
     assert wl.n_tokens // 64 == bsa.MAX_VIDEO_TILES * 2 and wl.n_video_tiles == bsa.MAX_VIDEO_TILES
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     perm = oracle.perm_static(wl.grid)[None]
     assert np.array_equal(g.perm(), perm)
     npf = wl.n_prefix

@@ -12,14 +12,14 @@ import torch
 import block_sparse_attention_39_amd as bsa
 from block_sparse_attention_39_amd._lib import lib
 import synthetic as S
-from parity import GpuRun, to_bits
+from parity import DeviceRun, to_bits
 
 W = S.Workload
 
 
 def run_both(wl):
     q, k, v = S.qkv(wl)
-    g = GpuRun(wl, q, k, v).run()
+    g = DeviceRun(wl, q, k, v).run()
     att, d = g.att, g.desc
     o_ws, lse_ws = torch.empty_like(att.o_t), torch.empty_like(att.lse)
     bsa.forward(d, att.q_t, att.k_f, att.v_f, att.block_idx, o_ws, lse_ws, workspace=att.workspace)

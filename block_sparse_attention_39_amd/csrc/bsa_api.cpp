@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <initializer_list>
 #include <cstdint>
 
 #include "bsa_kernels.h"
@@ -33,7 +34,24 @@ bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 // true when the byte ranges [p, p + pb) and [q, q + qb) intersect
 bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
-    return pb > 0 && qb > 0 && a < b + qb && b < a + pb;
+    return p && q && pb > 0 && qb > 0 && a < b + qb && b < a + pb;
+}
+
+// A byte range of a call's argument (null or empty: none).
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+// True if an output range meets another output or any input range.
+bool clash(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(o->p, o->bytes, o2->p, o2->bytes)) return true;
+        for (const Span& i : ins)
+            if (overlaps(o->p, o->bytes, i.p, i.bytes)) return true;
+    }
+    return false;
 }
 
 bsa_status check_desc(const bsa_desc* d, Geo* g) {
@@ -355,13 +373,22 @@ bsa_status bsa_forward_stats_offset(const bsa_desc* desc, size_t* offset) {
 
 namespace {
 
-// The forward's output must not overlap an input that other blocks still
-// read (the last check before a launch): Q and O raster (raster) or tiled,
-// K and V in the fragment layouts (the tiled size).
-bool forward_io_overlap(const Geo& g, const void* q, const void* k, const void* v, const void* o, bool raster) {
+// The forward's outputs (O, the lse, the group counters in the workspace)
+// must not overlap each other or an input that other blocks still read (the
+// last check before a launch): Q and O raster (raster) or tiled, K and V in
+// the fragment layouts (the tiled size), the kept lists (fixed keep: idx;
+// CSR: row_ptr and col_entries entries of idx), the permutation (raster).
+bool forward_io_overlap(const Geo& g, const void* q, const void* k, const void* v, const void* o, bool raster,
+                        const float* lse = nullptr, const int32_t* idx = nullptr, const int64_t* row_ptr = nullptr,
+                        int64_t col_entries = 0, const int32_t* perm = nullptr, const void* progress = nullptr) {
     const size_t tiled = (size_t)g.BH * g.n_tot * g.D * 2;
     const size_t io = raster ? (size_t)g.B * (g.npf + g.n_ras) * g.H * g.D * 2 : tiled;
-    return overlaps(o, io, q, io) || overlaps(o, io, k, tiled) || overlaps(o, io, v, tiled);
+    const size_t lse_b = (size_t)g.BH * g.n_tot * sizeof(float);
+    const size_t idx_b = (size_t)(row_ptr ? col_entries : g.BH * g.nvt * g.k) * sizeof(int32_t);
+    const size_t rp_b = row_ptr ? (size_t)(g.BH * g.nvt + 1) * sizeof(int64_t) : 0;
+    const size_t perm_b = raster ? (size_t)g.B * g.n_video * sizeof(int32_t) : 0;
+    return clash({{o, io}, {lse, lse_b}, {progress, bsa::forward_workspace_bytes()}},
+                 {{q, io}, {k, tiled}, {v, tiled}, {idx, idx_b}, {row_ptr, rp_b}, {perm, perm_b}});
 }
 
 // Checks shared by bsa_forward and bsa_forward_noalloc; fills the kernel
@@ -408,7 +435,8 @@ bsa_status bsa_forward(const bsa_desc* desc, const void* q_tiled, const void* k_
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
-    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false)) return BSA_ERR_ARG;
+    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false, lse, block_idx, nullptr, 0, nullptr, progress))
+        return BSA_ERR_ARG;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }
 
@@ -435,7 +463,8 @@ bsa_status bsa_forward_raster(const bsa_desc* desc, const void* q_raster, const 
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
-    if (forward_io_overlap(g, q_raster, k_frag, v_frag, o_raster, true)) return BSA_ERR_ARG;
+    if (forward_io_overlap(g, q_raster, k_frag, v_frag, o_raster, true, lse, block_idx, nullptr, 0, perm, progress))
+        return BSA_ERR_ARG;
     return launched(bsa::launch_forward(a, (int)g.D, progress, static_cast<hipStream_t>(stream)));
 }
 
@@ -446,7 +475,7 @@ bsa_status bsa_forward_noalloc(const bsa_desc* desc, const void* q_tiled, const 
     const bsa_status st = forward_args(desc, q_tiled, k_frag, v_frag, block_idx, o_tiled, lse, &g, &a);
     if (st != BSA_OK || g.empty) return st;
     if (bsa::forward_workspace_bytes() > bsa::forward_scratch_bytes()) return BSA_ERR_UNSUPPORTED;
-    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false)) return BSA_ERR_ARG;
+    if (forward_io_overlap(g, q_tiled, k_frag, v_frag, o_tiled, false, lse, block_idx)) return BSA_ERR_ARG;
     return launched(bsa::launch_forward_noalloc(a, (int)g.D, static_cast<hipStream_t>(stream)));
 }
 
@@ -559,7 +588,9 @@ bsa_status forward_csr_impl(const bsa_desc* desc, const void* q, const int32_t* 
         if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
         progress = reinterpret_cast<int*>(static_cast<char*>(ws) + L.fwd);
     }
-    if (forward_io_overlap(g, q, k_frag, v_frag, o, raster)) return BSA_ERR_ARG;
+    if (forward_io_overlap(g, q, k_frag, v_frag, o, raster, lse, g.nvt > 0 ? col_idx : nullptr,
+                           g.nvt > 0 ? row_ptr : nullptr, col_entries, raster ? perm : nullptr, progress))
+        return BSA_ERR_ARG;
     bsa::ForwardArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k_frag);
@@ -723,6 +754,18 @@ bsa_status backward_impl(const bsa_desc* desc, const void* q, const void* k, con
     const BwdLayout L = bwd_layout(g, tcap);
     if (!ws || ws_bytes < L.total) return BSA_ERR_WORKSPACE;
     if (misaligned(ws, kAlign)) return BSA_ERR_ALIGN;
+    {
+        // the gradients (raster, written last) must not overlap each other,
+        // an input or the workspace
+        const size_t ras = (size_t)g.B * (g.npf + g.n_ras) * g.H * g.D * 2;
+        const size_t idx_b = (size_t)(csr ? col_entries : g.BH * g.nvt * g.k) * sizeof(int32_t);
+        const size_t rp_b = csr ? (size_t)(g.BH * g.nvt + 1) * sizeof(int64_t) : 0;
+        if (clash({{dq, ras}, {dk, ras}, {dv, ras}},
+                  {{q, ras}, {k, ras}, {v, ras}, {o, ras}, {d_o, ras}, {lse, (size_t)g.BH * g.n_tot * sizeof(float)},
+                   {perm, (size_t)g.B * g.n_video * sizeof(int32_t)}, {idx, g.nvt > 0 ? idx_b : 0},
+                   {row_ptr, g.nvt > 0 ? rp_b : 0}, {ws, L.total}}))
+            return BSA_ERR_ARG;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
     uint16_t* f[7];

@@ -249,8 +249,10 @@ bsa_status bsa_select(const bsa_desc *desc, int32_t *block_idx, void *ws, size_t
  * bf16 products accumulated in float, a float online softmax, and o rounded to
  * bf16 (`o_tiled`, tiled layout).  `lse` (optional, NULL to skip) receives
  * float [B][H][Ntot]: the natural log of sum_j exp(scale * q.k_j) per query.
- * `block_idx` may be NULL only when there is no video.  `o_tiled` must not
- * overlap `q_tiled`, `k_frag` or `v_frag` (BSA_ERR_ARG).
+ * `block_idx` may be NULL only when there is no video.  The outputs
+ * (`o_tiled`, `lse`, and the workspace's group counters) must not overlap
+ * each other or an input (`q_tiled`, `k_frag`, `v_frag`, `block_idx`):
+ * BSA_ERR_ARG, nothing enqueued.
  * `ws` (optional): a workspace of bsa_workspace_size() bytes, 256-byte aligned.
  * With it, the video query tiles run as a persistent grid whose blocks, per
  * XCD, sweep the key tiles in step so that a key tile is fetched once into the
@@ -296,8 +298,9 @@ bsa_status bsa_forward_noalloc(const bsa_desc *desc, const void *q_tiled, const 
  * zeros and are not written.  `q_raster` and `o_raster` bf16 [B][Ntot][H][D]
  * (Ntot counting the real tokens), `perm` int32 [B][Nvideo]; `k_frag`,
  * `v_frag`, `block_idx`, `lse` (tiled [B][H][Ntot], padding slots included),
- * `ws` and the errors as bsa_forward.  o_raster must not overlap q_raster,
- * k_frag or v_frag (BSA_ERR_ARG).
+ * `ws` and the errors as bsa_forward.  o_raster, lse and the workspace's
+ * counters must not overlap each other, q_raster, perm, k_frag, v_frag or
+ * block_idx (BSA_ERR_ARG).
  */
 bsa_status bsa_forward_raster(const bsa_desc *desc, const void *q_raster, const int32_t *perm,
                               const void *k_frag, const void *v_frag, const int32_t *block_idx,
@@ -340,7 +343,9 @@ bsa_status bsa_forward_stats_offset(const bsa_desc *desc, size_t *offset);
  * workspace of bsa_workspace_size.
  * bsa_forward_csr is bsa_forward with the lists read from row_ptr/col_idx;
  * each row must hold 1..nVT entries (row bounds are clamped to that and to
- * col_entries, so a corrupt row_ptr cannot address outside col_idx).
+ * col_entries, so a corrupt row_ptr cannot address outside col_idx).  Its
+ * outputs must not overlap each other or an input, row_ptr and the first
+ * col_entries entries of col_idx included (BSA_ERR_ARG).
  */
 #define BSA_MAX_CSR_HEADS 256
 bsa_status bsa_csr_entries(const bsa_desc *desc, const int32_t *keep_per_head, int64_t *entries);
@@ -428,7 +433,9 @@ bsa_status bsa_backward_workspace_size(const bsa_desc *desc, size_t *bytes);
  * bf16 before their products, the gradients to bf16 at the end.  Tensors must
  * be 16-byte aligned (lse, perm, block_idx 4-byte); at most BSA_MAX_TILES
  * tiles and BSA_MAX_VIDEO_TILES video tiles per (batch, head).  Calls given the
- * same workspace must not run concurrently.  On a ragged grid
+ * same workspace must not run concurrently.  dq, dk and dv must not overlap
+ * each other, an input or the workspace (BSA_ERR_ARG, nothing enqueued).  On
+ * a ragged grid
  * (BSA_TILE_STATIC_PADDED) the gradients are those of the padded forward:
  * padding keys take no weight, padding slots are neither read nor written
  * (perm -1), and the lse is the forward's over the padded tiled order.

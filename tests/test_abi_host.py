@@ -395,6 +395,46 @@ def test_overlapping_output_is_rejected():
         assert L.bsa_permute(ctypes.byref(d), op, None, FAKE, None, FAKE, FAKE + 256, None, 0, None) == ARG, op
 
 
+def test_overlaps_of_lse_lists_and_gradients_are_rejected():
+    """The forward's lse may meet neither an input nor O, and O not the kept
+    lists or the permutation; the backward's three gradients may meet
+    neither each other, an input nor the workspace (BSA_ERR_ARG, nothing
+    enqueued).  Every other argument lies in a region of its own."""
+    L = lib()
+    d = cfg()
+    B, H, D = d.batch, d.heads, d.head_dim
+    n_tot = d.n_prefix + d.grid_t * d.grid_h * d.grid_w
+    tiled = B * H * n_tot * D * 2
+    step = 8 * tiled + (1 << 20)
+    step -= step % 4096
+    R = [FAKE + i * step for i in range(16)]  # disjoint regions
+    q, k, v, idx, o, lse, perm = R[0], R[1], R[2], R[3], R[4], R[5], R[6]
+    # forward, tiled: lse on q, lse on o, o on the kept lists
+    F = L.bsa_forward
+    assert F(ctypes.byref(d), q, k, v, idx, o, q + 256, None, 0, None) == ARG
+    assert F(ctypes.byref(d), q, k, v, idx, o, o + 512, None, 0, None) == ARG
+    assert F(ctypes.byref(d), q, k, v, idx, idx + 16, lse, None, 0, None) == ARG
+    # raster: o on the permutation, lse on k
+    G = L.bsa_forward_raster
+    assert G(ctypes.byref(d), q, perm, k, v, idx, perm, lse, None, 0, None) == ARG
+    assert G(ctypes.byref(d), q, perm, k, v, idx, o, k, None, 0, None) == ARG
+    # CSR: o on the row pointers
+    rp, col = R[7], R[8]
+    assert L.bsa_forward_csr(ctypes.byref(d), q, k, v, rp, col, 5, rp, lse, None, 0, None) == ARG
+    # backward
+    n = ctypes.c_size_t(0)
+    assert L.bsa_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    ws = R[9]
+    d_o, dq, dk, dv = R[10], R[11], R[12], R[13]
+    Bw = L.bsa_backward
+    args = lambda dq_, dk_, dv_: (ctypes.byref(d), q, k, v, o, d_o, lse, perm, idx, dq_, dk_, dv_, ws, n.value, None)
+    assert Bw(*args(dq, dq + 256, dv)) == ARG      # dq and dk meet
+    assert Bw(*args(dq, dk, ws + 4096)) == ARG     # dv inside the workspace
+    assert Bw(*args(d_o, dk, dv)) == ARG           # dq on dO
+    assert Bw(*args(dq, perm, dv)) == ARG          # dk on the permutation
+    assert Bw(*args(dq, dk, lse)) == ARG           # dv on the lse
+
+
 def test_keep_from_sparsity():
     """The sparsity -> kept-tiles helper against the pages' worked figures:
     sparsity 0.75 keeps 480 of 1,920 key tiles per query tile (Prism page,

@@ -51,18 +51,30 @@ __device__ inline int pad_class(const PadGeo& g, int vt) {
     return (((ti + 1) * g.tt > g.T) << 2 | ((hi + 1) * g.th > g.Hg) << 1 | ((wi + 1) * g.tw > g.W)) << 16;
 }
 
-// -inf for the padding keys among one lane's 16 elements of an S^T
-// accumulator of a 32-key half kh, given the class's 64-bit mask of real
-// keys.  The kfrag token order (swap23) puts key 32*kh + 16*c + 8*hf + e at
-// element 8*c + e of lane-half hf.
-template <class V>
-__device__ __attribute__((always_inline)) inline void mask_padding_keys(uint64_t real, int kh, int hf, V& sv) {
+// The real keys among one lane's 16 elements of an S^T accumulator of a
+// 32-key half kh, given the class's 64-bit mask of real keys: bit r set when
+// element r is a real key.  The kfrag token order (swap23) puts key
+// 32*kh + 16*c + 8*hf + e at element 8*c + e of lane-half hf.
+__device__ inline uint32_t real_key_bits(uint64_t real, int kh, int hf) {
     const uint32_t half = kh ? (uint32_t)(real >> 32) : (uint32_t)real;
     const uint32_t x = half >> (8 * hf);
-    const uint32_t bits = (x & 0xffu) | ((x >> 8) & 0xff00u);  // bit r: element r is a real key
+    return (x & 0xffu) | ((x >> 8) & 0xff00u);
+}
+
+// -inf for the elements whose bit is clear: per element a sign-extended bit
+// (0 or all ones) selects between the value and -inf bit by bit.
+template <class V>
+__device__ __attribute__((always_inline)) inline void mask_keys_by_bits(uint32_t bits, V& sv) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-        if (!((bits >> r) & 1u)) sv[r] = -__builtin_inff();
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)bits, r, 1);
+        sv[r] = __uint_as_float((__float_as_uint(sv[r]) & m) | (0xff800000u & ~m));
+    }
+}
+
+template <class V>
+__device__ __attribute__((always_inline)) inline void mask_padding_keys(uint64_t real, int kh, int hf, V& sv) {
+    mask_keys_by_bits(real_key_bits(real, kh, hf), sv);
 }
 
 // Static tile order: perm[b][p] for all b (the same closed form per batch).

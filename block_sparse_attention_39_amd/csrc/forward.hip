@@ -97,8 +97,11 @@ struct Cfg {
     // raster Q and O: the raster row of each of the tile's 64 tokens, past
     // both areas (written at staging, read by the epilogue's stores)
     static constexpr int ROWS = LDS_FLOATS;
-    template <bool kRas>
-    static constexpr int lds_floats() { return LDS_FLOATS + (kRas ? kTile : 0); }
+    // ragged grid: the 8 boundary classes' 64-bit masks of real keys, written
+    // once per block, after the rows
+    static constexpr int PTAB = LDS_FLOATS + kTile;
+    template <bool kRas, bool kPad>
+    static constexpr int lds_floats() { return LDS_FLOATS + (kRas || kPad ? kTile : 0) + (kPad ? 16 : 0); }
 };
 
 // max of x over lane l and lane l ^ 32
@@ -403,6 +406,13 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     int t_k_next = TILE_AT(2);  // tile whose K is loaded next
     int t_s = CLASSED_AT(0);    // ragged grid: slice n's list entry, with its boundary class
     int t_s_next = CLASSED_AT(1);
+    // ragged grid: the class table of real-key masks, and this lane's
+    // real-key bits of slice n + 1 (boundary slices only), read a step ahead
+    const uint64_t* ptab = (const uint64_t*)(lds + CF::PTAB);
+    auto slice_bits = [&](int ts) -> uint32_t {
+        return (kPad && (ts >> 16)) ? real_key_bits(ptab[ts >> 16], kh, hf) : 0xffffu;
+    };
+    uint32_t mb_next = kPad ? slice_bits(t_s) : 0xffffu;
 
     for (int n0 = 0; n0 <= my_n; n0 += 2) {
 #pragma unroll
@@ -441,6 +451,9 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
             constexpr int GSUM = NSA + 3;         // slot of the normaliser's dot products
             static_assert(NV == SD && NSA * PPS == 8 && GSUM < W, "window layout");
             float lrun[2];
+            // a boundary slice: this lane's real-key bits, for both halves
+            const uint32_t mb_s = mb_next;
+            if (kPad) mb_next = slice_bits(t_s_next);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 // h = 0: PV of query half 1 and S of half 1 (this slice);
@@ -448,7 +461,11 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
                 const int pq = 1 - h, sq = 1 - h;
                 const float neg_m = vmask - m_ref[h];
                 // a slice of a boundary tile: its padding keys out
-                if (kPad && (t_s >> 16)) mask_padding_keys(a.pad.real[t_s >> 16], kh, hf, sacc[h]);
+                if (kPad && (t_s >> 16)) {
+                    uint32_t mb = mb_s;
+                    asm volatile("" : "+v"(mb));  // per half: the 16 element masks are not kept live
+                    mask_keys_by_bits(mb, sacc[h]);
+                }
                 float xa[8][2], xe[8][2];
 #pragma unroll
                 for (int g = 0; g < W; ++g) {
@@ -538,6 +555,7 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
             if (kPad) {
                 t_s = t_s_next;
                 t_s_next = __builtin_amdgcn_readfirstlane(t_s_after);
+
             }
         }
     }
@@ -624,6 +642,20 @@ __device__ __attribute__((always_inline)) inline void run_tile(const ForwardArgs
     }
 }
 
+// Ragged grid: the boundary classes' masks of real keys into LDS (read after
+// the first tile's staging barrier), so that a slice's mask is an LDS read
+// instead of a dynamically indexed kernel argument.
+template <int D>
+__device__ inline void write_pad_table(const ForwardArgs& a, float* lds) {
+    if (threadIdx.x < 8) {
+        uint64_t v = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if ((int)threadIdx.x == c) v = a.pad.real[c];
+        ((uint64_t*)(lds + Cfg<D>::PTAB))[threadIdx.x] = v;
+    }
+}
+
 // The first loads of a block's first tile (nothing to overlap them with).
 template <int D, bool kRas>
 __device__ __attribute__((always_inline)) inline void fetch_first_direct(const ForwardArgs& a, const Item& it,
@@ -645,7 +677,7 @@ __device__ __attribute__((always_inline)) inline void fetch_first_direct(const F
 template <int D, bool kPad, bool kRas>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 sparse_fwd_kernel(ForwardArgs a, int64_t first) {
-    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::template lds_floats<kRas>()];
+    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::template lds_floats<kRas, kPad>()];
     const int64_t g = first + blockIdx.x;
     const int64_t n_pref = (int64_t)a.BH * a.npt;
     Item it;
@@ -657,6 +689,7 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
         it = Item{gv / a.nvt, a.npt + vi, vi};
     }
     const Wave w;
+    if (kPad) write_pad_table<D>(a, lds);
     bf16x8 kf[2][Cfg<D>::SD], vf[2][Cfg<D>::NV];
     u32x4 qpre[Regs<D>::QPT];
     int lpre[kListPre];
@@ -671,7 +704,7 @@ sparse_fwd_kernel(ForwardArgs a, int64_t first) {
 template <int D, bool kPad, bool kRas>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 sparse_fwd_grouped_kernel(ForwardArgs a, int* progress, int* stats) {
-    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::template lds_floats<kRas>()];
+    __shared__ __attribute__((aligned(16))) float lds[Cfg<D>::template lds_floats<kRas, kPad>()];
     const int group = blockIdx.x % kGroups, slot = blockIdx.x / kGroups;
     const int S = gridDim.x / kGroups;
     const int64_t n_items = (int64_t)a.BH * a.nvt;
@@ -681,6 +714,7 @@ sparse_fwd_grouped_kernel(ForwardArgs a, int* progress, int* stats) {
         return Item{item / a.nvt, a.npt + (int)(item % a.nvt), (int)(item % a.nvt)};
     };
     const Wave w;
+    if (kPad) write_pad_table<D>(a, lds);
     bf16x8 kf[2][Cfg<D>::SD], vf[2][Cfg<D>::NV];
     u32x4 qpre[Regs<D>::QPT];
     int lpre[kListPre];
